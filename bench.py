@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Mixed-resolution decode benchmark on one MI355X.
+
+One step = one decode step of one attention layer for the whole batch: route
+(per-head routing + compaction) then mixed-resolution attention (full-res +
+size-corrected summaries + expanded spans rebuilt from their factors) and the
+log-sum-exp combine.  Workload: Llama-3-8B-shaped layer (32 query heads, 8 KV
+heads, head dim 128, bf16), 128K context, batch 4, device-resident factors,
+5% union expansion per step, ranks 16..64 (synthetic seeded inputs; the
+pages' own evaluation sets are not available).  Inputs are resident in HBM
+before timing; the cache is rotated over >= 2 copies so the 256 MB last-level
+cache cannot hold the working set.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, plan, counts, lists, e):
+    """Bytes the method must move per step (dense work it avoids excluded).
+
+    Returns (route, attend, total): route = q + rho; attend = full-res K/V +
+    summaries kbar/vbar + factors of listed spans (+ q); total adds theta... as
+    the sum over sequences of Hq*d*(e+4) + per KV head (e*2d*n_full +
+    e*3d*n_seg + sum over listed spans of e*r*(L+2d) + 8r)."""
+    import numpy as np
+    d, Hq, Hkv = w.head_dim, w.n_q_heads, w.n_kv_heads
+    route = attend = total = 0
+    for b in range(w.batch):
+        nf, ns = int(plan.n_full[b]), int(plan.n_seg[b])
+        so = plan.seg_off[b]
+        L = (so[1:ns + 1] - so[:ns] - 1).astype(np.int64)
+        r = plan.rank[b, :ns].astype(np.int64)
+        fac = 0
+        for kv in range(Hkv):
+            c = int(counts[b, kv])
+            idx = lists[b, kv, :c]
+            fac += int((e * r[idx] * (L[idx] + 2 * d) + 8 * r[idx]).sum())
+        route += Hq * d * e + Hkv * ns * d * e
+        attend += Hq * d * e + Hkv * (e * 2 * d * nf + e * 2 * d * ns) + fac
+        total += Hq * d * (e + 4) + Hkv * (e * 2 * d * nf + e * 3 * d * ns) + fac
+    return route, attend, total
+
+
+def cpu_baseline(w, x, theta, budget_s=12.0):
+    """The oracle, as it stands, on one sequence of the workload (b = 0),
+    single-threaded BLAS; steps are timed until the budget is spent.  Scaled to
+    full steps by the batch size."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle as O
+    t0 = time.time()
+    with threadpool_limits(1):
+        cache = O.build_cache(x.k[:1], x.v[:1], x.surprisal[:1], x.boundary_thr[:1], x.route_proj, x.rank_req[:1],
+                              x.gate[:1], n_sink=w.n_sink, n_recent=w.n_recent, lo=w.min_span, hi=w.max_span,
+                              dtype=w.dtype)
+        log(f"oracle cache for sequence 0 built in {time.time() - t0:.1f}s")
+        G = w.group
+        n = 0
+        t1 = time.perf_counter()
+        while True:
+            st = n % x.q.shape[0]
+            q = x.q[st, 0]
+            z = np.concatenate([O.route_scores(q[kv * G:(kv + 1) * G], cache.rho[0][kv])
+                                for kv in range(w.n_kv_heads)])
+            dec = z > theta[0][:, None]
+            O.mixed_attention(cache, 0, q, dec, G)
+            n += 1
+            el = time.perf_counter() - t1
+            if el >= budget_s or n >= 64:
+                break
+    per_seq_step = el / n
+    steps_per_s = 1.0 / (per_seq_step * w.batch)
+    return {"value": steps_per_s, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequence 0 of {w.batch} (all {w.n_q_heads} heads), {n} decode steps (route + mixed "
+                      f"attention, fp64 numpy, 1 BLAS thread) in {el:.1f}s; steps/s = 1/(time per sequence-step "
+                      f"x batch {w.batch})",
+            "eff_ctx_tokens_per_s": steps_per_s * w.batch * w.n_ctx}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--frac", type=float, default=0.05, help="target union expansion fraction")
+    ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto, >= 2)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--queries", type=int, default=64)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    from hierarchical_kv_cache_sekv_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.workload(args.workload, factors_on_host=False)
+    e = 2 if w.dtype == "bf16" else 4
+    Q = args.queries
+    log(f"workload {w.name}: B={w.batch} T={w.n_ctx} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
+        f"{w.dtype} ranks {w.rank_lo}..{w.rank_hi} f={args.frac}")
+    t0 = time.time()
+    x = synth.make_inputs(w, n_steps=Q)
+    log(f"inputs drawn in {time.time() - t0:.1f}s")
+
+    ctx = B.Context(0)
+    cfg = B.make_config(w)
+    plan = B.plan_spans(cfg, x.surprisal, x.boundary_thr, x.rank_req)
+    cache = B.SpanCache(cfg, plan)
+    et = cache.elem
+    t0 = time.time()
+    kd = torch.from_numpy(x.k).to(et).cuda()
+    vd = torch.from_numpy(x.v).to(et).cuda()
+    B.build_spans(ctx, cache, kd, vd, x.surprisal, x.route_proj, x.gate)
+    del kd, vd
+    torch.cuda.synchronize()
+    log(f"library build (plan + summaries + rank-r factors) in {time.time() - t0:.1f}s; n_seg={plan.n_seg.tolist()}")
+
+    # thresholds: per-head quantiles of the routing scores over the query set
+    G = w.group
+    qf = torch.from_numpy(x.q).cuda()                      # [Q][B][Hq][d] f32 (bf16-exact)
+    rho = cache.rho.float()
+    theta = np.empty((w.batch, w.n_q_heads), np.float32)
+    for b in range(w.batch):
+        ns = int(plan.n_seg[b])
+        z = torch.empty((Q, w.n_q_heads, ns), device="cuda")
+        for kv in range(w.n_kv_heads):
+            z[:, kv * G:(kv + 1) * G] = qf[:, b, kv * G:(kv + 1) * G] @ rho[b, kv, :ns].T
+        theta[b] = synth.calibrate_theta(z.cpu().numpy(), args.frac, G)
+    theta_d = torch.from_numpy(theta).cuda()
+    qd = qf.to(et).contiguous()
+    del qf, rho
+
+    resident = cache.device_bytes()
+    ncopy = args.copies or max(2, math.ceil((1 << 30) / resident))
+    caches = [cache] + [cache.clone() for _ in range(ncopy - 1)]
+    structs = [c.struct() for c in caches]
+    outs = [B.RouteOut(cfg, cache.seg_cap) for _ in range(ncopy)]
+    rws = B.route_workspace(cache)
+    dws = B.DecodeWorkspace(cache)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    log(f"{ncopy} cache copies of {resident / 2**20:.0f} MiB each resident in HBM")
+
+    def step(i):
+        c = i % ncopy
+        qs = qd[i % Q]
+        B.route(ctx, caches[c], qs, theta_d[:], outs[c], rws, spans=structs[c])
+        B.decode(ctx, caches[c], qs, outs[c], out, dws, spans=structs[c])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ctx.profile(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    ev_ms = ev0.elapsed_time(ev1)
+    route_ms, route_n, att_ms, att_n = ctx.profile_read()
+    ctx.profile(False)
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ev_ms:.2f} ms; route avg "
+        f"{route_ms / max(route_n, 1) * 1e3:.1f} us, attention avg {att_ms / max(att_n, 1) * 1e3:.1f} us")
+
+    # algorithmic bytes of the timed steps (lists realized per query step)
+    per_q = []
+    for qi in range(Q):
+        B.route(ctx, cache, qd[qi], theta_d, outs[0], rws)
+        torch.cuda.synchronize()
+        cnt = outs[0].exp_count.cpu().numpy()
+        lst = outs[0].exp_list.cpu().numpy()
+        per_q.append(algorithmic_bytes(w, plan, cnt, lst, e) + (cnt.sum() / max(1, sum(int(plan.n_seg[b]) for b in range(w.batch)) * w.n_kv_heads),))
+    idx = [(args.warmup + i) % Q for i in range(args.steps)]
+    route_b = sum(per_q[i][0] for i in idx) / args.steps
+    att_b = sum(per_q[i][1] for i in idx) / args.steps
+    tot_b = sum(per_q[i][2] for i in idx) / args.steps
+    f_real = sum(per_q[i][3] for i in idx) / args.steps
+    att_avg_s = att_ms / 1e3 / max(att_n, 1)
+    route_avg_s = route_ms / 1e3 / max(route_n, 1)
+    achieved = att_b / att_avg_s / 1e9
+    step_gbs = tot_b / (ms_per_step / 1e3) / 1e9
+    steps_per_s = 1e3 / ms_per_step
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        base = cpu_baseline(w, x, theta)
+        log(f"oracle: {base['value']:.4f} steps/s ({base['sample']})")
+
+    rec = {
+        "metric": "mixed-res decode steps/s and effective ctx tokens/s @128K; % of HBM peak",
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; Llama-3-8B layer shape, lognormal surprisal, rank-4 block structure)",
+        "config": {"workload": w.name, "batch": w.batch, "n_ctx": w.n_ctx, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rank_range": [w.rank_lo, w.rank_hi],
+                   "expand_frac_target": args.frac, "expand_frac_realized": round(float(f_real), 4),
+                   "factors": "device", "layers": 1, "cache_copies_rotated": ncopy, "launch": "eager"},
+        "eff_ctx_tokens_per_s": steps_per_s * w.batch * w.n_ctx,
+        "algorithmic_bytes_per_step": int(tot_b),
+        "step_hbm_gbs": step_gbs,
+        "step_hbm_frac": step_gbs / PEAK_HBM_GBS,
+        "kernels_us": {"route": route_avg_s * 1e6, "attend": att_avg_s * 1e6},
+        "roofline": {"bound": "hbm", "kernel": "attend_kernel", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "bytes_per_launch": int(att_b)},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(rec), flush=True)
+    ctx.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,427 @@
+"""ctypes binding of libsekv (include/sekv.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of ``libsekv.so``.  torch is used for device memory and streams.  If
+the library is not built, importing this module raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsekv.so")
+
+SEKV_OK, SEKV_EINVAL, SEKV_ESHAPE, SEKV_ECAPACITY, SEKV_EHIP, SEKV_ENOMEM = range(6)
+SEKV_F32, SEKV_BF16 = 0, 1
+STATUS_NAMES = {0: "SEKV_OK", 1: "SEKV_EINVAL", 2: "SEKV_ESHAPE", 3: "SEKV_ECAPACITY", 4: "SEKV_EHIP", 5: "SEKV_ENOMEM"}
+
+EXPORTS = [
+    "sekv_ctx_create", "sekv_ctx_destroy", "sekv_last_error", "sekv_capacities", "sekv_plan_spans",
+    "sekv_build_spans", "sekv_route_workspace_bytes", "sekv_route", "sekv_reconstruct",
+    "sekv_decode_workspace_bytes", "sekv_decode_host_workspace_bytes", "sekv_mixed_attention_decode",
+    "sekv_profile_enable", "sekv_profile_read",
+]
+
+
+class SekvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_ctx", "n_q_heads", "n_kv_heads", "head_dim", "n_sink", "n_recent", "min_span",
+        "max_span", "dtype", "factors_on_host")]
+
+
+_p = ctypes.c_void_p
+
+
+class Spans(ctypes.Structure):
+    _fields_ = [
+        ("seg_cap", ctypes.c_int32), ("full_cap", ctypes.c_int32),
+        ("n_seg_host", _p), ("n_full_host", _p), ("seg_off", _p), ("rank", _p),
+        ("full_k", _p), ("full_v", _p), ("sum_k", _p), ("sum_v", _p), ("rho", _p),
+        ("fac_off", _p), ("sg_off", _p), ("fac", _p), ("sg", _p),
+        ("fac_elems", ctypes.c_int64), ("sg_elems", ctypes.c_int64),
+        ("seg_off_host", _p), ("rank_host", _p), ("fac_off_host", _p), ("sg_off_host", _p),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m hierarchical_kv_cache_sekv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    S, C = ctypes.POINTER(Spans), ctypes.POINTER(Config)
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "sekv_ctx_create": (i32, [ctypes.c_int, ctypes.POINTER(_p)]),
+        "sekv_ctx_destroy": (None, [_p]),
+        "sekv_last_error": (ctypes.c_char_p, []),
+        "sekv_capacities": (i32, [C, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+        "sekv_plan_spans": (i32, [C, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+        "sekv_build_spans": (i32, [_p, C, _p, _p, _p, _p, _p, i32, S, _p]),
+        "sekv_route_workspace_bytes": (sz, [C, S]),
+        "sekv_route": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, sz, _p]),
+        "sekv_reconstruct": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p]),
+        "sekv_decode_workspace_bytes": (sz, [C, S]),
+        "sekv_decode_host_workspace_bytes": (sz, [C, S]),
+        "sekv_mixed_attention_decode": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, sz, _p, sz, _p, _p]),
+        "sekv_profile_enable": (i32, [_p, i32]),
+        "sekv_profile_read": (i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
+                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+def last_error() -> str:
+    return LIB.sekv_last_error().decode()
+
+
+def _check(status: int):
+    if status != SEKV_OK:
+        raise SekvError(status, last_error())
+
+
+def _ptr(x) -> Optional[int]:
+    """Address of a torch tensor or numpy array (None for None)."""
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        assert x.flags["C_CONTIGUOUS"]
+        return x.ctypes.data
+    assert x.is_contiguous()
+    return x.data_ptr()
+
+
+def make_config(w, factors_on_host: Optional[bool] = None) -> Config:
+    """Config from a workload description (any object with the workload fields)."""
+    return Config(w.batch, w.n_ctx, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_sink, w.n_recent,
+                  w.min_span, w.max_span, SEKV_BF16 if w.dtype == "bf16" else SEKV_F32,
+                  int(w.factors_on_host if factors_on_host is None else factors_on_host))
+
+
+def capacities(cfg: Config):
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(LIB.sekv_capacities(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+@dataclasses.dataclass
+class Plan:
+    n_seg: np.ndarray
+    n_full: np.ndarray
+    seg_off: np.ndarray
+    rank: np.ndarray
+    fac_off: np.ndarray
+    sg_off: np.ndarray
+    fac_elems: int
+    sg_elems: int
+
+
+def plan_spans(cfg: Config, surprisal: np.ndarray, thr: np.ndarray, rank_req: np.ndarray) -> Plan:
+    """Host-only segmentation and pool layout (sekv_plan_spans)."""
+    B, Hkv = cfg.batch, cfg.n_kv_heads
+    cap, _ = capacities(cfg)
+    s = np.ascontiguousarray(surprisal, np.float32)
+    t = np.ascontiguousarray(thr, np.float32)
+    rr = np.ascontiguousarray(rank_req, np.int32)
+    assert s.shape == (B, cfg.n_ctx) and t.shape == (B,) and rr.shape == (B, cap)
+    n_seg = np.zeros(B, np.int32)
+    n_full = np.zeros(B, np.int32)
+    seg_off = np.zeros((B, cap + 1), np.int32)
+    rank = np.zeros((B, cap), np.int32)
+    fac_off = np.zeros((B, Hkv, cap), np.int64)
+    sg_off = np.zeros((B, Hkv, cap), np.int64)
+    fe, ge = ctypes.c_int64(), ctypes.c_int64()
+    _check(LIB.sekv_plan_spans(ctypes.byref(cfg), _ptr(s), _ptr(t), _ptr(rr), _ptr(n_seg), _ptr(n_full),
+                               _ptr(seg_off), _ptr(rank), _ptr(fac_off), _ptr(sg_off), ctypes.byref(fe),
+                               ctypes.byref(ge)))
+    return Plan(n_seg, n_full, seg_off, rank, fac_off, sg_off, fe.value, ge.value)
+
+
+class Context:
+    def __init__(self, device: int = 0):
+        h = _p()
+        _check(LIB.sekv_ctx_create(device, ctypes.byref(h)))
+        self.handle = h
+        self.device = device
+
+    def profile(self, enable: bool):
+        _check(LIB.sekv_profile_enable(self.handle, int(enable)))
+
+    def profile_read(self):
+        """(route_ms_total, route_launches, attend_ms_total, attend_launches) since the last read."""
+        rm, am = ctypes.c_double(), ctypes.c_double()
+        rn, an = ctypes.c_int64(), ctypes.c_int64()
+        _check(LIB.sekv_profile_read(self.handle, ctypes.byref(rm), ctypes.byref(rn), ctypes.byref(am),
+                                     ctypes.byref(an)))
+        return rm.value, rn.value, am.value, an.value
+
+    def close(self):
+        if self.handle:
+            LIB.sekv_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _torch():
+    import torch
+    return torch
+
+
+class SpanCache:
+    """Caller-owned span cache: torch device tensors plus the host plan arrays.
+
+    Element arrays use torch.bfloat16 (bit-identical to the raw bf16 the
+    kernels read) or torch.float32.  With factors_on_host the two factor pools
+    are pinned host tensors.
+    """
+
+    def __init__(self, cfg: Config, plan: Plan, device="cuda"):
+        torch = _torch()
+        self.cfg = cfg
+        self.plan = plan
+        self.seg_cap, self.full_cap = capacities(cfg)
+        B, Hkv, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+        et = torch.bfloat16 if cfg.dtype == SEKV_BF16 else torch.float32
+        self.elem = et
+        dev = torch.device(device)
+        self.seg_off = torch.from_numpy(plan.seg_off).to(dev)
+        self.rank = torch.from_numpy(plan.rank).to(dev)
+        self.fac_off = torch.from_numpy(plan.fac_off).to(dev)
+        self.sg_off = torch.from_numpy(plan.sg_off).to(dev)
+        self.full_k = torch.zeros((B, Hkv, self.full_cap, D), dtype=et, device=dev)
+        self.full_v = torch.zeros_like(self.full_k)
+        self.sum_k = torch.zeros((B, Hkv, self.seg_cap, D), dtype=et, device=dev)
+        self.sum_v = torch.zeros_like(self.sum_k)
+        self.rho = torch.zeros_like(self.sum_k)
+        nf = max(plan.fac_elems, 8)
+        ng = max(plan.sg_elems, 8)
+        if cfg.factors_on_host:
+            self.fac = torch.zeros(nf, dtype=et, pin_memory=True)
+            self.sg = torch.zeros(ng, dtype=torch.float32, pin_memory=True)
+        else:
+            self.fac = torch.zeros(nf, dtype=et, device=dev)
+            self.sg = torch.zeros(ng, dtype=torch.float32, device=dev)
+        self._host = [np.ascontiguousarray(a) for a in (plan.n_seg, plan.n_full, plan.seg_off, plan.rank,
+                                                          plan.fac_off, plan.sg_off)]
+
+    def struct(self) -> Spans:
+        n_seg, n_full, seg_off, rank, fac_off, sg_off = self._host
+        return Spans(self.seg_cap, self.full_cap, _ptr(n_seg), _ptr(n_full), _ptr(self.seg_off), _ptr(self.rank),
+                     _ptr(self.full_k), _ptr(self.full_v), _ptr(self.sum_k), _ptr(self.sum_v), _ptr(self.rho),
+                     _ptr(self.fac_off), _ptr(self.sg_off), _ptr(self.fac), _ptr(self.sg),
+                     self.fac.numel(), self.sg.numel(), _ptr(seg_off), _ptr(rank), _ptr(fac_off), _ptr(sg_off))
+
+    def clone(self) -> "SpanCache":
+        """Independent copy at new addresses (same contents)."""
+        new = object.__new__(SpanCache)
+        new.__dict__.update(self.__dict__)
+        for name in ("seg_off", "rank", "fac_off", "sg_off", "full_k", "full_v", "sum_k", "sum_v", "rho"):
+            setattr(new, name, getattr(self, name).clone())
+        if self.cfg.factors_on_host:
+            new.fac = self.fac.clone().pin_memory()
+            new.sg = self.sg.clone().pin_memory()
+        else:
+            new.fac = self.fac.clone()
+            new.sg = self.sg.clone()
+        return new
+
+    def device_bytes(self) -> int:
+        n = 0
+        for name in ("seg_off", "rank", "fac_off", "sg_off", "full_k", "full_v", "sum_k", "sum_v", "rho"):
+            t = getattr(self, name)
+            n += t.numel() * t.element_size()
+        if not self.cfg.factors_on_host:
+            n += self.fac.numel() * self.fac.element_size() + self.sg.numel() * 4
+        return n
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def build_spans(ctx: Context, cache: SpanCache, k, v, surprisal: np.ndarray, route_proj: np.ndarray,
+                gate: np.ndarray, stream=None):
+    """sekv_build_spans: fill ``cache`` from device K/V [B][Hkv][T][d]."""
+    cfg = cache.cfg
+    s = np.ascontiguousarray(surprisal, np.float32)
+    P = np.ascontiguousarray(route_proj, np.float32)
+    g = np.ascontiguousarray(gate, np.float32)
+    assert g.shape[:3] == (cfg.batch, cfg.n_kv_heads, cache.seg_cap)
+    st = cache.struct()
+    _check(LIB.sekv_build_spans(ctx.handle, ctypes.byref(cfg), _ptr(k), _ptr(v), _ptr(s), _ptr(P), _ptr(g),
+                                g.shape[3], ctypes.byref(st), _stream_handle(stream)))
+
+
+class RouteOut:
+    def __init__(self, cfg: Config, seg_cap: int, device="cuda"):
+        torch = _torch()
+        B, Hkv = cfg.batch, cfg.n_kv_heads
+        self.exp_list = torch.zeros((B, Hkv, seg_cap), dtype=torch.int32, device=device)
+        self.exp_mask = torch.zeros((B, Hkv, seg_cap), dtype=torch.uint8, device=device)
+        self.exp_count = torch.zeros((B, Hkv), dtype=torch.int32, device=device)
+
+
+def route_workspace(cache: SpanCache, device="cuda"):
+    torch = _torch()
+    n = LIB.sekv_route_workspace_bytes(ctypes.byref(cache.cfg), ctypes.byref(cache.struct()))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def route(ctx: Context, cache: SpanCache, q, theta, out: RouteOut, ws, stream=None, spans: Optional[Spans] = None):
+    """sekv_route: q [B][Hq][d] (cache dtype), theta [B][Hq] f32, all device."""
+    st = spans if spans is not None else cache.struct()
+    _check(LIB.sekv_route(ctx.handle, ctypes.byref(cache.cfg), ctypes.byref(st), _ptr(q), _ptr(theta),
+                          _ptr(out.exp_list), _ptr(out.exp_mask), _ptr(out.exp_count), _ptr(ws),
+                          ws.numel(), _stream_handle(stream)))
+
+
+def reconstruct(ctx: Context, cache: SpanCache, out: RouteOut, stream=None):
+    """sekv_reconstruct: returns (tok_off, k_out, v_out) device tensors."""
+    torch = _torch()
+    cfg = cache.cfg
+    B, Hkv, T, D = cfg.batch, cfg.n_kv_heads, cfg.n_ctx, cfg.head_dim
+    dev = out.exp_list.device
+    tok_off = torch.zeros((B, Hkv, cache.seg_cap + 1), dtype=torch.int32, device=dev)
+    k_out = torch.zeros((B, Hkv, T, D), dtype=torch.float32, device=dev)
+    v_out = torch.zeros_like(k_out)
+    _check(LIB.sekv_reconstruct(ctx.handle, ctypes.byref(cfg), ctypes.byref(cache.struct()), _ptr(out.exp_list),
+                                _ptr(out.exp_count), _ptr(tok_off), _ptr(k_out), _ptr(v_out), _stream_handle(stream)))
+    return tok_off, k_out, v_out
+
+
+class DecodeWorkspace:
+    def __init__(self, cache: SpanCache, device="cuda"):
+        torch = _torch()
+        st = cache.struct()
+        nd = LIB.sekv_decode_workspace_bytes(ctypes.byref(cache.cfg), ctypes.byref(st))
+        nh = LIB.sekv_decode_host_workspace_bytes(ctypes.byref(cache.cfg), ctypes.byref(st))
+        self.dev = torch.empty(max(nd, 256), dtype=torch.uint8, device=device)
+        self.host = torch.empty(nh, dtype=torch.uint8, pin_memory=True) if nh > 0 else None
+
+
+def decode(ctx: Context, cache: SpanCache, q, route_out: RouteOut, out, ws: DecodeWorkspace, stream=None,
+           copy_stream=None, spans: Optional[Spans] = None):
+    """sekv_mixed_attention_decode: out [B][Hq][d] f32 device."""
+    st = spans if spans is not None else cache.struct()
+    host_ptr = _ptr(ws.host) if ws.host is not None else None
+    host_n = ws.host.numel() if ws.host is not None else 0
+    cs = copy_stream.cuda_stream if copy_stream is not None else None
+    _check(LIB.sekv_mixed_attention_decode(ctx.handle, ctypes.byref(cache.cfg), ctypes.byref(st), _ptr(q),
+                                           _ptr(route_out.exp_list), _ptr(route_out.exp_mask),
+                                           _ptr(route_out.exp_count), _ptr(out), _ptr(ws.dev), ws.dev.numel(),
+                                           host_ptr, host_n, _stream_handle(stream), cs))
+
+
+# ----------------------------------------------------------------- marshalling
+def fill_cache(cache: SpanCache, parts) -> None:
+    """Copy span-cache contents given as plain per-sequence numpy arrays into
+    the ABI layout (layout marshalling only).
+
+    ``parts`` provides, for each sequence b and KV head kv: ``full_k[b][kv]``,
+    ``full_v``, ``sum_k``, ``sum_v``, ``rho`` ([n][d] arrays of values that are
+    exact in the cache dtype) and, for each span i, ``U[b][kv][i]`` [L][r],
+    ``sigma[b][kv][i]`` [r], ``gate[b][kv][i]`` [r], ``Vh[b][kv][i]`` [r][2d].
+    The plan of ``cache`` must describe the same spans and ranks.
+    """
+    torch = _torch()
+    cfg, plan = cache.cfg, cache.plan
+    B, Hkv, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    et = cache.elem
+    fk = np.zeros((B, Hkv, cache.full_cap, D), np.float32)
+    fv = np.zeros_like(fk)
+    sk = np.zeros((B, Hkv, cache.seg_cap, D), np.float32)
+    sv = np.zeros_like(sk)
+    rh = np.zeros_like(sk)
+    fac = np.zeros(cache.fac.numel(), np.float32)
+    sg = np.zeros(cache.sg.numel(), np.float32)
+    for b in range(B):
+        n = int(plan.n_seg[b])
+        so = plan.seg_off[b]
+        for kv in range(Hkv):
+            nf = parts.full_k[b][kv].shape[0]
+            fk[b, kv, :nf] = parts.full_k[b][kv]
+            fv[b, kv, :nf] = parts.full_v[b][kv]
+            sk[b, kv, :n] = parts.sum_k[b][kv]
+            sv[b, kv, :n] = parts.sum_v[b][kv]
+            rh[b, kv, :n] = parts.rho[b][kv]
+            for i in range(n):
+                U = np.asarray(parts.U[b][kv][i], np.float32)
+                Vh = np.asarray(parts.Vh[b][kv][i], np.float32)
+                L, r = U.shape
+                assert L == so[i + 1] - so[i] - 1 and r == plan.rank[b, i]
+                rp = (r + 7) // 8 * 8
+                o = int(plan.fac_off[b, kv, i])
+                blk = np.zeros((L, rp), np.float32)
+                blk[:, :r] = U
+                fac[o:o + L * rp] = blk.reshape(-1)
+                fac[o + L * rp:o + L * rp + r * 2 * D] = Vh.reshape(-1)
+                go = int(plan.sg_off[b, kv, i])
+                sg[go:go + r] = parts.sigma[b][kv][i]
+                sg[go + r:go + 2 * r] = parts.gate[b][kv][i]
+
+    def put(dst, src):
+        dst.copy_(torch.from_numpy(src).to(et))
+
+    put(cache.full_k, fk)
+    put(cache.full_v, fv)
+    put(cache.sum_k, sk)
+    put(cache.sum_v, sv)
+    put(cache.rho, rh)
+    cache.fac.copy_(torch.from_numpy(fac).to(et))
+    cache.sg.copy_(torch.from_numpy(sg))
+
+
+def layout_from_segments(cfg: Config, seg_offs, ranks) -> Plan:
+    """Plan (pool layout) for spans given by per-sequence offsets and ranks,
+    laid out in (b, kv, span) order like sekv_plan_spans.  Marshalling only."""
+    B, Hkv, D, T = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.n_ctx
+    cap, _ = capacities(cfg)
+    n_seg = np.zeros(B, np.int32)
+    n_full = np.zeros(B, np.int32)
+    seg_off = np.zeros((B, cap + 1), np.int32)
+    rank = np.zeros((B, cap), np.int32)
+    fac_off = np.zeros((B, Hkv, cap), np.int64)
+    sg_off = np.zeros((B, Hkv, cap), np.int64)
+    fo = go = 0
+    for b in range(B):
+        so = np.asarray(seg_offs[b], np.int64)
+        n = len(so) - 1
+        n_seg[b] = n
+        seg_off[b, :n + 1] = so
+        seg_off[b, n + 1:] = so[-1]
+        n_full[b] = cfg.n_sink + n + (T - int(so[-1]))
+        rank[b, :n] = np.asarray(ranks[b], np.int32)[:n]
+        L = so[1:] - so[:-1] - 1
+        for kv in range(Hkv):
+            for i in range(n):
+                r = int(rank[b, i])
+                rp = (r + 7) // 8 * 8
+                fac_off[b, kv, i] = fo
+                sg_off[b, kv, i] = go
+                fo += int(L[i]) * rp + r * 2 * D
+                go += 2 * r
+    return Plan(n_seg, n_full, seg_off, rank, fac_off, sg_off, fo, go)

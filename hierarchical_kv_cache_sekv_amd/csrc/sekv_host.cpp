@@ -1,0 +1,912 @@
+// Host runtime of libsekv: argument checks, span planning and building,
+// workspace layout and the launch sequence of one decode step.
+//
+// Pages (by title and section): gist.science German explainer of "SeKV:
+// Resolution-Adaptive KV Cache with Hierarchical Semantic Memory for
+// Long-Context LLM Inference", "Technisches Resümee" > "Methodik" parts 1-3,
+// and its Chinese counterpart "技术摘要" > "方法论" parts 1-3; the authors'
+// abstract (GPU summaries, CPU low-rank SVD basis, on-demand reconstruction).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <condition_variable>
+#include <cstdio>
+#include <cstdarg>
+#include <cstdlib>
+#include <cstring>
+#include <functional>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/sekv.h"
+#include "sekv_internal.h"
+
+using namespace sekv;
+
+namespace {
+
+thread_local std::string g_err;
+
+sekv_status fail(sekv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sekv_status fail(sekv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_OR_FAIL(call)                                                                  \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess) return fail(SEKV_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+// ---------------------------------------------------------------- thread pool
+class ThreadPool {
+ public:
+  explicit ThreadPool(int n) {
+    for (int i = 0; i < n; ++i) workers_.emplace_back([this] { loop(); });
+  }
+  ~ThreadPool() {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      stop_ = true;
+      ++gen_;
+    }
+    cv_.notify_all();
+    for (auto& t : workers_) t.join();
+  }
+  int size() const { return (int)workers_.size() + 1; }
+  // fn(i) for i in [0, n), spread over the workers and the calling thread.
+  void parallel_for(int64_t n, const std::function<void(int64_t)>& fn) {
+    if (n <= 0) return;
+    if (workers_.empty() || n == 1) {
+      for (int64_t i = 0; i < n; ++i) fn(i);
+      return;
+    }
+    std::unique_lock<std::mutex> lk(mu_);
+    job_ = &fn;
+    n_ = n;
+    next_.store(0);
+    active_ = (int)workers_.size();
+    ++gen_;
+    lk.unlock();
+    cv_.notify_all();
+    run();
+    lk.lock();
+    done_cv_.wait(lk, [this] { return active_ == 0; });
+    job_ = nullptr;
+  }
+
+ private:
+  void run() {
+    for (;;) {
+      const int64_t i = next_.fetch_add(1);
+      if (i >= n_) break;
+      (*job_)(i);
+    }
+  }
+  void loop() {
+    uint64_t seen = 0;
+    for (;;) {
+      std::unique_lock<std::mutex> lk(mu_);
+      cv_.wait(lk, [&] { return gen_ != seen; });
+      seen = gen_;
+      if (stop_) return;
+      lk.unlock();
+      run();
+      lk.lock();
+      if (--active_ == 0) done_cv_.notify_all();
+    }
+  }
+  std::vector<std::thread> workers_;
+  std::mutex mu_;
+  std::condition_variable cv_, done_cv_;
+  const std::function<void(int64_t)>* job_ = nullptr;
+  int64_t n_ = 0;
+  std::atomic<int64_t> next_{0};
+  int active_ = 0;
+  uint64_t gen_ = 0;
+  bool stop_ = false;
+};
+
+int default_threads() {
+  const char* env = std::getenv("SEKV_THREADS");
+  if (env && std::atoi(env) > 0) return std::atoi(env);
+  const unsigned hc = std::thread::hardware_concurrency();
+  return (int)std::max(1u, std::min(hc == 0 ? 8u : hc, 16u));
+}
+
+}  // namespace
+
+constexpr int kMaxCounters = 1 << 16;
+constexpr int kRing = 3;
+constexpr size_t kRingBytes = 8u << 20;
+
+struct EventPairs {
+  std::vector<hipEvent_t> ev;  // start, stop, start, stop, ...
+  size_t used = 0;             // events recorded since the last read
+};
+
+struct sekv_ctx {
+  int device = 0;
+  unsigned int* counters = nullptr;  // device, zeroed once, left zero by every route call
+  hipEvent_t ev_list = nullptr, ev_copy = nullptr;
+  hipEvent_t ev_ring[kRing] = {};
+  ThreadPool* pool = nullptr;
+  bool profile = false;
+  EventPairs prof_route, prof_attend;
+};
+
+namespace {
+hipError_t prof_mark(sekv_ctx* c, EventPairs& p, hipStream_t s) {
+  if (!c->profile) return hipSuccess;
+  if (p.used == p.ev.size()) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return err;
+    p.ev.push_back(e);
+  }
+  return hipEventRecord(p.ev[p.used++], s);
+}
+hipError_t prof_sum(EventPairs& p, double* ms, int64_t* n) {
+  double tot = 0;
+  for (size_t i = 0; i + 1 < p.used; i += 2) {
+    hipError_t err = hipEventSynchronize(p.ev[i + 1]);
+    if (err != hipSuccess) return err;
+    float t = 0;
+    err = hipEventElapsedTime(&t, p.ev[i], p.ev[i + 1]);
+    if (err != hipSuccess) return err;
+    tot += t;
+  }
+  *ms = tot;
+  *n = (int64_t)(p.used / 2);
+  p.used = 0;
+  return hipSuccess;
+}
+}  // namespace
+
+namespace {
+
+int elem_size(int dtype) { return dtype == SEKV_BF16 ? 2 : 4; }
+
+sekv_status check_config(const sekv_config* c) {
+  if (!c) return fail(SEKV_EINVAL, "config is NULL");
+  if (c->dtype != SEKV_F32 && c->dtype != SEKV_BF16) return fail(SEKV_EINVAL, "dtype %d is not SEKV_F32 or SEKV_BF16", c->dtype);
+  if (c->batch < 1 || c->batch > kMaxBatch) return fail(SEKV_ESHAPE, "batch %d outside [1, %d]", c->batch, kMaxBatch);
+  if (c->n_ctx < 1) return fail(SEKV_ESHAPE, "n_ctx %d < 1", c->n_ctx);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(SEKV_ESHAPE, "head_dim %d is not 64 or 128", c->head_dim);
+  if (c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads != 0)
+    return fail(SEKV_ESHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(SEKV_ESHAPE, "group size %d is not 1, 2, 4 or 8 (head mask is 8 bits)", G);
+  if ((int64_t)c->batch * c->n_kv_heads > kMaxGroups)
+    return fail(SEKV_ESHAPE, "batch * n_kv_heads = %d exceeds %d", c->batch * c->n_kv_heads, kMaxGroups);
+  if (c->n_sink < 0 || c->n_recent < 0) return fail(SEKV_EINVAL, "n_sink/n_recent must be >= 0");
+  if (c->n_sink + c->n_recent < 1) return fail(SEKV_EINVAL, "n_sink + n_recent must be >= 1 (full-resolution set never empty)");
+  if ((int64_t)c->n_sink + c->n_recent > c->n_ctx) return fail(SEKV_ESHAPE, "n_sink + n_recent = %d exceeds n_ctx %d", c->n_sink + c->n_recent, c->n_ctx);
+  if (c->min_span < 1) return fail(SEKV_EINVAL, "min_span %d < 1", c->min_span);
+  if (c->min_span > c->max_span) return fail(SEKV_EINVAL, "min_span %d > max_span %d", c->min_span, c->max_span);
+  if (c->max_span > kMaxSpan) return fail(SEKV_ESHAPE, "max_span %d exceeds %d", c->max_span, kMaxSpan);
+  if (c->factors_on_host != 0 && c->factors_on_host != 1) return fail(SEKV_EINVAL, "factors_on_host must be 0 or 1");
+  return SEKV_OK;
+}
+
+int32_t seg_cap_of(const sekv_config* c) {
+  return std::max(0, (c->n_ctx - c->n_sink - c->n_recent) / (c->min_span + 1)) + 1;
+}
+int32_t full_cap_of(const sekv_config* c) {
+  return std::min<int64_t>(c->n_ctx, (int64_t)c->n_sink + seg_cap_of(c) + c->n_recent + 1);
+}
+
+bool is_pinned_host(const void* p) {
+  hipPointerAttribute_t attr;
+  const hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeHost;
+}
+
+sekv_status check_spans(const sekv_config* c, const sekv_spans* s, bool need_factors) {
+  if (!s) return fail(SEKV_EINVAL, "spans is NULL");
+  if (s->seg_cap != seg_cap_of(c) || s->full_cap != full_cap_of(c))
+    return fail(SEKV_ESHAPE, "spans capacities (%d, %d) differ from the configuration's (%d, %d)", s->seg_cap,
+                s->full_cap, seg_cap_of(c), full_cap_of(c));
+  if (!s->n_seg_host || !s->n_full_host) return fail(SEKV_EINVAL, "n_seg_host / n_full_host is NULL");
+  if (!s->seg_off || !s->rank || !s->full_k || !s->full_v || !s->sum_k || !s->sum_v || !s->rho)
+    return fail(SEKV_EINVAL, "a span-cache device array is NULL");
+  for (int b = 0; b < c->batch; ++b) {
+    if (s->n_seg_host[b] < 0 || s->n_seg_host[b] > s->seg_cap)
+      return fail(SEKV_ESHAPE, "n_seg[%d] = %d outside [0, seg_cap=%d]", b, s->n_seg_host[b], s->seg_cap);
+    if (s->n_full_host[b] < 1 || s->n_full_host[b] > s->full_cap)
+      return fail(SEKV_ESHAPE, "n_full[%d] = %d outside [1, full_cap=%d]", b, s->n_full_host[b], s->full_cap);
+  }
+  if (need_factors) {
+    if (!s->fac_off || !s->sg_off || !s->fac || !s->sg) return fail(SEKV_EINVAL, "factor offsets or pools are NULL");
+    if (c->factors_on_host) {
+      if (!s->seg_off_host || !s->rank_host || !s->fac_off_host || !s->sg_off_host)
+        return fail(SEKV_EINVAL, "host-resident factors need the *_host plan arrays");
+      if (!is_pinned_host(s->fac) || !is_pinned_host(s->sg))
+        return fail(SEKV_EINVAL, "factors_on_host = 1 needs pinned host pools (hipHostMalloc), got pageable or device memory");
+    }
+  }
+  return SEKV_OK;
+}
+
+size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+uint16_t to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float from_bf16(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Store an fp64 value in the cache element type: fp64 -> f32 (nearest even) -> bf16 (nearest even).
+void store(void* base, int dtype, int64_t i, double x) {
+  const float f = (float)x;
+  if (dtype == SEKV_BF16) static_cast<uint16_t*>(base)[i] = to_bf16(f);
+  else static_cast<float*>(base)[i] = f;
+}
+double fetch(const void* base, int dtype, int64_t i) {
+  return dtype == SEKV_BF16 ? (double)from_bf16(static_cast<const uint16_t*>(base)[i])
+                            : (double)static_cast<const float*>(base)[i];
+}
+
+// Greedy segmentation of one sequence (see sekv_plan_spans in sekv.h).
+int segment_one(const float* s, float thr, const sekv_config* c, int32_t* seg_off, int32_t cap) {
+  const int a = c->n_sink, e = c->n_ctx - c->n_recent, lo = c->min_span, hi = c->max_span;
+  int n = 0;
+  if (e - a < 2) {
+    seg_off[0] = a;
+    return 0;
+  }
+  seg_off[n++] = a;
+  int h = a;
+  for (int t = a + 1; t < e; ++t) {
+    const int body = t - h - 1;
+    const bool forced = body == hi;
+    const bool data = s[t] > thr && body >= lo && (e - t - 1) >= lo;
+    if (forced || data) {
+      seg_off[n++] = t;
+      h = t;
+    }
+  }
+  int tail = e;
+  if (h == e - 1) {
+    --n;
+    tail = h;
+  }
+  (void)cap;
+  seg_off[n] = tail;
+  return n;
+}
+
+// One-sided Jacobi SVD of an L x n matrix M given by its rows (row-major,
+// overwritten).  On return sig[i] (descending), u[t*L + i] = U[t][i] and the
+// rows of M hold the right singular vectors' directions scaled by sig (order
+// given by perm: output component i is input row perm[i]).
+void jacobi_svd(int L, int n, double* M, double* Vc, double* sig, int* perm) {
+  for (int i = 0; i < L * L; ++i) Vc[i] = 0.0;
+  for (int i = 0; i < L; ++i) Vc[i * L + i] = 1.0;
+  const double eps = 1e-15;
+  for (int sweep = 0; sweep < 60; ++sweep) {
+    bool rotated = false;
+    for (int p = 0; p < L - 1; ++p) {
+      double* ap = M + (size_t)p * n;
+      for (int q = p + 1; q < L; ++q) {
+        double* aq = M + (size_t)q * n;
+        double al = 0, be = 0, ga = 0;
+        for (int k = 0; k < n; ++k) {
+          al += ap[k] * ap[k];
+          be += aq[k] * aq[k];
+          ga += ap[k] * aq[k];
+        }
+        if (ga == 0.0 || std::fabs(ga) <= eps * std::sqrt(al * be)) continue;
+        rotated = true;
+        const double zeta = (be - al) / (2.0 * ga);
+        const double t = (zeta >= 0 ? 1.0 : -1.0) / (std::fabs(zeta) + std::sqrt(1.0 + zeta * zeta));
+        const double cs = 1.0 / std::sqrt(1.0 + t * t), sn = cs * t;
+        for (int k = 0; k < n; ++k) {
+          const double x = ap[k], y = aq[k];
+          ap[k] = cs * x - sn * y;
+          aq[k] = sn * x + cs * y;
+        }
+        double* vp = Vc + (size_t)p * L;
+        double* vq = Vc + (size_t)q * L;
+        for (int k = 0; k < L; ++k) {
+          const double x = vp[k], y = vq[k];
+          vp[k] = cs * x - sn * y;
+          vq[k] = sn * x + cs * y;
+        }
+      }
+    }
+    if (!rotated) break;
+  }
+  std::vector<double> nrm(L);
+  for (int i = 0; i < L; ++i) {
+    double acc = 0;
+    const double* ai = M + (size_t)i * n;
+    for (int k = 0; k < n; ++k) acc += ai[k] * ai[k];
+    nrm[i] = std::sqrt(acc);
+    perm[i] = i;
+  }
+  std::stable_sort(perm, perm + L, [&](int x, int y) { return nrm[x] > nrm[y]; });
+  for (int i = 0; i < L; ++i) sig[i] = nrm[perm[i]];
+}
+
+}  // namespace
+
+// =================================================================== ABI
+extern "C" {
+
+const char* sekv_last_error(void) { return g_err.c_str(); }
+
+sekv_status sekv_ctx_create(int device, sekv_ctx** out) {
+  if (!out) return fail(SEKV_EINVAL, "out is NULL");
+  *out = nullptr;
+  int n = 0;
+  HIP_OR_FAIL(hipGetDeviceCount(&n));
+  if (device < 0 || device >= n) return fail(SEKV_EHIP, "device %d outside [0, %d)", device, n);
+  HIP_OR_FAIL(hipSetDevice(device));
+  sekv_ctx* c = new (std::nothrow) sekv_ctx();
+  if (!c) return fail(SEKV_ENOMEM, "cannot allocate the context");
+  c->device = device;
+  hipError_t e = hipMalloc(&c->counters, sizeof(unsigned int) * kMaxCounters);
+  if (e == hipSuccess) e = hipMemset(c->counters, 0, sizeof(unsigned int) * kMaxCounters);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_list, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming);
+  for (int i = 0; i < kRing && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->ev_ring[i], hipEventDisableTiming);
+  if (e != hipSuccess) {
+    sekv_ctx_destroy(c);
+    return fail(SEKV_EHIP, "context setup failed: %s", hipGetErrorString(e));
+  }
+  c->pool = new ThreadPool(default_threads() - 1);
+  *out = c;
+  return SEKV_OK;
+}
+
+void sekv_ctx_destroy(sekv_ctx* c) {
+  if (!c) return;
+  for (hipEvent_t e : c->prof_route.ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->prof_attend.ev) (void)hipEventDestroy(e);
+  if (c->counters) (void)hipFree(c->counters);
+  if (c->ev_list) (void)hipEventDestroy(c->ev_list);
+  if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
+  for (int i = 0; i < kRing; ++i)
+    if (c->ev_ring[i]) (void)hipEventDestroy(c->ev_ring[i]);
+  delete c->pool;
+  delete c;
+}
+
+sekv_status sekv_capacities(const sekv_config* cfg, int32_t* seg_cap, int32_t* full_cap) {
+  sekv_status st = check_config(cfg);
+  if (st != SEKV_OK) return st;
+  if (!seg_cap || !full_cap) return fail(SEKV_EINVAL, "seg_cap/full_cap output is NULL");
+  *seg_cap = seg_cap_of(cfg);
+  *full_cap = full_cap_of(cfg);
+  return SEKV_OK;
+}
+
+sekv_status sekv_plan_spans(const sekv_config* c, const float* surprisal, const float* thr, const int32_t* rank_req,
+                            int32_t* n_seg, int32_t* n_full, int32_t* seg_off, int32_t* rank, int64_t* fac_off,
+                            int64_t* sg_off, int64_t* fac_elems, int64_t* sg_elems) {
+  sekv_status st = check_config(c);
+  if (st != SEKV_OK) return st;
+  if (!surprisal || !thr || !rank_req || !n_seg || !n_full || !seg_off || !rank || !fac_off || !sg_off || !fac_elems ||
+      !sg_elems)
+    return fail(SEKV_EINVAL, "sekv_plan_spans: a pointer argument is NULL");
+  const int B = c->batch, T = c->n_ctx, Hkv = c->n_kv_heads, D = c->head_dim;
+  const int32_t cap = seg_cap_of(c);
+  for (int b = 0; b < B; ++b) {
+    if (!std::isfinite(thr[b])) return fail(SEKV_EINVAL, "boundary_thr[%d] is not finite", b);
+    for (int t = 0; t < T; ++t)
+      if (!std::isfinite(surprisal[(size_t)b * T + t])) return fail(SEKV_EINVAL, "surprisal[%d][%d] is not finite", b, t);
+  }
+  std::vector<int32_t> so((size_t)B * (cap + 1));
+  std::vector<int32_t> ns(B), nf(B);
+  for (int b = 0; b < B; ++b) {
+    int32_t* sob = so.data() + (size_t)b * (cap + 1);
+    const int n = segment_one(surprisal + (size_t)b * T, thr[b], c, sob, cap);
+    for (int i = n + 1; i <= cap; ++i) sob[i] = sob[n];
+    ns[b] = n;
+    nf[b] = c->n_sink + n + (T - sob[n]);
+    for (int i = 0; i < n; ++i)
+      if (rank_req[(size_t)b * cap + i] < 1) return fail(SEKV_EINVAL, "rank_req[%d][%d] = %d < 1", b, i, rank_req[(size_t)b * cap + i]);
+  }
+  int64_t fo = 0, go = 0;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* sob = so.data() + (size_t)b * (cap + 1);
+    for (int i = 0; i < cap; ++i) {
+      int32_t r = 0;
+      if (i < ns[b]) {
+        const int L = sob[i + 1] - sob[i] - 1;
+        r = std::min(std::min(rank_req[(size_t)b * cap + i], L), 2 * D);
+      }
+      rank[(size_t)b * cap + i] = r;
+    }
+    for (int kv = 0; kv < Hkv; ++kv) {
+      for (int i = 0; i < cap; ++i) {
+        const size_t o = ((size_t)b * Hkv + kv) * cap + i;
+        if (i < ns[b]) {
+          const int L = sob[i + 1] - sob[i] - 1;
+          const int r = rank[(size_t)b * cap + i];
+          const int rp = (r + 7) & ~7;
+          fac_off[o] = fo;
+          sg_off[o] = go;
+          fo += (int64_t)L * rp + (int64_t)r * 2 * D;
+          go += 2 * r;
+        } else {
+          fac_off[o] = 0;
+          sg_off[o] = 0;
+        }
+      }
+    }
+  }
+  std::memcpy(seg_off, so.data(), so.size() * sizeof(int32_t));
+  std::memcpy(n_seg, ns.data(), B * sizeof(int32_t));
+  std::memcpy(n_full, nf.data(), B * sizeof(int32_t));
+  *fac_elems = fo;
+  *sg_elems = go;
+  return SEKV_OK;
+}
+
+sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k, const void* v, const float* surprisal,
+                             const float* route_proj, const float* gate, int32_t gate_stride, const sekv_spans* s,
+                             hipStream_t stream) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  sekv_status st = check_config(c);
+  if (st != SEKV_OK) return st;
+  if (!k || !v || !surprisal || !route_proj || !gate) return fail(SEKV_EINVAL, "sekv_build_spans: an input is NULL");
+  st = check_spans(c, s, true);
+  if (st != SEKV_OK) return st;
+  if (!s->seg_off_host || !s->rank_host || !s->fac_off_host || !s->sg_off_host)
+    return fail(SEKV_EINVAL, "sekv_build_spans needs the plan's host arrays in spans");
+  const int B = c->batch, T = c->n_ctx, Hkv = c->n_kv_heads, D = c->head_dim, dt = c->dtype;
+  const int es = elem_size(dt);
+  const int32_t cap = s->seg_cap, fcap = s->full_cap;
+  // pool sizes implied by the plan
+  int64_t need_f = 0, need_g = 0;
+  for (int b = 0; b < B; ++b)
+    for (int kv = 0; kv < Hkv; ++kv)
+      for (int i = 0; i < s->n_seg_host[b]; ++i) {
+        const size_t o = ((size_t)b * Hkv + kv) * cap + i;
+        const int L = s->seg_off_host[(size_t)b * (cap + 1) + i + 1] - s->seg_off_host[(size_t)b * (cap + 1) + i] - 1;
+        const int r = s->rank_host[(size_t)b * cap + i];
+        if (r < 1 || r > std::min(L, 2 * D)) return fail(SEKV_EINVAL, "rank[%d][%d] = %d outside [1, min(L=%d, 2d)]", b, i, r, L);
+        if (r > gate_stride) return fail(SEKV_ESHAPE, "gate_stride %d < rank %d", gate_stride, r);
+        const int rp = (r + 7) & ~7;
+        need_f = std::max<int64_t>(need_f, s->fac_off_host[o] + (int64_t)L * rp + (int64_t)r * 2 * D);
+        need_g = std::max<int64_t>(need_g, s->sg_off_host[o] + 2 * r);
+      }
+  if (need_f > s->fac_elems || need_g > s->sg_elems)
+    return fail(SEKV_ECAPACITY, "factor pools hold (%lld, %lld) elements, plan needs (%lld, %lld)", (long long)s->fac_elems,
+                (long long)s->sg_elems, (long long)need_f, (long long)need_g);
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+
+  const size_t kv_elems = (size_t)B * Hkv * T * D;
+  std::vector<char> hk(kv_elems * es), hv(kv_elems * es);
+  HIP_OR_FAIL(hipMemcpyAsync(hk.data(), k, hk.size(), hipMemcpyDeviceToHost, stream));
+  HIP_OR_FAIL(hipMemcpyAsync(hv.data(), v, hv.size(), hipMemcpyDeviceToHost, stream));
+  HIP_OR_FAIL(hipStreamSynchronize(stream));
+
+  std::vector<char> full_k((size_t)B * Hkv * fcap * D * es, 0), full_v(full_k.size(), 0);
+  std::vector<char> sum_k((size_t)B * Hkv * cap * D * es, 0), sum_v(sum_k.size(), 0), rho(sum_k.size(), 0);
+  const bool on_host = c->factors_on_host != 0;
+  std::vector<char> fac_tmp;
+  std::vector<float> sg_tmp;
+  char* fac_dst;
+  float* sg_dst;
+  if (on_host) {
+    fac_dst = static_cast<char*>(const_cast<void*>(s->fac));
+    sg_dst = const_cast<float*>(s->sg);
+  } else {
+    fac_tmp.assign((size_t)need_f * es, 0);
+    sg_tmp.assign((size_t)need_g, 0.0f);
+    fac_dst = fac_tmp.data();
+    sg_dst = sg_tmp.data();
+  }
+
+  // work items: (b, kv, block of spans)
+  constexpr int kSpansPerItem = 64;
+  struct Item { int b, kv, i0, i1; };
+  std::vector<Item> items;
+  for (int b = 0; b < B; ++b)
+    for (int kv = 0; kv < Hkv; ++kv) {
+      for (int i0 = 0; i0 < s->n_seg_host[b]; i0 += kSpansPerItem)
+        items.push_back({b, kv, i0, std::min(s->n_seg_host[b], i0 + kSpansPerItem)});
+      if (s->n_seg_host[b] == 0) items.push_back({b, kv, 0, 0});
+    }
+
+  ctx->pool->parallel_for((int64_t)items.size(), [&](int64_t it) {
+    const Item w = items[it];
+    const int b = w.b, kv = w.kv;
+    const int32_t* so = s->seg_off_host + (size_t)b * (cap + 1);
+    const size_t g = (size_t)b * Hkv + kv;
+    const char* kb = hk.data() + g * T * D * es;
+    const char* vb = hv.data() + g * T * D * es;
+    const float* sb = surprisal + (size_t)b * T;
+    const float* P = route_proj + (size_t)kv * D * D;
+    // full-resolution rows (once per (b, kv)): sink, anchors, tail
+    if (w.i0 == 0) {
+      int row = 0;
+      const int ns = s->n_seg_host[b];
+      auto copy_row = [&](int t) {
+        std::memcpy(full_k.data() + (g * fcap + row) * D * es, kb + (size_t)t * D * es, (size_t)D * es);
+        std::memcpy(full_v.data() + (g * fcap + row) * D * es, vb + (size_t)t * D * es, (size_t)D * es);
+        ++row;
+      };
+      for (int t = 0; t < c->n_sink; ++t) copy_row(t);
+      for (int i = 0; i < ns; ++i) copy_row(so[i]);
+      for (int t = so[ns]; t < T; ++t) copy_row(t);
+    }
+    std::vector<double> M, Vc, sig, kbar(D), vbar(D), r(D), rh(D);
+    std::vector<int> perm;
+    for (int i = w.i0; i < w.i1; ++i) {
+      const int t0 = so[i] + 1, t1 = so[i + 1], L = t1 - t0;
+      // surprisal-weighted summaries
+      double tot = 0;
+      for (int t = t0; t < t1; ++t) tot += (double)sb[t];
+      std::fill(kbar.begin(), kbar.end(), 0.0);
+      std::fill(vbar.begin(), vbar.end(), 0.0);
+      for (int t = t0; t < t1; ++t) {
+        const double wt = tot > 0 ? (double)sb[t] / tot : 1.0 / L;
+        for (int j = 0; j < D; ++j) {
+          kbar[j] += wt * fetch(kb, dt, (int64_t)t * D + j);
+          vbar[j] += wt * fetch(vb, dt, (int64_t)t * D + j);
+        }
+      }
+      // routing key rho = P^T (P kbar / |P kbar|)
+      double nn = 0;
+      for (int a = 0; a < D; ++a) {
+        double acc = 0;
+        for (int j = 0; j < D; ++j) acc += (double)P[(size_t)a * D + j] * kbar[j];
+        r[a] = acc;
+        nn += acc * acc;
+      }
+      nn = std::sqrt(nn);
+      for (int a = 0; a < D; ++a) rh[a] = nn > 0 ? r[a] / nn : 0.0;
+      const size_t srow = (g * cap + i) * D;
+      for (int j = 0; j < D; ++j) {
+        double acc = 0;
+        for (int a = 0; a < D; ++a) acc += (double)P[(size_t)a * D + j] * rh[a];
+        store(rho.data(), dt, (int64_t)srow + j, acc);
+        store(sum_k.data(), dt, (int64_t)srow + j, kbar[j]);
+        store(sum_v.data(), dt, (int64_t)srow + j, vbar[j]);
+      }
+      // rank-r factors of [K_body | V_body]
+      const int n2 = 2 * D;
+      M.assign((size_t)L * n2, 0.0);
+      for (int t = 0; t < L; ++t)
+        for (int j = 0; j < D; ++j) {
+          M[(size_t)t * n2 + j] = fetch(kb, dt, (int64_t)(t0 + t) * D + j);
+          M[(size_t)t * n2 + D + j] = fetch(vb, dt, (int64_t)(t0 + t) * D + j);
+        }
+      Vc.resize((size_t)L * L);
+      sig.resize(L);
+      perm.resize(L);
+      jacobi_svd(L, n2, M.data(), Vc.data(), sig.data(), perm.data());
+      const int rk = s->rank_host[(size_t)b * cap + i];
+      const int rp = (rk + 7) & ~7;
+      const size_t o = g * cap + i;
+      const int64_t fbase = s->fac_off_host[o];
+      const int64_t gbase = s->sg_off_host[o];
+      const float* gt = gate + (g * cap + i) * (size_t)gate_stride;
+      for (int j = 0; j < rk; ++j) {
+        const int src = perm[j];
+        const double* u = Vc.data() + (size_t)src * L;  // column src of U
+        int imax = 0;
+        for (int t = 1; t < L; ++t)
+          if (std::fabs(u[t]) > std::fabs(u[imax])) imax = t;
+        const double sgn = u[imax] < 0 ? -1.0 : 1.0;
+        for (int t = 0; t < L; ++t) store(fac_dst, dt, fbase + (int64_t)t * rp + j, sgn * u[t]);
+        const double sj = sig[j];
+        const double inv = sj > 0 ? sgn / sj : 0.0;
+        const double* wrow = M.data() + (size_t)src * n2;
+        for (int col = 0; col < n2; ++col)
+          store(fac_dst, dt, fbase + (int64_t)L * rp + (int64_t)j * n2 + col, wrow[col] * inv);
+        sg_dst[gbase + j] = (float)sj;
+        sg_dst[gbase + rk + j] = gt[j];
+      }
+      for (int t = 0; t < L; ++t)
+        for (int j = rk; j < rp; ++j) store(fac_dst, dt, fbase + (int64_t)t * rp + j, 0.0);
+    }
+  });
+
+  auto up = [&](const void* dst, const void* src, size_t bytes) -> hipError_t {
+    return hipMemcpyAsync(const_cast<void*>(dst), src, bytes, hipMemcpyHostToDevice, stream);
+  };
+  HIP_OR_FAIL(up(s->seg_off, s->seg_off_host, (size_t)B * (cap + 1) * sizeof(int32_t)));
+  HIP_OR_FAIL(up(s->rank, s->rank_host, (size_t)B * cap * sizeof(int32_t)));
+  HIP_OR_FAIL(up(s->fac_off, s->fac_off_host, (size_t)B * Hkv * cap * sizeof(int64_t)));
+  HIP_OR_FAIL(up(s->sg_off, s->sg_off_host, (size_t)B * Hkv * cap * sizeof(int64_t)));
+  HIP_OR_FAIL(up(s->full_k, full_k.data(), full_k.size()));
+  HIP_OR_FAIL(up(s->full_v, full_v.data(), full_v.size()));
+  HIP_OR_FAIL(up(s->sum_k, sum_k.data(), sum_k.size()));
+  HIP_OR_FAIL(up(s->sum_v, sum_v.data(), sum_v.size()));
+  HIP_OR_FAIL(up(s->rho, rho.data(), rho.size()));
+  if (!on_host) {
+    HIP_OR_FAIL(up(s->fac, fac_tmp.data(), fac_tmp.size()));
+    HIP_OR_FAIL(up(s->sg, sg_tmp.data(), sg_tmp.size() * sizeof(float)));
+  }
+  HIP_OR_FAIL(hipStreamSynchronize(stream));
+  return SEKV_OK;
+}
+
+size_t sekv_route_workspace_bytes(const sekv_config* c, const sekv_spans* s) {
+  if (check_config(c) != SEKV_OK || !s) return 0;
+  return align_up((size_t)c->batch * c->n_kv_heads * s->seg_cap);
+}
+
+sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q, const float* theta,
+                       int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  sekv_status st = check_config(c);
+  if (st != SEKV_OK) return st;
+  st = check_spans(c, s, false);
+  if (st != SEKV_OK) return st;
+  if (!q || !theta || !exp_list || !exp_mask || !exp_count || !ws) return fail(SEKV_EINVAL, "sekv_route: a pointer argument is NULL");
+  if (ws_bytes < sekv_route_workspace_bytes(c, s))
+    return fail(SEKV_ECAPACITY, "route workspace %zu bytes < %zu needed", ws_bytes, sekv_route_workspace_bytes(c, s));
+  if ((int64_t)c->batch * c->n_kv_heads > kMaxCounters) return fail(SEKV_ESHAPE, "too many (b, kv) groups");
+  RouteArgs a{};
+  a.dtype = c->dtype;
+  a.B = c->batch; a.Hq = c->n_q_heads; a.Hkv = c->n_kv_heads; a.D = c->head_dim; a.seg_cap = s->seg_cap;
+  int mx = 0;
+  for (int b = 0; b < c->batch; ++b) { a.n_seg[b] = s->n_seg_host[b]; mx = std::max(mx, s->n_seg_host[b]); }
+  a.nblk = std::max(1, (mx + kRouteThreads - 1) / kRouteThreads);
+  a.q = q; a.theta = theta; a.rho = s->rho;
+  a.dmask = static_cast<uint8_t*>(ws);
+  a.counters = ctx->counters;
+  a.exp_list = exp_list; a.exp_mask = exp_mask; a.exp_count = exp_count;
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_route, stream));
+  HIP_OR_FAIL(launch_route(a, stream));
+  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_route, stream));
+  return SEKV_OK;
+}
+
+sekv_status sekv_reconstruct(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const int32_t* exp_list,
+                             const int32_t* exp_count, int32_t* tok_off, float* k_out, float* v_out, hipStream_t stream) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  sekv_status st = check_config(c);
+  if (st != SEKV_OK) return st;
+  st = check_spans(c, s, true);
+  if (st != SEKV_OK) return st;
+  if (!exp_list || !exp_count || !tok_off || !k_out || !v_out) return fail(SEKV_EINVAL, "sekv_reconstruct: a pointer argument is NULL");
+  ReconArgs a{};
+  a.dtype = c->dtype; a.B = c->batch; a.Hkv = c->n_kv_heads; a.D = c->head_dim; a.seg_cap = s->seg_cap; a.T = c->n_ctx;
+  a.seg_off = s->seg_off; a.rank = s->rank; a.fac_off = s->fac_off; a.sg_off = s->sg_off; a.fac = s->fac; a.sg = s->sg;
+  a.exp_list = exp_list; a.exp_count = exp_count; a.tok_off = tok_off; a.k_out = k_out; a.v_out = v_out;
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+  HIP_OR_FAIL(launch_reconstruct(a, stream));
+  return SEKV_OK;
+}
+
+namespace {
+
+struct DecodePlan {
+  AttendArgs a{};
+  size_t off_ml = 0, off_o = 0, off_stage_off = 0, off_stage_fac = 0, off_stage_sg = 0, dev_bytes = 0;
+  size_t h_list = 0, h_count = 0, h_stage_off = 0, h_sg = 0, h_ring = 0, host_bytes = 0;
+};
+
+void make_plan(const sekv_config* c, const sekv_spans* s, DecodePlan& p) {
+  const int B = c->batch, Hkv = c->n_kv_heads, D = c->head_dim, G = c->n_q_heads / Hkv;
+  const int BG = B * Hkv;
+  AttendArgs& a = p.a;
+  a.dtype = c->dtype; a.B = B; a.Hq = c->n_q_heads; a.Hkv = Hkv; a.D = D;
+  a.seg_cap = s->seg_cap; a.full_cap = s->full_cap;
+  int ntot = 1;
+  for (int b = 0; b < B; ++b) {
+    a.n_full[b] = s->n_full_host[b];
+    a.n_seg[b] = s->n_seg_host[b];
+    ntot = std::max(ntot, a.n_full[b] + a.n_seg[b]);
+  }
+  // about four role-A workgroups per compute unit, 64-row granularity
+  const int64_t target = 1024;
+  int64_t ch = ((int64_t)BG * ntot + target - 1) / target;
+  ch = (ch + 63) / 64 * 64;
+  ch = std::max<int64_t>(128, std::min<int64_t>(2048, ch));
+  if (const char* env = std::getenv("SEKV_A4_CHUNK")) {  // split-size override (invariance tests)
+    const int64_t v = std::atoll(env);
+    if (v > 0) ch = std::max<int64_t>(64, std::min<int64_t>(2048, (v + 63) / 64 * 64));
+  }
+  a.chunk_a4 = (int)ch;
+  a.nch_a4 = (ntot + a.chunk_a4 - 1) / a.chunk_a4;
+  a.P_max = a.nch_a4 + (s->seg_cap + kExpChunk - 1) / kExpChunk;
+  const int64_t max_items = (int64_t)BG * ((s->seg_cap + kExpChunk - 1) / kExpChunk);
+  a.n_a5_wg = (int)std::max<int64_t>(1, std::min<int64_t>(512, (max_items + 3) / 4));
+  a.n_a4_wg = BG * a.nch_a4;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)D));
+  size_t off = 0;
+  p.off_ml = off; off = align_up(off + (size_t)BG * a.P_max * G * 2 * sizeof(float));
+  p.off_o = off; off = align_up(off + (size_t)BG * a.P_max * G * D * sizeof(float));
+  if (c->factors_on_host) {
+    p.off_stage_off = off; off = align_up(off + (size_t)BG * s->seg_cap * 2 * sizeof(int64_t));
+    p.off_stage_fac = off; off = align_up(off + (size_t)s->fac_elems * elem_size(c->dtype));
+    p.off_stage_sg = off; off = align_up(off + (size_t)s->sg_elems * sizeof(float));
+  }
+  p.dev_bytes = off;
+  size_t h = 0;
+  if (c->factors_on_host) {
+    p.h_count = h; h = align_up(h + (size_t)BG * sizeof(int32_t));
+    p.h_list = h; h = align_up(h + (size_t)BG * s->seg_cap * sizeof(int32_t));
+    p.h_stage_off = h; h = align_up(h + (size_t)BG * s->seg_cap * 2 * sizeof(int64_t));
+    p.h_sg = h; h = align_up(h + (size_t)s->sg_elems * sizeof(float));
+    p.h_ring = h; h = align_up(h + (size_t)kRing * kRingBytes);
+  }
+  p.host_bytes = h;
+}
+
+}  // namespace
+
+size_t sekv_decode_workspace_bytes(const sekv_config* c, const sekv_spans* s) {
+  if (check_config(c) != SEKV_OK || !s) return 0;
+  DecodePlan p;
+  make_plan(c, s, p);
+  return p.dev_bytes;
+}
+
+size_t sekv_decode_host_workspace_bytes(const sekv_config* c, const sekv_spans* s) {
+  if (check_config(c) != SEKV_OK || !s) return 0;
+  DecodePlan p;
+  make_plan(c, s, p);
+  return p.host_bytes;
+}
+
+sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q,
+                                        const int32_t* exp_list, const uint8_t* exp_mask, const int32_t* exp_count,
+                                        float* out, void* dev_ws, size_t dev_ws_bytes, void* host_ws,
+                                        size_t host_ws_bytes, hipStream_t stream, hipStream_t copy_stream) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  sekv_status st = check_config(c);
+  if (st != SEKV_OK) return st;
+  st = check_spans(c, s, true);
+  if (st != SEKV_OK) return st;
+  if (!q || !exp_list || !exp_mask || !exp_count || !out || !dev_ws)
+    return fail(SEKV_EINVAL, "sekv_mixed_attention_decode: a pointer argument is NULL");
+  DecodePlan p;
+  make_plan(c, s, p);
+  if (dev_ws_bytes < p.dev_bytes) return fail(SEKV_ECAPACITY, "device workspace %zu bytes < %zu needed", dev_ws_bytes, p.dev_bytes);
+  if (p.a.chunk_a4 > 2048) return fail(SEKV_ESHAPE, "internal chunk size too large");
+  if (c->factors_on_host) {
+    if (!host_ws) return fail(SEKV_EINVAL, "host-resident factors need a pinned host workspace");
+    if (host_ws_bytes < p.host_bytes) return fail(SEKV_ECAPACITY, "host workspace %zu bytes < %zu needed", host_ws_bytes, p.host_bytes);
+    if (!is_pinned_host(host_ws)) return fail(SEKV_EINVAL, "host workspace must be pinned (hipHostMalloc)");
+  }
+  if (!copy_stream) copy_stream = stream;
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+  AttendArgs a = p.a;
+  char* dws = static_cast<char*>(dev_ws);
+  a.q = q; a.full_k = s->full_k; a.full_v = s->full_v; a.sum_k = s->sum_k; a.sum_v = s->sum_v;
+  a.seg_off = s->seg_off; a.rank = s->rank; a.fac_off = s->fac_off; a.sg_off = s->sg_off; a.fac = s->fac; a.sg = s->sg;
+  a.exp_list = exp_list; a.exp_mask = exp_mask; a.exp_count = exp_count;
+  a.part_ml = reinterpret_cast<float*>(dws + p.off_ml);
+  a.part_o = reinterpret_cast<float*>(dws + p.off_o);
+  a.out = out;
+  a.stage_off = nullptr;
+
+  if (!c->factors_on_host) {
+    HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+    HIP_OR_FAIL(launch_attend(a, stream));
+    HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+    HIP_OR_FAIL(launch_combine(a, stream));
+    return SEKV_OK;
+  }
+
+  // ---- host-resident factors
+  const int B = c->batch, Hkv = c->n_kv_heads, D = c->head_dim, BG = B * Hkv;
+  const int es = elem_size(c->dtype);
+  const int32_t cap = s->seg_cap;
+  char* hws = static_cast<char*>(host_ws);
+  int32_t* h_count = reinterpret_cast<int32_t*>(hws + p.h_count);
+  int32_t* h_list = reinterpret_cast<int32_t*>(hws + p.h_list);
+  int64_t* h_soff = reinterpret_cast<int64_t*>(hws + p.h_stage_off);
+  float* h_sg = reinterpret_cast<float*>(hws + p.h_sg);
+  char* h_ring = hws + p.h_ring;
+  // previous call's copies must be done before the pinned buffers are reused
+  HIP_OR_FAIL(hipEventSynchronize(ctx->ev_copy));
+  HIP_OR_FAIL(hipMemcpyAsync(h_count, exp_count, BG * sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  HIP_OR_FAIL(hipMemcpyAsync(h_list, exp_list, (size_t)BG * cap * sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  HIP_OR_FAIL(hipEventRecord(ctx->ev_list, stream));
+  // full-resolution + summary pass runs while the host gathers
+  AttendArgs a4 = a;
+  a4.n_a5_wg = 0;
+  HIP_OR_FAIL(launch_attend(a4, stream));
+  HIP_OR_FAIL(hipEventSynchronize(ctx->ev_list));
+
+  // staging layout in list order
+  struct Ent { const char* src; int64_t bytes; int64_t dst; };
+  std::vector<Ent> ents;
+  int64_t fo = 0, go = 0;
+  for (int g = 0; g < BG; ++g) {
+    const int b = g / Hkv;
+    const int cnt = h_count[g];
+    if (cnt < 0 || cnt > s->n_seg_host[b]) return fail(SEKV_EHIP, "route count %d for group %d is out of range", cnt, g);
+    const int32_t* so = s->seg_off_host + (size_t)b * (cap + 1);
+    for (int j = 0; j < cnt; ++j) {
+      const int S = h_list[(size_t)g * cap + j];
+      if (S < 0 || S >= s->n_seg_host[b]) return fail(SEKV_EHIP, "route list entry %d out of range", S);
+      const int L = so[S + 1] - so[S] - 1;
+      const int r = s->rank_host[(size_t)b * cap + S];
+      const int rp = (r + 7) & ~7;
+      const int64_t fe = (int64_t)L * rp + (int64_t)r * 2 * D;
+      const size_t o = (size_t)g * cap + S;
+      ents.push_back({static_cast<const char*>(s->fac) + s->fac_off_host[o] * es, fe * es, fo});
+      h_soff[((size_t)g * cap + j) * 2] = fo;
+      h_soff[((size_t)g * cap + j) * 2 + 1] = go;
+      std::memcpy(h_sg + go, s->sg + s->sg_off_host[o], 2 * r * sizeof(float));
+      fo += fe;
+      go += 2 * r;
+    }
+  }
+  char* d_stage_fac = dws + p.off_stage_fac;
+  HIP_OR_FAIL(hipMemcpyAsync(dws + p.off_stage_off, h_soff, (size_t)BG * cap * 2 * sizeof(int64_t), hipMemcpyHostToDevice, copy_stream));
+  HIP_OR_FAIL(hipMemcpyAsync(dws + p.off_stage_sg, h_sg, (size_t)go * sizeof(float), hipMemcpyHostToDevice, copy_stream));
+  // gather factor blocks into pinned ring buffers, copy each as it fills
+  size_t e0 = 0;
+  int slot = 0;
+  std::vector<int> used(kRing, 0);
+  while (e0 < ents.size()) {
+    size_t e1 = e0;
+    int64_t bytes = 0;
+    while (e1 < ents.size() && bytes + ents[e1].bytes <= (int64_t)kRingBytes) bytes += ents[e1++].bytes;
+    if (used[slot]) HIP_OR_FAIL(hipEventSynchronize(ctx->ev_ring[slot]));
+    char* buf = h_ring + (size_t)slot * kRingBytes;
+    const int64_t base = ents[e0].dst;
+    ctx->pool->parallel_for((int64_t)(e1 - e0), [&](int64_t i) {
+      const Ent& en = ents[e0 + i];
+      std::memcpy(buf + (en.dst - base) * es, en.src, en.bytes);
+    });
+    HIP_OR_FAIL(hipMemcpyAsync(d_stage_fac + base * es, buf, bytes, hipMemcpyHostToDevice, copy_stream));
+    HIP_OR_FAIL(hipEventRecord(ctx->ev_ring[slot], copy_stream));
+    used[slot] = 1;
+    slot = (slot + 1) % kRing;
+    e0 = e1;
+  }
+  HIP_OR_FAIL(hipEventRecord(ctx->ev_copy, copy_stream));
+  if (copy_stream != stream) HIP_OR_FAIL(hipStreamWaitEvent(stream, ctx->ev_copy, 0));
+  AttendArgs a5 = a;
+  a5.n_a4_wg = 0;
+  a5.stage_off = reinterpret_cast<const int64_t*>(dws + p.off_stage_off);
+  a5.stage_fac = d_stage_fac;
+  a5.stage_sg = reinterpret_cast<const float*>(dws + p.off_stage_sg);
+  HIP_OR_FAIL(launch_attend(a5, stream));
+  HIP_OR_FAIL(launch_combine(a, stream));
+  return SEKV_OK;
+}
+
+sekv_status sekv_profile_enable(sekv_ctx* ctx, int32_t enable) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  ctx->profile = enable != 0;
+  ctx->prof_route.used = ctx->prof_attend.used = 0;
+  return SEKV_OK;
+}
+
+sekv_status sekv_profile_read(sekv_ctx* ctx, double* route_ms, int64_t* route_n, double* attend_ms, int64_t* attend_n) {
+  if (!ctx || !route_ms || !route_n || !attend_ms || !attend_n) return fail(SEKV_EINVAL, "sekv_profile_read: NULL argument");
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+  HIP_OR_FAIL(prof_sum(ctx->prof_route, route_ms, route_n));
+  HIP_OR_FAIL(prof_sum(ctx->prof_attend, attend_ms, attend_n));
+  return SEKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal launch interface between the host runtime (sekv_host.cpp) and the
+// gfx950 kernels (sekv_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace sekv {
+
+constexpr int kMaxBatch = 64;        // per-sequence sizes travel in kernel arguments
+constexpr int kMaxGroups = 256;      // batch * kv heads handled by one decode launch
+constexpr int kMaxSpan = 128;        // longest span body / highest rank the kernels hold
+constexpr int kRouteThreads = 256;   // spans per route workgroup (one lane per span)
+constexpr int kAttnThreads = 256;    // four waves per attention workgroup
+constexpr int kExpChunk = 8;         // expanded spans per wave work item
+
+struct RouteArgs {
+  int dtype;                 // 0 f32, 1 bf16
+  int B, Hq, Hkv, D, seg_cap, nblk;
+  int n_seg[kMaxBatch];
+  const void* q;             // [B][Hq][D]
+  const float* theta;        // [B][Hq]
+  const void* rho;           // [B][Hkv][seg_cap][D]
+  uint8_t* dmask;            // [B][Hkv][seg_cap] workspace
+  unsigned int* counters;    // [B*Hkv] zero on entry, left zero on exit
+  int32_t* exp_list;         // [B][Hkv][seg_cap]
+  uint8_t* exp_mask;         // [B][Hkv][seg_cap]
+  int32_t* exp_count;        // [B][Hkv]
+};
+
+struct AttendArgs {
+  int dtype;
+  int B, Hq, Hkv, D, seg_cap, full_cap;
+  int n_full[kMaxBatch];
+  int n_seg[kMaxBatch];
+  int chunk_a4;              // memory entries per full-res/summary workgroup
+  int nch_a4;                // workgroups per (b, kv) for that pass
+  int P_max;                 // partial slots per (b, kv)
+  int n_a5_wg;               // workgroups running the expanded-span role
+  int n_a4_wg;               // workgroups running the full-res/summary role
+  float qscale;              // log2(e) / sqrt(D)
+  const void* q;
+  const void* full_k; const void* full_v;
+  const void* sum_k; const void* sum_v;
+  const int32_t* seg_off; const int32_t* rank;
+  const int64_t* fac_off; const int64_t* sg_off;   // device pools (staged == nullptr)
+  const void* fac; const float* sg;
+  const int64_t* stage_off;  // host-resident mode: [B*Hkv][seg_cap][2] (fac, sg) offsets per list entry
+  const void* stage_fac; const float* stage_sg;
+  const int32_t* exp_list; const uint8_t* exp_mask; const int32_t* exp_count;
+  float* part_ml;            // [B*Hkv][P_max][G][2]
+  float* part_o;             // [B*Hkv][P_max][G][D]
+  float* out;                // [B][Hq][D]
+};
+
+struct ReconArgs {
+  int dtype;
+  int B, Hkv, D, seg_cap;
+  const int32_t* seg_off; const int32_t* rank;
+  const int64_t* fac_off; const int64_t* sg_off;
+  const void* fac; const float* sg;
+  const int32_t* exp_list; const int32_t* exp_count;
+  int32_t* tok_off;          // [B][Hkv][seg_cap+1]
+  float* k_out; float* v_out;
+  int T;
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+hipError_t launch_combine(const AttendArgs& a, hipStream_t s);
+hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s);
+
+}  // namespace sekv

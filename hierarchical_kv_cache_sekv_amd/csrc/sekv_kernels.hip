@@ -1,0 +1,800 @@
+// gfx950 (CDNA4) kernels of the SeKV mixed-resolution decode path.
+//
+// Pages (by title and section): gist.science German explainer of "SeKV:
+// Resolution-Adaptive KV Cache with Hierarchical Semantic Memory for
+// Long-Context LLM Inference", "Technisches Resümee" > "Methodik" part 3
+// (Routing, Expansion, Mixed-Resolution Attention); the Chinese explainer,
+// "技术摘要" > "方法论" part 3; the authors' abstract (low-rank SVD basis per
+// span, on-demand token-level reconstruction).
+//
+// Kernels
+//   route_kernel    one lane per span, the G heads of a KV group per lane:
+//                   canonical float32 score, decision bits, then the last
+//                   workgroup of each (b, kv) compacts the ascending list.
+//   attend_kernel   two roles in one grid.  Role A (full-resolution entries +
+//                   size-corrected summaries) streams K/V rows with 16 lanes per
+//                   row (8 elements per lane, 16-byte loads) and keeps one
+//                   online-softmax state per row-subgroup.  Role E (expanded
+//                   spans) never materialises the rebuilt K/V: it applies the
+//                   factors to the query (y = sigma~ .* (Vh_K q)), scores the
+//                   tokens with U y, and applies the weights back through U and
+//                   Vh_V, which reads every factor byte once.
+//   combine_kernel  log-sum-exp merge of all partials of a query head.
+//   recon_*         standalone token-level K/V rebuild (tests, unfused use).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sekv_internal.h"
+
+namespace sekv {
+namespace {
+
+using bf16raw = uint16_t;
+
+// ---------------------------------------------------------------- loads
+__device__ __forceinline__ void load8(const float* p, float (&f)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+__device__ __forceinline__ void load8(const bf16raw* p, float (&f)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xffff0000u);
+  f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xffff0000u);
+  f[4] = __uint_as_float(u.z << 16); f[5] = __uint_as_float(u.z & 0xffff0000u);
+  f[6] = __uint_as_float(u.w << 16); f[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ float load1(const bf16raw* p) { return __uint_as_float(uint32_t(*p) << 16); }
+
+// ---------------------------------------------------------------- lane reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of LPR (8 or 16) lanes; every lane gets the group sum.
+// quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror, row_mirror.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  if constexpr (LPR == 16) x += dpp<0x140>(x);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// LDS written and read by different lanes of the same wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr float kNegInf = -__builtin_inff();
+
+// ================================================================ route
+// Canonical score: z = 0; for i in 0..D-1: z = fl32(z + fl32(q_i * rho_i)).
+// Contraction into FMA is switched off for exactly these two operations, so
+// each product is rounded to float32 before it is added.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a) {
+  __shared__ float qs[G * D];
+  __shared__ int wsum[kRouteThreads / 64];
+  __shared__ int s_last;
+  const int blk = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = b * a.Hkv + kv;
+  const int ns = a.n_seg[b];
+  const T* q = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
+  for (int i = tid; i < G * D; i += kRouteThreads) qs[i] = load1(q + i);
+  float th[G];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) th[gi] = a.theta[(size_t)b * a.Hq + kv * G + gi];
+  __syncthreads();
+
+  const int S = blk * kRouteThreads + tid;
+  uint32_t bits = 0;
+  if (S < ns) {
+    const T* r = static_cast<const T*>(a.rho) + ((size_t)g * a.seg_cap + S) * D;
+    float z[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) z[gi] = 0.0f;
+#pragma unroll 2
+    for (int c = 0; c < D; c += 8) {
+      float rv[8];
+      load8(r + c, rv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+#pragma clang fp contract(off)
+          const float prod = qs[gi * D + c + i] * rv[i];
+          z[gi] = z[gi] + prod;
+        }
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) bits |= (z[gi] > th[gi] ? 1u : 0u) << gi;
+  }
+  if (S < a.seg_cap) a.dmask[(size_t)g * a.seg_cap + S] = (uint8_t)bits;
+
+  // Publish this block's decisions; the last block of (b, kv) to arrive compacts.
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = atomicAdd(&a.counters[g], 1u);
+    s_last = (prev == (unsigned)(a.nblk - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  const uint8_t* dm = a.dmask + (size_t)g * a.seg_cap;
+  int32_t* lst = a.exp_list + (size_t)g * a.seg_cap;
+  uint8_t* msk = a.exp_mask + (size_t)g * a.seg_cap;
+  int base = 0;
+  for (int S0 = 0; S0 < ns; S0 += 4 * kRouteThreads) {
+    const int s0 = S0 + 4 * tid;
+    uint8_t m4[4];
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m4[i] = (s0 + i < ns) ? __builtin_nontemporal_load(dm + s0 + i) : (uint8_t)0;
+      c += m4[i] != 0;
+    }
+    // block exclusive scan of c
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int wbase = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kRouteThreads / 64; ++w) {
+      const int v = wsum[w];
+      if (w < wave) wbase += v;
+      total += v;
+    }
+    int pos = base + wbase + incl - c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (m4[i]) {
+        lst[pos] = s0 + i;
+        msk[pos] = m4[i];
+        ++pos;
+      }
+    }
+    base += total;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.exp_count[g] = base;
+    a.counters[g] = 0u;  // ready for the next call
+  }
+}
+
+// ================================================================ attention
+template <int D, int G>
+struct AttnLds {
+  // role A
+  static constexpr int kMaskBytes = 2048;  // >= chunk_a4 (host checks)
+  // role E, per wave: y/b buffer and p buffer, [kMaxSpan][G] floats each
+  static constexpr int kWaveFloats = 2 * kMaxSpan * G;
+  static constexpr int kMergeFloats = 4 * G * (D + 2);
+  static constexpr int kRoleA = kMaskBytes + kMaskBytes * 4 + kMergeFloats * 4;
+  static constexpr int kRoleE = 4 * kWaveFloats * 4 + (kMaxGroups + 1) * 4 * 2;
+  static constexpr int kBytes = kRoleA > kRoleE ? kRoleA : kRoleE;
+};
+
+template <int D, int G>
+__device__ __forceinline__ void write_partial_merged(const AttendArgs& a, int g, int slot, float (&m)[G],
+                                                     float (&l)[G], float (&o)[G][8], float* merge) {
+  // Merge the states of the row-subgroups of this wave, then of the 4 waves.
+  constexpr int LPR = D / 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int part = lane % LPR, sub = lane / LPR;
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    float M = m[gi];
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float f = (m[gi] == kNegInf) ? 0.0f : exp2f(m[gi] - M);
+    float lv = l[gi] * f;
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) lv += __shfl_xor(lv, off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float ov = o[gi][i] * f;
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) ov += __shfl_xor(ov, off);
+      o[gi][i] = ov;
+    }
+    m[gi] = M;
+    l[gi] = lv;
+  }
+  float* mm = merge;                 // [4][G]
+  float* ll = merge + 4 * G;         // [4][G]
+  float* oo = merge + 8 * G;         // [4][G][D]
+  if (lane == 0) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) { mm[wave * G + gi] = m[gi]; ll[wave * G + gi] = l[gi]; }
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) oo[(wave * G + gi) * D + part * 8 + i] = o[gi][i];
+  }
+  __syncthreads();
+  float* pml = a.part_ml + ((size_t)g * a.P_max + slot) * G * 2;
+  float* po = a.part_o + ((size_t)g * a.P_max + slot) * G * D;
+  for (int idx = tid; idx < G * D; idx += kAttnThreads) {
+    const int gi = idx / D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * G + gi]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mm[w * G + gi];
+      const float f = (mw == kNegInf) ? 0.0f : exp2f(mw - M);
+      acc += f * oo[(w * G + gi) * D + (idx % D)];
+    }
+    po[idx] = acc;
+  }
+  if (tid < G) {
+    const int gi = tid;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * G + gi]);
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mm[w * G + gi];
+      L += (mw == kNegInf) ? 0.0f : exp2f(mw - M) * ll[w * G + gi];
+    }
+    pml[gi * 2] = M;
+    pml[gi * 2 + 1] = L;
+  }
+}
+
+// Role A: one workgroup = one chunk of the (b, kv) memory stream
+// [full-res entries 0..n_full) ++ [span summaries 0..n_seg).
+template <typename T, int D, int G>
+__device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
+  constexpr int LPR = D / 8, RPW = 64 / LPR, U = 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane / LPR, part = lane % LPR;
+  const int g = idx / a.nch_a4, chunk = idx % a.nch_a4;
+  const int b = g / a.Hkv, kv = g % a.Hkv;
+  const int nf = a.n_full[b], ns = a.n_seg[b];
+  const int ntot = nf + ns;
+  const int e0 = min(ntot, chunk * a.chunk_a4), e1 = min(ntot, e0 + a.chunk_a4);
+  const int S0 = max(e0, nf) - nf, S1 = max(e1, nf) - nf;
+
+  uint8_t* smask = reinterpret_cast<uint8_t*>(lds);
+  float* slog = reinterpret_cast<float*>(lds + AttnLds<D, G>::kMaskBytes);
+  float* merge = reinterpret_cast<float*>(lds + AttnLds<D, G>::kMaskBytes * 5);
+
+  const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
+  for (int i = tid; i < S1 - S0; i += kAttnThreads) {
+    const int S = S0 + i;
+    smask[i] = 0;
+    slog[i] = log2f((float)(so[S + 1] - so[S] - 1));
+  }
+  __syncthreads();
+  if (S1 > S0) {
+    const int cnt = a.exp_count[g];
+    const int32_t* lst = a.exp_list + (size_t)g * a.seg_cap;
+    int lo = 0, hi = cnt;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (lst[mid] < S0) lo = mid + 1; else hi = mid;
+    }
+    for (int j = lo + tid; j < cnt; j += kAttnThreads) {
+      const int S = lst[j];
+      if (S >= S1) break;
+      smask[S - S0] = a.exp_mask[(size_t)g * a.seg_cap + j];
+    }
+  }
+  __syncthreads();
+
+  float qr[G][8];
+  const T* qb = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    load8(qb + (size_t)gi * D + part * 8, qr[gi]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qr[gi][i] *= a.qscale;
+  }
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    m[gi] = kNegInf; l[gi] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[gi][i] = 0.0f;
+  }
+
+  const int per_wave = (a.chunk_a4 + 3) / 4;
+  const int wb = min(e1, e0 + wave * per_wave), we = min(e1, wb + per_wave);
+  const T* fk = static_cast<const T*>(a.full_k) + (size_t)g * a.full_cap * D;
+  const T* fv = static_cast<const T*>(a.full_v) + (size_t)g * a.full_cap * D;
+  const T* sk = static_cast<const T*>(a.sum_k) + (size_t)g * a.seg_cap * D;
+  const T* sv = static_cast<const T*>(a.sum_v) + (size_t)g * a.seg_cap * D;
+
+  for (int base = wb; base < we; base += RPW * U) {
+    float kf[U][8], vf[U][8];
+    int ev[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = base + u * RPW + sub;
+      ev[u] = e;
+      const int ec = e < we ? e : wb;  // clamp: an in-range row, weight forced to 0 below
+      const T* kp = ec < nf ? fk + (size_t)ec * D : sk + (size_t)(ec - nf) * D;
+      const T* vp = ec < nf ? fv + (size_t)ec * D : sv + (size_t)(ec - nf) * D;
+      load8(kp + part * 8, kf[u]);
+      load8(vp + part * 8, vf[u]);
+    }
+    float s[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = ev[u];
+      uint32_t bits = 0;
+      float adj = 0.0f;
+      if (e >= nf && e < we) {
+        bits = smask[e - nf - S0];
+        adj = slog[e - nf - S0];
+      }
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += kf[u][i] * qr[gi][i];
+        acc = group_sum<LPR>(acc);
+        s[u][gi] = (e >= we || ((bits >> gi) & 1u)) ? kNegInf : acc + adj;
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      float mt = s[0][gi];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][gi]);
+      const float mn = fmaxf(m[gi], mt);
+      if (mn == kNegInf) continue;
+      const float alpha = exp2f(m[gi] - mn);
+      float p[U], ps = 0.0f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) { p[u] = exp2f(s[u][gi] - mn); ps += p[u]; }
+      l[gi] = l[gi] * alpha + ps;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float acc = o[gi][i] * alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc += p[u] * vf[u][i];
+        o[gi][i] = acc;
+      }
+      m[gi] = mn;
+    }
+  }
+  write_partial_merged<D, G>(a, g, chunk, m, l, o, merge);
+}
+
+// Role E: each wave takes work items of up to kExpChunk listed spans of one
+// (b, kv); a wave keeps one online-softmax state per head of the group.
+template <typename T, int D, int G>
+__device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
+  constexpr int LPR = D / 8, RPW = 64 / LPR, UK = 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane / LPR, part = lane % LPR;
+  const int BG = a.B * a.Hkv;
+  int* pre = reinterpret_cast<int*>(lds + 4 * AttnLds<D, G>::kWaveFloats * 4);  // [BG+1] chunk prefix
+  // chunk prefix over (b, kv): nch = ceil(count / kExpChunk)
+  {
+    int* tmp = pre + (kMaxGroups + 1);
+    for (int i = tid; i < BG; i += kAttnThreads) tmp[i] = (a.exp_count[i] + kExpChunk - 1) / kExpChunk;
+    __syncthreads();
+    if (wave == 0) {
+      int run = 0;
+      for (int c0 = 0; c0 < BG; c0 += 64) {
+        const int i = c0 + lane;
+        const int v = i < BG ? tmp[i] : 0;
+        int incl = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int t = __shfl_up(incl, off);
+          if (lane >= off) incl += t;
+        }
+        if (i < BG) pre[i] = run + incl - v;
+        run += __shfl(incl, 63);
+      }
+      if (lane == 0) pre[BG] = run;
+    }
+    __syncthreads();
+  }
+  const int total = pre[BG];
+  float* yb = reinterpret_cast<float*>(lds) + wave * AttnLds<D, G>::kWaveFloats;  // [kMaxSpan][G]
+  float* pb = yb + kMaxSpan * G;                                                   // [kMaxSpan][G]
+  const int nwaves = a.n_a5_wg * 4;
+  const bool staged = a.stage_off != nullptr;
+
+  for (int c = wg * 4 + wave; c < total; c += nwaves) {
+    int lo = 0, hi = BG;  // find g with pre[g] <= c < pre[g+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= c) lo = mid; else hi = mid;
+    }
+    const int g = lo, lc = c - pre[g];
+    const int b = g / a.Hkv, kv = g % a.Hkv;
+    const int cnt = a.exp_count[g];
+    const int j0 = lc * kExpChunk, j1 = min(cnt, j0 + kExpChunk);
+
+    float qr[G][8];
+    const T* qb = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      load8(qb + (size_t)gi * D + part * 8, qr[gi]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qr[gi][i] *= a.qscale;
+    }
+    float m[G], l[G], o[G][8];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      m[gi] = kNegInf; l[gi] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[gi][i] = 0.0f;
+    }
+    const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
+    for (int j = j0; j < j1; ++j) {
+      const int S = a.exp_list[(size_t)g * a.seg_cap + j];
+      const uint32_t bits = a.exp_mask[(size_t)g * a.seg_cap + j];
+      const int L = so[S + 1] - so[S] - 1;
+      const int r = a.rank[(size_t)b * a.seg_cap + S];
+      const int rp = (r + 7) & ~7;
+      const T* Ub;
+      const float* sgp;
+      if (staged) {
+        const int64_t* st = a.stage_off + ((size_t)g * a.seg_cap + j) * 2;
+        Ub = static_cast<const T*>(a.stage_fac) + st[0];
+        sgp = a.stage_sg + st[1];
+      } else {
+        Ub = static_cast<const T*>(a.fac) + a.fac_off[(size_t)g * a.seg_cap + S];
+        sgp = a.sg + a.sg_off[(size_t)g * a.seg_cap + S];
+      }
+      const T* Vb = Ub + (size_t)L * rp;
+
+      // step 1: y[k][gi] = sigma_k * gate_k * (Vh_K[k] . q_gi)   (q carries the softmax scale)
+      for (int k0 = 0; k0 < r; k0 += RPW * UK) {
+        float vk[UK][8];
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const int k = min(k0 + u * RPW + sub, r - 1);
+          load8(Vb + (size_t)k * 2 * D + part * 8, vk[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const int k = k0 + u * RPW + sub;
+          const float st = (k < r) ? sgp[k] * sgp[r + k] : 0.0f;
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc += vk[u][i] * qr[gi][i];
+            acc = group_sum<LPR>(acc);
+            if (part == 0 && k < r) yb[k * G + gi] = acc * st;
+          }
+        }
+      }
+      wave_lds_sync();
+      // step 2: token scores s_t = U[t] . y  (two tokens per lane at most)
+      float s[2][G];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = lane + 64 * tt;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) s[tt][gi] = kNegInf;
+        if (t < L) {
+          float acc[G];
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) acc[gi] = 0.0f;
+          for (int k8 = 0; k8 < rp; k8 += 8) {
+            float u8[8];
+            load8(Ub + (size_t)t * rp + k8, u8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              if (k8 + i < r) {
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi) acc[gi] += u8[i] * yb[(k8 + i) * G + gi];
+              }
+            }
+          }
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) s[tt][gi] = ((bits >> gi) & 1u) ? acc[gi] : kNegInf;
+        }
+      }
+      wave_lds_sync();
+      // step 3: online softmax over the span's tokens
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const float ms = wave_max(fmaxf(s[0][gi], s[1][gi]));
+        const float mn = fmaxf(m[gi], ms);
+        float p0 = 0.0f, p1 = 0.0f;
+        if (mn != kNegInf) {
+          const float alpha = exp2f(m[gi] - mn);
+          p0 = exp2f(s[0][gi] - mn);
+          p1 = exp2f(s[1][gi] - mn);
+          l[gi] = l[gi] * alpha + wave_sum(p0 + p1);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[gi][i] *= alpha;
+          m[gi] = mn;
+        }
+        if (lane < L) pb[lane * G + gi] = p0;
+        if (lane + 64 < L) pb[(lane + 64) * G + gi] = p1;
+      }
+      wave_lds_sync();
+      // step 4: a[k] = sum_t U[t][k] p_t, then b[k] = sigma_k * gate_k * a[k]  (into yb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int k = lane + 64 * kk;
+        if (k < r) {
+          float acc[G];
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) acc[gi] = 0.0f;
+          for (int t = 0; t < L; ++t) {
+            const float u = load1(Ub + (size_t)t * rp + k);
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) acc[gi] += u * pb[t * G + gi];
+          }
+          const float st = sgp[k] * sgp[r + k];
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) yb[k * G + gi] = acc[gi] * st;
+        }
+      }
+      wave_lds_sync();
+      // step 5: o += Vh_V^T b
+      for (int k0 = 0; k0 < r; k0 += RPW * UK) {
+        float vv[UK][8];
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const int k = min(k0 + u * RPW + sub, r - 1);
+          load8(Vb + (size_t)k * 2 * D + D + part * 8, vv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const int k = k0 + u * RPW + sub;
+          if (k < r) {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+              const float bk = yb[k * G + gi];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) o[gi][i] += bk * vv[u][i];
+            }
+          }
+        }
+      }
+      wave_lds_sync();
+    }
+    // merge the row-subgroups of this wave (states share m, l) and write the partial
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float ov = o[gi][i];
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) ov += __shfl_xor(ov, off);
+        o[gi][i] = ov;
+      }
+    const int slot = a.nch_a4 + lc;
+    float* pml = a.part_ml + ((size_t)g * a.P_max + slot) * G * 2;
+    float* po = a.part_o + ((size_t)g * a.P_max + slot) * G * D;
+    if (sub == 0) {
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) po[gi * D + part * 8 + i] = o[gi][i];
+    }
+    if (lane < G) {
+      float mv = m[0], lv = l[0];
+#pragma unroll
+      for (int gi = 1; gi < G; ++gi) if (lane == gi) { mv = m[gi]; lv = l[gi]; }
+      pml[lane * 2] = mv;
+      pml[lane * 2 + 1] = lv;
+    }
+  }
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttendArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  const int blk = blockIdx.x;
+  if (blk < a.n_a5_wg) role_expanded<T, D, G>(a, blk, lds);
+  else role_full_summary<T, D, G>(a, blk - a.n_a5_wg, lds);
+}
+
+// ================================================================ combine
+template <int D, int G>
+__global__ __launch_bounds__(64) void combine_kernel(const AttendArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const int g = b * a.Hkv + h / G, gi = h % G;
+  const int lane = threadIdx.x;
+  const int np = a.nch_a4 + (a.exp_count[g] + kExpChunk - 1) / kExpChunk;
+  const float* ml = a.part_ml + (size_t)g * a.P_max * G * 2;
+  const float* po = a.part_o + (size_t)g * a.P_max * G * D;
+  float M = kNegInf;
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[(p * G + gi) * 2]);
+  M = wave_max(M);
+  constexpr int EPL = D / 64;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+  float L = 0.0f;
+  for (int p = 0; p < np; ++p) {
+    const float mp = ml[(p * G + gi) * 2];
+    if (mp == kNegInf) continue;
+    const float f = exp2f(mp - M);
+    L += f * ml[(p * G + gi) * 2 + 1];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += f * po[((size_t)p * G + gi) * D + lane + 64 * e];
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) a.out[(size_t)bh * D + lane + 64 * e] = acc[e] * inv;
+}
+
+// ================================================================ reconstruct
+__global__ __launch_bounds__(64) void recon_scan_kernel(const ReconArgs a) {
+  const int g = blockIdx.x, b = g / a.Hkv;
+  const int lane = threadIdx.x;
+  const int cnt = a.exp_count[g];
+  const int32_t* lst = a.exp_list + (size_t)g * a.seg_cap;
+  const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
+  int32_t* to = a.tok_off + (size_t)g * (a.seg_cap + 1);
+  int run = 0;
+  for (int j0 = 0; j0 < cnt; j0 += 64) {
+    const int j = j0 + lane;
+    int v = 0;
+    if (j < cnt) {
+      const int S = lst[j];
+      v = so[S + 1] - so[S] - 1;
+    }
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    if (j < cnt) to[j] = run + incl - v;
+    run += __shfl(incl, 63);
+  }
+  if (lane == 0) to[cnt] = run;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
+  const int kv = blockIdx.y, b = blockIdx.z, g = b * a.Hkv + kv;
+  const int lane = threadIdx.x;
+  const int cnt = a.exp_count[g];
+  const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
+  constexpr int CPL = 2 * D / 64;  // output columns per lane
+  for (int j = blockIdx.x; j < cnt; j += gridDim.x) {
+    const int S = a.exp_list[(size_t)g * a.seg_cap + j];
+    const int L = so[S + 1] - so[S] - 1;
+    const int r = a.rank[(size_t)b * a.seg_cap + S];
+    const int rp = (r + 7) & ~7;
+    const T* Ub = static_cast<const T*>(a.fac) + a.fac_off[(size_t)g * a.seg_cap + S];
+    const T* Vb = Ub + (size_t)L * rp;
+    const float* sgp = a.sg + a.sg_off[(size_t)g * a.seg_cap + S];
+    const int row0 = a.tok_off[(size_t)g * (a.seg_cap + 1) + j];
+    for (int t = 0; t < L; ++t) {
+      float acc[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
+      for (int k = 0; k < r; ++k) {
+        const float w = load1(Ub + (size_t)t * rp + k) * (sgp[k] * sgp[r + k]);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] += w * load1(Vb + (size_t)k * 2 * D + lane + 64 * c);
+      }
+      const size_t orow = ((size_t)g * a.T + row0 + t) * D;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int col = lane + 64 * c;
+        if (col < D) a.k_out[orow + col] = acc[c];
+        else a.v_out[orow + col - D] = acc[c];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+#define SEKV_DISPATCH(DT, DIM, GRP, BODY)                                   \
+  do {                                                                      \
+    if ((DT) == 0) {                                                        \
+      using TT = float;                                                     \
+      SEKV_DISPATCH_D(DIM, GRP, BODY);                                      \
+    } else {                                                                \
+      using TT = bf16raw;                                                   \
+      SEKV_DISPATCH_D(DIM, GRP, BODY);                                      \
+    }                                                                       \
+  } while (0)
+#define SEKV_DISPATCH_D(DIM, GRP, BODY)                                     \
+  do {                                                                      \
+    if ((DIM) == 64) {                                                      \
+      constexpr int DD = 64;                                                \
+      SEKV_DISPATCH_G(GRP, BODY);                                           \
+    } else {                                                                \
+      constexpr int DD = 128;                                               \
+      SEKV_DISPATCH_G(GRP, BODY);                                           \
+    }                                                                       \
+  } while (0)
+#define SEKV_DISPATCH_G(GRP, BODY)                                          \
+  do {                                                                      \
+    switch (GRP) {                                                          \
+      case 1: { constexpr int GG = 1; BODY; } break;                        \
+      case 2: { constexpr int GG = 2; BODY; } break;                        \
+      case 4: { constexpr int GG = 4; BODY; } break;                        \
+      default: { constexpr int GG = 8; BODY; } break;                       \
+    }                                                                       \
+  } while (0)
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  dim3 grid(a.nblk, a.Hkv, a.B);
+  SEKV_DISPATCH(a.dtype, a.D, G, (route_kernel<TT, DD, GG><<<grid, kRouteThreads, 0, s>>>(a)));
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  const int nblk = a.n_a5_wg + a.n_a4_wg;
+  if (nblk == 0) return hipSuccess;
+  SEKV_DISPATCH(a.dtype, a.D, G,
+                (attend_kernel<TT, DD, GG><<<nblk, kAttnThreads, AttnLds<DD, GG>::kBytes, s>>>(a)));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const AttendArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  SEKV_DISPATCH_D(a.D, G, (combine_kernel<DD, GG><<<a.B * a.Hq, 64, 0, s>>>(a)));
+  return hipGetLastError();
+}
+
+hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s) {
+  recon_scan_kernel<<<a.B * a.Hkv, 64, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid(256, a.Hkv, a.B);
+  if (a.dtype == 0) {
+    if (a.D == 64) recon_kernel<float, 64><<<grid, 64, 0, s>>>(a);
+    else recon_kernel<float, 128><<<grid, 64, 0, s>>>(a);
+  } else {
+    if (a.D == 64) recon_kernel<bf16raw, 64><<<grid, 64, 0, s>>>(a);
+    else recon_kernel<bf16raw, 128><<<grid, 64, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sekv

@@ -168,7 +168,6 @@ def make_inputs(w: Workload, *, n_steps: int | None = None, rank_cap: int | None
         g2 = _rng(w, 2, b)
         starts, ends = _blocks(s, float(thr[b]), lo_tok, hi_tok)
         n_tok = int(ends[-1] - starts[0]) if starts.size else 0
-        blk = np.repeat(np.arange(starts.size), (ends - starts)) if starts.size else np.zeros(0, np.int64)
         for h in range(Hkv):
             k[b, h] = kv[0, h]
             v[b, h] = kv[1, h]
@@ -176,9 +175,12 @@ def make_inputs(w: Workload, *, n_steps: int | None = None, rank_cap: int | None
                 continue
             A = g2.standard_normal((n_tok, R), dtype=np.float32)                  # one row per token
             Bm = g2.standard_normal((starts.size, R, 2 * d), dtype=np.float32) * np.float32(1.0 / math.sqrt(R))
-            comp = np.zeros((n_tok, 2 * d), np.float32)
-            for r in range(R):                                                     # sum of R rank-1 terms
-                comp += A[:, r:r + 1] * np.repeat(Bm[:, r, :], ends - starts, axis=0)
+            lens = ends - starts
+            comp = np.empty((n_tok, 2 * d), np.float32)
+            for ell in np.unique(lens).tolist():                                   # blocks of equal length together
+                sel = np.nonzero(lens == ell)[0]
+                rows = ((starts[sel] - lo_tok)[:, None] + np.arange(ell)[None, :]).reshape(-1)
+                comp[rows] = np.matmul(A[rows].reshape(sel.size, ell, R), Bm[sel]).reshape(-1, 2 * d)
             k[b, h, lo_tok:lo_tok + n_tok] += comp[:, :d]
             v[b, h, lo_tok:lo_tok + n_tok] += comp[:, d:]
         del kv

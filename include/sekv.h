@@ -1,0 +1,257 @@
+/*
+ * sekv.h - C ABI of libsekv, an MI355X (gfx950) implementation of the
+ * decode-time hot path of SeKV's resolution-adaptive semantic KV cache.
+ *
+ * Pages cited (by title and section):
+ *   [abstract] the authors' abstract of "SeKV: Resolution-Adaptive KV Cache with
+ *              Hierarchical Semantic Memory for Long-Context LLM Inference"
+ *              (chatpaper.ai paper page, English part).
+ *   [de-1..3]  gist.science German explainer of the same paper, "Technisches
+ *              Resümee" > "Methodik", parts 1 (span segmentation), 2 (dual
+ *              resolution storage), 3 (zoom-in: routing, expansion,
+ *              mixed-resolution attention).
+ *   [zh-1..3]  gist.science Chinese explainer, "技术摘要" > "方法论", parts 1-3.
+ *
+ * Conventions shared by every call
+ *   - Shapes come from sekv_config.  B = batch, T = n_ctx, Hq / Hkv query / KV
+ *     heads, G = Hq / Hkv (1..8), d = head_dim (64 or 128).  Query head h
+ *     belongs to KV head h / G.
+ *   - "dtype" arrays hold float32 or bfloat16 (raw 16-bit patterns) per
+ *     sekv_config.dtype.  sigma, gate, theta and outputs are always float32.
+ *   - All arrays are C-order, caller-owned, and never freed or reallocated by
+ *     the library.  "device" = HBM of the context's GPU; "host" = CPU memory;
+ *     "pinned" = page-locked host memory from hipHostMalloc.
+ *   - Capacities (host-computable, see sekv_capacities):
+ *       seg_cap  = floor((T - n_sink - n_recent) / (min_span + 1)) + 1
+ *       full_cap = min(T, n_sink + seg_cap + n_recent + 1)
+ *   - Errors: every call returns a sekv_status; sekv_last_error() returns a
+ *     thread-local message for the last failing call of this thread.  All
+ *     argument checks run on the host before anything is enqueued; a call that
+ *     fails a check writes nothing.  No C++ exception crosses the ABI.
+ *   - Asynchrony: calls enqueue on the caller's stream and return, except
+ *     sekv_plan_spans and sekv_build_spans (host-synchronous) and the
+ *     host-resident decode (one documented host wait, see below).
+ *   - One context per device.  Calls that share a context must be ordered on
+ *     one stream (sekv_route keeps per-(b, KV head) completion counters in the
+ *     context).
+ */
+#ifndef SEKV_H
+#define SEKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sekv_status {
+  SEKV_OK = 0,
+  SEKV_EINVAL = 1,     /* null pointer, bad enum, bad parameter value        */
+  SEKV_ESHAPE = 2,     /* inconsistent or unsupported shape                  */
+  SEKV_ECAPACITY = 3,  /* a caller buffer or workspace is too small          */
+  SEKV_EHIP = 4,       /* a HIP runtime call failed                           */
+  SEKV_ENOMEM = 5      /* the library could not allocate its own state       */
+} sekv_status;
+
+typedef enum sekv_dtype { SEKV_F32 = 0, SEKV_BF16 = 1 } sekv_dtype;
+
+typedef struct sekv_config {
+  int32_t batch, n_ctx, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_sink;          /* full-resolution sink [0, n_sink)                      */
+  int32_t n_recent;        /* full-resolution recent window, last n_recent tokens   */
+  int32_t min_span;        /* lo: data heads need >= lo body tokens on both sides   */
+  int32_t max_span;        /* hi: a body of hi tokens forces the next head          */
+  int32_t dtype;           /* sekv_dtype of K/V, q, summaries, rho, factors         */
+  int32_t factors_on_host; /* 1: fac/sg pools are pinned host memory              */
+} sekv_config;
+
+/*
+ * The span cache: everything decode reads.  Built by sekv_plan_spans +
+ * sekv_build_spans, or filled by the caller directly (same layout).
+ *
+ *   seg_off [B][seg_cap+1] int32: anchor i of sequence b is token seg_off[i];
+ *       span body i is the open token interval (seg_off[i], seg_off[i+1]), of
+ *       length L_i = seg_off[i+1] - seg_off[i] - 1 (1..max_span); the tail
+ *       (full resolution) starts at seg_off[n_seg].  [de-1], [zh-1].
+ *   full_k/full_v [B][Hkv][full_cap][d] dtype: full-resolution keys/values in
+ *       token order sink, anchors (span order), tail.  n_full[b] rows valid.
+ *   sum_k/sum_v [B][Hkv][seg_cap][d] dtype: surprisal-weighted mean key/value of
+ *       each span body.  [de-2], [zh-2].
+ *   rho [B][Hkv][seg_cap][d] dtype: routing key, P^T normalize(P kbar), so that
+ *       q . rho equals the routing-space score of the projected query. [de-2/3]
+ *   rank [B][seg_cap] int32: r_i, 1 <= r_i <= min(L_i, 2d), shared by all KV
+ *       heads of the span.  [de-2], [zh-2] (adaptive rank budget).
+ *   fac pool (dtype): for span (b, kv, i) a block at element offset
+ *       fac_off[b][kv][i] (a multiple of 8) holding U [L_i][rp] (row stride
+ *       rp = ceil(r_i / 8) * 8, padding zero) followed by Vh [r_i][2d]
+ *       (columns 0..d-1 the key part, d..2d-1 the value part).
+ *   sg pool (float32): for span (b, kv, i) sigma[r_i] then gate[r_i] at offset
+ *       sg_off[b][kv][i].  Token K/V of the span are U diag(sigma*gate) Vh.
+ *       [abstract], [de-2], [zh-2].
+ *
+ * Device arrays are required for every field; the *_host fields are host
+ * copies the library reads to size grids (n_seg_host, n_full_host) and, in the
+ * host-resident mode, to gather factor blocks (seg_off_host, rank_host,
+ * fac_off_host, sg_off_host).  With factors_on_host = 1, fac and sg must be
+ * pinned host memory.
+ */
+typedef struct sekv_spans {
+  int32_t seg_cap, full_cap;
+  const int32_t* n_seg_host;    /* [B] host */
+  const int32_t* n_full_host;   /* [B] host */
+  const int32_t* seg_off;       /* [B][seg_cap+1] device */
+  const int32_t* rank;          /* [B][seg_cap] device */
+  const void* full_k;           /* [B][Hkv][full_cap][d] device */
+  const void* full_v;
+  const void* sum_k;            /* [B][Hkv][seg_cap][d] device */
+  const void* sum_v;
+  const void* rho;
+  const int64_t* fac_off;       /* [B][Hkv][seg_cap] device */
+  const int64_t* sg_off;        /* [B][Hkv][seg_cap] device */
+  const void* fac;              /* pool, fac_elems elements of dtype */
+  const float* sg;              /* pool, sg_elems floats */
+  int64_t fac_elems, sg_elems;
+  const int32_t* seg_off_host;  /* [B][seg_cap+1] host (host-resident mode) */
+  const int32_t* rank_host;     /* [B][seg_cap] host (host-resident mode)   */
+  const int64_t* fac_off_host;  /* [B][Hkv][seg_cap] host                    */
+  const int64_t* sg_off_host;   /* [B][Hkv][seg_cap] host                    */
+} sekv_spans;
+
+typedef struct sekv_ctx sekv_ctx;
+
+/* Context for one GPU: completion counters, events, copy-side thread pool.
+ * Errors: SEKV_EINVAL (out == NULL), SEKV_EHIP (bad device), SEKV_ENOMEM. */
+sekv_status sekv_ctx_create(int device, sekv_ctx** out);
+void sekv_ctx_destroy(sekv_ctx* ctx);
+/* Thread-local message of this thread's last failing call ("" if none). */
+const char* sekv_last_error(void);
+
+/* seg_cap and full_cap of a configuration (formulas above).  Host only. */
+sekv_status sekv_capacities(const sekv_config* cfg, int32_t* seg_cap, int32_t* full_cap);
+
+/*
+ * sekv_plan_spans - segmentation and pool layout (host only, no GPU).
+ * [de-1], [zh-1]: high-surprisal tokens become anchors, spans are the runs
+ * between neighbouring anchors.  Rule: token n_sink is the first head; for
+ * t in (n_sink, T - n_recent), with body = tokens since the last head, t is a
+ * head if body == max_span, or if surprisal[t] > boundary_thr[b] and
+ * body >= min_span and at least min_span tokens remain before the recent
+ * window; a last head with an empty body is returned to the tail.  Rank
+ * r_i = min(rank_req[b][i], L_i, 2d).
+ *   surprisal [B][T], boundary_thr [B], rank_req [B][seg_cap]: host, read.
+ *   Outputs (host, written): n_seg [B], n_full [B], seg_off [B][seg_cap+1]
+ *   (unused tail entries set to the tail start), rank [B][seg_cap] (0 past
+ *   n_seg), fac_off/sg_off [B][Hkv][seg_cap] (0 past n_seg), *fac_elems,
+ *   *sg_elems (pool sizes).  Errors: SEKV_EINVAL / SEKV_ESHAPE; non-finite
+ *   surprisal or threshold, rank_req < 1 -> SEKV_EINVAL.
+ */
+sekv_status sekv_plan_spans(const sekv_config* cfg, const float* surprisal, const float* boundary_thr,
+                            const int32_t* rank_req, int32_t* n_seg, int32_t* n_full, int32_t* seg_off,
+                            int32_t* rank, int64_t* fac_off, int64_t* sg_off, int64_t* fac_elems,
+                            int64_t* sg_elems);
+
+/*
+ * sekv_build_spans - fill the cache from the prefill K/V (host-synchronous).
+ * k, v [B][Hkv][T][d] dtype: device, read.  surprisal [B][T] f32: host.
+ * route_proj [Hkv][d][d] f32: host (one projection per KV head, [de-3]).
+ * gate [B][Hkv][seg_cap][gate_stride] f32: host (rank gates, first r_i used).
+ * spans: the plan fields (n_seg_host, n_full_host, seg_off_host, rank_host,
+ * fac_off_host, sg_off_host) must hold sekv_plan_spans output; every device
+ * array (and the pools, pinned host when factors_on_host) is written.
+ * Summaries: weights s_t / sum s over the body (uniform if the sum is 0).
+ * Routing key: rho = P^T r/|r|, r = P kbar (0 if |r| = 0).  Factors: rank-r_i
+ * truncated SVD of [K_body | V_body] (one-sided Jacobi, fp64), sign fixed so
+ * each U column's largest-magnitude entry is positive.  Stored values are fp64
+ * rounded to f32 (then to bf16, nearest-even).  Uses host threads.
+ * Errors: SEKV_EINVAL / SEKV_ESHAPE / SEKV_ECAPACITY (pool sizes) / SEKV_EHIP.
+ */
+sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* cfg, const void* k, const void* v,
+                             const float* surprisal, const float* route_proj, const float* gate,
+                             int32_t gate_stride, const sekv_spans* spans, hipStream_t stream);
+
+/* Device workspace of sekv_route, in bytes. */
+size_t sekv_route_workspace_bytes(const sekv_config* cfg, const sekv_spans* spans);
+
+/*
+ * sekv_route - routing and compaction for one decode step.  [de-3], [zh-3]:
+ * the query is scored against each span's routing summary through a sigmoid
+ * relevance gate, and a per-head threshold decides expansion.  Decision for
+ * query head h, span i: z > theta[b][h] (strict), where z = sum over
+ * j = 0..d-1 of q[b][h][j] * rho[b][kv][i][j], evaluated in float32 in that
+ * order with every product and sum rounded separately (sigma(z) > tau is
+ * z > logit(tau); theta may be +/-inf).
+ *   q [B][Hq][d] dtype, theta [B][Hq] f32: device, read.
+ *   exp_list [B][Hkv][seg_cap] int32: ascending span indices that any head of
+ *     the group expands (first exp_count entries valid).
+ *   exp_mask [B][Hkv][seg_cap] uint8: bit g set iff head kv*G+g expands it.
+ *   exp_count [B][Hkv] int32.  All device, written.
+ *   ws: device workspace of sekv_route_workspace_bytes (contents ignored).
+ * Errors: SEKV_EINVAL / SEKV_ESHAPE / SEKV_ECAPACITY / SEKV_EHIP.
+ */
+sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans, const void* q,
+                       const float* theta, int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * sekv_reconstruct - token-level K/V of listed spans (standalone, for checks
+ * and unfused use).  [de-3], [zh-3]: selected spans are rebuilt at token level;
+ * K_hat = U diag(sigma*gate) Vh[:, :d], V_hat = U diag(sigma*gate) Vh[:, d:].
+ *   exp_list, exp_count as written by sekv_route (device).
+ *   tok_off [B][Hkv][seg_cap+1] int32 device, written: row offset of list entry
+ *     j in the outputs (exclusive prefix of L), tok_off[count] = total rows.
+ *   k_out, v_out [B][Hkv][T][d] f32 device, written: rows in list order.
+ *   Host-resident factors are read directly from pinned memory.
+ * Errors: SEKV_EINVAL / SEKV_ESHAPE / SEKV_EHIP.
+ */
+sekv_status sekv_reconstruct(sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans,
+                             const int32_t* exp_list, const int32_t* exp_count, int32_t* tok_off,
+                             float* k_out, float* v_out, hipStream_t stream);
+
+/* Workspace sizes of sekv_mixed_attention_decode: device bytes, and pinned
+ * host bytes (0 unless factors_on_host). */
+size_t sekv_decode_workspace_bytes(const sekv_config* cfg, const sekv_spans* spans);
+size_t sekv_decode_host_workspace_bytes(const sekv_config* cfg, const sekv_spans* spans);
+
+/*
+ * sekv_mixed_attention_decode - one decode step of mixed-resolution attention.
+ * [de-3], [zh-3]: one softmax per query head over (a) full-resolution entries
+ * (sink, anchors, tail) with logit q.k/sqrt(d); (b) for each span this head
+ * does not expand, its summary with logit q.kbar/sqrt(d) + ln L_i and value
+ * vbar; (c) for each span this head expands, its L_i rebuilt tokens.  The
+ * rebuilt K/V never leave registers/LDS (the kernel applies the factors to the
+ * query and to the softmax weights directly).
+ *   q [B][Hq][d] dtype device; exp_list/exp_mask/exp_count from sekv_route.
+ *   out [B][Hq][d] f32 device, written.
+ *   dev_ws: device workspace (sekv_decode_workspace_bytes).
+ *   host_ws: pinned host workspace (sekv_decode_host_workspace_bytes), only
+ *     with factors_on_host.  In that mode the call copies the list to the host
+ *     and waits for it (the one host wait), gathers the listed factor blocks on
+ *     host threads into host_ws, and copies them with hipMemcpyAsync on
+ *     copy_stream while the full-resolution/summary pass runs on stream.
+ *   copy_stream may be NULL (then stream is used).
+ * Errors: SEKV_EINVAL / SEKV_ESHAPE / SEKV_ECAPACITY / SEKV_EHIP.
+ */
+sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans,
+                                        const void* q, const int32_t* exp_list, const uint8_t* exp_mask,
+                                        const int32_t* exp_count, float* out, void* dev_ws,
+                                        size_t dev_ws_bytes, void* host_ws, size_t host_ws_bytes,
+                                        hipStream_t stream, hipStream_t copy_stream);
+
+/*
+ * Measurement hook.  While enabled, sekv_route and sekv_mixed_attention_decode
+ * record a timing-event pair on the caller's stream around their main kernel
+ * (route kernel; attention kernel, both roles) so a benchmark can read the
+ * kernels' own durations.  sekv_profile_read waits for the recorded events,
+ * returns the summed milliseconds and launch counts since the last read, and
+ * resets them.  Errors: SEKV_EINVAL (NULL ctx/outputs), SEKV_EHIP.
+ */
+sekv_status sekv_profile_enable(sekv_ctx* ctx, int32_t enable);
+sekv_status sekv_profile_read(sekv_ctx* ctx, double* route_ms, int64_t* route_launches, double* attend_ms,
+                              int64_t* attend_launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SEKV_H */

@@ -1,0 +1,157 @@
+"""Shared test plumbing: seeded inputs -> oracle cache -> thresholds ->
+oracle route/decode results, and the same oracle-built cache marshalled into
+the library's ABI arrays.  Every expected value here comes from ``oracle``;
+the library only ever receives copies of oracle-built data as inputs."""
+from __future__ import annotations
+
+import dataclasses
+import sys
+import time
+
+import numpy as np
+
+import oracle as O
+from hierarchical_kv_cache_sekv_amd import synth
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def log(msg):
+    print(f"[harness {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@dataclasses.dataclass
+class Prepared:
+    w: synth.Workload
+    x: synth.Inputs
+    cache: O.OracleCache
+    theta: np.ndarray            # [B][Hq] f32
+    decisions: list              # [step][b] -> [Hq][n_seg] bool
+    steps: list                  # which query steps are used
+
+    @property
+    def group(self):
+        return self.w.group
+
+
+def scores(cache, q_b, b, group):
+    """Canonical float32 scores of all heads of sequence b: [Hq][n_seg]."""
+    Hq = q_b.shape[0]
+    parts = [O.route_scores(q_b[kv * group:(kv + 1) * group], cache.rho[b][kv]) for kv in range(Hq // group)]
+    return np.concatenate(parts, axis=0)
+
+
+def prepare(w, steps, *, full_rank=False, theta_mode="calibrated", calib_steps=None, frac=None,
+            drop_kv=False) -> Prepared:
+    t0 = time.time()
+    n_steps = max(steps) + 1
+    if calib_steps is not None:
+        n_steps = max(n_steps, calib_steps)
+    x = synth.make_inputs(w, n_steps=n_steps, full_rank_unit_gates=full_rank)
+    log(f"{w.name}: inputs {time.time() - t0:.1f}s")
+    cache = O.build_cache(x.k, x.v, x.surprisal, x.boundary_thr, x.route_proj, x.rank_req, x.gate,
+                          n_sink=w.n_sink, n_recent=w.n_recent, lo=w.min_span, hi=w.max_span, dtype=w.dtype)
+    log(f"{w.name}: oracle cache {time.time() - t0:.1f}s, n_seg={[cache.n_seg(b) for b in range(w.batch)]}")
+    B, Hq, G = w.batch, w.n_q_heads, w.group
+    theta = np.empty((B, Hq), np.float32)
+    for b in range(B):
+        if theta_mode == "plus_inf":
+            theta[b] = np.inf
+        elif theta_mode == "minus_inf":
+            theta[b] = -np.inf
+        else:
+            cs = range(calib_steps if calib_steps is not None else n_steps)
+            z = np.stack([scores(cache, x.q[st, b], b, G) for st in cs])
+            f = float(x.expand_frac[b]) if frac is None else frac
+            theta[b] = synth.calibrate_theta(z, f, G)
+    decisions = []
+    for st in steps:
+        decisions.append([scores(cache, x.q[st, b], b, G) > theta[b][:, None] for b in range(B)])
+    log(f"{w.name}: thresholds and decisions {time.time() - t0:.1f}s")
+    if drop_kv:
+        x.k = x.v = None
+    return Prepared(w, x, cache, theta, decisions, list(steps))
+
+
+def oracle_route(p: Prepared, si: int):
+    """Oracle route outputs of step index si in ABI layout."""
+    w = p.w
+    cap = synth.seg_capacity(w.n_ctx, w.n_sink, w.n_recent, w.min_span)
+    cnt = np.zeros((w.batch, w.n_kv_heads), np.int32)
+    lst = np.zeros((w.batch, w.n_kv_heads, cap), np.int32)
+    msk = np.zeros((w.batch, w.n_kv_heads, cap), np.uint8)
+    for b in range(w.batch):
+        lists, masks = O.compact(p.decisions[si][b], w.group)
+        for kv in range(w.n_kv_heads):
+            n = len(lists[kv])
+            cnt[b, kv] = n
+            lst[b, kv, :n] = lists[kv]
+            msk[b, kv, :n] = masks[kv]
+    return cnt, lst, msk
+
+
+def oracle_out(p: Prepared, si: int, bs=None):
+    st = p.steps[si]
+    bs = range(p.w.batch) if bs is None else bs
+    return {b: O.mixed_attention(p.cache, b, p.x.q[st, b], p.decisions[si][b], p.group) for b in bs}
+
+
+def realized_fraction(p: Prepared, si: int) -> float:
+    w = p.w
+    tot = exp = 0
+    for b in range(w.batch):
+        d = p.decisions[si][b]
+        for kv in range(w.n_kv_heads):
+            u = d[kv * w.group:(kv + 1) * w.group].any(axis=0)
+            tot += u.size
+            exp += int(u.sum())
+    return exp / max(tot, 1)
+
+
+class Device:
+    """The oracle cache marshalled to the library (torch tensors on cuda:0)."""
+
+    def __init__(self, p: Prepared, factors_on_host=None):
+        import torch
+        from hierarchical_kv_cache_sekv_amd import binding as B
+        self.B = B
+        self.p = p
+        w = p.w
+        self.cfg = B.make_config(w, factors_on_host)
+        plan = B.layout_from_segments(self.cfg, p.cache.seg_off, p.cache.rank)
+        self.cache = B.SpanCache(self.cfg, plan)
+        B.fill_cache(self.cache, p.cache)
+        self.et = self.cache.elem
+        self.theta = torch.from_numpy(p.theta).cuda()
+        self.route_out = B.RouteOut(self.cfg, self.cache.seg_cap)
+        self.route_ws = B.route_workspace(self.cache)
+        self.dec_ws = B.DecodeWorkspace(self.cache)
+        self.out = torch.zeros((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+
+    def q(self, si):
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(self.p.x.q[self.p.steps[si]])).to(self.et).cuda()
+
+    def route(self, ctx, si):
+        self.B.route(ctx, self.cache, self.q(si), self.theta, self.route_out, self.route_ws)
+
+    def decode(self, ctx, si, copy_stream=None):
+        self.B.decode(ctx, self.cache, self.q(si), self.route_out, self.out, self.dec_ws, copy_stream=copy_stream)
+
+    def route_numpy(self):
+        import torch
+        torch.cuda.synchronize()
+        return (self.route_out.exp_count.cpu().numpy(), self.route_out.exp_list.cpu().numpy(),
+                self.route_out.exp_mask.cpu().numpy())
+
+
+def compare_route(dev: Device, ref):
+    cnt, lst, msk = dev.route_numpy()
+    rc, rl, rm = ref
+    assert np.array_equal(cnt, rc), (cnt, rc)
+    for b in range(cnt.shape[0]):
+        for kv in range(cnt.shape[1]):
+            n = int(rc[b, kv])
+            assert np.array_equal(lst[b, kv, :n], rl[b, kv, :n]), (b, kv)
+            assert np.array_equal(msk[b, kv, :n], rm[b, kv, :n]), (b, kv)

@@ -1,0 +1,150 @@
+"""Host-side checks of libsekv that need no GPU: the library loads and exports
+every symbol include/sekv.h declares, and the host-only planning call
+(segmentation + pool layout) agrees exactly with the oracle and rejects bad
+arguments with the documented status.  No GPU work is launched here."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from hierarchical_kv_cache_sekv_amd import binding as B
+from hierarchical_kv_cache_sekv_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "sekv.h")).read()
+    declared = set(re.findall(r"^\s*(?:sekv_status|void|const char\*|size_t)\s+(sekv_[a-z_]+)\s*\(", hdr, re.M))
+    assert declared == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(B.LIB, name), name
+
+
+def _cfg(**kw):
+    w = synth.workload(1, **kw)
+    return w, B.make_config(w)
+
+
+def test_capacities_match_formula():
+    for T, a, rr, lo in [(2048, 4, 64, 4), (131072, 4, 256, 8), (10, 1, 1, 1), (7, 3, 4, 2)]:
+        w, cfg = _cfg(n_ctx=T, n_sink=a, n_recent=rr, min_span=lo, max_span=max(lo, 8))
+        assert B.capacities(cfg) == (synth.seg_capacity(T, a, rr, lo), synth.full_capacity(T, a, rr, lo))
+
+
+def test_plan_matches_oracle_segmentation_golden(golden_dir):
+    import json
+    g = json.load(open(os.path.join(golden_dir, "segmentation_hand.json")))
+    for c in g["cases"]:
+        s = np.full(c["T"], 0.5, np.float32)
+        s[c["high"]] = 2.0
+        w, cfg = _cfg(n_ctx=c["T"], n_sink=c["n_sink"], n_recent=c["n_recent"], min_span=c["lo"], max_span=c["hi"])
+        if c["n_sink"] + c["n_recent"] < 1:
+            continue
+        cap, _ = B.capacities(cfg)
+        p = B.plan_spans(cfg, s[None], np.array([c["thr"]], np.float32), np.full((1, cap), 3, np.int32))
+        n = int(p.n_seg[0])
+        assert p.seg_off[0, :n + 1].tolist() == c["seg_off"], c["name"]
+        assert int(p.n_full[0]) == len(c["full_res"])
+
+
+@pytest.mark.parametrize("wid", [1, 2, 4])
+def test_plan_matches_oracle_on_workload(wid):
+    w = synth.workload(wid, n_ctx=min(synth.workload(wid).n_ctx, 8192), batch=min(synth.workload(wid).batch, 3))
+    x = synth.make_inputs(w, n_steps=1)
+    cfg = B.make_config(w)
+    p = B.plan_spans(cfg, x.surprisal, x.boundary_thr, x.rank_req)
+    for b in range(w.batch):
+        so = O.segment(x.surprisal[b], float(x.boundary_thr[b]), w.n_sink, w.n_recent, w.min_span, w.max_span)
+        n = len(so) - 1
+        assert int(p.n_seg[b]) == n
+        assert p.seg_off[b, :n + 1].tolist() == so.tolist()
+        assert int(p.n_full[b]) == len(O.full_res_tokens(so, w.n_sink, w.n_ctx))
+        L = so[1:] - so[:-1] - 1
+        want_r = np.minimum(np.minimum(x.rank_req[b, :n], L), 2 * w.head_dim)
+        assert p.rank[b, :n].tolist() == want_r.tolist()
+        assert np.all(p.rank[b, n:] == 0)
+    # pool layout: blocks are contiguous, 8-element aligned, in (b, kv, span) order
+    off = 0
+    goff = 0
+    for b in range(w.batch):
+        so = p.seg_off[b]
+        for kv in range(w.n_kv_heads):
+            for i in range(int(p.n_seg[b])):
+                r = int(p.rank[b, i])
+                L = int(so[i + 1] - so[i] - 1)
+                assert p.fac_off[b, kv, i] == off and off % 8 == 0
+                assert p.sg_off[b, kv, i] == goff
+                off += L * ((r + 7) // 8 * 8) + r * 2 * w.head_dim
+                goff += 2 * r
+    assert p.fac_elems == off and p.sg_elems == goff
+
+
+def test_plan_random_small_matches_oracle():
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        T = int(rng.integers(2, 300))
+        a = int(rng.integers(0, 5))
+        rr = int(rng.integers(0, 12))
+        if a + rr < 1 or a + rr > T:
+            continue
+        lo = int(rng.integers(1, 6))
+        hi = int(rng.integers(lo, min(40, 128) + 1))
+        w, cfg = _cfg(n_ctx=T, n_sink=a, n_recent=rr, min_span=lo, max_span=hi)
+        s = rng.lognormal(0, 1, T).astype(np.float32)
+        thr = np.float32(np.quantile(s, 0.8, method="lower"))
+        cap, _ = B.capacities(cfg)
+        p = B.plan_spans(cfg, s[None], np.array([thr]), np.full((1, cap), 4, np.int32))
+        so = O.segment(s, float(thr), a, rr, lo, hi)
+        assert p.seg_off[0, :len(so)].tolist() == so.tolist()
+
+
+def _expect(status, fn):
+    with pytest.raises(B.SekvError) as ei:
+        fn()
+    assert ei.value.status == status, str(ei.value)
+    return str(ei.value)
+
+
+def test_plan_rejects_bad_arguments():
+    w, cfg = _cfg()
+    x = synth.make_inputs(w, n_steps=1)
+    cap, _ = B.capacities(cfg)
+
+    def plan(c=cfg, s=x.surprisal, t=x.boundary_thr, r=x.rank_req):
+        return B.plan_spans(c, s, t, r)
+
+    bad = B.make_config(w)
+    bad.n_q_heads, bad.n_kv_heads = 6, 4
+    assert "multiple" in _expect(B.SEKV_ESHAPE, lambda: B.capacities(bad))
+    w16 = synth.workload(1, n_q_heads=16, n_kv_heads=1)
+    assert "group size" in _expect(B.SEKV_ESHAPE, lambda: B.capacities(B.make_config(w16)))
+    bad = B.make_config(w)
+    bad.n_sink, bad.n_recent = 2000, 100
+    _expect(B.SEKV_ESHAPE, lambda: B.capacities(bad))
+    bad = B.make_config(w)
+    bad.min_span, bad.max_span = 9, 8
+    _expect(B.SEKV_EINVAL, lambda: B.capacities(bad))
+    bad = B.make_config(w)
+    bad.max_span = 129
+    _expect(B.SEKV_ESHAPE, lambda: B.capacities(bad))
+    bad = B.make_config(w)
+    bad.dtype = 7
+    _expect(B.SEKV_EINVAL, lambda: B.capacities(bad))
+    bad = B.make_config(w)
+    bad.head_dim = 96
+    _expect(B.SEKV_ESHAPE, lambda: B.capacities(bad))
+    bad = B.make_config(w)
+    bad.n_sink = bad.n_recent = 0
+    _expect(B.SEKV_EINVAL, lambda: B.capacities(bad))
+    s = x.surprisal.copy()
+    s[0, 17] = np.nan
+    assert "not finite" in _expect(B.SEKV_EINVAL, lambda: plan(s=s))
+    t = np.array([np.inf], np.float32)
+    _expect(B.SEKV_EINVAL, lambda: plan(t=t))
+    r = x.rank_req.copy()
+    r[0, 0] = 0
+    assert "rank_req" in _expect(B.SEKV_EINVAL, lambda: plan(r=r))
+    assert plan().n_seg[0] > 0

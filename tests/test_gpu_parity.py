@@ -1,0 +1,300 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Inputs are seeded (hierarchical_kv_cache_sekv_amd.synth); the span cache is
+built by the oracle and marshalled into the library's arrays, so decode parity
+does not depend on the library's own build (checked separately).  Bar: the
+expanded-span set (count, ascending list, head masks) bit-exact; outputs within
+1e-4 (float32 cache) or 2e-2 (bfloat16 cache, float32 accumulation).
+Sizes here span several tiles and ragged tails and finish in seconds; the
+full-size workloads are in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from hierarchical_kv_cache_sekv_amd import synth
+
+from _harness import TOL, Device, compare_route, log, oracle_out, oracle_route, prepare, realized_fraction
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny-f32-T2K": dict(wid=1, steps=[0, 5, 15]),
+    "bf16-d128-T4K": dict(wid=2, over=dict(n_ctx=4096), steps=[0, 1]),
+    "bf16-ragged-B3-T4K": dict(wid=4, over=dict(n_ctx=4096, batch=3), steps=[0]),
+    "bf16-g8-d64-T3000": dict(wid=2, over=dict(n_ctx=3000, n_q_heads=16, n_kv_heads=2, head_dim=64, min_span=3,
+                                               max_span=40, rank_lo=1, rank_hi=24), steps=[0, 3]),
+    "f32-g1-d128-T1500": dict(wid=1, over=dict(n_ctx=1500, n_q_heads=4, n_kv_heads=4, head_dim=128, rank_hi=20),
+                              steps=[0, 1]),
+    "bf16-g2-T2500-wide-rank": dict(wid=5, over=dict(n_ctx=2500, batch=2, n_q_heads=8, n_kv_heads=4, min_span=2,
+                                                     max_span=128, rank_lo=30, rank_hi=128, boundary_quantile=0.995),
+                                    steps=[0], frac=0.3),
+    "f32-len1-spans": dict(wid=1, over=dict(n_ctx=700, min_span=1, max_span=1), steps=[0, 1]),
+    "f32-no-spans": dict(wid=1, over=dict(n_ctx=69, n_recent=64, n_sink=4), steps=[0]),
+    "bf16-one-span": dict(wid=2, over=dict(n_ctx=300, n_recent=200, n_sink=4, min_span=8, max_span=128), steps=[0]),
+}
+
+_PREP = {}
+
+
+def _prep(name):
+    if name not in _PREP:
+        c = CASES[name]
+        w = synth.workload(c["wid"], **c.get("over", {}))
+        _PREP[name] = prepare(w, c["steps"], frac=c.get("frac"))
+    return _PREP[name]
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    assert torch.cuda.is_available()
+    c = B.Context(0)
+    yield c
+    torch.cuda.synchronize()
+    c.close()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_route_and_decode_parity(ctx, name):
+    import torch
+    p = _prep(name)
+    log(f"case {name}: n_seg={[p.cache.n_seg(b) for b in range(p.w.batch)]}")
+    dev = Device(p)
+    tol = TOL[p.w.dtype]
+    for si in range(len(p.steps)):
+        ref = oracle_route(p, si)
+        dev.route(ctx, si)
+        compare_route(dev, ref)
+        dev.route(ctx, si)                       # second run: identical bits (no races)
+        compare_route(dev, ref)
+        dev.decode(ctx, si)
+        torch.cuda.synchronize()
+        out = dev.out.cpu().numpy()
+        want = oracle_out(p, si)
+        err = max(float(np.abs(out[b] - want[b]).max()) for b in want)
+        log(f"case {name} step {p.steps[si]}: f={realized_fraction(p, si):.3f} max|err|={err:.3e} tol={tol}")
+        assert err <= tol
+        out2 = dev.out.clone()
+        dev.decode(ctx, si)
+        torch.cuda.synchronize()
+        assert torch.equal(out2, dev.out)        # deterministic
+
+
+@pytest.mark.parametrize("mode", ["plus_inf", "minus_inf"])
+def test_infinite_thresholds(ctx, mode):
+    import torch
+    w = synth.workload(2, n_ctx=3000, batch=2, rank_lo=2, rank_hi=40)
+    p = prepare(w, [0], theta_mode=mode)
+    dev = Device(p)
+    dev.route(ctx, 0)
+    cnt, lst, msk = dev.route_numpy()
+    for b in range(w.batch):
+        n = p.cache.n_seg(b)
+        if mode == "plus_inf":
+            assert np.all(cnt[b] == 0)
+        else:
+            assert np.all(cnt[b] == n)
+            assert np.array_equal(lst[b, :, :n], np.tile(np.arange(n), (w.n_kv_heads, 1)))
+            assert np.all(msk[b, :, :n] == (1 << w.group) - 1)
+    dev.decode(ctx, 0)
+    torch.cuda.synchronize()
+    out = dev.out.cpu().numpy()
+    want = oracle_out(p, 0)
+    err = max(float(np.abs(out[b] - want[b]).max()) for b in want)
+    log(f"theta {mode}: max|err|={err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_full_expansion_full_rank_equals_dense(ctx, dtype):
+    """Every span expanded at full rank with unit gates reduces to dense
+    softmax attention over the stored K/V."""
+    import torch
+    w = synth.workload(5, n_ctx=4096, batch=2, dtype=dtype)
+    p = prepare(w, [0, 1], full_rank=True, theta_mode="minus_inf")
+    dev = Device(p)
+    for si in range(2):
+        dev.route(ctx, si)
+        dev.decode(ctx, si)
+        torch.cuda.synchronize()
+        out = dev.out.cpu().numpy()
+        for b in range(w.batch):
+            dense = O.dense_attention(p.x.q[p.steps[si], b], p.x.k[b], p.x.v[b], w.group)
+            err = float(np.abs(out[b] - dense).max())
+            log(f"full expansion {dtype} b={b}: max|gpu - dense|={err:.3e}")
+            # bf16-stored factors reconstruct to ~1e-2 relative; fp32 to ~1e-6
+            assert err <= (2e-2 if dtype == "bf16" else 1e-4)
+
+
+def test_host_resident_factors_match_device_resident_bitwise(ctx):
+    import torch
+    w = synth.workload(3, n_ctx=8192)
+    p = prepare(w, [0, 1])
+    dev_d = Device(p, factors_on_host=False)
+    dev_h = Device(p, factors_on_host=True)
+    side = torch.cuda.Stream()
+    for si in range(2):
+        dev_d.route(ctx, si)
+        dev_d.decode(ctx, si)
+        dev_h.route(ctx, si)
+        dev_h.decode(ctx, si, copy_stream=side)
+        torch.cuda.synchronize()
+        assert torch.equal(dev_d.out, dev_h.out)
+        want = oracle_out(p, si)
+        out = dev_h.out.cpu().numpy()
+        assert max(float(np.abs(out[b] - want[b]).max()) for b in want) <= TOL[w.dtype]
+
+
+def test_reconstruct_matches_oracle(ctx):
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    w = synth.workload(2, n_ctx=3000, batch=2, rank_lo=1, rank_hi=40)
+    p = prepare(w, [0], frac=0.2)
+    dev = Device(p)
+    dev.route(ctx, 0)
+    tok_off, k_out, v_out = B.reconstruct(ctx, dev.cache, dev.route_out)
+    torch.cuda.synchronize()
+    cnt, lst, _ = dev.route_numpy()
+    to = tok_off.cpu().numpy()
+    K = k_out.cpu().numpy()
+    V = v_out.cpu().numpy()
+    worst = 0.0
+    for b in range(w.batch):
+        L = p.cache.span_len(b)
+        for kv in range(w.n_kv_heads):
+            n = int(cnt[b, kv])
+            assert to[b, kv, 0] == 0 and to[b, kv, n] == int(L[lst[b, kv, :n]].sum())
+            for j in range(n):
+                S = int(lst[b, kv, j])
+                kh, vh = O.reconstruct(p.cache.U[b][kv][S], p.cache.sigma[b][kv][S], p.cache.gate[b][kv][S],
+                                       p.cache.Vh[b][kv][S], w.head_dim)
+                r0 = int(to[b, kv, j])
+                worst = max(worst, float(np.abs(K[b, kv, r0:r0 + L[S]] - kh).max()),
+                            float(np.abs(V[b, kv, r0:r0 + L[S]] - vh).max()))
+    log(f"reconstruct max|err|={worst:.3e}")
+    assert worst <= 1e-4
+
+
+def test_split_invariance(ctx, monkeypatch):
+    """The result does not depend on how the memory is cut into split-K chunks."""
+    import torch
+    p = _prep("bf16-ragged-B3-T4K")
+    outs = []
+    for chunk in ("128", "512", "2048"):
+        monkeypatch.setenv("SEKV_A4_CHUNK", chunk)
+        dev = Device(p)
+        dev.route(ctx, 0)
+        dev.decode(ctx, 0)
+        torch.cuda.synchronize()
+        outs.append(dev.out.cpu().numpy())
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 1e-5
+
+
+def test_library_build_matches_oracle_build(ctx):
+    """sekv_plan_spans + sekv_build_spans against the oracle's build: offsets
+    and ranks exact; summaries and routing keys within one storage rounding;
+    factors through their invariants (orthonormality, singular values,
+    reconstruction error = tail energy)."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    for w in [synth.workload(1), synth.workload(2, n_ctx=4096, batch=2)]:
+        x = synth.make_inputs(w, n_steps=1)
+        cfg = B.make_config(w)
+        plan = B.plan_spans(cfg, x.surprisal, x.boundary_thr, x.rank_req)
+        cache = B.SpanCache(cfg, plan)
+        et = cache.elem
+        kd = torch.from_numpy(x.k).to(et).cuda()
+        vd = torch.from_numpy(x.v).to(et).cuda()
+        B.build_spans(ctx, cache, kd, vd, x.surprisal, x.route_proj, x.gate)
+        torch.cuda.synchronize()
+        oc = O.build_cache(x.k, x.v, x.surprisal, x.boundary_thr, x.route_proj, x.rank_req, x.gate,
+                           n_sink=w.n_sink, n_recent=w.n_recent, lo=w.min_span, hi=w.max_span, dtype=w.dtype)
+        rel = 2.0 ** -7 if w.dtype == "bf16" else 2.0 ** -22
+        fk = cache.full_k.float().cpu().numpy()
+        sk = cache.sum_k.float().cpu().numpy()
+        sv = cache.sum_v.float().cpu().numpy()
+        rh = cache.rho.float().cpu().numpy()
+        fac = cache.fac.float().cpu().numpy()
+        sg = cache.sg.cpu().numpy()
+        worst_recon = 0.0
+        for b in range(w.batch):
+            n = oc.n_seg(b)
+            assert int(plan.n_seg[b]) == n
+            assert plan.seg_off[b, :n + 1].tolist() == oc.seg_off[b].tolist()
+            assert plan.rank[b, :n].tolist() == oc.rank[b].tolist()
+            L = oc.span_len(b)
+            for kv in range(w.n_kv_heads):
+                nf = len(oc.full_idx[b])
+                assert np.array_equal(fk[b, kv, :nf], oc.full_k[b][kv])
+                for arr, ref in ((sk, oc.sum_k), (sv, oc.sum_v), (rh, oc.rho)):
+                    r = ref[b][kv]
+                    assert np.all(np.abs(arr[b, kv, :n] - r) <= rel * np.abs(r) + 1e-30)
+                for i in range(0, n, max(1, n // 40)):
+                    rk = int(plan.rank[b, i])
+                    rp = (rk + 7) // 8 * 8
+                    o = int(plan.fac_off[b, kv, i])
+                    U = fac[o:o + L[i] * rp].reshape(L[i], rp)[:, :rk]
+                    Vh = fac[o + L[i] * rp:o + L[i] * rp + rk * 2 * w.head_dim].reshape(rk, 2 * w.head_dim)
+                    go = int(plan.sg_off[b, kv, i])
+                    sig, gt = sg[go:go + rk], sg[go + rk:go + 2 * rk]
+                    assert np.allclose(sig, oc.sigma[b][kv][i], rtol=1e-5, atol=1e-6)
+                    assert np.array_equal(gt, oc.gate[b][kv][i].astype(np.float32))
+                    utol = 0.05 if w.dtype == "bf16" else 1e-5
+                    assert np.allclose(U.T @ U, np.eye(rk), atol=utol)
+                    assert np.allclose(Vh @ Vh.T, np.eye(rk), atol=utol)
+                    t0, t1 = oc.seg_off[b][i] + 1, oc.seg_off[b][i + 1]
+                    M = np.concatenate([x.k[b, kv, t0:t1], x.v[b, kv, t0:t1]], axis=1).astype(np.float64)
+                    R = (U * sig) @ Vh
+                    ko, vo = O.reconstruct(oc.U[b][kv][i], oc.sigma[b][kv][i], np.ones(rk), oc.Vh[b][kv][i],
+                                           w.head_dim)
+                    Ro = np.concatenate([ko, vo], axis=1)
+                    e_lib = np.linalg.norm(M - R)
+                    e_orc = np.linalg.norm(M - Ro)
+                    worst_recon = max(worst_recon, abs(e_lib - e_orc) / max(np.linalg.norm(M), 1e-30))
+        log(f"build {w.name}: worst relative reconstruction-error gap {worst_recon:.2e}")
+        assert worst_recon <= (2e-2 if w.dtype == "bf16" else 1e-5)
+
+
+def test_abi_errors_need_context(ctx):
+    """Argument checks of the GPU entry points: documented status, nothing written."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    p = _prep("tiny-f32-T2K")
+    dev = Device(p)
+    dev.route(ctx, 0)
+    torch.cuda.synchronize()
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.SekvError) as ei:
+        B.route(ctx, dev.cache, dev.q(0), dev.theta, dev.route_out, small)
+    assert ei.value.status == B.SEKV_ECAPACITY
+    sentinel = torch.full_like(dev.out, 123.0)
+    dev.out.copy_(sentinel)
+    ws = B.DecodeWorkspace(dev.cache)
+    ws.dev = ws.dev[:64]
+    with pytest.raises(B.SekvError) as ei:
+        B.decode(ctx, dev.cache, dev.q(0), dev.route_out, dev.out, ws)
+    assert ei.value.status == B.SEKV_ECAPACITY
+    torch.cuda.synchronize()
+    assert torch.equal(dev.out, sentinel)
+    # host-resident mode with pageable pools is refused
+    cfg_h = B.make_config(p.w, True)
+    st = dev.cache.struct()
+    with pytest.raises(B.SekvError) as ei:
+        import ctypes
+        B._check(B.LIB.sekv_mixed_attention_decode(ctx.handle, ctypes.byref(cfg_h), ctypes.byref(st),
+                                                   B._ptr(dev.q(0)), B._ptr(dev.route_out.exp_list),
+                                                   B._ptr(dev.route_out.exp_mask), B._ptr(dev.route_out.exp_count),
+                                                   B._ptr(dev.out), B._ptr(ws.dev), 1 << 40, None, 0, None, None))
+    assert ei.value.status == B.SEKV_EINVAL and "pinned" in str(ei.value)
+    # null query
+    with pytest.raises(B.SekvError) as ei:
+        import ctypes
+        B._check(B.LIB.sekv_route(ctx.handle, ctypes.byref(dev.cfg), ctypes.byref(st), None, B._ptr(dev.theta),
+                                  B._ptr(dev.route_out.exp_list), B._ptr(dev.route_out.exp_mask),
+                                  B._ptr(dev.route_out.exp_count), B._ptr(dev.route_ws), dev.route_ws.numel(), None))
+    assert ei.value.status == B.SEKV_EINVAL
+    torch.cuda.synchronize()
+    assert torch.equal(dev.out, sentinel)
