@@ -55,6 +55,10 @@ class Spans(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime; load it first so libsekv binds to that one
+    # instance (its DT_NEEDED libamdhip64.so.7 then resolves to the loaded copy)
+    # instead of bringing a second runtime into the process.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m hierarchical_kv_cache_sekv_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
