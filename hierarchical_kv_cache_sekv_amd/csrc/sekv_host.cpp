@@ -126,7 +126,6 @@ int default_threads() {
 
 }  // namespace
 
-constexpr int kMaxCounters = 1 << 16;
 constexpr int kRing = 3;
 constexpr size_t kRingBytes = 8u << 20;
 
@@ -137,7 +136,6 @@ struct EventPairs {
 
 struct sekv_ctx {
   int device = 0;
-  unsigned int* counters = nullptr;  // device, zeroed once, left zero by every route call
   hipEvent_t ev_list = nullptr, ev_copy = nullptr;
   hipEvent_t ev_ring[kRing] = {};
   ThreadPool* pool = nullptr;
@@ -367,10 +365,7 @@ sekv_status sekv_ctx_create(int device, sekv_ctx** out) {
   sekv_ctx* c = new (std::nothrow) sekv_ctx();
   if (!c) return fail(SEKV_ENOMEM, "cannot allocate the context");
   c->device = device;
-  hipError_t e = hipMalloc(&c->counters, sizeof(unsigned int) * kMaxCounters);
-  if (e == hipSuccess) e = hipMemset(c->counters, 0, sizeof(unsigned int) * kMaxCounters);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_list, hipEventDisableTiming);
+  hipError_t e = hipEventCreateWithFlags(&c->ev_list, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming);
   for (int i = 0; i < kRing && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->ev_ring[i], hipEventDisableTiming);
   if (e != hipSuccess) {
@@ -386,7 +381,6 @@ void sekv_ctx_destroy(sekv_ctx* c) {
   if (!c) return;
   for (hipEvent_t e : c->prof_route.ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof_attend.ev) (void)hipEventDestroy(e);
-  if (c->counters) (void)hipFree(c->counters);
   if (c->ev_list) (void)hipEventDestroy(c->ev_list);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
   for (int i = 0; i < kRing; ++i)
@@ -665,7 +659,6 @@ sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s,
   if (!q || !theta || !exp_list || !exp_mask || !exp_count || !ws) return fail(SEKV_EINVAL, "sekv_route: a pointer argument is NULL");
   if (ws_bytes < sekv_route_workspace_bytes(c, s))
     return fail(SEKV_ECAPACITY, "route workspace %zu bytes < %zu needed", ws_bytes, sekv_route_workspace_bytes(c, s));
-  if ((int64_t)c->batch * c->n_kv_heads > kMaxCounters) return fail(SEKV_ESHAPE, "too many (b, kv) groups");
   RouteArgs a{};
   a.dtype = c->dtype;
   a.B = c->batch; a.Hq = c->n_q_heads; a.Hkv = c->n_kv_heads; a.D = c->head_dim; a.seg_cap = s->seg_cap;
@@ -674,7 +667,6 @@ sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s,
   a.nblk = std::max(1, (mx + kRouteThreads - 1) / kRouteThreads);
   a.q = q; a.theta = theta; a.rho = s->rho;
   a.dmask = static_cast<uint8_t*>(ws);
-  a.counters = ctx->counters;
   a.exp_list = exp_list; a.exp_mask = exp_mask; a.exp_count = exp_count;
   HIP_OR_FAIL(hipSetDevice(ctx->device));
   HIP_OR_FAIL(prof_mark(ctx, ctx->prof_route, stream));

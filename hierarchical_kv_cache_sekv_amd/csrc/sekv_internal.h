@@ -22,7 +22,6 @@ struct RouteArgs {
   const float* theta;        // [B][Hq]
   const void* rho;           // [B][Hkv][seg_cap][D]
   uint8_t* dmask;            // [B][Hkv][seg_cap] workspace
-  unsigned int* counters;    // [B*Hkv] zero on entry, left zero on exit
   int32_t* exp_list;         // [B][Hkv][seg_cap]
   uint8_t* exp_mask;         // [B][Hkv][seg_cap]
   int32_t* exp_count;        // [B][Hkv]

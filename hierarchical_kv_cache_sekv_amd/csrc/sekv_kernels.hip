@@ -8,9 +8,10 @@
 // span, on-demand token-level reconstruction).
 //
 // Kernels
-//   route_kernel    one lane per span, the G heads of a KV group per lane:
-//                   canonical float32 score, decision bits, then the last
-//                   workgroup of each (b, kv) compacts the ascending list.
+//   route_decide_kernel   one lane per span, the G heads of a KV group per
+//                   lane: canonical float32 score and decision bits.
+//   route_compact_kernel  one workgroup per (b, kv): ascending list, head
+//                   masks and count.
 //   attend_kernel   two roles in one grid.  Role A (full-resolution entries +
 //                   size-corrected summaries) streams K/V rows with 16 lanes per
 //                   row (8 elements per lane, 16-byte loads) and keeps one
@@ -95,15 +96,19 @@ constexpr float kNegInf = -__builtin_inff();
 // Canonical score: z = 0; for i in 0..D-1: z = fl32(z + fl32(q_i * rho_i)).
 // Contraction into FMA is switched off for exactly these two operations, so
 // each product is rounded to float32 before it is added.
+//
+// Two kernels: route_decide_kernel (one lane per span, many workgroups) writes
+// the per-span head mask; route_compact_kernel (one workgroup per (b, kv))
+// turns it into the ascending list.  The kernel boundary makes the masks
+// visible across XCDs; no device-scope fence is needed inside either kernel.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a) {
+__global__ __launch_bounds__(kRouteThreads) void route_decide_kernel(const RouteArgs a) {
   __shared__ float qs[G * D];
-  __shared__ int wsum[kRouteThreads / 64];
-  __shared__ int s_last;
   const int blk = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int g = b * a.Hkv + kv;
   const int ns = a.n_seg[b];
+  if (blk * kRouteThreads >= ns) return;
   const T* q = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
   for (int i = tid; i < G * D; i += kRouteThreads) qs[i] = load1(q + i);
   float th[G];
@@ -112,56 +117,55 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a)
   __syncthreads();
 
   const int S = blk * kRouteThreads + tid;
-  uint32_t bits = 0;
-  if (S < ns) {
-    const T* r = static_cast<const T*>(a.rho) + ((size_t)g * a.seg_cap + S) * D;
-    float z[G];
+  if (S >= ns) return;
+  const T* r = static_cast<const T*>(a.rho) + ((size_t)g * a.seg_cap + S) * D;
+  float z[G];
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) z[gi] = 0.0f;
+  for (int gi = 0; gi < G; ++gi) z[gi] = 0.0f;
 #pragma unroll 2
-    for (int c = 0; c < D; c += 8) {
-      float rv[8];
-      load8(r + c, rv);
+  for (int c = 0; c < D; c += 8) {
+    float rv[8];
+    load8(r + c, rv);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
+      for (int gi = 0; gi < G; ++gi) {
 #pragma clang fp contract(off)
-          const float prod = qs[gi * D + c + i] * rv[i];
-          z[gi] = z[gi] + prod;
-        }
+        const float prod = qs[gi * D + c + i] * rv[i];
+        z[gi] = z[gi] + prod;
       }
     }
+  }
+  uint32_t bits = 0;
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) bits |= (z[gi] > th[gi] ? 1u : 0u) << gi;
-  }
-  if (S < a.seg_cap) a.dmask[(size_t)g * a.seg_cap + S] = (uint8_t)bits;
+  for (int gi = 0; gi < G; ++gi) bits |= (z[gi] > th[gi] ? 1u : 0u) << gi;
+  a.dmask[(size_t)g * a.seg_cap + S] = (uint8_t)bits;
+}
 
-  // Publish this block's decisions; the last block of (b, kv) to arrive compacts.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&a.counters[g], 1u);
-    s_last = (prev == (unsigned)(a.nblk - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
+// One workgroup per (b, kv).  The masks are staged in LDS by tiles with
+// coalesced loads; each thread then takes a contiguous run of spans, counts the
+// expanded ones, one block-wide exclusive scan gives its output position.
+constexpr int kCompactTile = 16384;
+__global__ __launch_bounds__(kRouteThreads) void route_compact_kernel(const RouteArgs a) {
+  __shared__ int wsum[kRouteThreads / 64];
+  __shared__ uint8_t tile[kCompactTile];
+  const int kv = blockIdx.x, b = blockIdx.y;
+  const int g = b * a.Hkv + kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ns = a.n_seg[b];
   const uint8_t* dm = a.dmask + (size_t)g * a.seg_cap;
   int32_t* lst = a.exp_list + (size_t)g * a.seg_cap;
   uint8_t* msk = a.exp_mask + (size_t)g * a.seg_cap;
   int base = 0;
-  for (int S0 = 0; S0 < ns; S0 += 4 * kRouteThreads) {
-    const int s0 = S0 + 4 * tid;
-    uint8_t m4[4];
+  for (int t0 = 0; t0 < ns; t0 += kCompactTile) {
+    const int n = min(kCompactTile, ns - t0);
+#pragma unroll 8
+    for (int i = tid; i < n; i += kRouteThreads) tile[i] = dm[t0 + i];
+    __syncthreads();
+    const int per = (n + kRouteThreads - 1) / kRouteThreads;
+    const int s0 = min(n, tid * per), s1 = min(n, s0 + per);
     int c = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m4[i] = (s0 + i < ns) ? __builtin_nontemporal_load(dm + s0 + i) : (uint8_t)0;
-      c += m4[i] != 0;
-    }
-    // block exclusive scan of c
+    for (int S = s0; S < s1; ++S) c += tile[S] != 0;
     int incl = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -178,21 +182,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a)
       total += v;
     }
     int pos = base + wbase + incl - c;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (m4[i]) {
-        lst[pos] = s0 + i;
-        msk[pos] = m4[i];
+    for (int S = s0; S < s1; ++S) {
+      const uint8_t m = tile[S];
+      if (m) {
+        lst[pos] = t0 + S;
+        msk[pos] = m;
         ++pos;
       }
     }
     base += total;
     __syncthreads();
   }
-  if (tid == 0) {
-    a.exp_count[g] = base;
-    a.counters[g] = 0u;  // ready for the next call
-  }
+  if (tid == 0) a.exp_count[g] = base;
 }
 
 // ================================================================ attention
@@ -633,34 +634,52 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttendArgs a
 }
 
 // ================================================================ combine
+// One workgroup per (b, h).  Pass 1: the maximum over partials (strided over
+// threads).  Pass 2: kCombineSplit thread groups each accumulate a strided
+// share of the partials for all D outputs; the groups are summed in LDS.
+constexpr int kCombineThreads = 256;
 template <int D, int G>
-__global__ __launch_bounds__(64) void combine_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const AttendArgs a) {
+  constexpr int SPLIT = kCombineThreads / D;   // 2 (D=128) or 4 (D=64)
+  __shared__ float red[kCombineThreads];
+  __shared__ float acc_s[SPLIT][D];
+  __shared__ float l_s[SPLIT];
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int g = b * a.Hkv + h / G, gi = h % G;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const int np = a.nch_a4 + (a.exp_count[g] + kExpChunk - 1) / kExpChunk;
   const float* ml = a.part_ml + (size_t)g * a.P_max * G * 2;
   const float* po = a.part_o + (size_t)g * a.P_max * G * D;
   float M = kNegInf;
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[(p * G + gi) * 2]);
-  M = wave_max(M);
-  constexpr int EPL = D / 64;
-  float acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  float L = 0.0f;
-  for (int p = 0; p < np; ++p) {
-    const float mp = ml[(p * G + gi) * 2];
-    if (mp == kNegInf) continue;
-    const float f = exp2f(mp - M);
-    L += f * ml[(p * G + gi) * 2 + 1];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += f * po[((size_t)p * G + gi) * D + lane + 64 * e];
+  for (int p = tid; p < np; p += kCombineThreads) M = fmaxf(M, ml[(p * G + gi) * 2]);
+  red[tid] = M;
+  __syncthreads();
+  for (int off = kCombineThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
   }
-  const float inv = 1.0f / L;
+  M = red[0];
+  const int j = tid % D, part = tid / D;
+  float acc = 0.0f, L = 0.0f;
+#pragma unroll 4
+  for (int p = part; p < np; p += SPLIT) {
+    const float mp = ml[(p * G + gi) * 2];
+    const float lp = ml[(p * G + gi) * 2 + 1];
+    const float ov = po[((size_t)p * G + gi) * D + j];
+    const float f = (mp == kNegInf) ? 0.0f : exp2f(mp - M);
+    L += f * lp;
+    acc += f * ov;
+  }
+  acc_s[part][j] = acc;
+  if (j == 0) l_s[part] = L;
+  __syncthreads();
+  if (tid < D) {
+    float o = 0.0f, Lt = 0.0f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) a.out[(size_t)bh * D + lane + 64 * e] = acc[e] * inv;
+    for (int s2 = 0; s2 < SPLIT; ++s2) { o += acc_s[s2][tid]; Lt += l_s[s2]; }
+    a.out[(size_t)bh * D + tid] = o / Lt;
+  }
 }
 
 // ================================================================ reconstruct
@@ -763,7 +782,10 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   dim3 grid(a.nblk, a.Hkv, a.B);
-  SEKV_DISPATCH(a.dtype, a.D, G, (route_kernel<TT, DD, GG><<<grid, kRouteThreads, 0, s>>>(a)));
+  SEKV_DISPATCH(a.dtype, a.D, G, (route_decide_kernel<TT, DD, GG><<<grid, kRouteThreads, 0, s>>>(a)));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  route_compact_kernel<<<dim3(a.Hkv, a.B), kRouteThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -778,7 +800,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
 
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  SEKV_DISPATCH_D(a.D, G, (combine_kernel<DD, GG><<<a.B * a.Hq, 64, 0, s>>>(a)));
+  SEKV_DISPATCH_D(a.D, G, (combine_kernel<DD, GG><<<a.B * a.Hq, kCombineThreads, 0, s>>>(a)));
   return hipGetLastError();
 }
 

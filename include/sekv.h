@@ -32,8 +32,8 @@
  *     sekv_plan_spans and sekv_build_spans (host-synchronous) and the
  *     host-resident decode (one documented host wait, see below).
  *   - One context per device.  Calls that share a context must be ordered on
- *     one stream (sekv_route keeps per-(b, KV head) completion counters in the
- *     context).
+ *     one stream (the context holds the host-resident path's events and
+ *     staging state).
  */
 #ifndef SEKV_H
 #define SEKV_H
@@ -121,7 +121,7 @@ typedef struct sekv_spans {
 
 typedef struct sekv_ctx sekv_ctx;
 
-/* Context for one GPU: completion counters, events, copy-side thread pool.
+/* Context for one GPU: events and the copy-side thread pool.
  * Errors: SEKV_EINVAL (out == NULL), SEKV_EHIP (bad device), SEKV_ENOMEM. */
 sekv_status sekv_ctx_create(int device, sekv_ctx** out);
 void sekv_ctx_destroy(sekv_ctx* ctx);
