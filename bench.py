@@ -33,15 +33,16 @@ def log(msg):
 
 
 def algorithmic_bytes(w, plan, counts, lists, e):
-    """Bytes the method must move per step (dense work it avoids excluded).
+    """Bytes the method must move per step (the dense work it avoids excluded).
 
-    Returns (route, attend, total): route = q + rho; attend = full-res K/V +
-    summaries kbar/vbar + factors of listed spans (+ q); total adds theta... as
-    the sum over sequences of Hq*d*(e+4) + per KV head (e*2d*n_full +
-    e*3d*n_seg + sum over listed spans of e*r*(L+2d) + 8r)."""
+    Per sequence: queries and outputs Hq*d*(e+4); per KV head the full-res K/V
+    e*2d*n_full, the summaries kbar, vbar and rho e*3d*n_seg, and for each
+    listed span its factors e*r*(L+2d) + 8r (sigma and gate in float32).
+    Returns per-kernel shares {route: q + rho, full: q + full-res K/V + kbar,
+    vbar, expand: q + factors} and the step total."""
     import numpy as np
     d, Hq, Hkv = w.head_dim, w.n_q_heads, w.n_kv_heads
-    route = attend = total = 0
+    route = full = expand = total = 0
     for b in range(w.batch):
         nf, ns = int(plan.n_full[b]), int(plan.n_seg[b])
         so = plan.seg_off[b]
@@ -52,10 +53,12 @@ def algorithmic_bytes(w, plan, counts, lists, e):
             c = int(counts[b, kv])
             idx = lists[b, kv, :c]
             fac += int((e * r[idx] * (L[idx] + 2 * d) + 8 * r[idx]).sum())
-        route += Hq * d * e + Hkv * ns * d * e
-        attend += Hq * d * e + Hkv * (e * 2 * d * nf + e * 2 * d * ns) + fac
+        qb = Hq * d * e
+        route += qb + Hkv * ns * d * e
+        full += qb + Hkv * e * 2 * d * (nf + ns)
+        expand += qb + fac
         total += Hq * d * (e + 4) + Hkv * (e * 2 * d * nf + e * 3 * d * ns) + fac
-    return route, attend, total
+    return {"route": route, "full": full, "expand": expand, "total": total}
 
 
 def cpu_baseline(w, x, theta, budget_s=12.0):
@@ -183,29 +186,30 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t1
     ev_ms = ev0.elapsed_time(ev1)
-    route_ms, route_n, att_ms, att_n = ctx.profile_read()
+    prof = ctx.profile_read()
     ctx.profile(False)
     ms_per_step = wall * 1e3 / args.steps
-    log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ev_ms:.2f} ms; route avg "
-        f"{route_ms / max(route_n, 1) * 1e3:.1f} us, attention avg {att_ms / max(att_n, 1) * 1e3:.1f} us")
+    kern_us = {k: (v[0] / max(v[1], 1)) * 1e3 for k, v in prof.items()}
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ev_ms:.2f} ms; per launch: " +
+        ", ".join(f"{k} {u:.1f} us" for k, u in kern_us.items()))
 
     # algorithmic bytes of the timed steps (lists realized per query step)
+    nseg_tot = sum(int(plan.n_seg[b]) for b in range(w.batch)) * w.n_kv_heads
     per_q = []
     for qi in range(Q):
         B.route(ctx, cache, qd[qi], theta_d, outs[0], rws)
         torch.cuda.synchronize()
         cnt = outs[0].exp_count.cpu().numpy()
         lst = outs[0].exp_list.cpu().numpy()
-        per_q.append(algorithmic_bytes(w, plan, cnt, lst, e) + (cnt.sum() / max(1, sum(int(plan.n_seg[b]) for b in range(w.batch)) * w.n_kv_heads),))
+        by = algorithmic_bytes(w, plan, cnt, lst, e)
+        by["frac"] = float(cnt.sum()) / max(1, nseg_tot)
+        per_q.append(by)
     idx = [(args.warmup + i) % Q for i in range(args.steps)]
-    route_b = sum(per_q[i][0] for i in idx) / args.steps
-    att_b = sum(per_q[i][1] for i in idx) / args.steps
-    tot_b = sum(per_q[i][2] for i in idx) / args.steps
-    f_real = sum(per_q[i][3] for i in idx) / args.steps
-    att_avg_s = att_ms / 1e3 / max(att_n, 1)
-    route_avg_s = route_ms / 1e3 / max(route_n, 1)
-    achieved = att_b / att_avg_s / 1e9
-    step_gbs = tot_b / (ms_per_step / 1e3) / 1e9
+    avg = {k: sum(per_q[i][k] for i in idx) / args.steps for k in per_q[0]}
+    gbs = {k: avg[k] / (kern_us[k] * 1e-6) / 1e9 for k in ("route", "full", "expand")}
+    dom = max(("full", "expand"), key=lambda k: kern_us[k])
+    names = {"full": "attend_full_kernel", "expand": "attend_expanded_kernel"}
+    step_gbs = avg["total"] / (ms_per_step / 1e3) / 1e9
     steps_per_s = 1e3 / ms_per_step
 
     base = None
@@ -229,16 +233,17 @@ def main():
         "data": "synthetic (seeded; Llama-3-8B layer shape, lognormal surprisal, rank-4 block structure)",
         "config": {"workload": w.name, "batch": w.batch, "n_ctx": w.n_ctx, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rank_range": [w.rank_lo, w.rank_hi],
-                   "expand_frac_target": args.frac, "expand_frac_realized": round(float(f_real), 4),
+                   "expand_frac_target": args.frac, "expand_frac_realized": round(float(avg["frac"]), 4),
                    "factors": "device", "layers": 1, "cache_copies_rotated": ncopy, "launch": "eager"},
         "eff_ctx_tokens_per_s": steps_per_s * w.batch * w.n_ctx,
-        "algorithmic_bytes_per_step": int(tot_b),
+        "algorithmic_bytes_per_step": int(avg["total"]),
         "step_hbm_gbs": step_gbs,
         "step_hbm_frac": step_gbs / PEAK_HBM_GBS,
-        "kernels_us": {"route": route_avg_s * 1e6, "attend": att_avg_s * 1e6},
-        "roofline": {"bound": "hbm", "kernel": "attend_kernel", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "bytes_per_launch": int(att_b)},
+        "kernels": {k: {"us_per_launch": kern_us[k], "algorithmic_bytes": int(avg[k]), "gbs": gbs[k],
+                        "hbm_frac": gbs[k] / PEAK_HBM_GBS} for k in ("route", "full", "expand")},
+        "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": gbs[dom], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gbs[dom] / PEAK_HBM_GBS, "traffic": None,
+                     "bytes_per_launch": int(avg[dom])},
         "cpu_baseline": base,
     }
     print(json.dumps(rec), flush=True)

@@ -78,8 +78,7 @@ def _load():
         "sekv_decode_host_workspace_bytes": (sz, [C, S]),
         "sekv_mixed_attention_decode": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, sz, _p, sz, _p, _p]),
         "sekv_profile_enable": (i32, [_p, i32]),
-        "sekv_profile_read": (i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64),
-                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+        "sekv_profile_read": (i32, [_p] + [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)] * 3),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -168,12 +167,12 @@ class Context:
         _check(LIB.sekv_profile_enable(self.handle, int(enable)))
 
     def profile_read(self):
-        """(route_ms_total, route_launches, attend_ms_total, attend_launches) since the last read."""
-        rm, am = ctypes.c_double(), ctypes.c_double()
-        rn, an = ctypes.c_int64(), ctypes.c_int64()
-        _check(LIB.sekv_profile_read(self.handle, ctypes.byref(rm), ctypes.byref(rn), ctypes.byref(am),
-                                     ctypes.byref(an)))
-        return rm.value, rn.value, am.value, an.value
+        """{kernel: (total_ms, launches)} for "route", "full", "expand" since the last read."""
+        ms = [ctypes.c_double() for _ in range(3)]
+        n = [ctypes.c_int64() for _ in range(3)]
+        _check(LIB.sekv_profile_read(self.handle, ctypes.byref(ms[0]), ctypes.byref(n[0]), ctypes.byref(ms[1]),
+                                     ctypes.byref(n[1]), ctypes.byref(ms[2]), ctypes.byref(n[2])))
+        return {k: (ms[i].value, n[i].value) for i, k in enumerate(("route", "full", "expand"))}
 
     def close(self):
         if self.handle:

@@ -136,11 +136,13 @@ struct EventPairs {
 
 struct sekv_ctx {
   int device = 0;
+  hipStream_t side = nullptr;        // runs the expanded-span kernel beside the full-res pass
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipEvent_t ev_list = nullptr, ev_copy = nullptr;
   hipEvent_t ev_ring[kRing] = {};
   ThreadPool* pool = nullptr;
   bool profile = false;
-  EventPairs prof_route, prof_attend;
+  EventPairs prof_route, prof_attend, prof_expand;
 };
 
 namespace {
@@ -365,7 +367,10 @@ sekv_status sekv_ctx_create(int device, sekv_ctx** out) {
   sekv_ctx* c = new (std::nothrow) sekv_ctx();
   if (!c) return fail(SEKV_ENOMEM, "cannot allocate the context");
   c->device = device;
-  hipError_t e = hipEventCreateWithFlags(&c->ev_list, hipEventDisableTiming);
+  hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_list, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming);
   for (int i = 0; i < kRing && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->ev_ring[i], hipEventDisableTiming);
   if (e != hipSuccess) {
@@ -381,6 +386,10 @@ void sekv_ctx_destroy(sekv_ctx* c) {
   if (!c) return;
   for (hipEvent_t e : c->prof_route.ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof_attend.ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->prof_expand.ev) (void)hipEventDestroy(e);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+  if (c->side) (void)hipStreamDestroy(c->side);
   if (c->ev_list) (void)hipEventDestroy(c->ev_list);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
   for (int i = 0; i < kRing; ++i)
@@ -797,9 +806,17 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   a.stage_off = nullptr;
 
   if (!c->factors_on_host) {
+    // fork: expanded spans on the side stream, full-res + summaries on the caller's
+    HIP_OR_FAIL(hipEventRecord(ctx->ev_fork, stream));
+    HIP_OR_FAIL(hipStreamWaitEvent(ctx->side, ctx->ev_fork, 0));
+    HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, ctx->side));
+    HIP_OR_FAIL(launch_attend_expanded(a, ctx->side));
+    HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, ctx->side));
+    HIP_OR_FAIL(hipEventRecord(ctx->ev_join, ctx->side));
     HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
-    HIP_OR_FAIL(launch_attend(a, stream));
+    HIP_OR_FAIL(launch_attend_full(a, stream));
     HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+    HIP_OR_FAIL(hipStreamWaitEvent(stream, ctx->ev_join, 0));
     HIP_OR_FAIL(launch_combine(a, stream));
     return SEKV_OK;
   }
@@ -820,9 +837,9 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   HIP_OR_FAIL(hipMemcpyAsync(h_list, exp_list, (size_t)BG * cap * sizeof(int32_t), hipMemcpyDeviceToHost, stream));
   HIP_OR_FAIL(hipEventRecord(ctx->ev_list, stream));
   // full-resolution + summary pass runs while the host gathers
-  AttendArgs a4 = a;
-  a4.n_a5_wg = 0;
-  HIP_OR_FAIL(launch_attend(a4, stream));
+  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+  HIP_OR_FAIL(launch_attend_full(a, stream));
+  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
   HIP_OR_FAIL(hipEventSynchronize(ctx->ev_list));
 
   // staging layout in list order
@@ -877,11 +894,12 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   HIP_OR_FAIL(hipEventRecord(ctx->ev_copy, copy_stream));
   if (copy_stream != stream) HIP_OR_FAIL(hipStreamWaitEvent(stream, ctx->ev_copy, 0));
   AttendArgs a5 = a;
-  a5.n_a4_wg = 0;
   a5.stage_off = reinterpret_cast<const int64_t*>(dws + p.off_stage_off);
   a5.stage_fac = d_stage_fac;
   a5.stage_sg = reinterpret_cast<const float*>(dws + p.off_stage_sg);
-  HIP_OR_FAIL(launch_attend(a5, stream));
+  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, stream));
+  HIP_OR_FAIL(launch_attend_expanded(a5, stream));
+  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, stream));
   HIP_OR_FAIL(launch_combine(a, stream));
   return SEKV_OK;
 }
@@ -889,15 +907,18 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
 sekv_status sekv_profile_enable(sekv_ctx* ctx, int32_t enable) {
   if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
   ctx->profile = enable != 0;
-  ctx->prof_route.used = ctx->prof_attend.used = 0;
+  ctx->prof_route.used = ctx->prof_attend.used = ctx->prof_expand.used = 0;
   return SEKV_OK;
 }
 
-sekv_status sekv_profile_read(sekv_ctx* ctx, double* route_ms, int64_t* route_n, double* attend_ms, int64_t* attend_n) {
-  if (!ctx || !route_ms || !route_n || !attend_ms || !attend_n) return fail(SEKV_EINVAL, "sekv_profile_read: NULL argument");
+sekv_status sekv_profile_read(sekv_ctx* ctx, double* route_ms, int64_t* route_n, double* full_ms, int64_t* full_n,
+                              double* expand_ms, int64_t* expand_n) {
+  if (!ctx || !route_ms || !route_n || !full_ms || !full_n || !expand_ms || !expand_n)
+    return fail(SEKV_EINVAL, "sekv_profile_read: NULL argument");
   HIP_OR_FAIL(hipSetDevice(ctx->device));
   HIP_OR_FAIL(prof_sum(ctx->prof_route, route_ms, route_n));
-  HIP_OR_FAIL(prof_sum(ctx->prof_attend, attend_ms, attend_n));
+  HIP_OR_FAIL(prof_sum(ctx->prof_attend, full_ms, full_n));
+  HIP_OR_FAIL(prof_sum(ctx->prof_expand, expand_ms, expand_n));
   return SEKV_OK;
 }
 

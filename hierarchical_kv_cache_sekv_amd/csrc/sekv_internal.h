@@ -35,8 +35,8 @@ struct AttendArgs {
   int chunk_a4;              // memory entries per full-res/summary workgroup
   int nch_a4;                // workgroups per (b, kv) for that pass
   int P_max;                 // partial slots per (b, kv)
-  int n_a5_wg;               // workgroups running the expanded-span role
-  int n_a4_wg;               // workgroups running the full-res/summary role
+  int n_a5_wg;               // workgroups of the expanded-span kernel
+  int n_a4_wg;               // workgroups of the full-res/summary kernel
   float qscale;              // log2(e) / sqrt(D)
   const void* q;
   const void* full_k; const void* full_v;
@@ -65,7 +65,8 @@ struct ReconArgs {
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
-hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_full(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s);
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s);
 hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s);
 

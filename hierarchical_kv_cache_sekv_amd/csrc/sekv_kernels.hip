@@ -12,14 +12,15 @@
 //                   lane: canonical float32 score and decision bits.
 //   route_compact_kernel  one workgroup per (b, kv): ascending list, head
 //                   masks and count.
-//   attend_kernel   two roles in one grid.  Role A (full-resolution entries +
-//                   size-corrected summaries) streams K/V rows with 16 lanes per
-//                   row (8 elements per lane, 16-byte loads) and keeps one
-//                   online-softmax state per row-subgroup.  Role E (expanded
-//                   spans) never materialises the rebuilt K/V: it applies the
-//                   factors to the query (y = sigma~ .* (Vh_K q)), scores the
-//                   tokens with U y, and applies the weights back through U and
-//                   Vh_V, which reads every factor byte once.
+//   attend_full_kernel  (role A) full-resolution entries + size-corrected
+//                   summaries: streams K/V rows with 16 lanes per row (8
+//                   elements per lane, 16-byte loads), one online-softmax state
+//                   per row subgroup.
+//   attend_expanded_kernel  (role E) expanded spans, never materialising the
+//                   rebuilt K/V: it applies the factors to the query
+//                   (y = sigma~ .* (Vh_K q)), scores the tokens with U y, and
+//                   applies the weights back through U and Vh_V, reading every
+//                   factor byte once.
 //   combine_kernel  log-sum-exp merge of all partials of a query head.
 //   recon_*         standalone token-level K/V rebuild (tests, unfused use).
 #include <hip/hip_runtime.h>
@@ -51,6 +52,52 @@ __device__ __forceinline__ void load8(const bf16raw* p, float (&f)[8]) {
 
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ float load1(const bf16raw* p) { return __uint_as_float(uint32_t(*p) << 16); }
+
+// Eight consecutive elements kept in their storage form (16 B of bf16 or 32 B
+// of float), so loads can be issued early and unpacked when used.
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16raw> { uint4 v; };
+template <> struct Vec8<float> { float4 a, b; };
+
+__device__ __forceinline__ Vec8<bf16raw> ld8(const bf16raw* p) { return {*reinterpret_cast<const uint4*>(p)}; }
+__device__ __forceinline__ Vec8<float> ld8(const float* p) {
+  return {*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+}
+__device__ __forceinline__ void st8(bf16raw* p, const Vec8<bf16raw>& x) { *reinterpret_cast<uint4*>(p) = x.v; }
+__device__ __forceinline__ void st8(float* p, const Vec8<float>& x) {
+  *reinterpret_cast<float4*>(p) = x.a;
+  *reinterpret_cast<float4*>(p + 4) = x.b;
+}
+__device__ __forceinline__ void zero8(Vec8<bf16raw>& x) { x.v = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void zero8(Vec8<float>& x) { x.a = x.b = make_float4(0, 0, 0, 0); }
+__device__ __forceinline__ void unpack(const Vec8<bf16raw>& x, float (&f)[8]) {
+  const uint4 u = x.v;
+  f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xffff0000u);
+  f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xffff0000u);
+  f[4] = __uint_as_float(u.z << 16); f[5] = __uint_as_float(u.z & 0xffff0000u);
+  f[6] = __uint_as_float(u.w << 16); f[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+__device__ __forceinline__ void unpack(const Vec8<float>& x, float (&f)[8]) {
+  f[0] = x.a.x; f[1] = x.a.y; f[2] = x.a.z; f[3] = x.a.w;
+  f[4] = x.b.x; f[5] = x.b.y; f[6] = x.b.z; f[7] = x.b.w;
+}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+// 8-term dot product of two stored vectors (bf16: four packed dot2 steps).
+__device__ __forceinline__ float dot8(const Vec8<bf16raw>& x, const Vec8<bf16raw>& y) {
+  float acc = dot2bf(x.v.x, y.v.x, 0.0f);
+  acc = dot2bf(x.v.y, y.v.y, acc);
+  acc = dot2bf(x.v.z, y.v.z, acc);
+  return dot2bf(x.v.w, y.v.w, acc);
+}
+__device__ __forceinline__ float dot8(const Vec8<float>& x, const Vec8<float>& y) {
+  float acc = x.a.x * y.a.x;
+  acc += x.a.y * y.a.y; acc += x.a.z * y.a.z; acc += x.a.w * y.a.w;
+  acc += x.b.x * y.b.x; acc += x.b.y * y.b.y; acc += x.b.z * y.b.z; acc += x.b.w * y.b.w;
+  return acc;
+}
 
 // ---------------------------------------------------------------- lane reductions
 template <int CTRL>
@@ -199,13 +246,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_compact_kernel(const Rout
 // ================================================================ attention
 template <int D, int G>
 struct AttnLds {
-  // role A
+  // role A: per-chunk summary masks and log2 span lengths, cross-wave merge
   static constexpr int kMaskBytes = 2048;  // >= chunk_a4 (host checks)
-  // role E, per wave: y/b buffer and p buffer, [kMaxSpan][G] floats each
-  static constexpr int kWaveFloats = 2 * kMaxSpan * G;
   static constexpr int kMergeFloats = 4 * G * (D + 2);
   static constexpr int kRoleA = kMaskBytes + kMaskBytes * 4 + kMergeFloats * 4;
-  static constexpr int kRoleE = 4 * kWaveFloats * 4 + (kMaxGroups + 1) * 4 * 2;
+  // role E, per wave: y/b [kMaxSpan][G], p [kMaxSpan][G], sigma*gate [kMaxSpan],
+  // and a slot for the span's U block
+  static constexpr int kUBytes = 4096;
+  static constexpr int kWaveBytes = (2 * kMaxSpan * G + kMaxSpan) * 4 + kUBytes;
+  static constexpr int kRoleE = 4 * kWaveBytes + (kMaxGroups + 1) * 4 * 2;
   static constexpr int kBytes = kRoleA > kRoleE ? kRoleA : kRoleE;
 };
 
@@ -322,14 +371,11 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
   }
   __syncthreads();
 
-  float qr[G][8];
+  Vec8<T> qv[G];
   const T* qb = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    load8(qb + (size_t)gi * D + part * 8, qr[gi]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qr[gi][i] *= a.qscale;
-  }
+  for (int gi = 0; gi < G; ++gi) qv[gi] = ld8(qb + (size_t)gi * D + part * 8);
+  const float qscale = a.qscale;
   float m[G], l[G], o[G][8];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
@@ -346,7 +392,7 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
   const T* sv = static_cast<const T*>(a.sum_v) + (size_t)g * a.seg_cap * D;
 
   for (int base = wb; base < we; base += RPW * U) {
-    float kf[U][8], vf[U][8];
+    Vec8<T> kr[U], vr[U];
     int ev[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -355,8 +401,8 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
       const int ec = e < we ? e : wb;  // clamp: an in-range row, weight forced to 0 below
       const T* kp = ec < nf ? fk + (size_t)ec * D : sk + (size_t)(ec - nf) * D;
       const T* vp = ec < nf ? fv + (size_t)ec * D : sv + (size_t)(ec - nf) * D;
-      load8(kp + part * 8, kf[u]);
-      load8(vp + part * 8, vf[u]);
+      kr[u] = ld8(kp + part * 8);
+      vr[u] = ld8(vp + part * 8);
     }
     float s[U][G];
 #pragma unroll
@@ -370,13 +416,13 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
       }
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc += kf[u][i] * qr[gi][i];
-        acc = group_sum<LPR>(acc);
-        s[u][gi] = (e >= we || ((bits >> gi) & 1u)) ? kNegInf : acc + adj;
+        const float acc = group_sum<LPR>(dot8(kr[u], qv[gi]));
+        s[u][gi] = (e >= we || ((bits >> gi) & 1u)) ? kNegInf : acc * qscale + adj;
       }
     }
+    float vf[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) unpack(vr[u], vf[u]);
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       float mt = s[0][gi];
@@ -403,15 +449,20 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
 }
 
 // Role E: each wave takes work items of up to kExpChunk listed spans of one
-// (b, kv); a wave keeps one online-softmax state per head of the group.
+// (b, kv); a wave keeps one online-softmax state per head of the group.  Per
+// span, every load (the first 8*RPW rank rows of Vh, key and value parts, the
+// U block and sigma/gate) is issued before any of it is used, so a span costs
+// one memory round trip; U is staged in LDS for the two passes over it.
 template <typename T, int D, int G>
 __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
-  constexpr int LPR = D / 8, RPW = 64 / LPR, UK = 4;
+  using L_ = AttnLds<D, G>;
+  constexpr int LPR = D / 8, RPW = 64 / LPR, UK = 8;
+  constexpr int RREG = UK * RPW;                      // rank rows per register pass
+  constexpr int UCAP = L_::kUBytes / (int)sizeof(T);  // U elements that fit the LDS slot
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane / LPR, part = lane % LPR;
   const int BG = a.B * a.Hkv;
-  int* pre = reinterpret_cast<int*>(lds + 4 * AttnLds<D, G>::kWaveFloats * 4);  // [BG+1] chunk prefix
-  // chunk prefix over (b, kv): nch = ceil(count / kExpChunk)
+  int* pre = reinterpret_cast<int*>(lds + 4 * L_::kWaveBytes);  // [BG+1] chunk prefix
   {
     int* tmp = pre + (kMaxGroups + 1);
     for (int i = tid; i < BG; i += kAttnThreads) tmp[i] = (a.exp_count[i] + kExpChunk - 1) / kExpChunk;
@@ -435,13 +486,17 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
     __syncthreads();
   }
   const int total = pre[BG];
-  float* yb = reinterpret_cast<float*>(lds) + wave * AttnLds<D, G>::kWaveFloats;  // [kMaxSpan][G]
-  float* pb = yb + kMaxSpan * G;                                                   // [kMaxSpan][G]
+  char* wl = lds + wave * L_::kWaveBytes;
+  float* yb = reinterpret_cast<float*>(wl);   // [kMaxSpan][G]: y, later b
+  float* pb = yb + kMaxSpan * G;              // [kMaxSpan][G]: softmax weights
+  float* stl = pb + kMaxSpan * G;             // [kMaxSpan]: sigma * gate
+  T* ub = reinterpret_cast<T*>(stl + kMaxSpan);
   const int nwaves = a.n_a5_wg * 4;
   const bool staged = a.stage_off != nullptr;
+  const float qscale = a.qscale;
 
   for (int c = wg * 4 + wave; c < total; c += nwaves) {
-    int lo = 0, hi = BG;  // find g with pre[g] <= c < pre[g+1]
+    int lo = 0, hi = BG;  // g with pre[g] <= c < pre[g+1]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (pre[mid] <= c) lo = mid; else hi = mid;
@@ -451,14 +506,10 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
     const int cnt = a.exp_count[g];
     const int j0 = lc * kExpChunk, j1 = min(cnt, j0 + kExpChunk);
 
-    float qr[G][8];
+    Vec8<T> qv[G];
     const T* qb = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      load8(qb + (size_t)gi * D + part * 8, qr[gi]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qr[gi][i] *= a.qscale;
-    }
+    for (int gi = 0; gi < G; ++gi) qv[gi] = ld8(qb + (size_t)gi * D + part * 8);
     float m[G], l[G], o[G][8];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
@@ -484,31 +535,76 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
         sgp = a.sg + a.sg_off[(size_t)g * a.seg_cap + S];
       }
       const T* Vb = Ub + (size_t)L * rp;
+      const int nU = L * rp;
+      const bool u_lds = nU <= UCAP;
 
-      // step 1: y[k][gi] = sigma_k * gate_k * (Vh_K[k] . q_gi)   (q carries the softmax scale)
-      for (int k0 = 0; k0 < r; k0 += RPW * UK) {
-        float vk[UK][8];
+      // ---- issue the loads step 1 needs: key-part rank rows, U block, sigma/gate
+      Vec8<T> vk[UK];
 #pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const int k = min(k0 + u * RPW + sub, r - 1);
-          load8(Vb + (size_t)k * 2 * D + part * 8, vk[u]);
-        }
+      for (int u = 0; u < UK; ++u) {
+        const int k = u * RPW + sub;
+        if (k < r) vk[u] = ld8(Vb + (size_t)k * 2 * D + part * 8);
+        else zero8(vk[u]);
+      }
+      Vec8<T> ureg[2];
 #pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const int k = k0 + u * RPW + sub;
-          const float st = (k < r) ? sgp[k] * sgp[r + k] : 0.0f;
+      for (int i = 0; i < 2; ++i) {
+        const int piece = lane + 64 * i;
+        if (u_lds && piece * 8 < nU) ureg[i] = ld8(Ub + piece * 8);
+      }
+      const float st0 = lane < r ? sgp[lane] * sgp[r + lane] : 0.0f;
+      const float st1 = lane + 64 < r ? sgp[lane + 64] * sgp[r + lane + 64] : 0.0f;
+      // ---- stage U and sigma*gate in LDS
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int piece = lane + 64 * i;
+        if (u_lds && piece * 8 < nU) st8(ub + piece * 8, ureg[i]);
+      }
+      for (int piece = lane + 128; u_lds && piece * 8 < nU; piece += 64) st8(ub + piece * 8, ld8(Ub + piece * 8));
+      if (lane < r) stl[lane] = st0;
+      if (lane + 64 < r) stl[lane + 64] = st1;
+      wave_lds_sync();
+      // ---- step 1: y[k][gi] = sigma_k gate_k (Vh_K[k] . q_gi) * log2(e)/sqrt(d)
+#pragma unroll
+      for (int u = 0; u < UK; ++u) {
+        if (u * RPW < r) {
+          const int k = u * RPW + sub;
 #pragma unroll
           for (int gi = 0; gi < G; ++gi) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc += vk[u][i] * qr[gi][i];
-            acc = group_sum<LPR>(acc);
-            if (part == 0 && k < r) yb[k * G + gi] = acc * st;
+            const float acc = group_sum<LPR>(dot8(vk[u], qv[gi]));
+            if (part == 0 && k < r) yb[k * G + gi] = acc * qscale * stl[k];
           }
         }
       }
+      for (int k0 = RREG; k0 < r; k0 += RREG) {  // ranks beyond the register pass
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const int k = k0 + u * RPW + sub;
+          if (k < r) vk[u] = ld8(Vb + (size_t)k * 2 * D + part * 8);
+          else zero8(vk[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          if (k0 + u * RPW < r) {
+            const int k = k0 + u * RPW + sub;
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+              const float acc = group_sum<LPR>(dot8(vk[u], qv[gi]));
+              if (part == 0 && k < r) yb[k * G + gi] = acc * qscale * stl[k];
+            }
+          }
+        }
+      }
+      // value-part rank rows: issued now, consumed in step 5 (latency overlaps steps 2-4)
+      Vec8<T> vv[UK];
+#pragma unroll
+      for (int u = 0; u < UK; ++u) {
+        const int k = u * RPW + sub;
+        if (k < r) vv[u] = ld8(Vb + (size_t)k * 2 * D + D + part * 8);
+        else zero8(vv[u]);
+      }
       wave_lds_sync();
-      // step 2: token scores s_t = U[t] . y  (two tokens per lane at most)
+      // ---- step 2: token scores s_t = U[t] . y
       float s[2][G];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -519,9 +615,10 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
           float acc[G];
 #pragma unroll
           for (int gi = 0; gi < G; ++gi) acc[gi] = 0.0f;
+          const T* urow = u_lds ? ub + t * rp : Ub + (size_t)t * rp;
           for (int k8 = 0; k8 < rp; k8 += 8) {
             float u8[8];
-            load8(Ub + (size_t)t * rp + k8, u8);
+            unpack(ld8(urow + k8), u8);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               if (k8 + i < r) {
@@ -534,8 +631,7 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
           for (int gi = 0; gi < G; ++gi) s[tt][gi] = ((bits >> gi) & 1u) ? acc[gi] : kNegInf;
         }
       }
-      wave_lds_sync();
-      // step 3: online softmax over the span's tokens
+      // ---- step 3: online softmax over the span's tokens
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         const float ms = wave_max(fmaxf(s[0][gi], s[1][gi]));
@@ -554,7 +650,7 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
         if (lane + 64 < L) pb[(lane + 64) * G + gi] = p1;
       }
       wave_lds_sync();
-      // step 4: a[k] = sum_t U[t][k] p_t, then b[k] = sigma_k * gate_k * a[k]  (into yb)
+      // ---- step 4: a[k] = sum_t U[t][k] p_t, b[k] = sigma_k gate_k a[k]  (into yb)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int k = lane + 64 * kk;
@@ -562,34 +658,54 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
           float acc[G];
 #pragma unroll
           for (int gi = 0; gi < G; ++gi) acc[gi] = 0.0f;
+          const T* ucol = (u_lds ? ub : Ub) + k;
+#pragma unroll 4
           for (int t = 0; t < L; ++t) {
-            const float u = load1(Ub + (size_t)t * rp + k);
+            const float u = load1(ucol + (size_t)t * rp);
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) acc[gi] += u * pb[t * G + gi];
           }
-          const float st = sgp[k] * sgp[r + k];
+          const float st = kk == 0 ? st0 : st1;
 #pragma unroll
           for (int gi = 0; gi < G; ++gi) yb[k * G + gi] = acc[gi] * st;
         }
       }
       wave_lds_sync();
-      // step 5: o += Vh_V^T b
-      for (int k0 = 0; k0 < r; k0 += RPW * UK) {
-        float vv[UK][8];
+      // ---- step 5: o += Vh_V^T b
 #pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const int k = min(k0 + u * RPW + sub, r - 1);
-          load8(Vb + (size_t)k * 2 * D + D + part * 8, vv[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const int k = k0 + u * RPW + sub;
+      for (int u = 0; u < UK; ++u) {
+        if (u * RPW < r) {
+          const int k = u * RPW + sub;
           if (k < r) {
+            float v8[8];
+            unpack(vv[u], v8);
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) {
               const float bk = yb[k * G + gi];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) o[gi][i] += bk * vv[u][i];
+              for (int i = 0; i < 8; ++i) o[gi][i] += bk * v8[i];
+            }
+          }
+        }
+      }
+      for (int k0 = RREG; k0 < r; k0 += RREG) {
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const int k = k0 + u * RPW + sub;
+          if (k < r) vv[u] = ld8(Vb + (size_t)k * 2 * D + D + part * 8);
+          else zero8(vv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+          const int k = k0 + u * RPW + sub;
+          if (k0 + u * RPW < r && k < r) {
+            float v8[8];
+            unpack(vv[u], v8);
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+              const float bk = yb[k * G + gi];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) o[gi][i] += bk * v8[i];
             }
           }
         }
@@ -625,12 +741,18 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
   }
 }
 
+// Full-resolution + summary pass (role A) and expanded-span pass (role E) are
+// separate kernels so each gets its own register budget; the host runs them
+// concurrently on two streams.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttnThreads) void attend_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(kAttnThreads) void attend_full_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
-  const int blk = blockIdx.x;
-  if (blk < a.n_a5_wg) role_expanded<T, D, G>(a, blk, lds);
-  else role_full_summary<T, D, G>(a, blk - a.n_a5_wg, lds);
+  role_full_summary<T, D, G>(a, blockIdx.x, lds);
+}
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kAttnThreads) void attend_expanded_kernel(const AttendArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  role_expanded<T, D, G>(a, blockIdx.x, lds);
 }
 
 // ================================================================ combine
@@ -789,12 +911,19 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+hipError_t launch_attend_full(const AttendArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const int nblk = a.n_a5_wg + a.n_a4_wg;
-  if (nblk == 0) return hipSuccess;
+  if (a.n_a4_wg == 0) return hipSuccess;
   SEKV_DISPATCH(a.dtype, a.D, G,
-                (attend_kernel<TT, DD, GG><<<nblk, kAttnThreads, AttnLds<DD, GG>::kBytes, s>>>(a)));
+                (attend_full_kernel<TT, DD, GG><<<a.n_a4_wg, kAttnThreads, AttnLds<DD, GG>::kRoleA, s>>>(a)));
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  if (a.n_a5_wg == 0) return hipSuccess;
+  SEKV_DISPATCH(a.dtype, a.D, G,
+                (attend_expanded_kernel<TT, DD, GG><<<a.n_a5_wg, kAttnThreads, AttnLds<DD, GG>::kRoleE, s>>>(a)));
   return hipGetLastError();
 }
 

@@ -121,7 +121,8 @@ typedef struct sekv_spans {
 
 typedef struct sekv_ctx sekv_ctx;
 
-/* Context for one GPU: events and the copy-side thread pool.
+/* Context for one GPU: a side stream for the expanded-span kernel, events and
+ * the copy-side thread pool.
  * Errors: SEKV_EINVAL (out == NULL), SEKV_EHIP (bad device), SEKV_ENOMEM. */
 sekv_status sekv_ctx_create(int device, sekv_ctx** out);
 void sekv_ctx_destroy(sekv_ctx* ctx);
@@ -241,15 +242,16 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* cfg, c
 
 /*
  * Measurement hook.  While enabled, sekv_route and sekv_mixed_attention_decode
- * record a timing-event pair on the caller's stream around their main kernel
- * (route kernel; attention kernel, both roles) so a benchmark can read the
- * kernels' own durations.  sekv_profile_read waits for the recorded events,
+ * record a timing-event pair around each of their main kernels, on the stream
+ * the kernel runs on: the route kernels; the full-resolution + summary kernel;
+ * the expanded-span kernel (on the context's side stream in the
+ * device-resident mode).  sekv_profile_read waits for the recorded events,
  * returns the summed milliseconds and launch counts since the last read, and
  * resets them.  Errors: SEKV_EINVAL (NULL ctx/outputs), SEKV_EHIP.
  */
 sekv_status sekv_profile_enable(sekv_ctx* ctx, int32_t enable);
-sekv_status sekv_profile_read(sekv_ctx* ctx, double* route_ms, int64_t* route_launches, double* attend_ms,
-                              int64_t* attend_launches);
+sekv_status sekv_profile_read(sekv_ctx* ctx, double* route_ms, int64_t* route_launches, double* full_ms,
+                              int64_t* full_launches, double* expand_ms, int64_t* expand_launches);
 
 #ifdef __cplusplus
 }
