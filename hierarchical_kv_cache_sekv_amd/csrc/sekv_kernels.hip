@@ -449,14 +449,65 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
 }
 
 // Role E: each wave takes work items of up to kExpChunk listed spans of one
-// (b, kv); a wave keeps one online-softmax state per head of the group.  Per
-// span, every load (the first 8*RPW rank rows of Vh, key and value parts, the
-// U block and sigma/gate) is issued before any of it is used, so a span costs
-// one memory round trip; U is staged in LDS for the two passes over it.
+// (b, kv); a wave keeps one online-softmax state per head of the group.
+// Latency hiding: the metadata of the item's spans is fetched once, one lane
+// per span; the key-part rank rows, U block and sigma*gate of span i+1 are
+// issued into the registers step 1 of span i has just released, so they are
+// in flight while steps 2-5 of span i run; the value-part rows of span i are
+// issued after its step 1.  U is staged in LDS for the two passes over it.
+template <typename T>
+struct SpanMeta {
+  int L, r, rp;
+  uint32_t bits;
+  const T* U;
+  const float* sg;
+};
+
+__device__ __forceinline__ int64_t readlane64(int64_t x, int i) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), i);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(x & 0xffffffff), i);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <typename T>
+__device__ __forceinline__ SpanMeta<T> span_meta(int i, int mL, int mr, int mbits, int64_t mfo, int64_t mgo,
+                                                 const T* fac_base, const float* sg_base) {
+  SpanMeta<T> sm;
+  sm.L = __builtin_amdgcn_readlane(mL, i);
+  sm.r = __builtin_amdgcn_readlane(mr, i);
+  sm.rp = (sm.r + 7) & ~7;
+  sm.bits = (uint32_t)__builtin_amdgcn_readlane(mbits, i);
+  sm.U = fac_base + readlane64(mfo, i);
+  sm.sg = sg_base + readlane64(mgo, i);
+  return sm;
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void issue_span_loads(const SpanMeta<T>& sm, int sub, int part, int lane, int ucap,
+                                                 Vec8<T> (&vk)[4], Vec8<T> (&ureg)[2], float& st0, float& st1) {
+  constexpr int RPW = 64 / (D / 8);
+  const T* Vb = sm.U + (size_t)sm.L * sm.rp;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int k = u * RPW + sub;
+    if (k < sm.r) vk[u] = ld8(Vb + (size_t)k * 2 * D + part * 8);
+    else zero8(vk[u]);
+  }
+  const int nU = sm.L * sm.rp;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int piece = lane + 64 * i;
+    if (nU <= ucap && piece * 8 < nU) ureg[i] = ld8(sm.U + piece * 8);
+    else zero8(ureg[i]);
+  }
+  st0 = lane < sm.r ? sm.sg[lane] * sm.sg[sm.r + lane] : 0.0f;
+  st1 = lane + 64 < sm.r ? sm.sg[lane + 64] * sm.sg[sm.r + lane + 64] : 0.0f;
+}
+
 template <typename T, int D, int G>
 __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
   using L_ = AttnLds<D, G>;
-  constexpr int LPR = D / 8, RPW = 64 / LPR, UK = 8;
+  constexpr int LPR = D / 8, RPW = 64 / LPR, UK = 4;
   constexpr int RREG = UK * RPW;                      // rank rows per register pass
   constexpr int UCAP = L_::kUBytes / (int)sizeof(T);  // U elements that fit the LDS slot
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -504,8 +555,31 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
     const int g = lo, lc = c - pre[g];
     const int b = g / a.Hkv, kv = g % a.Hkv;
     const int cnt = a.exp_count[g];
-    const int j0 = lc * kExpChunk, j1 = min(cnt, j0 + kExpChunk);
+    const int j0 = lc * kExpChunk, n = min(cnt, j0 + kExpChunk) - j0;
 
+    // metadata of the item's spans, lane i holds span j0 + i
+    const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
+    int mS = 0, mbits = 0, mL = 1, mr = 1;
+    int64_t mfo = 0, mgo = 0;
+    if (lane < n) {
+      mS = a.exp_list[(size_t)g * a.seg_cap + j0 + lane];
+      mbits = a.exp_mask[(size_t)g * a.seg_cap + j0 + lane];
+      if (staged) {
+        const int64_t* st = a.stage_off + ((size_t)g * a.seg_cap + j0 + lane) * 2;
+        mfo = st[0];
+        mgo = st[1];
+      }
+    }
+    if (lane < n) {
+      mL = so[mS + 1] - so[mS] - 1;
+      mr = a.rank[(size_t)b * a.seg_cap + mS];
+      if (!staged) {
+        mfo = a.fac_off[(size_t)g * a.seg_cap + mS];
+        mgo = a.sg_off[(size_t)g * a.seg_cap + mS];
+      }
+    }
+    const T* fac_base = staged ? static_cast<const T*>(a.stage_fac) : static_cast<const T*>(a.fac);
+    const float* sg_base = staged ? a.stage_sg : a.sg;
     Vec8<T> qv[G];
     const T* qb = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
 #pragma unroll
@@ -517,52 +591,30 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[gi][i] = 0.0f;
     }
-    const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
-    for (int j = j0; j < j1; ++j) {
-      const int S = a.exp_list[(size_t)g * a.seg_cap + j];
-      const uint32_t bits = a.exp_mask[(size_t)g * a.seg_cap + j];
-      const int L = so[S + 1] - so[S] - 1;
-      const int r = a.rank[(size_t)b * a.seg_cap + S];
-      const int rp = (r + 7) & ~7;
-      const T* Ub;
-      const float* sgp;
-      if (staged) {
-        const int64_t* st = a.stage_off + ((size_t)g * a.seg_cap + j) * 2;
-        Ub = static_cast<const T*>(a.stage_fac) + st[0];
-        sgp = a.stage_sg + st[1];
-      } else {
-        Ub = static_cast<const T*>(a.fac) + a.fac_off[(size_t)g * a.seg_cap + S];
-        sgp = a.sg + a.sg_off[(size_t)g * a.seg_cap + S];
-      }
+
+    Vec8<T> vk[UK], ureg[2];
+    float st0, st1;
+    SpanMeta<T> cur = span_meta<T>(0, mL, mr, mbits, mfo, mgo, fac_base, sg_base);
+    issue_span_loads<T, D, G>(cur, sub, part, lane, UCAP, vk, ureg, st0, st1);
+    for (int i = 0; i < n; ++i) {
+      const int L = cur.L, r = cur.r, rp = cur.rp;
+      const uint32_t bits = cur.bits;
+      const T* Ub = cur.U;
       const T* Vb = Ub + (size_t)L * rp;
       const int nU = L * rp;
       const bool u_lds = nU <= UCAP;
-
-      // ---- issue the loads step 1 needs: key-part rank rows, U block, sigma/gate
-      Vec8<T> vk[UK];
+      // ---- stage U and sigma*gate of this span in LDS
+      if (u_lds) {
 #pragma unroll
-      for (int u = 0; u < UK; ++u) {
-        const int k = u * RPW + sub;
-        if (k < r) vk[u] = ld8(Vb + (size_t)k * 2 * D + part * 8);
-        else zero8(vk[u]);
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int piece = lane + 64 * q2;
+          if (piece * 8 < nU) st8(ub + piece * 8, ureg[q2]);
+        }
+        for (int piece = lane + 128; piece * 8 < nU; piece += 64) st8(ub + piece * 8, ld8(Ub + piece * 8));
       }
-      Vec8<T> ureg[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int piece = lane + 64 * i;
-        if (u_lds && piece * 8 < nU) ureg[i] = ld8(Ub + piece * 8);
-      }
-      const float st0 = lane < r ? sgp[lane] * sgp[r + lane] : 0.0f;
-      const float st1 = lane + 64 < r ? sgp[lane + 64] * sgp[r + lane + 64] : 0.0f;
-      // ---- stage U and sigma*gate in LDS
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int piece = lane + 64 * i;
-        if (u_lds && piece * 8 < nU) st8(ub + piece * 8, ureg[i]);
-      }
-      for (int piece = lane + 128; u_lds && piece * 8 < nU; piece += 64) st8(ub + piece * 8, ld8(Ub + piece * 8));
-      if (lane < r) stl[lane] = st0;
-      if (lane + 64 < r) stl[lane + 64] = st1;
+      const float cst0 = st0, cst1 = st1;
+      if (lane < r) stl[lane] = cst0;
+      if (lane + 64 < r) stl[lane + 64] = cst1;
       wave_lds_sync();
       // ---- step 1: y[k][gi] = sigma_k gate_k (Vh_K[k] . q_gi) * log2(e)/sqrt(d)
 #pragma unroll
@@ -595,13 +647,17 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
           }
         }
       }
-      // value-part rank rows: issued now, consumed in step 5 (latency overlaps steps 2-4)
+      // value-part rank rows of this span, then the next span's key rows, U, sigma*gate
       Vec8<T> vv[UK];
 #pragma unroll
       for (int u = 0; u < UK; ++u) {
         const int k = u * RPW + sub;
         if (k < r) vv[u] = ld8(Vb + (size_t)k * 2 * D + D + part * 8);
         else zero8(vv[u]);
+      }
+      if (i + 1 < n) {
+        cur = span_meta<T>(i + 1, mL, mr, mbits, mfo, mgo, fac_base, sg_base);
+        issue_span_loads<T, D, G>(cur, sub, part, lane, UCAP, vk, ureg, st0, st1);
       }
       wave_lds_sync();
       // ---- step 2: token scores s_t = U[t] . y
@@ -615,15 +671,15 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
           float acc[G];
 #pragma unroll
           for (int gi = 0; gi < G; ++gi) acc[gi] = 0.0f;
-          const T* urow = u_lds ? ub + t * rp : Ub + (size_t)t * rp;
           for (int k8 = 0; k8 < rp; k8 += 8) {
             float u8[8];
-            unpack(ld8(urow + k8), u8);
+            if (u_lds) unpack(ld8(ub + t * rp + k8), u8);
+            else unpack(ld8(Ub + (size_t)t * rp + k8), u8);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              if (k8 + i < r) {
+            for (int e = 0; e < 8; ++e) {
+              if (k8 + e < r) {
 #pragma unroll
-                for (int gi = 0; gi < G; ++gi) acc[gi] += u8[i] * yb[(k8 + i) * G + gi];
+                for (int gi = 0; gi < G; ++gi) acc[gi] += u8[e] * yb[(k8 + e) * G + gi];
               }
             }
           }
@@ -643,7 +699,7 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
           p1 = exp2f(s[1][gi] - mn);
           l[gi] = l[gi] * alpha + wave_sum(p0 + p1);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) o[gi][i] *= alpha;
+          for (int e = 0; e < 8; ++e) o[gi][e] *= alpha;
           m[gi] = mn;
         }
         if (lane < L) pb[lane * G + gi] = p0;
@@ -658,14 +714,22 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
           float acc[G];
 #pragma unroll
           for (int gi = 0; gi < G; ++gi) acc[gi] = 0.0f;
-          const T* ucol = (u_lds ? ub : Ub) + k;
+          if (u_lds) {
 #pragma unroll 4
-          for (int t = 0; t < L; ++t) {
-            const float u = load1(ucol + (size_t)t * rp);
+            for (int t = 0; t < L; ++t) {
+              const float u = load1(ub + t * rp + k);
 #pragma unroll
-            for (int gi = 0; gi < G; ++gi) acc[gi] += u * pb[t * G + gi];
+              for (int gi = 0; gi < G; ++gi) acc[gi] += u * pb[t * G + gi];
+            }
+          } else {
+#pragma unroll 4
+            for (int t = 0; t < L; ++t) {
+              const float u = load1(Ub + (size_t)t * rp + k);
+#pragma unroll
+              for (int gi = 0; gi < G; ++gi) acc[gi] += u * pb[t * G + gi];
+            }
           }
-          const float st = kk == 0 ? st0 : st1;
+          const float st = kk == 0 ? cst0 : cst1;
 #pragma unroll
           for (int gi = 0; gi < G; ++gi) yb[k * G + gi] = acc[gi] * st;
         }
@@ -683,7 +747,7 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
             for (int gi = 0; gi < G; ++gi) {
               const float bk = yb[k * G + gi];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) o[gi][i] += bk * v8[i];
+              for (int e = 0; e < 8; ++e) o[gi][e] += bk * v8[e];
             }
           }
         }
@@ -705,7 +769,7 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
             for (int gi = 0; gi < G; ++gi) {
               const float bk = yb[k * G + gi];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) o[gi][i] += bk * v8[i];
+              for (int e = 0; e < 8; ++e) o[gi][e] += bk * v8[e];
             }
           }
         }
@@ -716,11 +780,11 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
 #pragma unroll
     for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float ov = o[gi][i];
+      for (int e = 0; e < 8; ++e) {
+        float ov = o[gi][e];
 #pragma unroll
         for (int off = LPR; off < 64; off <<= 1) ov += __shfl_xor(ov, off);
-        o[gi][i] = ov;
+        o[gi][e] = ov;
       }
     const int slot = a.nch_a4 + lc;
     float* pml = a.part_ml + ((size_t)g * a.P_max + slot) * G * 2;
@@ -729,7 +793,7 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
 #pragma unroll
       for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) po[gi * D + part * 8 + i] = o[gi][i];
+        for (int e = 0; e < 8; ++e) po[gi * D + part * 8 + e] = o[gi][e];
     }
     if (lane < G) {
       float mv = m[0], lv = l[0];
