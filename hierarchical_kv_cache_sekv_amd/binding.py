@@ -14,7 +14,7 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsekv.so")
+LIB_PATH = os.environ.get("SEKV_LIB") or os.path.join(_HERE, "libsekv.so")  # SEKV_LIB: load another build
 
 SEKV_OK, SEKV_EINVAL, SEKV_ESHAPE, SEKV_ECAPACITY, SEKV_EHIP, SEKV_ENOMEM = range(6)
 SEKV_F32, SEKV_BF16 = 0, 1

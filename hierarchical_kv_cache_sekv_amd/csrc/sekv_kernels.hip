@@ -130,11 +130,12 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// LDS written and read by different lanes of the same wave.
+// LDS written and read by different lanes of the same wave.  The LDS unit
+// executes one wave's ds instructions in order, so only the compiler must be
+// kept from reordering; no wait on outstanding global loads is wanted here.
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  asm volatile("" ::: "memory");
 }
 
 constexpr float kNegInf = -__builtin_inff();
@@ -482,26 +483,44 @@ __device__ __forceinline__ SpanMeta<T> span_meta(int i, int mL, int mr, int mbit
   return sm;
 }
 
+// Every load here is unconditional with a clamped, in-range address (rank rows
+// past r repeat row r-1, U pieces past the block repeat its last piece): a
+// predicated load whose value is used inside the branch would force a wait on
+// all loads in flight.  Lanes past r are masked where the values are used.
 template <typename T, int D, int G>
 __device__ __forceinline__ void issue_span_loads(const SpanMeta<T>& sm, int sub, int part, int lane, int ucap,
-                                                 Vec8<T> (&vk)[4], Vec8<T> (&ureg)[2], float& st0, float& st1) {
+                                                 Vec8<T> (&vk)[4], Vec8<T> (&ureg)[2], float (&sgr)[4]) {
   constexpr int RPW = 64 / (D / 8);
+  const int r1 = sm.r - 1;
+  sgr[0] = sm.sg[min(lane, r1)];
+  sgr[1] = sm.sg[sm.r + min(lane, r1)];
+  sgr[2] = sm.sg[min(lane + 64, r1)];
+  sgr[3] = sm.sg[sm.r + min(lane + 64, r1)];
+  const int nU = min(sm.L, ucap / sm.rp) * sm.rp;  // first token tile of U
+  const int lastp = nU / 8 - 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) ureg[i] = ld8(sm.U + min(lane + 64 * i, lastp) * 8);
   const T* Vb = sm.U + (size_t)sm.L * sm.rp;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int k = u * RPW + sub;
-    if (k < sm.r) vk[u] = ld8(Vb + (size_t)k * 2 * D + part * 8);
-    else zero8(vk[u]);
-  }
-  const int nU = sm.L * sm.rp;
+  for (int u = 0; u < 4; ++u) vk[u] = ld8(Vb + (size_t)min(u * RPW + sub, r1) * 2 * D + part * 8);
+}
+
+// The first token tile of U and sigma*gate of a span go to LDS once its loads
+// have landed.
+template <typename T>
+__device__ __forceinline__ void stage_span(const SpanMeta<T>& sm, int lane, int ucap, const Vec8<T> (&ureg)[2],
+                                           const float (&sgr)[4], T* ub, float* stl, float& c0, float& c1) {
+  const int nU = min(sm.L, ucap / sm.rp) * sm.rp;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int piece = lane + 64 * i;
-    if (nU <= ucap && piece * 8 < nU) ureg[i] = ld8(sm.U + piece * 8);
-    else zero8(ureg[i]);
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const int piece = lane + 64 * q2;
+    if (piece * 8 < nU) st8(ub + piece * 8, ureg[q2]);
   }
-  st0 = lane < sm.r ? sm.sg[lane] * sm.sg[sm.r + lane] : 0.0f;
-  st1 = lane + 64 < sm.r ? sm.sg[lane + 64] * sm.sg[sm.r + lane + 64] : 0.0f;
+  for (int piece = lane + 128; piece * 8 < nU; piece += 64) st8(ub + piece * 8, ld8(sm.U + piece * 8));
+  c0 = lane < sm.r ? sgr[0] * sgr[1] : 0.0f;
+  c1 = lane + 64 < sm.r ? sgr[2] * sgr[3] : 0.0f;
+  if (lane < sm.r) stl[lane] = c0;
+  if (lane + 64 < sm.r) stl[lane + 64] = c1;
 }
 
 template <typename T, int D, int G>
@@ -559,25 +578,20 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
 
     // metadata of the item's spans, lane i holds span j0 + i
     const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
-    int mS = 0, mbits = 0, mL = 1, mr = 1;
-    int64_t mfo = 0, mgo = 0;
-    if (lane < n) {
-      mS = a.exp_list[(size_t)g * a.seg_cap + j0 + lane];
-      mbits = a.exp_mask[(size_t)g * a.seg_cap + j0 + lane];
-      if (staged) {
-        const int64_t* st = a.stage_off + ((size_t)g * a.seg_cap + j0 + lane) * 2;
-        mfo = st[0];
-        mgo = st[1];
-      }
+    const int jl = j0 + min(lane, n - 1);
+    const int mS = a.exp_list[(size_t)g * a.seg_cap + jl];
+    const int mbits = a.exp_mask[(size_t)g * a.seg_cap + jl];
+    int64_t mfo, mgo;
+    if (staged) {
+      const int64_t* st = a.stage_off + ((size_t)g * a.seg_cap + jl) * 2;
+      mfo = st[0];
+      mgo = st[1];
+    } else {
+      mfo = a.fac_off[(size_t)g * a.seg_cap + mS];
+      mgo = a.sg_off[(size_t)g * a.seg_cap + mS];
     }
-    if (lane < n) {
-      mL = so[mS + 1] - so[mS] - 1;
-      mr = a.rank[(size_t)b * a.seg_cap + mS];
-      if (!staged) {
-        mfo = a.fac_off[(size_t)g * a.seg_cap + mS];
-        mgo = a.sg_off[(size_t)g * a.seg_cap + mS];
-      }
-    }
+    const int mL = so[mS + 1] - so[mS] - 1;
+    const int mr = a.rank[(size_t)b * a.seg_cap + mS];
     const T* fac_base = staged ? static_cast<const T*>(a.stage_fac) : static_cast<const T*>(a.fac);
     const float* sg_base = staged ? a.stage_sg : a.sg;
     Vec8<T> qv[G];
@@ -593,29 +607,20 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
     }
 
     Vec8<T> vk[UK], ureg[2];
-    float st0, st1;
+    float sgr[4];
     SpanMeta<T> cur = span_meta<T>(0, mL, mr, mbits, mfo, mgo, fac_base, sg_base);
-    issue_span_loads<T, D, G>(cur, sub, part, lane, UCAP, vk, ureg, st0, st1);
+    issue_span_loads<T, D, G>(cur, sub, part, lane, UCAP, vk, ureg, sgr);
+    // span i+1 is staged at the end of span i, so no load is pending across
+    // the loop back-edge.
+    float cst0, cst1;
+    stage_span<T>(cur, lane, UCAP, ureg, sgr, ub, stl, cst0, cst1);
+    wave_lds_sync();
     for (int i = 0; i < n; ++i) {
       const int L = cur.L, r = cur.r, rp = cur.rp;
       const uint32_t bits = cur.bits;
       const T* Ub = cur.U;
       const T* Vb = Ub + (size_t)L * rp;
-      const int nU = L * rp;
-      const bool u_lds = nU <= UCAP;
-      // ---- stage U and sigma*gate of this span in LDS
-      if (u_lds) {
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          const int piece = lane + 64 * q2;
-          if (piece * 8 < nU) st8(ub + piece * 8, ureg[q2]);
-        }
-        for (int piece = lane + 128; piece * 8 < nU; piece += 64) st8(ub + piece * 8, ld8(Ub + piece * 8));
-      }
-      const float cst0 = st0, cst1 = st1;
-      if (lane < r) stl[lane] = cst0;
-      if (lane + 64 < r) stl[lane + 64] = cst1;
-      wave_lds_sync();
+      const int TT = min(L, UCAP / rp);  // tokens per U tile held in LDS
       // ---- step 1: y[k][gi] = sigma_k gate_k (Vh_K[k] . q_gi) * log2(e)/sqrt(d)
 #pragma unroll
       for (int u = 0; u < UK; ++u) {
@@ -630,11 +635,7 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
       }
       for (int k0 = RREG; k0 < r; k0 += RREG) {  // ranks beyond the register pass
 #pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const int k = k0 + u * RPW + sub;
-          if (k < r) vk[u] = ld8(Vb + (size_t)k * 2 * D + part * 8);
-          else zero8(vk[u]);
-        }
+        for (int u = 0; u < UK; ++u) vk[u] = ld8(Vb + (size_t)min(k0 + u * RPW + sub, r - 1) * 2 * D + part * 8);
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
           if (k0 + u * RPW < r) {
@@ -650,88 +651,95 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
       // value-part rank rows of this span, then the next span's key rows, U, sigma*gate
       Vec8<T> vv[UK];
 #pragma unroll
-      for (int u = 0; u < UK; ++u) {
-        const int k = u * RPW + sub;
-        if (k < r) vv[u] = ld8(Vb + (size_t)k * 2 * D + D + part * 8);
-        else zero8(vv[u]);
-      }
-      if (i + 1 < n) {
-        cur = span_meta<T>(i + 1, mL, mr, mbits, mfo, mgo, fac_base, sg_base);
-        issue_span_loads<T, D, G>(cur, sub, part, lane, UCAP, vk, ureg, st0, st1);
-      }
+      for (int u = 0; u < UK; ++u) vv[u] = ld8(Vb + (size_t)min(u * RPW + sub, r - 1) * 2 * D + D + part * 8);
+      // (unconditional: the last span re-issues its own loads, which keeps the
+      // load state the same on every path)
+      const SpanMeta<T> nxt = span_meta<T>(min(i + 1, n - 1), mL, mr, mbits, mfo, mgo, fac_base, sg_base);
+      issue_span_loads<T, D, G>(nxt, sub, part, lane, UCAP, vk, ureg, sgr);
       wave_lds_sync();
-      // ---- step 2: token scores s_t = U[t] . y
-      float s[2][G];
+      // ---- steps 2-4 over token tiles of U (one tile unless L*rp exceeds the slot)
+      float am[2][G];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int t = lane + 64 * tt;
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) s[tt][gi] = kNegInf;
-        if (t < L) {
-          float acc[G];
+        for (int gi = 0; gi < G; ++gi) am[kk][gi] = 0.0f;
+      for (int t0 = 0; t0 < L; t0 += TT) {
+        const int tn = min(TT, L - t0);
+        if (t0 > 0) {
+          for (int piece = lane; piece * 8 < tn * rp; piece += 64)
+            st8(ub + piece * 8, ld8(Ub + (size_t)t0 * rp + piece * 8));
+          wave_lds_sync();
+        }
+        // step 2: token scores s_t = U[t] . y
+        float s[2][G];
 #pragma unroll
-          for (int gi = 0; gi < G; ++gi) acc[gi] = 0.0f;
-          for (int k8 = 0; k8 < rp; k8 += 8) {
-            float u8[8];
-            if (u_lds) unpack(ld8(ub + t * rp + k8), u8);
-            else unpack(ld8(Ub + (size_t)t * rp + k8), u8);
+        for (int tt = 0; tt < 2; ++tt) {
+          const int t = lane + 64 * tt;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              if (k8 + e < r) {
+          for (int gi = 0; gi < G; ++gi) s[tt][gi] = kNegInf;
+          if (t < tn) {
+            float acc[G];
 #pragma unroll
-                for (int gi = 0; gi < G; ++gi) acc[gi] += u8[e] * yb[(k8 + e) * G + gi];
+            for (int gi = 0; gi < G; ++gi) acc[gi] = 0.0f;
+            for (int k8 = 0; k8 < rp; k8 += 8) {
+              float u8[8];
+              unpack(ld8(ub + t * rp + k8), u8);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                if (k8 + e < r) {
+#pragma unroll
+                  for (int gi = 0; gi < G; ++gi) acc[gi] += u8[e] * yb[(k8 + e) * G + gi];
+                }
               }
             }
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) s[tt][gi] = ((bits >> gi) & 1u) ? acc[gi] : kNegInf;
           }
-#pragma unroll
-          for (int gi = 0; gi < G; ++gi) s[tt][gi] = ((bits >> gi) & 1u) ? acc[gi] : kNegInf;
         }
-      }
-      // ---- step 3: online softmax over the span's tokens
+        // step 3: online softmax; the span's partial U^T p is rescaled with o
 #pragma unroll
-      for (int gi = 0; gi < G; ++gi) {
-        const float ms = wave_max(fmaxf(s[0][gi], s[1][gi]));
-        const float mn = fmaxf(m[gi], ms);
-        float p0 = 0.0f, p1 = 0.0f;
-        if (mn != kNegInf) {
-          const float alpha = exp2f(m[gi] - mn);
-          p0 = exp2f(s[0][gi] - mn);
-          p1 = exp2f(s[1][gi] - mn);
-          l[gi] = l[gi] * alpha + wave_sum(p0 + p1);
+        for (int gi = 0; gi < G; ++gi) {
+          const float ms = wave_max(fmaxf(s[0][gi], s[1][gi]));
+          const float mn = fmaxf(m[gi], ms);
+          float p0 = 0.0f, p1 = 0.0f;
+          if (mn != kNegInf) {
+            const float alpha = exp2f(m[gi] - mn);
+            p0 = exp2f(s[0][gi] - mn);
+            p1 = exp2f(s[1][gi] - mn);
+            l[gi] = l[gi] * alpha + wave_sum(p0 + p1);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[gi][e] *= alpha;
-          m[gi] = mn;
+            for (int e = 0; e < 8; ++e) o[gi][e] *= alpha;
+            am[0][gi] *= alpha;
+            am[1][gi] *= alpha;
+            m[gi] = mn;
+          }
+          if (lane < tn) pb[lane * G + gi] = p0;
+          if (lane + 64 < tn) pb[(lane + 64) * G + gi] = p1;
         }
-        if (lane < L) pb[lane * G + gi] = p0;
-        if (lane + 64 < L) pb[(lane + 64) * G + gi] = p1;
+        wave_lds_sync();
+        // step 4: a[k] += sum_t U[t][k] p_t
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int k = lane + 64 * kk;
+          if (k < r) {
+#pragma unroll 4
+            for (int t = 0; t < tn; ++t) {
+              const float u = load1(ub + t * rp + k);
+#pragma unroll
+              for (int gi = 0; gi < G; ++gi) am[kk][gi] += u * pb[t * G + gi];
+            }
+          }
+        }
+        wave_lds_sync();
       }
-      wave_lds_sync();
-      // ---- step 4: a[k] = sum_t U[t][k] p_t, b[k] = sigma_k gate_k a[k]  (into yb)
+      // b[k] = sigma_k gate_k a[k]  (into yb)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int k = lane + 64 * kk;
         if (k < r) {
-          float acc[G];
-#pragma unroll
-          for (int gi = 0; gi < G; ++gi) acc[gi] = 0.0f;
-          if (u_lds) {
-#pragma unroll 4
-            for (int t = 0; t < L; ++t) {
-              const float u = load1(ub + t * rp + k);
-#pragma unroll
-              for (int gi = 0; gi < G; ++gi) acc[gi] += u * pb[t * G + gi];
-            }
-          } else {
-#pragma unroll 4
-            for (int t = 0; t < L; ++t) {
-              const float u = load1(Ub + (size_t)t * rp + k);
-#pragma unroll
-              for (int gi = 0; gi < G; ++gi) acc[gi] += u * pb[t * G + gi];
-            }
-          }
           const float st = kk == 0 ? cst0 : cst1;
 #pragma unroll
-          for (int gi = 0; gi < G; ++gi) yb[k * G + gi] = acc[gi] * st;
+          for (int gi = 0; gi < G; ++gi) yb[k * G + gi] = am[kk][gi] * st;
         }
       }
       wave_lds_sync();
@@ -754,11 +762,7 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
       }
       for (int k0 = RREG; k0 < r; k0 += RREG) {
 #pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const int k = k0 + u * RPW + sub;
-          if (k < r) vv[u] = ld8(Vb + (size_t)k * 2 * D + D + part * 8);
-          else zero8(vv[u]);
-        }
+        for (int u = 0; u < UK; ++u) vv[u] = ld8(Vb + (size_t)min(k0 + u * RPW + sub, r - 1) * 2 * D + D + part * 8);
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
           const int k = k0 + u * RPW + sub;
@@ -774,6 +778,9 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
           }
         }
       }
+      wave_lds_sync();
+      cur = nxt;
+      stage_span<T>(cur, lane, UCAP, ureg, sgr, ub, stl, cst0, cst1);
       wave_lds_sync();
     }
     // merge the row-subgroups of this wave (states share m, l) and write the partial
