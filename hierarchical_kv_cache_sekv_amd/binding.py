@@ -213,9 +213,9 @@ class SpanCache:
         self.fac_off = torch.from_numpy(plan.fac_off).to(dev)
         self.sg_off = torch.from_numpy(plan.sg_off).to(dev)
         self.full_k = torch.zeros((B, Hkv, self.full_cap, D), dtype=et, device=dev)
-        self.full_v = torch.zeros_like(self.full_k)
+        self.full_v = torch.zeros((B, Hkv, -(-self.full_cap // 32), D, 32), dtype=et, device=dev)
         self.sum_k = torch.zeros((B, Hkv, self.seg_cap, D), dtype=et, device=dev)
-        self.sum_v = torch.zeros_like(self.sum_k)
+        self.sum_v = torch.zeros((B, Hkv, -(-self.seg_cap // 32), D, 32), dtype=et, device=dev)
         self.rho = torch.zeros_like(self.sum_k)
         nf = max(plan.fac_elems, 8)
         ng = max(plan.sg_elems, 8)
@@ -340,6 +340,46 @@ def decode(ctx: Context, cache: SpanCache, q, route_out: RouteOut, out, ws: Deco
 
 
 # ----------------------------------------------------------------- marshalling
+def fac_block_elems(L: int, r: int, d: int) -> int:
+    """Elements of one span's factor block: U [L][rp] | Vh_K [r][d] | W_V [d][rp]."""
+    rp = (r + 7) // 8 * 8
+    return L * rp + r * d + d * rp
+
+
+def read_factors(cache: "SpanCache", b: int, kv: int, i: int):
+    """(U [L][r], sigma [r], gate [r], Vh [r][2d]) of span i from a cache's pools
+    (host copies, float64)."""
+    plan, D = cache.plan, cache.cfg.head_dim
+    so = plan.seg_off[b]
+    L = int(so[i + 1] - so[i] - 1)
+    r = int(plan.rank[b, i])
+    rp = (r + 7) // 8 * 8
+    o = int(plan.fac_off[b, kv, i])
+    fac = cache.fac[o:o + fac_block_elems(L, r, D)].float().cpu().numpy().astype(np.float64)
+    U = fac[:L * rp].reshape(L, rp)[:, :r]
+    vk = fac[L * rp:L * rp + r * D].reshape(r, D)
+    wv = fac[L * rp + r * D:].reshape(D, rp)[:, :r]
+    go = int(plan.sg_off[b, kv, i])
+    sg = cache.sg[go:go + 2 * r].float().cpu().numpy().astype(np.float64)
+    return U, sg[:r], sg[r:], np.concatenate([vk, wv.T], axis=1)
+
+
+def tile_values(rows: np.ndarray) -> np.ndarray:
+    """[..., n, d] value rows -> [..., ceil(n/32), d, 32] transposed 32-entry
+    tiles (zero padding), the layout of full_v / sum_v."""
+    *lead, n, d = rows.shape
+    nt = -(-n // 32)
+    pad = np.zeros((*lead, nt * 32, d), rows.dtype)
+    pad[..., :n, :] = rows
+    return np.ascontiguousarray(np.swapaxes(pad.reshape(*lead, nt, 32, d), -1, -2))
+
+
+def untile_values(tiles: np.ndarray, n: int) -> np.ndarray:
+    """Inverse of tile_values: [..., nt, d, 32] -> [..., n, d]."""
+    *lead, nt, d, _ = tiles.shape
+    return np.swapaxes(tiles, -1, -2).reshape(*lead, nt * 32, d)[..., :n, :]
+
+
 def fill_cache(cache: SpanCache, parts) -> None:
     """Copy span-cache contents given as plain per-sequence numpy arrays into
     the ABI layout (layout marshalling only).
@@ -381,7 +421,12 @@ def fill_cache(cache: SpanCache, parts) -> None:
                 blk = np.zeros((L, rp), np.float32)
                 blk[:, :r] = U
                 fac[o:o + L * rp] = blk.reshape(-1)
-                fac[o + L * rp:o + L * rp + r * 2 * D] = Vh.reshape(-1)
+                o += L * rp
+                fac[o:o + r * D] = Vh[:, :D].reshape(-1)             # key part [r][d]
+                o += r * D
+                wv = np.zeros((D, rp), np.float32)
+                wv[:, :r] = Vh[:, D:].T                             # value part transposed [d][rp]
+                fac[o:o + D * rp] = wv.reshape(-1)
                 go = int(plan.sg_off[b, kv, i])
                 sg[go:go + r] = parts.sigma[b][kv][i]
                 sg[go + r:go + 2 * r] = parts.gate[b][kv][i]
@@ -390,9 +435,9 @@ def fill_cache(cache: SpanCache, parts) -> None:
         dst.copy_(torch.from_numpy(src).to(et))
 
     put(cache.full_k, fk)
-    put(cache.full_v, fv)
+    put(cache.full_v, tile_values(fv))
     put(cache.sum_k, sk)
-    put(cache.sum_v, sv)
+    put(cache.sum_v, tile_values(sv))
     put(cache.rho, rh)
     cache.fac.copy_(torch.from_numpy(fac).to(et))
     cache.sg.copy_(torch.from_numpy(sg))
@@ -425,6 +470,6 @@ def layout_from_segments(cfg: Config, seg_offs, ranks) -> Plan:
                 rp = (r + 7) // 8 * 8
                 fac_off[b, kv, i] = fo
                 sg_off[b, kv, i] = go
-                fo += int(L[i]) * rp + r * 2 * D
+                fo += fac_block_elems(int(L[i]), r, D)
                 go += 2 * r
     return Plan(n_seg, n_full, seg_off, rank, fac_off, sg_off, fo, go)

@@ -177,6 +177,10 @@ namespace {
 
 int elem_size(int dtype) { return dtype == SEKV_BF16 ? 2 : 4; }
 
+// Factor block of one span: U [L][rp] | Vh_K [r][d] | W_V [d][rp] (the value
+// part of Vh transposed), rp = r rounded up to 8, padding zero.
+int64_t fac_block_elems(int L, int r, int rp, int D) { return (int64_t)L * rp + (int64_t)r * D + (int64_t)D * rp; }
+
 sekv_status check_config(const sekv_config* c) {
   if (!c) return fail(SEKV_EINVAL, "config is NULL");
   if (c->dtype != SEKV_F32 && c->dtype != SEKV_BF16) return fail(SEKV_EINVAL, "dtype %d is not SEKV_F32 or SEKV_BF16", c->dtype);
@@ -453,7 +457,7 @@ sekv_status sekv_plan_spans(const sekv_config* c, const float* surprisal, const 
           const int rp = (r + 7) & ~7;
           fac_off[o] = fo;
           sg_off[o] = go;
-          fo += (int64_t)L * rp + (int64_t)r * 2 * D;
+          fo += fac_block_elems(L, r, rp, D);
           go += 2 * r;
         } else {
           fac_off[o] = 0;
@@ -495,7 +499,7 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
         if (r < 1 || r > std::min(L, 2 * D)) return fail(SEKV_EINVAL, "rank[%d][%d] = %d outside [1, min(L=%d, 2d)]", b, i, r, L);
         if (r > gate_stride) return fail(SEKV_ESHAPE, "gate_stride %d < rank %d", gate_stride, r);
         const int rp = (r + 7) & ~7;
-        need_f = std::max<int64_t>(need_f, s->fac_off_host[o] + (int64_t)L * rp + (int64_t)r * 2 * D);
+        need_f = std::max<int64_t>(need_f, s->fac_off_host[o] + fac_block_elems(L, r, rp, D));
         need_g = std::max<int64_t>(need_g, s->sg_off_host[o] + 2 * r);
       }
   if (need_f > s->fac_elems || need_g > s->sg_elems)
@@ -509,8 +513,12 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
   HIP_OR_FAIL(hipMemcpyAsync(hv.data(), v, hv.size(), hipMemcpyDeviceToHost, stream));
   HIP_OR_FAIL(hipStreamSynchronize(stream));
 
-  std::vector<char> full_k((size_t)B * Hkv * fcap * D * es, 0), full_v(full_k.size(), 0);
-  std::vector<char> sum_k((size_t)B * Hkv * cap * D * es, 0), sum_v(sum_k.size(), 0), rho(sum_k.size(), 0);
+  const int ftiles = (fcap + 31) / 32, stiles = (cap + 31) / 32;
+  std::vector<char> full_k((size_t)B * Hkv * fcap * D * es, 0), full_v((size_t)B * Hkv * ftiles * 32 * D * es, 0);
+  std::vector<char> sum_k((size_t)B * Hkv * cap * D * es, 0), rho(sum_k.size(), 0);
+  std::vector<char> sum_v((size_t)B * Hkv * stiles * 32 * D * es, 0);
+  // value rows live in 32-entry tiles, each stored transposed: (e, j) -> ((e/32)*D + j)*32 + e%32
+  auto vt_index = [D](int64_t e, int j) { return ((e / 32) * D + j) * 32 + e % 32; };
   const bool on_host = c->factors_on_host != 0;
   std::vector<char> fac_tmp;
   std::vector<float> sg_tmp;
@@ -550,9 +558,11 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
     if (w.i0 == 0) {
       int row = 0;
       const int ns = s->n_seg_host[b];
+      char* fvb = full_v.data() + g * ftiles * 32 * D * es;
       auto copy_row = [&](int t) {
         std::memcpy(full_k.data() + (g * fcap + row) * D * es, kb + (size_t)t * D * es, (size_t)D * es);
-        std::memcpy(full_v.data() + (g * fcap + row) * D * es, vb + (size_t)t * D * es, (size_t)D * es);
+        for (int j = 0; j < D; ++j)
+          std::memcpy(fvb + vt_index(row, j) * es, vb + ((size_t)t * D + j) * es, es);
         ++row;
       };
       for (int t = 0; t < c->n_sink; ++t) copy_row(t);
@@ -586,12 +596,13 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
       nn = std::sqrt(nn);
       for (int a = 0; a < D; ++a) rh[a] = nn > 0 ? r[a] / nn : 0.0;
       const size_t srow = (g * cap + i) * D;
+      const int64_t svbase = (int64_t)g * stiles * 32 * D;
       for (int j = 0; j < D; ++j) {
         double acc = 0;
         for (int a = 0; a < D; ++a) acc += (double)P[(size_t)a * D + j] * rh[a];
         store(rho.data(), dt, (int64_t)srow + j, acc);
         store(sum_k.data(), dt, (int64_t)srow + j, kbar[j]);
-        store(sum_v.data(), dt, (int64_t)srow + j, vbar[j]);
+        store(sum_v.data(), dt, svbase + vt_index(i, j), vbar[j]);
       }
       // rank-r factors of [K_body | V_body]
       const int n2 = 2 * D;
@@ -622,13 +633,18 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
         const double sj = sig[j];
         const double inv = sj > 0 ? sgn / sj : 0.0;
         const double* wrow = M.data() + (size_t)src * n2;
-        for (int col = 0; col < n2; ++col)
-          store(fac_dst, dt, fbase + (int64_t)L * rp + (int64_t)j * n2 + col, wrow[col] * inv);
+        const int64_t kbase = fbase + (int64_t)L * rp, vbase = kbase + (int64_t)rk * D;
+        for (int col = 0; col < D; ++col) {
+          store(fac_dst, dt, kbase + (int64_t)j * D + col, wrow[col] * inv);
+          store(fac_dst, dt, vbase + (int64_t)col * rp + j, wrow[D + col] * inv);
+        }
         sg_dst[gbase + j] = (float)sj;
         sg_dst[gbase + rk + j] = gt[j];
       }
-      for (int t = 0; t < L; ++t)
-        for (int j = rk; j < rp; ++j) store(fac_dst, dt, fbase + (int64_t)t * rp + j, 0.0);
+      for (int j = rk; j < rp; ++j) {
+        for (int t = 0; t < L; ++t) store(fac_dst, dt, fbase + (int64_t)t * rp + j, 0.0);
+        for (int col = 0; col < D; ++col) store(fac_dst, dt, fbase + (int64_t)L * rp + (int64_t)rk * D + (int64_t)col * rp + j, 0.0);
+      }
     }
   });
 
@@ -715,23 +731,22 @@ void make_plan(const sekv_config* c, const sekv_spans* s, DecodePlan& p) {
   AttendArgs& a = p.a;
   a.dtype = c->dtype; a.B = B; a.Hq = c->n_q_heads; a.Hkv = Hkv; a.D = D;
   a.seg_cap = s->seg_cap; a.full_cap = s->full_cap;
-  int ntot = 1;
+  int ntiles = 1;  // 32-entry tiles of the longest (b, kv) stream: full-res tiles + summary tiles
   for (int b = 0; b < B; ++b) {
     a.n_full[b] = s->n_full_host[b];
     a.n_seg[b] = s->n_seg_host[b];
-    ntot = std::max(ntot, a.n_full[b] + a.n_seg[b]);
+    ntiles = std::max(ntiles, (a.n_full[b] + 31) / 32 + (a.n_seg[b] + 31) / 32);
   }
-  // about four role-A workgroups per compute unit, 64-row granularity
+  // about four full-res/summary workgroups per compute unit
   const int64_t target = 1024;
-  int64_t ch = ((int64_t)BG * ntot + target - 1) / target;
-  ch = (ch + 63) / 64 * 64;
-  ch = std::max<int64_t>(128, std::min<int64_t>(2048, ch));
-  if (const char* env = std::getenv("SEKV_A4_CHUNK")) {  // split-size override (invariance tests)
+  int64_t tc = ((int64_t)BG * ntiles + target - 1) / target;
+  tc = std::max<int64_t>(4, std::min<int64_t>(64, tc));
+  if (const char* env = std::getenv("SEKV_A4_CHUNK")) {  // split-size override in entries (invariance tests)
     const int64_t v = std::atoll(env);
-    if (v > 0) ch = std::max<int64_t>(64, std::min<int64_t>(2048, (v + 63) / 64 * 64));
+    if (v > 0) tc = std::max<int64_t>(1, std::min<int64_t>(64, (v + 31) / 32));
   }
-  a.chunk_a4 = (int)ch;
-  a.nch_a4 = (ntot + a.chunk_a4 - 1) / a.chunk_a4;
+  a.tiles_a4 = (int)tc;
+  a.nch_a4 = (ntiles + a.tiles_a4 - 1) / a.tiles_a4;
   a.P_max = a.nch_a4 + (s->seg_cap + kExpChunk - 1) / kExpChunk;
   const int64_t max_items = (int64_t)BG * ((s->seg_cap + kExpChunk - 1) / kExpChunk);
   a.n_a5_wg = (int)std::max<int64_t>(1, std::min<int64_t>(512, (max_items + 3) / 4));
@@ -787,7 +802,7 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   DecodePlan p;
   make_plan(c, s, p);
   if (dev_ws_bytes < p.dev_bytes) return fail(SEKV_ECAPACITY, "device workspace %zu bytes < %zu needed", dev_ws_bytes, p.dev_bytes);
-  if (p.a.chunk_a4 > 2048) return fail(SEKV_ESHAPE, "internal chunk size too large");
+  if (p.a.tiles_a4 * 32 > 2048) return fail(SEKV_ESHAPE, "internal chunk size too large");
   if (c->factors_on_host) {
     if (!host_ws) return fail(SEKV_EINVAL, "host-resident factors need a pinned host workspace");
     if (host_ws_bytes < p.host_bytes) return fail(SEKV_ECAPACITY, "host workspace %zu bytes < %zu needed", host_ws_bytes, p.host_bytes);
@@ -857,7 +872,7 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
       const int L = so[S + 1] - so[S] - 1;
       const int r = s->rank_host[(size_t)b * cap + S];
       const int rp = (r + 7) & ~7;
-      const int64_t fe = (int64_t)L * rp + (int64_t)r * 2 * D;
+      const int64_t fe = fac_block_elems(L, r, rp, D);
       const size_t o = (size_t)g * cap + S;
       ents.push_back({static_cast<const char*>(s->fac) + s->fac_off_host[o] * es, fe * es, fo});
       h_soff[((size_t)g * cap + j) * 2] = fo;

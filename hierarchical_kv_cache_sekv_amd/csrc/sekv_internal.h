@@ -32,7 +32,7 @@ struct AttendArgs {
   int B, Hq, Hkv, D, seg_cap, full_cap;
   int n_full[kMaxBatch];
   int n_seg[kMaxBatch];
-  int chunk_a4;              // memory entries per full-res/summary workgroup
+  int tiles_a4;              // 32-entry tiles per full-res/summary workgroup
   int nch_a4;                // workgroups per (b, kv) for that pass
   int P_max;                 // partial slots per (b, kv)
   int n_a5_wg;               // workgroups of the expanded-span kernel

@@ -92,6 +92,41 @@ __device__ __forceinline__ float dot8(const Vec8<bf16raw>& x, const Vec8<bf16raw
   acc = dot2bf(x.v.z, y.v.z, acc);
   return dot2bf(x.v.w, y.v.w, acc);
 }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// One MFMA accumulation over 32 contraction positions, 8 per lane class
+// (class = lane / 16): C[i][j] += sum over classes c and t < 8 of
+// A_lane(i, c)[t] * B_lane(j, c)[t], where lane 16c + i supplies row i of A and
+// lane 16c + j column j of B; lane 16c + j holds C[4c + v][j], v = 0..3.
+// bf16: one v_mfma_f32_16x16x32_bf16; float: eight v_mfma_f32_16x16x4f32.
+__device__ __forceinline__ f32x4_t mma8(const Vec8<bf16raw>& x, const Vec8<bf16raw>& y, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.v), __builtin_bit_cast(bf16x8_t, y.v),
+                                                 c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma8(const Vec8<float>& x, const Vec8<float>& y, f32x4_t c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.a.x, y.a.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.a.y, y.a.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.a.z, y.a.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.a.w, y.a.w, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.b.x, y.b.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.b.y, y.b.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.b.z, y.b.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.b.w, y.b.w, c, 0, 0, 0);
+  return c;
+}
+// Eight floats as an MFMA operand of the storage type (bf16: round to nearest even).
+__device__ __forceinline__ void pack8(const float (&p)[8], Vec8<bf16raw>& out) {
+  bf16x8_t v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (__bf16)p[i];
+  out.v = __builtin_bit_cast(uint4, v);
+}
+__device__ __forceinline__ void pack8(const float (&p)[8], Vec8<float>& out) {
+  out.a = make_float4(p[0], p[1], p[2], p[3]);
+  out.b = make_float4(p[4], p[5], p[6], p[7]);
+}
+
 __device__ __forceinline__ float dot8(const Vec8<float>& x, const Vec8<float>& y) {
   float acc = x.a.x * y.a.x;
   acc += x.a.y * y.a.y; acc += x.a.z * y.a.z; acc += x.a.w * y.a.w;
@@ -248,107 +283,42 @@ __global__ __launch_bounds__(kRouteThreads) void route_compact_kernel(const Rout
 template <int D, int G>
 struct AttnLds {
   // role A: per-chunk summary masks and log2 span lengths, cross-wave merge
-  static constexpr int kMaskBytes = 2048;  // >= chunk_a4 (host checks)
+  static constexpr int kMaskBytes = 2048;  // >= 32 * tiles_a4 (host checks)
   static constexpr int kMergeFloats = 4 * G * (D + 2);
   static constexpr int kRoleA = kMaskBytes + kMaskBytes * 4 + kMergeFloats * 4;
-  // role E, per wave: y/b [kMaxSpan][G], p [kMaxSpan][G], sigma*gate [kMaxSpan],
-  // and a slot for the span's U block
-  static constexpr int kUBytes = 4096;
-  static constexpr int kWaveBytes = (2 * kMaxSpan * G + kMaxSpan) * 4 + kUBytes;
+  // role E, per wave: one 32-token x 32-rank tile of U as float, row-major and
+  // transposed (row stride 36), y [16 heads][kMaxSpan], sigma*gate [kMaxSpan]
+  static constexpr int kTileStride = 36;
+  static constexpr int kWaveBytes = (2 * 32 * kTileStride + G * kMaxSpan + kMaxSpan) * 4;
   static constexpr int kRoleE = 4 * kWaveBytes + (kMaxGroups + 1) * 4 * 2;
   static constexpr int kBytes = kRoleA > kRoleE ? kRoleA : kRoleE;
 };
 
-template <int D, int G>
-__device__ __forceinline__ void write_partial_merged(const AttendArgs& a, int g, int slot, float (&m)[G],
-                                                     float (&l)[G], float (&o)[G][8], float* merge) {
-  // Merge the states of the row-subgroups of this wave, then of the 4 waves.
-  constexpr int LPR = D / 8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int part = lane % LPR, sub = lane / LPR;
-#pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    float M = m[gi];
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float f = (m[gi] == kNegInf) ? 0.0f : exp2f(m[gi] - M);
-    float lv = l[gi] * f;
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) lv += __shfl_xor(lv, off);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float ov = o[gi][i] * f;
-#pragma unroll
-      for (int off = LPR; off < 64; off <<= 1) ov += __shfl_xor(ov, off);
-      o[gi][i] = ov;
-    }
-    m[gi] = M;
-    l[gi] = lv;
-  }
-  float* mm = merge;                 // [4][G]
-  float* ll = merge + 4 * G;         // [4][G]
-  float* oo = merge + 8 * G;         // [4][G][D]
-  if (lane == 0) {
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) { mm[wave * G + gi] = m[gi]; ll[wave * G + gi] = l[gi]; }
-  }
-  if (sub == 0) {
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) oo[(wave * G + gi) * D + part * 8 + i] = o[gi][i];
-  }
-  __syncthreads();
-  float* pml = a.part_ml + ((size_t)g * a.P_max + slot) * G * 2;
-  float* po = a.part_o + ((size_t)g * a.P_max + slot) * G * D;
-  for (int idx = tid; idx < G * D; idx += kAttnThreads) {
-    const int gi = idx / D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * G + gi]);
-    float acc = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = mm[w * G + gi];
-      const float f = (mw == kNegInf) ? 0.0f : exp2f(mw - M);
-      acc += f * oo[(w * G + gi) * D + (idx % D)];
-    }
-    po[idx] = acc;
-  }
-  if (tid < G) {
-    const int gi = tid;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * G + gi]);
-    float L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = mm[w * G + gi];
-      L += (mw == kNegInf) ? 0.0f : exp2f(mw - M) * ll[w * G + gi];
-    }
-    pml[gi * 2] = M;
-    pml[gi * 2 + 1] = L;
-  }
-}
-
-// Role A: one workgroup = one chunk of the (b, kv) memory stream
-// [full-res entries 0..n_full) ++ [span summaries 0..n_seg).
+// Role A: one workgroup = a chunk of tiles_a4 32-entry tiles of the (b, kv)
+// memory stream [full-resolution tiles ++ summary tiles]; wave w takes tiles
+// w, w+4, ... of the chunk.  Per tile, q.K and P.V run on the matrix cores:
+//   scores  S^T[entry][head] = K rows (A operand) x q (B operand), two MFMA
+//           halves; lane 16c + h ends up holding the 8 scores of head h for
+//           entries 8c..8c+7 of the tile;
+//   output  O^T[j][head] += V^T (A operand, from the transposed value tile)
+//           x P (B operand = exactly those 8 softmax weights of the lane).
+// Each lane therefore keeps the online-softmax state of head (lane % 16) and
+// rescales only its own accumulators.
 template <typename T, int D, int G>
 __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
-  constexpr int LPR = D / 8, RPW = 64 / LPR, U = 4;
+  constexpr int NC = D / 32, NJ = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane / LPR, part = lane % LPR;
+  const int col = lane & 15, cls = lane >> 4;
   const int g = idx / a.nch_a4, chunk = idx % a.nch_a4;
   const int b = g / a.Hkv, kv = g % a.Hkv;
   const int nf = a.n_full[b], ns = a.n_seg[b];
-  const int ntot = nf + ns;
-  const int e0 = min(ntot, chunk * a.chunk_a4), e1 = min(ntot, e0 + a.chunk_a4);
-  const int S0 = max(e0, nf) - nf, S1 = max(e1, nf) - nf;
+  const int nft = (nf + 31) / 32, nst = (ns + 31) / 32;
+  const int t0 = min(nft + nst, chunk * a.tiles_a4), t1 = min(nft + nst, t0 + a.tiles_a4);
+  const int S0 = (max(t0, nft) - nft) * 32, S1 = min(ns, (max(t1, nft) - nft) * 32);
 
   uint8_t* smask = reinterpret_cast<uint8_t*>(lds);
   float* slog = reinterpret_cast<float*>(lds + AttnLds<D, G>::kMaskBytes);
   float* merge = reinterpret_cast<float*>(lds + AttnLds<D, G>::kMaskBytes * 5);
-
   const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
   for (int i = tid; i < S1 - S0; i += kAttnThreads) {
     const int S = S0 + i;
@@ -372,90 +342,156 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
   }
   __syncthreads();
 
-  Vec8<T> qv[G];
-  const T* qb = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
+  // q as the B operand: column = head (zero for columns >= G)
+  Vec8<T> qB[NC];
+  const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G + min(col, G - 1)) * D;
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi) qv[gi] = ld8(qb + (size_t)gi * D + part * 8);
+  for (int c = 0; c < NC; ++c) {
+    qB[c] = ld8(qrow + 32 * c + 8 * cls);
+    if (col >= G) zero8(qB[c]);
+  }
   const float qscale = a.qscale;
-  float m[G], l[G], o[G][8];
+  float m = kNegInf, lsum = 0.0f;
+  f32x4_t acc[NJ];
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    m[gi] = kNegInf; l[gi] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[gi][i] = 0.0f;
-  }
+  for (int jt = 0; jt < NJ; ++jt) acc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int per_wave = (a.chunk_a4 + 3) / 4;
-  const int wb = min(e1, e0 + wave * per_wave), we = min(e1, wb + per_wave);
+  const int ftiles = (a.full_cap + 31) / 32, stiles = (a.seg_cap + 31) / 32;
   const T* fk = static_cast<const T*>(a.full_k) + (size_t)g * a.full_cap * D;
-  const T* fv = static_cast<const T*>(a.full_v) + (size_t)g * a.full_cap * D;
+  const T* fvt = static_cast<const T*>(a.full_v) + (size_t)g * ftiles * 32 * D;
   const T* sk = static_cast<const T*>(a.sum_k) + (size_t)g * a.seg_cap * D;
-  const T* sv = static_cast<const T*>(a.sum_v) + (size_t)g * a.seg_cap * D;
+  const T* svt = static_cast<const T*>(a.sum_v) + (size_t)g * stiles * 32 * D;
 
-  for (int base = wb; base < we; base += RPW * U) {
-    Vec8<T> kr[U], vr[U];
-    int ev[U];
+  for (int t = t0 + wave; t < t1; t += 4) {
+    const bool summ = t >= nft;
+    const int tt = summ ? t - nft : t;
+    const int base = tt * 32;
+    const int npart = summ ? ns : nf;
+    const T* krows = summ ? sk : fk;
+    const T* vt = (summ ? svt : fvt) + (size_t)tt * 32 * D;
+    // K operands: MFMA half h, row (col) = entry 8*(col/4) + 4h + col%4 of the tile
+    Vec8<T> kop[2][NC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = base + u * RPW + sub;
-      ev[u] = e;
-      const int ec = e < we ? e : wb;  // clamp: an in-range row, weight forced to 0 below
-      const T* kp = ec < nf ? fk + (size_t)ec * D : sk + (size_t)(ec - nf) * D;
-      const T* vp = ec < nf ? fv + (size_t)ec * D : sv + (size_t)(ec - nf) * D;
-      kr[u] = ld8(kp + part * 8);
-      vr[u] = ld8(vp + part * 8);
+    for (int h = 0; h < 2; ++h) {
+      const int e = min(base + 8 * (col >> 2) + 4 * h + (col & 3), npart - 1);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kop[h][c] = ld8(krows + (size_t)e * D + 32 * c + 8 * cls);
     }
-    float s[U][G];
+    Vec8<T> vop[NJ];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = ev[u];
-      uint32_t bits = 0;
-      float adj = 0.0f;
-      if (e >= nf && e < we) {
-        bits = smask[e - nf - S0];
-        adj = slog[e - nf - S0];
-      }
+    for (int jt = 0; jt < NJ; ++jt) vop[jt] = ld8(vt + (16 * jt + col) * 32 + 8 * cls);
+    f32x4_t sc[2];
 #pragma unroll
-      for (int gi = 0; gi < G; ++gi) {
-        const float acc = group_sum<LPR>(dot8(kr[u], qv[gi]));
-        s[u][gi] = (e >= we || ((bits >> gi) & 1u)) ? kNegInf : acc * qscale + adj;
-      }
+    for (int h = 0; h < 2; ++h) {
+      sc[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sc[h] = mma8(kop[h][c], qB[c], sc[h]);
     }
-    float vf[U][8];
+    // this lane: head col, tile entries 8*cls + 4h + v
+    float sv[8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) unpack(vr[u], vf[u]);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      float mt = s[0][gi];
-#pragma unroll
-      for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][gi]);
-      const float mn = fmaxf(m[gi], mt);
-      if (mn == kNegInf) continue;
-      const float alpha = exp2f(m[gi] - mn);
-      float p[U], ps = 0.0f;
-#pragma unroll
-      for (int u = 0; u < U; ++u) { p[u] = exp2f(s[u][gi] - mn); ps += p[u]; }
-      l[gi] = l[gi] * alpha + ps;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float acc = o[gi][i] * alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc += p[u] * vf[u][i];
-        o[gi][i] = acc;
+      for (int v = 0; v < 4; ++v) {
+        const int e = base + 8 * cls + 4 * h + v;
+        float val = sc[h][v] * qscale;
+        if (e >= npart) {
+          val = kNegInf;
+        } else if (summ) {
+          const uint32_t bits = smask[e - S0];
+          val = ((bits >> col) & 1u) ? kNegInf : val + slog[e - S0];
+        }
+        sv[4 * h + v] = val;
       }
-      m[gi] = mn;
+    float mt = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    float p[8];
+    if (mn != kNegInf) {
+      const float alpha = exp2f(m - mn);
+      float ps = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { p[i] = exp2f(sv[i] - mn); ps += p[i]; }
+      lsum = lsum * alpha + ps;
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) acc[jt] *= alpha;
+      m = mn;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = 0.0f;
     }
+    Vec8<T> pB;
+    pack8(p, pB);
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) acc[jt] = mma8(vop[jt], pB, acc[jt]);
   }
-  write_partial_merged<D, G>(a, g, chunk, m, l, o, merge);
+
+  // this wave's state of head col: lsum summed over the four lane classes
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  float* mm = merge;                 // [4][G]
+  float* ll = merge + 4 * G;         // [4][G]
+  float* oo = merge + 8 * G;         // [4][G][D]
+  if (cls == 0 && col < G) {
+    mm[wave * G + col] = m;
+    ll[wave * G + col] = lsum;
+  }
+  if (col < G) {
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) oo[(wave * G + col) * D + 16 * jt + 4 * cls + v] = acc[jt][v];
+  }
+  __syncthreads();
+  float* pml = a.part_ml + ((size_t)g * a.P_max + chunk) * G * 2;
+  float* po = a.part_o + ((size_t)g * a.P_max + chunk) * G * D;
+  for (int i = tid; i < G * D; i += kAttnThreads) {
+    const int gi = i / D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * G + gi]);
+    float o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mm[w * G + gi];
+      o += (mw == kNegInf) ? 0.0f : exp2f(mw - M) * oo[(w * G + gi) * D + (i % D)];
+    }
+    po[i] = o;
+  }
+  if (tid < G) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * G + tid]);
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mm[w * G + tid];
+      L += (mw == kNegInf) ? 0.0f : exp2f(mw - M) * ll[w * G + tid];
+    }
+    pml[tid * 2] = M;
+    pml[tid * 2 + 1] = L;
+  }
 }
 
 // Role E: each wave takes work items of up to kExpChunk listed spans of one
-// (b, kv); a wave keeps one online-softmax state per head of the group.
-// Latency hiding: the metadata of the item's spans is fetched once, one lane
-// per span; the key-part rank rows, U block and sigma*gate of span i+1 are
-// issued into the registers step 1 of span i has just released, so they are
-// in flight while steps 2-5 of span i run; the value-part rows of span i are
-// issued after its step 1.  U is staged in LDS for the two passes over it.
+// (b, kv) and keeps, like role A, the online-softmax state of head (lane % 16).
+// Per span every contraction runs on the matrix cores (ranks and tokens in
+// blocks of 32; one block each for almost every span):
+//   step 1  y[k][h] = sigma_k gate_k (Vh_K[k] . q_h) / sqrt(d)   A = Vh_K rows, B = q
+//   step 2  s[t][h] = U[t] . y[:, h]                               A = U rows,    B = y
+//   step 3  online softmax over the span's tokens
+//   step 4  a[k][h] = sum_t U[t][k] p[t][h]                        A = U^T rows,  B = p
+//   step 5  o[j][h] += sum_k W_V[j][k] sigma_k gate_k a[k][h]      A = W_V rows,  B = b
+// Rows of each A operand are permuted so that lane 16c + h ends up holding the
+// 8 values (ranks or tokens 8c..8c+7) of head h that the next step takes as its
+// B operand: nothing moves between lanes from step to step.  Steps 2 and 4 run
+// in float32 (scores and weights unrounded); step 1 and 5 take the stored
+// element type (step 5's b is rounded to it).  U tiles are staged in LDS as
+// float, row-major and transposed.  The first tile, the first 32 key-part rank
+// rows and sigma/gate of span i+1 are loaded while span i is processed.
 template <typename T>
 struct SpanMeta {
   int L, r, rp;
@@ -483,56 +519,105 @@ __device__ __forceinline__ SpanMeta<T> span_meta(int i, int mL, int mr, int mbit
   return sm;
 }
 
-// Every load here is unconditional with a clamped, in-range address (rank rows
-// past r repeat row r-1, U pieces past the block repeat its last piece): a
-// predicated load whose value is used inside the branch would force a wait on
-// all loads in flight.  Lanes past r are masked where the values are used.
-template <typename T, int D, int G>
-__device__ __forceinline__ void issue_span_loads(const SpanMeta<T>& sm, int sub, int part, int lane, int ucap,
-                                                 Vec8<T> (&vk)[4], Vec8<T> (&ureg)[2], float (&sgr)[4]) {
-  constexpr int RPW = 64 / (D / 8);
+// Row of the A operand that MFMA half h gives to lane row i: the 4-row groups
+// interleave so output row 4c + v of half h is block position 8c + 4h + v.
+__device__ __forceinline__ int half_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// One 16-byte piece of U tile (tb, kb): piece p -> token p/4, ranks 8(p%4)..+8.
+// Clamped to an in-range address; pieces outside the span are zeroed when staged.
+template <typename T>
+__device__ __forceinline__ Vec8<T> ld_upiece(const SpanMeta<T>& sm, int tb, int kb, int p) {
+  const int t = min(tb * 32 + (p >> 2), sm.L - 1);
+  const int k8 = min(kb * 32 + 8 * (p & 3), sm.rp - 8);
+  return ld8(sm.U + (size_t)t * sm.rp + k8);
+}
+
+template <typename T, int NC>
+__device__ __forceinline__ void ld_vk(const SpanMeta<T>& sm, int kb, int col, int cls, int D, Vec8<T> (&vk)[2][NC]) {
+  const T* Vk = sm.U + (size_t)sm.L * sm.rp;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = min(kb * 32 + half_row(col, h), sm.r - 1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vk[h][c] = ld8(Vk + (size_t)k * D + 32 * c + 8 * cls);
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void issue_span_loads(const SpanMeta<T>& sm, int col, int cls, int lane,
+                                                 Vec8<T> (&vk)[2][D / 32], Vec8<T> (&ureg)[2], float (&sgr)[4]) {
   const int r1 = sm.r - 1;
   sgr[0] = sm.sg[min(lane, r1)];
   sgr[1] = sm.sg[sm.r + min(lane, r1)];
   sgr[2] = sm.sg[min(lane + 64, r1)];
   sgr[3] = sm.sg[sm.r + min(lane + 64, r1)];
-  const int nU = min(sm.L, ucap / sm.rp) * sm.rp;  // first token tile of U
-  const int lastp = nU / 8 - 1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) ureg[i] = ld8(sm.U + min(lane + 64 * i, lastp) * 8);
-  const T* Vb = sm.U + (size_t)sm.L * sm.rp;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) vk[u] = ld8(Vb + (size_t)min(u * RPW + sub, r1) * 2 * D + part * 8);
+  for (int i = 0; i < 2; ++i) ureg[i] = ld_upiece(sm, 0, 0, lane + 64 * i);
+  ld_vk<T, D / 32>(sm, 0, col, cls, D, vk);
 }
 
-// The first token tile of U and sigma*gate of a span go to LDS once its loads
-// have landed.
+// Stage U tile (tb, kb) from its two pieces per lane into LDS (float),
+// row-major ut[t][k] and transposed utt[k][t]; zero outside the span.
 template <typename T>
-__device__ __forceinline__ void stage_span(const SpanMeta<T>& sm, int lane, int ucap, const Vec8<T> (&ureg)[2],
-                                           const float (&sgr)[4], T* ub, float* stl, float& c0, float& c1) {
-  const int nU = min(sm.L, ucap / sm.rp) * sm.rp;
+__device__ __forceinline__ void stage_tile(const SpanMeta<T>& sm, int tb, int kb, int lane, const Vec8<T> (&ureg)[2],
+                                           float* ut, float* utt) {
+  constexpr int S = 36;
 #pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const int piece = lane + 64 * q2;
-    if (piece * 8 < nU) st8(ub + piece * 8, ureg[q2]);
+  for (int i = 0; i < 2; ++i) {
+    const int p = lane + 64 * i;
+    const int t = p >> 2, c8 = 8 * (p & 3);
+    const bool ok = tb * 32 + t < sm.L && kb * 32 + c8 < sm.rp;
+    float f[8];
+    unpack(ureg[i], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = ok ? f[e] : 0.0f;
+    *reinterpret_cast<float4*>(ut + t * S + c8) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4*>(ut + t * S + c8 + 4) = make_float4(f[4], f[5], f[6], f[7]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) utt[(c8 + e) * S + t] = f[e];
   }
-  for (int piece = lane + 128; piece * 8 < nU; piece += 64) st8(ub + piece * 8, ld8(sm.U + piece * 8));
-  c0 = lane < sm.r ? sgr[0] * sgr[1] : 0.0f;
-  c1 = lane + 64 < sm.r ? sgr[2] * sgr[3] : 0.0f;
-  if (lane < sm.r) stl[lane] = c0;
-  if (lane + 64 < sm.r) stl[lane + 64] = c1;
+}
+
+__device__ __forceinline__ Vec8<float> lds8f(const float* p) {
+  return {*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+}
+
+// Load and stage U tile (tb, kb) (synchronous; multi-block spans only).
+template <typename T>
+__device__ __forceinline__ void restage_tile(const SpanMeta<T>& sm, int tb, int kb, int lane, float* ut, float* utt) {
+  Vec8<T> up[2];
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) up[q2] = ld_upiece(sm, tb, kb, lane + 64 * q2);
+  wave_lds_sync();
+  stage_tile(sm, tb, kb, lane, up, ut, utt);
+  wave_lds_sync();
+}
+
+// Step 2 for token block tb: scores of tokens tb*32 + 8*cls + 4h + v for head
+// (lane % 16), summed over the RB rank blocks; y is read from LDS.  With
+// restage, each (tb, kb) tile is loaded first; otherwise tile (0, 0) is in LDS.
+template <typename T, int G>
+__device__ __forceinline__ void tile_scores(const SpanMeta<T>& sm, int tb, int RB, int col, int cls, int lane,
+                                            const float* yb, float* ut, float* utt, bool restage, f32x4_t (&sc)[2]) {
+  constexpr int TS = 36;
+  sc[0] = sc[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const float* yrow = yb + min(col, G - 1) * kMaxSpan;
+  for (int kb = 0; kb < RB; ++kb) {
+    if (restage) restage_tile(sm, tb, kb, lane, ut, utt);
+    const Vec8<float> yk = lds8f(yrow + kb * 32 + 8 * cls);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sc[h] = mma8(lds8f(ut + half_row(col, h) * TS + 8 * cls), yk, sc[h]);
+  }
 }
 
 template <typename T, int D, int G>
 __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
   using L_ = AttnLds<D, G>;
-  constexpr int LPR = D / 8, RPW = 64 / LPR, UK = 4;
-  constexpr int RREG = UK * RPW;                      // rank rows per register pass
-  constexpr int UCAP = L_::kUBytes / (int)sizeof(T);  // U elements that fit the LDS slot
+  constexpr int NC = D / 32, NJ = D / 16, TS = L_::kTileStride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane / LPR, part = lane % LPR;
+  const int col = lane & 15, cls = lane >> 4;
   const int BG = a.B * a.Hkv;
-  int* pre = reinterpret_cast<int*>(lds + 4 * L_::kWaveBytes);  // [BG+1] chunk prefix
+  int* pre = reinterpret_cast<int*>(lds + 4 * L_::kWaveBytes);  // [BG+1] item prefix
   {
     int* tmp = pre + (kMaxGroups + 1);
     for (int i = tid; i < BG; i += kAttnThreads) tmp[i] = (a.exp_count[i] + kExpChunk - 1) / kExpChunk;
@@ -556,11 +641,10 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
     __syncthreads();
   }
   const int total = pre[BG];
-  char* wl = lds + wave * L_::kWaveBytes;
-  float* yb = reinterpret_cast<float*>(wl);   // [kMaxSpan][G]: y, later b
-  float* pb = yb + kMaxSpan * G;              // [kMaxSpan][G]: softmax weights
-  float* stl = pb + kMaxSpan * G;             // [kMaxSpan]: sigma * gate
-  T* ub = reinterpret_cast<T*>(stl + kMaxSpan);
+  float* ut = reinterpret_cast<float*>(lds + wave * L_::kWaveBytes);  // [32][TS]
+  float* utt = ut + 32 * TS;                                           // [32][TS]
+  float* yb = utt + 32 * TS;                                           // [G][kMaxSpan]
+  float* stl = yb + G * kMaxSpan;                                      // [kMaxSpan]
   const int nwaves = a.n_a5_wg * 4;
   const bool staged = a.stage_off != nullptr;
   const float qscale = a.qscale;
@@ -594,220 +678,162 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
     const int mr = a.rank[(size_t)b * a.seg_cap + mS];
     const T* fac_base = staged ? static_cast<const T*>(a.stage_fac) : static_cast<const T*>(a.fac);
     const float* sg_base = staged ? a.stage_sg : a.sg;
-    Vec8<T> qv[G];
-    const T* qb = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) qv[gi] = ld8(qb + (size_t)gi * D + part * 8);
-    float m[G], l[G], o[G][8];
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      m[gi] = kNegInf; l[gi] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[gi][i] = 0.0f;
-    }
 
-    Vec8<T> vk[UK], ureg[2];
+    // q as the B operand of step 1: column = head (zero for columns >= G)
+    Vec8<T> qB[NC];
+    const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G + min(col, G - 1)) * D;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      qB[cc] = ld8(qrow + 32 * cc + 8 * cls);
+      if (col >= G) zero8(qB[cc]);
+    }
+    float m = kNegInf, lsum = 0.0f;
+    f32x4_t acc[NJ];
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) acc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    Vec8<T> vk[2][NC], ureg[2];
     float sgr[4];
     SpanMeta<T> cur = span_meta<T>(0, mL, mr, mbits, mfo, mgo, fac_base, sg_base);
-    issue_span_loads<T, D, G>(cur, sub, part, lane, UCAP, vk, ureg, sgr);
-    // span i+1 is staged at the end of span i, so no load is pending across
-    // the loop back-edge.
-    float cst0, cst1;
-    stage_span<T>(cur, lane, UCAP, ureg, sgr, ub, stl, cst0, cst1);
-    wave_lds_sync();
+    issue_span_loads<T, D>(cur, col, cls, lane, vk, ureg, sgr);
     for (int i = 0; i < n; ++i) {
       const int L = cur.L, r = cur.r, rp = cur.rp;
-      const uint32_t bits = cur.bits;
-      const T* Ub = cur.U;
-      const T* Vb = Ub + (size_t)L * rp;
-      const int TT = min(L, UCAP / rp);  // tokens per U tile held in LDS
-      // ---- step 1: y[k][gi] = sigma_k gate_k (Vh_K[k] . q_gi) * log2(e)/sqrt(d)
-#pragma unroll
-      for (int u = 0; u < UK; ++u) {
-        if (u * RPW < r) {
-          const int k = u * RPW + sub;
-#pragma unroll
-          for (int gi = 0; gi < G; ++gi) {
-            const float acc = group_sum<LPR>(dot8(vk[u], qv[gi]));
-            if (part == 0 && k < r) yb[k * G + gi] = acc * qscale * stl[k];
-          }
-        }
+      const int RB = (r + 31) >> 5, TB = (L + 31) >> 5;
+      const bool head_on = (cur.bits >> col) & 1u;
+      const T* Wv = cur.U + (size_t)L * rp + (size_t)r * D;
+      // ---- sigma*gate (zero past r) and the first U tile into LDS
+      {
+        const float c0 = lane < r ? sgr[0] * sgr[1] : 0.0f;
+        const float c1 = lane + 64 < r ? sgr[2] * sgr[3] : 0.0f;
+        stl[lane] = c0;
+        stl[lane + 64] = c1;
       }
-      for (int k0 = RREG; k0 < r; k0 += RREG) {  // ranks beyond the register pass
+      stage_tile(cur, 0, 0, lane, ureg, ut, utt);
+      wave_lds_sync();
+      // ---- step 1, rank blocks of 32 (block 0 was prefetched)
+      for (int kb = 0; kb < RB; ++kb) {
+        if (kb > 0) ld_vk<T, NC>(cur, kb, col, cls, D, vk);
 #pragma unroll
-        for (int u = 0; u < UK; ++u) vk[u] = ld8(Vb + (size_t)min(k0 + u * RPW + sub, r - 1) * 2 * D + part * 8);
+        for (int h = 0; h < 2; ++h) {
+          f32x4_t yc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          if (k0 + u * RPW < r) {
-            const int k = k0 + u * RPW + sub;
+          for (int cc = 0; cc < NC; ++cc) yc = mma8(vk[h][cc], qB[cc], yc);
+          if (col < G) {
 #pragma unroll
-            for (int gi = 0; gi < G; ++gi) {
-              const float acc = group_sum<LPR>(dot8(vk[u], qv[gi]));
-              if (part == 0 && k < r) yb[k * G + gi] = acc * qscale * stl[k];
+            for (int v = 0; v < 4; ++v) {
+              const int k = kb * 32 + 8 * cls + 4 * h + v;
+              yb[col * kMaxSpan + k] = yc[v] * qscale * stl[k];
             }
           }
         }
       }
-      // value-part rank rows of this span, then the next span's key rows, U, sigma*gate
-      Vec8<T> vv[UK];
+      // value-part rows (W_V, rank block 0) for step 5, then span i+1's loads
+      Vec8<T> wv[NJ];
+      {
+        const int k8 = min(8 * cls, rp - 8);
 #pragma unroll
-      for (int u = 0; u < UK; ++u) vv[u] = ld8(Vb + (size_t)min(u * RPW + sub, r - 1) * 2 * D + D + part * 8);
-      // (unconditional: the last span re-issues its own loads, which keeps the
-      // load state the same on every path)
+        for (int jt = 0; jt < NJ; ++jt) wv[jt] = ld8(Wv + (size_t)(16 * jt + col) * rp + k8);
+      }
       const SpanMeta<T> nxt = span_meta<T>(min(i + 1, n - 1), mL, mr, mbits, mfo, mgo, fac_base, sg_base);
-      issue_span_loads<T, D, G>(nxt, sub, part, lane, UCAP, vk, ureg, sgr);
+      issue_span_loads<T, D>(nxt, col, cls, lane, vk, ureg, sgr);
       wave_lds_sync();
-      // ---- steps 2-4 over token tiles of U (one tile unless L*rp exceeds the slot)
-      float am[2][G];
+
+      // ---- steps 2-5.  r <= L, so a span with one token block (L <= 32, almost
+      // all) has one rank block and its single U tile is already staged.  Longer
+      // spans take two passes: the span maximum first, then per rank block the
+      // weights and U^T p, re-staging tiles as needed.
+      float sv0[8];
+      float mt = kNegInf;
+      for (int tb = 0; tb < TB; ++tb) {
+        f32x4_t sc[2];
+        tile_scores<T, G>(cur, tb, RB, col, cls, lane, yb, ut, utt, TB > 1 || RB > 1, sc);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) am[kk][gi] = 0.0f;
-      for (int t0 = 0; t0 < L; t0 += TT) {
-        const int tn = min(TT, L - t0);
-        if (t0 > 0) {
-          for (int piece = lane; piece * 8 < tn * rp; piece += 64)
-            st8(ub + piece * 8, ld8(Ub + (size_t)t0 * rp + piece * 8));
-          wave_lds_sync();
-        }
-        // step 2: token scores s_t = U[t] . y
-        float s[2][G];
+          for (int v = 0; v < 4; ++v) {
+            const int t = tb * 32 + 8 * cls + 4 * h + v;
+            const float x = (head_on && t < L) ? sc[h][v] : kNegInf;
+            sv0[4 * h + v] = x;
+            mt = fmaxf(mt, x);
+          }
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
+      if (mn != kNegInf) {
+        const float alpha = exp2f(m - mn);
+        lsum *= alpha;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int t = lane + 64 * tt;
+        for (int jt = 0; jt < NJ; ++jt) acc[jt] *= alpha;
+        m = mn;
+      }
+      for (int kb = 0; kb < RB; ++kb) {
+        f32x4_t am[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+        for (int tb = 0; tb < TB; ++tb) {
+          float sv[8];
+          if (TB == 1) {
 #pragma unroll
-          for (int gi = 0; gi < G; ++gi) s[tt][gi] = kNegInf;
-          if (t < tn) {
-            float acc[G];
+            for (int e = 0; e < 8; ++e) sv[e] = sv0[e];
+          } else {
+            f32x4_t sc[2];
+            tile_scores<T, G>(cur, tb, RB, col, cls, lane, yb, ut, utt, true, sc);
 #pragma unroll
-            for (int gi = 0; gi < G; ++gi) acc[gi] = 0.0f;
-            for (int k8 = 0; k8 < rp; k8 += 8) {
-              float u8[8];
-              unpack(ld8(ub + t * rp + k8), u8);
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                if (k8 + e < r) {
-#pragma unroll
-                  for (int gi = 0; gi < G; ++gi) acc[gi] += u8[e] * yb[(k8 + e) * G + gi];
-                }
+              for (int v = 0; v < 4; ++v) {
+                const int t = tb * 32 + 8 * cls + 4 * h + v;
+                sv[4 * h + v] = (head_on && t < L) ? sc[h][v] : kNegInf;
               }
-            }
-#pragma unroll
-            for (int gi = 0; gi < G; ++gi) s[tt][gi] = ((bits >> gi) & 1u) ? acc[gi] : kNegInf;
+            restage_tile(cur, tb, kb, lane, ut, utt);
           }
-        }
-        // step 3: online softmax; the span's partial U^T p is rescaled with o
+          float pr[8];
+          float ps = 0.0f;
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-          const float ms = wave_max(fmaxf(s[0][gi], s[1][gi]));
-          const float mn = fmaxf(m[gi], ms);
-          float p0 = 0.0f, p1 = 0.0f;
-          if (mn != kNegInf) {
-            const float alpha = exp2f(m[gi] - mn);
-            p0 = exp2f(s[0][gi] - mn);
-            p1 = exp2f(s[1][gi] - mn);
-            l[gi] = l[gi] * alpha + wave_sum(p0 + p1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[gi][e] *= alpha;
-            am[0][gi] *= alpha;
-            am[1][gi] *= alpha;
-            m[gi] = mn;
+          for (int e = 0; e < 8; ++e) {
+            pr[e] = (m == kNegInf) ? 0.0f : exp2f(sv[e] - m);
+            ps += pr[e];
           }
-          if (lane < tn) pb[lane * G + gi] = p0;
-          if (lane + 64 < tn) pb[(lane + 64) * G + gi] = p1;
+          if (kb == 0) lsum += ps;
+          Vec8<float> pv;
+          pack8(pr, pv);
+          // step 4: a[k][h] += sum_t U[t][k] p[t][h]
+#pragma unroll
+          for (int h = 0; h < 2; ++h) am[h] = mma8(lds8f(utt + half_row(col, h) * TS + 8 * cls), pv, am[h]);
         }
-        wave_lds_sync();
-        // step 4: a[k] += sum_t U[t][k] p_t
+        // step 5: o[j][h] += sum_k W_V[j][k] b[k][h],  b = sigma*gate * a
+        if (kb > 0) {
+          const int k8 = min(kb * 32 + 8 * cls, rp - 8);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int k = lane + 64 * kk;
-          if (k < r) {
-#pragma unroll 4
-            for (int t = 0; t < tn; ++t) {
-              const float u = load1(ub + t * rp + k);
-#pragma unroll
-              for (int gi = 0; gi < G; ++gi) am[kk][gi] += u * pb[t * G + gi];
-            }
-          }
+          for (int jt = 0; jt < NJ; ++jt) wv[jt] = ld8(Wv + (size_t)(16 * jt + col) * rp + k8);
         }
-        wave_lds_sync();
-      }
-      // b[k] = sigma_k gate_k a[k]  (into yb)
+        float bv[8];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int k = lane + 64 * kk;
-        if (k < r) {
-          const float st = kk == 0 ? cst0 : cst1;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int gi = 0; gi < G; ++gi) yb[k * G + gi] = am[kk][gi] * st;
-        }
-      }
-      wave_lds_sync();
-      // ---- step 5: o += Vh_V^T b
+          for (int v = 0; v < 4; ++v) bv[4 * h + v] = am[h][v] * stl[kb * 32 + 8 * cls + 4 * h + v];
+        Vec8<T> bp;
+        pack8(bv, bp);
 #pragma unroll
-      for (int u = 0; u < UK; ++u) {
-        if (u * RPW < r) {
-          const int k = u * RPW + sub;
-          if (k < r) {
-            float v8[8];
-            unpack(vv[u], v8);
-#pragma unroll
-            for (int gi = 0; gi < G; ++gi) {
-              const float bk = yb[k * G + gi];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) o[gi][e] += bk * v8[e];
-            }
-          }
-        }
-      }
-      for (int k0 = RREG; k0 < r; k0 += RREG) {
-#pragma unroll
-        for (int u = 0; u < UK; ++u) vv[u] = ld8(Vb + (size_t)min(k0 + u * RPW + sub, r - 1) * 2 * D + D + part * 8);
-#pragma unroll
-        for (int u = 0; u < UK; ++u) {
-          const int k = k0 + u * RPW + sub;
-          if (k0 + u * RPW < r && k < r) {
-            float v8[8];
-            unpack(vv[u], v8);
-#pragma unroll
-            for (int gi = 0; gi < G; ++gi) {
-              const float bk = yb[k * G + gi];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) o[gi][e] += bk * v8[e];
-            }
-          }
-        }
+        for (int jt = 0; jt < NJ; ++jt) acc[jt] = mma8(wv[jt], bp, acc[jt]);
       }
       wave_lds_sync();
       cur = nxt;
-      stage_span<T>(cur, lane, UCAP, ureg, sgr, ub, stl, cst0, cst1);
-      wave_lds_sync();
     }
-    // merge the row-subgroups of this wave (states share m, l) and write the partial
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float ov = o[gi][e];
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) ov += __shfl_xor(ov, off);
-        o[gi][e] = ov;
-      }
+    // partial of this item: head col, summed over the four lane classes
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
     const int slot = a.nch_a4 + lc;
     float* pml = a.part_ml + ((size_t)g * a.P_max + slot) * G * 2;
     float* po = a.part_o + ((size_t)g * a.P_max + slot) * G * D;
-    if (sub == 0) {
+    if (col < G) {
 #pragma unroll
-      for (int gi = 0; gi < G; ++gi)
+      for (int jt = 0; jt < NJ; ++jt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) po[gi * D + part * 8 + e] = o[gi][e];
-    }
-    if (lane < G) {
-      float mv = m[0], lv = l[0];
-#pragma unroll
-      for (int gi = 1; gi < G; ++gi) if (lane == gi) { mv = m[gi]; lv = l[gi]; }
-      pml[lane * 2] = mv;
-      pml[lane * 2 + 1] = lv;
+        for (int v = 0; v < 4; ++v) po[col * D + 16 * jt + 4 * cls + v] = acc[jt][v];
+      if (cls == 0) {
+        pml[col * 2] = m;
+        pml[col * 2 + 1] = lsum;
+      }
     }
   }
 }
@@ -820,8 +846,11 @@ __global__ __launch_bounds__(kAttnThreads) void attend_full_kernel(const AttendA
   extern __shared__ __align__(16) char lds[];
   role_full_summary<T, D, G>(a, blockIdx.x, lds);
 }
+// Two waves per SIMD: the span steps are latency-bound, and a second resident wave hides
+// more of it than the few registers spilled to reach 256 VGPRs cost.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttnThreads) void attend_expanded_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attend_expanded_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
   role_expanded<T, D, G>(a, blockIdx.x, lds);
 }
@@ -916,7 +945,8 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
     const int r = a.rank[(size_t)b * a.seg_cap + S];
     const int rp = (r + 7) & ~7;
     const T* Ub = static_cast<const T*>(a.fac) + a.fac_off[(size_t)g * a.seg_cap + S];
-    const T* Vb = Ub + (size_t)L * rp;
+    const T* Vk = Ub + (size_t)L * rp;            // key part   [r][D]
+    const T* Wv = Vk + (size_t)r * D;             // value part [D][rp]
     const float* sgp = a.sg + a.sg_off[(size_t)g * a.seg_cap + S];
     const int row0 = a.tok_off[(size_t)g * (a.seg_cap + 1) + j];
     for (int t = 0; t < L; ++t) {
@@ -926,7 +956,10 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
       for (int k = 0; k < r; ++k) {
         const float w = load1(Ub + (size_t)t * rp + k) * (sgp[k] * sgp[r + k]);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] += w * load1(Vb + (size_t)k * 2 * D + lane + 64 * c);
+        for (int c = 0; c < CPL; ++c) {
+          const int colj = lane + 64 * c;
+          acc[c] += w * (colj < D ? load1(Vk + (size_t)k * D + colj) : load1(Wv + (size_t)(colj - D) * rp + k));
+        }
       }
       const size_t orow = ((size_t)g * a.T + row0 + t) * D;
 #pragma unroll

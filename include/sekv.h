@@ -75,20 +75,28 @@ typedef struct sekv_config {
  *       span body i is the open token interval (seg_off[i], seg_off[i+1]), of
  *       length L_i = seg_off[i+1] - seg_off[i] - 1 (1..max_span); the tail
  *       (full resolution) starts at seg_off[n_seg].  [de-1], [zh-1].
- *   full_k/full_v [B][Hkv][full_cap][d] dtype: full-resolution keys/values in
- *       token order sink, anchors (span order), tail.  n_full[b] rows valid.
- *   sum_k/sum_v [B][Hkv][seg_cap][d] dtype: surprisal-weighted mean key/value of
- *       each span body.  [de-2], [zh-2].
+ *   full_k [B][Hkv][full_cap][d] dtype: full-resolution keys in token order
+ *       sink, anchors (span order), tail.  n_full[b] rows valid.
+ *   full_v [B][Hkv][ceil(full_cap/32)][d][32] dtype: the matching values in
+ *       32-entry tiles, each tile transposed: value (entry e, dim j) of a
+ *       (b, kv) block at ((e/32)*d + j)*32 + e%32.  Padding entries must be
+ *       finite (zero).  (The transposed tile is the matrix-core operand of P.V.)
+ *   sum_k [B][Hkv][seg_cap][d] dtype: surprisal-weighted mean key of each span
+ *       body; sum_v [B][Hkv][ceil(seg_cap/32)][d][32]: the mean values, tiled
+ *       and transposed like full_v.  [de-2], [zh-2].
  *   rho [B][Hkv][seg_cap][d] dtype: routing key, P^T normalize(P kbar), so that
  *       q . rho equals the routing-space score of the projected query. [de-2/3]
  *   rank [B][seg_cap] int32: r_i, 1 <= r_i <= min(L_i, 2d), shared by all KV
  *       heads of the span.  [de-2], [zh-2] (adaptive rank budget).
  *   fac pool (dtype): for span (b, kv, i) a block at element offset
- *       fac_off[b][kv][i] (a multiple of 8) holding U [L_i][rp] (row stride
- *       rp = ceil(r_i / 8) * 8, padding zero) followed by Vh [r_i][2d]
- *       (columns 0..d-1 the key part, d..2d-1 the value part).
+ *       fac_off[b][kv][i] (a multiple of 8) holding, with rp = ceil(r_i/8)*8,
+ *       U [L_i][rp] (row stride rp, padding zero), then the key part of the
+ *       right singular vectors Vh_K [r_i][d], then the value part transposed,
+ *       W_V [d][rp] (W_V[j][k] = Vh[k][d + j], padding zero).  Block size
+ *       L_i*rp + r_i*d + d*rp elements.
  *   sg pool (float32): for span (b, kv, i) sigma[r_i] then gate[r_i] at offset
- *       sg_off[b][kv][i].  Token K/V of the span are U diag(sigma*gate) Vh.
+ *       sg_off[b][kv][i].  Token keys of the span are U diag(sigma*gate) Vh_K,
+ *       token values U diag(sigma*gate) W_V^T.
  *       [abstract], [de-2], [zh-2].
  *
  * Device arrays are required for every field; the *_host fields are host
@@ -104,10 +112,10 @@ typedef struct sekv_spans {
   const int32_t* seg_off;       /* [B][seg_cap+1] device */
   const int32_t* rank;          /* [B][seg_cap] device */
   const void* full_k;           /* [B][Hkv][full_cap][d] device */
-  const void* full_v;
+  const void* full_v;           /* [B][Hkv][ceil(full_cap/32)][d][32] device */
   const void* sum_k;            /* [B][Hkv][seg_cap][d] device */
-  const void* sum_v;
-  const void* rho;
+  const void* sum_v;            /* [B][Hkv][ceil(seg_cap/32)][d][32] device */
+  const void* rho;              /* [B][Hkv][seg_cap][d] device */
   const int64_t* fac_off;       /* [B][Hkv][seg_cap] device */
   const int64_t* sg_off;        /* [B][Hkv][seg_cap] device */
   const void* fac;              /* pool, fac_elems elements of dtype */
@@ -198,7 +206,7 @@ sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* 
 /*
  * sekv_reconstruct - token-level K/V of listed spans (standalone, for checks
  * and unfused use).  [de-3], [zh-3]: selected spans are rebuilt at token level;
- * K_hat = U diag(sigma*gate) Vh[:, :d], V_hat = U diag(sigma*gate) Vh[:, d:].
+ * K_hat = U diag(sigma*gate) Vh_K, V_hat = U diag(sigma*gate) W_V^T.
  *   exp_list, exp_count as written by sekv_route (device).
  *   tok_off [B][Hkv][seg_cap+1] int32 device, written: row offset of list entry
  *     j in the outputs (exclusive prefix of L), tok_off[count] = total rows.

@@ -77,7 +77,7 @@ def test_plan_matches_oracle_on_workload(wid):
                 L = int(so[i + 1] - so[i] - 1)
                 assert p.fac_off[b, kv, i] == off and off % 8 == 0
                 assert p.sg_off[b, kv, i] == goff
-                off += L * ((r + 7) // 8 * 8) + r * 2 * w.head_dim
+                off += B.fac_block_elems(L, r, w.head_dim)
                 goff += 2 * r
     assert p.fac_elems == off and p.sg_elems == goff
 

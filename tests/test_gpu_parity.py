@@ -178,7 +178,12 @@ def test_reconstruct_matches_oracle(ctx):
 
 
 def test_split_invariance(ctx, monkeypatch):
-    """The result does not depend on how the memory is cut into split-K chunks."""
+    """The result does not depend on how the memory is cut into split-K chunks,
+    up to rounding: with a bfloat16 cache the softmax weights enter the P.V
+    matrix-core product rounded to bfloat16 (relative 2^-9) after subtracting a
+    running maximum that depends on the split, so outputs (|o| < 4 here) may
+    move by a few 2^-9 * |v| ulps; 2e-3 bounds that, 10x under the parity
+    tolerance."""
     import torch
     p = _prep("bf16-ragged-B3-T4K")
     outs = []
@@ -190,7 +195,7 @@ def test_split_invariance(ctx, monkeypatch):
         torch.cuda.synchronize()
         outs.append(dev.out.cpu().numpy())
     for o in outs[1:]:
-        assert np.abs(o - outs[0]).max() <= 1e-5
+        assert np.abs(o - outs[0]).max() <= 2e-3
 
 
 def test_library_build_matches_oracle_build(ctx):
@@ -215,10 +220,10 @@ def test_library_build_matches_oracle_build(ctx):
         rel = 2.0 ** -7 if w.dtype == "bf16" else 2.0 ** -22
         fk = cache.full_k.float().cpu().numpy()
         sk = cache.sum_k.float().cpu().numpy()
-        sv = cache.sum_v.float().cpu().numpy()
+        sv = B.untile_values(cache.sum_v.float().cpu().numpy(), cache.seg_cap)
+        fv = B.untile_values(cache.full_v.float().cpu().numpy(), cache.full_cap)
         rh = cache.rho.float().cpu().numpy()
-        fac = cache.fac.float().cpu().numpy()
-        sg = cache.sg.cpu().numpy()
+
         worst_recon = 0.0
         for b in range(w.batch):
             n = oc.n_seg(b)
@@ -229,17 +234,13 @@ def test_library_build_matches_oracle_build(ctx):
             for kv in range(w.n_kv_heads):
                 nf = len(oc.full_idx[b])
                 assert np.array_equal(fk[b, kv, :nf], oc.full_k[b][kv])
+                assert np.array_equal(fv[b, kv, :nf], oc.full_v[b][kv])
                 for arr, ref in ((sk, oc.sum_k), (sv, oc.sum_v), (rh, oc.rho)):
                     r = ref[b][kv]
                     assert np.all(np.abs(arr[b, kv, :n] - r) <= rel * np.abs(r) + 1e-30)
                 for i in range(0, n, max(1, n // 40)):
                     rk = int(plan.rank[b, i])
-                    rp = (rk + 7) // 8 * 8
-                    o = int(plan.fac_off[b, kv, i])
-                    U = fac[o:o + L[i] * rp].reshape(L[i], rp)[:, :rk]
-                    Vh = fac[o + L[i] * rp:o + L[i] * rp + rk * 2 * w.head_dim].reshape(rk, 2 * w.head_dim)
-                    go = int(plan.sg_off[b, kv, i])
-                    sig, gt = sg[go:go + rk], sg[go + rk:go + 2 * rk]
+                    U, sig, gt, Vh = B.read_factors(cache, b, kv, i)
                     assert np.allclose(sig, oc.sigma[b][kv][i], rtol=1e-5, atol=1e-6)
                     assert np.array_equal(gt, oc.gate[b][kv][i].astype(np.float32))
                     utol = 0.05 if w.dtype == "bf16" else 1e-5
