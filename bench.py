@@ -107,6 +107,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto, >= 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--queries", type=int, default=64)
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="timed pass: replay of captured HIP graphs (default) or eager launches")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -166,32 +168,58 @@ def main():
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     log(f"{ncopy} cache copies of {resident / 2**20:.0f} MiB each resident in HBM")
 
+    nstep_combo = math.lcm(ncopy, Q)
+
     def step(i):
         c = i % ncopy
         qs = qd[i % Q]
-        B.route(ctx, caches[c], qs, theta_d[:], outs[c], rws, spans=structs[c])
+        B.route(ctx, caches[c], qs, theta_d, outs[c], rws, spans=structs[c])
         B.decode(ctx, caches[c], qs, outs[c], out, dws, spans=structs[c])
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    # profiled pass: the same steps launched eagerly, HIP events around every
+    # kernel on the stream it is launched on (per-kernel durations)
     ctx.profile(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ev0.record()
     for i in range(args.steps):
         step(args.warmup + i)
-    ev1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t1
-    ev_ms = ev0.elapsed_time(ev1)
+    eager_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     prof = ctx.profile_read()
     ctx.profile(False)
-    ms_per_step = wall * 1e3 / args.steps
     kern_us = {k: (v[0] / max(v[1], 1)) * 1e3 for k, v in prof.items()}
-    log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ev_ms:.2f} ms; per launch: " +
-        ", ".join(f"{k} {u:.1f} us" for k, u in kern_us.items()))
+    log(f"eager: {eager_ms * 1e3:.1f} us/step; per launch: " + ", ".join(f"{k} {u:.1f} us" for k, u in kern_us.items()))
+
+    # timed pass: one HIP graph per (cache copy, query) combination, replayed
+    graphs = None
+    if args.launch == "graph":
+        graphs = []
+        cap_stream = torch.cuda.Stream()
+        for j in range(nstep_combo):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=cap_stream):
+                step(j)
+            graphs.append(gr)
+        for i in range(args.warmup):
+            graphs[i % nstep_combo].replay()
+        torch.cuda.synchronize()
+        log(f"captured {nstep_combo} step graphs")
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if graphs is not None:
+        for i in range(args.steps):
+            graphs[(args.warmup + i) % nstep_combo].replay()
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps ({args.launch}): {ms_per_step * 1e3:.1f} us/step")
+    del graphs
 
     # algorithmic bytes of the timed steps (lists realized per query step)
     nseg_tot = sum(int(plan.n_seg[b]) for b in range(w.batch)) * w.n_kv_heads
@@ -234,7 +262,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_ctx": w.n_ctx, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rank_range": [w.rank_lo, w.rank_hi],
                    "expand_frac_target": args.frac, "expand_frac_realized": round(float(avg["frac"]), 4),
-                   "factors": "device", "layers": 1, "cache_copies_rotated": ncopy, "launch": "eager"},
+                   "factors": "device", "layers": 1, "cache_copies_rotated": ncopy, "launch": args.launch},
         "eff_ctx_tokens_per_s": steps_per_s * w.batch * w.n_ctx,
         "algorithmic_bytes_per_step": int(avg["total"]),
         "step_hbm_gbs": step_gbs,
@@ -244,6 +272,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": gbs[dom], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gbs[dom] / PEAK_HBM_GBS, "traffic": None,
                      "bytes_per_launch": int(avg[dom])},
+        "eager_ms_per_step": eager_ms,
         "cpu_baseline": base,
     }
     print(json.dumps(rec), flush=True)
