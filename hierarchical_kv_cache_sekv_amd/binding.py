@@ -341,9 +341,52 @@ def decode(ctx: Context, cache: SpanCache, q, route_out: RouteOut, out, ws: Deco
 
 # ----------------------------------------------------------------- marshalling
 def fac_block_elems(L: int, r: int, d: int) -> int:
-    """Elements of one span's factor block: U [L][rp] | Vh_K [r][d] | W_V [d][rp]."""
+    """Elements of one span's factor block: Vh_K [r][d] (groups of 8 rotated by
+    the row) | U [L][rp] | W_V in 16-rank column blocks [d][min(16, rp - 16 g)]."""
     rp = (r + 7) // 8 * 8
-    return L * rp + r * d + d * rp
+    return r * d + L * rp + d * rp
+
+
+def sg_entry_elems(r: int) -> int:
+    """Floats of one span's sigma|gate entry: sigma [rq] | gate [rq], rq = ceil(r/4)*4."""
+    return 2 * ((r + 3) // 4 * 4)
+
+
+def _vk_rotate(vk: np.ndarray) -> np.ndarray:
+    """[r][d] key part -> ABI order: row k's groups of 8 rotated by k."""
+    r, d = vk.shape
+    ng = d // 8
+    out = np.empty_like(vk)
+    for k in range(r):
+        g = vk[k].reshape(ng, 8)
+        out[k] = g[(np.arange(ng) - k) % ng].reshape(-1)   # position p holds group (p - k) mod ng
+    return out
+
+
+def _vk_unrotate(rot: np.ndarray) -> np.ndarray:
+    r, d = rot.shape
+    ng = d // 8
+    out = np.empty_like(rot)
+    for k in range(r):
+        g = rot[k].reshape(ng, 8)
+        out[k] = g[(np.arange(ng) + k) % ng].reshape(-1)   # group u sits at position (u + k) mod ng
+    return out
+
+
+def _wv_blocks(wv: np.ndarray) -> np.ndarray:
+    """[d][rp] value part -> flat 16-rank column blocks [d][wk] (ABI order)."""
+    d, rp = wv.shape
+    return np.concatenate([wv[:, k0:min(k0 + 16, rp)].reshape(-1) for k0 in range(0, rp, 16)])
+
+
+def _wv_unblock(flat: np.ndarray, d: int, rp: int) -> np.ndarray:
+    out = np.zeros((d, rp), flat.dtype)
+    o = 0
+    for k0 in range(0, rp, 16):
+        wk = min(16, rp - k0)
+        out[:, k0:k0 + wk] = flat[o:o + d * wk].reshape(d, wk)
+        o += d * wk
+    return out
 
 
 def read_factors(cache: "SpanCache", b: int, kv: int, i: int):
@@ -356,12 +399,13 @@ def read_factors(cache: "SpanCache", b: int, kv: int, i: int):
     rp = (r + 7) // 8 * 8
     o = int(plan.fac_off[b, kv, i])
     fac = cache.fac[o:o + fac_block_elems(L, r, D)].float().cpu().numpy().astype(np.float64)
-    U = fac[:L * rp].reshape(L, rp)[:, :r]
-    vk = fac[L * rp:L * rp + r * D].reshape(r, D)
-    wv = fac[L * rp + r * D:].reshape(D, rp)[:, :r]
+    vk = _vk_unrotate(fac[:r * D].reshape(r, D))
+    U = fac[r * D:r * D + L * rp].reshape(L, rp)[:, :r]
+    wv = _wv_unblock(fac[r * D + L * rp:], D, rp)[:, :r]
     go = int(plan.sg_off[b, kv, i])
-    sg = cache.sg[go:go + 2 * r].float().cpu().numpy().astype(np.float64)
-    return U, sg[:r], sg[r:], np.concatenate([vk, wv.T], axis=1)
+    rq = (r + 3) // 4 * 4
+    sg = cache.sg[go:go + 2 * rq].float().cpu().numpy().astype(np.float64)
+    return U, sg[:r], sg[rq:rq + r], np.concatenate([vk, wv.T], axis=1)
 
 
 def tile_values(rows: np.ndarray) -> np.ndarray:
@@ -418,18 +462,19 @@ def fill_cache(cache: SpanCache, parts) -> None:
                 assert L == so[i + 1] - so[i] - 1 and r == plan.rank[b, i]
                 rp = (r + 7) // 8 * 8
                 o = int(plan.fac_off[b, kv, i])
+                fac[o:o + r * D] = _vk_rotate(Vh[:, :D]).reshape(-1)  # key part [r][d], rotated groups
+                o += r * D
                 blk = np.zeros((L, rp), np.float32)
                 blk[:, :r] = U
                 fac[o:o + L * rp] = blk.reshape(-1)
                 o += L * rp
-                fac[o:o + r * D] = Vh[:, :D].reshape(-1)             # key part [r][d]
-                o += r * D
                 wv = np.zeros((D, rp), np.float32)
-                wv[:, :r] = Vh[:, D:].T                             # value part transposed [d][rp]
-                fac[o:o + D * rp] = wv.reshape(-1)
+                wv[:, :r] = Vh[:, D:].T                             # value part transposed, column blocks
+                fac[o:o + D * rp] = _wv_blocks(wv)
                 go = int(plan.sg_off[b, kv, i])
+                rq = (r + 3) // 4 * 4
                 sg[go:go + r] = parts.sigma[b][kv][i]
-                sg[go + r:go + 2 * r] = parts.gate[b][kv][i]
+                sg[go + rq:go + rq + r] = parts.gate[b][kv][i]
 
     def put(dst, src):
         dst.copy_(torch.from_numpy(src).to(et))
@@ -471,5 +516,5 @@ def layout_from_segments(cfg: Config, seg_offs, ranks) -> Plan:
                 fac_off[b, kv, i] = fo
                 sg_off[b, kv, i] = go
                 fo += fac_block_elems(int(L[i]), r, D)
-                go += 2 * r
+                go += sg_entry_elems(r)
     return Plan(n_seg, n_full, seg_off, rank, fac_off, sg_off, fo, go)

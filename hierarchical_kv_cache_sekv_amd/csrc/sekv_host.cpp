@@ -177,9 +177,23 @@ namespace {
 
 int elem_size(int dtype) { return dtype == SEKV_BF16 ? 2 : 4; }
 
-// Factor block of one span: U [L][rp] | Vh_K [r][d] | W_V [d][rp] (the value
-// part of Vh transposed), rp = r rounded up to 8, padding zero.
-int64_t fac_block_elems(int L, int r, int rp, int D) { return (int64_t)L * rp + (int64_t)r * D + (int64_t)D * rp; }
+// Factor block of one span: Vh_K [r][d] | U [L][rp] | W_V; rp = r rounded up
+// to 8, padding zero.  Vh_K row k holds its d/8 groups of 8 elements rotated
+// by k (group u at position (u + k) mod d/8).  W_V is the value part of Vh
+// transposed, cut into 16-rank column blocks g, each [d][min(16, rp - 16 g)].
+// In this order the expanded-span pass consumes the block front to back.
+int64_t fac_block_elems(int L, int r, int rp, int D) { return (int64_t)r * D + (int64_t)L * rp + (int64_t)D * rp; }
+int64_t fac_vk_index(int D, int k, int col) {
+  const int ng = D / 8;
+  return (int64_t)k * D + (int64_t)(((col / 8) + k) % ng) * 8 + (col % 8);
+}
+int64_t fac_u_index(int r, int rp, int D, int t, int j) { return (int64_t)r * D + (int64_t)t * rp + j; }
+int64_t fac_wv_index(int L, int r, int rp, int D, int col, int j) {
+  const int g = j / 16, wk = std::min(16, rp - 16 * g);
+  return (int64_t)r * D + (int64_t)L * rp + (int64_t)g * 16 * D + (int64_t)col * wk + (j % 16);
+}
+// sigma|gate entry of one span: sigma [rq] | gate [rq], rq = r rounded up to 4.
+int64_t sg_entry_elems(int r) { return 2 * (((int64_t)r + 3) & ~(int64_t)3); }
 
 sekv_status check_config(const sekv_config* c) {
   if (!c) return fail(SEKV_EINVAL, "config is NULL");
@@ -458,7 +472,7 @@ sekv_status sekv_plan_spans(const sekv_config* c, const float* surprisal, const 
           fac_off[o] = fo;
           sg_off[o] = go;
           fo += fac_block_elems(L, r, rp, D);
-          go += 2 * r;
+          go += sg_entry_elems(r);
         } else {
           fac_off[o] = 0;
           sg_off[o] = 0;
@@ -500,7 +514,9 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
         if (r > gate_stride) return fail(SEKV_ESHAPE, "gate_stride %d < rank %d", gate_stride, r);
         const int rp = (r + 7) & ~7;
         need_f = std::max<int64_t>(need_f, s->fac_off_host[o] + fac_block_elems(L, r, rp, D));
-        need_g = std::max<int64_t>(need_g, s->sg_off_host[o] + 2 * r);
+        need_g = std::max<int64_t>(need_g, s->sg_off_host[o] + sg_entry_elems(r));
+        if (s->fac_off_host[o] % 8 != 0 || s->sg_off_host[o] % 4 != 0)
+          return fail(SEKV_EINVAL, "pool offsets of span (%d, %d, %d) are not 8- and 4-element aligned", b, kv, i);
       }
   if (need_f > s->fac_elems || need_g > s->sg_elems)
     return fail(SEKV_ECAPACITY, "factor pools hold (%lld, %lld) elements, plan needs (%lld, %lld)", (long long)s->fac_elems,
@@ -629,21 +645,24 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
         for (int t = 1; t < L; ++t)
           if (std::fabs(u[t]) > std::fabs(u[imax])) imax = t;
         const double sgn = u[imax] < 0 ? -1.0 : 1.0;
-        for (int t = 0; t < L; ++t) store(fac_dst, dt, fbase + (int64_t)t * rp + j, sgn * u[t]);
+        for (int t = 0; t < L; ++t) store(fac_dst, dt, fbase + fac_u_index(rk, rp, D, t, j), sgn * u[t]);
         const double sj = sig[j];
         const double inv = sj > 0 ? sgn / sj : 0.0;
         const double* wrow = M.data() + (size_t)src * n2;
-        const int64_t kbase = fbase + (int64_t)L * rp, vbase = kbase + (int64_t)rk * D;
         for (int col = 0; col < D; ++col) {
-          store(fac_dst, dt, kbase + (int64_t)j * D + col, wrow[col] * inv);
-          store(fac_dst, dt, vbase + (int64_t)col * rp + j, wrow[D + col] * inv);
+          store(fac_dst, dt, fbase + fac_vk_index(D, j, col), wrow[col] * inv);
+          store(fac_dst, dt, fbase + fac_wv_index(L, rk, rp, D, col, j), wrow[D + col] * inv);
         }
         sg_dst[gbase + j] = (float)sj;
-        sg_dst[gbase + rk + j] = gt[j];
+        sg_dst[gbase + ((rk + 3) & ~3) + j] = gt[j];
       }
       for (int j = rk; j < rp; ++j) {
-        for (int t = 0; t < L; ++t) store(fac_dst, dt, fbase + (int64_t)t * rp + j, 0.0);
-        for (int col = 0; col < D; ++col) store(fac_dst, dt, fbase + (int64_t)L * rp + (int64_t)rk * D + (int64_t)col * rp + j, 0.0);
+        for (int t = 0; t < L; ++t) store(fac_dst, dt, fbase + fac_u_index(rk, rp, D, t, j), 0.0);
+        for (int col = 0; col < D; ++col) store(fac_dst, dt, fbase + fac_wv_index(L, rk, rp, D, col, j), 0.0);
+      }
+      for (int j = rk; j < ((rk + 3) & ~3); ++j) {
+        sg_dst[gbase + j] = 0.0f;
+        sg_dst[gbase + ((rk + 3) & ~3) + j] = 0.0f;
       }
     }
   });
@@ -749,8 +768,14 @@ void make_plan(const sekv_config* c, const sekv_spans* s, DecodePlan& p) {
   a.nch_a4 = (ntiles + a.tiles_a4 - 1) / a.tiles_a4;
   a.P_max = a.nch_a4 + (s->seg_cap + kExpChunk - 1) / kExpChunk;
   const int64_t max_items = (int64_t)BG * ((s->seg_cap + kExpChunk - 1) / kExpChunk);
-  a.n_a5_wg = (int)std::max<int64_t>(1, std::min<int64_t>(512, (max_items + 3) / 4));
+  a.n_a5_wg = (int)std::max<int64_t>(1, std::min<int64_t>(kExpWaves, max_items));
   a.n_a4_wg = BG * a.nch_a4;
+  int mr = 0;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* rk = s->rank_host + (size_t)b * s->seg_cap;
+    for (int i = 0; i < a.n_seg[b]; ++i) mr = std::max(mr, rk[i]);
+  }
+  a.max_rank = mr;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)D));
   size_t off = 0;
   p.off_ml = off; off = align_up(off + (size_t)BG * a.P_max * G * 2 * sizeof(float));
@@ -877,9 +902,9 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
       ents.push_back({static_cast<const char*>(s->fac) + s->fac_off_host[o] * es, fe * es, fo});
       h_soff[((size_t)g * cap + j) * 2] = fo;
       h_soff[((size_t)g * cap + j) * 2 + 1] = go;
-      std::memcpy(h_sg + go, s->sg + s->sg_off_host[o], 2 * r * sizeof(float));
+      std::memcpy(h_sg + go, s->sg + s->sg_off_host[o], sg_entry_elems(r) * sizeof(float));
       fo += fe;
-      go += 2 * r;
+      go += sg_entry_elems(r);
     }
   }
   char* d_stage_fac = dws + p.off_stage_fac;

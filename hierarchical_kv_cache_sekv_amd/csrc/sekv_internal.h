@@ -12,7 +12,9 @@ constexpr int kMaxGroups = 256;      // batch * kv heads handled by one decode l
 constexpr int kMaxSpan = 128;        // longest span body / highest rank the kernels hold
 constexpr int kRouteThreads = 256;   // spans per route workgroup (one lane per span)
 constexpr int kAttnThreads = 256;    // four waves per attention workgroup
-constexpr int kExpChunk = 8;         // expanded spans per wave work item
+constexpr int kExpChunk = 8;         // expanded spans per work item of the expanded-span kernel
+constexpr int kExpThreads = 64;      // one wave per expanded-span workgroup
+constexpr int kExpWaves = 4096;      // most waves (workgroups) of one expanded-span launch
 
 struct RouteArgs {
   int dtype;                 // 0 f32, 1 bf16
@@ -35,7 +37,8 @@ struct AttendArgs {
   int tiles_a4;              // 32-entry tiles per full-res/summary workgroup
   int nch_a4;                // workgroups per (b, kv) for that pass
   int P_max;                 // partial slots per (b, kv)
-  int n_a5_wg;               // workgroups of the expanded-span kernel
+  int n_a5_wg;               // workgroups (one wave each) of the expanded-span kernel
+  int max_rank;              // largest span rank (selects the expanded-span kernel's register tiling)
   int n_a4_wg;               // workgroups of the full-res/summary kernel
   float qscale;              // log2(e) / sqrt(D)
   const void* q;

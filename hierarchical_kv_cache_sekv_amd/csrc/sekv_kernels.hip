@@ -286,12 +286,6 @@ struct AttnLds {
   static constexpr int kMaskBytes = 2048;  // >= 32 * tiles_a4 (host checks)
   static constexpr int kMergeFloats = 4 * G * (D + 2);
   static constexpr int kRoleA = kMaskBytes + kMaskBytes * 4 + kMergeFloats * 4;
-  // role E, per wave: one 32-token x 32-rank tile of U as float, row-major and
-  // transposed (row stride 36), y [16 heads][kMaxSpan], sigma*gate [kMaxSpan]
-  static constexpr int kTileStride = 36;
-  static constexpr int kWaveBytes = (2 * 32 * kTileStride + G * kMaxSpan + kMaxSpan) * 4;
-  static constexpr int kRoleE = 4 * kWaveBytes + (kMaxGroups + 1) * 4 * 2;
-  static constexpr int kBytes = kRoleA > kRoleE ? kRoleA : kRoleE;
 };
 
 // Role A: one workgroup = a chunk of tiles_a4 32-entry tiles of the (b, kv)
@@ -476,191 +470,226 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
   }
 }
 
-// Role E: each wave takes work items of up to kExpChunk listed spans of one
-// (b, kv) and keeps, like role A, the online-softmax state of head (lane % 16).
-// Per span every contraction runs on the matrix cores (ranks and tokens in
-// blocks of 32; one block each for almost every span):
-//   step 1  y[k][h] = sigma_k gate_k (Vh_K[k] . q_h) / sqrt(d)   A = Vh_K rows, B = q
-//   step 2  s[t][h] = U[t] . y[:, h]                               A = U rows,    B = y
-//   step 3  online softmax over the span's tokens
-//   step 4  a[k][h] = sum_t U[t][k] p[t][h]                        A = U^T rows,  B = p
-//   step 5  o[j][h] += sum_k W_V[j][k] sigma_k gate_k a[k][h]      A = W_V rows,  B = b
-// Rows of each A operand are permuted so that lane 16c + h ends up holding the
-// 8 values (ranks or tokens 8c..8c+7) of head h that the next step takes as its
-// B operand: nothing moves between lanes from step to step.  Steps 2 and 4 run
-// in float32 (scores and weights unrounded); step 1 and 5 take the stored
-// element type (step 5's b is rounded to it).  U tiles are staged in LDS as
-// float, row-major and transposed.  The first tile, the first 32 key-part rank
-// rows and sigma/gate of span i+1 are loaded while span i is processed.
-template <typename T>
-struct SpanMeta {
-  int L, r, rp;
-  uint32_t bits;
-  const T* U;
-  const float* sg;
+// Role E (expanded spans): one wave per workgroup.  A work item is up to
+// kExpChunk consecutive entries of one (b, kv) expanded list.  The item's
+// factor data is consumed as one stream of 1 KB chunks: per span, its
+// sigma|gate entry (sg pool) and then its factor block
+//   Vh_K [r][d] (8-element groups rotated by the row) | U [L][rp] |
+//   W_V in 16-rank column blocks [d][min(16, rp - 16 g)],
+// each region starting on a chunk boundary.  A chunk is 16 bytes per lane,
+// loaded into registers one granule (ExpCfg::K chunks) ahead of the consumer
+// and written to a per-wave LDS ring a granule at a time, so the latency of
+// the next granule overlaps the arithmetic on the current one.  Lanes past
+// the end of a region re-read its last 16 bytes (no extra memory lines).
+// Every MFMA operand is then read from the ring.  For head h = lane % 16
+// (columns >= G unused), per span, in rank groups g and token groups of 16:
+//   step 1  y[k][h] = sigma_k gate_k (Vh_K[k] . q_h) log2(e)/sqrt(d)   A = Vh_K rows, B = q
+//   step 2  s[t][h] = U[t] . y[:, h]                                  A = U rows,    B = y
+//   step 3  online softmax over the span's tokens (log2 domain)
+//   step 4  a[k][h] = sum_t U[t][k] p[t][h]                           A = U^T rows,  B = p
+//   step 5  o[j][h] += sum_k W_V[j][k] sigma_k gate_k a[k][h]         A = W_V rows,  B = b
+// Steps 2, 4 and 5 are 16x16x16 products: the result of each (lane 16c + h
+// holds rows 4c..4c+3 of column h) is exactly the B operand the next one
+// takes, so nothing moves between lanes.  bf16: y enters step 2 as a
+// two-term bf16 split (hi + lo, about 16 significant bits), p and b are
+// rounded to bf16; float: every step in float32.
+// K: 1 KB chunks per granule in flight.  The ring holds a granule in flight
+// plus the largest piece read at once (16 rows of Vh_K or U, or one 16-rank
+// W_V block: 16 x 128 elements).  RGM: rank groups of 16 held in registers
+// (4: ranks up to 64, two waves per SIMD; 8: any rank, one wave per SIMD).
+template <typename T, int RGM> struct ExpCfg { static constexpr int K = 8; static constexpr int kRing = 16384; };
+template <> struct ExpCfg<bf16raw, 4> { static constexpr int K = 4; static constexpr int kRing = 8192; };
+
+template <typename T, int G, int RGM>
+struct ExpLds {
+  static constexpr int kRing = ExpCfg<T, RGM>::kRing;
+  static_assert((kRing & (kRing - 1)) == 0, "ring size is a power of two");
+  static_assert(kRing >= ExpCfg<T, RGM>::K * 1024 + 16 * kMaxSpan * (int)sizeof(T), "ring holds a granule and a piece");
+  static constexpr int kY = kRing;                          // y [rank group][class][G] 16 bytes
+  static constexpr int kStl = kY + RGM * 4 * G * 16;
+  static constexpr int kBytes = kStl + kMaxSpan * 4;        // sigma*gate [kMaxSpan] float
 };
 
-__device__ __forceinline__ int64_t readlane64(int64_t x, int i) {
+// Four elements of the storage type as an MFMA operand of a 16x16x16 product.
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16raw> { uint2 v; };
+template <> struct Vec4<float> { float4 v; };
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+// C[i][j] += sum over classes c and m < 4 of A_lane(16c+i)[m] * B_lane(16c+j)[m];
+// lane 16c + j holds C[4c + v][j].
+__device__ __forceinline__ f32x4_t mma4(const Vec4<bf16raw>& x, const Vec4<bf16raw>& y, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, x.v), __builtin_bit_cast(s16x4_t, y.v),
+                                                   c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma4(const Vec4<float>& x, const Vec4<float>& y, f32x4_t c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.v.x, y.v.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.v.y, y.v.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.v.z, y.v.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(x.v.w, y.v.w, c, 0, 0, 0);
+  return c;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ void pack4(const float (&p)[4], Vec4<bf16raw>& o) {
+  o.v = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+}
+__device__ __forceinline__ void pack4(const float (&p)[4], Vec4<float>& o) { o.v = make_float4(p[0], p[1], p[2], p[3]); }
+
+// Ring reads at ring byte offsets (already reduced modulo the ring size).
+template <typename T>
+__device__ __forceinline__ Vec4<T> rd4(const char* ring, uint32_t ob) {
+  Vec4<T> x;
+  if constexpr (sizeof(T) == 2) x.v = *reinterpret_cast<const uint2*>(ring + ob);
+  else x.v = *reinterpret_cast<const float4*>(ring + ob);
+  return x;
+}
+template <typename T>
+__device__ __forceinline__ Vec8<T> rd8(const char* ring, uint32_t ob, uint32_t mask) {
+  Vec8<T> x;
+  if constexpr (sizeof(T) == 2) {
+    x.v = *reinterpret_cast<const uint4*>(ring + ob);
+  } else {
+    x.a = *reinterpret_cast<const float4*>(ring + ob);
+    x.b = *reinterpret_cast<const float4*>(ring + ((ob + 16) & mask));
+  }
+  return x;
+}
+
+// 16 bytes from a global byte address (address space 1: a global load, not a
+// flat one that would also count against the LDS counter).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t g_u32x4;
+__device__ __forceinline__ uint4 gload16(uint64_t addr) {
+  const u32x4_t v = *reinterpret_cast<g_u32x4*>(addr);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int i) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), i);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(x & 0xffffffff), i);
-  return (int64_t)(((uint64_t)hi << 32) | lo);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(x & 0xffffffffu), i);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-template <typename T>
-__device__ __forceinline__ SpanMeta<T> span_meta(int i, int mL, int mr, int mbits, int64_t mfo, int64_t mgo,
-                                                 const T* fac_base, const float* sg_base) {
-  SpanMeta<T> sm;
-  sm.L = __builtin_amdgcn_readlane(mL, i);
-  sm.r = __builtin_amdgcn_readlane(mr, i);
-  sm.rp = (sm.r + 7) & ~7;
-  sm.bits = (uint32_t)__builtin_amdgcn_readlane(mbits, i);
-  sm.U = fac_base + readlane64(mfo, i);
-  sm.sg = sg_base + readlane64(mgo, i);
-  return sm;
+// Producer of the chunk stream (wave-uniform state): region `reg` (0 sg
+// entry, 1 factor block) of span j, at byte `off` of a region of `size`
+// bytes starting at global address `base`.  Past the last span the final
+// chunk is repeated (it is never read from the ring).
+struct ChunkCursor {
+  int j, reg, n;
+  uint32_t off, size;
+  uint64_t base;
+};
+struct ItemMeta {        // lane i < n: span i of the item
+  uint64_t sga, fa;      // global addresses of the sg entry and the factor block
+  uint32_t sgb, fb;      // their sizes in bytes
+};
+__device__ __forceinline__ uint64_t cursor_addr(const ChunkCursor& c, int lane) {
+  return c.base + min(c.off + 16u * (uint32_t)lane, c.size - 16u);
 }
-
-// Row of the A operand that MFMA half h gives to lane row i: the 4-row groups
-// interleave so output row 4c + v of half h is block position 8c + 4h + v.
-__device__ __forceinline__ int half_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
-
-// One 16-byte piece of U tile (tb, kb): piece p -> token p/4, ranks 8(p%4)..+8.
-// Clamped to an in-range address; pieces outside the span are zeroed when staged.
-template <typename T>
-__device__ __forceinline__ Vec8<T> ld_upiece(const SpanMeta<T>& sm, int tb, int kb, int p) {
-  const int t = min(tb * 32 + (p >> 2), sm.L - 1);
-  const int k8 = min(kb * 32 + 8 * (p & 3), sm.rp - 8);
-  return ld8(sm.U + (size_t)t * sm.rp + k8);
-}
-
-template <typename T, int NC>
-__device__ __forceinline__ void ld_vk(const SpanMeta<T>& sm, int kb, int col, int cls, int D, Vec8<T> (&vk)[2][NC]) {
-  const T* Vk = sm.U + (size_t)sm.L * sm.rp;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int k = min(kb * 32 + half_row(col, h), sm.r - 1);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) vk[h][c] = ld8(Vk + (size_t)k * D + 32 * c + 8 * cls);
+__device__ __forceinline__ void cursor_next(ChunkCursor& c, const ItemMeta& m) {
+  c.off += 1024u;
+  if (c.off < c.size) return;
+  if (c.reg == 0) {
+    c.reg = 1;
+    c.base = readlane64(m.fa, c.j);
+    c.size = (uint32_t)__builtin_amdgcn_readlane((int)m.fb, c.j);
+    c.off = 0;
+  } else if (c.j + 1 < c.n) {
+    c.j += 1;
+    c.reg = 0;
+    c.base = readlane64(m.sga, c.j);
+    c.size = (uint32_t)__builtin_amdgcn_readlane((int)m.sgb, c.j);
+    c.off = 0;
+  } else {
+    c.off -= 1024u;
   }
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void issue_span_loads(const SpanMeta<T>& sm, int col, int cls, int lane,
-                                                 Vec8<T> (&vk)[2][D / 32], Vec8<T> (&ureg)[2], float (&sgr)[4]) {
-  const int r1 = sm.r - 1;
-  sgr[0] = sm.sg[min(lane, r1)];
-  sgr[1] = sm.sg[sm.r + min(lane, r1)];
-  sgr[2] = sm.sg[min(lane + 64, r1)];
-  sgr[3] = sm.sg[sm.r + min(lane + 64, r1)];
+template <int K, int RING>
+__device__ __forceinline__ void stage_first(uint4 (&stg)[K], ChunkCursor& c, const ItemMeta& m, int lane) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) ureg[i] = ld_upiece(sm, 0, 0, lane + 64 * i);
-  ld_vk<T, D / 32>(sm, 0, col, cls, D, vk);
-}
-
-// Stage U tile (tb, kb) from its two pieces per lane into LDS (float),
-// row-major ut[t][k] and transposed utt[k][t]; zero outside the span.
-template <typename T>
-__device__ __forceinline__ void stage_tile(const SpanMeta<T>& sm, int tb, int kb, int lane, const Vec8<T> (&ureg)[2],
-                                           float* ut, float* utt) {
-  constexpr int S = 36;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = lane + 64 * i;
-    const int t = p >> 2, c8 = 8 * (p & 3);
-    const bool ok = tb * 32 + t < sm.L && kb * 32 + c8 < sm.rp;
-    float f[8];
-    unpack(ureg[i], f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = ok ? f[e] : 0.0f;
-    *reinterpret_cast<float4*>(ut + t * S + c8) = make_float4(f[0], f[1], f[2], f[3]);
-    *reinterpret_cast<float4*>(ut + t * S + c8 + 4) = make_float4(f[4], f[5], f[6], f[7]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) utt[(c8 + e) * S + t] = f[e];
+  for (int jj = 0; jj < K; ++jj) {
+    stg[jj] = gload16(cursor_addr(c, lane));
+    cursor_next(c, m);
   }
 }
 
-__device__ __forceinline__ Vec8<float> lds8f(const float* p) {
-  return {*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
-}
-
-// Load and stage U tile (tb, kb) (synchronous; multi-block spans only).
-template <typename T>
-__device__ __forceinline__ void restage_tile(const SpanMeta<T>& sm, int tb, int kb, int lane, float* ut, float* utt) {
-  Vec8<T> up[2];
+// Make stream bytes [.., e) readable from the ring: write staged granules and
+// stage the following ones until the ring holds everything before e.
+// `written` counts the stream bytes already in the ring (a multiple of 1024 K).
+template <int K, int RING>
+__device__ __forceinline__ void advance(uint4 (&stg)[K], uint32_t& written, uint32_t e, ChunkCursor& c,
+                                        const ItemMeta& m, int lane, char* ring) {
+  while (written < e) {
 #pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) up[q2] = ld_upiece(sm, tb, kb, lane + 64 * q2);
-  wave_lds_sync();
-  stage_tile(sm, tb, kb, lane, up, ut, utt);
-  wave_lds_sync();
-}
-
-// Step 2 for token block tb: scores of tokens tb*32 + 8*cls + 4h + v for head
-// (lane % 16), summed over the RB rank blocks; y is read from LDS.  With
-// restage, each (tb, kb) tile is loaded first; otherwise tile (0, 0) is in LDS.
-template <typename T, int G>
-__device__ __forceinline__ void tile_scores(const SpanMeta<T>& sm, int tb, int RB, int col, int cls, int lane,
-                                            const float* yb, float* ut, float* utt, bool restage, f32x4_t (&sc)[2]) {
-  constexpr int TS = 36;
-  sc[0] = sc[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const float* yrow = yb + min(col, G - 1) * kMaxSpan;
-  for (int kb = 0; kb < RB; ++kb) {
-    if (restage) restage_tile(sm, tb, kb, lane, ut, utt);
-    const Vec8<float> yk = lds8f(yrow + kb * 32 + 8 * cls);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) sc[h] = mma8(lds8f(ut + half_row(col, h) * TS + 8 * cls), yk, sc[h]);
-  }
-}
-
-template <typename T, int D, int G>
-__device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
-  using L_ = AttnLds<D, G>;
-  constexpr int NC = D / 32, NJ = D / 16, TS = L_::kTileStride;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, cls = lane >> 4;
-  const int BG = a.B * a.Hkv;
-  int* pre = reinterpret_cast<int*>(lds + 4 * L_::kWaveBytes);  // [BG+1] item prefix
-  {
-    int* tmp = pre + (kMaxGroups + 1);
-    for (int i = tid; i < BG; i += kAttnThreads) tmp[i] = (a.exp_count[i] + kExpChunk - 1) / kExpChunk;
-    __syncthreads();
-    if (wave == 0) {
-      int run = 0;
-      for (int c0 = 0; c0 < BG; c0 += 64) {
-        const int i = c0 + lane;
-        const int v = i < BG ? tmp[i] : 0;
-        int incl = v;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int t = __shfl_up(incl, off);
-          if (lane >= off) incl += t;
-        }
-        if (i < BG) pre[i] = run + incl - v;
-        run += __shfl(incl, 63);
-      }
-      if (lane == 0) pre[BG] = run;
+    for (int jj = 0; jj < K; ++jj) {
+      *reinterpret_cast<uint4*>(ring + ((written + 1024u * jj + 16u * (uint32_t)lane) & (RING - 1))) = stg[jj];
+      stg[jj] = gload16(cursor_addr(c, lane));
+      cursor_next(c, m);
     }
-    __syncthreads();
+    written += 1024u * K;
   }
-  const int total = pre[BG];
-  float* ut = reinterpret_cast<float*>(lds + wave * L_::kWaveBytes);  // [32][TS]
-  float* utt = ut + 32 * TS;                                           // [32][TS]
-  float* yb = utt + 32 * TS;                                           // [G][kMaxSpan]
-  float* stl = yb + G * kMaxSpan;                                      // [kMaxSpan]
-  const int nwaves = a.n_a5_wg * 4;
+  wave_lds_sync();
+}
+
+__device__ __forceinline__ uint32_t kb_round(uint32_t x) { return (x + 1023u) & ~1023u; }
+
+template <typename T, int D, int G, int RGM>
+__device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
+  using X = ExpLds<T, G, RGM>;
+  constexpr int K = ExpCfg<T, RGM>::K, RING = X::kRing;
+  constexpr uint32_t MASK = RING - 1;
+  constexpr int NC = D / 32, NJ = D / 16, ES = (int)sizeof(T), DG = D / 8;
+  const int lane = threadIdx.x;
+  const int col = lane & 15, cls = lane >> 4;
+  const int hc = min(col, G - 1);
+  char* ring = lds;
+  char* yb = lds + X::kY;
+  float* stl = reinterpret_cast<float*>(lds + X::kStl);
+  const int BG = a.B * a.Hkv;
   const bool staged = a.stage_off != nullptr;
   const float qscale = a.qscale;
 
-  for (int c = wg * 4 + wave; c < total; c += nwaves) {
-    int lo = 0, hi = BG;  // g with pre[g] <= c < pre[g+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pre[mid] <= c) lo = mid; else hi = mid;
+  // work items per group: lane holds groups 4 lane .. 4 lane + 3
+  int ip[4];
+  int own = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * lane + i;
+    const int c = g < BG ? a.exp_count[g] : 0;
+    ip[i] = own;
+    own += (c + kExpChunk - 1) / kExpChunk;
+  }
+  int incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  const int excl = incl - own;
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+
+  for (int c = wid; c < total; c += a.n_a5_wg) {
+    // group of item c: the last lane, then the last of its groups, starting at or before c
+    const uint64_t lm = __ballot(excl <= c);
+    const int ln = 63 - __builtin_clzll(lm);
+    const int lbase = __builtin_amdgcn_readlane(excl, ln);
+    int gi = 0, gstart = lbase;
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      const int st = lbase + __builtin_amdgcn_readlane(ip[i], ln);
+      if (st <= c) { gi = i; gstart = st; }
     }
-    const int g = lo, lc = c - pre[g];
+    const int g = 4 * ln + gi, lc = c - gstart;
     const int b = g / a.Hkv, kv = g % a.Hkv;
     const int cnt = a.exp_count[g];
     const int j0 = lc * kExpChunk, n = min(cnt, j0 + kExpChunk) - j0;
 
-    // metadata of the item's spans, lane i holds span j0 + i
+    // metadata of the item's spans: lane i holds span j0 + i
     const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
     const int jl = j0 + min(lane, n - 1);
     const int mS = a.exp_list[(size_t)g * a.seg_cap + jl];
@@ -676,12 +705,40 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
     }
     const int mL = so[mS + 1] - so[mS] - 1;
     const int mr = a.rank[(size_t)b * a.seg_cap + mS];
-    const T* fac_base = staged ? static_cast<const T*>(a.stage_fac) : static_cast<const T*>(a.fac);
-    const float* sg_base = staged ? a.stage_sg : a.sg;
+    const int mrp = (mr + 7) & ~7;
+    ItemMeta im;
+    {
+      const char* fb = static_cast<const char*>(staged ? a.stage_fac : a.fac);
+      const char* gb = reinterpret_cast<const char*>(staged ? a.stage_sg : a.sg);
+      im.sga = reinterpret_cast<uint64_t>(gb + mgo * 4);
+      im.fa = reinterpret_cast<uint64_t>(fb + mfo * ES);
+      im.sgb = 8u * (uint32_t)((mr + 3) & ~3);
+      im.fb = (uint32_t)ES * (uint32_t)(mr * D + mL * mrp + D * mrp);
+    }
+    // stream start of each span: both regions rounded up to whole chunks
+    const uint32_t mlen = lane < n ? kb_round(im.sgb) + kb_round(im.fb) : 0u;
+    uint32_t mend = mlen;
+#pragma unroll
+    for (int off = 1; off < kExpChunk; off <<= 1) {
+      const uint32_t t = __shfl_up(mend, off);
+      if (lane >= off) mend += t;
+    }
+    const int mstart = (int)(mend - mlen);
+
+    ChunkCursor cur;
+    cur.j = 0;
+    cur.reg = 0;
+    cur.n = n;
+    cur.off = 0;
+    cur.base = readlane64(im.sga, 0);
+    cur.size = (uint32_t)__builtin_amdgcn_readlane((int)im.sgb, 0);
+    uint4 stg[K];
+    uint32_t written = 0;
+    stage_first<K, RING>(stg, cur, im, lane);
 
     // q as the B operand of step 1: column = head (zero for columns >= G)
     Vec8<T> qB[NC];
-    const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G + min(col, G - 1)) * D;
+    const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G + hc) * D;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       qB[cc] = ld8(qrow + 32 * cc + 8 * cls);
@@ -692,132 +749,172 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) acc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    Vec8<T> vk[2][NC], ureg[2];
-    float sgr[4];
-    SpanMeta<T> cur = span_meta<T>(0, mL, mr, mbits, mfo, mgo, fac_base, sg_base);
-    issue_span_loads<T, D>(cur, col, cls, lane, vk, ureg, sgr);
-    for (int i = 0; i < n; ++i) {
-      const int L = cur.L, r = cur.r, rp = cur.rp;
-      const int RB = (r + 31) >> 5, TB = (L + 31) >> 5;
-      const bool head_on = (cur.bits >> col) & 1u;
-      const T* Wv = cur.U + (size_t)L * rp + (size_t)r * D;
-      // ---- sigma*gate (zero past r) and the first U tile into LDS
-      {
-        const float c0 = lane < r ? sgr[0] * sgr[1] : 0.0f;
-        const float c1 = lane + 64 < r ? sgr[2] * sgr[3] : 0.0f;
-        stl[lane] = c0;
-        stl[lane + 64] = c1;
+    // One loop over the item's pieces, so the ring producer is inlined once.
+    // Per span: piece 0 sigma|gate, then RG Vh_K rank groups (step 1), TG U
+    // token groups (steps 2-4), RG W_V blocks (step 5).
+    int L = 0, r = 0, rp = 8, rq = 4, RG = 0, TG = 0;
+    uint32_t bits = 0, s_sg = 0, s_vk = 0, s_u = 0, s_w = 0;
+    bool head_on = false;
+    f32x4_t am[RGM];
+    int i = -1, pc = 0, npc = 0;
+    for (;;) {
+      if (pc == npc) {
+        if (++i == n) break;
+        L = __builtin_amdgcn_readlane(mL, i);
+        r = __builtin_amdgcn_readlane(mr, i);
+        rp = (r + 7) & ~7;
+        rq = (r + 3) & ~3;
+        bits = (uint32_t)__builtin_amdgcn_readlane(mbits, i);
+        s_sg = (uint32_t)__builtin_amdgcn_readlane(mstart, i);
+        s_vk = s_sg + kb_round(8u * (uint32_t)rq);
+        s_u = s_vk + (uint32_t)(r * D * ES);
+        s_w = s_u + (uint32_t)(L * rp * ES);
+        RG = (r + 15) >> 4;
+        TG = (L + 15) >> 4;
+        head_on = (bits >> col) & 1u;
+        npc = 1 + 2 * RG + TG;
+        pc = 0;
+#pragma unroll
+        for (int rg = 0; rg < RGM; ++rg) am[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
-      stage_tile(cur, 0, 0, lane, ureg, ut, utt);
-      wave_lds_sync();
-      // ---- step 1, rank blocks of 32 (block 0 was prefetched)
-      for (int kb = 0; kb < RB; ++kb) {
-        if (kb > 0) ld_vk<T, NC>(cur, kb, col, cls, D, vk);
+      // end of the piece in the stream
+      uint32_t e;
+      if (pc == 0) e = s_sg + 8u * (uint32_t)rq;
+      else if (pc <= RG) e = s_vk + (uint32_t)(min(r, 16 * pc) * D * ES);
+      else if (pc <= RG + TG) e = s_u + (uint32_t)(min(L, 16 * (pc - RG)) * rp * ES);
+      else {
+        const int rg = pc - RG - TG - 1;
+        e = s_w + (uint32_t)((16 * rg * D + D * min(16, rp - 16 * rg)) * ES);
+      }
+      advance<K, RING>(stg, written, e, cur, im, lane, ring);
+
+      if (pc == 0) {
+        // sigma * gate (zero past r)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          f32x4_t yc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int k = lane + 64 * q2;
+          const int kc = min(k, r - 1);
+          const float sv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * kc) & MASK));
+          const float gv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * (rq + kc)) & MASK));
+          stl[k] = k < r ? sv * gv : 0.0f;
+        }
+      } else if (pc <= RG) {
+        // ---- step 1, rank group rg: rows 16 rg + col
+        const int rg = pc - 1;
+        const int k = min(16 * rg + col, r - 1);
+        f32x4_t yc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int cc = 0; cc < NC; ++cc) yc = mma8(vk[h][cc], qB[cc], yc);
-          if (col < G) {
+        for (int cc = 0; cc < NC; ++cc) {
+          const int pg = (4 * cc + cls + k) & (DG - 1);   // rotated 8-element group
+          yc = mma8(rd8<T>(ring, (s_vk + (uint32_t)((k * D + 8 * pg) * ES)) & MASK, MASK), qB[cc], yc);
+        }
+        // rows 16 rg + 4 cls + v of head col
+        const float4 sg4 = *reinterpret_cast<const float4*>(stl + 16 * rg + 4 * cls);
+        float y[4] = {yc[0] * qscale * sg4.x, yc[1] * qscale * sg4.y, yc[2] * qscale * sg4.z, yc[3] * qscale * sg4.w};
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int k = kb * 32 + 8 * cls + 4 * h + v;
-              yb[col * kMaxSpan + k] = yc[v] * qscale * stl[k];
+        for (int v = 0; v < 4; ++v) y[v] = (16 * rg + 4 * cls + v < r) ? y[v] : 0.0f;
+        if (col < G) {
+          char* dst = yb + ((rg * 4 + cls) * G + col) * 16;
+          if constexpr (ES == 2) {
+            Vec4<bf16raw> hi, lo;
+            pack4(y, hi);
+            float rem[4] = {y[0] - __uint_as_float(hi.v.x << 16), y[1] - __uint_as_float(hi.v.x & 0xffff0000u),
+                            y[2] - __uint_as_float(hi.v.y << 16), y[3] - __uint_as_float(hi.v.y & 0xffff0000u)};
+            pack4(rem, lo);
+            *reinterpret_cast<uint4*>(dst) = make_uint4(hi.v.x, hi.v.y, lo.v.x, lo.v.y);
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+          }
+        }
+      } else if (pc <= RG + TG) {
+        // ---- steps 2-4, token group tg (online softmax across groups and spans)
+        const int tg = pc - RG - 1;
+        const int trow = min(16 * tg + col, L - 1);
+        f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int rg = 0; rg < RGM; ++rg) {
+          if (rg < RG) {
+            const uint4 yv = *reinterpret_cast<const uint4*>(yb + ((rg * 4 + cls) * G + hc) * 16);
+            const int k0 = min(16 * rg + 4 * cls, rp - 4);
+            const Vec4<T> uop = rd4<T>(ring, (s_u + (uint32_t)((trow * rp + k0) * ES)) & MASK);
+            if constexpr (ES == 2) {
+              sc = mma4(uop, Vec4<bf16raw>{make_uint2(yv.x, yv.y)}, sc);
+              sc = mma4(uop, Vec4<bf16raw>{make_uint2(yv.z, yv.w)}, sc);
+            } else {
+              sc = mma4(uop, Vec4<float>{make_float4(__uint_as_float(yv.x), __uint_as_float(yv.y),
+                                                     __uint_as_float(yv.z), __uint_as_float(yv.w))}, sc);
             }
           }
         }
-      }
-      // value-part rows (W_V, rank block 0) for step 5, then span i+1's loads
-      Vec8<T> wv[NJ];
-      {
-        const int k8 = min(8 * cls, rp - 8);
+        // scores of tokens 16 tg + 4 cls + v for head col
+        float sv[4];
+        float mt = kNegInf;
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) wv[jt] = ld8(Wv + (size_t)(16 * jt + col) * rp + k8);
-      }
-      const SpanMeta<T> nxt = span_meta<T>(min(i + 1, n - 1), mL, mr, mbits, mfo, mgo, fac_base, sg_base);
-      issue_span_loads<T, D>(nxt, col, cls, lane, vk, ureg, sgr);
-      wave_lds_sync();
-
-      // ---- steps 2-5.  r <= L, so a span with one token block (L <= 32, almost
-      // all) has one rank block and its single U tile is already staged.  Longer
-      // spans take two passes: the span maximum first, then per rank block the
-      // weights and U^T p, re-staging tiles as needed.
-      float sv0[8];
-      float mt = kNegInf;
-      for (int tb = 0; tb < TB; ++tb) {
-        f32x4_t sc[2];
-        tile_scores<T, G>(cur, tb, RB, col, cls, lane, yb, ut, utt, TB > 1 || RB > 1, sc);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int t = tb * 32 + 8 * cls + 4 * h + v;
-            const float x = (head_on && t < L) ? sc[h][v] : kNegInf;
-            sv0[4 * h + v] = x;
-            mt = fmaxf(mt, x);
-          }
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m, mt);
-      if (mn != kNegInf) {
-        const float alpha = exp2f(m - mn);
-        lsum *= alpha;
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) acc[jt] *= alpha;
-        m = mn;
-      }
-      for (int kb = 0; kb < RB; ++kb) {
-        f32x4_t am[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
-        for (int tb = 0; tb < TB; ++tb) {
-          float sv[8];
-          if (TB == 1) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sv[e] = sv0[e];
-          } else {
-            f32x4_t sc[2];
-            tile_scores<T, G>(cur, tb, RB, col, cls, lane, yb, ut, utt, true, sc);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const int t = tb * 32 + 8 * cls + 4 * h + v;
-                sv[4 * h + v] = (head_on && t < L) ? sc[h][v] : kNegInf;
-              }
-            restage_tile(cur, tb, kb, lane, ut, utt);
-          }
-          float pr[8];
-          float ps = 0.0f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pr[e] = (m == kNegInf) ? 0.0f : exp2f(sv[e] - m);
-            ps += pr[e];
-          }
-          if (kb == 0) lsum += ps;
-          Vec8<float> pv;
-          pack8(pr, pv);
-          // step 4: a[k][h] += sum_t U[t][k] p[t][h]
-#pragma unroll
-          for (int h = 0; h < 2; ++h) am[h] = mma8(lds8f(utt + half_row(col, h) * TS + 8 * cls), pv, am[h]);
+        for (int v = 0; v < 4; ++v) {
+          const float x = (head_on && 16 * tg + 4 * cls + v < L) ? sc[v] : kNegInf;
+          sv[v] = x;
+          mt = fmaxf(mt, x);
         }
-        // step 5: o[j][h] += sum_k W_V[j][k] b[k][h],  b = sigma*gate * a
-        if (kb > 0) {
-          const int k8 = min(kb * 32 + 8 * cls, rp - 8);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        if (mn != kNegInf && mn != m) {
+          const float alpha = exp2f(m - mn);
+          lsum *= alpha;
 #pragma unroll
-          for (int jt = 0; jt < NJ; ++jt) wv[jt] = ld8(Wv + (size_t)(16 * jt + col) * rp + k8);
+          for (int jt = 0; jt < NJ; ++jt) acc[jt] *= alpha;
+#pragma unroll
+          for (int rg = 0; rg < RGM; ++rg)
+            if (rg < RG) am[rg] *= alpha;
+          m = mn;
         }
-        float bv[8];
+        float pr[4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int v = 0; v < 4; ++v) {
+          pr[v] = (m == kNegInf) ? 0.0f : exp2f(sv[v] - m);
+          lsum += pr[v];
+        }
+        Vec4<T> pB;
+        pack4(pr, pB);
+        // step 4: a[k][h] += sum_t U[t][k] p[t][h], rows k = 16 rg + col
 #pragma unroll
-          for (int v = 0; v < 4; ++v) bv[4 * h + v] = am[h][v] * stl[kb * 32 + 8 * cls + 4 * h + v];
-        Vec8<T> bp;
-        pack8(bv, bp);
+        for (int rg = 0; rg < RGM; ++rg) {
+          if (rg < RG) {
+            const int kc = min(16 * rg + col, rp - 1);
+            uint32_t ev[4];
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) acc[jt] = mma8(wv[jt], bp, acc[jt]);
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int t = min(16 * tg + 4 * cls + e4, L - 1);
+              const uint32_t ob = (s_u + (uint32_t)((t * rp + kc) * ES)) & MASK;
+              if constexpr (ES == 2) ev[e4] = *reinterpret_cast<const uint16_t*>(ring + ob);
+              else ev[e4] = *reinterpret_cast<const uint32_t*>(ring + ob);
+            }
+            Vec4<T> uop;
+            if constexpr (ES == 2) uop.v = make_uint2(ev[0] | (ev[1] << 16), ev[2] | (ev[3] << 16));
+            else uop.v = make_float4(__uint_as_float(ev[0]), __uint_as_float(ev[1]), __uint_as_float(ev[2]),
+                                     __uint_as_float(ev[3]));
+            am[rg] = mma4(uop, pB, am[rg]);
+          }
+        }
+      } else {
+        // ---- step 5, W_V block rg: b = sigma*gate * a
+        const int rg = pc - RG - TG - 1;
+        const int wk = min(16, rp - 16 * rg);
+        const uint32_t s_wg = s_w + (uint32_t)(16 * rg * D * ES);
+        const float4 sg4 = *reinterpret_cast<const float4*>(stl + 16 * rg + 4 * cls);
+        f32x4_t ar = am[0];
+#pragma unroll
+        for (int q2 = 1; q2 < RGM; ++q2) ar = (q2 == rg) ? am[q2] : ar;
+        const float bv[4] = {ar[0] * sg4.x, ar[1] * sg4.y, ar[2] * sg4.z, ar[3] * sg4.w};
+        Vec4<T> bB;
+        pack4(bv, bB);
+        const int k0 = min(4 * cls, wk - 4);
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt)
+          acc[jt] = mma4(rd4<T>(ring, (s_wg + (uint32_t)(((16 * jt + col) * wk + k0) * ES)) & MASK), bB, acc[jt]);
       }
       wave_lds_sync();
-      cur = nxt;
+      ++pc;
     }
     // partial of this item: head col, summed over the four lane classes
     lsum += __shfl_xor(lsum, 16);
@@ -835,6 +932,7 @@ __device__ void role_expanded(const AttendArgs& a, int wg, char* lds) {
         pml[col * 2 + 1] = lsum;
       }
     }
+    wave_lds_sync();
   }
 }
 
@@ -846,13 +944,18 @@ __global__ __launch_bounds__(kAttnThreads) void attend_full_kernel(const AttendA
   extern __shared__ __align__(16) char lds[];
   role_full_summary<T, D, G>(a, blockIdx.x, lds);
 }
-// Two waves per SIMD: the span steps are latency-bound, and a second resident wave hides
-// more of it than the few registers spilled to reach 256 VGPRs cost.
+// Ranks up to 64 (four rank groups in registers): two waves per SIMD.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kExpThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attend_expanded_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
-  role_expanded<T, D, G>(a, blockIdx.x, lds);
+  role_expanded<T, D, G, 4>(a, blockIdx.x, lds);
+}
+// Any rank up to kMaxSpan.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kExpThreads) void attend_expanded_wide_kernel(const AttendArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  role_expanded<T, D, G, kMaxSpan / 16>(a, blockIdx.x, lds);
 }
 
 // ================================================================ combine
@@ -944,9 +1047,10 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
     const int L = so[S + 1] - so[S] - 1;
     const int r = a.rank[(size_t)b * a.seg_cap + S];
     const int rp = (r + 7) & ~7;
-    const T* Ub = static_cast<const T*>(a.fac) + a.fac_off[(size_t)g * a.seg_cap + S];
-    const T* Vk = Ub + (size_t)L * rp;            // key part   [r][D]
-    const T* Wv = Vk + (size_t)r * D;             // value part [D][rp]
+    const T* Vk = static_cast<const T*>(a.fac) + a.fac_off[(size_t)g * a.seg_cap + S];  // key part [r][D], rotated groups
+    const T* Ub = Vk + (size_t)r * D;             // U [L][rp]
+    const T* Wv = Ub + (size_t)L * rp;            // value part, 16-rank column blocks [D][wk]
+    const int rq = (r + 3) & ~3;
     const float* sgp = a.sg + a.sg_off[(size_t)g * a.seg_cap + S];
     const int row0 = a.tok_off[(size_t)g * (a.seg_cap + 1) + j];
     for (int t = 0; t < L; ++t) {
@@ -954,11 +1058,13 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
       for (int k = 0; k < r; ++k) {
-        const float w = load1(Ub + (size_t)t * rp + k) * (sgp[k] * sgp[r + k]);
+        const float w = load1(Ub + (size_t)t * rp + k) * (sgp[k] * sgp[rq + k]);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const int colj = lane + 64 * c;
-          acc[c] += w * (colj < D ? load1(Vk + (size_t)k * D + colj) : load1(Wv + (size_t)(colj - D) * rp + k));
+          const int kg = k >> 4, wk = min(16, rp - 16 * kg);
+          acc[c] += w * (colj < D ? load1(Vk + (size_t)k * D + (((colj >> 3) + k) % (D / 8)) * 8 + (colj & 7))
+                                  : load1(Wv + (size_t)kg * 16 * D + (size_t)(colj - D) * wk + (k & 15)));
         }
       }
       const size_t orow = ((size_t)g * a.T + row0 + t) * D;
@@ -1027,7 +1133,10 @@ hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   if (a.n_a5_wg == 0) return hipSuccess;
   SEKV_DISPATCH(a.dtype, a.D, G,
-                (attend_expanded_kernel<TT, DD, GG><<<a.n_a5_wg, kAttnThreads, AttnLds<DD, GG>::kRoleE, s>>>(a)));
+                (a.max_rank <= 64
+                     ? attend_expanded_kernel<TT, DD, GG><<<a.n_a5_wg, kExpThreads, ExpLds<TT, GG, 4>::kBytes, s>>>(a)
+                     : attend_expanded_wide_kernel<TT, DD, GG>
+                           <<<a.n_a5_wg, kExpThreads, ExpLds<TT, GG, kMaxSpan / 16>::kBytes, s>>>(a)));
   return hipGetLastError();
 }
 

@@ -89,13 +89,18 @@ typedef struct sekv_config {
  *   rank [B][seg_cap] int32: r_i, 1 <= r_i <= min(L_i, 2d), shared by all KV
  *       heads of the span.  [de-2], [zh-2] (adaptive rank budget).
  *   fac pool (dtype): for span (b, kv, i) a block at element offset
- *       fac_off[b][kv][i] (a multiple of 8) holding, with rp = ceil(r_i/8)*8,
- *       U [L_i][rp] (row stride rp, padding zero), then the key part of the
- *       right singular vectors Vh_K [r_i][d], then the value part transposed,
- *       W_V [d][rp] (W_V[j][k] = Vh[k][d + j], padding zero).  Block size
- *       L_i*rp + r_i*d + d*rp elements.
- *   sg pool (float32): for span (b, kv, i) sigma[r_i] then gate[r_i] at offset
- *       sg_off[b][kv][i].  Token keys of the span are U diag(sigma*gate) Vh_K,
+ *       fac_off[b][kv][i] (a multiple of 8) holding, with rp = ceil(r_i/8)*8:
+ *       the key part of the right singular vectors Vh_K [r_i][d], where row
+ *       k stores its d/8 groups of 8 elements rotated by k (group u at
+ *       position (u + k) mod d/8, so that rows read side by side fall on
+ *       different LDS banks); then U [L_i][rp] (row stride rp, padding
+ *       zero); then the value part transposed, W_V[j][k] = Vh[k][d + j],
+ *       stored as column blocks of 16 ranks: block g = k / 16 of width
+ *       wk = min(16, rp - 16 g) is [d][wk] row-major at block offset 16 g d
+ *       (padding zero).  Block size r_i*d + L_i*rp + d*rp elements.
+ *   sg pool (float32): for span (b, kv, i) an entry at offset sg_off[b][kv][i]
+ *       (a multiple of 4): sigma[rq] then gate[rq], rq = ceil(r_i/4)*4,
+ *       padding zero.  Token keys of the span are U diag(sigma*gate) Vh_K,
  *       token values U diag(sigma*gate) W_V^T.
  *       [abstract], [de-2], [zh-2].
  *

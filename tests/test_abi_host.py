@@ -66,7 +66,7 @@ def test_plan_matches_oracle_on_workload(wid):
         want_r = np.minimum(np.minimum(x.rank_req[b, :n], L), 2 * w.head_dim)
         assert p.rank[b, :n].tolist() == want_r.tolist()
         assert np.all(p.rank[b, n:] == 0)
-    # pool layout: blocks are contiguous, 8-element aligned, in (b, kv, span) order
+    # pool layout: blocks are contiguous, 8-element (fac) / 4-float (sg) aligned, in (b, kv, span) order
     off = 0
     goff = 0
     for b in range(w.batch):
@@ -76,9 +76,9 @@ def test_plan_matches_oracle_on_workload(wid):
                 r = int(p.rank[b, i])
                 L = int(so[i + 1] - so[i] - 1)
                 assert p.fac_off[b, kv, i] == off and off % 8 == 0
-                assert p.sg_off[b, kv, i] == goff
+                assert p.sg_off[b, kv, i] == goff and goff % 4 == 0
                 off += B.fac_block_elems(L, r, w.head_dim)
-                goff += 2 * r
+                goff += B.sg_entry_elems(r)
     assert p.fac_elems == off and p.sg_elems == goff
 
 

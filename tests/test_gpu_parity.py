@@ -29,6 +29,8 @@ CASES = {
     "bf16-g2-T2500-wide-rank": dict(wid=5, over=dict(n_ctx=2500, batch=2, n_q_heads=8, n_kv_heads=4, min_span=2,
                                                      max_span=128, rank_lo=30, rank_hi=128, boundary_quantile=0.995),
                                     steps=[0], frac=0.3),
+    "f32-d64-T3000-wide-rank": dict(wid=1, over=dict(n_ctx=3000, min_span=2, max_span=128, rank_lo=40, rank_hi=128,
+                                                     boundary_quantile=0.995), steps=[0], frac=0.3),
     "f32-len1-spans": dict(wid=1, over=dict(n_ctx=700, min_span=1, max_span=1), steps=[0, 1]),
     "f32-no-spans": dict(wid=1, over=dict(n_ctx=69, n_recent=64, n_sink=4), steps=[0]),
     "bf16-one-span": dict(wid=2, over=dict(n_ctx=300, n_recent=200, n_sink=4, min_span=8, max_span=128), steps=[0]),
