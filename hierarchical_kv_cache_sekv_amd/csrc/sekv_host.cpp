@@ -689,7 +689,7 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
 
 size_t sekv_route_workspace_bytes(const sekv_config* c, const sekv_spans* s) {
   if (check_config(c) != SEKV_OK || !s) return 0;
-  return align_up((size_t)c->batch * c->n_kv_heads * s->seg_cap);
+  return align_up((size_t)c->batch * c->n_kv_heads * (((size_t)s->seg_cap + 15) & ~(size_t)15));
 }
 
 sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q, const float* theta,
@@ -709,6 +709,7 @@ sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s,
   int mx = 0;
   for (int b = 0; b < c->batch; ++b) { a.n_seg[b] = s->n_seg_host[b]; mx = std::max(mx, s->n_seg_host[b]); }
   a.nblk = std::max(1, (mx + kRouteThreads - 1) / kRouteThreads);
+  a.mstride = (s->seg_cap + 15) & ~15;
   a.q = q; a.theta = theta; a.rho = s->rho;
   a.dmask = static_cast<uint8_t*>(ws);
   a.exp_list = exp_list; a.exp_mask = exp_mask; a.exp_count = exp_count;

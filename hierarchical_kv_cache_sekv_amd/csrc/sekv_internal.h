@@ -19,11 +19,12 @@ constexpr int kExpWaves = 4096;      // most waves (workgroups) of one expanded-
 struct RouteArgs {
   int dtype;                 // 0 f32, 1 bf16
   int B, Hq, Hkv, D, seg_cap, nblk;
+  int mstride;               // row stride of dmask: seg_cap rounded up to 16
   int n_seg[kMaxBatch];
   const void* q;             // [B][Hq][D]
   const float* theta;        // [B][Hq]
   const void* rho;           // [B][Hkv][seg_cap][D]
-  uint8_t* dmask;            // [B][Hkv][seg_cap] workspace
+  uint8_t* dmask;            // [B][Hkv][mstride] workspace
   int32_t* exp_list;         // [B][Hkv][seg_cap]
   uint8_t* exp_mask;         // [B][Hkv][seg_cap]
   int32_t* exp_count;        // [B][Hkv]

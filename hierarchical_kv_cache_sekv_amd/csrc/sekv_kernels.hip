@@ -184,71 +184,116 @@ constexpr float kNegInf = -__builtin_inff();
 // the per-span head mask; route_compact_kernel (one workgroup per (b, kv))
 // turns it into the ascending list.  The kernel boundary makes the masks
 // visible across XCDs; no device-scope fence is needed inside either kernel.
+//
+// route_decide_kernel: a workgroup takes 256 consecutive spans of one (b, kv).
+// Their routing keys are staged through LDS 128 bytes of each row at a time
+// (coalesced 16-byte loads, 8 lanes per row), padded to a 144-byte row stride
+// so that each lane then reads its own row without bank conflicts.
+constexpr int kRouteRowBytes = 128;
+constexpr int kRouteRowStride = 144;
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kRouteThreads) void route_decide_kernel(const RouteArgs a) {
+  constexpr int EPP = kRouteRowBytes / (int)sizeof(T);   // elements of a row per pass
+  constexpr int NP = D / EPP;
   __shared__ float qs[G * D];
+  __shared__ __align__(16) char tile[kRouteThreads * kRouteRowStride];
   const int blk = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int g = b * a.Hkv + kv;
   const int ns = a.n_seg[b];
-  if (blk * kRouteThreads >= ns) return;
+  const int S0 = blk * kRouteThreads;
+  if (S0 >= ns) return;
+  const int nrow = min(kRouteThreads, ns - S0);
   const T* q = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
   for (int i = tid; i < G * D; i += kRouteThreads) qs[i] = load1(q + i);
   float th[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) th[gi] = a.theta[(size_t)b * a.Hq + kv * G + gi];
-  __syncthreads();
+  const char* rbase = static_cast<const char*>(a.rho) + ((size_t)g * a.seg_cap + S0) * D * sizeof(T);
 
-  const int S = blk * kRouteThreads + tid;
-  if (S >= ns) return;
-  const T* r = static_cast<const T*>(a.rho) + ((size_t)g * a.seg_cap + S) * D;
   float z[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) z[gi] = 0.0f;
-#pragma unroll 2
-  for (int c = 0; c < D; c += 8) {
-    float rv[8];
-    load8(r + c, rv);
+  for (int p = 0; p < NP; ++p) {
+    uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < 8; ++j) {
+      const int piece = tid + kRouteThreads * j, row = piece >> 3, c = piece & 7;
+      v[j] = row < nrow ? *reinterpret_cast<const uint4*>(rbase + (size_t)row * D * sizeof(T) + p * kRouteRowBytes + c * 16)
+                        : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();  // the previous pass's row reads (and the q staging) are done
 #pragma unroll
-      for (int gi = 0; gi < G; ++gi) {
+    for (int j = 0; j < 8; ++j) {
+      const int piece = tid + kRouteThreads * j, row = piece >> 3, c = piece & 7;
+      *reinterpret_cast<uint4*>(tile + row * kRouteRowStride + c * 16) = v[j];
+    }
+    __syncthreads();
+    if (tid < nrow) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float rv[16 / sizeof(T)];
+        const uint4 u = *reinterpret_cast<const uint4*>(tile + tid * kRouteRowStride + c * 16);
+        if constexpr (sizeof(T) == 2) {
+          rv[0] = __uint_as_float(u.x << 16); rv[1] = __uint_as_float(u.x & 0xffff0000u);
+          rv[2] = __uint_as_float(u.y << 16); rv[3] = __uint_as_float(u.y & 0xffff0000u);
+          rv[4] = __uint_as_float(u.z << 16); rv[5] = __uint_as_float(u.z & 0xffff0000u);
+          rv[6] = __uint_as_float(u.w << 16); rv[7] = __uint_as_float(u.w & 0xffff0000u);
+        } else {
+          rv[0] = __uint_as_float(u.x); rv[1] = __uint_as_float(u.y);
+          rv[2] = __uint_as_float(u.z); rv[3] = __uint_as_float(u.w);
+        }
+        const int i0 = p * EPP + c * (int)(16 / sizeof(T));
+#pragma unroll
+        for (int e = 0; e < (int)(16 / sizeof(T)); ++e) {
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) {
 #pragma clang fp contract(off)
-        const float prod = qs[gi * D + c + i] * rv[i];
-        z[gi] = z[gi] + prod;
+            const float prod = qs[gi * D + i0 + e] * rv[e];
+            z[gi] = z[gi] + prod;
+          }
+        }
       }
     }
   }
-  uint32_t bits = 0;
+  if (tid < nrow) {
+    uint32_t bits = 0;
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi) bits |= (z[gi] > th[gi] ? 1u : 0u) << gi;
-  a.dmask[(size_t)g * a.seg_cap + S] = (uint8_t)bits;
+    for (int gi = 0; gi < G; ++gi) bits |= (z[gi] > th[gi] ? 1u : 0u) << gi;
+    a.dmask[(size_t)g * a.mstride + S0 + tid] = (uint8_t)bits;
+  }
 }
 
-// One workgroup per (b, kv).  The masks are staged in LDS by tiles with
-// coalesced loads; each thread then takes a contiguous run of spans, counts the
-// expanded ones, one block-wide exclusive scan gives its output position.
-constexpr int kCompactTile = 16384;
+// Four bits, one per byte of w: set where the byte is nonzero.
+__device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t w) {
+  const uint32_t hi = ((((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u) >> 7;  // bits 0, 8, 16, 24
+  return ((hi * 0x00204081u) >> 21) & 0xFu;
+}
+__device__ __forceinline__ uint32_t nonzero_bytes16(const uint4& m) {
+  return nonzero_bytes4(m.x) | (nonzero_bytes4(m.y) << 4) | (nonzero_bytes4(m.z) << 8) | (nonzero_bytes4(m.w) << 12);
+}
+// One workgroup per (b, kv).  Each thread reads the masks of 32 consecutive
+// spans (two 16-byte loads), turns them into a 32-bit "expanded" set, and one
+// block-wide exclusive scan of the set sizes gives its output position.
 __global__ __launch_bounds__(kRouteThreads) void route_compact_kernel(const RouteArgs a) {
   __shared__ int wsum[kRouteThreads / 64];
-  __shared__ uint8_t tile[kCompactTile];
   const int kv = blockIdx.x, b = blockIdx.y;
   const int g = b * a.Hkv + kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ns = a.n_seg[b];
-  const uint8_t* dm = a.dmask + (size_t)g * a.seg_cap;
+  const uint8_t* dm = a.dmask + (size_t)g * a.mstride;
   int32_t* lst = a.exp_list + (size_t)g * a.seg_cap;
   uint8_t* msk = a.exp_mask + (size_t)g * a.seg_cap;
   int base = 0;
-  for (int t0 = 0; t0 < ns; t0 += kCompactTile) {
-    const int n = min(kCompactTile, ns - t0);
-#pragma unroll 8
-    for (int i = tid; i < n; i += kRouteThreads) tile[i] = dm[t0 + i];
-    __syncthreads();
-    const int per = (n + kRouteThreads - 1) / kRouteThreads;
-    const int s0 = min(n, tid * per), s1 = min(n, s0 + per);
-    int c = 0;
-    for (int S = s0; S < s1; ++S) c += tile[S] != 0;
+  for (int t0 = 0; t0 < ns; t0 += 32 * kRouteThreads) {
+    const int s0 = t0 + 32 * tid;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    const uint4 m0 = s0 < ns ? *reinterpret_cast<const uint4*>(dm + s0) : zero;
+    const uint4 m1 = s0 + 16 < ns ? *reinterpret_cast<const uint4*>(dm + s0 + 16) : zero;
+    uint32_t nz = nonzero_bytes16(m0) | (nonzero_bytes16(m1) << 16);
+    const int valid = ns - s0;
+    if (valid < 32) nz &= valid <= 0 ? 0u : ((1u << valid) - 1u);
+    const int c = __popc(nz);
     int incl = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -265,11 +310,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_compact_kernel(const Rout
       total += v;
     }
     int pos = base + wbase + incl - c;
-    for (int S = s0; S < s1; ++S) {
-      const uint8_t m = tile[S];
-      if (m) {
-        lst[pos] = t0 + S;
-        msk[pos] = m;
+    const uint32_t words[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (nz & (1u << k)) {
+        lst[pos] = s0 + k;
+        msk[pos] = (uint8_t)(words[k >> 2] >> (8 * (k & 3)));
         ++pos;
       }
     }
