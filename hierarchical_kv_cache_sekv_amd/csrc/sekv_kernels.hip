@@ -214,19 +214,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_decide_kernel(const Route
   float z[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) z[gi] = 0.0f;
-  for (int p = 0; p < NP; ++p) {
-    uint4 v[8];
+  // every pass's loads are issued up front (one memory round trip per workgroup)
+  uint4 v[NP][8];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int piece = tid + kRouteThreads * j, row = piece >> 3, c = piece & 7;
-      v[j] = row < nrow ? *reinterpret_cast<const uint4*>(rbase + (size_t)row * D * sizeof(T) + p * kRouteRowBytes + c * 16)
-                        : make_uint4(0, 0, 0, 0);
+      v[p][j] = row < nrow ? *reinterpret_cast<const uint4*>(rbase + (size_t)row * D * sizeof(T) + p * kRouteRowBytes + c * 16)
+                           : make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
     __syncthreads();  // the previous pass's row reads (and the q staging) are done
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int piece = tid + kRouteThreads * j, row = piece >> 3, c = piece & 7;
-      *reinterpret_cast<uint4*>(tile + row * kRouteRowStride + c * 16) = v[j];
+      *reinterpret_cast<uint4*>(tile + row * kRouteRowStride + c * 16) = v[p][j];
     }
     __syncthreads();
     if (tid < nrow) {
@@ -517,43 +521,50 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
 }
 
 // Role E (expanded spans): one wave per workgroup.  A work item is up to
-// kExpChunk consecutive entries of one (b, kv) expanded list.  The item's
-// factor data is consumed as one stream of 1 KB chunks: per span, its
-// sigma|gate entry (sg pool) and then its factor block
-//   Vh_K [r][d] (8-element groups rotated by the row) | U [L][rp] |
-//   W_V in 16-rank column blocks [d][min(16, rp - 16 g)],
-// each region starting on a chunk boundary.  A chunk is 16 bytes per lane,
-// loaded into registers one granule (ExpCfg::K chunks) ahead of the consumer
-// and written to a per-wave LDS ring a granule at a time, so the latency of
-// the next granule overlaps the arithmetic on the current one.  Lanes past
-// the end of a region re-read its last 16 bytes (no extra memory lines).
-// Every MFMA operand is then read from the ring.  For head h = lane % 16
-// (columns >= G unused), per span, in rank groups g and token groups of 16:
-//   step 1  y[k][h] = sigma_k gate_k (Vh_K[k] . q_h) log2(e)/sqrt(d)   A = Vh_K rows, B = q
-//   step 2  s[t][h] = U[t] . y[:, h]                                  A = U rows,    B = y
-//   step 3  online softmax over the span's tokens (log2 domain)
-//   step 4  a[k][h] = sum_t U[t][k] p[t][h]                           A = U^T rows,  B = p
-//   step 5  o[j][h] += sum_k W_V[j][k] sigma_k gate_k a[k][h]         A = W_V rows,  B = b
-// Steps 2, 4 and 5 are 16x16x16 products: the result of each (lane 16c + h
-// holds rows 4c..4c+3 of column h) is exactly the B operand the next one
-// takes, so nothing moves between lanes.  bf16: y enters step 2 as a
-// two-term bf16 split (hi + lo, about 16 significant bits), p and b are
-// rounded to bf16; float: every step in float32.
+// kExpChunk consecutive entries of one (b, kv) expanded list, processed in
+// chunks of consecutive spans whose token groups fit the wave's score
+// buffer.  Per chunk, two passes:
+//   pass 1, per span: y[k][h] = sigma_k gate_k (Vh_K[k] . q_h) log2(e)/sqrt(d)
+//           (A = Vh_K rows, B = q) and the token scores s[t][h] = U[t] . y[:, h]
+//           (A = U rows, B = y), kept in LDS; the chunk's maximum per head.
+//   pass 2, per span: p = exp2(s - m), a[k][h] = sum_t U[t][k] p[t][h]
+//           (A = U^T rows, B = p) and o[j][h] += sum_k W_V[j][k] sigma_k gate_k a[k][h]
+//           (A = W_V rows, B = b).
+// With the chunk maximum known before pass 2, the output accumulators are
+// rescaled once per chunk, not per span, and the two passes keep different
+// registers live.  Head h = lane % 16 (columns >= G unused); ranks and tokens
+// in groups of 16.  The products of scores, U^T p and W_V b are 16x16x16: the
+// result of each (lane 16c + h holds rows 4c..4c+3 of column h) is exactly
+// the B operand the next one takes, so nothing moves between lanes.  bf16: y
+// enters the score product as a two-term bf16 split (hi + lo, about 16
+// significant bits), p and b are rounded to bf16; float: every product in
+// float32.
+//
+// Factor data streams through a per-wave LDS ring in 1 KB chunks (16 bytes
+// per lane), loaded into registers one granule (ExpCfg::K chunks) ahead of
+// the consumer and written to the ring a granule at a time.  The stream is a
+// sequence of regions, each starting on a chunk boundary; per chunk of spans:
+//   pass 1: for each span  sigma|gate entry, then Vh_K | U (contiguous),
+//   pass 2: for each span  sigma|gate entry, then U | W_V (contiguous).
+// Factor block of a span: Vh_K [r][d] (8-element groups rotated by the row) |
+// U [L][rp] | W_V in 16-rank column blocks [d][min(16, rp - 16 g)].  Lanes
+// past the end of a region re-read its last 16 bytes (no extra memory lines).
+// U is read twice (about 6% of a span's factor bytes).
+template <typename T, int RGM> struct ExpCfg;
 // K: 1 KB chunks per granule in flight.  The ring holds a granule in flight
 // plus the largest piece read at once (16 rows of Vh_K or U, or one 16-rank
-// W_V block: 16 x 128 elements).  RGM: rank groups of 16 held in registers
-// (4: ranks up to 64, two waves per SIMD; 8: any rank, one wave per SIMD).
-template <typename T, int RGM> struct ExpCfg { static constexpr int K = 8; static constexpr int kRing = 16384; };
-template <> struct ExpCfg<bf16raw, 4> { static constexpr int K = 4; static constexpr int kRing = 8192; };
+// W_V block: 16 x 128 elements).
+template <int RGM> struct ExpCfg<bf16raw, RGM> { static constexpr int K = 4; static constexpr int kRing = 8192; };
+template <int RGM> struct ExpCfg<float, RGM> { static constexpr int K = 8; static constexpr int kRing = 16384; };
+constexpr int kExpTok = 256;   // tokens of one chunk of spans (score buffer)
 
 template <typename T, int G, int RGM>
 struct ExpLds {
   static constexpr int kRing = ExpCfg<T, RGM>::kRing;
   static_assert((kRing & (kRing - 1)) == 0, "ring size is a power of two");
   static_assert(kRing >= ExpCfg<T, RGM>::K * 1024 + 16 * kMaxSpan * (int)sizeof(T), "ring holds a granule and a piece");
-  static constexpr int kY = kRing;                          // y [rank group][class][G] 16 bytes
-  static constexpr int kStl = kY + RGM * 4 * G * 16;
-  static constexpr int kBytes = kStl + kMaxSpan * 4;        // sigma*gate [kMaxSpan] float
+  static constexpr int kS = kRing;                          // scores [token group][class][G] float4
+  static constexpr int kBytes = kS + (kExpTok / 16) * 4 * G * 16;
 };
 
 // Four elements of the storage type as an MFMA operand of a 16x16x16 product.
@@ -605,6 +616,21 @@ __device__ __forceinline__ Vec8<T> rd8(const char* ring, uint32_t ob, uint32_t m
   return x;
 }
 
+// Maximum and sum over the four 16-lane rows, same position in each row
+// (lanes h, h + 16, h + 32, h + 48): row swaps on the VALU, no LDS.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // 16 bytes from a global byte address (address space 1: a global load, not a
 // flat one that would also count against the LDS counter).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -619,70 +645,88 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t x, int i) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(x & 0xffffffffu), i);
   return ((uint64_t)hi << 32) | lo;
 }
+__device__ __forceinline__ uint32_t kb_round(uint32_t x) { return (x + 1023u) & ~1023u; }
 
-// Producer of the chunk stream (wave-uniform state): region `reg` (0 sg
-// entry, 1 factor block) of span j, at byte `off` of a region of `size`
-// bytes starting at global address `base`.  Past the last span the final
-// chunk is repeated (it is never read from the ring).
-struct ChunkCursor {
-  int j, reg, n;
+// Per-lane metadata of an item (lane i < n: span i of the item).
+struct ItemMeta {
+  int L, r, bits;
+  uint64_t sga, fa;   // global addresses of the sg entry and the factor block
+};
+// Region `kind` of span i: 0 / 2 sigma|gate, 1 Vh_K | U, 3 U | W_V.
+template <typename T, int D>
+__device__ __forceinline__ void region_of(const ItemMeta& m, int i, int kind, uint64_t& base, uint32_t& size) {
+  constexpr uint32_t ES = sizeof(T);
+  const int L = __builtin_amdgcn_readlane(m.L, i), r = __builtin_amdgcn_readlane(m.r, i);
+  const uint32_t rp = (uint32_t)((r + 7) & ~7), rq = (uint32_t)((r + 3) & ~3);
+  if ((kind & 1) == 0) {
+    base = readlane64(m.sga, i);
+    size = 8u * rq;
+  } else if (kind == 1) {
+    base = readlane64(m.fa, i);
+    size = ES * ((uint32_t)r * D + (uint32_t)L * rp);
+  } else {
+    base = readlane64(m.fa, i) + ES * (uint64_t)((uint32_t)r * D);
+    size = ES * ((uint32_t)L * rp + D * rp);
+  }
+}
+
+// Wave-uniform walk over the regions of an item: chunk [ca, cb) of spans,
+// span i, region kind, byte `off` of a region of `size` bytes at `base`.
+// Chunk starts are the set bits of `cmask` (bit n set as an end marker).
+// Past the last region the final chunk is repeated (never read from the ring).
+struct RegionCursor {
+  int i, kind, ca, cb, n;
+  uint32_t cmask;
   uint32_t off, size;
   uint64_t base;
 };
-struct ItemMeta {        // lane i < n: span i of the item
-  uint64_t sga, fa;      // global addresses of the sg entry and the factor block
-  uint32_t sgb, fb;      // their sizes in bytes
-};
-__device__ __forceinline__ uint64_t cursor_addr(const ChunkCursor& c, int lane) {
-  return c.base + min(c.off + 16u * (uint32_t)lane, c.size - 16u);
-}
-__device__ __forceinline__ void cursor_next(ChunkCursor& c, const ItemMeta& m) {
+__device__ __forceinline__ int chunk_end(uint32_t cmask, int a) { return a + 1 + __builtin_ctz(cmask >> (a + 1)); }
+
+template <typename T, int D>
+__device__ __forceinline__ void cursor_next(RegionCursor& c, const ItemMeta& m) {
   c.off += 1024u;
   if (c.off < c.size) return;
-  if (c.reg == 0) {
-    c.reg = 1;
-    c.base = readlane64(m.fa, c.j);
-    c.size = (uint32_t)__builtin_amdgcn_readlane((int)m.fb, c.j);
-    c.off = 0;
-  } else if (c.j + 1 < c.n) {
-    c.j += 1;
-    c.reg = 0;
-    c.base = readlane64(m.sga, c.j);
-    c.size = (uint32_t)__builtin_amdgcn_readlane((int)m.sgb, c.j);
-    c.off = 0;
+  if (c.kind == 0 || c.kind == 2) {
+    c.kind += 1;
+  } else if (c.i + 1 < c.cb) {
+    c.i += 1;
+    c.kind -= 1;
+  } else if (c.kind == 1) {
+    c.i = c.ca;
+    c.kind = 2;
+  } else if (c.cb < c.n) {
+    c.ca = c.cb;
+    c.cb = chunk_end(c.cmask, c.ca);
+    c.i = c.ca;
+    c.kind = 0;
   } else {
     c.off -= 1024u;
+    return;
   }
+  region_of<T, D>(m, c.i, c.kind, c.base, c.size);
+  c.off = 0;
 }
-
-template <int K, int RING>
-__device__ __forceinline__ void stage_first(uint4 (&stg)[K], ChunkCursor& c, const ItemMeta& m, int lane) {
-#pragma unroll
-  for (int jj = 0; jj < K; ++jj) {
-    stg[jj] = gload16(cursor_addr(c, lane));
-    cursor_next(c, m);
-  }
+__device__ __forceinline__ uint64_t cursor_addr(const RegionCursor& c, int lane) {
+  return c.base + min(c.off + 16u * (uint32_t)lane, c.size - 16u);
 }
 
 // Make stream bytes [.., e) readable from the ring: write staged granules and
 // stage the following ones until the ring holds everything before e.
 // `written` counts the stream bytes already in the ring (a multiple of 1024 K).
-template <int K, int RING>
-__device__ __forceinline__ void advance(uint4 (&stg)[K], uint32_t& written, uint32_t e, ChunkCursor& c,
+template <typename T, int D, int K, int RING>
+__device__ __forceinline__ void advance(uint4 (&stg)[K], uint32_t& written, uint32_t e, RegionCursor& c,
                                         const ItemMeta& m, int lane, char* ring) {
   while (written < e) {
 #pragma unroll
     for (int jj = 0; jj < K; ++jj) {
       *reinterpret_cast<uint4*>(ring + ((written + 1024u * jj + 16u * (uint32_t)lane) & (RING - 1))) = stg[jj];
       stg[jj] = gload16(cursor_addr(c, lane));
-      cursor_next(c, m);
+      cursor_next<T, D>(c, m);
     }
     written += 1024u * K;
   }
   wave_lds_sync();
 }
-
-__device__ __forceinline__ uint32_t kb_round(uint32_t x) { return (x + 1023u) & ~1023u; }
 
 template <typename T, int D, int G, int RGM>
 __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
@@ -694,8 +738,7 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
   const int col = lane & 15, cls = lane >> 4;
   const int hc = min(col, G - 1);
   char* ring = lds;
-  char* yb = lds + X::kY;
-  float* stl = reinterpret_cast<float*>(lds + X::kStl);
+  float4* sbuf = reinterpret_cast<float4*>(lds + X::kS);
   const int BG = a.B * a.Hkv;
   const bool staged = a.stage_off != nullptr;
   const float qscale = a.qscale;
@@ -736,235 +779,237 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
     const int j0 = lc * kExpChunk, n = min(cnt, j0 + kExpChunk) - j0;
 
     // metadata of the item's spans: lane i holds span j0 + i
-    const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
-    const int jl = j0 + min(lane, n - 1);
-    const int mS = a.exp_list[(size_t)g * a.seg_cap + jl];
-    const int mbits = a.exp_mask[(size_t)g * a.seg_cap + jl];
-    int64_t mfo, mgo;
-    if (staged) {
-      const int64_t* st = a.stage_off + ((size_t)g * a.seg_cap + jl) * 2;
-      mfo = st[0];
-      mgo = st[1];
-    } else {
-      mfo = a.fac_off[(size_t)g * a.seg_cap + mS];
-      mgo = a.sg_off[(size_t)g * a.seg_cap + mS];
-    }
-    const int mL = so[mS + 1] - so[mS] - 1;
-    const int mr = a.rank[(size_t)b * a.seg_cap + mS];
-    const int mrp = (mr + 7) & ~7;
     ItemMeta im;
     {
+      const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
+      const int jl = j0 + min(lane, n - 1);
+      const int mS = a.exp_list[(size_t)g * a.seg_cap + jl];
+      im.bits = a.exp_mask[(size_t)g * a.seg_cap + jl];
+      int64_t mfo, mgo;
+      if (staged) {
+        const int64_t* st = a.stage_off + ((size_t)g * a.seg_cap + jl) * 2;
+        mfo = st[0];
+        mgo = st[1];
+      } else {
+        mfo = a.fac_off[(size_t)g * a.seg_cap + mS];
+        mgo = a.sg_off[(size_t)g * a.seg_cap + mS];
+      }
+      im.L = so[mS + 1] - so[mS] - 1;
+      im.r = a.rank[(size_t)b * a.seg_cap + mS];
       const char* fb = static_cast<const char*>(staged ? a.stage_fac : a.fac);
       const char* gb = reinterpret_cast<const char*>(staged ? a.stage_sg : a.sg);
       im.sga = reinterpret_cast<uint64_t>(gb + mgo * 4);
       im.fa = reinterpret_cast<uint64_t>(fb + mfo * ES);
-      im.sgb = 8u * (uint32_t)((mr + 3) & ~3);
-      im.fb = (uint32_t)ES * (uint32_t)(mr * D + mL * mrp + D * mrp);
     }
-    // stream start of each span: both regions rounded up to whole chunks
-    const uint32_t mlen = lane < n ? kb_round(im.sgb) + kb_round(im.fb) : 0u;
-    uint32_t mend = mlen;
-#pragma unroll
-    for (int off = 1; off < kExpChunk; off <<= 1) {
-      const uint32_t t = __shfl_up(mend, off);
-      if (lane >= off) mend += t;
+    // chunks of spans: consecutive spans while their token groups fit kExpTok
+    uint32_t cmask = 1u | (1u << n);
+    {
+      int tg = 0;
+      for (int i = 0; i < n; ++i) {
+        const int t = (__builtin_amdgcn_readlane(im.L, i) + 15) >> 4;
+        if (tg + t > kExpTok / 16) {
+          cmask |= 1u << i;
+          tg = 0;
+        }
+        tg += t;
+      }
     }
-    const int mstart = (int)(mend - mlen);
-
-    ChunkCursor cur;
-    cur.j = 0;
-    cur.reg = 0;
+    RegionCursor cur;
     cur.n = n;
+    cur.cmask = cmask;
+    cur.ca = 0;
+    cur.cb = chunk_end(cmask, 0);
+    cur.i = 0;
+    cur.kind = 0;
     cur.off = 0;
-    cur.base = readlane64(im.sga, 0);
-    cur.size = (uint32_t)__builtin_amdgcn_readlane((int)im.sgb, 0);
+    region_of<T, D>(im, 0, 0, cur.base, cur.size);
     uint4 stg[K];
-    uint32_t written = 0;
-    stage_first<K, RING>(stg, cur, im, lane);
-
-    // q as the B operand of step 1: column = head (zero for columns >= G)
-    Vec8<T> qB[NC];
-    const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G + hc) * D;
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      qB[cc] = ld8(qrow + 32 * cc + 8 * cls);
-      if (col >= G) zero8(qB[cc]);
+    for (int jj = 0; jj < K; ++jj) {
+      stg[jj] = gload16(cursor_addr(cur, lane));
+      cursor_next<T, D>(cur, im);
+    }
+    uint32_t written = 0, spos = 0;
+
+    // q as the B operand of y: column = head (zero for columns >= G)
+    Vec8<T> qB[NC];
+    {
+      const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G + hc) * D;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        qB[cc] = ld8(qrow + 32 * cc + 8 * cls);
+        if (col >= G) zero8(qB[cc]);
+      }
     }
     float m = kNegInf, lsum = 0.0f;
     f32x4_t acc[NJ];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) acc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // One loop over the item's pieces, so the ring producer is inlined once.
-    // Per span: piece 0 sigma|gate, then RG Vh_K rank groups (step 1), TG U
-    // token groups (steps 2-4), RG W_V blocks (step 5).
-    int L = 0, r = 0, rp = 8, rq = 4, RG = 0, TG = 0;
-    uint32_t bits = 0, s_sg = 0, s_vk = 0, s_u = 0, s_w = 0;
-    bool head_on = false;
-    f32x4_t am[RGM];
-    int i = -1, pc = 0, npc = 0;
-    for (;;) {
-      if (pc == npc) {
-        if (++i == n) break;
-        L = __builtin_amdgcn_readlane(mL, i);
-        r = __builtin_amdgcn_readlane(mr, i);
-        rp = (r + 7) & ~7;
-        rq = (r + 3) & ~3;
-        bits = (uint32_t)__builtin_amdgcn_readlane(mbits, i);
-        s_sg = (uint32_t)__builtin_amdgcn_readlane(mstart, i);
-        s_vk = s_sg + kb_round(8u * (uint32_t)rq);
-        s_u = s_vk + (uint32_t)(r * D * ES);
-        s_w = s_u + (uint32_t)(L * rp * ES);
-        RG = (r + 15) >> 4;
-        TG = (L + 15) >> 4;
-        head_on = (bits >> col) & 1u;
-        npc = 1 + 2 * RG + TG;
-        pc = 0;
+    for (int ca = 0; ca < n; ca = chunk_end(cmask, ca)) {
+      const int cb = chunk_end(cmask, ca);
+      // ---------------- pass 1: scores of the chunk's tokens
+      float cmax = kNegInf;
+      int tgb = 0;
+      for (int i = ca; i < cb; ++i) {
+        const int L = __builtin_amdgcn_readlane(im.L, i), r = __builtin_amdgcn_readlane(im.r, i);
+        const int rp = (r + 7) & ~7, rq = (r + 3) & ~3;
+        const bool head_on = ((uint32_t)__builtin_amdgcn_readlane(im.bits, i) >> col) & 1u;
+        const int RG = (r + 15) >> 4, TG = (L + 15) >> 4;
+        const uint32_t s_sg = spos;
+        const uint32_t s_vk = s_sg + kb_round(8u * (uint32_t)rq);
+        const uint32_t s_u = s_vk + (uint32_t)(r * D * ES);
+        spos = s_vk + kb_round((uint32_t)((r * D + L * rp) * ES));
+        advance<T, D, K, RING>(stg, written, s_sg + 8u * (uint32_t)rq, cur, im, lane, ring);
+        // sigma * gate of ranks 16 rg + 4 cls + v, zero past r
+        float4 sgv[RGM];
 #pragma unroll
-        for (int rg = 0; rg < RGM; ++rg) am[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      }
-      // end of the piece in the stream
-      uint32_t e;
-      if (pc == 0) e = s_sg + 8u * (uint32_t)rq;
-      else if (pc <= RG) e = s_vk + (uint32_t)(min(r, 16 * pc) * D * ES);
-      else if (pc <= RG + TG) e = s_u + (uint32_t)(min(L, 16 * (pc - RG)) * rp * ES);
-      else {
-        const int rg = pc - RG - TG - 1;
-        e = s_w + (uint32_t)((16 * rg * D + D * min(16, rp - 16 * rg)) * ES);
-      }
-      advance<K, RING>(stg, written, e, cur, im, lane, ring);
-
-      if (pc == 0) {
-        // sigma * gate (zero past r)
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          const int k = lane + 64 * q2;
-          const int kc = min(k, r - 1);
-          const float sv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * kc) & MASK));
-          const float gv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * (rq + kc)) & MASK));
-          stl[k] = k < r ? sv * gv : 0.0f;
+        for (int rg = 0; rg < RGM; ++rg) {
+          const int k0 = min(16 * rg + 4 * cls, rq - 4);
+          const float4 sv = *reinterpret_cast<const float4*>(ring + ((s_sg + 4u * k0) & MASK));
+          const float4 gv = *reinterpret_cast<const float4*>(ring + ((s_sg + 4u * (rq + k0)) & MASK));
+          const int kk = 16 * rg + 4 * cls;
+          sgv[rg] = make_float4(kk + 0 < r ? sv.x * gv.x : 0.0f, kk + 1 < r ? sv.y * gv.y : 0.0f,
+                                kk + 2 < r ? sv.z * gv.z : 0.0f, kk + 3 < r ? sv.w * gv.w : 0.0f);
         }
-      } else if (pc <= RG) {
-        // ---- step 1, rank group rg: rows 16 rg + col
-        const int rg = pc - 1;
-        const int k = min(16 * rg + col, r - 1);
-        f32x4_t yc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          const int pg = (4 * cc + cls + k) & (DG - 1);   // rotated 8-element group
-          yc = mma8(rd8<T>(ring, (s_vk + (uint32_t)((k * D + 8 * pg) * ES)) & MASK, MASK), qB[cc], yc);
-        }
-        // rows 16 rg + 4 cls + v of head col
-        const float4 sg4 = *reinterpret_cast<const float4*>(stl + 16 * rg + 4 * cls);
-        float y[4] = {yc[0] * qscale * sg4.x, yc[1] * qscale * sg4.y, yc[2] * qscale * sg4.z, yc[3] * qscale * sg4.w};
-#pragma unroll
-        for (int v = 0; v < 4; ++v) y[v] = (16 * rg + 4 * cls + v < r) ? y[v] : 0.0f;
-        if (col < G) {
-          char* dst = yb + ((rg * 4 + cls) * G + col) * 16;
-          if constexpr (ES == 2) {
-            Vec4<bf16raw> hi, lo;
-            pack4(y, hi);
-            float rem[4] = {y[0] - __uint_as_float(hi.v.x << 16), y[1] - __uint_as_float(hi.v.x & 0xffff0000u),
-                            y[2] - __uint_as_float(hi.v.y << 16), y[3] - __uint_as_float(hi.v.y & 0xffff0000u)};
-            pack4(rem, lo);
-            *reinterpret_cast<uint4*>(dst) = make_uint4(hi.v.x, hi.v.y, lo.v.x, lo.v.y);
-          } else {
-            *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
-          }
-        }
-      } else if (pc <= RG + TG) {
-        // ---- steps 2-4, token group tg (online softmax across groups and spans)
-        const int tg = pc - RG - 1;
-        const int trow = min(16 * tg + col, L - 1);
-        f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        // y of rank groups rg, as the B operand of the score product
+        Vec4<T> yhi[RGM], ylo[RGM];
 #pragma unroll
         for (int rg = 0; rg < RGM; ++rg) {
           if (rg < RG) {
-            const uint4 yv = *reinterpret_cast<const uint4*>(yb + ((rg * 4 + cls) * G + hc) * 16);
-            const int k0 = min(16 * rg + 4 * cls, rp - 4);
-            const Vec4<T> uop = rd4<T>(ring, (s_u + (uint32_t)((trow * rp + k0) * ES)) & MASK);
+            advance<T, D, K, RING>(stg, written, s_vk + (uint32_t)(min(r, 16 * rg + 16) * D * ES), cur, im, lane, ring);
+            const int k = min(16 * rg + col, r - 1);
+            f32x4_t yc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc) {
+              const int pg = (4 * cc + cls + k) & (DG - 1);   // rotated 8-element group
+              yc = mma8(rd8<T>(ring, (s_vk + (uint32_t)((k * D + 8 * pg) * ES)) & MASK, MASK), qB[cc], yc);
+            }
+            float y[4] = {yc[0] * qscale * sgv[rg].x, yc[1] * qscale * sgv[rg].y, yc[2] * qscale * sgv[rg].z,
+                          yc[3] * qscale * sgv[rg].w};
+            pack4(y, yhi[rg]);
             if constexpr (ES == 2) {
-              sc = mma4(uop, Vec4<bf16raw>{make_uint2(yv.x, yv.y)}, sc);
-              sc = mma4(uop, Vec4<bf16raw>{make_uint2(yv.z, yv.w)}, sc);
-            } else {
-              sc = mma4(uop, Vec4<float>{make_float4(__uint_as_float(yv.x), __uint_as_float(yv.y),
-                                                     __uint_as_float(yv.z), __uint_as_float(yv.w))}, sc);
+              float rem[4] = {y[0] - __uint_as_float(yhi[rg].v.x << 16), y[1] - __uint_as_float(yhi[rg].v.x & 0xffff0000u),
+                              y[2] - __uint_as_float(yhi[rg].v.y << 16), y[3] - __uint_as_float(yhi[rg].v.y & 0xffff0000u)};
+              pack4(rem, ylo[rg]);
             }
           }
         }
-        // scores of tokens 16 tg + 4 cls + v for head col
-        float sv[4];
-        float mt = kNegInf;
+        // scores, one token group at a time
+        for (int tg = 0; tg < TG; ++tg) {
+          advance<T, D, K, RING>(stg, written, s_u + (uint32_t)(min(L, 16 * tg + 16) * rp * ES), cur, im, lane, ring);
+          const int trow = min(16 * tg + col, L - 1);
+          f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float x = (head_on && 16 * tg + 4 * cls + v < L) ? sc[v] : kNegInf;
-          sv[v] = x;
-          mt = fmaxf(mt, x);
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m, mt);
-        if (mn != kNegInf && mn != m) {
-          const float alpha = exp2f(m - mn);
-          lsum *= alpha;
-#pragma unroll
-          for (int jt = 0; jt < NJ; ++jt) acc[jt] *= alpha;
-#pragma unroll
-          for (int rg = 0; rg < RGM; ++rg)
-            if (rg < RG) am[rg] *= alpha;
-          m = mn;
-        }
-        float pr[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          pr[v] = (m == kNegInf) ? 0.0f : exp2f(sv[v] - m);
-          lsum += pr[v];
-        }
-        Vec4<T> pB;
-        pack4(pr, pB);
-        // step 4: a[k][h] += sum_t U[t][k] p[t][h], rows k = 16 rg + col
-#pragma unroll
-        for (int rg = 0; rg < RGM; ++rg) {
-          if (rg < RG) {
-            const int kc = min(16 * rg + col, rp - 1);
-            uint32_t ev[4];
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-              const int t = min(16 * tg + 4 * cls + e4, L - 1);
-              const uint32_t ob = (s_u + (uint32_t)((t * rp + kc) * ES)) & MASK;
-              if constexpr (ES == 2) ev[e4] = *reinterpret_cast<const uint16_t*>(ring + ob);
-              else ev[e4] = *reinterpret_cast<const uint32_t*>(ring + ob);
+          for (int rg = 0; rg < RGM; ++rg) {
+            if (rg < RG) {
+              const int k0 = min(16 * rg + 4 * cls, rp - 4);
+              const Vec4<T> uop = rd4<T>(ring, (s_u + (uint32_t)((trow * rp + k0) * ES)) & MASK);
+              sc = mma4(uop, yhi[rg], sc);
+              if constexpr (ES == 2) sc = mma4(uop, ylo[rg], sc);
             }
-            Vec4<T> uop;
-            if constexpr (ES == 2) uop.v = make_uint2(ev[0] | (ev[1] << 16), ev[2] | (ev[3] << 16));
-            else uop.v = make_float4(__uint_as_float(ev[0]), __uint_as_float(ev[1]), __uint_as_float(ev[2]),
-                                     __uint_as_float(ev[3]));
-            am[rg] = mma4(uop, pB, am[rg]);
           }
+          float4 sv;
+          {
+            const int t0 = 16 * tg + 4 * cls;
+            sv.x = (head_on && t0 + 0 < L) ? sc[0] : kNegInf;
+            sv.y = (head_on && t0 + 1 < L) ? sc[1] : kNegInf;
+            sv.z = (head_on && t0 + 2 < L) ? sc[2] : kNegInf;
+            sv.w = (head_on && t0 + 3 < L) ? sc[3] : kNegInf;
+          }
+          cmax = fmaxf(cmax, fmaxf(fmaxf(sv.x, sv.y), fmaxf(sv.z, sv.w)));
+          if (col < G) sbuf[((tgb + tg) * 4 + cls) * G + col] = sv;
         }
-      } else {
-        // ---- step 5, W_V block rg: b = sigma*gate * a
-        const int rg = pc - RG - TG - 1;
-        const int wk = min(16, rp - 16 * rg);
-        const uint32_t s_wg = s_w + (uint32_t)(16 * rg * D * ES);
-        const float4 sg4 = *reinterpret_cast<const float4*>(stl + 16 * rg + 4 * cls);
-        f32x4_t ar = am[0];
+        tgb += TG;
+      }
+      // chunk maximum per head; rescale the accumulators once
+      cmax = rows_max(cmax);
+      const float mn = fmaxf(m, cmax);
+      if (mn != kNegInf && mn != m) {
+        const float alpha = exp2f(m - mn);
+        lsum *= alpha;
 #pragma unroll
-        for (int q2 = 1; q2 < RGM; ++q2) ar = (q2 == rg) ? am[q2] : ar;
-        const float bv[4] = {ar[0] * sg4.x, ar[1] * sg4.y, ar[2] * sg4.z, ar[3] * sg4.w};
-        Vec4<T> bB;
-        pack4(bv, bB);
-        const int k0 = min(4 * cls, wk - 4);
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt)
-          acc[jt] = mma4(rd4<T>(ring, (s_wg + (uint32_t)(((16 * jt + col) * wk + k0) * ES)) & MASK), bB, acc[jt]);
+        for (int jt = 0; jt < NJ; ++jt) acc[jt] *= alpha;
+        m = mn;
       }
       wave_lds_sync();
-      ++pc;
+      // ---------------- pass 2: weights through U^T and W_V
+      tgb = 0;
+      for (int i = ca; i < cb; ++i) {
+        const int L = __builtin_amdgcn_readlane(im.L, i), r = __builtin_amdgcn_readlane(im.r, i);
+        const int rp = (r + 7) & ~7, rq = (r + 3) & ~3;
+        const int RG = (r + 15) >> 4, TG = (L + 15) >> 4;
+        const uint32_t s_sg = spos;
+        const uint32_t s_u = s_sg + kb_round(8u * (uint32_t)rq);
+        const uint32_t s_w = s_u + (uint32_t)(L * rp * ES);
+        spos = s_u + kb_round((uint32_t)((L * rp + D * rp) * ES));
+        advance<T, D, K, RING>(stg, written, s_sg + 8u * (uint32_t)rq, cur, im, lane, ring);
+        float4 sgv[RGM];
+#pragma unroll
+        for (int rg = 0; rg < RGM; ++rg) {
+          const int k0 = min(16 * rg + 4 * cls, rq - 4);
+          const float4 sv = *reinterpret_cast<const float4*>(ring + ((s_sg + 4u * k0) & MASK));
+          const float4 gv = *reinterpret_cast<const float4*>(ring + ((s_sg + 4u * (rq + k0)) & MASK));
+          const int kk = 16 * rg + 4 * cls;
+          sgv[rg] = make_float4(kk + 0 < r ? sv.x * gv.x : 0.0f, kk + 1 < r ? sv.y * gv.y : 0.0f,
+                                kk + 2 < r ? sv.z * gv.z : 0.0f, kk + 3 < r ? sv.w * gv.w : 0.0f);
+        }
+        f32x4_t am[RGM];
+#pragma unroll
+        for (int rg = 0; rg < RGM; ++rg) am[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int tg = 0; tg < TG; ++tg) {
+          advance<T, D, K, RING>(stg, written, s_u + (uint32_t)(min(L, 16 * tg + 16) * rp * ES), cur, im, lane, ring);
+          const float4 sv = sbuf[((tgb + tg) * 4 + cls) * G + hc];
+          float pr[4];
+          pr[0] = (m == kNegInf) ? 0.0f : exp2f(sv.x - m);
+          pr[1] = (m == kNegInf) ? 0.0f : exp2f(sv.y - m);
+          pr[2] = (m == kNegInf) ? 0.0f : exp2f(sv.z - m);
+          pr[3] = (m == kNegInf) ? 0.0f : exp2f(sv.w - m);
+          lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+          Vec4<T> pB;
+          pack4(pr, pB);
+#pragma unroll
+          for (int rg = 0; rg < RGM; ++rg) {
+            if (rg < RG) {
+              const int kc = min(16 * rg + col, rp - 1);
+              uint32_t ev[4];
+#pragma unroll
+              for (int e4 = 0; e4 < 4; ++e4) {
+                const int t = min(16 * tg + 4 * cls + e4, L - 1);
+                const uint32_t ob = (s_u + (uint32_t)((t * rp + kc) * ES)) & MASK;
+                if constexpr (ES == 2) ev[e4] = *reinterpret_cast<const uint16_t*>(ring + ob);
+                else ev[e4] = *reinterpret_cast<const uint32_t*>(ring + ob);
+              }
+              Vec4<T> uop;
+              if constexpr (ES == 2) uop.v = make_uint2(ev[0] | (ev[1] << 16), ev[2] | (ev[3] << 16));
+              else uop.v = make_float4(__uint_as_float(ev[0]), __uint_as_float(ev[1]), __uint_as_float(ev[2]),
+                                       __uint_as_float(ev[3]));
+              am[rg] = mma4(uop, pB, am[rg]);
+            }
+          }
+        }
+        tgb += TG;
+#pragma unroll
+        for (int rg = 0; rg < RGM; ++rg) {
+          if (rg < RG) {
+            const int wk = min(16, rp - 16 * rg);
+            const uint32_t s_wg = s_w + (uint32_t)(16 * rg * D * ES);
+            advance<T, D, K, RING>(stg, written, s_wg + (uint32_t)(D * wk * ES), cur, im, lane, ring);
+            const float bv[4] = {am[rg][0] * sgv[rg].x, am[rg][1] * sgv[rg].y, am[rg][2] * sgv[rg].z,
+                                 am[rg][3] * sgv[rg].w};
+            Vec4<T> bB;
+            pack4(bv, bB);
+            const int k0 = min(4 * cls, wk - 4);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+              acc[jt] = mma4(rd4<T>(ring, (s_wg + (uint32_t)(((16 * jt + col) * wk + k0) * ES)) & MASK), bB, acc[jt]);
+          }
+        }
+      }
+      wave_lds_sync();
     }
     // partial of this item: head col, summed over the four lane classes
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    lsum = rows_sum(lsum);
     const int slot = a.nch_a4 + lc;
     float* pml = a.part_ml + ((size_t)g * a.P_max + slot) * G * 2;
     float* po = a.part_o + ((size_t)g * a.P_max + slot) * G * D;
