@@ -12,7 +12,7 @@ constexpr int kMaxGroups = 256;      // batch * kv heads handled by one decode l
 constexpr int kMaxSpan = 128;        // longest span body / highest rank the kernels hold
 constexpr int kRouteThreads = 256;   // spans per route workgroup (one lane per span)
 constexpr int kAttnThreads = 256;    // four waves per attention workgroup
-constexpr int kExpChunk = 8;         // expanded spans per work item of the expanded-span kernel
+constexpr int kExpChunk = 4;         // expanded spans per work item of the expanded-span kernel
 constexpr int kExpThreads = 64;      // one wave per expanded-span workgroup
 constexpr int kExpWaves = 4096;      // most waves (workgroups) of one expanded-span launch
 

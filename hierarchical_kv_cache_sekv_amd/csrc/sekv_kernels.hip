@@ -556,7 +556,7 @@ template <typename T, int RGM> struct ExpCfg;
 // W_V block: 16 x 128 elements).
 template <int RGM> struct ExpCfg<bf16raw, RGM> { static constexpr int K = 4; static constexpr int kRing = 8192; };
 template <int RGM> struct ExpCfg<float, RGM> { static constexpr int K = 8; static constexpr int kRing = 16384; };
-constexpr int kExpTok = 256;   // tokens of one chunk of spans (score buffer)
+constexpr int kExpTok = 192;   // tokens of one chunk of spans (score buffer)
 
 template <typename T, int G, int RGM>
 struct ExpLds {
@@ -564,7 +564,9 @@ struct ExpLds {
   static_assert((kRing & (kRing - 1)) == 0, "ring size is a power of two");
   static_assert(kRing >= ExpCfg<T, RGM>::K * 1024 + 16 * kMaxSpan * (int)sizeof(T), "ring holds a granule and a piece");
   static constexpr int kS = kRing;                          // scores [token group][class][G] float4
-  static constexpr int kBytes = kS + (kExpTok / 16) * 4 * G * 16;
+  static constexpr int kQ = kS + (kExpTok / 16) * 4 * G * 16;   // q of the item's G heads [G][kMaxD]
+  static constexpr int kStl = kQ + G * 128 * (int)sizeof(T);    // sigma*gate of the current span [kMaxSpan]
+  static constexpr int kBytes = kStl + kMaxSpan * 4;
 };
 
 // Four elements of the storage type as an MFMA operand of a 16x16x16 product.
@@ -739,6 +741,7 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
   const int hc = min(col, G - 1);
   char* ring = lds;
   float4* sbuf = reinterpret_cast<float4*>(lds + X::kS);
+  float* stl = reinterpret_cast<float*>(lds + X::kStl);
   const int BG = a.B * a.Hkv;
   const bool staged = a.stage_off != nullptr;
   const float qscale = a.qscale;
@@ -831,15 +834,11 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
     }
     uint32_t written = 0, spos = 0;
 
-    // q as the B operand of y: column = head (zero for columns >= G)
-    Vec8<T> qB[NC];
+    // the item's G query rows, kept in LDS (read as the B operand of y)
+    T* qs = reinterpret_cast<T*>(lds + X::kQ);
     {
-      const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G + hc) * D;
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        qB[cc] = ld8(qrow + 32 * cc + 8 * cls);
-        if (col >= G) zero8(qB[cc]);
-      }
+      const T* q0 = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
+      for (int i = 8 * lane; i < G * D; i += 8 * 64) st8(qs + i, ld8(q0 + i));
     }
     float m = kNegInf, lsum = 0.0f;
     f32x4_t acc[NJ];
@@ -861,16 +860,15 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
         const uint32_t s_u = s_vk + (uint32_t)(r * D * ES);
         spos = s_vk + kb_round((uint32_t)((r * D + L * rp) * ES));
         advance<T, D, K, RING>(stg, written, s_sg + 8u * (uint32_t)rq, cur, im, lane, ring);
-        // sigma * gate of ranks 16 rg + 4 cls + v, zero past r
-        float4 sgv[RGM];
+        // sigma * gate (zero past r), staged in LDS: the ring holds the entry
+        // only until the next advance
 #pragma unroll
-        for (int rg = 0; rg < RGM; ++rg) {
-          const int k0 = min(16 * rg + 4 * cls, rq - 4);
-          const float4 sv = *reinterpret_cast<const float4*>(ring + ((s_sg + 4u * k0) & MASK));
-          const float4 gv = *reinterpret_cast<const float4*>(ring + ((s_sg + 4u * (rq + k0)) & MASK));
-          const int kk = 16 * rg + 4 * cls;
-          sgv[rg] = make_float4(kk + 0 < r ? sv.x * gv.x : 0.0f, kk + 1 < r ? sv.y * gv.y : 0.0f,
-                                kk + 2 < r ? sv.z * gv.z : 0.0f, kk + 3 < r ? sv.w * gv.w : 0.0f);
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int k = lane + 64 * q2;
+          const int kc = min(k, r - 1);
+          const float sv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * kc) & MASK));
+          const float gv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * (rq + kc)) & MASK));
+          stl[k] = k < r ? sv * gv : 0.0f;
         }
         // y of rank groups rg, as the B operand of the score product
         Vec4<T> yhi[RGM], ylo[RGM];
@@ -883,10 +881,14 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
 #pragma unroll
             for (int cc = 0; cc < NC; ++cc) {
               const int pg = (4 * cc + cls + k) & (DG - 1);   // rotated 8-element group
-              yc = mma8(rd8<T>(ring, (s_vk + (uint32_t)((k * D + 8 * pg) * ES)) & MASK, MASK), qB[cc], yc);
+              Vec8<T> qop = ld8(qs + hc * D + 32 * cc + 8 * cls);
+              if (col >= G) zero8(qop);
+              yc = mma8(rd8<T>(ring, (s_vk + (uint32_t)((k * D + 8 * pg) * ES)) & MASK, MASK), qop, yc);
             }
-            float y[4] = {yc[0] * qscale * sgv[rg].x, yc[1] * qscale * sgv[rg].y, yc[2] * qscale * sgv[rg].z,
-                          yc[3] * qscale * sgv[rg].w};
+            // sigma * gate of ranks 16 rg + 4 cls + v
+            const float4 sgv = *reinterpret_cast<const float4*>(stl + 16 * rg + 4 * cls);
+            float y[4] = {yc[0] * qscale * sgv.x, yc[1] * qscale * sgv.y, yc[2] * qscale * sgv.z,
+                          yc[3] * qscale * sgv.w};
             pack4(y, yhi[rg]);
             if constexpr (ES == 2) {
               float rem[4] = {y[0] - __uint_as_float(yhi[rg].v.x << 16), y[1] - __uint_as_float(yhi[rg].v.x & 0xffff0000u),
@@ -944,15 +946,14 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
         const uint32_t s_w = s_u + (uint32_t)(L * rp * ES);
         spos = s_u + kb_round((uint32_t)((L * rp + D * rp) * ES));
         advance<T, D, K, RING>(stg, written, s_sg + 8u * (uint32_t)rq, cur, im, lane, ring);
-        float4 sgv[RGM];
+        // sigma * gate (zero past r) for step 5, staged in LDS
 #pragma unroll
-        for (int rg = 0; rg < RGM; ++rg) {
-          const int k0 = min(16 * rg + 4 * cls, rq - 4);
-          const float4 sv = *reinterpret_cast<const float4*>(ring + ((s_sg + 4u * k0) & MASK));
-          const float4 gv = *reinterpret_cast<const float4*>(ring + ((s_sg + 4u * (rq + k0)) & MASK));
-          const int kk = 16 * rg + 4 * cls;
-          sgv[rg] = make_float4(kk + 0 < r ? sv.x * gv.x : 0.0f, kk + 1 < r ? sv.y * gv.y : 0.0f,
-                                kk + 2 < r ? sv.z * gv.z : 0.0f, kk + 3 < r ? sv.w * gv.w : 0.0f);
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int k = lane + 64 * q2;
+          const int kc = min(k, r - 1);
+          const float sv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * kc) & MASK));
+          const float gv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * (rq + kc)) & MASK));
+          stl[k] = k < r ? sv * gv : 0.0f;
         }
         f32x4_t am[RGM];
 #pragma unroll
@@ -995,8 +996,8 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
             const int wk = min(16, rp - 16 * rg);
             const uint32_t s_wg = s_w + (uint32_t)(16 * rg * D * ES);
             advance<T, D, K, RING>(stg, written, s_wg + (uint32_t)(D * wk * ES), cur, im, lane, ring);
-            const float bv[4] = {am[rg][0] * sgv[rg].x, am[rg][1] * sgv[rg].y, am[rg][2] * sgv[rg].z,
-                                 am[rg][3] * sgv[rg].w};
+            const float4 sg4 = *reinterpret_cast<const float4*>(stl + 16 * rg + 4 * cls);
+            const float bv[4] = {am[rg][0] * sg4.x, am[rg][1] * sg4.y, am[rg][2] * sg4.z, am[rg][3] * sg4.w};
             Vec4<T> bB;
             pack4(bv, bB);
             const int k0 = min(4 * cls, wk - 4);
@@ -1035,9 +1036,9 @@ __global__ __launch_bounds__(kAttnThreads) void attend_full_kernel(const AttendA
   extern __shared__ __align__(16) char lds[];
   role_full_summary<T, D, G>(a, blockIdx.x, lds);
 }
-// Ranks up to 64 (four rank groups in registers): two waves per SIMD.
+// Ranks up to 64 (four rank groups in registers): three waves per SIMD.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kExpThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kExpThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void attend_expanded_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
   role_expanded<T, D, G, 4>(a, blockIdx.x, lds);
