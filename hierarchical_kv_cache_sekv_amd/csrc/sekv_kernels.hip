@@ -338,6 +338,110 @@ struct AttnLds {
   static constexpr int kRoleA = kMaskBytes + kMaskBytes * 4 + kMergeFloats * 4;
 };
 
+// Maximum and sum over the four 16-lane rows, same position in each row
+// (lanes h, h + 16, h + 32, h + 48): row swaps on the VALU, no LDS.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Operands of one 32-entry tile of the full-resolution + summary stream.
+template <typename T, int D>
+struct TileOps {
+  Vec8<T> k[2][D / 32];   // K rows, MFMA halves: row (col) = entry 8*(col/4) + 4h + col%4
+  Vec8<T> v[D / 16];      // V^T rows 16 jt + col, entries 8 cls .. 8 cls + 7
+};
+template <typename T>
+struct TileSrc {
+  const T *fk, *fvt, *sk, *svt;   // full-res keys / value tiles, summary keys / value tiles
+  int nft, nf, ns;                // full-res tiles, full-res entries, summaries
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void tile_load(TileOps<T, D>& o, const TileSrc<T>& s, int t, int col, int cls) {
+  constexpr int NC = D / 32, NJ = D / 16;
+  const bool summ = t >= s.nft;
+  const int tt = summ ? t - s.nft : t;
+  const int base = tt * 32;
+  const int npart = summ ? s.ns : s.nf;
+  const T* krows = summ ? s.sk : s.fk;
+  const T* vt = (summ ? s.svt : s.fvt) + (size_t)tt * 32 * D;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = min(base + 8 * (col >> 2) + 4 * h + (col & 3), npart - 1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) o.k[h][c] = ld8(krows + (size_t)e * D + 32 * c + 8 * cls);
+  }
+#pragma unroll
+  for (int jt = 0; jt < NJ; ++jt) o.v[jt] = ld8(vt + (16 * jt + col) * 32 + 8 * cls);
+}
+
+// Scores, online softmax and P.V of one tile for head `col` of this lane.
+template <typename T, int D, int G>
+__device__ __forceinline__ void tile_step(const TileOps<T, D>& o, const TileSrc<T>& s, int t, int S0,
+                                          const uint8_t* smask, const float* slog, const Vec8<T> (&qB)[D / 32],
+                                          float qscale, int col, int cls, float& m, float& lsum,
+                                          f32x4_t (&acc)[D / 16]) {
+  constexpr int NC = D / 32, NJ = D / 16;
+  const bool summ = t >= s.nft;
+  const int base = (summ ? t - s.nft : t) * 32;
+  const int npart = summ ? s.ns : s.nf;
+  f32x4_t sc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    sc[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sc[h] = mma8(o.k[h][c], qB[c], sc[h]);
+  }
+  // this lane: head col, tile entries 8*cls + 4h + v
+  float sv[8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = base + 8 * cls + 4 * h + v;
+      float val = sc[h][v] * qscale;
+      if (e >= npart) {
+        val = kNegInf;
+      } else if (summ) {
+        const uint32_t bits = smask[e - S0];
+        val = ((bits >> col) & 1u) ? kNegInf : val + slog[e - S0];
+      }
+      sv[4 * h + v] = val;
+    }
+  float mt = sv[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
+  mt = rows_max(mt);
+  const float mn = fmaxf(m, mt);
+  float p[8];
+  if (mn != kNegInf) {
+    const float alpha = exp2f(m - mn);
+    float ps = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { p[i] = exp2f(sv[i] - mn); ps += p[i]; }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) acc[jt] *= alpha;
+    m = mn;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = 0.0f;
+  }
+  Vec8<T> pB;
+  pack8(p, pB);
+#pragma unroll
+  for (int jt = 0; jt < NJ; ++jt) acc[jt] = mma8(o.v[jt], pB, acc[jt]);
+}
+
 // Role A: one workgroup = a chunk of tiles_a4 32-entry tiles of the (b, kv)
 // memory stream [full-resolution tiles ++ summary tiles]; wave w takes tiles
 // w, w+4, ... of the chunk.  Per tile, q.K and P.V run on the matrix cores:
@@ -406,71 +510,24 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
   const T* sk = static_cast<const T*>(a.sum_k) + (size_t)g * a.seg_cap * D;
   const T* svt = static_cast<const T*>(a.sum_v) + (size_t)g * stiles * 32 * D;
 
-  for (int t = t0 + wave; t < t1; t += 4) {
-    const bool summ = t >= nft;
-    const int tt = summ ? t - nft : t;
-    const int base = tt * 32;
-    const int npart = summ ? ns : nf;
-    const T* krows = summ ? sk : fk;
-    const T* vt = (summ ? svt : fvt) + (size_t)tt * 32 * D;
-    // K operands: MFMA half h, row (col) = entry 8*(col/4) + 4h + col%4 of the tile
-    Vec8<T> kop[2][NC];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = min(base + 8 * (col >> 2) + 4 * h + (col & 3), npart - 1);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kop[h][c] = ld8(krows + (size_t)e * D + 32 * c + 8 * cls);
+  // Software pipeline over this wave's tiles t0 + wave, t0 + wave + 4, ...:
+  // the next tile's K rows and V^T tile are loaded while the current one is
+  // scored and accumulated (two operand sets, used alternately).
+  TileOps<T, D> opA, opB;
+  const TileSrc<T> src{fk, fvt, sk, svt, nft, nf, ns};
+  int t = t0 + wave;
+  if (t < t1) {
+    tile_load<T, D>(opA, src, t, col, cls);
+    for (;;) {
+      if (t + 4 < t1) tile_load<T, D>(opB, src, t + 4, col, cls);
+      tile_step<T, D, G>(opA, src, t, S0, smask, slog, qB, qscale, col, cls, m, lsum, acc);
+      t += 4;
+      if (t >= t1) break;
+      if (t + 4 < t1) tile_load<T, D>(opA, src, t + 4, col, cls);
+      tile_step<T, D, G>(opB, src, t, S0, smask, slog, qB, qscale, col, cls, m, lsum, acc);
+      t += 4;
+      if (t >= t1) break;
     }
-    Vec8<T> vop[NJ];
-#pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) vop[jt] = ld8(vt + (16 * jt + col) * 32 + 8 * cls);
-    f32x4_t sc[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      sc[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) sc[h] = mma8(kop[h][c], qB[c], sc[h]);
-    }
-    // this lane: head col, tile entries 8*cls + 4h + v
-    float sv[8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int e = base + 8 * cls + 4 * h + v;
-        float val = sc[h][v] * qscale;
-        if (e >= npart) {
-          val = kNegInf;
-        } else if (summ) {
-          const uint32_t bits = smask[e - S0];
-          val = ((bits >> col) & 1u) ? kNegInf : val + slog[e - S0];
-        }
-        sv[4 * h + v] = val;
-      }
-    float mt = sv[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m, mt);
-    float p[8];
-    if (mn != kNegInf) {
-      const float alpha = exp2f(m - mn);
-      float ps = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { p[i] = exp2f(sv[i] - mn); ps += p[i]; }
-      lsum = lsum * alpha + ps;
-#pragma unroll
-      for (int jt = 0; jt < NJ; ++jt) acc[jt] *= alpha;
-      m = mn;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.0f;
-    }
-    Vec8<T> pB;
-    pack8(p, pB);
-#pragma unroll
-    for (int jt = 0; jt < NJ; ++jt) acc[jt] = mma8(vop[jt], pB, acc[jt]);
   }
 
   // this wave's state of head col: lsum summed over the four lane classes
@@ -616,21 +673,6 @@ __device__ __forceinline__ Vec8<T> rd8(const char* ring, uint32_t ob, uint32_t m
     x.b = *reinterpret_cast<const float4*>(ring + ((ob + 16) & mask));
   }
   return x;
-}
-
-// Maximum and sum over the four 16-lane rows, same position in each row
-// (lanes h, h + 16, h + 32, h + 48): row swaps on the VALU, no LDS.
-__device__ __forceinline__ float rows_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // 16 bytes from a global byte address (address space 1: a global load, not a
@@ -1032,7 +1074,7 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
 // separate kernels so each gets its own register budget; the host runs them
 // concurrently on two streams.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttnThreads) void attend_full_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attend_full_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
   role_full_summary<T, D, G>(a, blockIdx.x, lds);
 }
