@@ -109,6 +109,7 @@ def main():
     ap.add_argument("--queries", type=int, default=64)
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="timed pass: replay of captured HIP graphs (default) or eager launches")
+    ap.add_argument("--graph-steps", type=int, default=8, help="decode steps captured per HIP graph")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -168,7 +169,8 @@ def main():
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     log(f"{ncopy} cache copies of {resident / 2**20:.0f} MiB each resident in HBM")
 
-    nstep_combo = math.lcm(ncopy, Q)
+    gs = max(1, args.graph_steps)
+    nstep_combo = math.lcm(ncopy, Q, gs)
 
     def step(i):
         c = i % ncopy
@@ -193,25 +195,29 @@ def main():
     kern_us = {k: (v[0] / max(v[1], 1)) * 1e3 for k, v in prof.items()}
     log(f"eager: {eager_ms * 1e3:.1f} us/step; per launch: " + ", ".join(f"{k} {u:.1f} us" for k, u in kern_us.items()))
 
-    # timed pass: one HIP graph per (cache copy, query) combination, replayed
+    # timed pass: HIP graphs of `gs` consecutive steps (cycling cache copies and
+    # queries), replayed; a multi-layer model would likewise launch many
+    # layer-steps per graph
     graphs = None
     if args.launch == "graph":
+        assert args.steps % gs == 0 and args.warmup % gs == 0, "--steps and --warmup must be multiples of --graph-steps"
         graphs = []
         cap_stream = torch.cuda.Stream()
-        for j in range(nstep_combo):
+        for j in range(nstep_combo // gs):
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr, stream=cap_stream):
-                step(j)
+                for u in range(gs):
+                    step(j * gs + u)
             graphs.append(gr)
-        for i in range(args.warmup):
-            graphs[i % nstep_combo].replay()
+        for i in range(0, args.warmup, gs):
+            graphs[(i // gs) % len(graphs)].replay()
         torch.cuda.synchronize()
-        log(f"captured {nstep_combo} step graphs")
+        log(f"captured {len(graphs)} graphs of {gs} steps")
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if graphs is not None:
-        for i in range(args.steps):
-            graphs[(args.warmup + i) % nstep_combo].replay()
+        for i in range(0, args.steps, gs):
+            graphs[((args.warmup + i) // gs) % len(graphs)].replay()
     else:
         for i in range(args.steps):
             step(args.warmup + i)
@@ -234,9 +240,20 @@ def main():
         per_q.append(by)
     idx = [(args.warmup + i) % Q for i in range(args.steps)]
     avg = {k: sum(per_q[i][k] for i in idx) / args.steps for k in per_q[0]}
-    gbs = {k: avg[k] / (kern_us[k] * 1e-6) / 1e9 for k in ("route", "full", "expand")}
-    dom = max(("full", "expand"), key=lambda k: kern_us[k])
-    names = {"full": "attend_full_kernel", "expand": "attend_expanded_kernel"}
+    # kernels timed by the library's events: "route" (decide + compact), and either
+    # one fused attention launch (reported under "full") or separate full-res /
+    # expanded-span launches
+    fused = prof["expand"][1] == 0
+    if fused:
+        avg["attend"] = avg["full"] + avg["expand"]
+        kern_us["attend"] = kern_us["full"]
+        keys = ("route", "attend")
+        names = {"attend": "attend_fused_kernel"}
+    else:
+        keys = ("route", "full", "expand")
+        names = {"full": "attend_full_kernel", "expand": "attend_expanded_kernel"}
+    gbs = {k: avg[k] / (kern_us[k] * 1e-6) / 1e9 for k in keys}
+    dom = max(names, key=lambda k: kern_us[k])
     step_gbs = avg["total"] / (ms_per_step / 1e3) / 1e9
     steps_per_s = 1e3 / ms_per_step
 
@@ -262,13 +279,14 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_ctx": w.n_ctx, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "rank_range": [w.rank_lo, w.rank_hi],
                    "expand_frac_target": args.frac, "expand_frac_realized": round(float(avg["frac"]), 4),
-                   "factors": "device", "layers": 1, "cache_copies_rotated": ncopy, "launch": args.launch},
+                   "factors": "device", "layers": 1, "cache_copies_rotated": ncopy, "launch": args.launch,
+                   "steps_per_graph": gs if args.launch == "graph" else None},
         "eff_ctx_tokens_per_s": steps_per_s * w.batch * w.n_ctx,
         "algorithmic_bytes_per_step": int(avg["total"]),
         "step_hbm_gbs": step_gbs,
         "step_hbm_frac": step_gbs / PEAK_HBM_GBS,
         "kernels": {k: {"us_per_launch": kern_us[k], "algorithmic_bytes": int(avg[k]), "gbs": gbs[k],
-                        "hbm_frac": gbs[k] / PEAK_HBM_GBS} for k in ("route", "full", "expand")},
+                        "hbm_frac": gbs[k] / PEAK_HBM_GBS} for k in keys},
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": gbs[dom], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gbs[dom] / PEAK_HBM_GBS, "traffic": None,
                      "bytes_per_launch": int(avg[dom])},

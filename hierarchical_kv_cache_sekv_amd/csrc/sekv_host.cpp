@@ -136,8 +136,6 @@ struct EventPairs {
 
 struct sekv_ctx {
   int device = 0;
-  hipStream_t side = nullptr;        // runs the expanded-span kernel beside the full-res pass
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipEvent_t ev_list = nullptr, ev_copy = nullptr;
   hipEvent_t ev_ring[kRing] = {};
   ThreadPool* pool = nullptr;
@@ -385,10 +383,7 @@ sekv_status sekv_ctx_create(int device, sekv_ctx** out) {
   sekv_ctx* c = new (std::nothrow) sekv_ctx();
   if (!c) return fail(SEKV_ENOMEM, "cannot allocate the context");
   c->device = device;
-  hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_list, hipEventDisableTiming);
+  hipError_t e = hipEventCreateWithFlags(&c->ev_list, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming);
   for (int i = 0; i < kRing && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->ev_ring[i], hipEventDisableTiming);
   if (e != hipSuccess) {
@@ -405,9 +400,6 @@ void sekv_ctx_destroy(sekv_ctx* c) {
   for (hipEvent_t e : c->prof_route.ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof_attend.ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof_expand.ev) (void)hipEventDestroy(e);
-  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
-  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
-  if (c->side) (void)hipStreamDestroy(c->side);
   if (c->ev_list) (void)hipEventDestroy(c->ev_list);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
   for (int i = 0; i < kRing; ++i)
@@ -770,6 +762,7 @@ void make_plan(const sekv_config* c, const sekv_spans* s, DecodePlan& p) {
   a.P_max = a.nch_a4 + (s->seg_cap + kExpChunk - 1) / kExpChunk;
   const int64_t max_items = (int64_t)BG * ((s->seg_cap + kExpChunk - 1) / kExpChunk);
   a.n_a5_wg = (int)std::max<int64_t>(1, std::min<int64_t>(kExpWaves, max_items));
+  a.n_fx_wg = (a.n_a5_wg + 3) / 4;
   a.n_a4_wg = BG * a.nch_a4;
   int mr = 0;
   for (int b = 0; b < B; ++b) {
@@ -847,17 +840,19 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   a.stage_off = nullptr;
 
   if (!c->factors_on_host) {
-    // fork: expanded spans on the side stream, full-res + summaries on the caller's
-    HIP_OR_FAIL(hipEventRecord(ctx->ev_fork, stream));
-    HIP_OR_FAIL(hipStreamWaitEvent(ctx->side, ctx->ev_fork, 0));
-    HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, ctx->side));
-    HIP_OR_FAIL(launch_attend_expanded(a, ctx->side));
-    HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, ctx->side));
-    HIP_OR_FAIL(hipEventRecord(ctx->ev_join, ctx->side));
-    HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
-    HIP_OR_FAIL(launch_attend_full(a, stream));
-    HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
-    HIP_OR_FAIL(hipStreamWaitEvent(stream, ctx->ev_join, 0));
+    if (a.max_rank <= 64) {
+      // both passes in one launch on the caller's stream
+      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+      HIP_OR_FAIL(launch_attend_fused(a, stream));
+      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+    } else {
+      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, stream));
+      HIP_OR_FAIL(launch_attend_expanded(a, stream));
+      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, stream));
+      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+      HIP_OR_FAIL(launch_attend_full(a, stream));
+      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+    }
     HIP_OR_FAIL(launch_combine(a, stream));
     return SEKV_OK;
   }

@@ -39,6 +39,7 @@ struct AttendArgs {
   int nch_a4;                // workgroups per (b, kv) for that pass
   int P_max;                 // partial slots per (b, kv)
   int n_a5_wg;               // workgroups (one wave each) of the expanded-span kernel
+  int n_fx_wg;               // workgroups (four expanded-span waves each) of the fused launch
   int max_rank;              // largest span rank (selects the expanded-span kernel's register tiling)
   int n_a4_wg;               // workgroups of the full-res/summary kernel
   float qscale;              // log2(e) / sqrt(D)
@@ -71,6 +72,7 @@ struct ReconArgs {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_attend_full(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s);
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s);
 hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s);
 

@@ -772,13 +772,15 @@ __device__ __forceinline__ void advance(uint4 (&stg)[K], uint32_t& written, uint
   wave_lds_sync();
 }
 
+// `wid`: this wave's index among the `nwaves` waves running the pass; `lds`:
+// the wave's own LDS area (ExpLds::kBytes).
 template <typename T, int D, int G, int RGM>
-__device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
+__device__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* lds) {
   using X = ExpLds<T, G, RGM>;
   constexpr int K = ExpCfg<T, RGM>::K, RING = X::kRing;
   constexpr uint32_t MASK = RING - 1;
   constexpr int NC = D / 32, NJ = D / 16, ES = (int)sizeof(T), DG = D / 8;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int col = lane & 15, cls = lane >> 4;
   const int hc = min(col, G - 1);
   char* ring = lds;
@@ -807,7 +809,7 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
   const int excl = incl - own;
   const int total = __builtin_amdgcn_readlane(incl, 63);
 
-  for (int c = wid; c < total; c += a.n_a5_wg) {
+  for (int c = wid; c < total; c += nwaves) {
     // group of item c: the last lane, then the last of its groups, starting at or before c
     const uint64_t lm = __ballot(excl <= c);
     const int ln = 63 - __builtin_clzll(lm);
@@ -1070,9 +1072,24 @@ __device__ void role_expanded(const AttendArgs& a, int wid, char* lds) {
   }
 }
 
-// Full-resolution + summary pass (role A) and expanded-span pass (role E) are
-// separate kernels so each gets its own register budget; the host runs them
-// concurrently on two streams.
+// Full-resolution + summary pass (role A) and expanded-span pass (role E).
+// With every rank at most 64 both run in one launch: the first n_fx_wg
+// workgroups are four independent expanded-span waves each, the rest are
+// full-resolution chunks, so the two passes share the machine without a
+// second stream; otherwise (wider ranks, or host-resident factors that
+// arrive after the full-resolution pass starts) they are separate kernels.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attend_fused_kernel(const AttendArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  const int nx = a.n_fx_wg;
+  if ((int)blockIdx.x < nx) {
+    const int wave = threadIdx.x >> 6;
+    role_expanded<T, D, G, 4>(a, blockIdx.x * 4 + wave, nx * 4, lds + wave * ExpLds<T, G, 4>::kBytes);
+  } else {
+    role_full_summary<T, D, G>(a, blockIdx.x - nx, lds);
+  }
+}
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attend_full_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
@@ -1083,61 +1100,84 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__(kExpThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void attend_expanded_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
-  role_expanded<T, D, G, 4>(a, blockIdx.x, lds);
+  role_expanded<T, D, G, 4>(a, blockIdx.x, a.n_a5_wg, lds);
 }
 // Any rank up to kMaxSpan.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kExpThreads) void attend_expanded_wide_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
-  role_expanded<T, D, G, kMaxSpan / 16>(a, blockIdx.x, lds);
+  role_expanded<T, D, G, kMaxSpan / 16>(a, blockIdx.x, a.n_a5_wg, lds);
 }
 
 // ================================================================ combine
-// One workgroup per (b, h).  Pass 1: the maximum over partials (strided over
-// threads).  Pass 2: kCombineSplit thread groups each accumulate a strided
-// share of the partials for all D outputs; the groups are summed in LDS.
+// One workgroup per (b, h).  The partials of the head are split over
+// kCombineThreads / (D/4) thread groups; each thread owns four output
+// elements and merges its group's partials in one online log-sum-exp pass
+// (running maximum, rescale on increase).  The groups are merged in LDS.
 constexpr int kCombineThreads = 256;
 template <int D, int G>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const AttendArgs a) {
-  constexpr int SPLIT = kCombineThreads / D;   // 2 (D=128) or 4 (D=64)
-  __shared__ float red[kCombineThreads];
-  __shared__ float acc_s[SPLIT][D];
-  __shared__ float l_s[SPLIT];
+  constexpr int TPG = D / 4;                       // threads per group
+  constexpr int NG = kCombineThreads / TPG;        // 8 (D=128) or 16 (D=64)
+  __shared__ float m_s[NG], l_s[NG];
+  __shared__ float4 o_s[NG][TPG];
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int g = b * a.Hkv + h / G, gi = h % G;
   const int tid = threadIdx.x;
+  const int grp = tid / TPG, j4 = tid % TPG;
   const int np = a.nch_a4 + (a.exp_count[g] + kExpChunk - 1) / kExpChunk;
   const float* ml = a.part_ml + (size_t)g * a.P_max * G * 2;
   const float* po = a.part_o + (size_t)g * a.P_max * G * D;
-  float M = kNegInf;
-  for (int p = tid; p < np; p += kCombineThreads) M = fmaxf(M, ml[(p * G + gi) * 2]);
-  red[tid] = M;
-  __syncthreads();
-  for (int off = kCombineThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  M = red[0];
-  const int j = tid % D, part = tid / D;
-  float acc = 0.0f, L = 0.0f;
-#pragma unroll 4
-  for (int p = part; p < np; p += SPLIT) {
-    const float mp = ml[(p * G + gi) * 2];
-    const float lp = ml[(p * G + gi) * 2 + 1];
-    const float ov = po[((size_t)p * G + gi) * D + j];
-    const float f = (mp == kNegInf) ? 0.0f : exp2f(mp - M);
-    L += f * lp;
-    acc += f * ov;
-  }
-  acc_s[part][j] = acc;
-  if (j == 0) l_s[part] = L;
-  __syncthreads();
-  if (tid < D) {
-    float o = 0.0f, Lt = 0.0f;
+  // four partials per iteration, loads issued together, merged without branches
+  float M = kNegInf, L = 0.0f;
+  float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int p0 = grp; p0 < np; p0 += 4 * NG) {
+    float2 mlp[4];
+    float4 ov[4];
 #pragma unroll
-    for (int s2 = 0; s2 < SPLIT; ++s2) { o += acc_s[s2][tid]; Lt += l_s[s2]; }
-    a.out[(size_t)bh * D + tid] = o / Lt;
+    for (int u = 0; u < 4; ++u) {
+      const int p = min(p0 + u * NG, np - 1);
+      mlp[u] = *reinterpret_cast<const float2*>(ml + (p * G + gi) * 2);
+      ov[u] = *reinterpret_cast<const float4*>(po + ((size_t)p * G + gi) * D + 4 * j4);
+      if (p0 + u * NG >= np) mlp[u].x = kNegInf;
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, mlp[u].x);
+    if (Mn == kNegInf) continue;
+    const float sc = exp2f(M - Mn);   // 0 while M is -inf
+    L *= sc;
+    O = make_float4(O.x * sc, O.y * sc, O.z * sc, O.w * sc);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float f = exp2f(mlp[u].x - Mn);   // 0 for -inf partials
+      L += f * mlp[u].y;
+      O = make_float4(O.x + f * ov[u].x, O.y + f * ov[u].y, O.z + f * ov[u].z, O.w + f * ov[u].w);
+    }
+    M = Mn;
+  }
+  if (j4 == 0) {
+    m_s[grp] = M;
+    l_s[grp] = L;
+  }
+  o_s[grp][j4] = O;
+  __syncthreads();
+  if (tid < TPG) {
+    float Mt = kNegInf;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) Mt = fmaxf(Mt, m_s[q]);
+    float Lt = 0.0f;
+    float4 Ot = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const float f = (m_s[q] == kNegInf) ? 0.0f : exp2f(m_s[q] - Mt);
+      const float4 oq = o_s[q][tid];
+      Lt += f * l_s[q];
+      Ot = make_float4(Ot.x + f * oq.x, Ot.y + f * oq.y, Ot.z + f * oq.z, Ot.w + f * oq.w);
+    }
+    const float inv = 1.0f / Lt;
+    *reinterpret_cast<float4*>(a.out + (size_t)bh * D + 4 * tid) = make_float4(Ot.x * inv, Ot.y * inv, Ot.z * inv, Ot.w * inv);
   }
 }
 
@@ -1271,6 +1311,18 @@ hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s) {
                      ? attend_expanded_kernel<TT, DD, GG><<<a.n_a5_wg, kExpThreads, ExpLds<TT, GG, 4>::kBytes, s>>>(a)
                      : attend_expanded_wide_kernel<TT, DD, GG>
                            <<<a.n_a5_wg, kExpThreads, ExpLds<TT, GG, kMaxSpan / 16>::kBytes, s>>>(a)));
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  if (a.n_fx_wg + a.n_a4_wg == 0) return hipSuccess;
+  SEKV_DISPATCH(a.dtype, a.D, G,
+                (attend_fused_kernel<TT, DD, GG><<<a.n_fx_wg + a.n_a4_wg, kAttnThreads,
+                                                   (AttnLds<DD, GG>::kRoleA > 4 * ExpLds<TT, GG, 4>::kBytes
+                                                        ? AttnLds<DD, GG>::kRoleA
+                                                        : 4 * ExpLds<TT, GG, 4>::kBytes),
+                                                   s>>>(a)));
   return hipGetLastError();
 }
 

@@ -134,8 +134,7 @@ typedef struct sekv_spans {
 
 typedef struct sekv_ctx sekv_ctx;
 
-/* Context for one GPU: a side stream for the expanded-span kernel, events and
- * the copy-side thread pool.
+/* Context for one GPU: events, timing hooks and the copy-side thread pool.
  * Errors: SEKV_EINVAL (out == NULL), SEKV_EHIP (bad device), SEKV_ENOMEM. */
 sekv_status sekv_ctx_create(int device, sekv_ctx** out);
 void sekv_ctx_destroy(sekv_ctx* ctx);
@@ -245,6 +244,8 @@ size_t sekv_decode_host_workspace_bytes(const sekv_config* cfg, const sekv_spans
  *     host threads into host_ws, and copies them with hipMemcpyAsync on
  *     copy_stream while the full-resolution/summary pass runs on stream.
  *   copy_stream may be NULL (then stream is used).
+ *   Device-resident factors: every kernel runs on stream, in order; no host
+ *   wait (the call may be captured into a HIP graph).
  * Errors: SEKV_EINVAL / SEKV_ESHAPE / SEKV_ECAPACITY / SEKV_EHIP.
  */
 sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans,
@@ -256,9 +257,11 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* cfg, c
 /*
  * Measurement hook.  While enabled, sekv_route and sekv_mixed_attention_decode
  * record a timing-event pair around each of their main kernels, on the stream
- * the kernel runs on: the route kernels; the full-resolution + summary kernel;
- * the expanded-span kernel (on the context's side stream in the
- * device-resident mode).  sekv_profile_read waits for the recorded events,
+ * the kernel runs on: the route kernels ("route"); the attention kernels
+ * ("full": the full-resolution + summary pass, which with device-resident
+ * factors and ranks up to 64 is one launch together with the expanded-span
+ * pass; "expand": the expanded-span pass when it is a launch of its own).
+ * sekv_profile_read waits for the recorded events,
  * returns the summed milliseconds and launch counts since the last read, and
  * resets them.  Errors: SEKV_EINVAL (NULL ctx/outputs), SEKV_EHIP.
  */
