@@ -31,15 +31,19 @@ COUNTERS = os.path.join(ROOT, "profiles", "memory_counters.json")
 
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
-    counter runs (scaled by a 1 GiB copy's counts), or None when the kernel
-    source has changed since they were taken."""
+    counter runs (scaled by a 1 GiB copy's counts), or None when a source they
+    depend on (the kernels and the launch constants and plan) has changed since
+    they were taken: the record holds the SHA-256 of the sources' contents,
+    concatenated in the listed order."""
     import hashlib
     try:
         rec = json.load(open(COUNTERS))
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        h = hashlib.sha256()
+        for path in rec["sources"]:
+            h.update(open(os.path.join(ROOT, path), "rb").read())
     except (OSError, ValueError, KeyError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256") or kernel not in rec.get("kernels", {}):
+    if h.hexdigest() != rec.get("sources_sha256") or kernel not in rec.get("kernels", {}):
         return None
     return rec["kernels"][kernel]["hbm_bytes_per_launch"]
 

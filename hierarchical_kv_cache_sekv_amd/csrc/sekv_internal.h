@@ -14,7 +14,7 @@ constexpr int kRouteThreads = 256;   // spans per route workgroup (one lane per 
 constexpr int kAttnThreads = 256;    // four waves per attention workgroup
 constexpr int kExpChunk = 4;         // expanded spans per work item of the expanded-span kernel
 constexpr int kExpThreads = 64;      // one wave per expanded-span workgroup
-constexpr int kExpWaves = 4096;      // most waves (workgroups) of one expanded-span launch
+constexpr int kExpWaves = 2048;      // most waves (workgroups) of one expanded-span launch
 
 struct RouteArgs {
   int dtype;                 // 0 f32, 1 bf16

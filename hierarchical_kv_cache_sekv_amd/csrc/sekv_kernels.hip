@@ -1114,11 +1114,11 @@ __global__ __launch_bounds__(kExpThreads) void attend_expanded_wide_kernel(const
 // kCombineThreads / (D/4) thread groups; each thread owns four output
 // elements and merges its group's partials in one online log-sum-exp pass
 // (running maximum, rescale on increase).  The groups are merged in LDS.
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 512;
 template <int D, int G>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const AttendArgs a) {
   constexpr int TPG = D / 4;                       // threads per group
-  constexpr int NG = kCombineThreads / TPG;        // 8 (D=128) or 16 (D=64)
+  constexpr int NG = kCombineThreads / TPG;        // 16 (D=128) or 32 (D=64)
   __shared__ float m_s[NG], l_s[NG];
   __shared__ float4 o_s[NG][TPG];
   const int bh = blockIdx.x;
