@@ -11,6 +11,7 @@ constexpr int kMaxBatch = 64;        // per-sequence sizes travel in kernel argu
 constexpr int kMaxGroups = 256;      // batch * kv heads handled by one decode launch
 constexpr int kMaxSpan = 128;        // longest span body / highest rank the kernels hold
 constexpr int kRouteThreads = 256;   // spans per route workgroup (one lane per span)
+constexpr int kCompactThreads = 256; // threads of the compaction workgroup of one (b, kv)
 constexpr int kAttnThreads = 256;    // four waves per attention workgroup
 constexpr int kExpChunk = 4;         // expanded spans per work item of the expanded-span kernel
 constexpr int kExpThreads = 64;      // one wave per expanded-span workgroup

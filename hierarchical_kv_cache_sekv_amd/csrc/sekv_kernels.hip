@@ -276,11 +276,12 @@ __device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t w) {
 __device__ __forceinline__ uint32_t nonzero_bytes16(const uint4& m) {
   return nonzero_bytes4(m.x) | (nonzero_bytes4(m.y) << 4) | (nonzero_bytes4(m.z) << 8) | (nonzero_bytes4(m.w) << 12);
 }
-// One workgroup per (b, kv).  Each thread reads the masks of 32 consecutive
-// spans (two 16-byte loads), turns them into a 32-bit "expanded" set, and one
-// block-wide exclusive scan of the set sizes gives its output position.
-__global__ __launch_bounds__(kRouteThreads) void route_compact_kernel(const RouteArgs a) {
-  __shared__ int wsum[kRouteThreads / 64];
+// One workgroup of kCompactThreads per (b, kv).  Each thread reads the masks
+// of 32 consecutive spans (two 16-byte loads), turns them into a 32-bit
+// "expanded" set, and one block-wide exclusive scan of the set sizes gives its
+// output position.
+__global__ __launch_bounds__(kCompactThreads) void route_compact_kernel(const RouteArgs a) {
+  __shared__ int wsum[kCompactThreads / 64];
   const int kv = blockIdx.x, b = blockIdx.y;
   const int g = b * a.Hkv + kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_compact_kernel(const Rout
   int32_t* lst = a.exp_list + (size_t)g * a.seg_cap;
   uint8_t* msk = a.exp_mask + (size_t)g * a.seg_cap;
   int base = 0;
-  for (int t0 = 0; t0 < ns; t0 += 32 * kRouteThreads) {
+  for (int t0 = 0; t0 < ns; t0 += 32 * kCompactThreads) {
     const int s0 = t0 + 32 * tid;
     const uint4 zero = make_uint4(0, 0, 0, 0);
     const uint4 m0 = s0 < ns ? *reinterpret_cast<const uint4*>(dm + s0) : zero;
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_compact_kernel(const Rout
     __syncthreads();
     int wbase = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < kRouteThreads / 64; ++w) {
+    for (int w = 0; w < kCompactThreads / 64; ++w) {
       const int v = wsum[w];
       if (w < wave) wbase += v;
       total += v;
@@ -453,7 +454,7 @@ __device__ __forceinline__ void tile_step(const TileOps<T, D>& o, const TileSrc<
 // Each lane therefore keeps the online-softmax state of head (lane % 16) and
 // rescales only its own accumulators.
 template <typename T, int D, int G>
-__device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
+__device__ __forceinline__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
   constexpr int NC = D / 32, NJ = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, cls = lane >> 4;
@@ -467,20 +468,55 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
   uint8_t* smask = reinterpret_cast<uint8_t*>(lds);
   float* slog = reinterpret_cast<float*>(lds + AttnLds<D, G>::kMaskBytes);
   float* merge = reinterpret_cast<float*>(lds + AttnLds<D, G>::kMaskBytes * 5);
+
+  const int ftiles = (a.full_cap + 31) / 32, stiles = (a.seg_cap + 31) / 32;
+  const T* fk = static_cast<const T*>(a.full_k) + (size_t)g * a.full_cap * D;
+  const T* fvt = static_cast<const T*>(a.full_v) + (size_t)g * ftiles * 32 * D;
+  const T* sk = static_cast<const T*>(a.sum_k) + (size_t)g * a.seg_cap * D;
+  const T* svt = static_cast<const T*>(a.sum_v) + (size_t)g * stiles * 32 * D;
+
+  // This wave's first tile (t0 + wave) and q are put in flight before the
+  // summary masks are gathered, so the gather's memory round trips overlap
+  // the tile loads.
+  TileOps<T, D> opA;
+  const TileSrc<T> src{fk, fvt, sk, svt, nft, nf, ns};
+  int t = t0 + wave;
+  if (t < t1) tile_load<T, D>(opA, src, t, col, cls);
+  // q as the B operand: column = head (zero for columns >= G)
+  Vec8<T> qB[NC];
+  const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G + min(col, G - 1)) * D;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    qB[c] = ld8(qrow + 32 * c + 8 * cls);
+    if (col >= G) zero8(qB[c]);
+  }
+
+  // Summaries of this chunk: log2 of the span length, and the head mask of
+  // spans in the expanded list (0 for the others).  The list is ascending, so
+  // its entries in [S0, S1) are one run starting at lo = the number of entries
+  // below S0, found in two rounds of parallel probes.
   const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
   for (int i = tid; i < S1 - S0; i += kAttnThreads) {
     const int S = S0 + i;
     smask[i] = 0;
     slog[i] = log2f((float)(so[S + 1] - so[S] - 1));
   }
-  __syncthreads();
   if (S1 > S0) {
     const int cnt = a.exp_count[g];
     const int32_t* lst = a.exp_list + (size_t)g * a.seg_cap;
-    int lo = 0, hi = cnt;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (lst[mid] < S0) lo = mid + 1; else hi = mid;
+    // round 1: probe entries 0, step, 2 step, ...; the probes below S0 are a prefix
+    const int step = (cnt + kAttnThreads - 1) / kAttnThreads;
+    const int pj = tid * step;
+    const int nb = __syncthreads_count(pj < cnt && lst[pj] < S0);
+    int lo = 0;
+    if (nb > 0) {
+      // lo lies in ((nb - 1) step, nb step]: count the unknown entries between
+      const int base = (nb - 1) * step + 1, end = min(nb * step, cnt);
+      lo = base;
+      for (int k0 = 0; k0 < end - base; k0 += kAttnThreads) {
+        const int j = base + k0 + tid;
+        lo += __syncthreads_count(j < end && lst[j] < S0);
+      }
     }
     for (int j = lo + tid; j < cnt; j += kAttnThreads) {
       const int S = lst[j];
@@ -490,44 +526,19 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
   }
   __syncthreads();
 
-  // q as the B operand: column = head (zero for columns >= G)
-  Vec8<T> qB[NC];
-  const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G + min(col, G - 1)) * D;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    qB[c] = ld8(qrow + 32 * c + 8 * cls);
-    if (col >= G) zero8(qB[c]);
-  }
   const float qscale = a.qscale;
   float m = kNegInf, lsum = 0.0f;
   f32x4_t acc[NJ];
 #pragma unroll
   for (int jt = 0; jt < NJ; ++jt) acc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int ftiles = (a.full_cap + 31) / 32, stiles = (a.seg_cap + 31) / 32;
-  const T* fk = static_cast<const T*>(a.full_k) + (size_t)g * a.full_cap * D;
-  const T* fvt = static_cast<const T*>(a.full_v) + (size_t)g * ftiles * 32 * D;
-  const T* sk = static_cast<const T*>(a.sum_k) + (size_t)g * a.seg_cap * D;
-  const T* svt = static_cast<const T*>(a.sum_v) + (size_t)g * stiles * 32 * D;
-
-  // Software pipeline over this wave's tiles t0 + wave, t0 + wave + 4, ...:
-  // the next tile's K rows and V^T tile are loaded while the current one is
-  // scored and accumulated (two operand sets, used alternately).
-  TileOps<T, D> opA, opB;
-  const TileSrc<T> src{fk, fvt, sk, svt, nft, nf, ns};
-  int t = t0 + wave;
-  if (t < t1) {
-    tile_load<T, D>(opA, src, t, col, cls);
-    for (;;) {
-      if (t + 4 < t1) tile_load<T, D>(opB, src, t + 4, col, cls);
-      tile_step<T, D, G>(opA, src, t, S0, smask, slog, qB, qscale, col, cls, m, lsum, acc);
-      t += 4;
-      if (t >= t1) break;
-      if (t + 4 < t1) tile_load<T, D>(opA, src, t + 4, col, cls);
-      tile_step<T, D, G>(opB, src, t, S0, smask, slog, qB, qscale, col, cls, m, lsum, acc);
-      t += 4;
-      if (t >= t1) break;
-    }
+  // This wave's tiles t, t + 4, ...: one operand set, loaded as soon as the
+  // previous tile is scored.  A single set keeps the fused launch at three
+  // waves per SIMD; the other waves of the SIMD cover the load latency.
+  while (t < t1) {
+    tile_step<T, D, G>(opA, src, t, S0, smask, slog, qB, qscale, col, cls, m, lsum, acc);
+    t += 4;
+    if (t < t1) tile_load<T, D>(opA, src, t, col, cls);
   }
 
   // this wave's state of head col: lsum summed over the four lane classes
@@ -610,15 +621,38 @@ __device__ void role_full_summary(const AttendArgs& a, int idx, char* lds) {
 template <typename T, int RGM> struct ExpCfg;
 // K: 1 KB chunks per granule in flight.  The ring holds a granule in flight
 // plus the largest piece read at once (16 rows of Vh_K or U, or one 16-rank
-// W_V block: 16 x 128 elements).
+// W_V block: 16 x 128 elements).  The four waves of a workgroup stay within
+// 64 KB of LDS: more than that per workgroup halves the workgroups a compute
+// unit holds.
 template <int RGM> struct ExpCfg<bf16raw, RGM> { static constexpr int K = 4; static constexpr int kRing = 8192; };
 template <int RGM> struct ExpCfg<float, RGM> { static constexpr int K = 8; static constexpr int kRing = 16384; };
 constexpr int kExpTok = 192;   // tokens of one chunk of spans (score buffer)
 
+// Byte positions in a per-wave ring of RING bytes (a multiple of 1 KB, not
+// necessarily a power of two).
+template <uint32_t RING>
+struct RingPos {
+  static constexpr bool kPow2 = (RING & (RING - 1)) == 0;
+  // stream offset x -> ring position
+  __device__ static __forceinline__ uint32_t of(uint32_t x) {
+    if constexpr (kPow2) return x & (RING - 1);
+    else return x % RING;
+  }
+  // (p + o) mod RING for a ring position p and an offset o < RING
+  __device__ static __forceinline__ uint32_t add(uint32_t p, uint32_t o) {
+    if constexpr (kPow2) {
+      return (p + o) & (RING - 1);
+    } else {
+      const uint32_t x = p + o;
+      return x >= RING ? x - RING : x;
+    }
+  }
+};
+
 template <typename T, int G, int RGM>
 struct ExpLds {
   static constexpr int kRing = ExpCfg<T, RGM>::kRing;
-  static_assert((kRing & (kRing - 1)) == 0, "ring size is a power of two");
+  static_assert(kRing % 1024 == 0, "ring size is a whole number of 1 KB chunks");
   static_assert(kRing >= ExpCfg<T, RGM>::K * 1024 + 16 * kMaxSpan * (int)sizeof(T), "ring holds a granule and a piece");
   static constexpr int kS = kRing;                          // scores [token group][class][G] float4
   static constexpr int kQ = kS + (kExpTok / 16) * 4 * G * 16;   // q of the item's G heads [G][kMaxD]
@@ -663,14 +697,14 @@ __device__ __forceinline__ Vec4<T> rd4(const char* ring, uint32_t ob) {
   else x.v = *reinterpret_cast<const float4*>(ring + ob);
   return x;
 }
-template <typename T>
-__device__ __forceinline__ Vec8<T> rd8(const char* ring, uint32_t ob, uint32_t mask) {
+template <typename T, uint32_t RING>
+__device__ __forceinline__ Vec8<T> rd8(const char* ring, uint32_t ob) {
   Vec8<T> x;
   if constexpr (sizeof(T) == 2) {
     x.v = *reinterpret_cast<const uint4*>(ring + ob);
   } else {
     x.a = *reinterpret_cast<const float4*>(ring + ob);
-    x.b = *reinterpret_cast<const float4*>(ring + ((ob + 16) & mask));
+    x.b = *reinterpret_cast<const float4*>(ring + RingPos<RING>::add(ob, 16u));
   }
   return x;
 }
@@ -761,9 +795,10 @@ template <typename T, int D, int K, int RING>
 __device__ __forceinline__ void advance(uint4 (&stg)[K], uint32_t& written, uint32_t e, RegionCursor& c,
                                         const ItemMeta& m, int lane, char* ring) {
   while (written < e) {
+    const uint32_t w0 = RingPos<RING>::of(written);
 #pragma unroll
     for (int jj = 0; jj < K; ++jj) {
-      *reinterpret_cast<uint4*>(ring + ((written + 1024u * jj + 16u * (uint32_t)lane) & (RING - 1))) = stg[jj];
+      *reinterpret_cast<uint4*>(ring + RingPos<RING>::add(w0, 1024u * jj) + 16u * (uint32_t)lane) = stg[jj];
       stg[jj] = gload16(cursor_addr(c, lane));
       cursor_next<T, D>(c, m);
     }
@@ -775,10 +810,11 @@ __device__ __forceinline__ void advance(uint4 (&stg)[K], uint32_t& written, uint
 // `wid`: this wave's index among the `nwaves` waves running the pass; `lds`:
 // the wave's own LDS area (ExpLds::kBytes).
 template <typename T, int D, int G, int RGM>
-__device__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* lds) {
+__device__ __forceinline__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* lds) {
   using X = ExpLds<T, G, RGM>;
-  constexpr int K = ExpCfg<T, RGM>::K, RING = X::kRing;
-  constexpr uint32_t MASK = RING - 1;
+  constexpr int K = ExpCfg<T, RGM>::K;
+  constexpr uint32_t RING = X::kRing;
+  using RP = RingPos<RING>;
   constexpr int NC = D / 32, NJ = D / 16, ES = (int)sizeof(T), DG = D / 8;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, cls = lane >> 4;
@@ -910,8 +946,8 @@ __device__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* ld
         for (int q2 = 0; q2 < 2; ++q2) {
           const int k = lane + 64 * q2;
           const int kc = min(k, r - 1);
-          const float sv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * kc) & MASK));
-          const float gv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * (rq + kc)) & MASK));
+          const float sv = *reinterpret_cast<const float*>(ring + RP::add(RP::of(s_sg), 4u * kc));
+          const float gv = *reinterpret_cast<const float*>(ring + RP::add(RP::of(s_sg), 4u * (rq + kc)));
           stl[k] = k < r ? sv * gv : 0.0f;
         }
         // y of rank groups rg, as the B operand of the score product
@@ -921,13 +957,14 @@ __device__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* ld
           if (rg < RG) {
             advance<T, D, K, RING>(stg, written, s_vk + (uint32_t)(min(r, 16 * rg + 16) * D * ES), cur, im, lane, ring);
             const int k = min(16 * rg + col, r - 1);
+            const uint32_t b_vk = RP::of(s_vk + (uint32_t)(16 * rg * D * ES));   // this rank group's 16 rows
             f32x4_t yc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int cc = 0; cc < NC; ++cc) {
               const int pg = (4 * cc + cls + k) & (DG - 1);   // rotated 8-element group
               Vec8<T> qop = ld8(qs + hc * D + 32 * cc + 8 * cls);
               if (col >= G) zero8(qop);
-              yc = mma8(rd8<T>(ring, (s_vk + (uint32_t)((k * D + 8 * pg) * ES)) & MASK, MASK), qop, yc);
+              yc = mma8(rd8<T, RING>(ring, RP::add(b_vk, (uint32_t)(((k - 16 * rg) * D + 8 * pg) * ES))), qop, yc);
             }
             // sigma * gate of ranks 16 rg + 4 cls + v
             const float4 sgv = *reinterpret_cast<const float4*>(stl + 16 * rg + 4 * cls);
@@ -945,12 +982,13 @@ __device__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* ld
         for (int tg = 0; tg < TG; ++tg) {
           advance<T, D, K, RING>(stg, written, s_u + (uint32_t)(min(L, 16 * tg + 16) * rp * ES), cur, im, lane, ring);
           const int trow = min(16 * tg + col, L - 1);
+          const uint32_t b_tg = RP::of(s_u + (uint32_t)(16 * tg * rp * ES));   // this token group's 16 rows
           f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int rg = 0; rg < RGM; ++rg) {
             if (rg < RG) {
               const int k0 = min(16 * rg + 4 * cls, rp - 4);
-              const Vec4<T> uop = rd4<T>(ring, (s_u + (uint32_t)((trow * rp + k0) * ES)) & MASK);
+              const Vec4<T> uop = rd4<T>(ring, RP::add(b_tg, (uint32_t)(((trow - 16 * tg) * rp + k0) * ES)));
               sc = mma4(uop, yhi[rg], sc);
               if constexpr (ES == 2) sc = mma4(uop, ylo[rg], sc);
             }
@@ -995,8 +1033,8 @@ __device__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* ld
         for (int q2 = 0; q2 < 2; ++q2) {
           const int k = lane + 64 * q2;
           const int kc = min(k, r - 1);
-          const float sv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * kc) & MASK));
-          const float gv = *reinterpret_cast<const float*>(ring + ((s_sg + 4u * (rq + kc)) & MASK));
+          const float sv = *reinterpret_cast<const float*>(ring + RP::add(RP::of(s_sg), 4u * kc));
+          const float gv = *reinterpret_cast<const float*>(ring + RP::add(RP::of(s_sg), 4u * (rq + kc)));
           stl[k] = k < r ? sv * gv : 0.0f;
         }
         f32x4_t am[RGM];
@@ -1005,6 +1043,7 @@ __device__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* ld
         for (int tg = 0; tg < TG; ++tg) {
           advance<T, D, K, RING>(stg, written, s_u + (uint32_t)(min(L, 16 * tg + 16) * rp * ES), cur, im, lane, ring);
           const float4 sv = sbuf[((tgb + tg) * 4 + cls) * G + hc];
+          const uint32_t b_tg = RP::of(s_u + (uint32_t)(16 * tg * rp * ES));   // this token group's 16 rows
           float pr[4];
           pr[0] = (m == kNegInf) ? 0.0f : exp2f(sv.x - m);
           pr[1] = (m == kNegInf) ? 0.0f : exp2f(sv.y - m);
@@ -1021,7 +1060,7 @@ __device__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* ld
 #pragma unroll
               for (int e4 = 0; e4 < 4; ++e4) {
                 const int t = min(16 * tg + 4 * cls + e4, L - 1);
-                const uint32_t ob = (s_u + (uint32_t)((t * rp + kc) * ES)) & MASK;
+                const uint32_t ob = RP::add(b_tg, (uint32_t)(((t - 16 * tg) * rp + kc) * ES));
                 if constexpr (ES == 2) ev[e4] = *reinterpret_cast<const uint16_t*>(ring + ob);
                 else ev[e4] = *reinterpret_cast<const uint32_t*>(ring + ob);
               }
@@ -1045,9 +1084,10 @@ __device__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* ld
             Vec4<T> bB;
             pack4(bv, bB);
             const int k0 = min(4 * cls, wk - 4);
+            const uint32_t b_wg = RP::of(s_wg);
 #pragma unroll
             for (int jt = 0; jt < NJ; ++jt)
-              acc[jt] = mma4(rd4<T>(ring, (s_wg + (uint32_t)(((16 * jt + col) * wk + k0) * ES)) & MASK), bB, acc[jt]);
+              acc[jt] = mma4(rd4<T>(ring, RP::add(b_wg, (uint32_t)(((16 * jt + col) * wk + k0) * ES))), bB, acc[jt]);
           }
         }
       }
@@ -1078,8 +1118,10 @@ __device__ void role_expanded(const AttendArgs& a, int wid, int nwaves, char* ld
 // full-resolution chunks, so the two passes share the machine without a
 // second stream; otherwise (wider ranks, or host-resident factors that
 // arrive after the full-resolution pass starts) they are separate kernels.
+// Three waves per SIMD: with every slot taken by a wave at the start, the
+// expanded-span waves leave a third of the slots to full-resolution chunks.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void attend_fused_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
   const int nx = a.n_fx_wg;
@@ -1091,7 +1133,7 @@ void attend_fused_kernel(const AttendArgs a) {
   }
 }
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2))) void attend_full_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(3))) void attend_full_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
   role_full_summary<T, D, G>(a, blockIdx.x, lds);
 }
@@ -1110,37 +1152,37 @@ __global__ __launch_bounds__(kExpThreads) void attend_expanded_wide_kernel(const
 }
 
 // ================================================================ combine
-// One workgroup per (b, h).  The partials of the head are split over
-// kCombineThreads / (D/4) thread groups; each thread owns four output
-// elements and merges its group's partials in one online log-sum-exp pass
-// (running maximum, rescale on increase).  The groups are merged in LDS.
-constexpr int kCombineThreads = 512;
+// One workgroup per (b, h, slice of 32 output elements): D/32 workgroups per
+// head, so a launch has B * Hq * D/32 of them.  The 256 threads form 32 rows
+// of 8; row r merges partials r, r + 32, ... (four loads in flight per step,
+// branch-free online log-sum-exp), each thread owning four of the slice's
+// elements.  The 32 row states then merge pairwise in LDS in five halving
+// steps.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineRows = kCombineThreads / 8;
 template <int D, int G>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const AttendArgs a) {
-  constexpr int TPG = D / 4;                       // threads per group
-  constexpr int NG = kCombineThreads / TPG;        // 16 (D=128) or 32 (D=64)
-  __shared__ float m_s[NG], l_s[NG];
-  __shared__ float4 o_s[NG][TPG];
-  const int bh = blockIdx.x;
+  constexpr int NSL = D / 32;
+  __shared__ float m_s[kCombineRows], l_s[kCombineRows];
+  __shared__ float4 o_s[kCombineRows][8];
+  const int bh = blockIdx.x / NSL, sl = blockIdx.x % NSL;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int g = b * a.Hkv + h / G, gi = h % G;
-  const int tid = threadIdx.x;
-  const int grp = tid / TPG, j4 = tid % TPG;
+  const int tid = threadIdx.x, row = tid >> 3, c4 = tid & 7;
   const int np = a.nch_a4 + (a.exp_count[g] + kExpChunk - 1) / kExpChunk;
   const float* ml = a.part_ml + (size_t)g * a.P_max * G * 2;
-  const float* po = a.part_o + (size_t)g * a.P_max * G * D;
-  // four partials per iteration, loads issued together, merged without branches
+  const float* po = a.part_o + (size_t)g * a.P_max * G * D + 32 * sl + 4 * c4;
   float M = kNegInf, L = 0.0f;
   float4 O = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int p0 = grp; p0 < np; p0 += 4 * NG) {
+  for (int p0 = row; p0 < np; p0 += 4 * kCombineRows) {
     float2 mlp[4];
     float4 ov[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int p = min(p0 + u * NG, np - 1);
+      const int p = min(p0 + u * kCombineRows, np - 1);
       mlp[u] = *reinterpret_cast<const float2*>(ml + (p * G + gi) * 2);
-      ov[u] = *reinterpret_cast<const float4*>(po + ((size_t)p * G + gi) * D + 4 * j4);
-      if (p0 + u * NG >= np) mlp[u].x = kNegInf;
+      ov[u] = *reinterpret_cast<const float4*>(po + ((size_t)p * G + gi) * D);
+      if (p0 + u * kCombineRows >= np) mlp[u].x = kNegInf;
     }
     float Mn = M;
 #pragma unroll
@@ -1157,27 +1199,37 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const AttendAr
     }
     M = Mn;
   }
-  if (j4 == 0) {
-    m_s[grp] = M;
-    l_s[grp] = L;
+  // rows [s, 2s) fold into rows [0, s): reads and writes of one step touch
+  // disjoint rows, so one barrier per step orders them
+  if (c4 == 0) {
+    m_s[row] = M;
+    l_s[row] = L;
   }
-  o_s[grp][j4] = O;
-  __syncthreads();
-  if (tid < TPG) {
-    float Mt = kNegInf;
+  o_s[row][c4] = O;
 #pragma unroll
-    for (int q = 0; q < NG; ++q) Mt = fmaxf(Mt, m_s[q]);
-    float Lt = 0.0f;
-    float4 Ot = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      const float f = (m_s[q] == kNegInf) ? 0.0f : exp2f(m_s[q] - Mt);
-      const float4 oq = o_s[q][tid];
-      Lt += f * l_s[q];
-      Ot = make_float4(Ot.x + f * oq.x, Ot.y + f * oq.y, Ot.z + f * oq.z, Ot.w + f * oq.w);
+  for (int s = kCombineRows / 2; s >= 1; s >>= 1) {
+    __syncthreads();
+    if (row < s) {
+      const float m2 = m_s[row + s], l2 = l_s[row + s];
+      const float4 o2 = o_s[row + s][c4];
+      const float Mn = fmaxf(M, m2);
+      if (Mn != kNegInf) {
+        const float f1 = exp2f(M - Mn), f2 = exp2f(m2 - Mn);
+        L = L * f1 + l2 * f2;
+        O = make_float4(O.x * f1 + o2.x * f2, O.y * f1 + o2.y * f2, O.z * f1 + o2.z * f2, O.w * f1 + o2.w * f2);
+        M = Mn;
+      }
+      if (c4 == 0) {
+        m_s[row] = M;
+        l_s[row] = L;
+      }
+      o_s[row][c4] = O;
     }
-    const float inv = 1.0f / Lt;
-    *reinterpret_cast<float4*>(a.out + (size_t)bh * D + 4 * tid) = make_float4(Ot.x * inv, Ot.y * inv, Ot.z * inv, Ot.w * inv);
+  }
+  if (row == 0) {
+    const float inv = 1.0f / L;
+    *reinterpret_cast<float4*>(a.out + (size_t)bh * D + 32 * sl + 4 * c4) =
+        make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
   }
 }
 
@@ -1291,7 +1343,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   SEKV_DISPATCH(a.dtype, a.D, G, (route_decide_kernel<TT, DD, GG><<<grid, kRouteThreads, 0, s>>>(a)));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  route_compact_kernel<<<dim3(a.Hkv, a.B), kRouteThreads, 0, s>>>(a);
+  route_compact_kernel<<<dim3(a.Hkv, a.B), kCompactThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1328,7 +1380,7 @@ hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s) {
 
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  SEKV_DISPATCH_D(a.D, G, (combine_kernel<DD, GG><<<a.B * a.Hq, kCombineThreads, 0, s>>>(a)));
+  SEKV_DISPATCH_D(a.D, G, (combine_kernel<DD, GG><<<a.B * a.Hq * (DD / 32), kCombineThreads, 0, s>>>(a)));
   return hipGetLastError();
 }
 
