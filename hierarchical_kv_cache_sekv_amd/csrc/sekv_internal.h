@@ -13,7 +13,7 @@ constexpr int kMaxSpan = 128;        // longest span body / highest rank the ker
 constexpr int kRouteThreads = 256;   // spans per route workgroup (one lane per span)
 constexpr int kCompactThreads = 256; // threads of the compaction workgroup of one (b, kv)
 constexpr int kAttnThreads = 256;    // four waves per attention workgroup
-constexpr int kExpChunk = 4;         // expanded spans per work item of the expanded-span kernel
+constexpr int kExpChunk = 8;         // expanded spans per work item of the expanded-span kernel
 constexpr int kExpThreads = 64;      // one wave per expanded-span workgroup
 constexpr int kExpWaves = 2048;      // most waves (workgroups) of one expanded-span launch
 

@@ -12,15 +12,16 @@
 //                   lane: canonical float32 score and decision bits.
 //   route_compact_kernel  one workgroup per (b, kv): ascending list, head
 //                   masks and count.
+//   attend_fused_kernel  both attention passes in one launch (every rank
+//                   <= 64): expanded-span waves first, then full-resolution
+//                   chunks.
 //   attend_full_kernel  (role A) full-resolution entries + size-corrected
-//                   summaries: streams K/V rows with 16 lanes per row (8
-//                   elements per lane, 16-byte loads), one online-softmax state
-//                   per row subgroup.
+//                   summaries in 32-entry tiles, q.K and P.V on the matrix
+//                   cores, one online-softmax state per head.
 //   attend_expanded_kernel  (role E) expanded spans, never materialising the
 //                   rebuilt K/V: it applies the factors to the query
 //                   (y = sigma~ .* (Vh_K q)), scores the tokens with U y, and
-//                   applies the weights back through U and Vh_V, reading every
-//                   factor byte once.
+//                   applies the weights back through U and Vh_V.
 //   combine_kernel  log-sum-exp merge of all partials of a query head.
 //   recon_*         standalone token-level K/V rebuild (tests, unfused use).
 #include <hip/hip_runtime.h>
@@ -183,7 +184,9 @@ constexpr float kNegInf = -__builtin_inff();
 // Two kernels: route_decide_kernel (one lane per span, many workgroups) writes
 // the per-span head mask; route_compact_kernel (one workgroup per (b, kv))
 // turns it into the ascending list.  The kernel boundary makes the masks
-// visible across XCDs; no device-scope fence is needed inside either kernel.
+// visible across XCDs; no device-scope fence is needed inside either kernel
+// (a variant where the last workgroup of each (b, kv) compacts behind
+// agent-scope fences ran the route about five times slower).
 //
 // route_decide_kernel: a workgroup takes 256 consecutive spans of one (b, kv).
 // Their routing keys are staged through LDS 128 bytes of each row at a time

@@ -210,6 +210,23 @@ def test_fullsize_t128k_b4_sweep(ctx):
         frac = f.check_route(dec, cnt, lst, msk)
         err = f.check_out(1, dec, out, groups)
         log(f"{w.name} f={frac_t}: route exact, realized f={frac:.3f}, max err {err:.2e}")
+    # Back-to-back route calls on one workspace, alternating queries and
+    # thresholds: every call's list, masks and counts stay bit-exact (the
+    # per-group arrival counters return to zero after each call).
+    import torch
+    cases = []
+    for frac_t in (0.05, 0.50):
+        th = f.thresholds([frac_t] * w.batch)
+        for st in (0, 1):
+            cases.append((torch.from_numpy(np.ascontiguousarray(f.x.q[st])).to(f.cache.elem).cuda(),
+                          torch.from_numpy(th).cuda(), f.expected_route(st, th)))
+    for rep in range(24):
+        qd, td, dec = cases[rep % len(cases)]
+        f.B.route(ctx, f.cache, qd, td, f.route_out, f.route_ws)
+        torch.cuda.synchronize()
+        f.check_route(dec, f.route_out.exp_count.cpu().numpy(), f.route_out.exp_list.cpu().numpy(),
+                      f.route_out.exp_mask.cpu().numpy())
+    log(f"{w.name}: 24 consecutive route calls bit-exact")
 
 
 def test_fullsize_t128k_b4_full_expansion_equals_dense(ctx):
