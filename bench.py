@@ -117,6 +117,104 @@ def cpu_baseline(w, x, theta, budget_s=12.0):
             "eff_ctx_tokens_per_s": steps_per_s * w.batch * w.n_ctx}
 
 
+def host_resident(args):
+    """The host-resident workload: 128K context, batch 1, ranks 8..32, factor
+    pools in pinned host memory, the listed spans' factor blocks gathered and
+    copied to the device every step (a host wait on the route list, a copy
+    stream overlapped with the full-resolution pass).  Not graph-capturable;
+    eager steps.  Prints one JSON line: end-to-end steps/s including the PCIe
+    copy, the factor bytes that cross PCIe per step and their rate, and the
+    kernels' HBM fraction on their algorithmic bytes."""
+    import numpy as np
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    from hierarchical_kv_cache_sekv_amd import synth
+
+    w = synth.workload(3, factors_on_host=True)
+    e = 2 if w.dtype == "bf16" else 4
+    Q = args.queries
+    log(f"workload {w.name}: B={w.batch} T={w.n_ctx} ranks {w.rank_lo}..{w.rank_hi} f={w.expand_frac}, pinned host factors")
+    x = synth.make_inputs(w, n_steps=Q)
+    ctx = B.Context(0)
+    cfg = B.make_config(w)
+    plan = B.plan_spans(cfg, x.surprisal, x.boundary_thr, x.rank_req)
+    cache = B.SpanCache(cfg, plan)
+    et = cache.elem
+    kd = torch.from_numpy(x.k).to(et).cuda()
+    vd = torch.from_numpy(x.v).to(et).cuda()
+    B.build_spans(ctx, cache, kd, vd, x.surprisal, x.route_proj, x.gate)
+    del kd, vd
+    torch.cuda.synchronize()
+    G = w.group
+    qf = torch.from_numpy(x.q).cuda()
+    rho = cache.rho.float()
+    theta = np.empty((w.batch, w.n_q_heads), np.float32)
+    for b in range(w.batch):
+        ns = int(plan.n_seg[b])
+        z = torch.empty((Q, w.n_q_heads, ns), device="cuda")
+        for kv in range(w.n_kv_heads):
+            z[:, kv * G:(kv + 1) * G] = qf[:, b, kv * G:(kv + 1) * G] @ rho[b, kv, :ns].T
+        theta[b] = synth.calibrate_theta(z.cpu().numpy(), w.expand_frac, G)
+    theta_d = torch.from_numpy(theta).cuda()
+    qd = qf.to(et).contiguous()
+    del qf, rho
+    ro = B.RouteOut(cfg, cache.seg_cap)
+    rws = B.route_workspace(cache)
+    dws = B.DecodeWorkspace(cache)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    copy_stream = torch.cuda.Stream()
+
+    def step(i):
+        qs = qd[i % Q]
+        B.route(ctx, cache, qs, theta_d, ro, rws)
+        B.decode(ctx, cache, qs, ro, out, dws, copy_stream=copy_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ctx.profile(True)
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    prof = ctx.profile_read()
+    ctx.profile(False)
+    kern_us = {k: (v[0] / max(v[1], 1)) * 1e3 for k, v in prof.items()}
+    # algorithmic bytes and PCIe bytes of the timed steps (lists realized per query)
+    per_q = []
+    nseg_tot = sum(int(plan.n_seg[b]) for b in range(w.batch)) * w.n_kv_heads
+    for qi in range(Q):
+        B.route(ctx, cache, qd[qi], theta_d, ro, rws)
+        torch.cuda.synchronize()
+        cnt = ro.exp_count.cpu().numpy()
+        by = algorithmic_bytes(w, plan, cnt, ro.exp_list.cpu().numpy(), e)
+        by["frac"] = float(cnt.sum()) / max(1, nseg_tot)
+        per_q.append(by)
+    idx = [(args.warmup + i) % Q for i in range(args.steps)]
+    avg = {k: sum(per_q[i][k] for i in idx) / args.steps for k in per_q[0]}
+    pcie = avg["expand"] - w.batch * w.n_q_heads * w.head_dim * e      # the listed spans' factors and sigma, gate
+    kern_total_us = kern_us["route"] + kern_us["full"] + kern_us["expand"]
+    rec = {
+        "metric": "host-resident mixed-res decode steps/s (PCIe copy of the listed factors included)",
+        "value": 1e3 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "launch": "eager (host wait on the route list each step)",
+        "dtype": w.dtype, "data": "synthetic (seeded; Llama-3-8B layer shape)",
+        "config": {"workload": w.name, "batch": w.batch, "n_ctx": w.n_ctx, "rank_range": [w.rank_lo, w.rank_hi],
+                   "expand_frac_target": w.expand_frac, "expand_frac_realized": round(float(avg["frac"]), 4),
+                   "factors": "pinned host"},
+        "eff_ctx_tokens_per_s": 1e3 / ms * w.batch * w.n_ctx,
+        "pcie_factor_bytes_per_step": int(pcie),
+        "pcie_gbs_over_step": pcie / (ms * 1e-3) / 1e9,
+        "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "kernel_hbm_frac": avg["total"] / (kern_total_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        "kernel_time_fraction_of_step": kern_total_us / (ms * 1e3),
+        "algorithmic_bytes_per_step": int(avg["total"]),
+    }
+    print(json.dumps(rec), flush=True)
+    ctx.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +228,8 @@ def main():
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="timed pass: replay of captured HIP graphs (default) or eager launches")
     ap.add_argument("--graph-steps", type=int, default=8, help="decode steps captured per HIP graph")
+    ap.add_argument("--host-resident", action="store_true",
+                    help="only measure the host-resident workload (pinned host factors fetched per step) and print its own line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy three times (reference kernel for memory counters)")
     args = ap.parse_args()
@@ -146,6 +246,9 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.host_resident:
+        host_resident(args)
+        return
 
     import numpy as np
     import torch
