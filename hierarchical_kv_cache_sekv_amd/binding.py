@@ -24,8 +24,11 @@ EXPORTS = [
     "sekv_ctx_create", "sekv_ctx_destroy", "sekv_last_error", "sekv_capacities", "sekv_plan_spans",
     "sekv_build_spans", "sekv_route_workspace_bytes", "sekv_route", "sekv_reconstruct",
     "sekv_decode_workspace_bytes", "sekv_decode_host_workspace_bytes", "sekv_mixed_attention_decode",
-    "sekv_profile_enable", "sekv_profile_read",
+    "sekv_profile_enable", "sekv_profile_read", "sekv_ctx_set_split", "sekv_ctx_set_fetch_mode",
+    "sekv_ctx_inject_fault", "sekv_profile_read_host",
 ]
+SEKV_FETCH_STAGED, SEKV_FETCH_DIRECT = 0, 1
+SEKV_FAULT_NONE, SEKV_FAULT_GATHER = 0, 1
 
 
 class SekvError(RuntimeError):
@@ -74,8 +77,12 @@ def _load():
         "sekv_route_workspace_bytes": (sz, [C, S]),
         "sekv_route": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, sz, _p]),
         "sekv_reconstruct": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p]),
-        "sekv_decode_workspace_bytes": (sz, [C, S]),
-        "sekv_decode_host_workspace_bytes": (sz, [C, S]),
+        "sekv_decode_workspace_bytes": (sz, [_p, C, S]),
+        "sekv_decode_host_workspace_bytes": (sz, [_p, C, S]),
+        "sekv_ctx_set_split": (i32, [_p, i32]),
+        "sekv_ctx_set_fetch_mode": (i32, [_p, i32]),
+        "sekv_ctx_inject_fault": (i32, [_p, i32]),
+        "sekv_profile_read_host": (i32, [_p] + [ctypes.POINTER(ctypes.c_double)] * 3 + [ctypes.POINTER(i64)]),
         "sekv_mixed_attention_decode": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, sz, _p, sz, _p, _p]),
         "sekv_profile_enable": (i32, [_p, i32]),
         "sekv_profile_read": (i32, [_p] + [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)] * 3),
@@ -173,6 +180,27 @@ class Context:
         _check(LIB.sekv_profile_read(self.handle, ctypes.byref(ms[0]), ctypes.byref(n[0]), ctypes.byref(ms[1]),
                                      ctypes.byref(n[1]), ctypes.byref(ms[2]), ctypes.byref(n[2])))
         return {k: (ms[i].value, n[i].value) for i, k in enumerate(("route", "full", "expand"))}
+
+    def set_split(self, entries: int):
+        """Full-resolution entries per split-K chunk (0: the library chooses)."""
+        _check(LIB.sekv_ctx_set_split(self.handle, int(entries)))
+
+    def set_fetch_mode(self, mode: int):
+        _check(LIB.sekv_ctx_set_fetch_mode(self.handle, int(mode)))
+
+    def inject_fault(self, fault: int):
+        _check(LIB.sekv_ctx_inject_fault(self.handle, int(fault)))
+
+    def host_timing(self):
+        """Per-call microseconds of the staged host-resident decode's host
+        phases since the last read: wait for the list, gather, whole call."""
+        ms = [ctypes.c_double() for _ in range(3)]
+        n = ctypes.c_int64()
+        _check(LIB.sekv_profile_read_host(self.handle, ctypes.byref(ms[0]), ctypes.byref(ms[1]), ctypes.byref(ms[2]),
+                                          ctypes.byref(n)))
+        k = max(n.value, 1)
+        return {"calls": n.value, "wait_us": ms[0].value * 1e3 / k, "gather_us": ms[1].value * 1e3 / k,
+                "call_us": ms[2].value * 1e3 / k}
 
     def close(self):
         if self.handle:
@@ -289,9 +317,10 @@ class RouteOut:
 
 
 def route_workspace(cache: SpanCache, device="cuda"):
+    """Zero-filled route workspace (sekv_route leaves it zero after each call)."""
     torch = _torch()
     n = LIB.sekv_route_workspace_bytes(ctypes.byref(cache.cfg), ctypes.byref(cache.struct()))
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def route(ctx: Context, cache: SpanCache, q, theta, out: RouteOut, ws, stream=None, spans: Optional[Spans] = None):
@@ -317,11 +346,15 @@ def reconstruct(ctx: Context, cache: SpanCache, out: RouteOut, stream=None):
 
 
 class DecodeWorkspace:
-    def __init__(self, cache: SpanCache, device="cuda"):
+    """Device (and, for the staged host-resident fetch, pinned host) workspace
+    sized for ``ctx``'s split and fetch mode (ctx None: the defaults)."""
+
+    def __init__(self, cache: SpanCache, device="cuda", ctx: Optional["Context"] = None):
         torch = _torch()
         st = cache.struct()
-        nd = LIB.sekv_decode_workspace_bytes(ctypes.byref(cache.cfg), ctypes.byref(st))
-        nh = LIB.sekv_decode_host_workspace_bytes(ctypes.byref(cache.cfg), ctypes.byref(st))
+        h = ctx.handle if ctx is not None else None
+        nd = LIB.sekv_decode_workspace_bytes(h, ctypes.byref(cache.cfg), ctypes.byref(st))
+        nh = LIB.sekv_decode_host_workspace_bytes(h, ctypes.byref(cache.cfg), ctypes.byref(st))
         self.dev = torch.empty(max(nd, 256), dtype=torch.uint8, device=device)
         self.host = torch.empty(nh, dtype=torch.uint8, pin_memory=True) if nh > 0 else None
 

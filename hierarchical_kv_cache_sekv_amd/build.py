@@ -1,6 +1,9 @@
 """Build libsekv.so in-tree with hipcc for gfx950.
 
     python -m hierarchical_kv_cache_sekv_amd.build
+
+Each source is compiled to an object in its own hipcc process (in parallel),
+then the objects are linked into ``libsekv.so`` next to this file.
 """
 from __future__ import annotations
 
@@ -12,11 +15,12 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsekv.so")
-SOURCES = [os.path.join(HERE, "csrc", "sekv_kernels.hip"), os.path.join(HERE, "csrc", "sekv_host.cpp")]
+OBJ_DIR = os.path.join(ROOT, "_build")
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("sekv_kernels.hip", "sekv_host.cpp")]
 
 # gfx950 only.  Packed FP32 instructions are disabled for all device code.
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
@@ -31,14 +35,32 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *FLAGS, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+        objs.append(obj)
+    failed = False
+    for cmd, p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(out)
+            failed = True
+    if failed:
+        raise RuntimeError("libsekv build failed")
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-o", tmp, *SOURCES, "-lpthread"]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("libsekv build failed")
+        raise RuntimeError("libsekv link failed")
     os.replace(tmp, LIB)
     return LIB
 

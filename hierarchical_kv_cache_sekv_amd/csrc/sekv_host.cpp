@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <cstdio>
@@ -141,6 +142,13 @@ struct sekv_ctx {
   ThreadPool* pool = nullptr;
   bool profile = false;
   EventPairs prof_route, prof_attend, prof_expand;
+  int32_t split_entries = 0;      // full-resolution entries per split-K chunk (0: automatic)
+  int32_t fetch_mode = SEKV_FETCH_DIRECT;
+  int32_t fault = SEKV_FAULT_NONE;  // injected failure of the next host-resident decode
+  int route_resident[2][2][4] = {};   // route workgroups resident at once, by dtype, d == 128, log2 G (0: unknown)
+  // host phases of host-resident decode calls since the last read
+  double host_wait_ms = 0, host_gather_ms = 0, host_call_ms = 0;
+  int64_t host_calls = 0;
 };
 
 namespace {
@@ -220,6 +228,15 @@ int32_t seg_cap_of(const sekv_config* c) {
 }
 int32_t full_cap_of(const sekv_config* c) {
   return std::min<int64_t>(c->n_ctx, (int64_t)c->n_sink + seg_cap_of(c) + c->n_recent + 1);
+}
+
+const void* device_address(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return attr.devicePointer;
 }
 
 bool is_pinned_host(const void* p) {
@@ -679,37 +696,65 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
   return SEKV_OK;
 }
 
+// Route workspace: per group a ticket, then per group one status word per
+// 256-span tile (all uint32, zero between calls).
+static int32_t route_tiles_cap(const sekv_spans* s) { return std::max(1, (s->seg_cap + kRouteThreads - 1) / kRouteThreads); }
+
 size_t sekv_route_workspace_bytes(const sekv_config* c, const sekv_spans* s) {
   if (check_config(c) != SEKV_OK || !s) return 0;
-  return align_up((size_t)c->batch * c->n_kv_heads * (((size_t)s->seg_cap + 15) & ~(size_t)15));
+  const size_t BG = (size_t)c->batch * c->n_kv_heads;
+  return align_up(BG * (1 + (size_t)route_tiles_cap(s)) * sizeof(uint32_t));
 }
 
-sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q, const float* theta,
-                       int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+namespace {
+sekv_status route_checked(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q, const float* theta,
+                          int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count) {
   if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
   sekv_status st = check_config(c);
   if (st != SEKV_OK) return st;
   st = check_spans(c, s, false);
   if (st != SEKV_OK) return st;
-  if (!q || !theta || !exp_list || !exp_mask || !exp_count || !ws) return fail(SEKV_EINVAL, "sekv_route: a pointer argument is NULL");
-  if (ws_bytes < sekv_route_workspace_bytes(c, s))
-    return fail(SEKV_ECAPACITY, "route workspace %zu bytes < %zu needed", ws_bytes, sekv_route_workspace_bytes(c, s));
+  if (!q || !theta || !exp_list || !exp_mask || !exp_count) return fail(SEKV_EINVAL, "sekv_route: a pointer argument is NULL");
+  return SEKV_OK;
+}
+
+sekv_status route_launch(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q, const float* theta,
+                         int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count, void* ws, bool timed,
+                         hipStream_t stream) {
   RouteArgs a{};
   a.dtype = c->dtype;
   a.B = c->batch; a.Hq = c->n_q_heads; a.Hkv = c->n_kv_heads; a.D = c->head_dim; a.seg_cap = s->seg_cap;
   int mx = 0;
   for (int b = 0; b < c->batch; ++b) { a.n_seg[b] = s->n_seg_host[b]; mx = std::max(mx, s->n_seg_host[b]); }
   a.nblk = std::max(1, (mx + kRouteThreads - 1) / kRouteThreads);
-  a.mstride = (s->seg_cap + 15) & ~15;
+  a.nblk_cap = route_tiles_cap(s);
   a.q = q; a.theta = theta; a.rho = s->rho;
-  a.dmask = static_cast<uint8_t*>(ws);
+  const size_t BG = (size_t)c->batch * c->n_kv_heads;
+  a.ticket = static_cast<uint32_t*>(ws);
+  a.status = a.ticket + BG;
   a.exp_list = exp_list; a.exp_mask = exp_mask; a.exp_count = exp_count;
   HIP_OR_FAIL(hipSetDevice(ctx->device));
-  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_route, stream));
+  // tiles in dispatch order when the whole grid is resident at once, tickets otherwise
+  const int G = c->n_q_heads / c->n_kv_heads;
+  int& resident = ctx->route_resident[c->dtype == SEKV_BF16][c->head_dim == 128][G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3];
+  if (resident == 0) HIP_OR_FAIL(route_resident_blocks(a, ctx->device, &resident));
+  a.use_ticket = (int64_t)a.nblk * c->n_kv_heads * c->batch > resident ? 1 : 0;
+  if (timed) HIP_OR_FAIL(prof_mark(ctx, ctx->prof_route, stream));
   HIP_OR_FAIL(launch_route(a, stream));
-  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_route, stream));
+  if (timed) HIP_OR_FAIL(prof_mark(ctx, ctx->prof_route, stream));
   return SEKV_OK;
+}
+}  // namespace
+
+sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q, const float* theta,
+                       int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  sekv_status st = route_checked(ctx, c, s, q, theta, exp_list, exp_mask, exp_count);
+  if (st != SEKV_OK) return st;
+  if (!ws) return fail(SEKV_EINVAL, "sekv_route: ws is NULL");
+  if (ws_bytes < sekv_route_workspace_bytes(c, s))
+    return fail(SEKV_ECAPACITY, "route workspace %zu bytes < %zu needed", ws_bytes, sekv_route_workspace_bytes(c, s));
+  return route_launch(ctx, c, s, q, theta, exp_list, exp_mask, exp_count, ws, true, stream);
 }
 
 sekv_status sekv_reconstruct(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const int32_t* exp_list,
@@ -737,7 +782,7 @@ struct DecodePlan {
   size_t h_list = 0, h_count = 0, h_stage_off = 0, h_sg = 0, h_ring = 0, host_bytes = 0;
 };
 
-void make_plan(const sekv_config* c, const sekv_spans* s, DecodePlan& p) {
+void make_plan(const sekv_config* c, const sekv_spans* s, int32_t split_entries, bool staged, DecodePlan& p) {
   const int B = c->batch, Hkv = c->n_kv_heads, D = c->head_dim, G = c->n_q_heads / Hkv;
   const int BG = B * Hkv;
   AttendArgs& a = p.a;
@@ -753,10 +798,7 @@ void make_plan(const sekv_config* c, const sekv_spans* s, DecodePlan& p) {
   const int64_t target = 1024;
   int64_t tc = ((int64_t)BG * ntiles + target - 1) / target;
   tc = std::max<int64_t>(4, std::min<int64_t>(64, tc));
-  if (const char* env = std::getenv("SEKV_A4_CHUNK")) {  // split-size override in entries (invariance tests)
-    const int64_t v = std::atoll(env);
-    if (v > 0) tc = std::max<int64_t>(1, std::min<int64_t>(64, (v + 31) / 32));
-  }
+  if (split_entries > 0) tc = std::max<int64_t>(1, std::min<int64_t>(64, (split_entries + 31) / 32));
   a.tiles_a4 = (int)tc;
   a.nch_a4 = (ntiles + a.tiles_a4 - 1) / a.tiles_a4;
   a.P_max = a.nch_a4 + (s->seg_cap + kExpChunk - 1) / kExpChunk;
@@ -774,36 +816,40 @@ void make_plan(const sekv_config* c, const sekv_spans* s, DecodePlan& p) {
   size_t off = 0;
   p.off_ml = off; off = align_up(off + (size_t)BG * a.P_max * G * 2 * sizeof(float));
   p.off_o = off; off = align_up(off + (size_t)BG * a.P_max * G * D * sizeof(float));
-  if (c->factors_on_host) {
-    p.off_stage_off = off; off = align_up(off + (size_t)BG * s->seg_cap * 2 * sizeof(int64_t));
+  if (staged) {
+    p.off_stage_off = off; off = align_up(off + (size_t)BG * (2 * (size_t)s->seg_cap + 1) * sizeof(int64_t));
     p.off_stage_fac = off; off = align_up(off + (size_t)s->fac_elems * elem_size(c->dtype));
     p.off_stage_sg = off; off = align_up(off + (size_t)s->sg_elems * sizeof(float));
   }
   p.dev_bytes = off;
   size_t h = 0;
-  if (c->factors_on_host) {
+  if (staged) {
     p.h_count = h; h = align_up(h + (size_t)BG * sizeof(int32_t));
     p.h_list = h; h = align_up(h + (size_t)BG * s->seg_cap * sizeof(int32_t));
-    p.h_stage_off = h; h = align_up(h + (size_t)BG * s->seg_cap * 2 * sizeof(int64_t));
+    p.h_stage_off = h; h = align_up(h + (size_t)BG * (2 * (size_t)s->seg_cap + 1) * sizeof(int64_t));
     p.h_sg = h; h = align_up(h + (size_t)s->sg_elems * sizeof(float));
     p.h_ring = h; h = align_up(h + (size_t)kRing * kRingBytes);
   }
   p.host_bytes = h;
 }
 
+bool staged_fetch(const sekv_ctx* ctx, const sekv_config* c) {
+  return c->factors_on_host && ctx && ctx->fetch_mode == SEKV_FETCH_STAGED;
+}
+
 }  // namespace
 
-size_t sekv_decode_workspace_bytes(const sekv_config* c, const sekv_spans* s) {
+size_t sekv_decode_workspace_bytes(const sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s) {
   if (check_config(c) != SEKV_OK || !s) return 0;
   DecodePlan p;
-  make_plan(c, s, p);
+  make_plan(c, s, ctx ? ctx->split_entries : 0, staged_fetch(ctx, c), p);
   return p.dev_bytes;
 }
 
-size_t sekv_decode_host_workspace_bytes(const sekv_config* c, const sekv_spans* s) {
+size_t sekv_decode_host_workspace_bytes(const sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s) {
   if (check_config(c) != SEKV_OK || !s) return 0;
   DecodePlan p;
-  make_plan(c, s, p);
+  make_plan(c, s, ctx ? ctx->split_entries : 0, staged_fetch(ctx, c), p);
   return p.host_bytes;
 }
 
@@ -818,11 +864,12 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   if (st != SEKV_OK) return st;
   if (!q || !exp_list || !exp_mask || !exp_count || !out || !dev_ws)
     return fail(SEKV_EINVAL, "sekv_mixed_attention_decode: a pointer argument is NULL");
+  const bool staged = staged_fetch(ctx, c);
   DecodePlan p;
-  make_plan(c, s, p);
+  make_plan(c, s, ctx->split_entries, staged, p);
   if (dev_ws_bytes < p.dev_bytes) return fail(SEKV_ECAPACITY, "device workspace %zu bytes < %zu needed", dev_ws_bytes, p.dev_bytes);
   if (p.a.tiles_a4 * 32 > 2048) return fail(SEKV_ESHAPE, "internal chunk size too large");
-  if (c->factors_on_host) {
+  if (staged) {
     if (!host_ws) return fail(SEKV_EINVAL, "host-resident factors need a pinned host workspace");
     if (host_ws_bytes < p.host_bytes) return fail(SEKV_ECAPACITY, "host workspace %zu bytes < %zu needed", host_ws_bytes, p.host_bytes);
     if (!is_pinned_host(host_ws)) return fail(SEKV_EINVAL, "host workspace must be pinned (hipHostMalloc)");
@@ -838,8 +885,15 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   a.part_o = reinterpret_cast<float*>(dws + p.off_o);
   a.out = out;
   a.stage_off = nullptr;
+  if (c->factors_on_host && !staged) {
+    // direct fetch: the kernels read the listed spans' factor blocks from the
+    // pinned host pools over the bus, through the pools' device addresses
+    a.fac = device_address(s->fac);
+    a.sg = static_cast<const float*>(device_address(s->sg));
+    if (!a.fac || !a.sg) return fail(SEKV_EHIP, "pinned factor pools have no device address");
+  }
 
-  if (!c->factors_on_host) {
+  if (!staged) {
     if (a.max_rank <= 64) {
       // both passes in one launch on the caller's stream
       HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
@@ -867,6 +921,7 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   int64_t* h_soff = reinterpret_cast<int64_t*>(hws + p.h_stage_off);
   float* h_sg = reinterpret_cast<float*>(hws + p.h_sg);
   char* h_ring = hws + p.h_ring;
+  const auto t_call = std::chrono::steady_clock::now();
   // previous call's copies must be done before the pinned buffers are reused
   HIP_OR_FAIL(hipEventSynchronize(ctx->ev_copy));
   HIP_OR_FAIL(hipMemcpyAsync(h_count, exp_count, BG * sizeof(int32_t), hipMemcpyDeviceToHost, stream));
@@ -876,39 +931,51 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
   HIP_OR_FAIL(launch_attend_full(a, stream));
   HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+  const auto t_wait = std::chrono::steady_clock::now();
   HIP_OR_FAIL(hipEventSynchronize(ctx->ev_list));
+  const auto t_listed = std::chrono::steady_clock::now();
+  if (ctx->fault == SEKV_FAULT_GATHER) {
+    ctx->fault = SEKV_FAULT_NONE;
+    return fail(SEKV_EHIP, "factor gather failed (injected by sekv_ctx_inject_fault); out was not written");
+  }
 
-  // staging layout in list order
+  // staging layout in list order; the offset table is [BG] per-group bases
+  // (in list entries) followed by one (fac, sg) offset pair per listed entry
   struct Ent { const char* src; int64_t bytes; int64_t dst; };
   std::vector<Ent> ents;
-  int64_t fo = 0, go = 0;
+  int64_t fo = 0, go = 0, ne = 0;
   for (int g = 0; g < BG; ++g) {
     const int b = g / Hkv;
     const int cnt = h_count[g];
-    if (cnt < 0 || cnt > s->n_seg_host[b]) return fail(SEKV_EHIP, "route count %d for group %d is out of range", cnt, g);
+    if (cnt < 0 || cnt > s->n_seg_host[b])
+      return fail(SEKV_EHIP, "route count %d for group %d is out of range; out was not written", cnt, g);
+    h_soff[g] = ne;
     const int32_t* so = s->seg_off_host + (size_t)b * (cap + 1);
     for (int j = 0; j < cnt; ++j) {
       const int S = h_list[(size_t)g * cap + j];
-      if (S < 0 || S >= s->n_seg_host[b]) return fail(SEKV_EHIP, "route list entry %d out of range", S);
+      if (S < 0 || S >= s->n_seg_host[b])
+        return fail(SEKV_EHIP, "route list entry %d out of range; out was not written", S);
       const int L = so[S + 1] - so[S] - 1;
       const int r = s->rank_host[(size_t)b * cap + S];
       const int rp = (r + 7) & ~7;
       const int64_t fe = fac_block_elems(L, r, rp, D);
       const size_t o = (size_t)g * cap + S;
       ents.push_back({static_cast<const char*>(s->fac) + s->fac_off_host[o] * es, fe * es, fo});
-      h_soff[((size_t)g * cap + j) * 2] = fo;
-      h_soff[((size_t)g * cap + j) * 2 + 1] = go;
+      h_soff[BG + 2 * (ne + j)] = fo;
+      h_soff[BG + 2 * (ne + j) + 1] = go;
       std::memcpy(h_sg + go, s->sg + s->sg_off_host[o], sg_entry_elems(r) * sizeof(float));
       fo += fe;
       go += sg_entry_elems(r);
     }
+    ne += cnt;
   }
   char* d_stage_fac = dws + p.off_stage_fac;
-  HIP_OR_FAIL(hipMemcpyAsync(dws + p.off_stage_off, h_soff, (size_t)BG * cap * 2 * sizeof(int64_t), hipMemcpyHostToDevice, copy_stream));
+  HIP_OR_FAIL(hipMemcpyAsync(dws + p.off_stage_off, h_soff, (size_t)(BG + 2 * ne) * sizeof(int64_t), hipMemcpyHostToDevice, copy_stream));
   HIP_OR_FAIL(hipMemcpyAsync(dws + p.off_stage_sg, h_sg, (size_t)go * sizeof(float), hipMemcpyHostToDevice, copy_stream));
   // gather factor blocks into pinned ring buffers, copy each as it fills
   size_t e0 = 0;
   int slot = 0;
+  double gather_ms = 0;
   std::vector<int> used(kRing, 0);
   while (e0 < ents.size()) {
     size_t e1 = e0;
@@ -917,10 +984,12 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
     if (used[slot]) HIP_OR_FAIL(hipEventSynchronize(ctx->ev_ring[slot]));
     char* buf = h_ring + (size_t)slot * kRingBytes;
     const int64_t base = ents[e0].dst;
+    const auto t_g0 = std::chrono::steady_clock::now();
     ctx->pool->parallel_for((int64_t)(e1 - e0), [&](int64_t i) {
       const Ent& en = ents[e0 + i];
       std::memcpy(buf + (en.dst - base) * es, en.src, en.bytes);
     });
+    gather_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_g0).count();
     HIP_OR_FAIL(hipMemcpyAsync(d_stage_fac + base * es, buf, bytes, hipMemcpyHostToDevice, copy_stream));
     HIP_OR_FAIL(hipEventRecord(ctx->ev_ring[slot], copy_stream));
     used[slot] = 1;
@@ -937,6 +1006,43 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   HIP_OR_FAIL(launch_attend_expanded(a5, stream));
   HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, stream));
   HIP_OR_FAIL(launch_combine(a, stream));
+  const auto t_end = std::chrono::steady_clock::now();
+  ctx->host_wait_ms += std::chrono::duration<double, std::milli>(t_listed - t_wait).count();
+  ctx->host_gather_ms += gather_ms;
+  ctx->host_call_ms += std::chrono::duration<double, std::milli>(t_end - t_call).count();
+  ctx->host_calls += 1;
+  return SEKV_OK;
+}
+
+sekv_status sekv_ctx_set_split(sekv_ctx* ctx, int32_t entries) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  if (entries < 0 || entries > 2048) return fail(SEKV_EINVAL, "split of %d entries outside [0, 2048]", entries);
+  ctx->split_entries = entries;
+  return SEKV_OK;
+}
+
+sekv_status sekv_ctx_set_fetch_mode(sekv_ctx* ctx, int32_t mode) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  if (mode != SEKV_FETCH_STAGED && mode != SEKV_FETCH_DIRECT) return fail(SEKV_EINVAL, "fetch mode %d is not SEKV_FETCH_STAGED or SEKV_FETCH_DIRECT", mode);
+  ctx->fetch_mode = mode;
+  return SEKV_OK;
+}
+
+sekv_status sekv_ctx_inject_fault(sekv_ctx* ctx, int32_t fault) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  if (fault != SEKV_FAULT_NONE && fault != SEKV_FAULT_GATHER) return fail(SEKV_EINVAL, "fault %d is not SEKV_FAULT_NONE or SEKV_FAULT_GATHER", fault);
+  ctx->fault = fault;
+  return SEKV_OK;
+}
+
+sekv_status sekv_profile_read_host(sekv_ctx* ctx, double* wait_ms, double* gather_ms, double* call_ms, int64_t* calls) {
+  if (!ctx || !wait_ms || !gather_ms || !call_ms || !calls) return fail(SEKV_EINVAL, "sekv_profile_read_host: NULL argument");
+  *wait_ms = ctx->host_wait_ms;
+  *gather_ms = ctx->host_gather_ms;
+  *call_ms = ctx->host_call_ms;
+  *calls = ctx->host_calls;
+  ctx->host_wait_ms = ctx->host_gather_ms = ctx->host_call_ms = 0;
+  ctx->host_calls = 0;
   return SEKV_OK;
 }
 

@@ -11,7 +11,6 @@ constexpr int kMaxBatch = 64;        // per-sequence sizes travel in kernel argu
 constexpr int kMaxGroups = 256;      // batch * kv heads handled by one decode launch
 constexpr int kMaxSpan = 128;        // longest span body / highest rank the kernels hold
 constexpr int kRouteThreads = 256;   // spans per route workgroup (one lane per span)
-constexpr int kCompactThreads = 256; // threads of the compaction workgroup of one (b, kv)
 constexpr int kAttnThreads = 256;    // four waves per attention workgroup
 constexpr int kExpChunk = 8;         // expanded spans per work item of the expanded-span kernel
 constexpr int kExpThreads = 64;      // one wave per expanded-span workgroup
@@ -20,12 +19,14 @@ constexpr int kExpWaves = 2048;      // most waves (workgroups) of one expanded-
 struct RouteArgs {
   int dtype;                 // 0 f32, 1 bf16
   int B, Hq, Hkv, D, seg_cap, nblk;
-  int mstride;               // row stride of dmask: seg_cap rounded up to 16
+  int nblk_cap;              // status words per group: ceil(seg_cap / kRouteThreads)
+  int use_ticket;            // 1: tiles by per-group tickets (grid larger than the GPU holds at once)
   int n_seg[kMaxBatch];
   const void* q;             // [B][Hq][D]
   const float* theta;        // [B][Hq]
   const void* rho;           // [B][Hkv][seg_cap][D]
-  uint8_t* dmask;            // [B][Hkv][mstride] workspace
+  uint32_t* ticket;          // [B*Hkv] workspace, zero between calls
+  uint32_t* status;          // [B*Hkv][nblk_cap] workspace, zero between calls
   int32_t* exp_list;         // [B][Hkv][seg_cap]
   uint8_t* exp_mask;         // [B][Hkv][seg_cap]
   int32_t* exp_count;        // [B][Hkv]
@@ -50,7 +51,7 @@ struct AttendArgs {
   const int32_t* seg_off; const int32_t* rank;
   const int64_t* fac_off; const int64_t* sg_off;   // device pools (staged == nullptr)
   const void* fac; const float* sg;
-  const int64_t* stage_off;  // host-resident mode: [B*Hkv][seg_cap][2] (fac, sg) offsets per list entry
+  const int64_t* stage_off;  // staged host-resident mode: [B*Hkv] first entry of each group, then (fac, sg) offsets per listed entry
   const void* stage_fac; const float* stage_sg;
   const int32_t* exp_list; const uint8_t* exp_mask; const int32_t* exp_count;
   float* part_ml;            // [B*Hkv][P_max][G][2]
@@ -71,6 +72,8 @@ struct ReconArgs {
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// Route workgroups the device holds at once (occupancy x compute units).
+hipError_t route_resident_blocks(const RouteArgs& a, int device, int* blocks);
 hipError_t launch_attend_full(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s);

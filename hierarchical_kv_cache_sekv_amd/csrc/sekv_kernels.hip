@@ -8,10 +8,9 @@
 // span, on-demand token-level reconstruction).
 //
 // Kernels
-//   route_decide_kernel   one lane per span, the G heads of a KV group per
-//                   lane: canonical float32 score and decision bits.
-//   route_compact_kernel  one workgroup per (b, kv): ascending list, head
-//                   masks and count.
+//   route_kernel    one lane per span, the G heads of a KV group per lane:
+//                   canonical float32 score, decision bits, and the
+//                   ascending list, head masks and count of each (b, kv).
 //   attend_fused_kernel  both attention passes in one launch (every rank
 //                   <= 64): expanded-span waves first, then full-resolution
 //                   chunks.
@@ -27,6 +26,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
 
 #include "sekv_internal.h"
 
@@ -178,46 +178,93 @@ constexpr float kNegInf = -__builtin_inff();
 
 // ================================================================ route
 // Canonical score: z = 0; for i in 0..D-1: z = fl32(z + fl32(q_i * rho_i)).
-// Contraction into FMA is switched off for exactly these two operations, so
-// each product is rounded to float32 before it is added.
 //
-// Two kernels: route_decide_kernel (one lane per span, many workgroups) writes
-// the per-span head mask; route_compact_kernel (one workgroup per (b, kv))
-// turns it into the ascending list.  The kernel boundary makes the masks
-// visible across XCDs; no device-scope fence is needed inside either kernel
-// (a variant where the last workgroup of each (b, kv) compacts behind
-// agent-scope fences ran the route about five times slower).
+// One launch per call.  A workgroup scores 256 consecutive spans of one
+// (b, kv) (one lane per span, the G heads of the group per lane), compacts
+// its own expanded spans and writes them at their final list positions.  A
+// position needs the number of expanded spans in the group's earlier tiles:
+// every workgroup but the group's last publishes its own count in a status
+// word as soon as it has it, then takes the counts of all earlier tiles from
+// their status words (one lane per tile).  Only these counts cross
+// workgroups, through relaxed device-scope atomics, so no fence has to order
+// any other memory (a fenced variant, in which the last workgroup of a group
+// compacted masks written by the others, ran about five times slower).  A
+// workgroup only ever waits for tiles that come before its own, and those
+// publish without waiting:
+//   - when the whole grid fits on the GPU at once (the host checks the
+//     occupancy), tile = blockIdx.x: every earlier workgroup is resident or
+//     done, since workgroups are dispatched in index order;
+//   - otherwise a per-group ticket drawn at the start gives the tile, so the
+//     tiles waited for belong to workgroups that are already running (the
+//     ticket's atomic round trip costs about 5 us per call, hence the first
+//     form when it is safe).
+// Every wait therefore ends; it is also bounded, and a workgroup that gives up
+// reports exp_count = -1.
 //
-// route_decide_kernel: a workgroup takes 256 consecutive spans of one (b, kv).
-// Their routing keys are staged through LDS 128 bytes of each row at a time
-// (coalesced 16-byte loads, 8 lanes per row), padded to a 144-byte row stride
-// so that each lane then reads its own row without bank conflicts.
+// The workspace is all zero between calls, and each of its words is returned
+// to zero by operations on that word alone (so no ordering between different
+// words is assumed): the workgroup drawing a group's last ticket stores 0 to
+// the ticket; a status word holds (count + 1) in its low 16 bits, published
+// by a store, and in its high 16 bits the number of later tiles that have
+// read it, counted by their atomic adds once they see it published; the
+// reader that completes the count stores 0.
+//
+// A guarded fused multiply-add (exact when every bf16 product is a normal
+// float32) was tried for the score chain: the range checks and the extra
+// vote cost more than the multiplies saved (1.5 us slower per call).
+//
 constexpr int kRouteRowBytes = 128;
 constexpr int kRouteRowStride = 144;
+constexpr int kRouteSpinLimit = 1 << 20;
+
+__device__ __forceinline__ uint32_t atomic_add_dev(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_load_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Routing keys are staged through LDS 128 bytes of each row at a time
+// (coalesced 16-byte loads, 8 lanes per row), padded to a 144-byte row stride
+// so that each lane then reads its own row without bank conflicts; every
+// pass's loads are issued up front.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kRouteThreads) void route_decide_kernel(const RouteArgs a) {
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a) {
   constexpr int EPP = kRouteRowBytes / (int)sizeof(T);   // elements of a row per pass
   constexpr int NP = D / EPP;
   __shared__ float qs[G * D];
   __shared__ __align__(16) char tile[kRouteThreads * kRouteRowStride];
-  const int blk = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
+  __shared__ int s_ticket, s_prefix, s_fail;
+  __shared__ int s_wcnt[kRouteThreads / 64];
+  const int kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = b * a.Hkv + kv;
   const int ns = a.n_seg[b];
-  const int S0 = blk * kRouteThreads;
-  if (S0 >= ns) return;
-  const int nrow = min(kRouteThreads, ns - S0);
+  const int nb = (ns + kRouteThreads - 1) / kRouteThreads;
+  if (ns == 0) {
+    if (blockIdx.x == 0 && tid == 0) a.exp_count[g] = 0;
+    return;
+  }
+  if ((int)blockIdx.x >= nb) return;
+  if (tid == 0) s_ticket = a.use_ticket ? (int)atomic_add_dev(a.ticket + g, 1u) : (int)blockIdx.x;
   const T* q = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
   for (int i = tid; i < G * D; i += kRouteThreads) qs[i] = load1(q + i);
   float th[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) th[gi] = a.theta[(size_t)b * a.Hq + kv * G + gi];
+  __syncthreads();
+  const int vb = s_ticket;
+  if (a.use_ticket && tid == 0 && vb == nb - 1) atomic_store_dev(a.ticket + g, 0u);   // every ticket of this call is drawn
+  const int S0 = vb * kRouteThreads;
+  const int nrow = min(kRouteThreads, ns - S0);
   const char* rbase = static_cast<const char*>(a.rho) + ((size_t)g * a.seg_cap + S0) * D * sizeof(T);
 
   float z[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) z[gi] = 0.0f;
-  // every pass's loads are issued up front (one memory round trip per workgroup)
   uint4 v[NP][8];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
@@ -263,74 +310,64 @@ __global__ __launch_bounds__(kRouteThreads) void route_decide_kernel(const Route
       }
     }
   }
+  // this tile's expanded spans, their order within the tile, and the tile count
+  uint32_t bits = 0;
   if (tid < nrow) {
-    uint32_t bits = 0;
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) bits |= (z[gi] > th[gi] ? 1u : 0u) << gi;
-    a.dmask[(size_t)g * a.mstride + S0 + tid] = (uint8_t)bits;
   }
-}
-
-// Four bits, one per byte of w: set where the byte is nonzero.
-__device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t w) {
-  const uint32_t hi = ((((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u) >> 7;  // bits 0, 8, 16, 24
-  return ((hi * 0x00204081u) >> 21) & 0xFu;
-}
-__device__ __forceinline__ uint32_t nonzero_bytes16(const uint4& m) {
-  return nonzero_bytes4(m.x) | (nonzero_bytes4(m.y) << 4) | (nonzero_bytes4(m.z) << 8) | (nonzero_bytes4(m.w) << 12);
-}
-// One workgroup of kCompactThreads per (b, kv).  Each thread reads the masks
-// of 32 consecutive spans (two 16-byte loads), turns them into a 32-bit
-// "expanded" set, and one block-wide exclusive scan of the set sizes gives its
-// output position.
-__global__ __launch_bounds__(kCompactThreads) void route_compact_kernel(const RouteArgs a) {
-  __shared__ int wsum[kCompactThreads / 64];
-  const int kv = blockIdx.x, b = blockIdx.y;
-  const int g = b * a.Hkv + kv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ns = a.n_seg[b];
-  const uint8_t* dm = a.dmask + (size_t)g * a.mstride;
-  int32_t* lst = a.exp_list + (size_t)g * a.seg_cap;
-  uint8_t* msk = a.exp_mask + (size_t)g * a.seg_cap;
-  int base = 0;
-  for (int t0 = 0; t0 < ns; t0 += 32 * kCompactThreads) {
-    const int s0 = t0 + 32 * tid;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    const uint4 m0 = s0 < ns ? *reinterpret_cast<const uint4*>(dm + s0) : zero;
-    const uint4 m1 = s0 + 16 < ns ? *reinterpret_cast<const uint4*>(dm + s0 + 16) : zero;
-    uint32_t nz = nonzero_bytes16(m0) | (nonzero_bytes16(m1) << 16);
-    const int valid = ns - s0;
-    if (valid < 32) nz &= valid <= 0 ? 0u : ((1u << valid) - 1u);
-    const int c = __popc(nz);
-    int incl = c;
+  const uint64_t bal = __ballot(bits != 0);
+  const int wexcl = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) s_wcnt[wave] = __popcll(bal);
+  __syncthreads();
+  int woff = 0, cnt = 0;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off);
-      if (lane >= off) incl += t;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int wbase = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kCompactThreads / 64; ++w) {
-      const int v = wsum[w];
-      if (w < wave) wbase += v;
-      total += v;
-    }
-    int pos = base + wbase + incl - c;
-    const uint32_t words[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      if (nz & (1u << k)) {
-        lst[pos] = s0 + k;
-        msk[pos] = (uint8_t)(words[k >> 2] >> (8 * (k & 3)));
-        ++pos;
+  for (int w = 0; w < kRouteThreads / 64; ++w) {
+    const int c = s_wcnt[w];
+    if (w < wave) woff += c;
+    cnt += c;
+  }
+  uint32_t* status = a.status + (size_t)g * a.nblk_cap;
+  if (tid == 0 && vb < nb - 1) atomic_store_dev(status + vb, (uint32_t)cnt + 1u);   // count + 1 (0 = not yet)
+  if (wave == 0) {
+    int acc = 0, fail = 0;
+    for (int i = lane; i < vb; i += 64) {
+      uint32_t st = atomic_load_dev(status + i);
+      for (int spin = 0; (st & 0xFFFFu) == 0u; ++spin) {
+        if (spin == kRouteSpinLimit) break;
+        __builtin_amdgcn_s_sleep(2);
+        st = atomic_load_dev(status + i);
       }
+      if ((st & 0xFFFFu) == 0u) {
+        fail = 1;
+        continue;
+      }
+      const uint32_t old = atomic_add_dev(status + i, 1u << 16);   // this tile has read tile i
+      acc += (int)(old & 0xFFFFu) - 1;
+      if ((old >> 16) + 1u == (uint32_t)(nb - 1 - i)) atomic_store_dev(status + i, 0u);   // its last reader
     }
-    base += total;
-    __syncthreads();
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      acc += __shfl_xor(acc, off);
+      fail |= __shfl_xor(fail, off);
+    }
+    if (lane == 0) {
+      s_prefix = acc;
+      s_fail = fail;
+    }
   }
-  if (tid == 0) a.exp_count[g] = base;
+  __syncthreads();
+  const int prefix = s_prefix;
+  if (s_fail) {
+    if (tid == 0) a.exp_count[g] = -1;
+    return;
+  }
+  if (bits != 0) {
+    const int pos = prefix + woff + wexcl;
+    a.exp_list[(size_t)g * a.seg_cap + pos] = S0 + tid;
+    a.exp_mask[(size_t)g * a.seg_cap + pos] = (uint8_t)bits;
+  }
+  if (tid == 0 && vb == nb - 1) a.exp_count[g] = prefix + cnt;
 }
 
 // ================================================================ attention
@@ -873,7 +910,7 @@ __device__ __forceinline__ void role_expanded(const AttendArgs& a, int wid, int 
       im.bits = a.exp_mask[(size_t)g * a.seg_cap + jl];
       int64_t mfo, mgo;
       if (staged) {
-        const int64_t* st = a.stage_off + ((size_t)g * a.seg_cap + jl) * 2;
+        const int64_t* st = a.stage_off + BG + (a.stage_off[g] + jl) * 2;
         mfo = st[0];
         mgo = st[1];
       } else {
@@ -1123,8 +1160,13 @@ __device__ __forceinline__ void role_expanded(const AttendArgs& a, int wid, int 
 // arrive after the full-resolution pass starts) they are separate kernels.
 // Three waves per SIMD: with every slot taken by a wave at the start, the
 // expanded-span waves leave a third of the slots to full-resolution chunks.
+// Waves per SIMD the attention kernels ask for: three for bf16 caches (166
+// VGPRs); float32 operands take twice the registers, and a cap of three waves
+// would spill them, so float32 kernels take no cap.
+template <typename T> struct AttnOcc { static constexpr int kWaves = sizeof(T) == 2 ? 3 : 1; };
+
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(AttnOcc<T>::kWaves)))
 void attend_fused_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
   const int nx = a.n_fx_wg;
@@ -1136,13 +1178,14 @@ void attend_fused_kernel(const AttendArgs a) {
   }
 }
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(3))) void attend_full_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(AttnOcc<T>::kWaves)))
+void attend_full_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
   role_full_summary<T, D, G>(a, blockIdx.x, lds);
 }
 // Ranks up to 64 (four rank groups in registers): three waves per SIMD.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kExpThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kExpThreads) __attribute__((amdgpu_waves_per_eu(AttnOcc<T>::kWaves)))
 void attend_expanded_kernel(const AttendArgs a) {
   extern __shared__ __align__(16) char lds[];
   role_expanded<T, D, G, 4>(a, blockIdx.x, a.n_a5_wg, lds);
@@ -1343,11 +1386,22 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   dim3 grid(a.nblk, a.Hkv, a.B);
-  SEKV_DISPATCH(a.dtype, a.D, G, (route_decide_kernel<TT, DD, GG><<<grid, kRouteThreads, 0, s>>>(a)));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  route_compact_kernel<<<dim3(a.Hkv, a.B), kCompactThreads, 0, s>>>(a);
+  SEKV_DISPATCH(a.dtype, a.D, G, (route_kernel<TT, DD, GG><<<grid, kRouteThreads, 0, s>>>(a)));
   return hipGetLastError();
+}
+
+hipError_t route_resident_blocks(const RouteArgs& a, int device, int* blocks) {
+  const int G = a.Hq / a.Hkv;
+  int per_cu = 0;
+  hipError_t e = hipSuccess;
+  SEKV_DISPATCH(a.dtype, a.D, G,
+                (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, route_kernel<TT, DD, GG>, kRouteThreads, 0)));
+  if (e != hipSuccess) return e;
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return e;
+  *blocks = per_cu * cus;
+  return hipSuccess;
 }
 
 hipError_t launch_attend_full(const AttendArgs& a, hipStream_t s) {

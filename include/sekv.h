@@ -27,7 +27,11 @@
  *   - Errors: every call returns a sekv_status; sekv_last_error() returns a
  *     thread-local message for the last failing call of this thread.  All
  *     argument checks run on the host before anything is enqueued; a call that
- *     fails a check writes nothing.  No C++ exception crosses the ABI.
+ *     fails a check writes nothing.  The staged host-resident decode also
+ *     checks the route list after its one host wait: a failure found then (or
+ *     an injected gather fault) returns before anything writes `out`, but the
+ *     device workspace may already have been written.  No C++ exception
+ *     crosses the ABI.
  *   - Asynchrony: calls enqueue on the caller's stream and return, except
  *     sekv_plan_spans and sekv_build_spans (host-synchronous) and the
  *     host-resident decode (one documented host wait, see below).
@@ -56,6 +60,18 @@ typedef enum sekv_status {
 } sekv_status;
 
 typedef enum sekv_dtype { SEKV_F32 = 0, SEKV_BF16 = 1 } sekv_dtype;
+
+/* How host-resident factors reach the expanded-span pass (sekv_ctx_set_fetch_mode). */
+typedef enum sekv_fetch_mode {
+  SEKV_FETCH_STAGED = 0,  /* host threads gather the listed blocks into pinned staging,
+                             one copy per staging slot on the copy stream, after one
+                             host wait for the route list */
+  SEKV_FETCH_DIRECT = 1   /* (default) the kernels read the listed blocks from the
+                             pinned pools over the bus; no host wait, graph-capturable */
+} sekv_fetch_mode;
+
+/* Failures a test can force from the host (sekv_ctx_inject_fault). */
+typedef enum sekv_fault { SEKV_FAULT_NONE = 0, SEKV_FAULT_GATHER = 1 } sekv_fault;
 
 typedef struct sekv_config {
   int32_t batch, n_ctx, n_q_heads, n_kv_heads, head_dim;
@@ -184,7 +200,7 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* cfg, const void* 
                              const float* surprisal, const float* route_proj, const float* gate,
                              int32_t gate_stride, const sekv_spans* spans, hipStream_t stream);
 
-/* Device workspace of sekv_route, in bytes. */
+/* Device workspace of sekv_route, in bytes (0 for an invalid configuration). */
 size_t sekv_route_workspace_bytes(const sekv_config* cfg, const sekv_spans* spans);
 
 /*
@@ -199,8 +215,14 @@ size_t sekv_route_workspace_bytes(const sekv_config* cfg, const sekv_spans* span
  *   exp_list [B][Hkv][seg_cap] int32: ascending span indices that any head of
  *     the group expands (first exp_count entries valid).
  *   exp_mask [B][Hkv][seg_cap] uint8: bit g set iff head kv*G+g expands it.
- *   exp_count [B][Hkv] int32.  All device, written.
- *   ws: device workspace of sekv_route_workspace_bytes (contents ignored).
+ *   exp_count [B][Hkv] int32.  All device, written.  A count of -1 reports
+ *     that the call could not finish that group's list (an internal bounded
+ *     wait ran out; not expected in normal operation): the list is then
+ *     invalid and the workspace must be zero-filled again.
+ *   ws: device workspace of sekv_route_workspace_bytes.  It must be
+ *     zero-filled once before its first use; every call leaves it zero again.
+ *     Calls that may run concurrently need workspaces of their own.
+ * One kernel launch; every (b, kv) tile of 256 spans is one workgroup.
  * Errors: SEKV_EINVAL / SEKV_ESHAPE / SEKV_ECAPACITY / SEKV_EHIP.
  */
 sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans, const void* q,
@@ -223,9 +245,28 @@ sekv_status sekv_reconstruct(sekv_ctx* ctx, const sekv_config* cfg, const sekv_s
                              float* k_out, float* v_out, hipStream_t stream);
 
 /* Workspace sizes of sekv_mixed_attention_decode: device bytes, and pinned
- * host bytes (0 unless factors_on_host). */
-size_t sekv_decode_workspace_bytes(const sekv_config* cfg, const sekv_spans* spans);
-size_t sekv_decode_host_workspace_bytes(const sekv_config* cfg, const sekv_spans* spans);
+ * host bytes (0 unless factors_on_host with the staged fetch).  They depend on
+ * the context's split and fetch mode; ctx may be NULL (automatic split,
+ * direct fetch).  0 for an invalid configuration. */
+size_t sekv_decode_workspace_bytes(const sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans);
+size_t sekv_decode_host_workspace_bytes(const sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans);
+
+/* Full-resolution entries per split-K chunk of the decode (rounded up to a
+ * multiple of 32); 0 (the default) lets the library choose.  The result does
+ * not depend on the split beyond rounding (the log-sum-exp merge is exact in
+ * real arithmetic).  Errors: SEKV_EINVAL (NULL ctx, entries outside [0, 2048]). */
+sekv_status sekv_ctx_set_split(sekv_ctx* ctx, int32_t entries);
+
+/* Fetch mode of host-resident factors (sekv_fetch_mode), default DIRECT.
+ * [de-2], [de-3]: the factor tier lives in CPU memory and is loaded
+ * asynchronously on expansion.  Errors: SEKV_EINVAL. */
+sekv_status sekv_ctx_set_fetch_mode(sekv_ctx* ctx, int32_t mode);
+
+/* Test hook: with SEKV_FAULT_GATHER the next staged host-resident decode of
+ * this context fails its host gather after the one host wait: it returns
+ * SEKV_EHIP, does not write `out`, and the context stays usable.  The fault
+ * fires once.  Errors: SEKV_EINVAL. */
+sekv_status sekv_ctx_inject_fault(sekv_ctx* ctx, int32_t fault);
 
 /*
  * sekv_mixed_attention_decode - one decode step of mixed-resolution attention.
@@ -239,10 +280,12 @@ size_t sekv_decode_host_workspace_bytes(const sekv_config* cfg, const sekv_spans
  *   out [B][Hq][d] f32 device, written.
  *   dev_ws: device workspace (sekv_decode_workspace_bytes).
  *   host_ws: pinned host workspace (sekv_decode_host_workspace_bytes), only
- *     with factors_on_host.  In that mode the call copies the list to the host
- *     and waits for it (the one host wait), gathers the listed factor blocks on
- *     host threads into host_ws, and copies them with hipMemcpyAsync on
- *     copy_stream while the full-resolution/summary pass runs on stream.
+ *     with factors_on_host and the staged fetch.  In that mode the call copies
+ *     the list to the host and waits for it (the one host wait), gathers the
+ *     listed factor blocks on host threads into host_ws, and copies them with
+ *     hipMemcpyAsync on copy_stream while the full-resolution/summary pass
+ *     runs on stream.  With the direct fetch the kernels read the pinned
+ *     pools themselves; there is no host wait and host_ws is not used.
  *   copy_stream may be NULL (then stream is used).
  *   Device-resident factors: every kernel runs on stream, in order; no host
  *   wait (the call may be captured into a HIP graph).
@@ -268,6 +311,13 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* cfg, c
 sekv_status sekv_profile_enable(sekv_ctx* ctx, int32_t enable);
 sekv_status sekv_profile_read(sekv_ctx* ctx, double* route_ms, int64_t* route_launches, double* full_ms,
                               int64_t* full_launches, double* expand_ms, int64_t* expand_launches);
+
+/* Host-side phases of staged host-resident decode calls since the last read
+ * (always recorded): the host wait for the route list, the threaded gather of
+ * factor blocks into pinned staging, and the whole call, in milliseconds
+ * summed over `calls` calls; then reset.  Errors: SEKV_EINVAL. */
+sekv_status sekv_profile_read_host(sekv_ctx* ctx, double* wait_ms, double* gather_ms, double* call_ms,
+                                   int64_t* calls);
 
 #ifdef __cplusplus
 }

@@ -112,7 +112,7 @@ def realized_fraction(p: Prepared, si: int) -> float:
 class Device:
     """The oracle cache marshalled to the library (torch tensors on cuda:0)."""
 
-    def __init__(self, p: Prepared, factors_on_host=None):
+    def __init__(self, p: Prepared, factors_on_host=None, ctx=None):
         import torch
         from hierarchical_kv_cache_sekv_amd import binding as B
         self.B = B
@@ -126,7 +126,7 @@ class Device:
         self.theta = torch.from_numpy(p.theta).cuda()
         self.route_out = B.RouteOut(self.cfg, self.cache.seg_cap)
         self.route_ws = B.route_workspace(self.cache)
-        self.dec_ws = B.DecodeWorkspace(self.cache)
+        self.dec_ws = B.DecodeWorkspace(self.cache, ctx=ctx)
         self.out = torch.zeros((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
 
     def q(self, si):

@@ -6,12 +6,14 @@ ABI; the oracle works from the same seeded inputs.
 * Route: the oracle's segmentation, summaries and routing keys are computed
   for every (sequence, KV head) (no factors needed), its canonical float32
   scores give the thresholds and the expected expanded sets; the device's
-  count, list and head masks must match bit for bit for the whole batch.
-* Decode: sampled (sequence, KV head) groups get a full oracle cache (factors
-  included) and the oracle's mixed-resolution attention for the group's query
-  heads; the device output must be within the tolerance.
+  count, list and head masks must match bit for bit for the whole batch, on
+  every query step of the workload.
+* Decode: every (sequence, KV head) group gets an oracle cache (factors of
+  the spans the checked step expands) and the oracle's mixed-resolution
+  attention for the group's query heads; the device output must be within
+  the tolerance for every group.
 * Full expansion at full rank with unit gates is compared with the oracle's
-  dense attention on sampled heads.
+  dense attention for every head.
 
 The library's factors come from its own SVD, so they may differ from the
 oracle's in sign and in the last rounding bits; attention outputs do not
@@ -45,12 +47,13 @@ def ctx():
 class Full:
     """Library-built cache on the device plus the oracle's routing view."""
 
-    def __init__(self, ctx, w, *, n_steps=2, factors_on_host=False, full_rank=False):
+    def __init__(self, ctx, w, *, n_steps=None, factors_on_host=False, full_rank=False):
         import torch
         from hierarchical_kv_cache_sekv_amd import binding as B
         t0 = time.time()
         self.B, self.w = B, w
-        self.x = x = synth.make_inputs(w, n_steps=n_steps, full_rank_unit_gates=full_rank)
+        self.n_steps = w.steps if n_steps is None else n_steps
+        self.x = x = synth.make_inputs(w, n_steps=self.n_steps, full_rank_unit_gates=full_rank)
         log(f"{w.name}: inputs {time.time() - t0:.1f}s")
         self.cfg = B.make_config(w, factors_on_host)
         self.plan = B.plan_spans(self.cfg, x.surprisal, x.boundary_thr, x.rank_req)
@@ -75,17 +78,25 @@ class Full:
                 kbar, _ = O.span_summaries(x.k[b, kv], x.v[b, kv], x.surprisal[b], so)
                 rb.append(O.storage_round(O.routing_keys(kbar, x.route_proj[kv]), w.dtype))
             self.rho.append(rb)
+        self._z = {}
         log(f"{w.name}: oracle routing keys {time.time() - t0:.1f}s")
         self.route_out = B.RouteOut(self.cfg, self.cache.seg_cap)
         self.route_ws = B.route_workspace(self.cache)
-        self.dec_ws = B.DecodeWorkspace(self.cache)
         self.out = torch.zeros((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
-        self._slices = {}
+        self.dec_ws = None
 
     def scores(self, st, b):
-        G = self.w.group
-        return np.concatenate([O.route_scores(self.x.q[st, b, kv * G:(kv + 1) * G], self.rho[b][kv])
-                               for kv in range(self.w.n_kv_heads)])
+        """Canonical float32 scores [Hq][n_seg] of query step st, sequence b.
+        All steps of a sequence are scored in one call per KV head (each score
+        is its own sequential float32 chain, so batching rows changes no bit)."""
+        if b not in self._z:
+            w, G = self.w, self.w.group
+            z = np.empty((self.n_steps, w.n_q_heads, len(self.seg[b]) - 1), np.float32)
+            for kv in range(w.n_kv_heads):
+                qs = self.x.q[:self.n_steps, b, kv * G:(kv + 1) * G].reshape(-1, w.head_dim)
+                z[:, kv * G:(kv + 1) * G] = O.route_scores(qs, self.rho[b][kv]).reshape(self.n_steps, G, -1)
+            self._z[b] = z
+        return self._z[b][st]
 
     def thresholds(self, fracs, mode=None):
         w = self.w
@@ -94,26 +105,31 @@ class Full:
             if mode == "minus_inf":
                 th[b] = -np.inf
             else:
-                z = np.stack([self.scores(st, b) for st in range(self.x.q.shape[0])])
+                z = np.stack([self.scores(st, b) for st in range(self.n_steps)])
                 th[b] = synth.calibrate_theta(z, float(fracs[b]), w.group)
         return th
 
-    def run(self, ctx, st, theta):
-        """Device route + decode of query step st; returns (count, list, mask, out)."""
+    def decisions(self, st, theta):
+        return [self.scores(st, b) > theta[b][:, None] for b in range(self.w.batch)]
+
+    def _q(self, st):
         import torch
-        B = self.B
-        qd = torch.from_numpy(np.ascontiguousarray(self.x.q[st])).to(self.cache.elem).cuda()
-        td = torch.from_numpy(theta).cuda()
-        B.route(ctx, self.cache, qd, td, self.route_out, self.route_ws)
-        B.decode(ctx, self.cache, qd, self.route_out, self.out, self.dec_ws)
+        return torch.from_numpy(np.ascontiguousarray(self.x.q[st])).to(self.cache.elem).cuda()
+
+    def route(self, ctx, st, theta_d):
+        import torch
+        self.B.route(ctx, self.cache, self._q(st), theta_d, self.route_out, self.route_ws)
         torch.cuda.synchronize()
         return (self.route_out.exp_count.cpu().numpy(), self.route_out.exp_list.cpu().numpy(),
-                self.route_out.exp_mask.cpu().numpy(), self.out.cpu().numpy())
+                self.route_out.exp_mask.cpu().numpy())
 
-    def expected_route(self, st, theta):
-        w = self.w
-        dec = [self.scores(st, b) > theta[b][:, None] for b in range(w.batch)]
-        return dec
+    def decode(self, ctx, st, copy_stream=None):
+        import torch
+        if self.dec_ws is None:
+            self.dec_ws = self.B.DecodeWorkspace(self.cache, ctx=ctx)
+        self.B.decode(ctx, self.cache, self._q(st), self.route_out, self.out, self.dec_ws, copy_stream=copy_stream)
+        torch.cuda.synchronize()
+        return self.out.cpu().numpy()
 
     def check_route(self, dec, cnt, lst, msk):
         w = self.w
@@ -129,34 +145,59 @@ class Full:
                 exp += n
         return exp / max(tot, 1)
 
-    def oracle_slice(self, b, kv):
-        """Full oracle cache (factors included) of one (sequence, KV head)."""
-        if (b, kv) not in self._slices:
-            t0 = time.time()
-            x, w = self.x, self.w
-            self._slices[(b, kv)] = O.build_cache(
-                x.k[b:b + 1, kv:kv + 1], x.v[b:b + 1, kv:kv + 1], x.surprisal[b:b + 1], x.boundary_thr[b:b + 1],
-                x.route_proj[kv:kv + 1], x.rank_req[b:b + 1], x.gate[b:b + 1, kv:kv + 1],
-                n_sink=w.n_sink, n_recent=w.n_recent, lo=w.min_span, hi=w.max_span, dtype=w.dtype)
-            log(f"{w.name}: oracle slice ({b}, {kv}) {time.time() - t0:.1f}s")
-        return self._slices[(b, kv)]
+    def check_route_every_step(self, ctx, theta):
+        """Device route of every query step, bit-exact against the oracle."""
+        import torch
+        td = torch.from_numpy(theta).cuda()
+        fr = []
+        for st in range(self.n_steps):
+            cnt, lst, msk = self.route(ctx, st, td)
+            fr.append(self.check_route(self.decisions(st, theta), cnt, lst, msk))
+        return float(np.mean(fr))
 
-    def check_out(self, st, dec, out, groups):
-        w, G = self.w, self.w.group
+    def check_out(self, st, dec, out):
+        """Oracle mixed attention for EVERY (sequence, KV head) group."""
+        w, G, x = self.w, self.w.group, self.x
         worst = 0.0
-        for b, kv in groups:
-            cs = self.oracle_slice(b, kv)
-            hs = slice(kv * G, (kv + 1) * G)
-            ref = O.mixed_attention(cs, 0, self.x.q[st, b, hs], dec[b][hs], G)
-            err = float(np.abs(out[b, hs] - ref).max())
-            worst = max(worst, err)
-            assert err <= TOL[w.dtype], (b, kv, err)
+        for b in range(w.batch):
+            for kv in range(w.n_kv_heads):
+                hs = slice(kv * G, (kv + 1) * G)
+                need = np.nonzero(dec[b][hs].any(axis=0))[0]
+                cs = O.build_cache(
+                    x.k[b:b + 1, kv:kv + 1], x.v[b:b + 1, kv:kv + 1], x.surprisal[b:b + 1], x.boundary_thr[b:b + 1],
+                    x.route_proj[kv:kv + 1], x.rank_req[b:b + 1], x.gate[b:b + 1, kv:kv + 1],
+                    n_sink=w.n_sink, n_recent=w.n_recent, lo=w.min_span, hi=w.max_span, dtype=w.dtype,
+                    factor_spans={(0, 0): need})
+                ref = O.mixed_attention(cs, 0, x.q[st, b, hs], dec[b][hs], G)
+                err = float(np.abs(out[b, hs] - ref).max())
+                worst = max(worst, err)
+                assert err <= TOL[w.dtype], (b, kv, err)
         return worst
 
 
-def _sample_groups(w, n, seed):
-    rng = np.random.default_rng(seed)
-    return [(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(n)]
+def _run(ctx, f, theta, steps_out, copy_stream=None):
+    """Route of every step bit-exact; outputs of every group on steps_out."""
+    import torch
+    frac = f.check_route_every_step(ctx, theta)
+    td = torch.from_numpy(theta).cuda()
+    worst = 0.0
+    for st in steps_out:
+        cnt, lst, msk = f.route(ctx, st, td)
+        dec = f.decisions(st, theta)
+        f.check_route(dec, cnt, lst, msk)
+        out = f.decode(ctx, st, copy_stream=copy_stream)
+        worst = max(worst, f.check_out(st, dec, out))
+    return frac, worst
+
+
+def test_fullsize_t2k_tiny_every_step(ctx):
+    """The tiny float32 workload (2K context, 4 query heads on 1 KV head):
+    route on all 16 steps, outputs on every step."""
+    w = synth.workload(1)
+    f = Full(ctx, w)
+    th = f.thresholds([w.expand_frac] * w.batch)
+    frac, err = _run(ctx, f, th, range(w.steps))
+    log(f"{w.name}: route exact on {w.steps} steps (mean f={frac:.3f}), max err {err:.2e}")
 
 
 def test_fullsize_t32k_b1(ctx):
@@ -164,88 +205,81 @@ def test_fullsize_t32k_b1(ctx):
     w = synth.workload(2)
     f = Full(ctx, w)
     th = f.thresholds([0.10] * w.batch)
-    for st in range(2):
-        dec = f.expected_route(st, th)
-        cnt, lst, msk, out = f.run(ctx, st, th)
-        frac = f.check_route(dec, cnt, lst, msk)
-        err = f.check_out(st, dec, out, _sample_groups(w, 2, st))
-        log(f"{w.name} step {st}: route exact, realized f={frac:.3f}, max err {err:.2e}")
+    frac, err = _run(ctx, f, th, [0, 1, 63])
+    log(f"{w.name}: route exact on {w.steps} steps (mean f={frac:.3f}), all groups max err {err:.2e}")
 
 
 def test_fullsize_t32k_b8_ragged(ctx):
     """32K context, batch 8, per-sequence expansion fractions U(0, 30%): the
-    ragged split-K case."""
+    ragged split-K case, every one of the 64 groups checked."""
     w = synth.workload(4)
     f = Full(ctx, w)
     th = f.thresholds(f.x.expand_frac)
-    dec = f.expected_route(0, th)
-    cnt, lst, msk, out = f.run(ctx, 0, th)
-    frac = f.check_route(dec, cnt, lst, msk)
-    err = f.check_out(0, dec, out, _sample_groups(w, 3, 4))
-    log(f"{w.name}: route exact, realized f={frac:.3f}, max err {err:.2e}")
+    frac, err = _run(ctx, f, th, [0])
+    log(f"{w.name}: route exact on {w.steps} steps (mean f={frac:.3f}), all groups max err {err:.2e}")
 
 
-def test_fullsize_t128k_host_resident(ctx):
-    """128K context, batch 1, factors in pinned host memory fetched per step."""
+@pytest.mark.parametrize("mode", ["staged", "direct"])
+def test_fullsize_t128k_host_resident(ctx, mode):
+    """128K context, batch 1, factors in pinned host memory fetched per step:
+    staged (host gather + copy) and direct (kernels read the pinned pools)."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
     w = synth.workload(3, factors_on_host=True)
     f = Full(ctx, w, factors_on_host=True)
     th = f.thresholds([0.05] * w.batch)
-    dec = f.expected_route(0, th)
-    cnt, lst, msk, out = f.run(ctx, 0, th)
-    frac = f.check_route(dec, cnt, lst, msk)
-    err = f.check_out(0, dec, out, _sample_groups(w, 2, 3))
-    log(f"{w.name}: route exact, realized f={frac:.3f}, max err {err:.2e}")
+    try:
+        ctx.set_fetch_mode(B.SEKV_FETCH_STAGED if mode == "staged" else B.SEKV_FETCH_DIRECT)
+        frac, err = _run(ctx, f, th, [0, 31], copy_stream=torch.cuda.Stream() if mode == "staged" else None)
+    finally:
+        ctx.set_fetch_mode(B.SEKV_FETCH_DIRECT)
+    log(f"{w.name} ({mode}): route exact on {w.steps} steps (mean f={frac:.3f}), all groups max err {err:.2e}")
 
 
 def test_fullsize_t128k_b4_sweep(ctx):
     """The benchmark workload (128K, batch 4, ranks 16..64) at expansion
-    fractions 0, 5, 20 and 50%."""
+    fractions 0, 5, 20 and 50%: route on all 64 steps, every group's output."""
+    import torch
     w = synth.workload(5, factors_on_host=False)
     f = Full(ctx, w)
-    groups = _sample_groups(w, 2, 5)
     for frac_t in (0.0, 0.05, 0.20, 0.50):
         th = f.thresholds([frac_t] * w.batch)
-        dec = f.expected_route(1, th)
-        cnt, lst, msk, out = f.run(ctx, 1, th)
-        frac = f.check_route(dec, cnt, lst, msk)
-        err = f.check_out(1, dec, out, groups)
-        log(f"{w.name} f={frac_t}: route exact, realized f={frac:.3f}, max err {err:.2e}")
+        frac, err = _run(ctx, f, th, [1])
+        log(f"{w.name} f={frac_t}: route exact on {w.steps} steps (mean f={frac:.3f}), all groups max err {err:.2e}")
     # Back-to-back route calls on one workspace, alternating queries and
     # thresholds: every call's list, masks and counts stay bit-exact (the
-    # per-group arrival counters return to zero after each call).
-    import torch
+    # workspace's tickets and status words return to zero
+    # after each call).
     cases = []
     for frac_t in (0.05, 0.50):
         th = f.thresholds([frac_t] * w.batch)
         for st in (0, 1):
-            cases.append((torch.from_numpy(np.ascontiguousarray(f.x.q[st])).to(f.cache.elem).cuda(),
-                          torch.from_numpy(th).cuda(), f.expected_route(st, th)))
+            cases.append((st, torch.from_numpy(th).cuda(), f.decisions(st, th)))
     for rep in range(24):
-        qd, td, dec = cases[rep % len(cases)]
-        f.B.route(ctx, f.cache, qd, td, f.route_out, f.route_ws)
-        torch.cuda.synchronize()
-        f.check_route(dec, f.route_out.exp_count.cpu().numpy(), f.route_out.exp_list.cpu().numpy(),
-                      f.route_out.exp_mask.cpu().numpy())
-    log(f"{w.name}: 24 consecutive route calls bit-exact")
+        st, td, dec = cases[rep % len(cases)]
+        f.check_route(dec, *f.route(ctx, st, td))
+    assert int(f.route_ws.count_nonzero()) == 0
+    log(f"{w.name}: 24 consecutive route calls bit-exact, workspace zero after them")
 
 
 def test_fullsize_t128k_b4_full_expansion_equals_dense(ctx):
     """Every span expanded at full rank with unit gates (library build) equals
-    the oracle's dense attention over the stored K/V, on sampled heads."""
+    the oracle's dense attention over the stored K/V, for every head."""
+    import torch
     w = synth.workload(5, factors_on_host=False)
     f = Full(ctx, w, n_steps=1, full_rank=True)
     th = f.thresholds(None, mode="minus_inf")
-    cnt, lst, msk, out = f.run(ctx, 0, th)
+    cnt, lst, msk = f.route(ctx, 0, torch.from_numpy(th).cuda())
     for b in range(w.batch):
         n = len(f.seg[b]) - 1
         assert np.all(cnt[b] == n)
         assert np.all(lst[b, :, :n] == np.arange(n))
         assert np.all(msk[b, :, :n] == (1 << w.group) - 1)
+    out = f.decode(ctx, 0)
     worst = 0.0
-    for b, kv in _sample_groups(w, 3, 9):
-        hs = slice(kv * w.group, (kv + 1) * w.group)
-        ref = O.dense_attention(f.x.q[0, b, hs], f.x.k[b, kv:kv + 1], f.x.v[b, kv:kv + 1], w.group)
-        err = float(np.abs(out[b, hs] - ref).max())
+    for b in range(w.batch):
+        ref = O.dense_attention(f.x.q[0, b], f.x.k[b], f.x.v[b], w.group)
+        err = float(np.abs(out[b] - ref).max())
         worst = max(worst, err)
-        assert err <= TOL[w.dtype], (b, kv, err)
-    log(f"{w.name} full expansion: max err vs dense {worst:.2e}")
+        assert err <= TOL[w.dtype], (b, err)
+    log(f"{w.name} full expansion: max err vs dense over all heads {worst:.2e}")

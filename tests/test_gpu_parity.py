@@ -84,6 +84,86 @@ def test_route_and_decode_parity(ctx, name):
         assert torch.equal(out2, dev.out)        # deterministic
 
 
+def test_route_out_of_range_keys_stay_bit_exact(ctx):
+    """Routing keys with extreme magnitudes (tiny, a bf16 subnormal, huge) in
+    some spans: products that underflow to subnormals or carry large
+    exponents still follow the canonical separately rounded chain, so the
+    expanded set stays bit-exact."""
+    from _harness import scores
+    w = synth.workload(2, n_ctx=4096, batch=2)
+    p = prepare(w, [0, 1])
+    rng = np.random.default_rng(17)
+    c = p.cache
+    tiny = O.storage_round(2.0 ** -80 * 1.5, "bf16")
+    sub = float(np.array([1 << 16], np.uint32).view(np.float32)[0])     # smallest bf16 subnormal
+    huge = O.storage_round(2.0 ** 70 * 1.25, "bf16")
+    for b in range(w.batch):
+        n = c.n_seg(b)
+        for kv in range(w.n_kv_heads):
+            for S in rng.choice(n, 6, replace=False).tolist():
+                rho = c.rho[b][kv][S].copy()
+                rho[int(rng.integers(0, 64))] = tiny
+                rho[int(rng.integers(0, 64))] = sub
+                rho[64 + int(rng.integers(0, 64))] = huge * (1 if S % 2 else -1)
+                c.rho[b][kv][S] = rho
+    p.decisions = [[scores(c, p.x.q[st, b], b, w.group) > p.theta[b][:, None] for b in range(w.batch)]
+                   for st in p.steps]
+    dev = Device(p)
+    for si in range(len(p.steps)):
+        dev.route(ctx, si)
+        compare_route(dev, oracle_route(p, si))
+
+
+def test_route_ticket_order_on_a_grid_larger_than_the_gpu_holds(ctx):
+    """64 sequences x 4 KV heads x >= 5 tiles of 256 spans: more route
+    workgroups than the GPU holds at once, so tiles are taken by per-group
+    tickets.  Route only (the cache holds the oracle's routing keys); every
+    list bit-exact on two consecutive calls, workspace zero afterwards."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    w = synth.workload(1, batch=64, n_q_heads=8, n_kv_heads=4, head_dim=64, dtype="bf16", n_ctx=4096,
+                       min_span=1, max_span=8, boundary_quantile=0.5, rank_lo=1, rank_hi=4)
+    x = synth.make_inputs(w, n_steps=2)
+    cfg = B.make_config(w)
+    segs = [O.segment(x.surprisal[b], float(x.boundary_thr[b]), w.n_sink, w.n_recent, w.min_span, w.max_span)
+            for b in range(w.batch)]
+    plan = B.layout_from_segments(cfg, segs, [np.ones(len(so) - 1, np.int32) for so in segs])
+    cache = B.SpanCache(cfg, plan)
+    nblk = -(-max(len(so) - 1 for so in segs) // 256)
+    assert nblk * w.n_kv_heads * w.batch >= 1280          # more than 4 workgroups per compute unit
+    rho = np.zeros((w.batch, w.n_kv_heads, cache.seg_cap, w.head_dim), np.float32)
+    G = w.group
+    theta = np.empty((w.batch, w.n_q_heads), np.float32)
+    z = {}
+    for b in range(w.batch):
+        for kv in range(w.n_kv_heads):
+            kbar, _ = O.span_summaries(x.k[b, kv], x.v[b, kv], x.surprisal[b], segs[b])
+            r = O.storage_round(O.routing_keys(kbar, x.route_proj[kv]), w.dtype)
+            rho[b, kv, :len(r)] = r
+            for st in range(2):
+                z[(st, b, kv)] = O.route_scores(x.q[st, b, kv * G:(kv + 1) * G], r)
+        zb = np.stack([np.concatenate([z[(st, b, kv)] for kv in range(w.n_kv_heads)]) for st in range(2)])
+        theta[b] = synth.calibrate_theta(zb, 0.15, G)
+    cache.rho.copy_(torch.from_numpy(rho).to(cache.elem))
+    td = torch.from_numpy(theta).cuda()
+    ro = B.RouteOut(cfg, cache.seg_cap)
+    ws = B.route_workspace(cache)
+    for st in range(2):
+        B.route(ctx, cache, torch.from_numpy(np.ascontiguousarray(x.q[st])).to(cache.elem).cuda(), td, ro, ws)
+        torch.cuda.synchronize()
+        cnt, lst, msk = ro.exp_count.cpu().numpy(), ro.exp_list.cpu().numpy(), ro.exp_mask.cpu().numpy()
+        for b in range(w.batch):
+            dec = np.concatenate([z[(st, b, kv)] for kv in range(w.n_kv_heads)]) > theta[b][:, None]
+            lists, masks = O.compact(dec, G)
+            for kv in range(w.n_kv_heads):
+                n = len(lists[kv])
+                assert cnt[b, kv] == n
+                assert lst[b, kv, :n].tolist() == lists[kv].tolist()
+                assert msk[b, kv, :n].tolist() == masks[kv].tolist()
+    assert int(ws.count_nonzero()) == 0
+    log(f"ticket-ordered route: {nblk * w.n_kv_heads * w.batch} workgroups, lists bit-exact")
+
+
 @pytest.mark.parametrize("mode", ["plus_inf", "minus_inf"])
 def test_infinite_thresholds(ctx, mode):
     import torch
@@ -131,22 +211,29 @@ def test_full_expansion_full_rank_equals_dense(ctx, dtype):
 
 
 def test_host_resident_factors_match_device_resident_bitwise(ctx):
+    """Staged fetch (host gather + copy): same factor bits as the
+    device-resident path, so the same output bits."""
     import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
     w = synth.workload(3, n_ctx=8192)
     p = prepare(w, [0, 1])
     dev_d = Device(p, factors_on_host=False)
-    dev_h = Device(p, factors_on_host=True)
     side = torch.cuda.Stream()
-    for si in range(2):
-        dev_d.route(ctx, si)
-        dev_d.decode(ctx, si)
-        dev_h.route(ctx, si)
-        dev_h.decode(ctx, si, copy_stream=side)
-        torch.cuda.synchronize()
-        assert torch.equal(dev_d.out, dev_h.out)
-        want = oracle_out(p, si)
-        out = dev_h.out.cpu().numpy()
-        assert max(float(np.abs(out[b] - want[b]).max()) for b in want) <= TOL[w.dtype]
+    try:
+        ctx.set_fetch_mode(B.SEKV_FETCH_STAGED)
+        dev_h = Device(p, factors_on_host=True, ctx=ctx)
+        for si in range(2):
+            dev_d.route(ctx, si)
+            dev_d.decode(ctx, si)
+            dev_h.route(ctx, si)
+            dev_h.decode(ctx, si, copy_stream=side)
+            torch.cuda.synchronize()
+            assert torch.equal(dev_d.out, dev_h.out)
+            want = oracle_out(p, si)
+            out = dev_h.out.cpu().numpy()
+            assert max(float(np.abs(out[b] - want[b]).max()) for b in want) <= TOL[w.dtype]
+    finally:
+        ctx.set_fetch_mode(B.SEKV_FETCH_DIRECT)
 
 
 def test_reconstruct_matches_oracle(ctx):
@@ -179,7 +266,7 @@ def test_reconstruct_matches_oracle(ctx):
     assert worst <= 1e-4
 
 
-def test_split_invariance(ctx, monkeypatch):
+def test_split_invariance(ctx):
     """The result does not depend on how the memory is cut into split-K chunks,
     up to rounding: with a bfloat16 cache the softmax weights enter the P.V
     matrix-core product rounded to bfloat16 (relative 2^-9) after subtracting a
@@ -189,15 +276,74 @@ def test_split_invariance(ctx, monkeypatch):
     import torch
     p = _prep("bf16-ragged-B3-T4K")
     outs = []
-    for chunk in ("128", "512", "2048"):
-        monkeypatch.setenv("SEKV_A4_CHUNK", chunk)
-        dev = Device(p)
-        dev.route(ctx, 0)
-        dev.decode(ctx, 0)
-        torch.cuda.synchronize()
-        outs.append(dev.out.cpu().numpy())
+    try:
+        for chunk in (128, 512, 2048):
+            ctx.set_split(chunk)
+            dev = Device(p, ctx=ctx)
+            dev.route(ctx, 0)
+            dev.decode(ctx, 0)
+            torch.cuda.synchronize()
+            outs.append(dev.out.cpu().numpy())
+    finally:
+        ctx.set_split(0)
     for o in outs[1:]:
         assert np.abs(o - outs[0]).max() <= 2e-3
+
+
+def test_host_resident_direct_fetch_matches_device_resident_bitwise(ctx):
+    """Direct fetch: the kernels read the pinned host pools over the bus.  Same
+    kernels and same factor bits as the device-resident path, so the same
+    output bits; graph capture needs no host wait in this mode."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    w = synth.workload(3, n_ctx=8192)
+    p = prepare(w, [0, 1])
+    dev_d = Device(p, factors_on_host=False)
+    try:
+        ctx.set_fetch_mode(B.SEKV_FETCH_DIRECT)      # the default
+        dev_h = Device(p, factors_on_host=True, ctx=ctx)
+        assert dev_h.dec_ws.host is None
+        for si in range(2):
+            dev_d.route(ctx, si)
+            dev_d.decode(ctx, si)
+            dev_h.route(ctx, si)
+            dev_h.decode(ctx, si)
+            torch.cuda.synchronize()
+            assert torch.equal(dev_d.out, dev_h.out)
+    finally:
+        ctx.set_fetch_mode(B.SEKV_FETCH_DIRECT)
+
+
+def test_injected_gather_fault_leaves_out_untouched_and_context_usable(ctx):
+    """A forced failure of the staged host gather (set from the host, after the
+    one host wait) returns SEKV_EHIP without writing `out`; the next call on
+    the same context and workspace gives the normal result."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    w = synth.workload(3, n_ctx=8192)
+    p = prepare(w, [0])
+    dev_d = Device(p, factors_on_host=False)
+    dev_d.route(ctx, 0)
+    dev_d.decode(ctx, 0)
+    side = torch.cuda.Stream()
+    try:
+        ctx.set_fetch_mode(B.SEKV_FETCH_STAGED)
+        dev_h = Device(p, factors_on_host=True, ctx=ctx)
+        dev_h.route(ctx, 0)
+        sentinel = torch.full_like(dev_h.out, -7.0)
+        dev_h.out.copy_(sentinel)
+        torch.cuda.synchronize()
+        ctx.inject_fault(B.SEKV_FAULT_GATHER)
+        with pytest.raises(B.SekvError) as ei:
+            dev_h.decode(ctx, 0, copy_stream=side)
+        assert ei.value.status == B.SEKV_EHIP and "injected" in str(ei.value)
+        torch.cuda.synchronize()
+        assert torch.equal(dev_h.out, sentinel)
+        dev_h.decode(ctx, 0, copy_stream=side)
+        torch.cuda.synchronize()
+        assert torch.equal(dev_h.out, dev_d.out)
+    finally:
+        ctx.set_fetch_mode(B.SEKV_FETCH_DIRECT)
 
 
 def test_library_build_matches_oracle_build(ctx):
