@@ -229,13 +229,18 @@ class OracleCache:
         return (so[1:] - so[:-1] - 1).astype(np.int64)
 
 
-def build_cache(k, v, s, thr, P, rank_req, gate, *, n_sink, n_recent, lo, hi, dtype) -> OracleCache:
+def build_cache(k, v, s, thr, P, rank_req, gate, *, n_sink, n_recent, lo, hi, dtype,
+                factor_spans=None) -> OracleCache:
     """Build the mixed-resolution cache from stored K/V [B][Hkv][T][d], surprisal
     [B][T], boundary thresholds [B], projections [Hkv][d][d], requested ranks
     [B][>=n_seg] and gates [B][Hkv][>=n_seg][>=r].
 
     Reading: rank r_S = min(requested, L_S, 2d), shared by the span's KV heads;
     gates are applied at decode, not folded into the factors.
+
+    ``factor_spans`` (optional): {(b, kv head): span indices}; only those spans
+    get factors (the others hold None and must not be expanded).  This skips
+    work only; every value computed is the same.
     """
     B, Hkv, T, d = k.shape
     seg_offs, full_idx, fk, fv, sk, sv, rh, ranks, Us, sigs, gts, Vhs = ([] for _ in range(12))
@@ -259,7 +264,11 @@ def build_cache(k, v, s, thr, P, rank_req, gate, *, n_sink, n_recent, lo, hi, dt
             sv_b.append(storage_round(vbar, dtype))
             rh_b.append(storage_round(routing_keys(kbar, P[h]), dtype))
             Uh, sgh, gh, Vhh = [], [], [], []
+            want = None if factor_spans is None else set(int(i) for i in factor_spans.get((b, h), ()))
             for i in range(n_seg):
+                if want is not None and i not in want:
+                    Uh.append(None); sgh.append(None); gh.append(None); Vhh.append(None)
+                    continue
                 lo_t, hi_t = int(so[i]) + 1, int(so[i + 1])
                 Ui, si, Vi = span_factors(kk[lo_t:hi_t], vv[lo_t:hi_t], int(r[i]))
                 Uh.append(storage_round(Ui, dtype))
