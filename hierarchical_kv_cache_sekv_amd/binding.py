@@ -25,7 +25,7 @@ EXPORTS = [
     "sekv_build_spans", "sekv_route_workspace_bytes", "sekv_route", "sekv_reconstruct",
     "sekv_decode_workspace_bytes", "sekv_decode_host_workspace_bytes", "sekv_mixed_attention_decode",
     "sekv_profile_enable", "sekv_profile_read", "sekv_ctx_set_split", "sekv_ctx_set_fetch_mode",
-    "sekv_ctx_inject_fault", "sekv_profile_read_host",
+    "sekv_ctx_inject_fault", "sekv_profile_read_host", "sekv_route_noalloc",
 ]
 SEKV_FETCH_STAGED, SEKV_FETCH_DIRECT = 0, 1
 SEKV_FAULT_NONE, SEKV_FAULT_GATHER = 0, 1
@@ -76,6 +76,7 @@ def _load():
         "sekv_build_spans": (i32, [_p, C, _p, _p, _p, _p, _p, i32, S, _p]),
         "sekv_route_workspace_bytes": (sz, [C, S]),
         "sekv_route": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, sz, _p]),
+        "sekv_route_noalloc": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p]),
         "sekv_reconstruct": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p]),
         "sekv_decode_workspace_bytes": (sz, [_p, C, S]),
         "sekv_decode_host_workspace_bytes": (sz, [_p, C, S]),
@@ -329,6 +330,16 @@ def route(ctx: Context, cache: SpanCache, q, theta, out: RouteOut, ws, stream=No
     _check(LIB.sekv_route(ctx.handle, ctypes.byref(cache.cfg), ctypes.byref(st), _ptr(q), _ptr(theta),
                           _ptr(out.exp_list), _ptr(out.exp_mask), _ptr(out.exp_count), _ptr(ws),
                           ws.numel(), _stream_handle(stream)))
+
+
+def route_noalloc(ctx: Context, cache: SpanCache, q, theta, out: RouteOut, stream=None,
+                  spans: Optional[Spans] = None):
+    """sekv_route_noalloc: like route(), with the library's static route state
+    instead of a workspace (nothing is allocated by the call)."""
+    st = spans if spans is not None else cache.struct()
+    _check(LIB.sekv_route_noalloc(ctx.handle, ctypes.byref(cache.cfg), ctypes.byref(st), _ptr(q), _ptr(theta),
+                                  _ptr(out.exp_list), _ptr(out.exp_mask), _ptr(out.exp_count),
+                                  _stream_handle(stream)))
 
 
 def reconstruct(ctx: Context, cache: SpanCache, out: RouteOut, stream=None):

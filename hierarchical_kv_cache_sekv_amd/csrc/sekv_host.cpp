@@ -145,6 +145,7 @@ struct sekv_ctx {
   int32_t split_entries = 0;      // full-resolution entries per split-K chunk (0: automatic)
   int32_t fetch_mode = SEKV_FETCH_DIRECT;
   int32_t fault = SEKV_FAULT_NONE;  // injected failure of the next host-resident decode
+  void* route_scratch = nullptr;      // this device's static route state (sekv_route_noalloc)
   int route_resident[2][2][4] = {};   // route workgroups resident at once, by dtype, d == 128, log2 G (0: unknown)
   // host phases of host-resident decode calls since the last read
   double host_wait_ms = 0, host_gather_ms = 0, host_call_ms = 0;
@@ -406,6 +407,11 @@ sekv_status sekv_ctx_create(int device, sekv_ctx** out) {
   if (e != hipSuccess) {
     sekv_ctx_destroy(c);
     return fail(SEKV_EHIP, "context setup failed: %s", hipGetErrorString(e));
+  }
+  e = route_scratch_address(device, &c->route_scratch);
+  if (e != hipSuccess) {
+    sekv_ctx_destroy(c);
+    return fail(SEKV_EHIP, "route scratch setup failed: %s", hipGetErrorString(e));
   }
   c->pool = new ThreadPool(default_threads() - 1);
   *out = c;
@@ -755,6 +761,19 @@ sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s,
   if (ws_bytes < sekv_route_workspace_bytes(c, s))
     return fail(SEKV_ECAPACITY, "route workspace %zu bytes < %zu needed", ws_bytes, sekv_route_workspace_bytes(c, s));
   return route_launch(ctx, c, s, q, theta, exp_list, exp_mask, exp_count, ws, true, stream);
+}
+
+sekv_status sekv_route_noalloc(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q,
+                               const float* theta, int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count,
+                               hipStream_t stream) {
+  sekv_status st = route_checked(ctx, c, s, q, theta, exp_list, exp_mask, exp_count);
+  if (st != SEKV_OK) return st;
+  const size_t need = sekv_route_workspace_bytes(c, s);
+  if (need > kRouteScratchBytes)
+    return fail(SEKV_ECAPACITY, "route state of %zu bytes exceeds the %zu-byte static scratch of sekv_route_noalloc",
+                need, kRouteScratchBytes);
+  if (!ctx->route_scratch) return fail(SEKV_EHIP, "the context has no route scratch address");
+  return route_launch(ctx, c, s, q, theta, exp_list, exp_mask, exp_count, ctx->route_scratch, false, stream);
 }
 
 sekv_status sekv_reconstruct(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const int32_t* exp_list,

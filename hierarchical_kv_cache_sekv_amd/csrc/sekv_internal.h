@@ -15,6 +15,8 @@ constexpr int kAttnThreads = 256;    // four waves per attention workgroup
 constexpr int kExpChunk = 8;         // expanded spans per work item of the expanded-span kernel
 constexpr int kExpThreads = 64;      // one wave per expanded-span workgroup
 constexpr int kExpWaves = 2048;      // most waves (workgroups) of one expanded-span launch
+constexpr int kMaxDevices = 64;      // devices with a route scratch address
+constexpr size_t kRouteScratchBytes = size_t(1) << 20;  // static route state of sekv_route_noalloc
 
 struct RouteArgs {
   int dtype;                 // 0 f32, 1 bf16
@@ -74,6 +76,9 @@ struct ReconArgs {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // Route workgroups the device holds at once (occupancy x compute units).
 hipError_t route_resident_blocks(const RouteArgs& a, int device, int* blocks);
+// Device address of the static route state on `device` (must be current);
+// taken and zero-filled on the first call per device.
+hipError_t route_scratch_address(int device, void** ptr);
 hipError_t launch_attend_full(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s);

@@ -27,6 +27,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 
 #include "sekv_internal.h"
 
@@ -1381,7 +1382,35 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
     }                                                                       \
   } while (0)
 
+// ---------------------------------------------------------------- route scratch
+// State of sekv_route_noalloc: the route workspace (tickets and status words)
+// held in a file-scope device array.  Every GPU the library runs on holds its
+// own copy until the process ends, and every call on that GPU shares it.  In
+// host code the array's name is only a stand-in: its device address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) uint32_t scratch[kRouteScratchBytes / sizeof(uint32_t)];
+
 }  // namespace
+
+hipError_t route_scratch_address(int device, void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // the route state must start at zero; every route call leaves it zero
+    e = hipMemset(p, 0, kRouteScratchBytes);
+    if (e != hipSuccess) return e;
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return e;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;

@@ -230,6 +230,23 @@ sekv_status sekv_route(sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* 
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * sekv_route_noalloc - sekv_route for callers that cannot allocate memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors as sekv_route, without the
+ * workspace: the route state lives in a static device array of 1 MiB that the
+ * library holds on each GPU it runs on until the process ends (created and
+ * zero-filled once per device by sekv_ctx_create; every call leaves it zero).
+ * Configurations whose route state (sekv_route_workspace_bytes) exceeds
+ * 1 MiB are rejected with SEKV_ECAPACITY.  The call allocates nothing and
+ * records no timing events.  All calls on one GPU share the array: calls that
+ * may overlap on one GPU (other streams, other threads, other contexts) race
+ * and must be serialized by the caller.
+ */
+sekv_status sekv_route_noalloc(sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans, const void* q,
+                               const float* theta, int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count,
+                               hipStream_t stream);
+
+/*
  * sekv_reconstruct - token-level K/V of listed spans (standalone, for checks
  * and unfused use).  [de-3], [zh-3]: selected spans are rebuilt at token level;
  * K_hat = U diag(sigma*gate) Vh_K, V_hat = U diag(sigma*gate) W_V^T.
