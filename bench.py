@@ -446,6 +446,84 @@ def measure_device(w, x, fracs, args, label, full_rank=False):
     return recs
 
 
+# ------------------------------------------------------------------ dense baseline
+def measure_dense(w, x, args, label):
+    """Dense flash-decode over all T cached tokens (the full-KV decode SeKV is
+    compared with), timed like the mixed path: graph replays of the timed
+    steps, per-kernel events in an eager pass, >= 1 GiB of rotated K/V copies."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+
+    e = 2 if w.dtype == "bf16" else 4
+    Q = min(args.queries, x.q.shape[0])
+    ctx = B.Context(0)
+    cfg = B.make_config(w, False)
+    et = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    k0 = torch.from_numpy(x.k).to(et).cuda()
+    v0 = B.tile_values_device(torch.from_numpy(x.v).to(et).cuda())
+    kv_bytes = k0.numel() * e + v0.numel() * e
+    ncopy = args.copies or max(2, math.ceil((1 << 30) / kv_bytes))
+    ks = [k0] + [k0.clone() for _ in range(ncopy - 1)]
+    vs = [v0] + [v0.clone() for _ in range(ncopy - 1)]
+    qd = torch.from_numpy(x.q[:Q]).to(et).cuda().contiguous()
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    ws = B.dense_workspace(ctx, cfg)
+    stream = torch.cuda.Stream()
+    period = math.lcm(ncopy, Q)
+
+    def step(i):
+        c = i % ncopy
+        B.dense_decode(ctx, cfg, ks[c], vs[c], qd[i % Q], out, ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        ctx.profile(True)
+        for i in range(args.steps):
+            step(args.warmup + i)
+    torch.cuda.synchronize()
+    prof = ctx.profile_read()
+    ctx.profile(False)
+    us = prof["full"][0] / prof["full"][1] * 1e3
+    chunks = graph_chunks(args.warmup, args.steps, max(1, args.graph_steps))
+    graphs = {}
+    for first, n in chunks:
+        key = graph_key(first, n, period)
+        if key not in graphs:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                for u in range(n):
+                    step(first + u)
+            graphs[key] = gr
+    for gr in graphs.values():
+        gr.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for first, n in chunks:
+        graphs[graph_key(first, n, period)].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    del graphs
+    T, d = w.n_ctx, w.head_dim
+    step_bytes = w.batch * (w.n_kv_heads * T * 2 * d * e + w.n_q_heads * d * (e + 4))
+    kern_bytes = w.batch * (w.n_kv_heads * T * 2 * d * e + w.n_q_heads * d * e)
+    log(f"{label} dense: {ms * 1e3:.1f} us/step, attend_full_kernel {us:.1f} us")
+    ctx.close()
+    return {
+        "metric": "dense flash-decode steps/s (baseline: softmax over all T cached tokens)",
+        "value": 1e3 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "dtype": w.dtype, "data": "synthetic (seeded)",
+        "config": {"workload": w.name + "-dense", "batch": w.batch, "n_ctx": T, "cache_copies_rotated": ncopy,
+                   "launch": "hip-graph"},
+        "eff_ctx_tokens_per_s": 1e3 / ms * w.batch * T,
+        "algorithmic_bytes_per_step": step_bytes,
+        "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "kernel": "attend_full_kernel", "achieved": kern_bytes / (us * 1e-6) / 1e9,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kern_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                     "bytes_per_launch": kern_bytes},
+    }
+
+
 # ------------------------------------------------------------------ host-resident measurement
 def measure_host_resident(args):
     """The host-resident workload: 128K context, batch 1, ranks 8..32, factor
@@ -560,6 +638,8 @@ def main():
                     help="only measure the host-resident workload (pinned host factors fetched per step)")
     ap.add_argument("--fetch", choices=("staged", "direct"), default="direct",
                     help="host-resident fetch: host gather + copy (staged) or kernels reading pinned memory (direct)")
+    ap.add_argument("--dense", action="store_true",
+                    help="only measure the dense flash-decode baseline on the workload's K/V")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy three times (reference kernel for memory counters)")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -599,6 +679,9 @@ def main():
     t0 = time.time()
     x = synth.make_inputs(w, n_steps=Q)
     log(f"inputs drawn in {time.time() - t0:.1f}s")
+    if args.dense:
+        print(json.dumps(measure_dense(w, x, args, w.name)), flush=True)
+        return
     pool = None
     if not args.no_cpu_baseline:
         nw = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
@@ -619,6 +702,7 @@ def main():
         if args.sweep:
             for r, _ in recs[1:]:
                 print(json.dumps(r), flush=True)
+            print(json.dumps(measure_dense(w, x, args, w.name)), flush=True)
             del x
             xf = synth.make_inputs(w, n_steps=Q, full_rank_unit_gates=True)
             for r, _ in measure_device(w, xf, [None], args, w.name + " full rank", full_rank=True):

@@ -25,7 +25,8 @@ EXPORTS = [
     "sekv_build_spans", "sekv_route_workspace_bytes", "sekv_route", "sekv_reconstruct",
     "sekv_decode_workspace_bytes", "sekv_decode_host_workspace_bytes", "sekv_mixed_attention_decode",
     "sekv_profile_enable", "sekv_profile_read", "sekv_ctx_set_split", "sekv_ctx_set_fetch_mode",
-    "sekv_ctx_inject_fault", "sekv_profile_read_host", "sekv_route_noalloc",
+    "sekv_ctx_inject_fault", "sekv_profile_read_host", "sekv_route_noalloc", "sekv_dense_workspace_bytes",
+    "sekv_dense_attention_decode",
 ]
 SEKV_FETCH_STAGED, SEKV_FETCH_DIRECT = 0, 1
 SEKV_FAULT_NONE, SEKV_FAULT_GATHER = 0, 1
@@ -77,6 +78,8 @@ def _load():
         "sekv_route_workspace_bytes": (sz, [C, S]),
         "sekv_route": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, sz, _p]),
         "sekv_route_noalloc": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p]),
+        "sekv_dense_workspace_bytes": (sz, [_p, C]),
+        "sekv_dense_attention_decode": (i32, [_p, C, _p, _p, _p, _p, _p, sz, _p]),
         "sekv_reconstruct": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p]),
         "sekv_decode_workspace_bytes": (sz, [_p, C, S]),
         "sekv_decode_host_workspace_bytes": (sz, [_p, C, S]),
@@ -381,6 +384,31 @@ def decode(ctx: Context, cache: SpanCache, q, route_out: RouteOut, out, ws: Deco
                                            _ptr(route_out.exp_list), _ptr(route_out.exp_mask),
                                            _ptr(route_out.exp_count), _ptr(out), _ptr(ws.dev), ws.dev.numel(),
                                            host_ptr, host_n, _stream_handle(stream), cs))
+
+
+def tile_values_device(v):
+    """Device value rows [..., T, d] -> [..., ceil(T/32), d, 32] transposed
+    32-token tiles (zero padding): the layout of full_v / sum_v and of the
+    dense baseline's values (layout marshalling only)."""
+    torch = _torch()
+    *lead, T, d = v.shape
+    nt = -(-T // 32)
+    pad = torch.zeros((*lead, nt * 32, d), dtype=v.dtype, device=v.device)
+    pad[..., :T, :] = v
+    return pad.view(*lead, nt, 32, d).transpose(-1, -2).contiguous()
+
+
+def dense_workspace(ctx: Context, cfg: Config, device="cuda"):
+    torch = _torch()
+    n = LIB.sekv_dense_workspace_bytes(ctx.handle, ctypes.byref(cfg))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def dense_decode(ctx: Context, cfg: Config, k, v_tiles, q, out, ws, stream=None):
+    """sekv_dense_attention_decode: k [B][Hkv][T][d], v_tiles [B][Hkv][ceil(T/32)][d][32]
+    (cache dtype), q [B][Hq][d], out [B][Hq][d] f32, all device."""
+    _check(LIB.sekv_dense_attention_decode(ctx.handle, ctypes.byref(cfg), _ptr(k), _ptr(v_tiles), _ptr(q), _ptr(out),
+                                           _ptr(ws), ws.numel(), _stream_handle(stream)))
 
 
 # ----------------------------------------------------------------- marshalling

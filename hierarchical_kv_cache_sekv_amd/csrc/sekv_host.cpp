@@ -153,15 +153,19 @@ struct sekv_ctx {
 };
 
 namespace {
-hipError_t prof_mark(sekv_ctx* c, EventPairs& p, hipStream_t s) {
+// Start/stop events of one timed launch (both null while timing is off).
+hipError_t prof_pair(sekv_ctx* c, EventPairs& p, hipEvent_t* e0, hipEvent_t* e1) {
+  *e0 = *e1 = nullptr;
   if (!c->profile) return hipSuccess;
-  if (p.used == p.ev.size()) {
+  while (p.used + 2 > p.ev.size()) {
     hipEvent_t e;
     hipError_t err = hipEventCreate(&e);
     if (err != hipSuccess) return err;
     p.ev.push_back(e);
   }
-  return hipEventRecord(p.ev[p.used++], s);
+  *e0 = p.ev[p.used++];
+  *e1 = p.ev[p.used++];
+  return hipSuccess;
 }
 hipError_t prof_sum(EventPairs& p, double* ms, int64_t* n) {
   double tot = 0;
@@ -745,9 +749,9 @@ sekv_status route_launch(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* 
   int& resident = ctx->route_resident[c->dtype == SEKV_BF16][c->head_dim == 128][G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3];
   if (resident == 0) HIP_OR_FAIL(route_resident_blocks(a, ctx->device, &resident));
   a.use_ticket = (int64_t)a.nblk * c->n_kv_heads * c->batch > resident ? 1 : 0;
-  if (timed) HIP_OR_FAIL(prof_mark(ctx, ctx->prof_route, stream));
-  HIP_OR_FAIL(launch_route(a, stream));
-  if (timed) HIP_OR_FAIL(prof_mark(ctx, ctx->prof_route, stream));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (timed) HIP_OR_FAIL(prof_pair(ctx, ctx->prof_route, &e0, &e1));
+  HIP_OR_FAIL(launch_route(a, stream, e0, e1));
   return SEKV_OK;
 }
 }  // namespace
@@ -915,16 +919,15 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   if (!staged) {
     if (a.max_rank <= 64) {
       // both passes in one launch on the caller's stream
-      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
-      HIP_OR_FAIL(launch_attend_fused(a, stream));
-      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+      hipEvent_t e0, e1;
+      HIP_OR_FAIL(prof_pair(ctx, ctx->prof_attend, &e0, &e1));
+      HIP_OR_FAIL(launch_attend_fused(a, stream, e0, e1));
     } else {
-      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, stream));
-      HIP_OR_FAIL(launch_attend_expanded(a, stream));
-      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, stream));
-      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
-      HIP_OR_FAIL(launch_attend_full(a, stream));
-      HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+      hipEvent_t e0, e1;
+      HIP_OR_FAIL(prof_pair(ctx, ctx->prof_expand, &e0, &e1));
+      HIP_OR_FAIL(launch_attend_expanded(a, stream, e0, e1));
+      HIP_OR_FAIL(prof_pair(ctx, ctx->prof_attend, &e0, &e1));
+      HIP_OR_FAIL(launch_attend_full(a, stream, e0, e1));
     }
     HIP_OR_FAIL(launch_combine(a, stream));
     return SEKV_OK;
@@ -947,9 +950,9 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   HIP_OR_FAIL(hipMemcpyAsync(h_list, exp_list, (size_t)BG * cap * sizeof(int32_t), hipMemcpyDeviceToHost, stream));
   HIP_OR_FAIL(hipEventRecord(ctx->ev_list, stream));
   // full-resolution + summary pass runs while the host gathers
-  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
-  HIP_OR_FAIL(launch_attend_full(a, stream));
-  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_attend, stream));
+  hipEvent_t t0, t1;
+  HIP_OR_FAIL(prof_pair(ctx, ctx->prof_attend, &t0, &t1));
+  HIP_OR_FAIL(launch_attend_full(a, stream, t0, t1));
   const auto t_wait = std::chrono::steady_clock::now();
   HIP_OR_FAIL(hipEventSynchronize(ctx->ev_list));
   const auto t_listed = std::chrono::steady_clock::now();
@@ -1021,15 +1024,73 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   a5.stage_off = reinterpret_cast<const int64_t*>(dws + p.off_stage_off);
   a5.stage_fac = d_stage_fac;
   a5.stage_sg = reinterpret_cast<const float*>(dws + p.off_stage_sg);
-  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, stream));
-  HIP_OR_FAIL(launch_attend_expanded(a5, stream));
-  HIP_OR_FAIL(prof_mark(ctx, ctx->prof_expand, stream));
+  HIP_OR_FAIL(prof_pair(ctx, ctx->prof_expand, &t0, &t1));
+  HIP_OR_FAIL(launch_attend_expanded(a5, stream, t0, t1));
   HIP_OR_FAIL(launch_combine(a, stream));
   const auto t_end = std::chrono::steady_clock::now();
   ctx->host_wait_ms += std::chrono::duration<double, std::milli>(t_listed - t_wait).count();
   ctx->host_gather_ms += gather_ms;
   ctx->host_call_ms += std::chrono::duration<double, std::milli>(t_end - t_call).count();
   ctx->host_calls += 1;
+  return SEKV_OK;
+}
+
+// ---------------------------------------------------------------- dense baseline
+namespace {
+// Dense decode: the full-resolution pass over all T tokens of every (b, kv),
+// split into chunks of tiles_a4 32-token tiles, then the combine.
+void make_dense_plan(const sekv_config* c, int32_t split_entries, AttendArgs& a, size_t& off_ml, size_t& off_o,
+                     size_t& bytes) {
+  const int B = c->batch, Hkv = c->n_kv_heads, D = c->head_dim, G = c->n_q_heads / Hkv, T = c->n_ctx;
+  const int BG = B * Hkv;
+  a = AttendArgs{};
+  a.dtype = c->dtype; a.B = B; a.Hq = c->n_q_heads; a.Hkv = Hkv; a.D = D;
+  a.seg_cap = 1; a.full_cap = T;
+  for (int b = 0; b < B; ++b) { a.n_full[b] = T; a.n_seg[b] = 0; }
+  const int ntiles = (T + 31) / 32;
+  int64_t tc = ((int64_t)BG * ntiles + 1023) / 1024;
+  tc = std::max<int64_t>(4, std::min<int64_t>(64, tc));
+  if (split_entries > 0) tc = std::max<int64_t>(1, std::min<int64_t>(64, (split_entries + 31) / 32));
+  a.tiles_a4 = (int)tc;
+  a.nch_a4 = (ntiles + a.tiles_a4 - 1) / a.tiles_a4;
+  a.P_max = a.nch_a4;
+  a.n_a4_wg = BG * a.nch_a4;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)D));
+  off_ml = 0;
+  off_o = align_up((size_t)BG * a.P_max * G * 2 * sizeof(float));
+  bytes = align_up(off_o + (size_t)BG * a.P_max * G * D * sizeof(float));
+}
+}  // namespace
+
+size_t sekv_dense_workspace_bytes(const sekv_ctx* ctx, const sekv_config* c) {
+  if (check_config(c) != SEKV_OK) return 0;
+  AttendArgs a;
+  size_t ml, o, bytes;
+  make_dense_plan(c, ctx ? ctx->split_entries : 0, a, ml, o, bytes);
+  return bytes;
+}
+
+sekv_status sekv_dense_attention_decode(sekv_ctx* ctx, const sekv_config* c, const void* k, const void* v,
+                                        const void* q, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  sekv_status st = check_config(c);
+  if (st != SEKV_OK) return st;
+  if (!k || !v || !q || !out || !ws) return fail(SEKV_EINVAL, "sekv_dense_attention_decode: a pointer argument is NULL");
+  AttendArgs a;
+  size_t off_ml, off_o, bytes;
+  make_dense_plan(c, ctx->split_entries, a, off_ml, off_o, bytes);
+  if (ws_bytes < bytes) return fail(SEKV_ECAPACITY, "dense workspace %zu bytes < %zu needed", ws_bytes, bytes);
+  char* w = static_cast<char*>(ws);
+  a.q = q; a.full_k = k; a.full_v = v; a.sum_k = k; a.sum_v = v;
+  a.exp_count = nullptr;
+  a.part_ml = reinterpret_cast<float*>(w + off_ml);
+  a.part_o = reinterpret_cast<float*>(w + off_o);
+  a.out = out;
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+  hipEvent_t e0, e1;
+  HIP_OR_FAIL(prof_pair(ctx, ctx->prof_attend, &e0, &e1));
+  HIP_OR_FAIL(launch_attend_full(a, stream, e0, e1));
+  HIP_OR_FAIL(launch_combine(a, stream));
   return SEKV_OK;
 }
 

@@ -55,7 +55,8 @@ struct AttendArgs {
   const void* fac; const float* sg;
   const int64_t* stage_off;  // staged host-resident mode: [B*Hkv] first entry of each group, then (fac, sg) offsets per listed entry
   const void* stage_fac; const float* stage_sg;
-  const int32_t* exp_list; const uint8_t* exp_mask; const int32_t* exp_count;
+  const int32_t* exp_list; const uint8_t* exp_mask;
+  const int32_t* exp_count;  // nullptr: no expanded spans (dense decode)
   float* part_ml;            // [B*Hkv][P_max][G][2]
   float* part_o;             // [B*Hkv][P_max][G][D]
   float* out;                // [B][Hq][D]
@@ -73,15 +74,16 @@ struct ReconArgs {
   int T;
 };
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// ev0/ev1: optional start/stop events of the kernel itself (both or neither)
+hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // Route workgroups the device holds at once (occupancy x compute units).
 hipError_t route_resident_blocks(const RouteArgs& a, int device, int* blocks);
 // Device address of the static route state on `device` (must be current);
 // taken and zero-filled on the first call per device.
 hipError_t route_scratch_address(int device, void** ptr);
-hipError_t launch_attend_full(const AttendArgs& a, hipStream_t s);
-hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s);
-hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_full(const AttendArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s);
 hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s);
 

@@ -24,6 +24,7 @@
 //   combine_kernel  log-sum-exp merge of all partials of a query head.
 //   recon_*         standalone token-level K/V rebuild (tests, unfused use).
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -1216,7 +1217,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const AttendAr
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int g = b * a.Hkv + h / G, gi = h % G;
   const int tid = threadIdx.x, row = tid >> 3, c4 = tid & 7;
-  const int np = a.nch_a4 + (a.exp_count[g] + kExpChunk - 1) / kExpChunk;
+  const int np = a.nch_a4 + (a.exp_count ? (a.exp_count[g] + kExpChunk - 1) / kExpChunk : 0);
   const float* ml = a.part_ml + (size_t)g * a.P_max * G * 2;
   const float* po = a.part_o + (size_t)g * a.P_max * G * D + 32 * sl + 4 * c4;
   float M = kNegInf, L = 0.0f;
@@ -1412,10 +1413,18 @@ hipError_t route_scratch_address(int device, void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+// Timed launches: with a start/stop event pair (both non-null) the events are
+// recorded at the start and the end of the kernel's own execution.
+#define SEKV_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, S, EV0, EV1, ARG)                                  \
+  do {                                                                                             \
+    if ((EV0) && (EV1)) hipExtLaunchKernelGGL(KERNEL, dim3(GRID), dim3(BLOCK), SHMEM, S, EV0, EV1, 0, ARG); \
+    else KERNEL<<<dim3(GRID), dim3(BLOCK), SHMEM, S>>>(ARG);                                       \
+  } while (0)
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int G = a.Hq / a.Hkv;
   dim3 grid(a.nblk, a.Hkv, a.B);
-  SEKV_DISPATCH(a.dtype, a.D, G, (route_kernel<TT, DD, GG><<<grid, kRouteThreads, 0, s>>>(a)));
+  SEKV_DISPATCH(a.dtype, a.D, G, ({ SEKV_LAUNCH((route_kernel<TT, DD, GG>), grid, kRouteThreads, 0, s, ev0, ev1, a); }));
   return hipGetLastError();
 }
 
@@ -1433,34 +1442,37 @@ hipError_t route_resident_blocks(const RouteArgs& a, int device, int* blocks) {
   return hipSuccess;
 }
 
-hipError_t launch_attend_full(const AttendArgs& a, hipStream_t s) {
+hipError_t launch_attend_full(const AttendArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int G = a.Hq / a.Hkv;
   if (a.n_a4_wg == 0) return hipSuccess;
   SEKV_DISPATCH(a.dtype, a.D, G,
-                (attend_full_kernel<TT, DD, GG><<<a.n_a4_wg, kAttnThreads, AttnLds<DD, GG>::kRoleA, s>>>(a)));
+                ({ SEKV_LAUNCH((attend_full_kernel<TT, DD, GG>), a.n_a4_wg, kAttnThreads, (AttnLds<DD, GG>::kRoleA), s,
+                               ev0, ev1, a); }));
   return hipGetLastError();
 }
 
-hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s) {
+hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int G = a.Hq / a.Hkv;
   if (a.n_a5_wg == 0) return hipSuccess;
-  SEKV_DISPATCH(a.dtype, a.D, G,
-                (a.max_rank <= 64
-                     ? attend_expanded_kernel<TT, DD, GG><<<a.n_a5_wg, kExpThreads, ExpLds<TT, GG, 4>::kBytes, s>>>(a)
-                     : attend_expanded_wide_kernel<TT, DD, GG>
-                           <<<a.n_a5_wg, kExpThreads, ExpLds<TT, GG, kMaxSpan / 16>::kBytes, s>>>(a)));
+  SEKV_DISPATCH(a.dtype, a.D, G, ({
+                  if (a.max_rank <= 64)
+                    SEKV_LAUNCH((attend_expanded_kernel<TT, DD, GG>), a.n_a5_wg, kExpThreads, (ExpLds<TT, GG, 4>::kBytes),
+                                s, ev0, ev1, a);
+                  else
+                    SEKV_LAUNCH((attend_expanded_wide_kernel<TT, DD, GG>), a.n_a5_wg, kExpThreads,
+                                (ExpLds<TT, GG, kMaxSpan / 16>::kBytes), s, ev0, ev1, a);
+                }));
   return hipGetLastError();
 }
 
-hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s) {
+hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int G = a.Hq / a.Hkv;
   if (a.n_fx_wg + a.n_a4_wg == 0) return hipSuccess;
   SEKV_DISPATCH(a.dtype, a.D, G,
-                (attend_fused_kernel<TT, DD, GG><<<a.n_fx_wg + a.n_a4_wg, kAttnThreads,
-                                                   (AttnLds<DD, GG>::kRoleA > 4 * ExpLds<TT, GG, 4>::kBytes
-                                                        ? AttnLds<DD, GG>::kRoleA
-                                                        : 4 * ExpLds<TT, GG, 4>::kBytes),
-                                                   s>>>(a)));
+                ({ SEKV_LAUNCH((attend_fused_kernel<TT, DD, GG>), a.n_fx_wg + a.n_a4_wg, kAttnThreads,
+                               (AttnLds<DD, GG>::kRoleA > 4 * ExpLds<TT, GG, 4>::kBytes ? AttnLds<DD, GG>::kRoleA
+                                                                                        : 4 * ExpLds<TT, GG, 4>::kBytes),
+                               s, ev0, ev1, a); }));
   return hipGetLastError();
 }
 

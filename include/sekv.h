@@ -315,6 +315,27 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* cfg, c
                                         hipStream_t stream, hipStream_t copy_stream);
 
 /*
+ * sekv_dense_attention_decode - the dense baseline: plain softmax attention of
+ * each query head over all T cached tokens (logit q.k/sqrt(d)), with the same
+ * split-K matrix-core pass and log-sum-exp merge as the full-resolution part
+ * of sekv_mixed_attention_decode.  It is the full-KV decode that the pages
+ * compare SeKV's latency with ("Experimentelle Ergebnisse", efficiency).
+ *   k [B][Hkv][T][d] dtype device (token order).
+ *   v [B][Hkv][ceil(T/32)][d][32] dtype device: values in 32-token tiles, each
+ *     tile transposed (value (t, j) at ((t/32)*d + j)*32 + t%32; padding
+ *     entries finite).
+ *   q [B][Hq][d] dtype device; out [B][Hq][d] f32 device, written.
+ *   ws: device workspace of sekv_dense_workspace_bytes (contents ignored).
+ * Only batch, n_ctx, head counts, head_dim and dtype of cfg are used (the
+ * span fields must still pass the usual checks).  The context's split setting
+ * applies.  Timed under "full" by the measurement hook.
+ * Errors: SEKV_EINVAL / SEKV_ESHAPE / SEKV_ECAPACITY / SEKV_EHIP.
+ */
+size_t sekv_dense_workspace_bytes(const sekv_ctx* ctx, const sekv_config* cfg);
+sekv_status sekv_dense_attention_decode(sekv_ctx* ctx, const sekv_config* cfg, const void* k, const void* v,
+                                        const void* q, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Measurement hook.  While enabled, sekv_route and sekv_mixed_attention_decode
  * record a timing-event pair around each of their main kernels, on the stream
  * the kernel runs on: the route kernels ("route"); the attention kernels

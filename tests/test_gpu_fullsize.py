@@ -283,3 +283,27 @@ def test_fullsize_t128k_b4_full_expansion_equals_dense(ctx):
         worst = max(worst, err)
         assert err <= TOL[w.dtype], (b, err)
     log(f"{w.name} full expansion: max err vs dense over all heads {worst:.2e}")
+
+
+def test_fullsize_t128k_b4_dense_baseline(ctx):
+    """The dense flash-decode baseline over the benchmark workload's stored
+    K/V (128K context, batch 4), every head against the oracle's dense
+    attention."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    w = synth.workload(5)
+    x = synth.make_inputs(w, n_steps=1)
+    cfg = B.make_config(w)
+    k = torch.from_numpy(x.k).to(torch.bfloat16).cuda()
+    vt = B.tile_values_device(torch.from_numpy(x.v).to(torch.bfloat16).cuda())
+    q = torch.from_numpy(np.ascontiguousarray(x.q[0])).to(torch.bfloat16).cuda()
+    out = torch.zeros((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    B.dense_decode(ctx, cfg, k, vt, q, out, B.dense_workspace(ctx, cfg))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    worst = 0.0
+    for b in range(w.batch):
+        err = float(np.abs(got[b] - O.dense_attention(x.q[0, b], x.k[b], x.v[b], w.group)).max())
+        worst = max(worst, err)
+        assert err <= TOL[w.dtype], (b, err)
+    log(f"{w.name} dense baseline: max err over all heads {worst:.2e}")

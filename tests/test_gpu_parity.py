@@ -447,3 +447,26 @@ def test_abi_errors_need_context(ctx):
     assert ei.value.status == B.SEKV_EINVAL
     torch.cuda.synchronize()
     assert torch.equal(dev.out, sentinel)
+
+
+@pytest.mark.parametrize("dtype,T,G,d", [("bf16", 4113, 4, 128), ("f32", 3000, 2, 64), ("bf16", 70, 8, 64)])
+def test_dense_baseline_matches_oracle(ctx, dtype, T, G, d):
+    """The dense flash-decode baseline (all T tokens, no spans) against the
+    oracle's dense softmax attention; ragged last tile."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    w = synth.workload(2, n_ctx=T, batch=2, dtype=dtype, n_q_heads=2 * G, n_kv_heads=2, head_dim=d,
+                       n_recent=min(64, T - 4))
+    x = synth.make_inputs(w, n_steps=1)
+    cfg = B.make_config(w)
+    et = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k = torch.from_numpy(x.k).to(et).cuda()
+    vt = B.tile_values_device(torch.from_numpy(x.v).to(et).cuda())
+    q = torch.from_numpy(np.ascontiguousarray(x.q[0])).to(et).cuda()
+    out = torch.zeros((w.batch, w.n_q_heads, d), dtype=torch.float32, device="cuda")
+    B.dense_decode(ctx, cfg, k, vt, q, out, B.dense_workspace(ctx, cfg))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = max(float(np.abs(got[b] - O.dense_attention(x.q[0, b], x.k[b], x.v[b], G)).max()) for b in range(w.batch))
+    log(f"dense baseline {dtype} T={T} G={G} d={d}: max|err|={err:.3e}")
+    assert err <= TOL[dtype]
