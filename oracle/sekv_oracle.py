@@ -42,7 +42,8 @@ __all__ = [
     "storage_round", "segment", "full_res_tokens", "span_summary", "span_summaries",
     "routing_keys", "span_factors", "OracleCache", "build_cache", "route_scores",
     "route", "compact", "reconstruct", "mixed_attention", "mixed_attention_all",
-    "dense_attention", "SIZE_CORRECTION",
+    "dense_attention", "SIZE_CORRECTION", "span_factors_separate", "span_ranks", "fold_matrix",
+    "fold_query", "key_scales", "route_scores_folded", "reconstruct_span",
 ]
 
 # Reading: the size correction of an unexpanded span's summary logit is +ln|S|
@@ -194,6 +195,80 @@ def span_factors(k_body, v_body, r: int):
     return U, sig, Vh
 
 
+def span_factors_separate(k_body, v_body, r: int):
+    """Reading variant: one rank-r basis for the keys and another for the
+    values of a span (two SVDs of L x d matrices instead of one of L x 2d).
+
+    [de-2]/[zh-2] speak of one low-rank SVD basis per span; this variant tests
+    that reading.  Returns ((U_K, sigma_K, Vh_K [r][d]), (U_V, sigma_V,
+    Vh_V [r][d])), each signed like ``span_factors``.
+    """
+    out = []
+    for M in (np.asarray(k_body, np.float64), np.asarray(v_body, np.float64)):
+        U, sig, Vh = np.linalg.svd(M, full_matrices=False)
+        U, sig, Vh = U[:, :r].copy(), sig[:r].copy(), Vh[:r].copy()
+        for j in range(r):
+            i = int(np.argmax(np.abs(U[:, j])))
+            if U[i, j] < 0:
+                U[:, j] *= -1.0
+                Vh[j] *= -1.0
+        out.append((U, sig, Vh))
+    return tuple(out)
+
+
+def span_ranks(rank_req, L, d: int, rank_cap: str = "full", basis: str = "joint"):
+    """Rank of each span: r = min(requested, cap(L), rank of the factored
+    matrix).  Readings: cap(L) = L (default) or ceil(L / 2) (variant "half");
+    the factored matrix is L x 2d (joint basis) or L x d (separate bases)."""
+    L = np.asarray(L, np.int64)
+    cap = L if rank_cap == "full" else (L + 1) // 2
+    width = 2 * d if basis == "joint" else d
+    return np.minimum(np.minimum(np.asarray(rank_req, np.int64), cap), width)
+
+
+# --------------------------------------------------------------------------
+# reading variant: routing folded onto the attention summary key
+# --------------------------------------------------------------------------
+def fold_matrix(P) -> np.ndarray:
+    """M = P^T P (fp64), accumulated over the rows a of P in order:
+    M += outer(P[a], P[a]), each product and sum rounded in fp64."""
+    P = np.asarray(P, np.float64)
+    M = np.zeros((P.shape[1], P.shape[1]))
+    for a in range(P.shape[0]):
+        M = M + np.multiply.outer(P[a], P[a])
+    return M
+
+
+def fold_query(M, q) -> np.ndarray:
+    """Folded query q' = M q per head, as float32: for each output element a
+    sequential fp64 sum over j of M[i][j] * q[j] (each product and sum rounded
+    in fp64), then rounded to float32.  q: [G][d] stored values."""
+    M = np.asarray(M, np.float64)
+    q = np.asarray(q, np.float64)
+    acc = np.zeros((q.shape[0], M.shape[0]))
+    for j in range(M.shape[1]):
+        acc = acc + np.multiply.outer(q[:, j], M[:, j])
+    return acc.astype(np.float32)
+
+
+def key_scales(kbar, P) -> np.ndarray:
+    """Per-span scale 1 / |P kbar| (0 if the norm is 0), float32, from the
+    unrounded fp64 summary key."""
+    r = np.asarray(kbar, np.float64) @ np.asarray(P, np.float64).T
+    nrm = np.sqrt((r * r).sum(axis=1))
+    return np.where(nrm > 0, 1.0 / np.where(nrm > 0, nrm, 1.0), 0.0).astype(np.float32)
+
+
+def route_scores_folded(qf, kbar, scale) -> np.ndarray:
+    """Reading variant of the routing score: (P q) . normalize(P kbar) written
+    as (P^T P q) . kbar / |P kbar|, so the route reads the stored attention
+    summary key kbar instead of a separate routing key.  Canonical float32
+    order: z = sequential float32 sum over i of fl32(q'_i * kbar_i), then
+    z' = fl32(z * scale).  qf: folded queries [G][d] float32 (fold_query)."""
+    z = route_scores(qf, kbar)
+    return np.multiply(z, np.asarray(scale, np.float32)[None, :], dtype=np.float32)
+
+
 # --------------------------------------------------------------------------
 # cache build (prefill side)
 # --------------------------------------------------------------------------
@@ -219,7 +294,13 @@ class OracleCache:
     U: List[List[List[np.ndarray]]]           # [b][kv][S] -> [L][r]
     sigma: List[List[List[np.ndarray]]]       # [b][kv][S] -> [r]
     gate: List[List[List[np.ndarray]]]        # [b][kv][S] -> [r]
-    Vh: List[List[List[np.ndarray]]]          # [b][kv][S] -> [r][2d]
+    Vh: List[List[List[np.ndarray]]]          # [b][kv][S] -> [r][2d] (joint) or [r][d] (keys, separate)
+    basis: str = "joint"
+    U_V: List = None                          # separate bases: [b][kv][S] -> [L][r]
+    sigma_V: List = None                      # [b][kv][S] -> [r]
+    Vh_V: List = None                         # [b][kv][S] -> [r][d]
+    key_scale: List = None                    # folded routing: [b][kv] -> [n_seg] float32
+    fold: List = None                         # folded routing: [kv] -> [d][d] fp64
 
     def n_seg(self, b: int) -> int:
         return len(self.seg_off[b]) - 1
@@ -230,30 +311,36 @@ class OracleCache:
 
 
 def build_cache(k, v, s, thr, P, rank_req, gate, *, n_sink, n_recent, lo, hi, dtype,
-                factor_spans=None) -> OracleCache:
+                factor_spans=None, rank_cap="full", basis="joint") -> OracleCache:
     """Build the mixed-resolution cache from stored K/V [B][Hkv][T][d], surprisal
     [B][T], boundary thresholds [B], projections [Hkv][d][d], requested ranks
     [B][>=n_seg] and gates [B][Hkv][>=n_seg][>=r].
 
-    Reading: rank r_S = min(requested, L_S, 2d), shared by the span's KV heads;
-    gates are applied at decode, not folded into the factors.
+    Reading: rank r_S = min(requested, L_S, 2d) (``span_ranks``), shared by
+    the span's KV heads; gates are applied at decode, not folded into the
+    factors.  Variants: ``rank_cap="half"`` caps r_S at ceil(L_S / 2);
+    ``basis="separate"`` factors keys and values separately (r_S <= d), with
+    the same gate vector on both.  The folded-routing fields (fold matrix and
+    per-span key scales) are always filled.
 
     ``factor_spans`` (optional): {(b, kv head): span indices}; only those spans
     get factors (the others hold None and must not be expanded).  This skips
     work only; every value computed is the same.
     """
     B, Hkv, T, d = k.shape
+    sep = basis == "separate"
     seg_offs, full_idx, fk, fv, sk, sv, rh, ranks, Us, sigs, gts, Vhs = ([] for _ in range(12))
+    UVs, sVs, VVs, kss = [], [], [], []
     for b in range(B):
         so = segment(s[b], float(thr[b]), n_sink, n_recent, lo, hi)
         n_seg = len(so) - 1
         L = (so[1:] - so[:-1] - 1).astype(np.int64)
-        r = np.minimum(np.minimum(np.asarray(rank_req[b][:n_seg], np.int64), L), 2 * d)
+        r = span_ranks(rank_req[b][:n_seg], L, d, rank_cap, basis)
         fi = full_res_tokens(so, n_sink, T)
         seg_offs.append(so)
         full_idx.append(fi)
         ranks.append(r)
-        fk_b, fv_b, sk_b, sv_b, rh_b, U_b, sg_b, g_b, Vh_b = ([] for _ in range(9))
+        fk_b, fv_b, sk_b, sv_b, rh_b, U_b, sg_b, g_b, Vh_b, UV_b, sV_b, VV_b, ks_b = ([] for _ in range(13))
         for h in range(Hkv):
             kk = np.asarray(k[b, h], np.float64)
             vv = np.asarray(v[b, h], np.float64)
@@ -263,25 +350,36 @@ def build_cache(k, v, s, thr, P, rank_req, gate, *, n_sink, n_recent, lo, hi, dt
             sk_b.append(storage_round(kbar, dtype))
             sv_b.append(storage_round(vbar, dtype))
             rh_b.append(storage_round(routing_keys(kbar, P[h]), dtype))
-            Uh, sgh, gh, Vhh = [], [], [], []
+            ks_b.append(key_scales(kbar, P[h]))
+            Uh, sgh, gh, Vhh, UVh, sVh, VVh = [], [], [], [], [], [], []
             want = None if factor_spans is None else set(int(i) for i in factor_spans.get((b, h), ()))
             for i in range(n_seg):
                 if want is not None and i not in want:
-                    Uh.append(None); sgh.append(None); gh.append(None); Vhh.append(None)
+                    for lst in (Uh, sgh, gh, Vhh, UVh, sVh, VVh):
+                        lst.append(None)
                     continue
                 lo_t, hi_t = int(so[i]) + 1, int(so[i + 1])
-                Ui, si, Vi = span_factors(kk[lo_t:hi_t], vv[lo_t:hi_t], int(r[i]))
+                ri = int(r[i])
+                if sep:
+                    (Ui, si, Vi), (Uv, sv_, Vv) = span_factors_separate(kk[lo_t:hi_t], vv[lo_t:hi_t], ri)
+                    UVh.append(storage_round(Uv, dtype))
+                    sVh.append(sv_.copy() if dtype == "f64" else sv_.astype(np.float32).astype(np.float64))
+                    VVh.append(storage_round(Vv, dtype))
+                else:
+                    Ui, si, Vi = span_factors(kk[lo_t:hi_t], vv[lo_t:hi_t], ri)
+                    UVh.append(None); sVh.append(None); VVh.append(None)
                 Uh.append(storage_round(Ui, dtype))
                 sgh.append(si.copy() if dtype == "f64" else si.astype(np.float32).astype(np.float64))
-                gh.append(np.asarray(gate[b][h][i][: int(r[i])], np.float32).astype(np.float64))
+                gh.append(np.asarray(gate[b][h][i][:ri], np.float32).astype(np.float64))
                 Vhh.append(storage_round(Vi, dtype))
-            U_b.append(Uh)
-            sg_b.append(sgh)
-            g_b.append(gh)
-            Vh_b.append(Vhh)
+            U_b.append(Uh); sg_b.append(sgh); g_b.append(gh); Vh_b.append(Vhh)
+            UV_b.append(UVh); sV_b.append(sVh); VV_b.append(VVh)
         fk.append(fk_b); fv.append(fv_b); sk.append(sk_b); sv.append(sv_b); rh.append(rh_b)
         Us.append(U_b); sigs.append(sg_b); gts.append(g_b); Vhs.append(Vh_b)
-    return OracleCache(dtype, n_sink, T, d, seg_offs, full_idx, fk, fv, sk, sv, rh, ranks, Us, sigs, gts, Vhs)
+        UVs.append(UV_b); sVs.append(sV_b); VVs.append(VV_b); kss.append(ks_b)
+    folds = [fold_matrix(P[h]) for h in range(Hkv)]
+    return OracleCache(dtype, n_sink, T, d, seg_offs, full_idx, fk, fv, sk, sv, rh, ranks, Us, sigs, gts, Vhs,
+                       basis=basis, U_V=UVs, sigma_V=sVs, Vh_V=VVs, key_scale=kss, fold=folds)
 
 
 # --------------------------------------------------------------------------
@@ -350,6 +448,20 @@ def reconstruct(U, sigma, gate, Vh, d: int):
     return M[:, :d], M[:, d:]
 
 
+def reconstruct_span(cache: "OracleCache", b: int, kv: int, S: int):
+    """Token-level (K, V) of span S from the cache's factors: one joint basis
+    (``reconstruct``), or separate key and value bases U_K diag(sigma_K * g)
+    Vh_K and U_V diag(sigma_V * g) Vh_V."""
+    d = cache.d
+    if cache.basis != "separate":
+        return reconstruct(cache.U[b][kv][S], cache.sigma[b][kv][S], cache.gate[b][kv][S], cache.Vh[b][kv][S], d)
+    g = np.asarray(cache.gate[b][kv][S], np.float64)
+    K = np.asarray(cache.U[b][kv][S]) @ ((np.asarray(cache.sigma[b][kv][S]) * g)[:, None] * np.asarray(cache.Vh[b][kv][S]))
+    V = np.asarray(cache.U_V[b][kv][S]) @ ((np.asarray(cache.sigma_V[b][kv][S]) * g)[:, None]
+                                           * np.asarray(cache.Vh_V[b][kv][S]))
+    return K, V
+
+
 def _softmax_pool(logits: np.ndarray, values: np.ndarray) -> np.ndarray:
     m = logits.max()
     p = np.exp(logits - m)
@@ -383,8 +495,7 @@ def mixed_attention(cache: OracleCache, b: int, q_b, decisions_b, group: int) ->
             union |= decisions_b[h]
         rebuilt = {}
         for S in np.nonzero(union)[0].tolist():
-            rebuilt[S] = reconstruct(cache.U[b][kv][S], cache.sigma[b][kv][S], cache.gate[b][kv][S],
-                                     cache.Vh[b][kv][S], d)
+            rebuilt[S] = reconstruct_span(cache, b, kv, S)
         for h in heads:
             qh = q_b[h]
             keys = [cache.full_k[b][kv]]
