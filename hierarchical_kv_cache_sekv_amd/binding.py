@@ -41,7 +41,7 @@ class SekvError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_ctx", "n_q_heads", "n_kv_heads", "head_dim", "n_sink", "n_recent", "min_span",
-        "max_span", "dtype", "factors_on_host")]
+        "max_span", "dtype", "factors_on_host", "rank_cap", "basis", "route_keys")]
 
 
 _p = ctypes.c_void_p
@@ -55,6 +55,7 @@ class Spans(ctypes.Structure):
         ("fac_off", _p), ("sg_off", _p), ("fac", _p), ("sg", _p),
         ("fac_elems", ctypes.c_int64), ("sg_elems", ctypes.c_int64),
         ("seg_off_host", _p), ("rank_host", _p), ("fac_off_host", _p), ("sg_off_host", _p),
+        ("key_scale", _p), ("fold", _p),
     ]
 
 
@@ -122,10 +123,14 @@ def _ptr(x) -> Optional[int]:
 
 
 def make_config(w, factors_on_host: Optional[bool] = None) -> Config:
-    """Config from a workload description (any object with the workload fields)."""
+    """Config from a workload description (any object with the workload fields;
+    the reading-variant fields rank_cap, basis and route_keys default to the
+    default readings)."""
     return Config(w.batch, w.n_ctx, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_sink, w.n_recent,
                   w.min_span, w.max_span, SEKV_BF16 if w.dtype == "bf16" else SEKV_F32,
-                  int(w.factors_on_host if factors_on_host is None else factors_on_host))
+                  int(w.factors_on_host if factors_on_host is None else factors_on_host),
+                  int(getattr(w, "rank_cap", "full") == "half"), int(getattr(w, "basis", "joint") == "separate"),
+                  int(getattr(w, "route_keys", "rho") == "folded"))
 
 
 def capacities(cfg: Config):
@@ -249,6 +254,8 @@ class SpanCache:
         self.sum_k = torch.zeros((B, Hkv, self.seg_cap, D), dtype=et, device=dev)
         self.sum_v = torch.zeros((B, Hkv, -(-self.seg_cap // 32), D, 32), dtype=et, device=dev)
         self.rho = torch.zeros_like(self.sum_k)
+        self.key_scale = torch.zeros((B, Hkv, self.seg_cap), dtype=torch.float32, device=dev)
+        self.fold = torch.zeros((Hkv, D, D), dtype=torch.float64, device=dev)
         nf = max(plan.fac_elems, 8)
         ng = max(plan.sg_elems, 8)
         if cfg.factors_on_host:
@@ -265,13 +272,15 @@ class SpanCache:
         return Spans(self.seg_cap, self.full_cap, _ptr(n_seg), _ptr(n_full), _ptr(self.seg_off), _ptr(self.rank),
                      _ptr(self.full_k), _ptr(self.full_v), _ptr(self.sum_k), _ptr(self.sum_v), _ptr(self.rho),
                      _ptr(self.fac_off), _ptr(self.sg_off), _ptr(self.fac), _ptr(self.sg),
-                     self.fac.numel(), self.sg.numel(), _ptr(seg_off), _ptr(rank), _ptr(fac_off), _ptr(sg_off))
+                     self.fac.numel(), self.sg.numel(), _ptr(seg_off), _ptr(rank), _ptr(fac_off), _ptr(sg_off),
+                     _ptr(self.key_scale), _ptr(self.fold))
 
     def clone(self) -> "SpanCache":
         """Independent copy at new addresses (same contents)."""
         new = object.__new__(SpanCache)
         new.__dict__.update(self.__dict__)
-        for name in ("seg_off", "rank", "fac_off", "sg_off", "full_k", "full_v", "sum_k", "sum_v", "rho"):
+        for name in ("seg_off", "rank", "fac_off", "sg_off", "full_k", "full_v", "sum_k", "sum_v", "rho",
+                     "key_scale", "fold"):
             setattr(new, name, getattr(self, name).clone())
         if self.cfg.factors_on_host:
             new.fac = self.fac.clone().pin_memory()
@@ -283,7 +292,9 @@ class SpanCache:
 
     def device_bytes(self) -> int:
         n = 0
-        for name in ("seg_off", "rank", "fac_off", "sg_off", "full_k", "full_v", "sum_k", "sum_v", "rho"):
+        names = ["seg_off", "rank", "fac_off", "sg_off", "full_k", "full_v", "sum_k", "sum_v"]
+        names += ["key_scale", "fold"] if self.cfg.route_keys else ["rho"]
+        for name in names:
             t = getattr(self, name)
             n += t.numel() * t.element_size()
         if not self.cfg.factors_on_host:
@@ -412,16 +423,18 @@ def dense_decode(ctx: Context, cfg: Config, k, v_tiles, q, out, ws, stream=None)
 
 
 # ----------------------------------------------------------------- marshalling
-def fac_block_elems(L: int, r: int, d: int) -> int:
+def fac_block_elems(L: int, r: int, d: int, sep: bool = False) -> int:
     """Elements of one span's factor block: Vh_K [r][d] (groups of 8 rotated by
-    the row) | U [L][rp] | W_V in 16-rank column blocks [d][min(16, rp - 16 g)]."""
+    the row) | U [L][rp] | (separate bases: U_V [L][rp]) | W_V in 16-rank
+    column blocks [d][min(16, rp - 16 g)]."""
     rp = (r + 7) // 8 * 8
-    return r * d + L * rp + d * rp
+    return r * d + L * rp * (2 if sep else 1) + d * rp
 
 
-def sg_entry_elems(r: int) -> int:
-    """Floats of one span's sigma|gate entry: sigma [rq] | gate [rq], rq = ceil(r/4)*4."""
-    return 2 * ((r + 3) // 4 * 4)
+def sg_entry_elems(r: int, sep: bool = False) -> int:
+    """Floats of one span's sigma|gate entry: sigma [rq] | gate [rq], rq = ceil(r/4)*4
+    (separate bases: sigma_K | gate | sigma_V | gate)."""
+    return (4 if sep else 2) * ((r + 3) // 4 * 4)
 
 
 def _vk_rotate(vk: np.ndarray) -> np.ndarray:
@@ -462,22 +475,28 @@ def _wv_unblock(flat: np.ndarray, d: int, rp: int) -> np.ndarray:
 
 
 def read_factors(cache: "SpanCache", b: int, kv: int, i: int):
-    """(U [L][r], sigma [r], gate [r], Vh [r][2d]) of span i from a cache's pools
-    (host copies, float64)."""
+    """Factors of span i from a cache's pools (host copies, float64): one basis
+    (U [L][r], sigma [r], gate [r], Vh [r][2d]); separate bases ((U_K, sigma_K,
+    gate, Vh_K [r][d]), (U_V, sigma_V, gate, Vh_V [r][d]))."""
     plan, D = cache.plan, cache.cfg.head_dim
+    sep = bool(cache.cfg.basis)
     so = plan.seg_off[b]
     L = int(so[i + 1] - so[i] - 1)
     r = int(plan.rank[b, i])
     rp = (r + 7) // 8 * 8
     o = int(plan.fac_off[b, kv, i])
-    fac = cache.fac[o:o + fac_block_elems(L, r, D)].float().cpu().numpy().astype(np.float64)
+    fac = cache.fac[o:o + fac_block_elems(L, r, D, sep)].float().cpu().numpy().astype(np.float64)
     vk = _vk_unrotate(fac[:r * D].reshape(r, D))
     U = fac[r * D:r * D + L * rp].reshape(L, rp)[:, :r]
-    wv = _wv_unblock(fac[r * D + L * rp:], D, rp)[:, :r]
+    w0 = r * D + L * rp * (2 if sep else 1)
+    wv = _wv_unblock(fac[w0:], D, rp)[:, :r]
     go = int(plan.sg_off[b, kv, i])
     rq = (r + 3) // 4 * 4
-    sg = cache.sg[go:go + 2 * rq].float().cpu().numpy().astype(np.float64)
-    return U, sg[:r], sg[rq:rq + r], np.concatenate([vk, wv.T], axis=1)
+    sg = cache.sg[go:go + sg_entry_elems(r, sep)].float().cpu().numpy().astype(np.float64)
+    if not sep:
+        return U, sg[:r], sg[rq:rq + r], np.concatenate([vk, wv.T], axis=1)
+    Uv = fac[r * D + L * rp:r * D + 2 * L * rp].reshape(L, rp)[:, :r]
+    return (U, sg[:r], sg[rq:rq + r], vk), (Uv, sg[2 * rq:2 * rq + r], sg[3 * rq:3 * rq + r], wv.T)
 
 
 def tile_values(rows: np.ndarray) -> np.ndarray:
@@ -502,9 +521,12 @@ def fill_cache(cache: SpanCache, parts) -> None:
 
     ``parts`` provides, for each sequence b and KV head kv: ``full_k[b][kv]``,
     ``full_v``, ``sum_k``, ``sum_v``, ``rho`` ([n][d] arrays of values that are
-    exact in the cache dtype) and, for each span i, ``U[b][kv][i]`` [L][r],
-    ``sigma[b][kv][i]`` [r], ``gate[b][kv][i]`` [r], ``Vh[b][kv][i]`` [r][2d].
-    The plan of ``cache`` must describe the same spans and ranks.
+    exact in the cache dtype), ``key_scale[b][kv]`` [n] and ``fold[kv]`` [d][d]
+    and, for each span i, ``U[b][kv][i]`` [L][r], ``sigma[b][kv][i]`` [r],
+    ``gate[b][kv][i]`` [r], ``Vh[b][kv][i]`` ([r][2d] for one basis; [r][d]
+    key part for separate bases, with ``U_V``, ``sigma_V``, ``Vh_V`` [r][d]).
+    Spans whose U is None are left zero.  The plan of ``cache`` must describe
+    the same spans and ranks.
     """
     torch = _torch()
     cfg, plan = cache.cfg, cache.plan
@@ -515,6 +537,8 @@ def fill_cache(cache: SpanCache, parts) -> None:
     sk = np.zeros((B, Hkv, cache.seg_cap, D), np.float32)
     sv = np.zeros_like(sk)
     rh = np.zeros_like(sk)
+    ks = np.zeros((B, Hkv, cache.seg_cap), np.float32)
+    sep = bool(cfg.basis)
     fac = np.zeros(cache.fac.numel(), np.float32)
     sg = np.zeros(cache.sg.numel(), np.float32)
     for b in range(B):
@@ -527,7 +551,11 @@ def fill_cache(cache: SpanCache, parts) -> None:
             sk[b, kv, :n] = parts.sum_k[b][kv]
             sv[b, kv, :n] = parts.sum_v[b][kv]
             rh[b, kv, :n] = parts.rho[b][kv]
+            if getattr(parts, "key_scale", None) is not None:
+                ks[b, kv, :n] = parts.key_scale[b][kv]
             for i in range(n):
+                if parts.U[b][kv][i] is None:
+                    continue
                 U = np.asarray(parts.U[b][kv][i], np.float32)
                 Vh = np.asarray(parts.Vh[b][kv][i], np.float32)
                 L, r = U.shape
@@ -536,17 +564,21 @@ def fill_cache(cache: SpanCache, parts) -> None:
                 o = int(plan.fac_off[b, kv, i])
                 fac[o:o + r * D] = _vk_rotate(Vh[:, :D]).reshape(-1)  # key part [r][d], rotated groups
                 o += r * D
-                blk = np.zeros((L, rp), np.float32)
-                blk[:, :r] = U
-                fac[o:o + L * rp] = blk.reshape(-1)
-                o += L * rp
+                for Ub in ([U, np.asarray(parts.U_V[b][kv][i], np.float32)] if sep else [U]):
+                    blk = np.zeros((L, rp), np.float32)
+                    blk[:, :r] = Ub
+                    fac[o:o + L * rp] = blk.reshape(-1)
+                    o += L * rp
                 wv = np.zeros((D, rp), np.float32)
-                wv[:, :r] = Vh[:, D:].T                             # value part transposed, column blocks
-                fac[o:o + D * rp] = _wv_blocks(wv)
+                wv[:, :r] = np.asarray(parts.Vh_V[b][kv][i], np.float32).T if sep else Vh[:, D:].T
+                fac[o:o + D * rp] = _wv_blocks(wv)                  # value part transposed, column blocks
                 go = int(plan.sg_off[b, kv, i])
                 rq = (r + 3) // 4 * 4
                 sg[go:go + r] = parts.sigma[b][kv][i]
                 sg[go + rq:go + rq + r] = parts.gate[b][kv][i]
+                if sep:
+                    sg[go + 2 * rq:go + 2 * rq + r] = parts.sigma_V[b][kv][i]
+                    sg[go + 3 * rq:go + 3 * rq + r] = parts.gate[b][kv][i]
 
     def put(dst, src):
         dst.copy_(torch.from_numpy(src).to(et))
@@ -556,6 +588,9 @@ def fill_cache(cache: SpanCache, parts) -> None:
     put(cache.sum_k, sk)
     put(cache.sum_v, tile_values(sv))
     put(cache.rho, rh)
+    cache.key_scale.copy_(torch.from_numpy(ks))
+    if getattr(parts, "fold", None) is not None:
+        cache.fold.copy_(torch.from_numpy(np.ascontiguousarray(np.stack(parts.fold), np.float64)))
     cache.fac.copy_(torch.from_numpy(fac).to(et))
     cache.sg.copy_(torch.from_numpy(sg))
 
@@ -584,9 +619,8 @@ def layout_from_segments(cfg: Config, seg_offs, ranks) -> Plan:
         for kv in range(Hkv):
             for i in range(n):
                 r = int(rank[b, i])
-                rp = (r + 7) // 8 * 8
                 fac_off[b, kv, i] = fo
                 sg_off[b, kv, i] = go
-                fo += fac_block_elems(int(L[i]), r, D)
-                go += sg_entry_elems(r)
+                fo += fac_block_elems(int(L[i]), r, D, bool(cfg.basis))
+                go += sg_entry_elems(r, bool(cfg.basis))
     return Plan(n_seg, n_full, seg_off, rank, fac_off, sg_off, fo, go)

@@ -146,7 +146,7 @@ struct sekv_ctx {
   int32_t fetch_mode = SEKV_FETCH_DIRECT;
   int32_t fault = SEKV_FAULT_NONE;  // injected failure of the next host-resident decode
   void* route_scratch = nullptr;      // this device's static route state (sekv_route_noalloc)
-  int route_resident[2][2][4] = {};   // route workgroups resident at once, by dtype, d == 128, log2 G (0: unknown)
+  int route_resident[2][2][4][2] = {};  // route workgroups resident at once, by dtype, d == 128, log2 G, fold
   // host phases of host-resident decode calls since the last read
   double host_wait_ms = 0, host_gather_ms = 0, host_call_ms = 0;
   int64_t host_calls = 0;
@@ -193,18 +193,23 @@ int elem_size(int dtype) { return dtype == SEKV_BF16 ? 2 : 4; }
 // by k (group u at position (u + k) mod d/8).  W_V is the value part of Vh
 // transposed, cut into 16-rank column blocks g, each [d][min(16, rp - 16 g)].
 // In this order the expanded-span pass consumes the block front to back.
-int64_t fac_block_elems(int L, int r, int rp, int D) { return (int64_t)r * D + (int64_t)L * rp + (int64_t)D * rp; }
+// With separate bases (sep) a second U [L][rp] (the value basis) follows U.
+int64_t fac_block_elems(int L, int r, int rp, int D, bool sep = false) {
+  return (int64_t)r * D + (int64_t)L * rp * (sep ? 2 : 1) + (int64_t)D * rp;
+}
 int64_t fac_vk_index(int D, int k, int col) {
   const int ng = D / 8;
   return (int64_t)k * D + (int64_t)(((col / 8) + k) % ng) * 8 + (col % 8);
 }
 int64_t fac_u_index(int r, int rp, int D, int t, int j) { return (int64_t)r * D + (int64_t)t * rp + j; }
-int64_t fac_wv_index(int L, int r, int rp, int D, int col, int j) {
+int64_t fac_uv_index(int L, int r, int rp, int D, int t, int j) { return (int64_t)r * D + (int64_t)L * rp + (int64_t)t * rp + j; }
+int64_t fac_wv_index(int L, int r, int rp, int D, int col, int j, bool sep = false) {
   const int g = j / 16, wk = std::min(16, rp - 16 * g);
-  return (int64_t)r * D + (int64_t)L * rp + (int64_t)g * 16 * D + (int64_t)col * wk + (j % 16);
+  return (int64_t)r * D + (int64_t)L * rp * (sep ? 2 : 1) + (int64_t)g * 16 * D + (int64_t)col * wk + (j % 16);
 }
-// sigma|gate entry of one span: sigma [rq] | gate [rq], rq = r rounded up to 4.
-int64_t sg_entry_elems(int r) { return 2 * (((int64_t)r + 3) & ~(int64_t)3); }
+// sigma|gate entry of one span: sigma [rq] | gate [rq], rq = r rounded up to 4;
+// with separate bases sigma_K | gate | sigma_V | gate.
+int64_t sg_entry_elems(int r, bool sep = false) { return (sep ? 4 : 2) * (((int64_t)r + 3) & ~(int64_t)3); }
 
 sekv_status check_config(const sekv_config* c) {
   if (!c) return fail(SEKV_EINVAL, "config is NULL");
@@ -225,6 +230,9 @@ sekv_status check_config(const sekv_config* c) {
   if (c->min_span > c->max_span) return fail(SEKV_EINVAL, "min_span %d > max_span %d", c->min_span, c->max_span);
   if (c->max_span > kMaxSpan) return fail(SEKV_ESHAPE, "max_span %d exceeds %d", c->max_span, kMaxSpan);
   if (c->factors_on_host != 0 && c->factors_on_host != 1) return fail(SEKV_EINVAL, "factors_on_host must be 0 or 1");
+  if (c->rank_cap != 0 && c->rank_cap != 1) return fail(SEKV_EINVAL, "rank_cap must be 0 or 1");
+  if (c->basis != 0 && c->basis != 1) return fail(SEKV_EINVAL, "basis must be 0 or 1");
+  if (c->route_keys != 0 && c->route_keys != 1) return fail(SEKV_EINVAL, "route_keys must be 0 or 1");
   return SEKV_OK;
 }
 
@@ -260,8 +268,10 @@ sekv_status check_spans(const sekv_config* c, const sekv_spans* s, bool need_fac
     return fail(SEKV_ESHAPE, "spans capacities (%d, %d) differ from the configuration's (%d, %d)", s->seg_cap,
                 s->full_cap, seg_cap_of(c), full_cap_of(c));
   if (!s->n_seg_host || !s->n_full_host) return fail(SEKV_EINVAL, "n_seg_host / n_full_host is NULL");
-  if (!s->seg_off || !s->rank || !s->full_k || !s->full_v || !s->sum_k || !s->sum_v || !s->rho)
+  if (!s->seg_off || !s->rank || !s->full_k || !s->full_v || !s->sum_k || !s->sum_v)
     return fail(SEKV_EINVAL, "a span-cache device array is NULL");
+  if (c->route_keys == 0 && !s->rho) return fail(SEKV_EINVAL, "route_keys = 0 needs rho");
+  if (c->route_keys == 1 && (!s->key_scale || !s->fold)) return fail(SEKV_EINVAL, "route_keys = 1 needs key_scale and fold");
   for (int b = 0; b < c->batch; ++b) {
     if (s->n_seg_host[b] < 0 || s->n_seg_host[b] > s->seg_cap)
       return fail(SEKV_ESHAPE, "n_seg[%d] = %d outside [0, seg_cap=%d]", b, s->n_seg_host[b], s->seg_cap);
@@ -333,6 +343,21 @@ int segment_one(const float* s, float thr, const sekv_config* c, int32_t* seg_of
   (void)cap;
   seg_off[n] = tail;
   return n;
+}
+
+// M = P^T P for a d x d row-major P: M[i][j] = sum over rows a of P[a][i] *
+// P[a][j], accumulated in row order with every product and sum rounded in fp64.
+void fold_matrix(const float* P, int D, double* M) {
+#pragma clang fp contract(off)
+  for (int i = 0; i < D * D; ++i) M[i] = 0.0;
+  for (int a = 0; a < D; ++a)
+    for (int i = 0; i < D; ++i) {
+      const double pi = (double)P[(size_t)a * D + i];
+      for (int j = 0; j < D; ++j) {
+        const double prod = pi * (double)P[(size_t)a * D + j];
+        M[(size_t)i * D + j] = M[(size_t)i * D + j] + prod;
+      }
+    }
 }
 
 // One-sided Jacobi SVD of an L x n matrix M given by its rows (row-major,
@@ -477,7 +502,8 @@ sekv_status sekv_plan_spans(const sekv_config* c, const float* surprisal, const 
       int32_t r = 0;
       if (i < ns[b]) {
         const int L = sob[i + 1] - sob[i] - 1;
-        r = std::min(std::min(rank_req[(size_t)b * cap + i], L), 2 * D);
+        const int Lc = c->rank_cap ? (L + 1) / 2 : L;
+        r = std::min(std::min(rank_req[(size_t)b * cap + i], Lc), c->basis ? D : 2 * D);
       }
       rank[(size_t)b * cap + i] = r;
     }
@@ -490,8 +516,8 @@ sekv_status sekv_plan_spans(const sekv_config* c, const float* surprisal, const 
           const int rp = (r + 7) & ~7;
           fac_off[o] = fo;
           sg_off[o] = go;
-          fo += fac_block_elems(L, r, rp, D);
-          go += sg_entry_elems(r);
+          fo += fac_block_elems(L, r, rp, D, c->basis != 0);
+          go += sg_entry_elems(r, c->basis != 0);
         } else {
           fac_off[o] = 0;
           sg_off[o] = 0;
@@ -529,11 +555,12 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
         const size_t o = ((size_t)b * Hkv + kv) * cap + i;
         const int L = s->seg_off_host[(size_t)b * (cap + 1) + i + 1] - s->seg_off_host[(size_t)b * (cap + 1) + i] - 1;
         const int r = s->rank_host[(size_t)b * cap + i];
-        if (r < 1 || r > std::min(L, 2 * D)) return fail(SEKV_EINVAL, "rank[%d][%d] = %d outside [1, min(L=%d, 2d)]", b, i, r, L);
+        const int rmax = std::min(c->rank_cap ? (L + 1) / 2 : L, c->basis ? D : 2 * D);
+        if (r < 1 || r > rmax) return fail(SEKV_EINVAL, "rank[%d][%d] = %d outside [1, %d] (L = %d)", b, i, r, rmax, L);
         if (r > gate_stride) return fail(SEKV_ESHAPE, "gate_stride %d < rank %d", gate_stride, r);
         const int rp = (r + 7) & ~7;
-        need_f = std::max<int64_t>(need_f, s->fac_off_host[o] + fac_block_elems(L, r, rp, D));
-        need_g = std::max<int64_t>(need_g, s->sg_off_host[o] + sg_entry_elems(r));
+        need_f = std::max<int64_t>(need_f, s->fac_off_host[o] + fac_block_elems(L, r, rp, D, c->basis != 0));
+        need_g = std::max<int64_t>(need_g, s->sg_off_host[o] + sg_entry_elems(r, c->basis != 0));
         if (s->fac_off_host[o] % 8 != 0 || s->sg_off_host[o] % 4 != 0)
           return fail(SEKV_EINVAL, "pool offsets of span (%d, %d, %d) are not 8- and 4-element aligned", b, kv, i);
       }
@@ -552,6 +579,7 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
   std::vector<char> full_k((size_t)B * Hkv * fcap * D * es, 0), full_v((size_t)B * Hkv * ftiles * 32 * D * es, 0);
   std::vector<char> sum_k((size_t)B * Hkv * cap * D * es, 0), rho(sum_k.size(), 0);
   std::vector<char> sum_v((size_t)B * Hkv * stiles * 32 * D * es, 0);
+  std::vector<float> key_scale((size_t)B * Hkv * cap, 0.0f);
   // value rows live in 32-entry tiles, each stored transposed: (e, j) -> ((e/32)*D + j)*32 + e%32
   auto vt_index = [D](int64_t e, int j) { return ((e / 32) * D + j) * 32 + e % 32; };
   const bool on_host = c->factors_on_host != 0;
@@ -639,52 +667,75 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
         store(sum_k.data(), dt, (int64_t)srow + j, kbar[j]);
         store(sum_v.data(), dt, svbase + vt_index(i, j), vbar[j]);
       }
-      // rank-r factors of [K_body | V_body]
-      const int n2 = 2 * D;
-      M.assign((size_t)L * n2, 0.0);
-      for (int t = 0; t < L; ++t)
-        for (int j = 0; j < D; ++j) {
-          M[(size_t)t * n2 + j] = fetch(kb, dt, (int64_t)(t0 + t) * D + j);
-          M[(size_t)t * n2 + D + j] = fetch(vb, dt, (int64_t)(t0 + t) * D + j);
-        }
-      Vc.resize((size_t)L * L);
-      sig.resize(L);
-      perm.resize(L);
-      jacobi_svd(L, n2, M.data(), Vc.data(), sig.data(), perm.data());
+      key_scale[g * cap + i] = nn > 0 ? (float)(1.0 / nn) : 0.0f;
+      // rank-r factors: one basis of [K_body | V_body], or separate bases of
+      // K_body (part 0) and V_body (part 1)
+      const bool sep = c->basis != 0;
       const int rk = s->rank_host[(size_t)b * cap + i];
-      const int rp = (rk + 7) & ~7;
+      const int rp = (rk + 7) & ~7, rq = (rk + 3) & ~3;
       const size_t o = g * cap + i;
       const int64_t fbase = s->fac_off_host[o];
       const int64_t gbase = s->sg_off_host[o];
       const float* gt = gate + (g * cap + i) * (size_t)gate_stride;
-      for (int j = 0; j < rk; ++j) {
-        const int src = perm[j];
-        const double* u = Vc.data() + (size_t)src * L;  // column src of U
-        int imax = 0;
-        for (int t = 1; t < L; ++t)
-          if (std::fabs(u[t]) > std::fabs(u[imax])) imax = t;
-        const double sgn = u[imax] < 0 ? -1.0 : 1.0;
-        for (int t = 0; t < L; ++t) store(fac_dst, dt, fbase + fac_u_index(rk, rp, D, t, j), sgn * u[t]);
-        const double sj = sig[j];
-        const double inv = sj > 0 ? sgn / sj : 0.0;
-        const double* wrow = M.data() + (size_t)src * n2;
-        for (int col = 0; col < D; ++col) {
-          store(fac_dst, dt, fbase + fac_vk_index(D, j, col), wrow[col] * inv);
-          store(fac_dst, dt, fbase + fac_wv_index(L, rk, rp, D, col, j), wrow[D + col] * inv);
+      for (int part = 0; part < (sep ? 2 : 1); ++part) {
+        const int n = sep ? D : 2 * D;
+        M.assign((size_t)L * n, 0.0);
+        for (int t = 0; t < L; ++t)
+          for (int j = 0; j < D; ++j) {
+            const double kx = fetch(kb, dt, (int64_t)(t0 + t) * D + j), vx = fetch(vb, dt, (int64_t)(t0 + t) * D + j);
+            if (sep) {
+              M[(size_t)t * n + j] = part == 0 ? kx : vx;
+            } else {
+              M[(size_t)t * n + j] = kx;
+              M[(size_t)t * n + D + j] = vx;
+            }
+          }
+        Vc.resize((size_t)L * L);
+        sig.resize(L);
+        perm.resize(L);
+        jacobi_svd(L, n, M.data(), Vc.data(), sig.data(), perm.data());
+        auto u_at = [&](int t, int j) {
+          return part == 0 ? fac_u_index(rk, rp, D, t, j) : fac_uv_index(L, rk, rp, D, t, j);
+        };
+        for (int j = 0; j < rk; ++j) {
+          const int src = perm[j];
+          const double* u = Vc.data() + (size_t)src * L;  // column src of U
+          int imax = 0;
+          for (int t = 1; t < L; ++t)
+            if (std::fabs(u[t]) > std::fabs(u[imax])) imax = t;
+          const double sgn = u[imax] < 0 ? -1.0 : 1.0;
+          for (int t = 0; t < L; ++t) store(fac_dst, dt, fbase + u_at(t, j), sgn * u[t]);
+          const double sj = sig[j];
+          const double inv = sj > 0 ? sgn / sj : 0.0;
+          const double* wrow = M.data() + (size_t)src * n;
+          for (int col = 0; col < D; ++col) {
+            if (!sep || part == 0) store(fac_dst, dt, fbase + fac_vk_index(D, j, col), wrow[col] * inv);
+            if (!sep) store(fac_dst, dt, fbase + fac_wv_index(L, rk, rp, D, col, j), wrow[D + col] * inv);
+            if (sep && part == 1) store(fac_dst, dt, fbase + fac_wv_index(L, rk, rp, D, col, j, true), wrow[col] * inv);
+          }
+          sg_dst[gbase + 2 * part * rq + j] = (float)sj;
+          sg_dst[gbase + 2 * part * rq + rq + j] = gt[j];
         }
-        sg_dst[gbase + j] = (float)sj;
-        sg_dst[gbase + ((rk + 3) & ~3) + j] = gt[j];
-      }
-      for (int j = rk; j < rp; ++j) {
-        for (int t = 0; t < L; ++t) store(fac_dst, dt, fbase + fac_u_index(rk, rp, D, t, j), 0.0);
-        for (int col = 0; col < D; ++col) store(fac_dst, dt, fbase + fac_wv_index(L, rk, rp, D, col, j), 0.0);
-      }
-      for (int j = rk; j < ((rk + 3) & ~3); ++j) {
-        sg_dst[gbase + j] = 0.0f;
-        sg_dst[gbase + ((rk + 3) & ~3) + j] = 0.0f;
+        for (int j = rk; j < rp; ++j) {
+          for (int t = 0; t < L; ++t) store(fac_dst, dt, fbase + u_at(t, j), 0.0);
+          if (!sep || part == 1)
+            for (int col = 0; col < D; ++col) store(fac_dst, dt, fbase + fac_wv_index(L, rk, rp, D, col, j, sep), 0.0);
+        }
+        for (int j = rk; j < rq; ++j) {
+          sg_dst[gbase + 2 * part * rq + j] = 0.0f;
+          sg_dst[gbase + 2 * part * rq + rq + j] = 0.0f;
+        }
       }
     }
   });
+
+  // fold matrices M = P^T P of the folded routing, accumulated over the rows
+  // of P in order (each product and sum rounded in fp64)
+  std::vector<double> fold;
+  if (s->fold) {
+    fold.assign((size_t)Hkv * D * D, 0.0);
+    for (int kv = 0; kv < Hkv; ++kv) fold_matrix(route_proj + (size_t)kv * D * D, D, fold.data() + (size_t)kv * D * D);
+  }
 
   auto up = [&](const void* dst, const void* src, size_t bytes) -> hipError_t {
     return hipMemcpyAsync(const_cast<void*>(dst), src, bytes, hipMemcpyHostToDevice, stream);
@@ -697,7 +748,9 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
   HIP_OR_FAIL(up(s->full_v, full_v.data(), full_v.size()));
   HIP_OR_FAIL(up(s->sum_k, sum_k.data(), sum_k.size()));
   HIP_OR_FAIL(up(s->sum_v, sum_v.data(), sum_v.size()));
-  HIP_OR_FAIL(up(s->rho, rho.data(), rho.size()));
+  if (s->rho) HIP_OR_FAIL(up(s->rho, rho.data(), rho.size()));
+  if (s->key_scale) HIP_OR_FAIL(up(s->key_scale, key_scale.data(), key_scale.size() * sizeof(float)));
+  if (s->fold) HIP_OR_FAIL(up(s->fold, fold.data(), fold.size() * sizeof(double)));
   if (!on_host) {
     HIP_OR_FAIL(up(s->fac, fac_tmp.data(), fac_tmp.size()));
     HIP_OR_FAIL(up(s->sg, sg_tmp.data(), sg_tmp.size() * sizeof(float)));
@@ -710,10 +763,17 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
 // 256-span tile (all uint32, zero between calls).
 static int32_t route_tiles_cap(const sekv_spans* s) { return std::max(1, (s->seg_cap + kRouteThreads - 1) / kRouteThreads); }
 
-size_t sekv_route_workspace_bytes(const sekv_config* c, const sekv_spans* s) {
-  if (check_config(c) != SEKV_OK || !s) return 0;
+// Folded routing adds the folded queries [B][Hq][d] f32 after them.
+static size_t route_words_bytes(const sekv_config* c, const sekv_spans* s) {
   const size_t BG = (size_t)c->batch * c->n_kv_heads;
   return align_up(BG * (1 + (size_t)route_tiles_cap(s)) * sizeof(uint32_t));
+}
+
+size_t sekv_route_workspace_bytes(const sekv_config* c, const sekv_spans* s) {
+  if (check_config(c) != SEKV_OK || !s) return 0;
+  size_t n = route_words_bytes(c, s);
+  if (c->route_keys) n += align_up((size_t)c->batch * c->n_q_heads * c->head_dim * sizeof(float));
+  return n;
 }
 
 namespace {
@@ -738,15 +798,20 @@ sekv_status route_launch(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* 
   for (int b = 0; b < c->batch; ++b) { a.n_seg[b] = s->n_seg_host[b]; mx = std::max(mx, s->n_seg_host[b]); }
   a.nblk = std::max(1, (mx + kRouteThreads - 1) / kRouteThreads);
   a.nblk_cap = route_tiles_cap(s);
-  a.q = q; a.theta = theta; a.rho = s->rho;
+  a.q = q; a.theta = theta; a.rho = c->route_keys ? s->sum_k : s->rho;
   const size_t BG = (size_t)c->batch * c->n_kv_heads;
   a.ticket = static_cast<uint32_t*>(ws);
   a.status = a.ticket + BG;
+  a.fold = c->route_keys;
+  a.key_scale = s->key_scale;
+  a.foldm = s->fold;
+  a.qfold = c->route_keys ? reinterpret_cast<float*>(static_cast<char*>(ws) + route_words_bytes(c, s)) : nullptr;
   a.exp_list = exp_list; a.exp_mask = exp_mask; a.exp_count = exp_count;
   HIP_OR_FAIL(hipSetDevice(ctx->device));
   // tiles in dispatch order when the whole grid is resident at once, tickets otherwise
   const int G = c->n_q_heads / c->n_kv_heads;
-  int& resident = ctx->route_resident[c->dtype == SEKV_BF16][c->head_dim == 128][G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3];
+  int& resident =
+      ctx->route_resident[c->dtype == SEKV_BF16][c->head_dim == 128][G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3][c->route_keys];
   if (resident == 0) HIP_OR_FAIL(route_resident_blocks(a, ctx->device, &resident));
   a.use_ticket = (int64_t)a.nblk * c->n_kv_heads * c->batch > resident ? 1 : 0;
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -790,6 +855,7 @@ sekv_status sekv_reconstruct(sekv_ctx* ctx, const sekv_config* c, const sekv_spa
   if (!exp_list || !exp_count || !tok_off || !k_out || !v_out) return fail(SEKV_EINVAL, "sekv_reconstruct: a pointer argument is NULL");
   ReconArgs a{};
   a.dtype = c->dtype; a.B = c->batch; a.Hkv = c->n_kv_heads; a.D = c->head_dim; a.seg_cap = s->seg_cap; a.T = c->n_ctx;
+  a.sep = c->basis;
   a.seg_off = s->seg_off; a.rank = s->rank; a.fac_off = s->fac_off; a.sg_off = s->sg_off; a.fac = s->fac; a.sg = s->sg;
   a.exp_list = exp_list; a.exp_count = exp_count; a.tok_off = tok_off; a.k_out = k_out; a.v_out = v_out;
   HIP_OR_FAIL(hipSetDevice(ctx->device));
@@ -811,6 +877,7 @@ void make_plan(const sekv_config* c, const sekv_spans* s, int32_t split_entries,
   AttendArgs& a = p.a;
   a.dtype = c->dtype; a.B = B; a.Hq = c->n_q_heads; a.Hkv = Hkv; a.D = D;
   a.seg_cap = s->seg_cap; a.full_cap = s->full_cap;
+  a.sep = c->basis;
   int ntiles = 1;  // 32-entry tiles of the longest (b, kv) stream: full-res tiles + summary tiles
   for (int b = 0; b < B; ++b) {
     a.n_full[b] = s->n_full_host[b];
@@ -980,14 +1047,14 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
       const int L = so[S + 1] - so[S] - 1;
       const int r = s->rank_host[(size_t)b * cap + S];
       const int rp = (r + 7) & ~7;
-      const int64_t fe = fac_block_elems(L, r, rp, D);
+      const int64_t fe = fac_block_elems(L, r, rp, D, c->basis != 0);
       const size_t o = (size_t)g * cap + S;
       ents.push_back({static_cast<const char*>(s->fac) + s->fac_off_host[o] * es, fe * es, fo});
       h_soff[BG + 2 * (ne + j)] = fo;
       h_soff[BG + 2 * (ne + j) + 1] = go;
-      std::memcpy(h_sg + go, s->sg + s->sg_off_host[o], sg_entry_elems(r) * sizeof(float));
+      std::memcpy(h_sg + go, s->sg + s->sg_off_host[o], sg_entry_elems(r, c->basis != 0) * sizeof(float));
       fo += fe;
-      go += sg_entry_elems(r);
+      go += sg_entry_elems(r, c->basis != 0);
     }
     ne += cnt;
   }

@@ -29,6 +29,10 @@ struct RouteArgs {
   const void* rho;           // [B][Hkv][seg_cap][D]
   uint32_t* ticket;          // [B*Hkv] workspace, zero between calls
   uint32_t* status;          // [B*Hkv][nblk_cap] workspace, zero between calls
+  int fold;                  // 1: folded routing (keys = kbar in `rho`, scaled by key_scale)
+  const float* key_scale;    // [B][Hkv][seg_cap]
+  const double* foldm;       // [Hkv][D][D]
+  float* qfold;              // [B][Hq][D] workspace: folded queries
   int32_t* exp_list;         // [B][Hkv][seg_cap]
   uint8_t* exp_mask;         // [B][Hkv][seg_cap]
   int32_t* exp_count;        // [B][Hkv]
@@ -45,6 +49,7 @@ struct AttendArgs {
   int n_a5_wg;               // workgroups (one wave each) of the expanded-span kernel
   int n_fx_wg;               // workgroups (four expanded-span waves each) of the fused launch
   int max_rank;              // largest span rank (selects the expanded-span kernel's register tiling)
+  int sep;                   // 1: separate key and value bases (factor block and sigma|gate layout)
   int n_a4_wg;               // workgroups of the full-res/summary kernel
   float qscale;              // log2(e) / sqrt(D)
   const void* q;
@@ -64,6 +69,7 @@ struct AttendArgs {
 
 struct ReconArgs {
   int dtype;
+  int sep;                   // 1: separate key and value bases
   int B, Hkv, D, seg_cap;
   const int32_t* seg_off; const int32_t* rank;
   const int64_t* fac_off; const int64_t* sg_off;

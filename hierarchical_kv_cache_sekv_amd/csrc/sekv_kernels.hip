@@ -233,7 +233,31 @@ __device__ __forceinline__ uint32_t atomic_load_dev(const uint32_t* p) {
 // (coalesced 16-byte loads, 8 lanes per row), padded to a 144-byte row stride
 // so that each lane then reads its own row without bank conflicts; every
 // pass's loads are issued up front.
-template <typename T, int D, int G>
+// Folded routing (route_keys = 1): the query is folded once per call,
+// q'[b][h][j] = fl32(sum over m of fold[kv][j][m] * q[b][h][m]), a sequential
+// fp64 chain in m with every product and sum rounded separately (one thread
+// per output element).
+template <typename T>
+__global__ __launch_bounds__(256) void fold_query_kernel(const RouteArgs a) {
+#pragma clang fp contract(off)
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int D = a.D, G = a.Hq / a.Hkv;
+  if (idx >= a.B * a.Hq * D) return;
+  const int j = idx % D, bh = idx / D, h = bh % a.Hq;
+  const double* M = a.foldm + ((size_t)(h / G) * D + j) * D;
+  const T* q = static_cast<const T*>(a.q) + (size_t)bh * D;
+  double acc = 0.0;
+  for (int m = 0; m < D; ++m) {
+    const double prod = M[m] * (double)load1(q + m);
+    acc = acc + prod;
+  }
+  a.qfold[idx] = (float)acc;
+}
+
+// FOLD: the keys are the attention summary keys kbar and the query the folded
+// one; the chain's result is then scaled by the span's key scale,
+// z' = fl32(z * key_scale).
+template <typename T, int D, int G, bool FOLD>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a) {
   constexpr int EPP = kRouteRowBytes / (int)sizeof(T);   // elements of a row per pass
   constexpr int NP = D / EPP;
@@ -252,8 +276,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a)
   }
   if ((int)blockIdx.x >= nb) return;
   if (tid == 0) s_ticket = a.use_ticket ? (int)atomic_add_dev(a.ticket + g, 1u) : (int)blockIdx.x;
-  const T* q = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
-  for (int i = tid; i < G * D; i += kRouteThreads) qs[i] = load1(q + i);
+  if constexpr (FOLD) {
+    const float* qf = a.qfold + ((size_t)b * a.Hq + (size_t)kv * G) * D;
+    for (int i = tid; i < G * D; i += kRouteThreads) qs[i] = qf[i];
+  } else {
+    const T* q = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
+    for (int i = tid; i < G * D; i += kRouteThreads) qs[i] = load1(q + i);
+  }
   float th[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) th[gi] = a.theta[(size_t)b * a.Hq + kv * G + gi];
@@ -267,6 +296,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a)
   float z[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) z[gi] = 0.0f;
+  const float ksc = FOLD && tid < nrow ? a.key_scale[(size_t)g * a.seg_cap + S0 + tid] : 0.0f;
   uint4 v[NP][8];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
@@ -310,6 +340,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a)
           }
         }
       }
+    }
+  }
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+#pragma clang fp contract(off)
+      z[gi] = z[gi] * ksc;
     }
   }
   // this tile's expanded spans, their order within the tile, and the tile count
@@ -772,20 +809,23 @@ struct ItemMeta {
   int L, r, bits;
   uint64_t sga, fa;   // global addresses of the sg entry and the factor block
 };
-// Region `kind` of span i: 0 / 2 sigma|gate, 1 Vh_K | U, 3 U | W_V.
+// Region `kind` of span i: 0 / 2 sigma|gate, 1 Vh_K | U, 3 U | W_V.  With
+// separate key and value bases (sep) the block is Vh_K | U_K | U_V | W_V and
+// the sigma|gate entry sigma_K | gate | sigma_V | gate: region 2 is the second
+// half of the entry and region 3 is U_V | W_V.
 template <typename T, int D>
-__device__ __forceinline__ void region_of(const ItemMeta& m, int i, int kind, uint64_t& base, uint32_t& size) {
+__device__ __forceinline__ void region_of(const ItemMeta& m, int i, int kind, bool sep, uint64_t& base, uint32_t& size) {
   constexpr uint32_t ES = sizeof(T);
   const int L = __builtin_amdgcn_readlane(m.L, i), r = __builtin_amdgcn_readlane(m.r, i);
   const uint32_t rp = (uint32_t)((r + 7) & ~7), rq = (uint32_t)((r + 3) & ~3);
   if ((kind & 1) == 0) {
-    base = readlane64(m.sga, i);
+    base = readlane64(m.sga, i) + (kind == 2 && sep ? 8u * rq : 0u);
     size = 8u * rq;
   } else if (kind == 1) {
     base = readlane64(m.fa, i);
     size = ES * ((uint32_t)r * D + (uint32_t)L * rp);
   } else {
-    base = readlane64(m.fa, i) + ES * (uint64_t)((uint32_t)r * D);
+    base = readlane64(m.fa, i) + ES * (uint64_t)((uint32_t)r * D + (sep ? (uint32_t)L * rp : 0u));
     size = ES * ((uint32_t)L * rp + D * rp);
   }
 }
@@ -796,6 +836,7 @@ __device__ __forceinline__ void region_of(const ItemMeta& m, int i, int kind, ui
 // Past the last region the final chunk is repeated (never read from the ring).
 struct RegionCursor {
   int i, kind, ca, cb, n;
+  bool sep;
   uint32_t cmask;
   uint32_t off, size;
   uint64_t base;
@@ -823,7 +864,7 @@ __device__ __forceinline__ void cursor_next(RegionCursor& c, const ItemMeta& m) 
     c.off -= 1024u;
     return;
   }
-  region_of<T, D>(m, c.i, c.kind, c.base, c.size);
+  region_of<T, D>(m, c.i, c.kind, c.sep, c.base, c.size);
   c.off = 0;
 }
 __device__ __forceinline__ uint64_t cursor_addr(const RegionCursor& c, int lane) {
@@ -941,13 +982,14 @@ __device__ __forceinline__ void role_expanded(const AttendArgs& a, int wid, int 
     }
     RegionCursor cur;
     cur.n = n;
+    cur.sep = a.sep != 0;
     cur.cmask = cmask;
     cur.ca = 0;
     cur.cb = chunk_end(cmask, 0);
     cur.i = 0;
     cur.kind = 0;
     cur.off = 0;
-    region_of<T, D>(im, 0, 0, cur.base, cur.size);
+    region_of<T, D>(im, 0, 0, cur.sep, cur.base, cur.size);
     uint4 stg[K];
 #pragma unroll
     for (int jj = 0; jj < K; ++jj) {
@@ -1322,8 +1364,9 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
     const int r = a.rank[(size_t)b * a.seg_cap + S];
     const int rp = (r + 7) & ~7;
     const T* Vk = static_cast<const T*>(a.fac) + a.fac_off[(size_t)g * a.seg_cap + S];  // key part [r][D], rotated groups
-    const T* Ub = Vk + (size_t)r * D;             // U [L][rp]
-    const T* Wv = Ub + (size_t)L * rp;            // value part, 16-rank column blocks [D][wk]
+    const T* Ub = Vk + (size_t)r * D;             // U [L][rp] (the key basis U_K with separate bases)
+    const T* Uv = a.sep ? Ub + (size_t)L * rp : Ub;   // U of the values
+    const T* Wv = Uv + (size_t)L * rp;            // value part, 16-rank column blocks [D][wk]
     const int rq = (r + 3) & ~3;
     const float* sgp = a.sg + a.sg_off[(size_t)g * a.seg_cap + S];
     const int row0 = a.tok_off[(size_t)g * (a.seg_cap + 1) + j];
@@ -1332,13 +1375,14 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
       for (int k = 0; k < r; ++k) {
-        const float w = load1(Ub + (size_t)t * rp + k) * (sgp[k] * sgp[rq + k]);
+        const float wkey = load1(Ub + (size_t)t * rp + k) * (sgp[k] * sgp[rq + k]);
+        const float wval = a.sep ? load1(Uv + (size_t)t * rp + k) * (sgp[2 * rq + k] * sgp[3 * rq + k]) : wkey;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const int colj = lane + 64 * c;
           const int kg = k >> 4, wk = min(16, rp - 16 * kg);
-          acc[c] += w * (colj < D ? load1(Vk + (size_t)k * D + (((colj >> 3) + k) % (D / 8)) * 8 + (colj & 7))
-                                  : load1(Wv + (size_t)kg * 16 * D + (size_t)(colj - D) * wk + (k & 15)));
+          acc[c] += colj < D ? wkey * load1(Vk + (size_t)k * D + (((colj >> 3) + k) % (D / 8)) * 8 + (colj & 7))
+                             : wval * load1(Wv + (size_t)kg * 16 * D + (size_t)(colj - D) * wk + (k & 15));
         }
       }
       const size_t orow = ((size_t)g * a.T + row0 + t) * D;
@@ -1413,18 +1457,30 @@ hipError_t route_scratch_address(int device, void** ptr) {
   return hipSuccess;
 }
 
-// Timed launches: with a start/stop event pair (both non-null) the events are
-// recorded at the start and the end of the kernel's own execution.
+// Timed launches: a non-null start (stop) event is recorded at the start (the
+// end) of the kernel's own execution.
 #define SEKV_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, S, EV0, EV1, ARG)                                  \
   do {                                                                                             \
-    if ((EV0) && (EV1)) hipExtLaunchKernelGGL(KERNEL, dim3(GRID), dim3(BLOCK), SHMEM, S, EV0, EV1, 0, ARG); \
+    if ((EV0) || (EV1)) hipExtLaunchKernelGGL(KERNEL, dim3(GRID), dim3(BLOCK), SHMEM, S, EV0, EV1, 0, ARG); \
     else KERNEL<<<dim3(GRID), dim3(BLOCK), SHMEM, S>>>(ARG);                                       \
   } while (0)
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int G = a.Hq / a.Hkv;
   dim3 grid(a.nblk, a.Hkv, a.B);
-  SEKV_DISPATCH(a.dtype, a.D, G, ({ SEKV_LAUNCH((route_kernel<TT, DD, GG>), grid, kRouteThreads, 0, s, ev0, ev1, a); }));
+  if (a.fold) {
+    const int n = a.B * a.Hq * a.D;
+    hipEvent_t none = nullptr;
+    if (a.dtype == 0) SEKV_LAUNCH(fold_query_kernel<float>, (n + 255) / 256, 256, 0, s, ev0, none, a);
+    else SEKV_LAUNCH(fold_query_kernel<bf16raw>, (n + 255) / 256, 256, 0, s, ev0, none, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SEKV_DISPATCH(a.dtype, a.D, G,
+                  ({ SEKV_LAUNCH((route_kernel<TT, DD, GG, true>), grid, kRouteThreads, 0, s, none, ev1, a); }));
+  } else {
+    SEKV_DISPATCH(a.dtype, a.D, G,
+                  ({ SEKV_LAUNCH((route_kernel<TT, DD, GG, false>), grid, kRouteThreads, 0, s, ev0, ev1, a); }));
+  }
   return hipGetLastError();
 }
 
@@ -1433,7 +1489,10 @@ hipError_t route_resident_blocks(const RouteArgs& a, int device, int* blocks) {
   int per_cu = 0;
   hipError_t e = hipSuccess;
   SEKV_DISPATCH(a.dtype, a.D, G,
-                (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, route_kernel<TT, DD, GG>, kRouteThreads, 0)));
+                (e = a.fold ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, route_kernel<TT, DD, GG, true>,
+                                                                            kRouteThreads, 0)
+                            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, route_kernel<TT, DD, GG, false>,
+                                                                            kRouteThreads, 0)));
   if (e != hipSuccess) return e;
   int cus = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);

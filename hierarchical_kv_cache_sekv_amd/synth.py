@@ -50,6 +50,10 @@ class Workload:
     factors_on_host: bool = False
     boundary_quantile: float = 0.90
     lowrank_rank: int = 4
+    # reading variants (the defaults are the default readings)
+    rank_cap: str = "full"      # "full": r <= L; "half": r <= ceil(L / 2)
+    basis: str = "joint"        # "joint": one basis of [K | V]; "separate": K and V bases
+    route_keys: str = "rho"     # "rho": route on rho; "folded": (P^T P q) . kbar / |P kbar|
 
     @property
     def group(self) -> int:

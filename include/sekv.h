@@ -81,6 +81,11 @@ typedef struct sekv_config {
   int32_t max_span;        /* hi: a body of hi tokens forces the next head          */
   int32_t dtype;           /* sekv_dtype of K/V, q, summaries, rho, factors         */
   int32_t factors_on_host; /* 1: fac/sg pools are pinned host memory              */
+  /* Reading variants (0 = the default reading): */
+  int32_t rank_cap;        /* 0: r_i <= L_i; 1: r_i <= ceil(L_i / 2)                */
+  int32_t basis;           /* 0: one basis for [K | V]; 1: separate K and V bases   */
+  int32_t route_keys;      /* 0: route on rho; 1: route on kbar with key_scale and
+                              the fold matrix (P^T P q) . kbar / |P kbar|         */
 } sekv_config;
 
 /*
@@ -104,6 +109,9 @@ typedef struct sekv_config {
  *       q . rho equals the routing-space score of the projected query. [de-2/3]
  *   rank [B][seg_cap] int32: r_i, 1 <= r_i <= min(L_i, 2d), shared by all KV
  *       heads of the span.  [de-2], [zh-2] (adaptive rank budget).
+ *   key_scale [B][Hkv][seg_cap] f32 (route_keys = 1): 1 / |P kbar| of each
+ *       span (0 if the norm is 0), kbar the unrounded summary key.
+ *   fold [Hkv][d][d] f64 (route_keys = 1): M = P^T P of each KV head.
  *   fac pool (dtype): for span (b, kv, i) a block at element offset
  *       fac_off[b][kv][i] (a multiple of 8) holding, with rp = ceil(r_i/8)*8:
  *       the key part of the right singular vectors Vh_K [r_i][d], where row
@@ -114,10 +122,15 @@ typedef struct sekv_config {
  *       stored as column blocks of 16 ranks: block g = k / 16 of width
  *       wk = min(16, rp - 16 g) is [d][wk] row-major at block offset 16 g d
  *       (padding zero).  Block size r_i*d + L_i*rp + d*rp elements.
+ *       With basis = 1 the block is Vh_K [r_i][d] (rotated as above) | U_K
+ *       [L_i][rp] | U_V [L_i][rp] | W_V blocks of the value basis, size
+ *       r_i*d + 2*L_i*rp + d*rp; keys are U_K diag(sigma_K*gate) Vh_K and
+ *       values U_V diag(sigma_V*gate) W_V^T.
  *   sg pool (float32): for span (b, kv, i) an entry at offset sg_off[b][kv][i]
  *       (a multiple of 4): sigma[rq] then gate[rq], rq = ceil(r_i/4)*4,
  *       padding zero.  Token keys of the span are U diag(sigma*gate) Vh_K,
- *       token values U diag(sigma*gate) W_V^T.
+ *       token values U diag(sigma*gate) W_V^T.  With basis = 1 the entry is
+ *       sigma_K[rq] | gate[rq] | sigma_V[rq] | gate[rq] (4*rq floats).
  *       [abstract], [de-2], [zh-2].
  *
  * Device arrays are required for every field; the *_host fields are host
@@ -146,6 +159,8 @@ typedef struct sekv_spans {
   const int32_t* rank_host;     /* [B][seg_cap] host (host-resident mode)   */
   const int64_t* fac_off_host;  /* [B][Hkv][seg_cap] host                    */
   const int64_t* sg_off_host;   /* [B][Hkv][seg_cap] host                    */
+  const float* key_scale;       /* [B][Hkv][seg_cap] device (route_keys = 1) */
+  const double* fold;           /* [Hkv][d][d] device (route_keys = 1)       */
 } sekv_spans;
 
 typedef struct sekv_ctx sekv_ctx;
@@ -168,7 +183,9 @@ sekv_status sekv_capacities(const sekv_config* cfg, int32_t* seg_cap, int32_t* f
  * head if body == max_span, or if surprisal[t] > boundary_thr[b] and
  * body >= min_span and at least min_span tokens remain before the recent
  * window; a last head with an empty body is returned to the tail.  Rank
- * r_i = min(rank_req[b][i], L_i, 2d).
+ * r_i = min(rank_req[b][i], L_i, 2d), with ceil(L_i / 2) in place of L_i when
+ * cfg->rank_cap = 1 and d in place of 2d when cfg->basis = 1 (each part of
+ * separate bases is L_i x d).
  *   surprisal [B][T], boundary_thr [B], rank_req [B][seg_cap]: host, read.
  *   Outputs (host, written): n_seg [B], n_full [B], seg_off [B][seg_cap+1]
  *   (unused tail entries set to the tail start), rank [B][seg_cap] (0 past
@@ -190,8 +207,10 @@ sekv_status sekv_plan_spans(const sekv_config* cfg, const float* surprisal, cons
  * fac_off_host, sg_off_host) must hold sekv_plan_spans output; every device
  * array (and the pools, pinned host when factors_on_host) is written.
  * Summaries: weights s_t / sum s over the body (uniform if the sum is 0).
- * Routing key: rho = P^T r/|r|, r = P kbar (0 if |r| = 0).  Factors: rank-r_i
- * truncated SVD of [K_body | V_body] (one-sided Jacobi, fp64), sign fixed so
+ * Routing key: rho = P^T r/|r|, r = P kbar (0 if |r| = 0); with route_keys = 1
+ * instead key_scale = 1/|r| and fold = P^T P (rho may then be NULL).
+ * Factors: rank-r_i truncated SVD of [K_body | V_body] (basis 0) or of K_body
+ * and V_body separately (basis 1; one-sided Jacobi, fp64), sign fixed so
  * each U column's largest-magnitude entry is positive.  Stored values are fp64
  * rounded to f32 (then to bf16, nearest-even).  Uses host threads.
  * Errors: SEKV_EINVAL / SEKV_ESHAPE / SEKV_ECAPACITY (pool sizes) / SEKV_EHIP.
@@ -210,7 +229,11 @@ size_t sekv_route_workspace_bytes(const sekv_config* cfg, const sekv_spans* span
  * query head h, span i: z > theta[b][h] (strict), where z = sum over
  * j = 0..d-1 of q[b][h][j] * rho[b][kv][i][j], evaluated in float32 in that
  * order with every product and sum rounded separately (sigma(z) > tau is
- * z > logit(tau); theta may be +/-inf).
+ * z > logit(tau); theta may be +/-inf).  With route_keys = 1 the score is
+ * z' = fl32(z * key_scale[b][kv][i]) with z the same float32 chain over the
+ * folded query q'[h][j] and kbar (sum_k) instead of q and rho, where
+ * q'[h][j] = fl32(sum over m of fold[kv][j][m] * q[h][m]), a sequential fp64
+ * chain in m with every product and sum rounded separately.
  *   q [B][Hq][d] dtype, theta [B][Hq] f32: device, read.
  *   exp_list [B][Hkv][seg_cap] int32: ascending span indices that any head of
  *     the group expands (first exp_count entries valid).

@@ -35,10 +35,18 @@ class Prepared:
         return self.w.group
 
 
-def scores(cache, q_b, b, group):
-    """Canonical float32 scores of all heads of sequence b: [Hq][n_seg]."""
+def scores(cache, q_b, b, group, route_keys="rho"):
+    """Canonical float32 scores of all heads of sequence b: [Hq][n_seg]; with
+    route_keys="folded" the folded score on the summary key."""
     Hq = q_b.shape[0]
-    parts = [O.route_scores(q_b[kv * group:(kv + 1) * group], cache.rho[b][kv]) for kv in range(Hq // group)]
+    parts = []
+    for kv in range(Hq // group):
+        qh = q_b[kv * group:(kv + 1) * group]
+        if route_keys == "folded":
+            parts.append(O.route_scores_folded(O.fold_query(cache.fold[kv], qh), cache.sum_k[b][kv],
+                                               cache.key_scale[b][kv]))
+        else:
+            parts.append(O.route_scores(qh, cache.rho[b][kv]))
     return np.concatenate(parts, axis=0)
 
 
@@ -51,7 +59,8 @@ def prepare(w, steps, *, full_rank=False, theta_mode="calibrated", calib_steps=N
     x = synth.make_inputs(w, n_steps=n_steps, full_rank_unit_gates=full_rank)
     log(f"{w.name}: inputs {time.time() - t0:.1f}s")
     cache = O.build_cache(x.k, x.v, x.surprisal, x.boundary_thr, x.route_proj, x.rank_req, x.gate,
-                          n_sink=w.n_sink, n_recent=w.n_recent, lo=w.min_span, hi=w.max_span, dtype=w.dtype)
+                          n_sink=w.n_sink, n_recent=w.n_recent, lo=w.min_span, hi=w.max_span, dtype=w.dtype,
+                          rank_cap=w.rank_cap, basis=w.basis)
     log(f"{w.name}: oracle cache {time.time() - t0:.1f}s, n_seg={[cache.n_seg(b) for b in range(w.batch)]}")
     B, Hq, G = w.batch, w.n_q_heads, w.group
     theta = np.empty((B, Hq), np.float32)
@@ -62,12 +71,12 @@ def prepare(w, steps, *, full_rank=False, theta_mode="calibrated", calib_steps=N
             theta[b] = -np.inf
         else:
             cs = range(calib_steps if calib_steps is not None else n_steps)
-            z = np.stack([scores(cache, x.q[st, b], b, G) for st in cs])
+            z = np.stack([scores(cache, x.q[st, b], b, G, w.route_keys) for st in cs])
             f = float(x.expand_frac[b]) if frac is None else frac
             theta[b] = synth.calibrate_theta(z, f, G)
     decisions = []
     for st in steps:
-        decisions.append([scores(cache, x.q[st, b], b, G) > theta[b][:, None] for b in range(B)])
+        decisions.append([scores(cache, x.q[st, b], b, G, w.route_keys) > theta[b][:, None] for b in range(B)])
     log(f"{w.name}: thresholds and decisions {time.time() - t0:.1f}s")
     if drop_kv:
         x.k = x.v = None

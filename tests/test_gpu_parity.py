@@ -34,6 +34,16 @@ CASES = {
     "f32-len1-spans": dict(wid=1, over=dict(n_ctx=700, min_span=1, max_span=1), steps=[0, 1]),
     "f32-no-spans": dict(wid=1, over=dict(n_ctx=69, n_recent=64, n_sink=4), steps=[0]),
     "bf16-one-span": dict(wid=2, over=dict(n_ctx=300, n_recent=200, n_sink=4, min_span=8, max_span=128), steps=[0]),
+    # reading variants
+    "bf16-rank-cap-half": dict(wid=5, over=dict(n_ctx=4096, batch=2, rank_cap="half"), steps=[0, 1]),
+    "bf16-separate-bases": dict(wid=5, over=dict(n_ctx=4096, batch=2, basis="separate"), steps=[0, 1]),
+    "bf16-folded-route": dict(wid=2, over=dict(n_ctx=4096, batch=2, route_keys="folded"), steps=[0, 1]),
+    "bf16-boundary-q97": dict(wid=2, over=dict(n_ctx=8192, boundary_quantile=0.97), steps=[0, 1]),
+    "f32-d64-all-variants": dict(wid=1, over=dict(n_ctx=3000, rank_cap="half", basis="separate",
+                                                  route_keys="folded"), steps=[0, 3]),
+    "bf16-separate-wide-rank": dict(wid=5, over=dict(n_ctx=2500, batch=2, n_q_heads=8, n_kv_heads=4, min_span=2,
+                                                     max_span=128, rank_lo=30, rank_hi=128, boundary_quantile=0.995,
+                                                     basis="separate"), steps=[0], frac=0.3),
 }
 
 _PREP = {}
@@ -210,12 +220,13 @@ def test_full_expansion_full_rank_equals_dense(ctx, dtype):
             assert err <= (2e-2 if dtype == "bf16" else 1e-4)
 
 
-def test_host_resident_factors_match_device_resident_bitwise(ctx):
+@pytest.mark.parametrize("basis", ["joint", "separate"])
+def test_host_resident_factors_match_device_resident_bitwise(ctx, basis):
     """Staged fetch (host gather + copy): same factor bits as the
     device-resident path, so the same output bits."""
     import torch
     from hierarchical_kv_cache_sekv_amd import binding as B
-    w = synth.workload(3, n_ctx=8192)
+    w = synth.workload(3, n_ctx=8192, basis=basis)
     p = prepare(w, [0, 1])
     dev_d = Device(p, factors_on_host=False)
     side = torch.cuda.Stream()
@@ -236,10 +247,11 @@ def test_host_resident_factors_match_device_resident_bitwise(ctx):
         ctx.set_fetch_mode(B.SEKV_FETCH_DIRECT)
 
 
-def test_reconstruct_matches_oracle(ctx):
+@pytest.mark.parametrize("basis", ["joint", "separate"])
+def test_reconstruct_matches_oracle(ctx, basis):
     import torch
     from hierarchical_kv_cache_sekv_amd import binding as B
-    w = synth.workload(2, n_ctx=3000, batch=2, rank_lo=1, rank_hi=40)
+    w = synth.workload(2, n_ctx=3000, batch=2, rank_lo=1, rank_hi=40, basis=basis)
     p = prepare(w, [0], frac=0.2)
     dev = Device(p)
     dev.route(ctx, 0)
@@ -257,8 +269,7 @@ def test_reconstruct_matches_oracle(ctx):
             assert to[b, kv, 0] == 0 and to[b, kv, n] == int(L[lst[b, kv, :n]].sum())
             for j in range(n):
                 S = int(lst[b, kv, j])
-                kh, vh = O.reconstruct(p.cache.U[b][kv][S], p.cache.sigma[b][kv][S], p.cache.gate[b][kv][S],
-                                       p.cache.Vh[b][kv][S], w.head_dim)
+                kh, vh = O.reconstruct_span(p.cache, b, kv, S)
                 r0 = int(to[b, kv, j])
                 worst = max(worst, float(np.abs(K[b, kv, r0:r0 + L[S]] - kh).max()),
                             float(np.abs(V[b, kv, r0:r0 + L[S]] - vh).max()))
@@ -346,14 +357,23 @@ def test_injected_gather_fault_leaves_out_untouched_and_context_usable(ctx):
         ctx.set_fetch_mode(B.SEKV_FETCH_DIRECT)
 
 
-def test_library_build_matches_oracle_build(ctx):
+@pytest.mark.parametrize("variant", ["default", "variants"])
+def test_library_build_matches_oracle_build(ctx, variant):
     """sekv_plan_spans + sekv_build_spans against the oracle's build: offsets
-    and ranks exact; summaries and routing keys within one storage rounding;
-    factors through their invariants (orthonormality, singular values,
-    reconstruction error = tail energy)."""
+    and ranks exact; summaries, routing keys and key scales within one storage
+    rounding; fold matrices within fp64 rounding; factors through their
+    invariants (orthonormality, singular values, reconstruction error = tail
+    energy), per part for separate bases."""
     import torch
     from hierarchical_kv_cache_sekv_amd import binding as B
-    for w in [synth.workload(1), synth.workload(2, n_ctx=4096, batch=2)]:
+    if variant == "default":
+        wls = [synth.workload(1), synth.workload(2, n_ctx=4096, batch=2)]
+    else:
+        wls = [synth.workload(1, rank_cap="half", basis="separate", route_keys="folded"),
+               synth.workload(2, n_ctx=4096, batch=2, basis="separate", route_keys="folded"),
+               synth.workload(5, n_ctx=4096, batch=1, rank_cap="half")]
+    for w in wls:
+        sep = w.basis == "separate"
         x = synth.make_inputs(w, n_steps=1)
         cfg = B.make_config(w)
         plan = B.plan_spans(cfg, x.surprisal, x.boundary_thr, x.rank_req)
@@ -364,21 +384,25 @@ def test_library_build_matches_oracle_build(ctx):
         B.build_spans(ctx, cache, kd, vd, x.surprisal, x.route_proj, x.gate)
         torch.cuda.synchronize()
         oc = O.build_cache(x.k, x.v, x.surprisal, x.boundary_thr, x.route_proj, x.rank_req, x.gate,
-                           n_sink=w.n_sink, n_recent=w.n_recent, lo=w.min_span, hi=w.max_span, dtype=w.dtype)
+                           n_sink=w.n_sink, n_recent=w.n_recent, lo=w.min_span, hi=w.max_span, dtype=w.dtype,
+                           rank_cap=w.rank_cap, basis=w.basis)
         rel = 2.0 ** -7 if w.dtype == "bf16" else 2.0 ** -22
         fk = cache.full_k.float().cpu().numpy()
         sk = cache.sum_k.float().cpu().numpy()
         sv = B.untile_values(cache.sum_v.float().cpu().numpy(), cache.seg_cap)
         fv = B.untile_values(cache.full_v.float().cpu().numpy(), cache.full_cap)
         rh = cache.rho.float().cpu().numpy()
-
+        ks = cache.key_scale.cpu().numpy()
+        fold = cache.fold.cpu().numpy()
+        for kv in range(w.n_kv_heads):
+            assert np.allclose(fold[kv], oc.fold[kv], rtol=1e-12, atol=1e-14)
         worst_recon = 0.0
+        utol = 0.05 if w.dtype == "bf16" else 1e-5
         for b in range(w.batch):
             n = oc.n_seg(b)
             assert int(plan.n_seg[b]) == n
             assert plan.seg_off[b, :n + 1].tolist() == oc.seg_off[b].tolist()
             assert plan.rank[b, :n].tolist() == oc.rank[b].tolist()
-            L = oc.span_len(b)
             for kv in range(w.n_kv_heads):
                 nf = len(oc.full_idx[b])
                 assert np.array_equal(fk[b, kv, :nf], oc.full_k[b][kv])
@@ -386,24 +410,29 @@ def test_library_build_matches_oracle_build(ctx):
                 for arr, ref in ((sk, oc.sum_k), (sv, oc.sum_v), (rh, oc.rho)):
                     r = ref[b][kv]
                     assert np.all(np.abs(arr[b, kv, :n] - r) <= rel * np.abs(r) + 1e-30)
+                assert np.allclose(ks[b, kv, :n], oc.key_scale[b][kv], rtol=2.0 ** -22, atol=0)
                 for i in range(0, n, max(1, n // 40)):
                     rk = int(plan.rank[b, i])
-                    U, sig, gt, Vh = B.read_factors(cache, b, kv, i)
-                    assert np.allclose(sig, oc.sigma[b][kv][i], rtol=1e-5, atol=1e-6)
-                    assert np.array_equal(gt, oc.gate[b][kv][i].astype(np.float32))
-                    utol = 0.05 if w.dtype == "bf16" else 1e-5
-                    assert np.allclose(U.T @ U, np.eye(rk), atol=utol)
-                    assert np.allclose(Vh @ Vh.T, np.eye(rk), atol=utol)
                     t0, t1 = oc.seg_off[b][i] + 1, oc.seg_off[b][i + 1]
-                    M = np.concatenate([x.k[b, kv, t0:t1], x.v[b, kv, t0:t1]], axis=1).astype(np.float64)
-                    R = (U * sig) @ Vh
-                    ko, vo = O.reconstruct(oc.U[b][kv][i], oc.sigma[b][kv][i], np.ones(rk), oc.Vh[b][kv][i],
-                                           w.head_dim)
-                    Ro = np.concatenate([ko, vo], axis=1)
-                    e_lib = np.linalg.norm(M - R)
-                    e_orc = np.linalg.norm(M - Ro)
-                    worst_recon = max(worst_recon, abs(e_lib - e_orc) / max(np.linalg.norm(M), 1e-30))
-        log(f"build {w.name}: worst relative reconstruction-error gap {worst_recon:.2e}")
+                    got = B.read_factors(cache, b, kv, i)
+                    if sep:
+                        parts = [(got[0], x.k[b, kv, t0:t1], oc.U[b][kv][i], oc.sigma[b][kv][i], oc.Vh[b][kv][i]),
+                                 (got[1], x.v[b, kv, t0:t1], oc.U_V[b][kv][i], oc.sigma_V[b][kv][i],
+                                  oc.Vh_V[b][kv][i])]
+                    else:
+                        parts = [(got, np.concatenate([x.k[b, kv, t0:t1], x.v[b, kv, t0:t1]], axis=1), oc.U[b][kv][i],
+                                  oc.sigma[b][kv][i], oc.Vh[b][kv][i])]
+                    for (U, sig, gt, Vh), M, Uo, so_, Vo in parts:
+                        assert np.allclose(sig, so_, rtol=1e-5, atol=1e-6)
+                        assert np.array_equal(gt, oc.gate[b][kv][i].astype(np.float32))
+                        assert np.allclose(U.T @ U, np.eye(rk), atol=utol)
+                        assert np.allclose(Vh @ Vh.T, np.eye(rk), atol=utol)
+                        M = M.astype(np.float64)
+                        e_lib = np.linalg.norm(M - (U * sig) @ Vh)
+                        e_orc = np.linalg.norm(M - (np.asarray(Uo) * so_) @ np.asarray(Vo))
+                        worst_recon = max(worst_recon, abs(e_lib - e_orc) / max(np.linalg.norm(M), 1e-30))
+        log(f"build {w.name} ({w.rank_cap}, {w.basis}, {w.route_keys}): worst relative reconstruction-error gap "
+            f"{worst_recon:.2e}")
         assert worst_recon <= (2e-2 if w.dtype == "bf16" else 1e-5)
 
 
