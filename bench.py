@@ -47,6 +47,11 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+# reading variants (each swaps one reading the pages leave open)
+VARIANTS = {"rank-cap-half": dict(rank_cap="half"), "separate-bases": dict(basis="separate"),
+            "folded-route": dict(route_keys="folded"), "boundary-q97": dict(boundary_quantile=0.97)}
+
+
 # ------------------------------------------------------------------ schedule
 def graph_chunks(start: int, steps: int, per_graph: int):
     """Consecutive chunks (first global step, n steps) covering global steps
@@ -427,7 +432,9 @@ def measure_device(w, x, fracs, args, label, full_rank=False):
                        (target[0] if len(set(target)) == 1 else [round(f, 4) for f in target]),
                        "expand_frac_realized": round(float(avg["frac"]), 4), "full_rank_unit_gates": full_rank,
                        "factors": "device", "layers": 1, "cache_copies_rotated": ncopy, "launch": "hip-graph",
-                       "steps_per_graph": gs},
+                       "steps_per_graph": gs,
+                       "reading": {"rank_cap": w.rank_cap, "basis": w.basis, "route_keys": w.route_keys,
+                                   "boundary_quantile": w.boundary_quantile}},
             "eff_ctx_tokens_per_s": steps_per_s * w.batch * w.n_ctx,
             "algorithmic_bytes_per_step": int(avg["total"]),
             "step_hbm_gbs": step_gbs, "step_hbm_frac": step_gbs / PEAK_HBM_GBS,
@@ -638,6 +645,8 @@ def main():
                     help="only measure the host-resident workload (pinned host factors fetched per step)")
     ap.add_argument("--fetch", choices=("staged", "direct"), default="direct",
                     help="host-resident fetch: host gather + copy (staged) or kernels reading pinned memory (direct)")
+    ap.add_argument("--variant", choices=sorted(VARIANTS), default=None,
+                    help="measure a reading variant of the workload instead of the default readings")
     ap.add_argument("--dense", action="store_true",
                     help="only measure the dense flash-decode baseline on the workload's K/V")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -672,7 +681,7 @@ def main():
         return
 
     from hierarchical_kv_cache_sekv_amd import synth
-    w = synth.workload(args.workload, factors_on_host=False)
+    w = synth.workload(args.workload, factors_on_host=False, **(VARIANTS[args.variant] if args.variant else {}))
     Q = args.queries
     log(f"workload {w.name}: B={w.batch} T={w.n_ctx} Hq={w.n_q_heads} Hkv={w.n_kv_heads} d={w.head_dim} "
         f"{w.dtype} ranks {w.rank_lo}..{w.rank_hi} f={args.frac}")
@@ -703,6 +712,12 @@ def main():
             for r, _ in recs[1:]:
                 print(json.dumps(r), flush=True)
             print(json.dumps(measure_dense(w, x, args, w.name)), flush=True)
+            for name, over in VARIANTS.items():
+                wv = w.with_(**over)
+                xv = x if "boundary_quantile" not in over else synth.make_inputs(wv, n_steps=Q)
+                for r, _ in measure_device(wv, xv, [args.frac], args, f"{w.name} {name}"):
+                    print(json.dumps(r), flush=True)
+                del xv
             del x
             xf = synth.make_inputs(w, n_steps=Q, full_rank_unit_gates=True)
             for r, _ in measure_device(w, xf, [None], args, w.name + " full rank", full_rank=True):

@@ -874,15 +874,25 @@ __device__ __forceinline__ uint64_t cursor_addr(const RegionCursor& c, int lane)
 // Make stream bytes [.., e) readable from the ring: write staged granules and
 // stage the following ones until the ring holds everything before e.
 // `written` counts the stream bytes already in the ring (a multiple of 1024 K).
+// The staging registers hold kExpStages granules in flight, oldest first: the
+// oldest is written to the ring, the others move up, and the next granule of
+// the stream is requested into the last stage.  One stage: two (8 KB in
+// flight per wave) took the fused kernel to 168 registers with spills and
+// ran slower (fused attention 98 against 80 us at 128K batch 4).
+constexpr int kExpStages = 1;
 template <typename T, int D, int K, int RING>
-__device__ __forceinline__ void advance(uint4 (&stg)[K], uint32_t& written, uint32_t e, RegionCursor& c,
+__device__ __forceinline__ void advance(uint4 (&stg)[K * kExpStages], uint32_t& written, uint32_t e, RegionCursor& c,
                                         const ItemMeta& m, int lane, char* ring) {
   while (written < e) {
     const uint32_t w0 = RingPos<RING>::of(written);
 #pragma unroll
-    for (int jj = 0; jj < K; ++jj) {
+    for (int jj = 0; jj < K; ++jj)
       *reinterpret_cast<uint4*>(ring + RingPos<RING>::add(w0, 1024u * jj) + 16u * (uint32_t)lane) = stg[jj];
-      stg[jj] = gload16(cursor_addr(c, lane));
+#pragma unroll
+    for (int jj = 0; jj < K * (kExpStages - 1); ++jj) stg[jj] = stg[jj + K];
+#pragma unroll
+    for (int jj = 0; jj < K; ++jj) {
+      stg[K * (kExpStages - 1) + jj] = gload16(cursor_addr(c, lane));
       cursor_next<T, D>(c, m);
     }
     written += 1024u * K;
@@ -990,9 +1000,9 @@ __device__ __forceinline__ void role_expanded(const AttendArgs& a, int wid, int 
     cur.kind = 0;
     cur.off = 0;
     region_of<T, D>(im, 0, 0, cur.sep, cur.base, cur.size);
-    uint4 stg[K];
+    uint4 stg[K * kExpStages];
 #pragma unroll
-    for (int jj = 0; jj < K; ++jj) {
+    for (int jj = 0; jj < K * kExpStages; ++jj) {
       stg[jj] = gload16(cursor_addr(cur, lane));
       cursor_next<T, D>(cur, im);
     }

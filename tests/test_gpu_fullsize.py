@@ -67,7 +67,9 @@ class Full:
         log(f"{w.name}: library build {time.time() - t0:.1f}s")
         # oracle: segmentation, routing keys per (b, kv)
         self.seg = []
-        self.rho = []
+        self.rho = []          # routing keys: rho, or (kbar stored, key scale) for folded routing
+        self.fold = [O.fold_matrix(x.route_proj[kv]) for kv in range(w.n_kv_heads)] \
+            if w.route_keys == "folded" else None
         for b in range(w.batch):
             so = O.segment(x.surprisal[b], float(x.boundary_thr[b]), w.n_sink, w.n_recent, w.min_span, w.max_span)
             n = len(so) - 1
@@ -76,7 +78,10 @@ class Full:
             rb = []
             for kv in range(w.n_kv_heads):
                 kbar, _ = O.span_summaries(x.k[b, kv], x.v[b, kv], x.surprisal[b], so)
-                rb.append(O.storage_round(O.routing_keys(kbar, x.route_proj[kv]), w.dtype))
+                if self.fold is not None:
+                    rb.append((O.storage_round(kbar, w.dtype), O.key_scales(kbar, x.route_proj[kv])))
+                else:
+                    rb.append(O.storage_round(O.routing_keys(kbar, x.route_proj[kv]), w.dtype))
             self.rho.append(rb)
         self._z = {}
         log(f"{w.name}: oracle routing keys {time.time() - t0:.1f}s")
@@ -94,7 +99,12 @@ class Full:
             z = np.empty((self.n_steps, w.n_q_heads, len(self.seg[b]) - 1), np.float32)
             for kv in range(w.n_kv_heads):
                 qs = self.x.q[:self.n_steps, b, kv * G:(kv + 1) * G].reshape(-1, w.head_dim)
-                z[:, kv * G:(kv + 1) * G] = O.route_scores(qs, self.rho[b][kv]).reshape(self.n_steps, G, -1)
+                if self.fold is not None:
+                    kb, sc = self.rho[b][kv]
+                    zz = O.route_scores_folded(O.fold_query(self.fold[kv], qs), kb, sc)
+                else:
+                    zz = O.route_scores(qs, self.rho[b][kv])
+                z[:, kv * G:(kv + 1) * G] = zz.reshape(self.n_steps, G, -1)
             self._z[b] = z
         return self._z[b][st]
 
@@ -167,7 +177,7 @@ class Full:
                     x.k[b:b + 1, kv:kv + 1], x.v[b:b + 1, kv:kv + 1], x.surprisal[b:b + 1], x.boundary_thr[b:b + 1],
                     x.route_proj[kv:kv + 1], x.rank_req[b:b + 1], x.gate[b:b + 1, kv:kv + 1],
                     n_sink=w.n_sink, n_recent=w.n_recent, lo=w.min_span, hi=w.max_span, dtype=w.dtype,
-                    factor_spans={(0, 0): need})
+                    factor_spans={(0, 0): need}, rank_cap=w.rank_cap, basis=w.basis)
                 ref = O.mixed_attention(cs, 0, x.q[st, b, hs], dec[b][hs], G)
                 err = float(np.abs(out[b, hs] - ref).max())
                 worst = max(worst, err)
@@ -307,3 +317,17 @@ def test_fullsize_t128k_b4_dense_baseline(ctx):
         worst = max(worst, err)
         assert err <= TOL[w.dtype], (b, err)
     log(f"{w.name} dense baseline: max err over all heads {worst:.2e}")
+
+
+@pytest.mark.parametrize("variant", [dict(rank_cap="half"), dict(basis="separate"), dict(route_keys="folded"),
+                                     dict(boundary_quantile=0.97)],
+                         ids=["rank-cap-half", "separate-bases", "folded-route", "boundary-q97"])
+def test_fullsize_t128k_b4_reading_variants(ctx, variant):
+    """Each reading variant on the benchmark workload (128K, batch 4, ranks
+    16..64, 5% expansion): route bit-exact on all 64 steps, every group's
+    output within the tolerance."""
+    w = synth.workload(5, factors_on_host=False, **variant)
+    f = Full(ctx, w)
+    th = f.thresholds([0.05] * w.batch)
+    frac, err = _run(ctx, f, th, [1])
+    log(f"{w.name} {variant}: route exact on {w.steps} steps (mean f={frac:.3f}), all groups max err {err:.2e}")
