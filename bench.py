@@ -82,10 +82,11 @@ def algorithmic_bytes(w, plan, counts, lists, e):
     e*2d*n_full, the summaries kbar, vbar and rho e*3d*n_seg, and for each
     listed span its factors e*r*(L+2d) + 8r (sigma and gate in float32).
     Returns per-kernel shares {route: q + rho, attend: q + full-res K/V +
-    kbar, vbar + factors} and the step total."""
+    kbar, vbar + factors, full: q + full-res K/V (the part of attend that
+    decode_step overlaps with the route)} and the step total."""
     import numpy as np
     d, Hq, Hkv = w.head_dim, w.n_q_heads, w.n_kv_heads
-    route = attend = total = fac_all = 0
+    route = attend = total = fac_all = full = 0
     for b in range(w.batch):
         nf, ns = int(plan.n_full[b]), int(plan.n_seg[b])
         so = plan.seg_off[b]
@@ -99,9 +100,10 @@ def algorithmic_bytes(w, plan, counts, lists, e):
         qb = Hq * d * e
         route += qb + Hkv * ns * d * e
         attend += qb + Hkv * e * 2 * d * (nf + ns) + fac
+        full += qb + Hkv * e * 2 * d * nf
         total += Hq * d * (e + 4) + Hkv * (e * 2 * d * nf + e * 3 * d * ns) + fac
         fac_all += fac
-    return {"route": route, "attend": attend, "total": total, "factors": fac_all}
+    return {"route": route, "attend": attend, "total": total, "factors": fac_all, "full": full}
 
 
 def resident_bytes(w, plan, cache):
@@ -353,8 +355,11 @@ def measure_device(w, x, fracs, args, label, full_rank=False):
         def step(i, theta_d=theta_d):
             c = i % ncopy
             qs = qd[i % Q]
-            B.route(ctx, caches[c], qs, theta_d, outs[c], rws, stream=stream, spans=structs[c])
-            B.decode(ctx, caches[c], qs, outs[c], out, dws, stream=stream, spans=structs[c])
+            if args.overlap:
+                B.decode_step(ctx, caches[c], qs, theta_d, outs[c], out, rws, dws, stream=stream, spans=structs[c])
+            else:
+                B.route(ctx, caches[c], qs, theta_d, outs[c], rws, stream=stream, spans=structs[c])
+                B.decode(ctx, caches[c], qs, outs[c], out, dws, stream=stream, spans=structs[c])
 
         chunks = graph_chunks(args.warmup, args.steps, gs)
         with torch.cuda.stream(stream):
@@ -408,14 +413,20 @@ def measure_device(w, x, fracs, args, label, full_rank=False):
         idx = [(args.warmup + i) % Q for i in range(args.steps)]
         avg = {k: sum(per_q[i][k] for i in idx) / args.steps for k in per_q[0]}
         qb = w.batch * w.n_q_heads * w.head_dim * e
-        if "expand" in kern_us:           # separate full-resolution and expanded-span launches
-            names = {"full": "attend_full_kernel", "expand": "attend_expanded_kernel"}
-            shares = {"route": avg["route"], "full": avg["attend"] - avg["factors"], "expand": avg["factors"] + qb}
+        names, shares = {}, {"route": avg["route"]}
+        rest = avg["attend"]
+        if "overlap" in kern_us:          # decode_step: the full-resolution pass beside the route
+            names["overlap"] = "attend_full_kernel"
+            shares["overlap"] = avg["full"]
+            rest = avg["attend"] - avg["full"] + qb
+        if "expand" in kern_us:           # separate summary and expanded-span launches
+            names.update(full="attend_full_kernel", expand="attend_expanded_kernel")
+            shares.update(full=rest - avg["factors"], expand=avg["factors"] + qb)
         else:                             # one fused attention launch, timed under "full"
-            names = {"attend": "attend_fused_kernel"}
+            names["attend"] = "attend_fused_kernel"
             kern_us["attend"] = kern_us.pop("full")
             kern_n["attend"] = kern_n.pop("full")
-            shares = {"route": avg["route"], "attend": avg["attend"]}
+            shares["attend"] = rest
         gbs = {k: shares[k] / (kern_us[k] * 1e-6) / 1e9 for k in shares}
         dom = max(names, key=lambda k: kern_us[k])
         step_gbs = avg["total"] / (ms_per_step / 1e3) / 1e9
@@ -433,6 +444,7 @@ def measure_device(w, x, fracs, args, label, full_rank=False):
                        "expand_frac_realized": round(float(avg["frac"]), 4), "full_rank_unit_gates": full_rank,
                        "factors": "device", "layers": 1, "cache_copies_rotated": ncopy, "launch": "hip-graph",
                        "steps_per_graph": gs,
+                       "route_overlap": "full-resolution pass on a second stream" if args.overlap else "none",
                        "reading": {"rank_cap": w.rank_cap, "basis": w.basis, "route_keys": w.route_keys,
                                    "boundary_quantile": w.boundary_quantile}},
             "eff_ctx_tokens_per_s": steps_per_s * w.batch * w.n_ctx,
@@ -638,6 +650,9 @@ def main():
     ap.add_argument("--cpu-workers", type=int, default=0, help="oracle worker processes (0: host cores, at most 16)")
     ap.add_argument("--queries", type=int, default=64)
     ap.add_argument("--graph-steps", type=int, default=8, help="decode steps captured per HIP graph")
+    ap.add_argument("--overlap", action="store_true",
+                    help="one sekv_decode_step call per step (full-resolution pass on a second stream beside the "
+                         "route) instead of sekv_route + sekv_mixed_attention_decode")
     ap.add_argument("--sweep", action="store_true",
                     help="after the headline line, one line per further point: 0/20/50%% and full expansion of the "
                          "headline workload, the 32K batch-1 and batch-8 workloads, and the host-resident workload")

@@ -26,7 +26,7 @@ EXPORTS = [
     "sekv_decode_workspace_bytes", "sekv_decode_host_workspace_bytes", "sekv_mixed_attention_decode",
     "sekv_profile_enable", "sekv_profile_read", "sekv_ctx_set_split", "sekv_ctx_set_fetch_mode",
     "sekv_ctx_inject_fault", "sekv_profile_read_host", "sekv_route_noalloc", "sekv_dense_workspace_bytes",
-    "sekv_dense_attention_decode",
+    "sekv_dense_attention_decode", "sekv_decode_step", "sekv_profile_read_overlap",
 ]
 SEKV_FETCH_STAGED, SEKV_FETCH_DIRECT = 0, 1
 SEKV_FAULT_NONE, SEKV_FAULT_GATHER = 0, 1
@@ -91,6 +91,8 @@ def _load():
         "sekv_mixed_attention_decode": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, sz, _p, sz, _p, _p]),
         "sekv_profile_enable": (i32, [_p, i32]),
         "sekv_profile_read": (i32, [_p] + [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)] * 3),
+        "sekv_profile_read_overlap": (i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+        "sekv_decode_step": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, _p, sz, _p, sz, _p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -183,12 +185,17 @@ class Context:
         _check(LIB.sekv_profile_enable(self.handle, int(enable)))
 
     def profile_read(self):
-        """{kernel: (total_ms, launches)} for "route", "full", "expand" since the last read."""
+        """{kernel: (total_ms, launches)} for "route", "full", "expand" and
+        "overlap" (decode_step's full-resolution pass) since the last read."""
         ms = [ctypes.c_double() for _ in range(3)]
         n = [ctypes.c_int64() for _ in range(3)]
         _check(LIB.sekv_profile_read(self.handle, ctypes.byref(ms[0]), ctypes.byref(n[0]), ctypes.byref(ms[1]),
                                      ctypes.byref(n[1]), ctypes.byref(ms[2]), ctypes.byref(n[2])))
-        return {k: (ms[i].value, n[i].value) for i, k in enumerate(("route", "full", "expand"))}
+        res = {k: (ms[i].value, n[i].value) for i, k in enumerate(("route", "full", "expand"))}
+        m1, n1 = ctypes.c_double(), ctypes.c_int64()
+        _check(LIB.sekv_profile_read_overlap(self.handle, ctypes.byref(m1), ctypes.byref(n1)))
+        res["overlap"] = (m1.value, n1.value)
+        return res
 
     def set_split(self, entries: int):
         """Full-resolution entries per split-K chunk (0: the library chooses)."""
@@ -395,6 +402,17 @@ def decode(ctx: Context, cache: SpanCache, q, route_out: RouteOut, out, ws: Deco
                                            _ptr(route_out.exp_list), _ptr(route_out.exp_mask),
                                            _ptr(route_out.exp_count), _ptr(out), _ptr(ws.dev), ws.dev.numel(),
                                            host_ptr, host_n, _stream_handle(stream), cs))
+
+
+def decode_step(ctx: Context, cache: SpanCache, q, theta, route_out: RouteOut, out, route_ws, ws: DecodeWorkspace,
+                stream=None, spans: Optional[Spans] = None):
+    """sekv_decode_step: route + attention of one step, the full-resolution
+    pass on the context's second stream beside the route."""
+    st = spans if spans is not None else cache.struct()
+    _check(LIB.sekv_decode_step(ctx.handle, ctypes.byref(cache.cfg), ctypes.byref(st), _ptr(q), _ptr(theta),
+                                _ptr(route_out.exp_list), _ptr(route_out.exp_mask), _ptr(route_out.exp_count),
+                                _ptr(out), _ptr(route_ws), route_ws.numel(), _ptr(ws.dev), ws.dev.numel(),
+                                _stream_handle(stream)))
 
 
 def tile_values_device(v):

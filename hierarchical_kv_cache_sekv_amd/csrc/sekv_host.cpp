@@ -141,7 +141,9 @@ struct sekv_ctx {
   hipEvent_t ev_ring[kRing] = {};
   ThreadPool* pool = nullptr;
   bool profile = false;
-  EventPairs prof_route, prof_attend, prof_expand;
+  EventPairs prof_route, prof_attend, prof_expand, prof_overlap;
+  hipStream_t aux = nullptr;                          // second stream of sekv_decode_step (default priority)
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;    // its fork / join points
   int32_t split_entries = 0;      // full-resolution entries per split-K chunk (0: automatic)
   int32_t fetch_mode = SEKV_FETCH_DIRECT;
   int32_t fault = SEKV_FAULT_NONE;  // injected failure of the next host-resident decode
@@ -433,6 +435,9 @@ sekv_status sekv_ctx_create(int device, sekv_ctx** out) {
   hipError_t e = hipEventCreateWithFlags(&c->ev_list, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming);
   for (int i = 0; i < kRing && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->ev_ring[i], hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking);
   if (e != hipSuccess) {
     sekv_ctx_destroy(c);
     return fail(SEKV_EHIP, "context setup failed: %s", hipGetErrorString(e));
@@ -452,6 +457,10 @@ void sekv_ctx_destroy(sekv_ctx* c) {
   for (hipEvent_t e : c->prof_route.ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof_attend.ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof_expand.ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->prof_overlap.ev) (void)hipEventDestroy(e);
+  if (c->aux) (void)hipStreamDestroy(c->aux);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->ev_list) (void)hipEventDestroy(c->ev_list);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
   for (int i = 0; i < kRing; ++i)
@@ -878,19 +887,25 @@ void make_plan(const sekv_config* c, const sekv_spans* s, int32_t split_entries,
   a.dtype = c->dtype; a.B = B; a.Hq = c->n_q_heads; a.Hkv = Hkv; a.D = D;
   a.seg_cap = s->seg_cap; a.full_cap = s->full_cap;
   a.sep = c->basis;
-  int ntiles = 1;  // 32-entry tiles of the longest (b, kv) stream: full-res tiles + summary tiles
+  // 32-entry tiles of the longest (b, kv) full-resolution and summary streams
+  int nft = 1, nst = 0;
   for (int b = 0; b < B; ++b) {
     a.n_full[b] = s->n_full_host[b];
     a.n_seg[b] = s->n_seg_host[b];
-    ntiles = std::max(ntiles, (a.n_full[b] + 31) / 32 + (a.n_seg[b] + 31) / 32);
+    nft = std::max(nft, (a.n_full[b] + 31) / 32);
+    nst = std::max(nst, (a.n_seg[b] + 31) / 32);
   }
   // about four full-res/summary workgroups per compute unit
   const int64_t target = 1024;
-  int64_t tc = ((int64_t)BG * ntiles + target - 1) / target;
+  int64_t tc = ((int64_t)BG * (nft + nst) + target - 1) / target;
   tc = std::max<int64_t>(4, std::min<int64_t>(64, tc));
   if (split_entries > 0) tc = std::max<int64_t>(1, std::min<int64_t>(64, (split_entries + 31) / 32));
   a.tiles_a4 = (int)tc;
-  a.nch_a4 = (ntiles + a.tiles_a4 - 1) / a.tiles_a4;
+  // full-resolution chunks first, then summary chunks; no chunk mixes the two
+  a.nch_full = (int)((nft + tc - 1) / tc);
+  a.nch_a4 = a.nch_full + (int)((nst + tc - 1) / tc);
+  a.a4_lo = 0;
+  a.a4_n = a.nch_a4;
   a.P_max = a.nch_a4 + (s->seg_cap + kExpChunk - 1) / kExpChunk;
   const int64_t max_items = (int64_t)BG * ((s->seg_cap + kExpChunk - 1) / kExpChunk);
   a.n_a5_wg = (int)std::max<int64_t>(1, std::min<int64_t>(kExpWaves, max_items));
@@ -943,30 +958,24 @@ size_t sekv_decode_host_workspace_bytes(const sekv_ctx* ctx, const sekv_config* 
   return p.host_bytes;
 }
 
-sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q,
-                                        const int32_t* exp_list, const uint8_t* exp_mask, const int32_t* exp_count,
-                                        float* out, void* dev_ws, size_t dev_ws_bytes, void* host_ws,
-                                        size_t host_ws_bytes, hipStream_t stream, hipStream_t copy_stream) {
+namespace {
+// Checks shared by the decode entry points, and the attention arguments of
+// one call (all chunks of the full-resolution + summary pass).
+sekv_status decode_setup(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q,
+                         const int32_t* exp_list, const uint8_t* exp_mask, const int32_t* exp_count, float* out,
+                         void* dev_ws, size_t dev_ws_bytes, bool staged, const char* who, DecodePlan& p,
+                         AttendArgs& a) {
   if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
   sekv_status st = check_config(c);
   if (st != SEKV_OK) return st;
   st = check_spans(c, s, true);
   if (st != SEKV_OK) return st;
   if (!q || !exp_list || !exp_mask || !exp_count || !out || !dev_ws)
-    return fail(SEKV_EINVAL, "sekv_mixed_attention_decode: a pointer argument is NULL");
-  const bool staged = staged_fetch(ctx, c);
-  DecodePlan p;
+    return fail(SEKV_EINVAL, "%s: a pointer argument is NULL", who);
   make_plan(c, s, ctx->split_entries, staged, p);
   if (dev_ws_bytes < p.dev_bytes) return fail(SEKV_ECAPACITY, "device workspace %zu bytes < %zu needed", dev_ws_bytes, p.dev_bytes);
   if (p.a.tiles_a4 * 32 > 2048) return fail(SEKV_ESHAPE, "internal chunk size too large");
-  if (staged) {
-    if (!host_ws) return fail(SEKV_EINVAL, "host-resident factors need a pinned host workspace");
-    if (host_ws_bytes < p.host_bytes) return fail(SEKV_ECAPACITY, "host workspace %zu bytes < %zu needed", host_ws_bytes, p.host_bytes);
-    if (!is_pinned_host(host_ws)) return fail(SEKV_EINVAL, "host workspace must be pinned (hipHostMalloc)");
-  }
-  if (!copy_stream) copy_stream = stream;
-  HIP_OR_FAIL(hipSetDevice(ctx->device));
-  AttendArgs a = p.a;
+  a = p.a;
   char* dws = static_cast<char*>(dev_ws);
   a.q = q; a.full_k = s->full_k; a.full_v = s->full_v; a.sum_k = s->sum_k; a.sum_v = s->sum_v;
   a.seg_off = s->seg_off; a.rank = s->rank; a.fac_off = s->fac_off; a.sg_off = s->sg_off; a.fac = s->fac; a.sg = s->sg;
@@ -982,21 +991,52 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
     a.sg = static_cast<const float*>(device_address(s->sg));
     if (!a.fac || !a.sg) return fail(SEKV_EHIP, "pinned factor pools have no device address");
   }
+  return SEKV_OK;
+}
+
+// The attention launches on device-visible factors for the role-A chunks
+// a.a4_lo .. a.a4_lo + a.a4_n - 1 of each (b, kv), then the combine.
+hipError_t launch_attention(sekv_ctx* ctx, AttendArgs a, hipStream_t stream) {
+  const int BG = a.B * a.Hkv;
+  a.n_a4_wg = BG * a.a4_n;
+  hipEvent_t e0, e1;
+  if (a.max_rank <= 64) {
+    // both passes in one launch on the caller's stream
+    hipError_t e = prof_pair(ctx, ctx->prof_attend, &e0, &e1);
+    if (e == hipSuccess) e = launch_attend_fused(a, stream, e0, e1);
+    if (e != hipSuccess) return e;
+  } else {
+    hipError_t e = prof_pair(ctx, ctx->prof_expand, &e0, &e1);
+    if (e == hipSuccess) e = launch_attend_expanded(a, stream, e0, e1);
+    if (e == hipSuccess) e = prof_pair(ctx, ctx->prof_attend, &e0, &e1);
+    if (e == hipSuccess) e = launch_attend_full(a, stream, e0, e1);
+    if (e != hipSuccess) return e;
+  }
+  return launch_combine(a, stream);
+}
+}  // namespace
+
+sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q,
+                                        const int32_t* exp_list, const uint8_t* exp_mask, const int32_t* exp_count,
+                                        float* out, void* dev_ws, size_t dev_ws_bytes, void* host_ws,
+                                        size_t host_ws_bytes, hipStream_t stream, hipStream_t copy_stream) {
+  const bool staged = ctx && c && staged_fetch(ctx, c);
+  DecodePlan p;
+  AttendArgs a;
+  sekv_status st = decode_setup(ctx, c, s, q, exp_list, exp_mask, exp_count, out, dev_ws, dev_ws_bytes, staged,
+                                "sekv_mixed_attention_decode", p, a);
+  if (st != SEKV_OK) return st;
+  if (staged) {
+    if (!host_ws) return fail(SEKV_EINVAL, "host-resident factors need a pinned host workspace");
+    if (host_ws_bytes < p.host_bytes) return fail(SEKV_ECAPACITY, "host workspace %zu bytes < %zu needed", host_ws_bytes, p.host_bytes);
+    if (!is_pinned_host(host_ws)) return fail(SEKV_EINVAL, "host workspace must be pinned (hipHostMalloc)");
+  }
+  if (!copy_stream) copy_stream = stream;
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+  char* dws = static_cast<char*>(dev_ws);
 
   if (!staged) {
-    if (a.max_rank <= 64) {
-      // both passes in one launch on the caller's stream
-      hipEvent_t e0, e1;
-      HIP_OR_FAIL(prof_pair(ctx, ctx->prof_attend, &e0, &e1));
-      HIP_OR_FAIL(launch_attend_fused(a, stream, e0, e1));
-    } else {
-      hipEvent_t e0, e1;
-      HIP_OR_FAIL(prof_pair(ctx, ctx->prof_expand, &e0, &e1));
-      HIP_OR_FAIL(launch_attend_expanded(a, stream, e0, e1));
-      HIP_OR_FAIL(prof_pair(ctx, ctx->prof_attend, &e0, &e1));
-      HIP_OR_FAIL(launch_attend_full(a, stream, e0, e1));
-    }
-    HIP_OR_FAIL(launch_combine(a, stream));
+    HIP_OR_FAIL(launch_attention(ctx, a, stream));
     return SEKV_OK;
   }
 
@@ -1102,6 +1142,51 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   return SEKV_OK;
 }
 
+// ---------------------------------------------------------------- decode step
+sekv_status sekv_decode_step(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q,
+                             const float* theta, int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count, float* out,
+                             void* route_ws, size_t route_ws_bytes, void* dev_ws, size_t dev_ws_bytes,
+                             hipStream_t stream) {
+  sekv_status st = route_checked(ctx, c, s, q, theta, exp_list, exp_mask, exp_count);
+  if (st != SEKV_OK) return st;
+  if (!route_ws) return fail(SEKV_EINVAL, "sekv_decode_step: route_ws is NULL");
+  if (route_ws_bytes < sekv_route_workspace_bytes(c, s))
+    return fail(SEKV_ECAPACITY, "route workspace %zu bytes < %zu needed", route_ws_bytes, sekv_route_workspace_bytes(c, s));
+  if (staged_fetch(ctx, c))
+    return fail(SEKV_EINVAL, "sekv_decode_step: staged host-resident fetch runs through sekv_route and "
+                             "sekv_mixed_attention_decode");
+  DecodePlan p;
+  AttendArgs a;
+  st = decode_setup(ctx, c, s, q, exp_list, exp_mask, exp_count, out, dev_ws, dev_ws_bytes, false,
+                    "sekv_decode_step", p, a);
+  if (st != SEKV_OK) return st;
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+  // the full-resolution chunks read neither the route's outputs nor anything
+  // it writes: they run on the second stream while the route runs here
+  AttendArgs af = a;
+  af.a4_lo = 0;
+  af.a4_n = a.nch_full;
+  af.n_a4_wg = c->batch * c->n_kv_heads * a.nch_full;
+  HIP_OR_FAIL(hipEventRecord(ctx->ev_fork, stream));
+  HIP_OR_FAIL(hipStreamWaitEvent(ctx->aux, ctx->ev_fork, 0));
+  hipEvent_t e0, e1;
+  hipError_t he = prof_pair(ctx, ctx->prof_overlap, &e0, &e1);
+  if (he == hipSuccess) he = launch_attend_full(af, ctx->aux, e0, e1);
+  const hipError_t hj = hipEventRecord(ctx->ev_join, ctx->aux);
+  if (he != hipSuccess || hj != hipSuccess) {
+    (void)hipStreamWaitEvent(stream, ctx->ev_join, 0);
+    return fail(SEKV_EHIP, "sekv_decode_step: %s", hipGetErrorString(he != hipSuccess ? he : hj));
+  }
+  st = route_launch(ctx, c, s, q, theta, exp_list, exp_mask, exp_count, route_ws, true, stream);
+  HIP_OR_FAIL(hipStreamWaitEvent(stream, ctx->ev_join, 0));   // joined on every path
+  if (st != SEKV_OK) return st;
+  AttendArgs ar = a;
+  ar.a4_lo = a.nch_full;
+  ar.a4_n = a.nch_a4 - a.nch_full;
+  HIP_OR_FAIL(launch_attention(ctx, ar, stream));
+  return SEKV_OK;
+}
+
 // ---------------------------------------------------------------- dense baseline
 namespace {
 // Dense decode: the full-resolution pass over all T tokens of every (b, kv),
@@ -1120,6 +1205,9 @@ void make_dense_plan(const sekv_config* c, int32_t split_entries, AttendArgs& a,
   if (split_entries > 0) tc = std::max<int64_t>(1, std::min<int64_t>(64, (split_entries + 31) / 32));
   a.tiles_a4 = (int)tc;
   a.nch_a4 = (ntiles + a.tiles_a4 - 1) / a.tiles_a4;
+  a.nch_full = a.nch_a4;
+  a.a4_lo = 0;
+  a.a4_n = a.nch_a4;
   a.P_max = a.nch_a4;
   a.n_a4_wg = BG * a.nch_a4;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)D));
@@ -1196,7 +1284,7 @@ sekv_status sekv_profile_read_host(sekv_ctx* ctx, double* wait_ms, double* gathe
 sekv_status sekv_profile_enable(sekv_ctx* ctx, int32_t enable) {
   if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
   ctx->profile = enable != 0;
-  ctx->prof_route.used = ctx->prof_attend.used = ctx->prof_expand.used = 0;
+  ctx->prof_route.used = ctx->prof_attend.used = ctx->prof_expand.used = ctx->prof_overlap.used = 0;
   return SEKV_OK;
 }
 
@@ -1208,6 +1296,13 @@ sekv_status sekv_profile_read(sekv_ctx* ctx, double* route_ms, int64_t* route_n,
   HIP_OR_FAIL(prof_sum(ctx->prof_route, route_ms, route_n));
   HIP_OR_FAIL(prof_sum(ctx->prof_attend, full_ms, full_n));
   HIP_OR_FAIL(prof_sum(ctx->prof_expand, expand_ms, expand_n));
+  return SEKV_OK;
+}
+
+sekv_status sekv_profile_read_overlap(sekv_ctx* ctx, double* ms, int64_t* launches) {
+  if (!ctx || !ms || !launches) return fail(SEKV_EINVAL, "sekv_profile_read_overlap: NULL argument");
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+  HIP_OR_FAIL(prof_sum(ctx->prof_overlap, ms, launches));
   return SEKV_OK;
 }
 

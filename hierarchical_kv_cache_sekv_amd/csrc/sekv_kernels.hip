@@ -211,9 +211,12 @@ constexpr float kNegInf = -__builtin_inff();
 // read it, counted by their atomic adds once they see it published; the
 // reader that completes the count stores 0.
 //
-// A guarded fused multiply-add (exact when every bf16 product is a normal
-// float32) was tried for the score chain: the range checks and the extra
-// vote cost more than the multiplies saved (1.5 us slower per call).
+// Fused multiply-adds were tried twice for the score chain (exact when every
+// bf16 product is exact in float32): with per-product range checks (1.5 us
+// slower per call), and with a per-tile bound on min/max |q| and |rho| plus
+// the query in scalar registers (24 against 22 us at 128K batch 4).  The call
+// is bound by its memory phase: without the chain it still takes 18 us, and
+// streaming the keys alone 12 us.
 //
 constexpr int kRouteRowBytes = 128;
 constexpr int kRouteRowStride = 144;
@@ -537,11 +540,22 @@ __device__ __forceinline__ void role_full_summary(const AttendArgs& a, int idx, 
   constexpr int NC = D / 32, NJ = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, cls = lane >> 4;
-  const int g = idx / a.nch_a4, chunk = idx % a.nch_a4;
+  const int g = idx / a.a4_n, chunk = a.a4_lo + idx % a.a4_n;
   const int b = g / a.Hkv, kv = g % a.Hkv;
   const int nf = a.n_full[b], ns = a.n_seg[b];
   const int nft = (nf + 31) / 32, nst = (ns + 31) / 32;
-  const int t0 = min(nft + nst, chunk * a.tiles_a4), t1 = min(nft + nst, t0 + a.tiles_a4);
+  // chunks [0, nch_full) hold full-resolution tiles only, the rest summary
+  // tiles only (a full-resolution chunk never reads the route's outputs, so
+  // it may run while the route does); tiles numbered full first, then summary
+  int t0, t1;
+  if (chunk < a.nch_full) {
+    t0 = min(nft, chunk * a.tiles_a4);
+    t1 = min(nft, t0 + a.tiles_a4);
+  } else {
+    const int cs = (chunk - a.nch_full) * a.tiles_a4;
+    t0 = nft + min(nst, cs);
+    t1 = nft + min(nst, cs + a.tiles_a4);
+  }
   const int S0 = (max(t0, nft) - nft) * 32, S1 = min(ns, (max(t1, nft) - nft) * 32);
 
   uint8_t* smask = reinterpret_cast<uint8_t*>(lds);

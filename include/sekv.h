@@ -338,6 +338,32 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* cfg, c
                                         hipStream_t stream, hipStream_t copy_stream);
 
 /*
+ * sekv_decode_step - sekv_route and sekv_mixed_attention_decode of one decode
+ * step in one call, with the full-resolution entries' attention (sink,
+ * anchors, tail: the part that does not depend on the routing decision,
+ * [de-3]) running on a second stream of the context while the route runs on
+ * `stream`; the summaries, the expanded spans and the merge follow on
+ * `stream` after both.  Results are bit-identical to sekv_route followed by
+ * sekv_mixed_attention_decode with the same context and workspaces.
+ *   Arguments as in those two calls: q, theta, exp_list/exp_mask/exp_count
+ *   (written), out (written), route_ws (sekv_route_workspace_bytes, same
+ *   zero-between-calls contract), dev_ws (sekv_decode_workspace_bytes).
+ *   Device-resident factors or the direct host fetch only; with the staged
+ *   host fetch the call returns SEKV_EINVAL.
+ *   Everything the call enqueues is ordered after the work already on
+ *   `stream`, and later work on `stream` is ordered after all of it (the
+ *   second stream forks from and joins `stream` through events, so the call
+ *   may be captured into a HIP graph).  Calls on one context must not overlap
+ *   in time (they share its second stream and events).
+ * Errors: as sekv_route and sekv_mixed_attention_decode; nothing is enqueued
+ * when the arguments are rejected.
+ */
+sekv_status sekv_decode_step(sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans, const void* q,
+                             const float* theta, int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count,
+                             float* out, void* route_ws, size_t route_ws_bytes, void* dev_ws, size_t dev_ws_bytes,
+                             hipStream_t stream);
+
+/*
  * sekv_dense_attention_decode - the dense baseline: plain softmax attention of
  * each query head over all T cached tokens (logit q.k/sqrt(d)), with the same
  * split-K matrix-core pass and log-sum-exp merge as the full-resolution part
@@ -372,6 +398,10 @@ sekv_status sekv_dense_attention_decode(sekv_ctx* ctx, const sekv_config* cfg, c
 sekv_status sekv_profile_enable(sekv_ctx* ctx, int32_t enable);
 sekv_status sekv_profile_read(sekv_ctx* ctx, double* route_ms, int64_t* route_launches, double* full_ms,
                               int64_t* full_launches, double* expand_ms, int64_t* expand_launches);
+/* The same for the full-resolution pass that sekv_decode_step runs on its
+ * second stream beside the route ("overlap"; in that call "full" times only
+ * the summary + expanded-span launch). */
+sekv_status sekv_profile_read_overlap(sekv_ctx* ctx, double* ms, int64_t* launches);
 
 /* Host-side phases of staged host-resident decode calls since the last read
  * (always recorded): the host wait for the route list, the threaded gather of

@@ -148,6 +148,13 @@ class Device:
     def decode(self, ctx, si, copy_stream=None):
         self.B.decode(ctx, self.cache, self.q(si), self.route_out, self.out, self.dec_ws, copy_stream=copy_stream)
 
+    def step(self, ctx, si, stream=None, q=None):
+        """route + decode in one sekv_decode_step call (full-resolution pass on
+        the context's second stream beside the route); q: a device copy of
+        step si's queries made beforehand (needed under graph capture)."""
+        self.B.decode_step(ctx, self.cache, self.q(si) if q is None else q, self.theta, self.route_out, self.out,
+                           self.route_ws, self.dec_ws, stream=stream)
+
     def route_numpy(self):
         import torch
         torch.cuda.synchronize()

@@ -258,7 +258,7 @@ def test_fullsize_t128k_b4_sweep(ctx):
         log(f"{w.name} f={frac_t}: route exact on {w.steps} steps (mean f={frac:.3f}), all groups max err {err:.2e}")
     # Back-to-back route calls on one workspace, alternating queries and
     # thresholds: every call's list, masks and counts stay bit-exact (the
-    # workspace's tickets and status words return to zero
+    # workspace's status words return to zero
     # after each call).
     cases = []
     for frac_t in (0.05, 0.50):

@@ -92,6 +92,14 @@ def test_route_and_decode_parity(ctx, name):
         dev.decode(ctx, si)
         torch.cuda.synchronize()
         assert torch.equal(out2, dev.out)        # deterministic
+        # one sekv_decode_step call (full-resolution pass beside the route):
+        # the same route outputs and the same output bits
+        dev.out.zero_()
+        dev.route_out.exp_count.fill_(-7)
+        dev.step(ctx, si)
+        torch.cuda.synchronize()
+        compare_route(dev, ref)
+        assert torch.equal(out2, dev.out)
 
 
 def test_route_out_of_range_keys_stay_bit_exact(ctx):
@@ -172,6 +180,131 @@ def test_route_ticket_order_on_a_grid_larger_than_the_gpu_holds(ctx):
                 assert msk[b, kv, :n].tolist() == masks[kv].tolist()
     assert int(ws.count_nonzero()) == 0
     log(f"ticket-ordered route: {nblk * w.n_kv_heads * w.batch} workgroups, lists bit-exact")
+
+
+def _route_raw(ctx, w, rho, q, theta):
+    """Route a hand-made set of routing keys rho [B][Hkv][n][d] (one sequence
+    layout shared by the batch) with queries q [B][Hq][d] and thresholds
+    theta [B][Hq]; returns (count, list, mask) on the host."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    cfg = B.make_config(w)
+    n = rho.shape[2]
+    L = w.min_span
+    so = np.arange(w.n_sink, w.n_sink + (n + 1) * (L + 1), L + 1, dtype=np.int64)
+    assert so[-1] == w.n_ctx - w.n_recent
+    segs = [so] * w.batch
+    plan = B.layout_from_segments(cfg, segs, [np.ones(n, np.int32)] * w.batch)
+    cache = B.SpanCache(cfg, plan)
+    full = np.zeros((w.batch, w.n_kv_heads, cache.seg_cap, w.head_dim), np.float32)
+    full[:, :, :n] = rho
+    cache.rho.copy_(torch.from_numpy(full).to(cache.elem))
+    ro = B.RouteOut(cfg, cache.seg_cap)
+    ws = B.route_workspace(cache)
+    B.route(ctx, cache, torch.from_numpy(np.ascontiguousarray(q, np.float32)).to(cache.elem).cuda(),
+            torch.from_numpy(np.ascontiguousarray(theta, np.float32)).cuda(), ro, ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+    return ro.exp_count.cpu().numpy(), ro.exp_list.cpu().numpy(), ro.exp_mask.cpu().numpy()
+
+
+def test_route_keeps_separate_rounding_where_fused_steps_would_differ(ctx):
+    """Two tiles hold spans on which a fused multiply-add chain and the
+    canonical chain (separately rounded products) decide differently, and
+    thresholds sit exactly on the canonical score:
+      - a product below the subnormal grid: 2^-16 * 3*2^-133 = 3*2^-149, then
+        2^-17 * 2^-133 = 2^-150, which rounds to 0 on its own (ties to even)
+        but carries 3.5*2^-149 -> 4*2^-149 inside a fused step;
+      - an overflowing product: -1.5*2^64 * 2^63 = -1.5*2^127, then
+        2^64 * 2^64 = 2^128, which overflows to +inf on its own but cancels
+        to 2^126 inside a fused step.
+    A third tile holds ordinary keys.  Every decision must equal the oracle's
+    separately rounded chain."""
+    import warnings
+    n = 700                                      # three tiles of 256 spans of length 2
+    w = synth.workload(2, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, dtype="bf16",
+                       n_ctx=4 + 3 * n + 256, n_sink=4, n_recent=256, min_span=2, max_span=8)
+    G, d = w.group, w.head_dim
+    rng = np.random.default_rng(31)
+    rho = O.storage_round(rng.standard_normal((w.batch, w.n_kv_heads, n, d)) / 8, "bf16")
+    q = O.storage_round(rng.standard_normal((w.batch, w.n_q_heads, d)), "bf16")
+    theta = np.zeros((w.batch, w.n_q_heads), np.float32)
+    # sequence 0: sub-grid products in group 0 tile 1 (span 300) and group 1
+    # tile 0 (span 5); the queries are zero past their first two entries, so
+    # the other keys of those spans (tiny, nonzero) add exact zeros
+    q[0, :, :2] = [2.0 ** -16, 2.0 ** -17]
+    q[0, :, 2:] = 0.0
+    for kv, S in ((0, 300), (1, 5)):
+        rho[0, kv, S, :2] = [3 * 2.0 ** -133, 2.0 ** -133]
+        rho[0, kv, S, 2:] = 2.0 ** -120
+    # sequence 1: overflow with cancellation in group 1 tile 2 (span 650)
+    q[1, :, :2] = [-1.5 * 2.0 ** 64, 2.0 ** 64]
+    rho[1, 1, 650] = 0.0
+    rho[1, 1, 650, :2] = [2.0 ** 63, 2.0 ** 64]
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", RuntimeWarning)     # the canonical overflow to inf
+        z = np.stack([np.concatenate([O.route_scores(q[b, kv * G:(kv + 1) * G], rho[b, kv])[:, None, :]
+                                      for kv in range(w.n_kv_heads)], 1) for b in range(w.batch)])
+    # z [B][G][Hkv][n]; the planted spans' canonical scores, and what a fused
+    # chain would give there (exact sums in float64, one rounding to float32)
+    assert (z[0, :, 0, 300] == np.float32(3 * 2.0 ** -149)).all() and (z[0, :, 1, 5] == z[0, :, 0, 300]).all()
+    assert np.float32(3.5 * 2.0 ** -149) == np.float32(4 * 2.0 ** -149)
+    assert np.isinf(z[1, :, 1, 650]).all() and (z[1, :, 1, 650] > 0).all()
+    assert np.float32(-1.5 * 2.0 ** 127 + 2.0 ** 128) == np.float32(2.0 ** 126) < np.float32(3e38)
+    # thresholds: on the canonical sub-grid score (fused would be above it),
+    # and between the fused and canonical overflow results
+    theta[0, :] = np.float32(3 * 2.0 ** -149)
+    theta[1, :] = rng.standard_normal(w.n_q_heads).astype(np.float32)
+    theta[1, G:2 * G] = np.float32(3e38)
+    cnt, lst, msk = _route_raw(ctx, w, rho, q, theta)
+    for b in range(w.batch):
+        dec = np.concatenate([z[b, :, kv] for kv in range(w.n_kv_heads)]) > theta[b][:, None]
+        lists, masks = O.compact(dec, G)
+        for kv in range(w.n_kv_heads):
+            m = len(lists[kv])
+            assert cnt[b, kv] == m, (b, kv)
+            assert lst[b, kv, :m].tolist() == lists[kv].tolist()
+            assert msk[b, kv, :m].tolist() == masks[kv].tolist()
+    assert 650 in lst[1, 1, :cnt[1, 1]].tolist()            # +inf > 3e38: expanded
+    assert 300 not in lst[0, 0, :cnt[0, 0]].tolist()        # z == theta: not expanded
+    log("route: sub-grid and overflowing products bit-exact")
+
+
+def test_decode_step_in_a_hip_graph_replays_like_eager(ctx):
+    """sekv_decode_step captured into a HIP graph (its second stream forks
+    from and joins the capture stream): several replays, with eager library
+    work and host synchronisation between them, each bit-identical to the
+    eager call of the same step."""
+    import torch
+    p = _prep("bf16-d128-T4K")
+    dev = Device(p)
+    stream = torch.cuda.Stream()
+    want = []
+    for si in range(len(p.steps)):
+        with torch.cuda.stream(stream):
+            dev.step(ctx, si, stream=stream)
+        torch.cuda.synchronize()
+        want.append((dev.out.clone(), dev.route_numpy()))
+    q0 = dev.q(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        dev.step(ctx, 0, stream=stream, q=q0)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        dev.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dev.out, want[0][0]), rep
+        cnt, lst, msk = dev.route_numpy()
+        assert np.array_equal(cnt, want[0][1][0])
+        # eager work between replays: the other step, eagerly
+        with torch.cuda.stream(stream):
+            dev.step(ctx, len(p.steps) - 1, stream=stream)
+        torch.cuda.synchronize()
+        assert torch.equal(dev.out, want[-1][0])
+    assert int(dev.route_ws.count_nonzero()) == 0
+    log("decode_step: 4 graph replays bit-identical to eager")
 
 
 @pytest.mark.parametrize("mode", ["plus_inf", "minus_inf"])
