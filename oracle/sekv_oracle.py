@@ -43,7 +43,7 @@ __all__ = [
     "routing_keys", "span_factors", "OracleCache", "build_cache", "route_scores",
     "route", "compact", "reconstruct", "mixed_attention", "mixed_attention_all",
     "dense_attention", "SIZE_CORRECTION", "span_factors_separate", "span_ranks", "fold_matrix",
-    "fold_query", "key_scales", "route_scores_folded", "reconstruct_span",
+    "fold_query", "key_scales", "route_scores_folded", "reconstruct_span", "sealed_segment", "seal_next",
 ]
 
 # Reading: the size correction of an unexpanded span's summary logit is +ln|S|
@@ -117,6 +117,48 @@ def segment(s, thr: float, n_sink: int, n_recent: int, lo: int, hi: int) -> np.n
     else:
         tail = e
     return np.array(heads + [tail], dtype=np.int64)
+
+
+def sealed_segment(s, thr: float, n_sink: int, n_recent: int, lo: int, hi: int) -> np.ndarray:
+    """Span offsets of a context during decode: only the sealed spans.
+
+    [de-1]/[zh-1] define the segmentation at prefill; during decode tokens
+    keep arriving and leave the recent window.  Reading (when a span seals):
+    the rule of ``segment`` decides token t for good once t <= e - 1 - lo,
+    e = T - n_recent: from then on the data-head condition's room before the
+    recent window (e - t - 1 >= lo) holds at every longer context, and the
+    forced-head condition never depended on e.  A span seals when its closing
+    head is decided.  The cache of a context holds the sealed spans; every
+    token from the last sealed head on (that head is the anchor of the span
+    still open) stays at full resolution.
+
+    Returns ``seg_off`` in the format of ``segment``: the decided heads
+    h_0 .. h_k, the last of which is the tail start (n_seg = k).
+    """
+    s = np.asarray(s)
+    e = s.shape[0] - n_recent
+    heads = [int(h) for h in segment(s, thr, n_sink, n_recent, lo, hi)[:-1] if h <= e - 1 - lo]
+    if not heads:
+        heads = [n_sink]
+    return np.array(heads, dtype=np.int64)
+
+
+def seal_next(seg_off, s, thr: float, n_sink: int, n_recent: int, lo: int, hi: int) -> np.ndarray:
+    """One decode step of online sealing: ``seg_off`` is the sealed layout of
+    the context of len(s) - 1 tokens, s the surprisal of len(s) tokens (the
+    last one new).  With the new token one more token becomes decided,
+    t = len(s) - n_recent - 1 - lo; it is a head if its body (tokens since the
+    last sealed head) has reached ``hi``, or if s[t] > thr and the body holds
+    at least ``lo`` tokens.  A new head closes (seals) the span after the last
+    sealed head.  Returns the sealed layout of the longer context."""
+    so = [int(x) for x in seg_off]
+    t = len(s) - n_recent - 1 - lo
+    if t >= n_sink + 1:
+        h = so[-1]
+        body = t - h - 1
+        if body == hi or (s[t] > thr and body >= lo):
+            so.append(t)
+    return np.array(so, dtype=np.int64)
 
 
 def full_res_tokens(seg_off: np.ndarray, n_sink: int, T: int) -> np.ndarray:
@@ -311,7 +353,7 @@ class OracleCache:
 
 
 def build_cache(k, v, s, thr, P, rank_req, gate, *, n_sink, n_recent, lo, hi, dtype,
-                factor_spans=None, rank_cap="full", basis="joint") -> OracleCache:
+                factor_spans=None, rank_cap="full", basis="joint", sealed=False) -> OracleCache:
     """Build the mixed-resolution cache from stored K/V [B][Hkv][T][d], surprisal
     [B][T], boundary thresholds [B], projections [Hkv][d][d], requested ranks
     [B][>=n_seg] and gates [B][Hkv][>=n_seg][>=r].
@@ -326,13 +368,17 @@ def build_cache(k, v, s, thr, P, rank_req, gate, *, n_sink, n_recent, lo, hi, dt
     ``factor_spans`` (optional): {(b, kv head): span indices}; only those spans
     get factors (the others hold None and must not be expanded).  This skips
     work only; every value computed is the same.
+
+    ``sealed``: the layout of a context during decode (``sealed_segment``):
+    only sealed spans, a longer full-resolution tail.
     """
     B, Hkv, T, d = k.shape
     sep = basis == "separate"
     seg_offs, full_idx, fk, fv, sk, sv, rh, ranks, Us, sigs, gts, Vhs = ([] for _ in range(12))
     UVs, sVs, VVs, kss = [], [], [], []
     for b in range(B):
-        so = segment(s[b], float(thr[b]), n_sink, n_recent, lo, hi)
+        seg = sealed_segment if sealed else segment
+        so = seg(s[b], float(thr[b]), n_sink, n_recent, lo, hi)
         n_seg = len(so) - 1
         L = (so[1:] - so[:-1] - 1).astype(np.int64)
         r = span_ranks(rank_req[b][:n_seg], L, d, rank_cap, basis)
