@@ -544,6 +544,60 @@ def measure_dense(w, x, args, label):
 
 
 # ------------------------------------------------------------------ host-resident measurement
+def measure_append(args):
+    """Online span sealing: the headline workload's caches in the decode-time
+    (sealed) layout at 128K, grown by --append tokens with one
+    sekv_append_token call per token (append every (b, kv) row; summarise,
+    route-key and factor each span that seals).  One record: calls/s and
+    microseconds per call (host decisions and upload included, synchronised
+    once at the end), spans sealed."""
+    import numpy as np
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    from hierarchical_kv_cache_sekv_amd import synth
+
+    base = synth.workload(args.workload, factors_on_host=False)
+    T0, N = base.n_ctx, args.append
+    w = base.with_(n_ctx=T0 + N)
+    x = synth.make_inputs(w, n_steps=1)
+    ctx = B.Context(0)
+    cfg = B.make_config(w)
+    cfg.sealed, cfg.n_ctx_max, cfg.n_ctx = 1, T0 + N, T0
+    plan = B.plan_spans(cfg, x.surprisal[:, :T0], x.boundary_thr, x.rank_req)
+    cmax = B.make_config(w)
+    cmax.sealed, cmax.n_ctx_max = 1, T0 + N
+    pmax = B.plan_spans(cmax, x.surprisal, x.boundary_thr, x.rank_req)
+    cache = B.SpanCache(cfg, plan, fac_capacity=pmax.fac_elems, sg_capacity=pmax.sg_elems)
+    et = cache.elem
+    kd = torch.from_numpy(x.k).to(et).cuda()
+    vd = torch.from_numpy(x.v).to(et).cuda()
+    B.build_spans(ctx, cache, kd[:, :, :T0].contiguous(), vd[:, :, :T0].contiguous(), x.surprisal[:, :T0],
+                  x.route_proj, x.gate)
+    P = torch.from_numpy(np.ascontiguousarray(x.route_proj, np.float32)).cuda()
+    ws = B.append_workspace(cache)
+    kn = [kd[:, :, t].contiguous() for t in range(T0, T0 + N)]
+    vn = [vd[:, :, t].contiguous() for t in range(T0, T0 + N)]
+    del kd, vd
+    torch.cuda.synchronize()
+    sealed = 0
+    t1 = time.perf_counter()
+    for i in range(N):
+        sealed += int(B.append_token(ctx, cache, kn[i], vn[i], x.surprisal, x.boundary_thr, P, x.gate, x.rank_req,
+                                     ws).sum())
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t1
+    ctx.close()
+    log(f"append: {N} calls, {sealed} spans sealed, {dt * 1e6 / N:.1f} us/call")
+    return {"metric": "online span sealing (sekv_append_token) calls/s", "value": N / dt, "unit": "calls/s",
+            "n_gpus": 1, "steps": N, "warmup": 0, "ms_per_step": dt * 1e3 / N, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded)",
+            "config": {"workload": base.name + " decode-time layout, +%d tokens" % N, "batch": w.batch,
+                       "n_ctx_start": T0, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                       "spans_sealed": sealed, "spans_sealed_per_call": sealed / N,
+                       "timing": "host wall clock over all calls (decisions, one upload, two kernels each), "
+                                 "synchronised at the end"}}
+
+
 def measure_host_resident(args):
     """The host-resident workload: 128K context, batch 1, ranks 8..32, factor
     pools in pinned host memory, the listed spans' factor blocks gathered and
@@ -656,6 +710,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="after the headline line, one line per further point: 0/20/50%% and full expansion of the "
                          "headline workload, the 32K batch-1 and batch-8 workloads, and the host-resident workload")
+    ap.add_argument("--append", type=int, default=0, metavar="N",
+                    help="only measure online span sealing: N sekv_append_token calls on the workload's caches")
     ap.add_argument("--host-resident", action="store_true",
                     help="only measure the host-resident workload (pinned host factors fetched per step)")
     ap.add_argument("--fetch", choices=("staged", "direct"), default="direct",
@@ -693,6 +749,9 @@ def main():
         sys.exit(2)
     if args.host_resident:
         print(json.dumps(measure_host_resident(args)), flush=True)
+        return
+    if args.append:
+        print(json.dumps(measure_append(args)), flush=True)
         return
 
     from hierarchical_kv_cache_sekv_amd import synth
@@ -746,6 +805,8 @@ def main():
                     print(json.dumps(r), flush=True)
                 del x2
             print(json.dumps(measure_host_resident(args)), flush=True)
+            args.append = args.append or 512
+            print(json.dumps(measure_append(args)), flush=True)
     finally:
         if pool is not None:
             pool.close()

@@ -26,7 +26,8 @@ EXPORTS = [
     "sekv_decode_workspace_bytes", "sekv_decode_host_workspace_bytes", "sekv_mixed_attention_decode",
     "sekv_profile_enable", "sekv_profile_read", "sekv_ctx_set_split", "sekv_ctx_set_fetch_mode",
     "sekv_ctx_inject_fault", "sekv_profile_read_host", "sekv_route_noalloc", "sekv_dense_workspace_bytes",
-    "sekv_dense_attention_decode", "sekv_decode_step", "sekv_profile_read_overlap",
+    "sekv_dense_attention_decode", "sekv_decode_step", "sekv_profile_read_overlap", "sekv_append_workspace_bytes",
+    "sekv_append_token",
 ]
 SEKV_FETCH_STAGED, SEKV_FETCH_DIRECT = 0, 1
 SEKV_FAULT_NONE, SEKV_FAULT_GATHER = 0, 1
@@ -41,7 +42,7 @@ class SekvError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_ctx", "n_q_heads", "n_kv_heads", "head_dim", "n_sink", "n_recent", "min_span",
-        "max_span", "dtype", "factors_on_host", "rank_cap", "basis", "route_keys")]
+        "max_span", "dtype", "factors_on_host", "rank_cap", "basis", "route_keys", "sealed", "n_ctx_max")]
 
 
 _p = ctypes.c_void_p
@@ -93,6 +94,9 @@ def _load():
         "sekv_profile_read": (i32, [_p] + [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)] * 3),
         "sekv_profile_read_overlap": (i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
         "sekv_decode_step": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, _p, sz, _p, sz, _p]),
+        "sekv_append_workspace_bytes": (sz, [C, S]),
+        "sekv_append_token": (i32, [_p, C, S, _p, _p, _p, i32, _p, _p, _p, i32, _p, ctypes.POINTER(i64),
+                                    ctypes.POINTER(i64), _p, _p, sz, _p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -132,7 +136,8 @@ def make_config(w, factors_on_host: Optional[bool] = None) -> Config:
                   w.min_span, w.max_span, SEKV_BF16 if w.dtype == "bf16" else SEKV_F32,
                   int(w.factors_on_host if factors_on_host is None else factors_on_host),
                   int(getattr(w, "rank_cap", "full") == "half"), int(getattr(w, "basis", "joint") == "separate"),
-                  int(getattr(w, "route_keys", "rho") == "folded"))
+                  int(getattr(w, "route_keys", "rho") == "folded"), int(getattr(w, "sealed", False)),
+                  int(getattr(w, "n_ctx_max", 0)))
 
 
 def capacities(cfg: Config):
@@ -243,7 +248,9 @@ class SpanCache:
     are pinned host tensors.
     """
 
-    def __init__(self, cfg: Config, plan: Plan, device="cuda"):
+    def __init__(self, cfg: Config, plan: Plan, device="cuda", fac_capacity: int = 0, sg_capacity: int = 0):
+        """fac_capacity / sg_capacity: pool elements to allocate (at least the
+        plan's; more leaves room for spans sealed during decode)."""
         torch = _torch()
         self.cfg = cfg
         self.plan = plan
@@ -263,8 +270,9 @@ class SpanCache:
         self.rho = torch.zeros_like(self.sum_k)
         self.key_scale = torch.zeros((B, Hkv, self.seg_cap), dtype=torch.float32, device=dev)
         self.fold = torch.zeros((Hkv, D, D), dtype=torch.float64, device=dev)
-        nf = max(plan.fac_elems, 8)
-        ng = max(plan.sg_elems, 8)
+        nf = max(plan.fac_elems, fac_capacity, 8)
+        ng = max(plan.sg_elems, sg_capacity, 8)
+        self.fac_used, self.sg_used = plan.fac_elems, plan.sg_elems
         if cfg.factors_on_host:
             self.fac = torch.zeros(nf, dtype=et, pin_memory=True)
             self.sg = torch.zeros(ng, dtype=torch.float32, pin_memory=True)
@@ -327,6 +335,36 @@ def build_spans(ctx: Context, cache: SpanCache, k, v, surprisal: np.ndarray, rou
     st = cache.struct()
     _check(LIB.sekv_build_spans(ctx.handle, ctypes.byref(cfg), _ptr(k), _ptr(v), _ptr(s), _ptr(P), _ptr(g),
                                 g.shape[3], ctypes.byref(st), _stream_handle(stream)))
+
+
+def append_workspace(cache: SpanCache, device="cuda"):
+    torch = _torch()
+    n = LIB.sekv_append_workspace_bytes(ctypes.byref(cache.cfg), ctypes.byref(cache.struct()))
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def append_token(ctx: Context, cache: SpanCache, k_new, v_new, surprisal: np.ndarray, thr: np.ndarray,
+                 route_proj_dev, gate: np.ndarray, rank_req: np.ndarray, ws, stream=None) -> np.ndarray:
+    """sekv_append_token: the cache (sealed layout of cache.cfg.n_ctx tokens)
+    grows by one token; k_new, v_new [B][Hkv][d] device; surprisal [B][>= n_ctx
+    + 1] host; route_proj_dev [Hkv][d][d] f32 device.  Advances cache.cfg.n_ctx
+    and the pools' use; returns the per-sequence sealed flags."""
+    cfg = cache.cfg
+    s = np.ascontiguousarray(surprisal, np.float32)
+    t = np.ascontiguousarray(thr, np.float32)
+    g = np.ascontiguousarray(gate, np.float32)
+    rr = np.ascontiguousarray(rank_req, np.int32)
+    assert g.shape[:3] == (cfg.batch, cfg.n_kv_heads, cache.seg_cap) and rr.shape == (cfg.batch, cache.seg_cap)
+    fu, gu = ctypes.c_int64(cache.fac_used), ctypes.c_int64(cache.sg_used)
+    sealed = np.zeros(cfg.batch, np.int32)
+    st = cache.struct()
+    _check(LIB.sekv_append_token(ctx.handle, ctypes.byref(cfg), ctypes.byref(st), _ptr(k_new), _ptr(v_new), _ptr(s),
+                                 s.shape[1], _ptr(t), _ptr(route_proj_dev), _ptr(g), g.shape[3], _ptr(rr),
+                                 ctypes.byref(fu), ctypes.byref(gu), _ptr(sealed), _ptr(ws), ws.numel(),
+                                 _stream_handle(stream)))
+    cache.fac_used, cache.sg_used = fu.value, gu.value
+    cfg.n_ctx += 1
+    return sealed
 
 
 class RouteOut:

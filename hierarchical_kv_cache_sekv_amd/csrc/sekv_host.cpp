@@ -235,14 +235,20 @@ sekv_status check_config(const sekv_config* c) {
   if (c->rank_cap != 0 && c->rank_cap != 1) return fail(SEKV_EINVAL, "rank_cap must be 0 or 1");
   if (c->basis != 0 && c->basis != 1) return fail(SEKV_EINVAL, "basis must be 0 or 1");
   if (c->route_keys != 0 && c->route_keys != 1) return fail(SEKV_EINVAL, "route_keys must be 0 or 1");
+  if (c->sealed != 0 && c->sealed != 1) return fail(SEKV_EINVAL, "sealed must be 0 or 1");
+  if (c->n_ctx_max < 0) return fail(SEKV_EINVAL, "n_ctx_max %d < 0", c->n_ctx_max);
   return SEKV_OK;
 }
 
+int32_t cap_ctx(const sekv_config* c) { return std::max(c->n_ctx, c->n_ctx_max); }
 int32_t seg_cap_of(const sekv_config* c) {
-  return std::max(0, (c->n_ctx - c->n_sink - c->n_recent) / (c->min_span + 1)) + 1;
+  return std::max(0, (cap_ctx(c) - c->n_sink - c->n_recent) / (c->min_span + 1)) + 1;
 }
+// The sealed layout's tail also holds the undecided tokens (min_span + 1) and
+// the open span's body (at most max_span) before the recent window.
 int32_t full_cap_of(const sekv_config* c) {
-  return std::min<int64_t>(c->n_ctx, (int64_t)c->n_sink + seg_cap_of(c) + c->n_recent + 1);
+  const int64_t extra = c->sealed ? (int64_t)c->min_span + c->max_span : 0;
+  return std::min<int64_t>(cap_ctx(c), (int64_t)c->n_sink + seg_cap_of(c) + c->n_recent + 1 + extra);
 }
 
 const void* device_address(const void* p) {
@@ -344,6 +350,17 @@ int segment_one(const float* s, float thr, const sekv_config* c, int32_t* seg_of
   }
   (void)cap;
   seg_off[n] = tail;
+  if (c->sealed) {
+    // decode-time layout: only the decided heads (t <= e - 1 - lo) stay
+    // heads; the last of them starts the tail
+    int k = 0;
+    while (k < n && seg_off[k] <= e - 1 - lo) ++k;
+    if (k == 0) {
+      seg_off[0] = a;
+      return 0;
+    }
+    return k - 1;
+  }
   return n;
 }
 
@@ -1139,6 +1156,172 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   ctx->host_gather_ms += gather_ms;
   ctx->host_call_ms += std::chrono::duration<double, std::milli>(t_end - t_call).count();
   ctx->host_calls += 1;
+  return SEKV_OK;
+}
+
+// ---------------------------------------------------------------- online sealing
+namespace {
+constexpr int kSealVldsMax = 90;   // longest span whose eigenvectors stay in LDS beside its Gram matrix
+size_t seal_lds_bytes(int L) {
+  const size_t n2 = (size_t)((L + 1) & ~1);
+  return n2 * n2 * sizeof(double) * (L <= kSealVldsMax ? 2 : 1) + (n2 / 2) * 4 * sizeof(double);
+}
+struct SealLayout {
+  size_t desc, weights, gates, vscratch, bytes;
+};
+SealLayout seal_layout(const sekv_config* c) {
+  const size_t B = c->batch, Hkv = c->n_kv_heads;
+  SealLayout l;
+  size_t off = 0;
+  l.desc = off; off = align_up(off + B * sizeof(SealDesc));
+  l.weights = off; off = align_up(off + B * kMaxSpan * sizeof(double));
+  l.gates = off; off = align_up(off + B * Hkv * kMaxSpan * sizeof(float));
+  l.vscratch = off;
+  if (c->max_span > kSealVldsMax) off = align_up(off + B * Hkv * (size_t)kMaxSpan * kMaxSpan * sizeof(double));
+  l.bytes = off;
+  return l;
+}
+}  // namespace
+
+size_t sekv_append_workspace_bytes(const sekv_config* c, const sekv_spans* s) {
+  if (check_config(c) != SEKV_OK || !s) return 0;
+  return seal_layout(c).bytes;
+}
+
+sekv_status sekv_append_token(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* k_new,
+                              const void* v_new, const float* surprisal, int32_t s_stride, const float* boundary_thr,
+                              const float* route_proj, const float* gate, int32_t gate_stride,
+                              const int32_t* rank_req, int64_t* fac_used, int64_t* sg_used, int32_t* sealed_out,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  sekv_status st = check_config(c);
+  if (st != SEKV_OK) return st;
+  if (c->sealed != 1) return fail(SEKV_EINVAL, "sekv_append_token needs the decode-time layout (cfg->sealed = 1)");
+  if (c->basis != 0) return fail(SEKV_EINVAL, "sekv_append_token supports the joint basis (cfg->basis = 0)");
+  st = check_spans(c, s, true);
+  if (st != SEKV_OK) return st;
+  if (!k_new || !v_new || !surprisal || !boundary_thr || !route_proj || !gate || !rank_req || !fac_used || !sg_used ||
+      !ws)
+    return fail(SEKV_EINVAL, "sekv_append_token: a pointer argument is NULL");
+  if (!s->seg_off_host || !s->rank_host || !s->fac_off_host || !s->sg_off_host)
+    return fail(SEKV_EINVAL, "sekv_append_token needs the host arrays of spans");
+  const SealLayout lay = seal_layout(c);
+  if (ws_bytes < lay.bytes) return fail(SEKV_ECAPACITY, "append workspace %zu bytes < %zu needed", ws_bytes, lay.bytes);
+  const int B = c->batch, Hkv = c->n_kv_heads, D = c->head_dim, a = c->n_sink, lo = c->min_span, hi = c->max_span;
+  const int T = c->n_ctx, Tn = T + 1;
+  const int32_t cap = s->seg_cap;
+  if (Tn > cap_ctx(c)) return fail(SEKV_ECAPACITY, "context %d exceeds the capacities' %d", Tn, cap_ctx(c));
+  if (s_stride < Tn) return fail(SEKV_ESHAPE, "s_stride %d < n_ctx + 1 = %d", s_stride, Tn);
+  // decide this step's token of every sequence and lay out the sealed spans
+  std::vector<SealDesc> desc(B);
+  std::vector<double> wts;
+  std::vector<float> gts;
+  int64_t fu = (*fac_used + 7) & ~(int64_t)7, gu = (*sg_used + 3) & ~(int64_t)3;
+  size_t lds = 0;
+  for (int b = 0; b < B; ++b) {
+    SealDesc& d = desc[b];
+    d = SealDesc{};
+    const int ns = s->n_seg_host[b];
+    d.n_full_old = s->n_full_host[b];
+    d.n_seg_old = ns;
+    if (d.n_full_old + 1 > s->full_cap)
+      return fail(SEKV_ECAPACITY, "sequence %d: %d full-resolution rows exceed full_cap %d", b, d.n_full_old + 1, s->full_cap);
+    if (!std::isfinite(boundary_thr[b])) return fail(SEKV_EINVAL, "boundary_thr[%d] is not finite", b);
+    const int t = Tn - c->n_recent - 1 - lo;   // the token decided by this step
+    if (t < a + 1) continue;
+    const float* sb = surprisal + (size_t)b * s_stride;
+    const int h = s->seg_off_host[(size_t)b * (cap + 1) + ns];
+    const int body = t - h - 1;
+    if (body < 0 || body > hi) return fail(SEKV_EINVAL, "sequence %d: span state (tail at %d, token %d) is not the sealed layout of %d tokens", b, h, t, T);
+    if (!std::isfinite(sb[t])) return fail(SEKV_EINVAL, "surprisal[%d][%d] is not finite", b, t);
+    if (!(body == hi || (sb[t] > boundary_thr[b] && body >= lo))) continue;
+    if (ns + 1 > cap) return fail(SEKV_ECAPACITY, "sequence %d: span %d exceeds seg_cap %d", b, ns + 1, cap);
+    const int L = body;
+    const int req = rank_req[(size_t)b * cap + ns];
+    if (req < 1) return fail(SEKV_EINVAL, "rank_req[%d][%d] = %d < 1", b, ns, req);
+    const int r = std::min(std::min(req, c->rank_cap ? (L + 1) / 2 : L), 2 * D);
+    if (r > gate_stride) return fail(SEKV_ESHAPE, "gate_stride %d < rank %d", gate_stride, r);
+    const int rp = (r + 7) & ~7;
+    d.sealed = 1;
+    d.h_old = h;
+    d.h_new = t;
+    d.L = L;
+    d.r = r;
+    d.row0 = a + ns + 1;
+    d.fac_stride = fac_block_elems(L, r, rp, D);
+    d.sg_stride = sg_entry_elems(r);
+    d.fac_base = fu;
+    d.sg_base = gu;
+    fu += (int64_t)Hkv * d.fac_stride;
+    gu += (int64_t)Hkv * d.sg_stride;
+    if (fu > s->fac_elems || gu > s->sg_elems)
+      return fail(SEKV_ECAPACITY, "factor pools hold (%lld, %lld) elements, the sealed spans need (%lld, %lld)",
+                  (long long)s->fac_elems, (long long)s->sg_elems, (long long)fu, (long long)gu);
+    // surprisal weights of the body, as in the prefill build
+    double tot = 0;
+    for (int u = h + 1; u < t; ++u) tot += (double)sb[u];
+    d.w_off = (int)wts.size();
+    for (int u = h + 1; u < t; ++u) wts.push_back(tot > 0 ? (double)sb[u] / tot : 1.0 / L);
+    d.g_off = (int)gts.size();
+    for (int kv = 0; kv < Hkv; ++kv)
+      for (int j = 0; j < r; ++j) gts.push_back(gate[(((size_t)b * Hkv + kv) * cap + ns) * (size_t)gate_stride + j]);
+    lds = std::max(lds, seal_lds_bytes(L));
+  }
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+  char* w8 = static_cast<char*>(ws);
+  // one upload: descriptors, weights and gates at their workspace offsets
+  const size_t up_bytes = gts.empty() ? (wts.empty() ? B * sizeof(SealDesc) : lay.weights + wts.size() * sizeof(double))
+                                      : lay.gates + gts.size() * sizeof(float);
+  std::vector<char> up(up_bytes, 0);
+  std::memcpy(up.data() + lay.desc, desc.data(), B * sizeof(SealDesc));
+  if (!wts.empty()) std::memcpy(up.data() + lay.weights, wts.data(), wts.size() * sizeof(double));
+  if (!gts.empty()) std::memcpy(up.data() + lay.gates, gts.data(), gts.size() * sizeof(float));
+  HIP_OR_FAIL(hipMemcpyAsync(w8, up.data(), up_bytes, hipMemcpyHostToDevice, stream));
+  SealArgs sa{};
+  sa.dtype = c->dtype; sa.B = B; sa.Hkv = Hkv; sa.D = D; sa.seg_cap = cap; sa.full_cap = s->full_cap;
+  sa.vlds_max = kSealVldsMax;
+  sa.desc = reinterpret_cast<const SealDesc*>(w8 + lay.desc);
+  sa.weights = reinterpret_cast<const double*>(w8 + lay.weights);
+  sa.gates = reinterpret_cast<const float*>(w8 + lay.gates);
+  sa.vscratch = reinterpret_cast<double*>(w8 + lay.vscratch);
+  sa.k_new = k_new; sa.v_new = v_new; sa.route_proj = route_proj;
+  sa.full_k = const_cast<void*>(s->full_k); sa.full_v = const_cast<void*>(s->full_v);
+  sa.sum_k = const_cast<void*>(s->sum_k); sa.sum_v = const_cast<void*>(s->sum_v);
+  sa.rho = const_cast<void*>(s->rho); sa.key_scale = const_cast<float*>(s->key_scale);
+  sa.seg_off = const_cast<int32_t*>(s->seg_off); sa.rank = const_cast<int32_t*>(s->rank);
+  sa.fac_off = const_cast<int64_t*>(s->fac_off); sa.sg_off = const_cast<int64_t*>(s->sg_off);
+  if (c->factors_on_host) {
+    sa.fac = const_cast<void*>(device_address(s->fac));
+    sa.sg = static_cast<float*>(const_cast<void*>(device_address(s->sg)));
+    if (!sa.fac || !sa.sg) return fail(SEKV_EHIP, "pinned factor pools have no device address");
+  } else {
+    sa.fac = const_cast<void*>(s->fac);
+    sa.sg = const_cast<float*>(s->sg);
+  }
+  HIP_OR_FAIL(launch_seal(sa, lds, stream));
+  // the host mirrors follow
+  int32_t* n_seg_h = const_cast<int32_t*>(s->n_seg_host);
+  int32_t* n_full_h = const_cast<int32_t*>(s->n_full_host);
+  int32_t* so_h = const_cast<int32_t*>(s->seg_off_host);
+  int32_t* rank_h = const_cast<int32_t*>(s->rank_host);
+  int64_t* fo_h = const_cast<int64_t*>(s->fac_off_host);
+  int64_t* go_h = const_cast<int64_t*>(s->sg_off_host);
+  for (int b = 0; b < B; ++b) {
+    const SealDesc& d = desc[b];
+    if (sealed_out) sealed_out[b] = d.sealed;
+    n_full_h[b] = d.n_full_old + 1 - (d.sealed ? d.L : 0);
+    if (!d.sealed) continue;
+    const int ns = d.n_seg_old;
+    n_seg_h[b] = ns + 1;
+    so_h[(size_t)b * (cap + 1) + ns + 1] = d.h_new;
+    rank_h[(size_t)b * cap + ns] = d.r;
+    for (int kv = 0; kv < Hkv; ++kv) {
+      fo_h[((size_t)b * Hkv + kv) * cap + ns] = d.fac_base + kv * d.fac_stride;
+      go_h[((size_t)b * Hkv + kv) * cap + ns] = d.sg_base + kv * d.sg_stride;
+    }
+  }
+  *fac_used = fu;
+  *sg_used = gu;
   return SEKV_OK;
 }
 

@@ -82,6 +82,35 @@ struct ReconArgs {
   int T;
 };
 
+// One decode step of online sealing, per sequence b (written by the host).
+struct SealDesc {
+  int sealed;          // 1: the newly decided token closes a span this step
+  int n_full_old;      // full-resolution rows before the new token is appended
+  int n_seg_old;       // sealed spans before this step (the new span's index)
+  int h_old, h_new;    // its anchor and its closing head (tokens)
+  int L, r;            // body length and rank of the new span
+  int row0;            // full-resolution row of the first body token
+  int w_off, g_off;    // offsets of its weights (doubles) and gates (floats, [Hkv][r])
+  int64_t fac_base, fac_stride;   // factor block of KV head kv at fac_base + kv * fac_stride
+  int64_t sg_base, sg_stride;     // sigma|gate entry of KV head kv at sg_base + kv * sg_stride
+};
+
+struct SealArgs {
+  int dtype;
+  int B, Hkv, D, seg_cap, full_cap;
+  int rank_cap_unused;
+  int vlds_max;        // largest L whose eigenvector matrix fits in LDS next to the Gram matrix
+  const SealDesc* desc;        // [B] device
+  const double* weights;       // device
+  const float* gates;          // device
+  const void* k_new; const void* v_new;   // [B][Hkv][D]
+  const float* route_proj;     // [Hkv][D][D] device
+  void* full_k; void* full_v; void* sum_k; void* sum_v; void* rho; float* key_scale;
+  void* fac; float* sg;
+  int32_t* seg_off; int32_t* rank; int64_t* fac_off; int64_t* sg_off;
+  double* vscratch;            // [B][Hkv][kMaxSpan][kMaxSpan] eigenvectors of spans longer than vlds_max
+};
+
 // ev0/ev1: optional start/stop events of the kernel itself (both or neither)
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // Route workgroups the device holds at once (occupancy x compute units).
@@ -94,5 +123,9 @@ hipError_t launch_attend_expanded(const AttendArgs& a, hipStream_t s, hipEvent_t
 hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s);
 hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s);
+// Online sealing: append the new token, build the sealed spans (summaries,
+// routing keys, factors, CSR entries), then compact the full-resolution tails.
+// lds_bytes: dynamic LDS of the build kernel.
+hipError_t launch_seal(const SealArgs& a, size_t lds_bytes, hipStream_t s);
 
 }  // namespace sekv

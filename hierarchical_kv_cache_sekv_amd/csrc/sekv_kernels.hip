@@ -1451,6 +1451,331 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
     }                                                                       \
   } while (0)
 
+// ================================================================ online sealing
+// Pages: German explainer, "Methodik" parts 1 (boundaries at high surprisal,
+// spans between anchors) and 2 (per-span summary and low-rank basis); the
+// Chinese explainer, "方法论" parts 1 and 2.  During decode the newest token
+// is appended to the full-resolution tail, and when the token that just got
+// decided closes a span, that span is summarised and factored in place.
+//
+// Build kernel: one workgroup per (b, kv) (256 threads).  Every workgroup
+// appends its new key/value row; a workgroup whose sequence seals a span also
+//   - summarises it: kbar, vbar = sum_t w_t k_t, w_t v_t in fp64, t in order
+//     (the weights w_t = s_t / sum s come from the host), stored rounded;
+//   - computes its routing key rho = P^T (r / |r|), r = P kbar (fp64, index
+//     order), or the key scale 1 / |r|;
+//   - factors M = [K_body | V_body] (L x 2d): the Gram matrix G = M M^T in
+//     fp64, its eigenvectors by cyclic two-sided Jacobi with all L/2 disjoint
+//     rotations of a round-robin step applied at once (rows, then columns and
+//     the eigenvector matrix), then for the r largest eigenvalues
+//     u_j = the eigenvector, w_j = M^T u_j, sigma_j = |w_j|, W column w_j /
+//     sigma_j; each column pair's sign makes u's largest-magnitude entry
+//     positive (first on ties);
+//   - writes the factor block, the sigma|gate entry and its CSR entries.
+// Arithmetic whose result the host builder also produces (summaries, routing
+// key, key scale) follows the builder's operation order with contraction off,
+// so both give the same stored bits.
+template <typename T>
+__device__ __forceinline__ double ld_el(const void* p, size_t i) {
+  if constexpr (sizeof(T) == 2) return (double)__uint_as_float(uint32_t(static_cast<const bf16raw*>(p)[i]) << 16);
+  else return (double)static_cast<const float*>(p)[i];
+}
+// fp64 -> f32 (nearest even) -> storage type (bf16: nearest even on the upper 16 bits)
+template <typename T>
+__device__ __forceinline__ void st_el(void* p, size_t i, double x) {
+  const float f = (float)x;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    static_cast<bf16raw*>(p)[i] = (bf16raw)(u >> 16);
+  } else {
+    static_cast<float*>(p)[i] = f;
+  }
+}
+// value (entry e, dim j) of a (b, kv) block of 32-entry transposed tiles
+__device__ __forceinline__ size_t vt_at(size_t e, int j, int D) { return ((e / 32) * D + j) * 32 + e % 32; }
+
+constexpr int kSealThreads = 256;
+constexpr int kJacobiSweeps = 40;
+constexpr double kJacobiTol = 1e-24;   // (off-diagonal / diagonal Frobenius norm)^2 at convergence
+
+template <typename T, int D>
+__global__ __launch_bounds__(kSealThreads) void seal_build_kernel(const SealArgs a) {
+#pragma clang fp contract(off)
+  extern __shared__ __align__(16) char lds[];
+  __shared__ double s_kbar[D], s_vbar[D], s_r[D];
+  __shared__ double s_red[kSealThreads / 64][2];
+  const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t g = (size_t)b * a.Hkv + kv;
+  const SealDesc& ds = a.desc[b];
+  const int ftiles = (a.full_cap + 31) / 32, stiles = (a.seg_cap + 31) / 32;
+  T* fk = static_cast<T*>(a.full_k) + g * a.full_cap * D;
+  T* fv = static_cast<T*>(a.full_v) + g * ftiles * 32 * D;
+  // the new token at full-resolution row n_full_old
+  for (int j = tid; j < D; j += kSealThreads) {
+    fk[(size_t)ds.n_full_old * D + j] = static_cast<const T*>(a.k_new)[g * D + j];
+    fv[vt_at(ds.n_full_old, j, D)] = static_cast<const T*>(a.v_new)[g * D + j];
+  }
+  if (!ds.sealed) return;
+  const int L = ds.L, r = ds.r, S = ds.n_seg_old;
+  const int rp = (r + 7) & ~7, rq = (r + 3) & ~3;
+  const double* w = a.weights + ds.w_off;
+  // ---- summaries (thread j: one dimension, tokens in order)
+  for (int j = tid; j < D; j += kSealThreads) {
+    double kb = 0.0, vb = 0.0;
+    for (int t = 0; t < L; ++t) {
+      kb += w[t] * ld_el<T>(fk, (size_t)(ds.row0 + t) * D + j);
+      vb += w[t] * ld_el<T>(fv, vt_at(ds.row0 + t, j, D));
+    }
+    s_kbar[j] = kb;
+    s_vbar[j] = vb;
+    st_el<T>(a.sum_k, (g * a.seg_cap + S) * D + j, kb);
+    st_el<T>(static_cast<T*>(a.sum_v) + g * stiles * 32 * D, vt_at(S, j, D), vb);
+  }
+  __syncthreads();
+  // ---- routing key
+  const float* P = a.route_proj + (size_t)kv * D * D;
+  for (int i = tid; i < D; i += kSealThreads) {
+    double acc = 0.0;
+    for (int j = 0; j < D; ++j) acc += (double)P[(size_t)i * D + j] * s_kbar[j];
+    s_r[i] = acc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double nn = 0.0;
+    for (int i = 0; i < D; ++i) nn += s_r[i] * s_r[i];
+    s_red[0][0] = sqrt(nn);
+  }
+  __syncthreads();
+  const double nrm = s_red[0][0];
+  __syncthreads();
+  if (a.rho) {
+    for (int j = tid; j < D; j += kSealThreads) {
+      double acc = 0.0;
+      for (int i = 0; i < D; ++i) acc += (double)P[(size_t)i * D + j] * (nrm > 0 ? s_r[i] / nrm : 0.0);
+      st_el<T>(a.rho, (g * a.seg_cap + S) * D + j, acc);
+    }
+  }
+  if (a.key_scale && tid == 0) a.key_scale[g * a.seg_cap + S] = nrm > 0 ? (float)(1.0 / nrm) : 0.0f;
+
+  // ---- factors: Gram matrix and Jacobi
+  const int n2 = (L + 1) & ~1;                    // even order (a dummy index past L when L is odd)
+  const bool vlds = L <= a.vlds_max;
+  double* G = reinterpret_cast<double*>(lds);     // [n2][n2]
+  double* V = vlds ? G + (size_t)n2 * n2 : a.vscratch + g * kMaxSpan * kMaxSpan;   // [n2][n2]
+  double* rot = G + (size_t)n2 * n2 * (vlds ? 2 : 1);                             // [n2/2]: c, s, (p, q)
+  auto mval = [&](int t, int c) -> double {
+    return c < D ? ld_el<T>(fk, (size_t)(ds.row0 + t) * D + c) : ld_el<T>(fv, vt_at(ds.row0 + t, c - D, D));
+  };
+  for (int e = tid; e < n2 * n2; e += kSealThreads) {
+    const int i = e / n2, j = e % n2;
+    double acc = 0.0;
+    if (i < L && j < L && i <= j)
+      for (int c = 0; c < 2 * D; ++c) acc += mval(i, c) * mval(j, c);
+    if (i <= j) {
+      G[(size_t)i * n2 + j] = acc;
+      G[(size_t)j * n2 + i] = acc;
+    }
+    V[(size_t)i * n2 + j] = i == j ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
+    // stop once the off-diagonal mass is negligible against the diagonal's
+    double off = 0.0, dia = 0.0;
+    for (int e = tid; e < n2 * n2; e += kSealThreads) {
+      const double x = G[e];
+      if (e / n2 == e % n2) dia += x * x;
+      else off += x * x;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      off += __shfl_xor(off, o);
+      dia += __shfl_xor(dia, o);
+    }
+    if (lane == 0) {
+      s_red[wave][0] = off;
+      s_red[wave][1] = dia;
+    }
+    __syncthreads();
+    double offt = 0.0, diat = 0.0;
+    for (int w2 = 0; w2 < kSealThreads / 64; ++w2) {
+      offt += s_red[w2][0];
+      diat += s_red[w2][1];
+    }
+    __syncthreads();   // s_red is rewritten by the next sweep
+    if (!(offt > kJacobiTol * diat)) break;
+    for (int st = 0; st < n2 - 1; ++st) {
+      // round-robin step st: pair k joins (n2 - 1, st) for k = 0, else
+      // ((st + k) mod (n2 - 1), (st - k) mod (n2 - 1))
+      for (int k = tid; k < n2 / 2; k += kSealThreads) {
+        int p = k == 0 ? n2 - 1 : (st + k) % (n2 - 1);
+        int q = k == 0 ? st : (st - k + n2 - 1) % (n2 - 1);
+        if (p > q) { const int x = p; p = q; q = x; }
+        double c = 1.0, s = 0.0;
+        const double apq = G[(size_t)p * n2 + q];
+        if (q < L && apq != 0.0) {
+          const double tau = (G[(size_t)q * n2 + q] - G[(size_t)p * n2 + p]) / (2.0 * apq);
+          const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+          c = 1.0 / sqrt(1.0 + t * t);
+          s = t * c;
+        }
+        rot[4 * k + 0] = c;
+        rot[4 * k + 1] = s;
+        reinterpret_cast<int*>(rot + 4 * k + 2)[0] = p;
+        reinterpret_cast<int*>(rot + 4 * k + 2)[1] = q;
+      }
+      __syncthreads();
+      // rows p, q of G  (G <- J^T G)
+      for (int e = tid; e < (n2 / 2) * n2; e += kSealThreads) {
+        const int k = e / n2, col = e % n2;
+        const double c = rot[4 * k], s = rot[4 * k + 1];
+        const int p = reinterpret_cast<const int*>(rot + 4 * k + 2)[0], q = reinterpret_cast<const int*>(rot + 4 * k + 2)[1];
+        const double gp = G[(size_t)p * n2 + col], gq = G[(size_t)q * n2 + col];
+        G[(size_t)p * n2 + col] = c * gp - s * gq;
+        G[(size_t)q * n2 + col] = s * gp + c * gq;
+      }
+      __syncthreads();
+      // columns p, q of G and of V  (G <- G J, V <- V J)
+      for (int e = tid; e < (n2 / 2) * n2; e += kSealThreads) {
+        const int k = e / n2, row = e % n2;
+        const double c = rot[4 * k], s = rot[4 * k + 1];
+        const int p = reinterpret_cast<const int*>(rot + 4 * k + 2)[0], q = reinterpret_cast<const int*>(rot + 4 * k + 2)[1];
+        const double gp = G[(size_t)row * n2 + p], gq = G[(size_t)row * n2 + q];
+        G[(size_t)row * n2 + p] = c * gp - s * gq;
+        G[(size_t)row * n2 + q] = s * gp + c * gq;
+        const double vp = V[(size_t)row * n2 + p], vq = V[(size_t)row * n2 + q];
+        V[(size_t)row * n2 + p] = c * vp - s * vq;
+        V[(size_t)row * n2 + q] = s * vp + c * vq;
+      }
+      __syncthreads();
+    }
+  }
+  // ---- the r largest eigenvalues: position of eigenvalue i in descending order
+  int* perm = reinterpret_cast<int*>(s_r);         // D doubles hold kMaxSpan ints; s_r is no longer read
+  __syncthreads();
+  for (int i = tid; i < L; i += kSealThreads) {
+    const double li = G[(size_t)i * n2 + i];
+    int pos = 0;
+    for (int j = 0; j < L; ++j) {
+      const double lj = G[(size_t)j * n2 + j];
+      pos += (lj > li || (lj == li && j < i)) ? 1 : 0;
+    }
+    if (pos < r) perm[pos] = i;
+  }
+  __syncthreads();
+  void* fac = a.fac;
+  const int64_t fb = ds.fac_base + (int64_t)kv * ds.fac_stride;
+  const int64_t gb = ds.sg_base + (int64_t)kv * ds.sg_stride;
+  const float* gt = a.gates + ds.g_off + (size_t)kv * r;
+  // one wave per factor column j: sign, U column, W column, sigma
+  for (int j = wave; j < rp; j += kSealThreads / 64) {
+    if (j >= r) {
+      for (int t = lane; t < L; t += 64) st_el<T>(fac, fb + (int64_t)r * D + (int64_t)t * rp + j, 0.0);
+      for (int col = lane; col < D; col += 64) {
+        const int gg = j / 16, wk = min(16, rp - 16 * gg);
+        st_el<T>(fac, fb + (int64_t)r * D + (int64_t)L * rp + (int64_t)gg * 16 * D + (int64_t)col * wk + (j % 16), 0.0);
+      }
+      continue;
+    }
+    const int src = perm[j];
+    // sign: largest |u_t|, first on ties
+    double best = -1.0;
+    int bi = 0;
+    for (int t = lane; t < L; t += 64) {
+      const double x = fabs(V[(size_t)t * n2 + src]);
+      if (x > best) { best = x; bi = t; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const double ob = __shfl_xor(best, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    }
+    const double sgn = V[(size_t)bi * n2 + src] < 0.0 ? -1.0 : 1.0;
+    for (int t = lane; t < L; t += 64) st_el<T>(fac, fb + (int64_t)r * D + (int64_t)t * rp + j, sgn * V[(size_t)t * n2 + src]);
+    // w = M^T u (2d entries, 4 per lane for d = 128), sigma = |w|
+    double wv[2 * D / 64];
+    double ss = 0.0;
+#pragma unroll
+    for (int m = 0; m < 2 * D / 64; ++m) {
+      const int col = lane + 64 * m;
+      double acc = 0.0;
+      for (int t = 0; t < L; ++t) acc += mval(t, col) * (sgn * V[(size_t)t * n2 + src]);
+      wv[m] = acc;
+      ss += acc * acc;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    const double sig = sqrt(ss);
+    const double inv = sig > 0.0 ? 1.0 / sig : 0.0;
+#pragma unroll
+    for (int m = 0; m < 2 * D / 64; ++m) {
+      const int col = lane + 64 * m;
+      if (col < D) {
+        const int ng = D / 8;
+        st_el<T>(fac, fb + (int64_t)j * D + (int64_t)(((col / 8) + j) % ng) * 8 + (col % 8), wv[m] * inv);
+      } else {
+        const int cv = col - D, gg = j / 16, wk = min(16, rp - 16 * gg);
+        st_el<T>(fac, fb + (int64_t)r * D + (int64_t)L * rp + (int64_t)gg * 16 * D + (int64_t)cv * wk + (j % 16),
+                 wv[m] * inv);
+      }
+    }
+    if (lane == 0) {
+      a.sg[gb + j] = (float)sig;
+      a.sg[gb + rq + j] = gt[j];
+    }
+  }
+  for (int j = r + tid; j < rq; j += kSealThreads) {
+    a.sg[gb + j] = 0.0f;
+    a.sg[gb + rq + j] = 0.0f;
+  }
+  // ---- CSR entries of the new span
+  if (tid == 0) {
+    a.fac_off[g * a.seg_cap + S] = fb;
+    a.sg_off[g * a.seg_cap + S] = gb;
+    if (kv == 0) {
+      a.seg_off[(size_t)b * (a.seg_cap + 1) + S + 1] = ds.h_new;
+      a.rank[(size_t)b * a.seg_cap + S] = r;
+    }
+  }
+}
+
+// Compaction of a sealing sequence's full-resolution rows: the body rows
+// [row0, row0 + L) leave, rows [row0 + L, n_full_old + 1) move down by L.
+// Destinations lie below sources, so ascending chunks staged through LDS
+// (all of a chunk read before any of it is written) never overwrite a row
+// still to be read.
+constexpr int kSealChunk = 64;
+template <typename T, int D>
+__global__ __launch_bounds__(kSealThreads) void seal_compact_kernel(const SealArgs a) {
+  __shared__ T buf[kSealChunk * D];
+  const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const SealDesc& ds = a.desc[b];
+  if (!ds.sealed) return;
+  const size_t g = (size_t)b * a.Hkv + kv;
+  const int ftiles = (a.full_cap + 31) / 32;
+  T* fk = static_cast<T*>(a.full_k) + g * a.full_cap * D;
+  T* fv = static_cast<T*>(a.full_v) + g * ftiles * 32 * D;
+  const int L = ds.L, s0 = ds.row0 + L, s1 = ds.n_full_old + 1;
+  for (int c0 = s0; c0 < s1; c0 += kSealChunk) {
+    const int nrow = min(kSealChunk, s1 - c0);
+    for (int e = tid; e < nrow * D; e += kSealThreads) buf[e] = fk[(size_t)(c0 + e / D) * D + e % D];
+    __syncthreads();
+    for (int e = tid; e < nrow * D; e += kSealThreads) fk[(size_t)(c0 - L + e / D) * D + e % D] = buf[e];
+    __syncthreads();
+    for (int e = tid; e < nrow * D; e += kSealThreads) buf[e] = fv[vt_at(c0 + e / D, e % D, D)];
+    __syncthreads();
+    for (int e = tid; e < nrow * D; e += kSealThreads) fv[vt_at(c0 - L + e / D, e % D, D)] = buf[e];
+    __syncthreads();
+  }
+  // the vacated rows past the new end hold zeros (padding stays finite)
+  for (int e = tid; e < L * D; e += kSealThreads) {
+    const int row = s1 - L + e / D, j = e % D;
+    fk[(size_t)row * D + j] = T(0);
+    fv[vt_at(row, j, D)] = T(0);
+  }
+}
+
 // ---------------------------------------------------------------- route scratch
 // State of sekv_route_noalloc: the route workspace (tickets and status words)
 // held in a file-scope device array.  Every GPU the library runs on holds its
@@ -1562,6 +1887,43 @@ hipError_t launch_attend_fused(const AttendArgs& a, hipStream_t s, hipEvent_t ev
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   SEKV_DISPATCH_D(a.D, G, (combine_kernel<DD, GG><<<a.B * a.Hq * (DD / 32), kCombineThreads, 0, s>>>(a)));
+  return hipGetLastError();
+}
+
+hipError_t launch_seal(const SealArgs& a, size_t lds_bytes, hipStream_t s) {
+  const dim3 grid(a.Hkv, a.B);
+  hipError_t e = hipSuccess;
+  if (a.dtype == 0) {
+    if (a.D == 64) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&seal_build_kernel<float, 64>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+      if (e == hipSuccess) seal_build_kernel<float, 64><<<grid, kSealThreads, lds_bytes, s>>>(a);
+    } else {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&seal_build_kernel<float, 128>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+      if (e == hipSuccess) seal_build_kernel<float, 128><<<grid, kSealThreads, lds_bytes, s>>>(a);
+    }
+  } else {
+    if (a.D == 64) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&seal_build_kernel<bf16raw, 64>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+      if (e == hipSuccess) seal_build_kernel<bf16raw, 64><<<grid, kSealThreads, lds_bytes, s>>>(a);
+    } else {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&seal_build_kernel<bf16raw, 128>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+      if (e == hipSuccess) seal_build_kernel<bf16raw, 128><<<grid, kSealThreads, lds_bytes, s>>>(a);
+    }
+  }
+  if (e != hipSuccess) return e;
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.dtype == 0) {
+    if (a.D == 64) seal_compact_kernel<float, 64><<<grid, kSealThreads, 0, s>>>(a);
+    else seal_compact_kernel<float, 128><<<grid, kSealThreads, 0, s>>>(a);
+  } else {
+    if (a.D == 64) seal_compact_kernel<bf16raw, 64><<<grid, kSealThreads, 0, s>>>(a);
+    else seal_compact_kernel<bf16raw, 128><<<grid, kSealThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -86,6 +86,9 @@ typedef struct sekv_config {
   int32_t basis;           /* 0: one basis for [K | V]; 1: separate K and V bases   */
   int32_t route_keys;      /* 0: route on rho; 1: route on kbar with key_scale and
                               the fold matrix (P^T P q) . kbar / |P kbar|         */
+  /* Decode-time layout (online sealing, sekv_append_token): */
+  int32_t sealed;          /* 0: prefill layout; 1: only sealed spans (below)      */
+  int32_t n_ctx_max;       /* capacities are sized for max(n_ctx, n_ctx_max)       */
 } sekv_config;
 
 /*
@@ -362,6 +365,63 @@ sekv_status sekv_decode_step(sekv_ctx* ctx, const sekv_config* cfg, const sekv_s
                              const float* theta, int32_t* exp_list, uint8_t* exp_mask, int32_t* exp_count,
                              float* out, void* route_ws, size_t route_ws_bytes, void* dev_ws, size_t dev_ws_bytes,
                              hipStream_t stream);
+
+/*
+ * Online span sealing (decode-time layout).  [de-1], [zh-1] place span
+ * boundaries at high-surprisal tokens and define the segmentation at prefill;
+ * during decode new tokens keep leaving the recent window.  Reading: the
+ * boundary rule of sekv_plan_spans decides token t for good once
+ * t <= T - n_recent - 1 - min_span (its room before the recent window then
+ * holds at every longer context, and the forced-head test never depended on
+ * it); a span seals when its closing head is decided.  With cfg->sealed = 1,
+ * sekv_plan_spans returns only the sealed spans of a context: heads up to that
+ * token, the last of them starting the full-resolution tail (which then also
+ * holds the undecided tokens and the open span's body).  Capacities (seg_cap,
+ * full_cap) follow max(n_ctx, n_ctx_max), so a cache can be allocated once for
+ * the longest context it will reach.
+ */
+size_t sekv_append_workspace_bytes(const sekv_config* cfg, const sekv_spans* spans);
+
+/*
+ * sekv_append_token - one decode step of online sealing: the context grows
+ * from cfg->n_ctx to n_ctx + 1 tokens.  The new token's key and value are
+ * appended to every (b, kv) full-resolution tail; the one token this step
+ * decides (T + 1 - n_recent - 1 - min_span) becomes a head when its body since
+ * the last sealed head has reached max_span, or when surprisal[b][t] >
+ * boundary_thr[b] and the body holds at least min_span tokens; a new head
+ * seals the span before it ([de-1], [zh-1]), which is then summarised, given
+ * its routing key (or key scale) and factored exactly as sekv_build_spans does
+ * ([de-2], [zh-2]; summaries and routing keys in the builder's fp64 operation
+ * order, the rank-r factors from the fp64 Gram matrix's Jacobi eigenvectors),
+ * its body rows leave the full-resolution tail and its factor block and
+ * sigma|gate entry are appended to the pools.
+ *   cfg: sealed = 1, basis = 0; n_ctx = T, the context before the call.
+ *   spans: the cache of the sealed layout of T tokens.  Written in place:
+ *     device arrays, pools (pinned host pools through their device
+ *     addresses) and the host arrays n_seg_host, n_full_host, seg_off_host,
+ *     rank_host, fac_off_host, sg_off_host (the pointers must be writable).
+ *     Entries of seg_off (device and host) past n_seg are left as they were.
+ *   k_new, v_new [B][Hkv][d] dtype: device, read.
+ *   surprisal [B][s_stride] f32: host, entries [0, T] (the new token's at T).
+ *   boundary_thr [B] f32: host.  route_proj [Hkv][d][d] f32: device.
+ *   gate [B][Hkv][seg_cap][gate_stride] f32, rank_req [B][seg_cap]: host,
+ *     indexed by span as in sekv_build_spans.
+ *   fac_used, sg_used: in/out, pool elements in use (sekv_plan_spans'
+ *     fac_elems / sg_elems after a build); spans->fac_elems / sg_elems are
+ *     the pools' capacities.
+ *   sealed_out [B] int32 host (may be NULL): 1 where a span sealed.
+ *   ws: device workspace of sekv_append_workspace_bytes.
+ * Enqueued on stream (small host-to-device copies, then two kernels); the
+ * host arrays are updated before the call returns.  After it the cache holds
+ * the sealed layout of T + 1 tokens: set cfg->n_ctx = T + 1 for later calls.
+ * Errors (nothing written): SEKV_EINVAL / SEKV_ESHAPE / SEKV_ECAPACITY
+ * (n_ctx_max, seg_cap, full_cap or the pools would overflow) / SEKV_EHIP.
+ */
+sekv_status sekv_append_token(sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans, const void* k_new,
+                              const void* v_new, const float* surprisal, int32_t s_stride,
+                              const float* boundary_thr, const float* route_proj, const float* gate,
+                              int32_t gate_stride, const int32_t* rank_req, int64_t* fac_used, int64_t* sg_used,
+                              int32_t* sealed_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * sekv_dense_attention_decode - the dense baseline: plain softmax attention of
