@@ -330,7 +330,8 @@ def measure_device(w, x, fracs, args, label, full_rank=False):
     B.build_spans(ctx, cache, kd, vd, x.surprisal, x.route_proj, x.gate)
     del kd, vd
     torch.cuda.synchronize()
-    log(f"{label}: library build (plan + summaries + rank-r factors) in {time.time() - t0:.1f}s; "
+    build_s = time.time() - t0
+    log(f"{label}: library build (plan + summaries + rank-r factors) in {build_s:.2f}s; "
         f"n_seg={plan.n_seg.tolist()}")
     qd = torch.from_numpy(x.q[:Q]).to(cache.elem).cuda().contiguous()
     resident = cache.device_bytes()
@@ -459,6 +460,8 @@ def measure_device(w, x, fracs, args, label, full_rank=False):
                          "duration_source": "HIP events around each launch on its stream, eager pass over the "
                                             "same steps as the timed region"},
             "memory": resident_bytes(w, plan, cache),
+            "build": {"seconds": build_s, "where": "device" if w.basis == "joint" else "host",
+                      "includes": "plan, K/V upload, summaries, routing keys, factors, synchronised"},
         }
         recs.append((rec, theta))
     ctx.close()

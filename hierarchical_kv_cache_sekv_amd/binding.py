@@ -27,10 +27,11 @@ EXPORTS = [
     "sekv_profile_enable", "sekv_profile_read", "sekv_ctx_set_split", "sekv_ctx_set_fetch_mode",
     "sekv_ctx_inject_fault", "sekv_profile_read_host", "sekv_route_noalloc", "sekv_dense_workspace_bytes",
     "sekv_dense_attention_decode", "sekv_decode_step", "sekv_profile_read_overlap", "sekv_append_workspace_bytes",
-    "sekv_append_token",
+    "sekv_append_token", "sekv_ctx_set_build_mode",
 ]
 SEKV_FETCH_STAGED, SEKV_FETCH_DIRECT = 0, 1
 SEKV_FAULT_NONE, SEKV_FAULT_GATHER = 0, 1
+SEKV_BUILD_DEVICE, SEKV_BUILD_HOST = 0, 1
 
 
 class SekvError(RuntimeError):
@@ -88,6 +89,7 @@ def _load():
         "sekv_ctx_set_split": (i32, [_p, i32]),
         "sekv_ctx_set_fetch_mode": (i32, [_p, i32]),
         "sekv_ctx_inject_fault": (i32, [_p, i32]),
+        "sekv_ctx_set_build_mode": (i32, [_p, i32]),
         "sekv_profile_read_host": (i32, [_p] + [ctypes.POINTER(ctypes.c_double)] * 3 + [ctypes.POINTER(i64)]),
         "sekv_mixed_attention_decode": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, sz, _p, sz, _p, _p]),
         "sekv_profile_enable": (i32, [_p, i32]),
@@ -208,6 +210,10 @@ class Context:
 
     def set_fetch_mode(self, mode: int):
         _check(LIB.sekv_ctx_set_fetch_mode(self.handle, int(mode)))
+
+    def set_build_mode(self, mode: int):
+        """Where sekv_build_spans works: SEKV_BUILD_DEVICE (default) or SEKV_BUILD_HOST."""
+        _check(LIB.sekv_ctx_set_build_mode(self.handle, int(mode)))
 
     def inject_fault(self, fault: int):
         _check(LIB.sekv_ctx_inject_fault(self.handle, int(fault)))

@@ -146,6 +146,7 @@ struct sekv_ctx {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;    // its fork / join points
   int32_t split_entries = 0;      // full-resolution entries per split-K chunk (0: automatic)
   int32_t fetch_mode = SEKV_FETCH_DIRECT;
+  int32_t build_mode = SEKV_BUILD_DEVICE;
   int32_t fault = SEKV_FAULT_NONE;  // injected failure of the next host-resident decode
   void* route_scratch = nullptr;      // this device's static route state (sekv_route_noalloc)
   int route_resident[2][2][4][2] = {};  // route workgroups resident at once, by dtype, d == 128, log2 G, fold
@@ -559,6 +560,120 @@ sekv_status sekv_plan_spans(const sekv_config* c, const float* surprisal, const 
   return SEKV_OK;
 }
 
+namespace {
+size_t seal_lds_bytes(int L);
+constexpr int kBuildVldsMax = 90;   // longest span whose eigenvectors stay in LDS beside its Gram matrix
+
+// Device arrays a call allocates for itself and frees on every return path.
+struct DevBuffers {
+  std::vector<void*> p;
+  ~DevBuffers() {
+    for (void* x : p) (void)hipFree(x);
+  }
+  hipError_t alloc(void** out, size_t bytes) {
+    *out = nullptr;
+    if (bytes == 0) return hipSuccess;
+    const hipError_t e = hipMalloc(out, bytes);
+    if (e == hipSuccess) p.push_back(*out);
+    return e;
+  }
+};
+
+// sekv_build_spans on the GPU (joint basis): the plan's offsets, per-token
+// surprisal weights, projections and gates go up; the full-resolution rows
+// are gathered and every span built by kernels; the fold matrices stay host
+// work.
+sekv_status build_on_device(sekv_ctx* ctx, const sekv_config* c, const void* k, const void* v, const float* surprisal,
+                            const float* route_proj, const float* gate, int32_t gate_stride, const sekv_spans* s,
+                            int64_t need_f, int64_t need_g, hipStream_t stream) {
+  const int B = c->batch, T = c->n_ctx, Hkv = c->n_kv_heads, D = c->head_dim, dt = c->dtype;
+  const int es = elem_size(dt);
+  const int32_t cap = s->seg_cap, fcap = s->full_cap;
+  // surprisal weight of every body token within its span (as the host build)
+  std::vector<double> wts((size_t)B * T, 0.0);
+  int n_items = 0;
+  BuildArgs ba{};
+  for (int b = 0; b < B; ++b) {
+    const int32_t* so = s->seg_off_host + (size_t)b * (cap + 1);
+    const float* sb = surprisal + (size_t)b * T;
+    const int ns = s->n_seg_host[b];
+    for (int i = 0; i < ns; ++i) {
+      const int t0 = so[i] + 1, t1 = so[i + 1], L = t1 - t0;
+      double tot = 0;
+      for (int t = t0; t < t1; ++t) tot += (double)sb[t];
+      for (int t = t0; t < t1; ++t) wts[(size_t)b * T + t] = tot > 0 ? (double)sb[t] / tot : 1.0 / L;
+    }
+    ba.item_base[b] = n_items;
+    ba.n_seg[b] = ns;
+    ba.n_full[b] = s->n_full_host[b];
+    n_items += Hkv * ns;
+  }
+  const size_t lds = std::max(seal_lds_bytes(std::min(c->max_span, kBuildVldsMax)), seal_lds_bytes(c->max_span));
+  ba.dtype = dt; ba.B = B; ba.Hkv = Hkv; ba.D = D; ba.T = T; ba.seg_cap = cap; ba.full_cap = fcap;
+  ba.n_sink = c->n_sink; ba.gate_stride = gate_stride; ba.vlds_max = kBuildVldsMax; ba.n_items = n_items;
+  int resident = 0;
+  HIP_OR_FAIL(build_resident_blocks(ba, lds, ctx->device, &resident));
+  if (resident <= 0) return fail(SEKV_EHIP, "the span build kernel does not fit on the device");
+  const int grid = std::max(1, std::min(n_items, resident));
+  DevBuffers buf;
+  void *d_w, *d_p, *d_g, *d_vs;
+  HIP_OR_FAIL(buf.alloc(&d_w, wts.size() * sizeof(double)));
+  HIP_OR_FAIL(buf.alloc(&d_p, (size_t)Hkv * D * D * sizeof(float)));
+  HIP_OR_FAIL(buf.alloc(&d_g, (size_t)B * Hkv * cap * gate_stride * sizeof(float)));
+  HIP_OR_FAIL(buf.alloc(&d_vs, c->max_span > kBuildVldsMax ? (size_t)grid * kMaxSpan * kMaxSpan * sizeof(double) : 0));
+  auto up = [&](const void* dst, const void* src, size_t bytes) -> hipError_t {
+    return hipMemcpyAsync(const_cast<void*>(dst), src, bytes, hipMemcpyHostToDevice, stream);
+  };
+  HIP_OR_FAIL(up(d_w, wts.data(), wts.size() * sizeof(double)));
+  HIP_OR_FAIL(up(d_p, route_proj, (size_t)Hkv * D * D * sizeof(float)));
+  HIP_OR_FAIL(up(d_g, gate, (size_t)B * Hkv * cap * gate_stride * sizeof(float)));
+  HIP_OR_FAIL(up(s->seg_off, s->seg_off_host, (size_t)B * (cap + 1) * sizeof(int32_t)));
+  HIP_OR_FAIL(up(s->rank, s->rank_host, (size_t)B * cap * sizeof(int32_t)));
+  HIP_OR_FAIL(up(s->fac_off, s->fac_off_host, (size_t)B * Hkv * cap * sizeof(int64_t)));
+  HIP_OR_FAIL(up(s->sg_off, s->sg_off_host, (size_t)B * Hkv * cap * sizeof(int64_t)));
+  // every output starts at zero (padding rows and entries stay zero, as in the host build)
+  const int ftiles = (fcap + 31) / 32, stiles = (cap + 31) / 32;
+  const size_t BG = (size_t)B * Hkv;
+  HIP_OR_FAIL(hipMemsetAsync(const_cast<void*>(s->full_k), 0, BG * fcap * D * es, stream));
+  HIP_OR_FAIL(hipMemsetAsync(const_cast<void*>(s->full_v), 0, BG * ftiles * 32 * D * es, stream));
+  HIP_OR_FAIL(hipMemsetAsync(const_cast<void*>(s->sum_k), 0, BG * cap * D * es, stream));
+  HIP_OR_FAIL(hipMemsetAsync(const_cast<void*>(s->sum_v), 0, BG * stiles * 32 * D * es, stream));
+  if (s->rho) HIP_OR_FAIL(hipMemsetAsync(const_cast<void*>(s->rho), 0, BG * cap * D * es, stream));
+  if (s->key_scale) HIP_OR_FAIL(hipMemsetAsync(const_cast<float*>(s->key_scale), 0, BG * cap * sizeof(float), stream));
+  void* fac = const_cast<void*>(s->fac);
+  float* sg = const_cast<float*>(s->sg);
+  if (c->factors_on_host) {
+    HIP_OR_FAIL(hipStreamSynchronize(stream));
+    std::memset(fac, 0, (size_t)need_f * es);
+    std::memset(sg, 0, (size_t)need_g * sizeof(float));
+    fac = const_cast<void*>(device_address(s->fac));
+    sg = static_cast<float*>(const_cast<void*>(device_address(s->sg)));
+    if (!fac || !sg) return fail(SEKV_EHIP, "pinned factor pools have no device address");
+  } else {
+    HIP_OR_FAIL(hipMemsetAsync(fac, 0, (size_t)need_f * es, stream));
+    HIP_OR_FAIL(hipMemsetAsync(sg, 0, (size_t)need_g * sizeof(float), stream));
+  }
+  ba.seg_off = s->seg_off; ba.rank = s->rank; ba.fac_off = s->fac_off; ba.sg_off = s->sg_off;
+  ba.weights = static_cast<const double*>(d_w);
+  ba.route_proj = static_cast<const float*>(d_p);
+  ba.gates = static_cast<const float*>(d_g);
+  ba.k = k; ba.v = v;
+  ba.full_k = const_cast<void*>(s->full_k); ba.full_v = const_cast<void*>(s->full_v);
+  ba.sum_k = const_cast<void*>(s->sum_k); ba.sum_v = const_cast<void*>(s->sum_v);
+  ba.rho = const_cast<void*>(s->rho); ba.key_scale = const_cast<float*>(s->key_scale);
+  ba.fac = fac; ba.sg = sg;
+  ba.vscratch = static_cast<double*>(d_vs);
+  HIP_OR_FAIL(launch_build(ba, grid, lds, stream));
+  if (s->fold) {
+    std::vector<double> fold((size_t)Hkv * D * D, 0.0);
+    for (int kv = 0; kv < Hkv; ++kv) fold_matrix(route_proj + (size_t)kv * D * D, D, fold.data() + (size_t)kv * D * D);
+    HIP_OR_FAIL(up(s->fold, fold.data(), fold.size() * sizeof(double)));
+  }
+  HIP_OR_FAIL(hipStreamSynchronize(stream));
+  return SEKV_OK;
+}
+}  // namespace
+
 sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k, const void* v, const float* surprisal,
                              const float* route_proj, const float* gate, int32_t gate_stride, const sekv_spans* s,
                              hipStream_t stream) {
@@ -594,6 +709,8 @@ sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* c, const void* k,
     return fail(SEKV_ECAPACITY, "factor pools hold (%lld, %lld) elements, plan needs (%lld, %lld)", (long long)s->fac_elems,
                 (long long)s->sg_elems, (long long)need_f, (long long)need_g);
   HIP_OR_FAIL(hipSetDevice(ctx->device));
+  if (ctx->build_mode == SEKV_BUILD_DEVICE && c->basis == 0)
+    return build_on_device(ctx, c, k, v, surprisal, route_proj, gate, gate_stride, s, need_f, need_g, stream);
 
   const size_t kv_elems = (size_t)B * Hkv * T * D;
   std::vector<char> hk(kv_elems * es), hv(kv_elems * es);
@@ -1443,6 +1560,13 @@ sekv_status sekv_ctx_set_fetch_mode(sekv_ctx* ctx, int32_t mode) {
   if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
   if (mode != SEKV_FETCH_STAGED && mode != SEKV_FETCH_DIRECT) return fail(SEKV_EINVAL, "fetch mode %d is not SEKV_FETCH_STAGED or SEKV_FETCH_DIRECT", mode);
   ctx->fetch_mode = mode;
+  return SEKV_OK;
+}
+
+sekv_status sekv_ctx_set_build_mode(sekv_ctx* ctx, int32_t mode) {
+  if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
+  if (mode != SEKV_BUILD_DEVICE && mode != SEKV_BUILD_HOST) return fail(SEKV_EINVAL, "build mode %d is not SEKV_BUILD_DEVICE or SEKV_BUILD_HOST", mode);
+  ctx->build_mode = mode;
   return SEKV_OK;
 }
 

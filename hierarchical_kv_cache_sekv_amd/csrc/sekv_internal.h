@@ -111,6 +111,23 @@ struct SealArgs {
   double* vscratch;            // [B][Hkv][kMaxSpan][kMaxSpan] eigenvectors of spans longer than vlds_max
 };
 
+// Prefill build on the GPU (every span of the plan).
+struct BuildArgs {
+  int dtype;
+  int B, Hkv, D, T, seg_cap, full_cap, n_sink, gate_stride, vlds_max;
+  int n_items;                 // spans of all (b, kv)
+  int item_base[kMaxBatch];    // first item of sequence b (its Hkv groups' spans follow in kv order)
+  int n_seg[kMaxBatch], n_full[kMaxBatch];
+  const int32_t* seg_off; const int32_t* rank; const int64_t* fac_off; const int64_t* sg_off;   // device
+  const double* weights;       // [B][T] surprisal weight of each body token within its span
+  const float* route_proj;     // [Hkv][D][D]
+  const float* gates;          // [B][Hkv][seg_cap][gate_stride]
+  const void* k; const void* v;   // [B][Hkv][T][D]
+  void* full_k; void* full_v; void* sum_k; void* sum_v; void* rho; float* key_scale;
+  void* fac; float* sg;
+  double* vscratch;            // [grid][kMaxSpan][kMaxSpan]
+};
+
 // ev0/ev1: optional start/stop events of the kernel itself (both or neither)
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // Route workgroups the device holds at once (occupancy x compute units).
@@ -127,5 +144,10 @@ hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s);
 // routing keys, factors, CSR entries), then compact the full-resolution tails.
 // lds_bytes: dynamic LDS of the build kernel.
 hipError_t launch_seal(const SealArgs& a, size_t lds_bytes, hipStream_t s);
+// Prefill build: full-resolution rows, then every span (persistent grid of
+// `grid` workgroups, dynamic LDS lds_bytes).
+hipError_t launch_build(const BuildArgs& a, int grid, size_t lds_bytes, hipStream_t s);
+// Workgroups of the span build kernel resident at once with lds_bytes of dynamic LDS.
+hipError_t build_resident_blocks(const BuildArgs& a, size_t lds_bytes, int device, int* blocks);
 
 }  // namespace sekv

@@ -1499,42 +1499,65 @@ constexpr int kSealThreads = 256;
 constexpr int kJacobiSweeps = 40;
 constexpr double kJacobiTol = 1e-24;   // (off-diagonal / diagonal Frobenius norm)^2 at convergence
 
+// What one span's build needs and where it goes.
+struct SpanJob {
+  int L, r, S;            // body length, rank, span index
+  size_t g;               // (b, kv) group
+  const double* w;        // body weights [L]
+  const float* P;         // routing projection of the KV head [D][D]
+  const float* gt;        // gates [r]
+  int64_t fb, gb;         // factor block and sigma|gate entry (pool element offsets)
+  double* vscr;           // [kMaxSpan][kMaxSpan] eigenvectors when L > vlds_max
+};
+struct SpanDst {
+  int seg_cap, vlds_max;
+  void* sum_k; void* sum_v; void* rho; float* key_scale;
+  void* fac; float* sg;
+};
+// Body rows in the full-resolution rows of a (b, kv) (keys row-major, values
+// in transposed 32-entry tiles), from row row0 on.
 template <typename T, int D>
-__global__ __launch_bounds__(kSealThreads) void seal_build_kernel(const SealArgs a) {
+struct RowsFull {
+  const T* fk; const T* fv; int row0;
+  __device__ double k(int t, int c) const { return ld_el<T>(fk, (size_t)(row0 + t) * D + c); }
+  __device__ double v(int t, int c) const { return ld_el<T>(fv, vt_at(row0 + t, c, D)); }
+};
+// Body rows in the prefill keys and values [T][D] of a (b, kv), from token t0 on.
+template <typename T, int D>
+struct RowsRaw {
+  const T* kp; const T* vp; int t0;
+  __device__ double k(int t, int c) const { return ld_el<T>(kp, (size_t)(t0 + t) * D + c); }
+  __device__ double v(int t, int c) const { return ld_el<T>(vp, (size_t)(t0 + t) * D + c); }
+};
+
+// One span: summaries, routing key or key scale, factors and sigma|gate entry
+// (all threads of the workgroup; lds: seal_lds_bytes(L) bytes).
+template <typename T, int D, class Rows>
+__device__ void build_span(const Rows& rows, const SpanJob& j, const SpanDst& o, char* lds, double* s_kbar,
+                           double* s_vbar, double* s_r, double (*s_red)[2]) {
 #pragma clang fp contract(off)
-  extern __shared__ __align__(16) char lds[];
-  __shared__ double s_kbar[D], s_vbar[D], s_r[D];
-  __shared__ double s_red[kSealThreads / 64][2];
-  const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t g = (size_t)b * a.Hkv + kv;
-  const SealDesc& ds = a.desc[b];
-  const int ftiles = (a.full_cap + 31) / 32, stiles = (a.seg_cap + 31) / 32;
-  T* fk = static_cast<T*>(a.full_k) + g * a.full_cap * D;
-  T* fv = static_cast<T*>(a.full_v) + g * ftiles * 32 * D;
-  // the new token at full-resolution row n_full_old
-  for (int j = tid; j < D; j += kSealThreads) {
-    fk[(size_t)ds.n_full_old * D + j] = static_cast<const T*>(a.k_new)[g * D + j];
-    fv[vt_at(ds.n_full_old, j, D)] = static_cast<const T*>(a.v_new)[g * D + j];
-  }
-  if (!ds.sealed) return;
-  const int L = ds.L, r = ds.r, S = ds.n_seg_old;
+  const int L = j.L, r = j.r, S = j.S;
+  const size_t g = j.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int stiles = (o.seg_cap + 31) / 32;
+  __syncthreads();   // LDS of the previous span is no longer read
   const int rp = (r + 7) & ~7, rq = (r + 3) & ~3;
-  const double* w = a.weights + ds.w_off;
+  const double* w = j.w;
   // ---- summaries (thread j: one dimension, tokens in order)
-  for (int j = tid; j < D; j += kSealThreads) {
+  for (int jj = tid; jj < D; jj += kSealThreads) {
     double kb = 0.0, vb = 0.0;
     for (int t = 0; t < L; ++t) {
-      kb += w[t] * ld_el<T>(fk, (size_t)(ds.row0 + t) * D + j);
-      vb += w[t] * ld_el<T>(fv, vt_at(ds.row0 + t, j, D));
+      kb += w[t] * rows.k(t, jj);
+      vb += w[t] * rows.v(t, jj);
     }
-    s_kbar[j] = kb;
-    s_vbar[j] = vb;
-    st_el<T>(a.sum_k, (g * a.seg_cap + S) * D + j, kb);
-    st_el<T>(static_cast<T*>(a.sum_v) + g * stiles * 32 * D, vt_at(S, j, D), vb);
+    s_kbar[jj] = kb;
+    s_vbar[jj] = vb;
+    st_el<T>(o.sum_k, (g * o.seg_cap + S) * D + jj, kb);
+    st_el<T>(static_cast<T*>(o.sum_v) + g * stiles * 32 * D, vt_at(S, jj, D), vb);
   }
   __syncthreads();
   // ---- routing key
-  const float* P = a.route_proj + (size_t)kv * D * D;
+  const float* P = j.P;
   for (int i = tid; i < D; i += kSealThreads) {
     double acc = 0.0;
     for (int j = 0; j < D; ++j) acc += (double)P[(size_t)i * D + j] * s_kbar[j];
@@ -1549,24 +1572,22 @@ __global__ __launch_bounds__(kSealThreads) void seal_build_kernel(const SealArgs
   __syncthreads();
   const double nrm = s_red[0][0];
   __syncthreads();
-  if (a.rho) {
-    for (int j = tid; j < D; j += kSealThreads) {
+  if (o.rho) {
+    for (int jj = tid; jj < D; jj += kSealThreads) {
       double acc = 0.0;
-      for (int i = 0; i < D; ++i) acc += (double)P[(size_t)i * D + j] * (nrm > 0 ? s_r[i] / nrm : 0.0);
-      st_el<T>(a.rho, (g * a.seg_cap + S) * D + j, acc);
+      for (int i = 0; i < D; ++i) acc += (double)P[(size_t)i * D + jj] * (nrm > 0 ? s_r[i] / nrm : 0.0);
+      st_el<T>(o.rho, (g * o.seg_cap + S) * D + jj, acc);
     }
   }
-  if (a.key_scale && tid == 0) a.key_scale[g * a.seg_cap + S] = nrm > 0 ? (float)(1.0 / nrm) : 0.0f;
+  if (o.key_scale && tid == 0) o.key_scale[g * o.seg_cap + S] = nrm > 0 ? (float)(1.0 / nrm) : 0.0f;
 
   // ---- factors: Gram matrix and Jacobi
   const int n2 = (L + 1) & ~1;                    // even order (a dummy index past L when L is odd)
-  const bool vlds = L <= a.vlds_max;
+  const bool vlds = L <= o.vlds_max;
   double* G = reinterpret_cast<double*>(lds);     // [n2][n2]
-  double* V = vlds ? G + (size_t)n2 * n2 : a.vscratch + g * kMaxSpan * kMaxSpan;   // [n2][n2]
+  double* V = vlds ? G + (size_t)n2 * n2 : j.vscr;   // [n2][n2]
   double* rot = G + (size_t)n2 * n2 * (vlds ? 2 : 1);                             // [n2/2]: c, s, (p, q)
-  auto mval = [&](int t, int c) -> double {
-    return c < D ? ld_el<T>(fk, (size_t)(ds.row0 + t) * D + c) : ld_el<T>(fv, vt_at(ds.row0 + t, c - D, D));
-  };
+  auto mval = [&](int t, int c) -> double { return c < D ? rows.k(t, c) : rows.v(t, c - D); };
   for (int e = tid; e < n2 * n2; e += kSealThreads) {
     const int i = e / n2, j = e % n2;
     double acc = 0.0;
@@ -1663,21 +1684,20 @@ __global__ __launch_bounds__(kSealThreads) void seal_build_kernel(const SealArgs
     if (pos < r) perm[pos] = i;
   }
   __syncthreads();
-  void* fac = a.fac;
-  const int64_t fb = ds.fac_base + (int64_t)kv * ds.fac_stride;
-  const int64_t gb = ds.sg_base + (int64_t)kv * ds.sg_stride;
-  const float* gt = a.gates + ds.g_off + (size_t)kv * r;
-  // one wave per factor column j: sign, U column, W column, sigma
-  for (int j = wave; j < rp; j += kSealThreads / 64) {
-    if (j >= r) {
-      for (int t = lane; t < L; t += 64) st_el<T>(fac, fb + (int64_t)r * D + (int64_t)t * rp + j, 0.0);
+  void* fac = o.fac;
+  const int64_t fb = j.fb, gb = j.gb;
+  const float* gt = j.gt;
+  // one wave per factor column jc: sign, U column, W column, sigma
+  for (int jc = wave; jc < rp; jc += kSealThreads / 64) {
+    if (jc >= r) {
+      for (int t = lane; t < L; t += 64) st_el<T>(fac, fb + (int64_t)r * D + (int64_t)t * rp + jc, 0.0);
       for (int col = lane; col < D; col += 64) {
-        const int gg = j / 16, wk = min(16, rp - 16 * gg);
-        st_el<T>(fac, fb + (int64_t)r * D + (int64_t)L * rp + (int64_t)gg * 16 * D + (int64_t)col * wk + (j % 16), 0.0);
+        const int gg = jc / 16, wk = min(16, rp - 16 * gg);
+        st_el<T>(fac, fb + (int64_t)r * D + (int64_t)L * rp + (int64_t)gg * 16 * D + (int64_t)col * wk + (jc % 16), 0.0);
       }
       continue;
     }
-    const int src = perm[j];
+    const int src = perm[jc];
     // sign: largest |u_t|, first on ties
     double best = -1.0;
     int bi = 0;
@@ -1692,7 +1712,7 @@ __global__ __launch_bounds__(kSealThreads) void seal_build_kernel(const SealArgs
       if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     }
     const double sgn = V[(size_t)bi * n2 + src] < 0.0 ? -1.0 : 1.0;
-    for (int t = lane; t < L; t += 64) st_el<T>(fac, fb + (int64_t)r * D + (int64_t)t * rp + j, sgn * V[(size_t)t * n2 + src]);
+    for (int t = lane; t < L; t += 64) st_el<T>(fac, fb + (int64_t)r * D + (int64_t)t * rp + jc, sgn * V[(size_t)t * n2 + src]);
     // w = M^T u (2d entries, 4 per lane for d = 128), sigma = |w|
     double wv[2 * D / 64];
     double ss = 0.0;
@@ -1713,30 +1733,116 @@ __global__ __launch_bounds__(kSealThreads) void seal_build_kernel(const SealArgs
       const int col = lane + 64 * m;
       if (col < D) {
         const int ng = D / 8;
-        st_el<T>(fac, fb + (int64_t)j * D + (int64_t)(((col / 8) + j) % ng) * 8 + (col % 8), wv[m] * inv);
+        st_el<T>(fac, fb + (int64_t)jc * D + (int64_t)(((col / 8) + jc) % ng) * 8 + (col % 8), wv[m] * inv);
       } else {
-        const int cv = col - D, gg = j / 16, wk = min(16, rp - 16 * gg);
-        st_el<T>(fac, fb + (int64_t)r * D + (int64_t)L * rp + (int64_t)gg * 16 * D + (int64_t)cv * wk + (j % 16),
+        const int cv = col - D, gg = jc / 16, wk = min(16, rp - 16 * gg);
+        st_el<T>(fac, fb + (int64_t)r * D + (int64_t)L * rp + (int64_t)gg * 16 * D + (int64_t)cv * wk + (jc % 16),
                  wv[m] * inv);
       }
     }
     if (lane == 0) {
-      a.sg[gb + j] = (float)sig;
-      a.sg[gb + rq + j] = gt[j];
+      o.sg[gb + jc] = (float)sig;
+      o.sg[gb + rq + jc] = gt[jc];
     }
   }
-  for (int j = r + tid; j < rq; j += kSealThreads) {
-    a.sg[gb + j] = 0.0f;
-    a.sg[gb + rq + j] = 0.0f;
+  for (int jc = r + tid; jc < rq; jc += kSealThreads) {
+    o.sg[gb + jc] = 0.0f;
+    o.sg[gb + rq + jc] = 0.0f;
   }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kSealThreads) void seal_build_kernel(const SealArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  __shared__ double s_kbar[D], s_vbar[D], s_r[D];
+  __shared__ double s_red[kSealThreads / 64][2];
+  const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const size_t g = (size_t)b * a.Hkv + kv;
+  const SealDesc& ds = a.desc[b];
+  const int ftiles = (a.full_cap + 31) / 32;
+  T* fk = static_cast<T*>(a.full_k) + g * a.full_cap * D;
+  T* fv = static_cast<T*>(a.full_v) + g * ftiles * 32 * D;
+  // the new token at full-resolution row n_full_old
+  for (int j = tid; j < D; j += kSealThreads) {
+    fk[(size_t)ds.n_full_old * D + j] = static_cast<const T*>(a.k_new)[g * D + j];
+    fv[vt_at(ds.n_full_old, j, D)] = static_cast<const T*>(a.v_new)[g * D + j];
+  }
+  if (!ds.sealed) return;
+  const int S = ds.n_seg_old;
+  SpanJob job;
+  job.L = ds.L; job.r = ds.r; job.S = S; job.g = g;
+  job.w = a.weights + ds.w_off;
+  job.P = a.route_proj + (size_t)kv * D * D;
+  job.gt = a.gates + ds.g_off + (size_t)kv * ds.r;
+  job.fb = ds.fac_base + (int64_t)kv * ds.fac_stride;
+  job.gb = ds.sg_base + (int64_t)kv * ds.sg_stride;
+  job.vscr = a.vscratch + g * kMaxSpan * kMaxSpan;
+  SpanDst dst{a.seg_cap, a.vlds_max, a.sum_k, a.sum_v, a.rho, a.key_scale, a.fac, a.sg};
+  build_span<T, D>(RowsFull<T, D>{fk, fv, ds.row0}, job, dst, lds, s_kbar, s_vbar, s_r, s_red);
   // ---- CSR entries of the new span
   if (tid == 0) {
-    a.fac_off[g * a.seg_cap + S] = fb;
-    a.sg_off[g * a.seg_cap + S] = gb;
+    a.fac_off[g * a.seg_cap + S] = job.fb;
+    a.sg_off[g * a.seg_cap + S] = job.gb;
     if (kv == 0) {
       a.seg_off[(size_t)b * (a.seg_cap + 1) + S + 1] = ds.h_new;
-      a.rank[(size_t)b * a.seg_cap + S] = r;
+      a.rank[(size_t)b * a.seg_cap + S] = ds.r;
     }
+  }
+}
+
+// Prefill build (every span of every (b, kv)): a persistent grid, workgroup w
+// taking spans w, w + grid, ... of the list (b, then kv, then span), each
+// with its own eigenvector scratch; the plan's offsets are already on the
+// device.
+template <typename T, int D>
+__global__ __launch_bounds__(kSealThreads) void build_spans_kernel(const BuildArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  __shared__ double s_kbar[D], s_vbar[D], s_r[D];
+  __shared__ double s_red[kSealThreads / 64][2];
+  const SpanDst dst{a.seg_cap, a.vlds_max, a.sum_k, a.sum_v, a.rho, a.key_scale, a.fac, a.sg};
+  for (int it = blockIdx.x; it < a.n_items; it += gridDim.x) {
+    int b = 0;
+    while (b + 1 < a.B && a.item_base[b + 1] <= it) ++b;
+    const int ns = a.n_seg[b];
+    const int rel = it - a.item_base[b];
+    const int kv = rel / ns, S = rel % ns;
+    const size_t g = (size_t)b * a.Hkv + kv;
+    const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
+    const int t0 = so[S] + 1;
+    SpanJob job;
+    job.L = so[S + 1] - t0;
+    job.r = a.rank[(size_t)b * a.seg_cap + S];
+    job.S = S;
+    job.g = g;
+    job.w = a.weights + (size_t)b * a.T + t0;
+    job.P = a.route_proj + (size_t)kv * D * D;
+    job.gt = a.gates + (g * a.seg_cap + S) * (size_t)a.gate_stride;
+    job.fb = a.fac_off[g * a.seg_cap + S];
+    job.gb = a.sg_off[g * a.seg_cap + S];
+    job.vscr = a.vscratch + (size_t)blockIdx.x * kMaxSpan * kMaxSpan;
+    const T* kp = static_cast<const T*>(a.k) + g * a.T * D;
+    const T* vp = static_cast<const T*>(a.v) + g * a.T * D;
+    build_span<T, D>(RowsRaw<T, D>{kp, vp, t0}, job, dst, lds, s_kbar, s_vbar, s_r, s_red);
+  }
+}
+
+// Full-resolution rows of the prefill (sink, anchors, tail) of a (b, kv).
+template <typename T, int D>
+__global__ __launch_bounds__(kSealThreads) void build_full_kernel(const BuildArgs a) {
+  const int kv = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
+  const size_t g = (size_t)b * a.Hkv + kv;
+  const int ns = a.n_seg[b], nf = a.n_full[b], sink = a.n_sink;
+  const int32_t* so = a.seg_off + (size_t)b * (a.seg_cap + 1);
+  const int ftiles = (a.full_cap + 31) / 32;
+  T* fk = static_cast<T*>(a.full_k) + g * a.full_cap * D;
+  T* fv = static_cast<T*>(a.full_v) + g * ftiles * 32 * D;
+  const T* kp = static_cast<const T*>(a.k) + g * a.T * D;
+  const T* vp = static_cast<const T*>(a.v) + g * a.T * D;
+  for (int e = threadIdx.x + blockIdx.y * kSealThreads; e < nf * D; e += kSealThreads * gridDim.y) {
+    const int row = e / D, c = e % D;
+    const int t = row < sink ? row : row < sink + ns ? so[row - sink] : so[ns] + (row - sink - ns);
+    fk[(size_t)row * D + c] = kp[(size_t)t * D + c];
+    fv[vt_at(row, c, D)] = vp[(size_t)t * D + c];
   }
 }
 
@@ -1925,6 +2031,52 @@ hipError_t launch_seal(const SealArgs& a, size_t lds_bytes, hipStream_t s) {
     else seal_compact_kernel<bf16raw, 128><<<grid, kSealThreads, 0, s>>>(a);
   }
   return hipGetLastError();
+}
+
+#define SEKV_DISPATCH_TD(DT, DIM, BODY)                                     \
+  do {                                                                      \
+    if ((DT) == 0) {                                                        \
+      using TT = float;                                                     \
+      if ((DIM) == 64) { constexpr int DD = 64; BODY; }                     \
+      else { constexpr int DD = 128; BODY; }                                \
+    } else {                                                                \
+      using TT = bf16raw;                                                   \
+      if ((DIM) == 64) { constexpr int DD = 64; BODY; }                     \
+      else { constexpr int DD = 128; BODY; }                                \
+    }                                                                       \
+  } while (0)
+
+hipError_t launch_build(const BuildArgs& a, int grid, size_t lds_bytes, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  SEKV_DISPATCH_TD(a.dtype, a.D, ({
+                     build_full_kernel<TT, DD><<<dim3(a.B * a.Hkv, 8), kSealThreads, 0, s>>>(a);
+                     e = hipGetLastError();
+                     if (e == hipSuccess && a.n_items > 0) {
+                       e = hipFuncSetAttribute(reinterpret_cast<const void*>(&build_spans_kernel<TT, DD>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+                       if (e == hipSuccess) build_spans_kernel<TT, DD><<<grid, kSealThreads, lds_bytes, s>>>(a);
+                     }
+                   }));
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t build_resident_blocks(const BuildArgs& a, size_t lds_bytes, int device, int* blocks) {
+  int per_cu = 0;
+  hipError_t e = hipSuccess;
+  SEKV_DISPATCH_TD(a.dtype, a.D, ({
+                     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&build_spans_kernel<TT, DD>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+                     if (e == hipSuccess)
+                       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, build_spans_kernel<TT, DD>,
+                                                                        kSealThreads, lds_bytes);
+                   }));
+  if (e != hipSuccess) return e;
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return e;
+  *blocks = per_cu * cus;
+  return hipSuccess;
 }
 
 hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s) {

@@ -70,6 +70,14 @@ typedef enum sekv_fetch_mode {
                              pinned pools over the bus; no host wait, graph-capturable */
 } sekv_fetch_mode;
 
+/* Where sekv_build_spans computes summaries, routing keys and factors
+ * (sekv_ctx_set_build_mode). */
+typedef enum sekv_build_mode {
+  SEKV_BUILD_DEVICE = 0,  /* (default) GPU kernels; separate bases (basis = 1) fall
+                             back to the host */
+  SEKV_BUILD_HOST = 1     /* host threads (one-sided Jacobi) */
+} sekv_build_mode;
+
 /* Failures a test can force from the host (sekv_ctx_inject_fault). */
 typedef enum sekv_fault { SEKV_FAULT_NONE = 0, SEKV_FAULT_GATHER = 1 } sekv_fault;
 
@@ -213,9 +221,15 @@ sekv_status sekv_plan_spans(const sekv_config* cfg, const float* surprisal, cons
  * Routing key: rho = P^T r/|r|, r = P kbar (0 if |r| = 0); with route_keys = 1
  * instead key_scale = 1/|r| and fold = P^T P (rho may then be NULL).
  * Factors: rank-r_i truncated SVD of [K_body | V_body] (basis 0) or of K_body
- * and V_body separately (basis 1; one-sided Jacobi, fp64), sign fixed so
- * each U column's largest-magnitude entry is positive.  Stored values are fp64
- * rounded to f32 (then to bf16, nearest-even).  Uses host threads.
+ * and V_body separately (basis 1), in fp64, sign fixed so each U column's
+ * largest-magnitude entry is positive.  Stored values are fp64 rounded to f32
+ * (then to bf16, nearest-even).  Build mode DEVICE (the context's default,
+ * basis 0): GPU kernels, one workgroup per span of a persistent grid, the
+ * factors from the Jacobi eigenvectors of the fp64 Gram matrix M M^T (as
+ * sekv_append_token); summaries, routing keys and key scales in the host
+ * builder's fp64 operation order (same bits).  Build mode HOST, or basis 1:
+ * host threads, one-sided Jacobi on M.  The segmentation scan and the fold
+ * matrices are host work in both modes.
  * Errors: SEKV_EINVAL / SEKV_ESHAPE / SEKV_ECAPACITY (pool sizes) / SEKV_EHIP.
  */
 sekv_status sekv_build_spans(sekv_ctx* ctx, const sekv_config* cfg, const void* k, const void* v,
@@ -304,6 +318,10 @@ sekv_status sekv_ctx_set_split(sekv_ctx* ctx, int32_t entries);
  * [de-2], [de-3]: the factor tier lives in CPU memory and is loaded
  * asynchronously on expansion.  Errors: SEKV_EINVAL. */
 sekv_status sekv_ctx_set_fetch_mode(sekv_ctx* ctx, int32_t mode);
+
+/* Build mode of sekv_build_spans (sekv_build_mode), default DEVICE.
+ * Errors: SEKV_EINVAL. */
+sekv_status sekv_ctx_set_build_mode(sekv_ctx* ctx, int32_t mode);
 
 /* Test hook: with SEKV_FAULT_GATHER the next staged host-resident decode of
  * this context fails its host gather after the one host wait: it returns

@@ -569,6 +569,52 @@ def test_library_build_matches_oracle_build(ctx, variant):
         assert worst_recon <= (2e-2 if w.dtype == "bf16" else 1e-5)
 
 
+@pytest.mark.parametrize("wid,over", [(1, {}), (2, dict(n_ctx=4096, batch=2)),
+                                      (1, dict(max_span=120, boundary_quantile=0.995, route_keys="folded"))])
+def test_device_build_matches_host_build(ctx, wid, over):
+    """sekv_build_spans in build mode DEVICE (GPU kernels) against build mode
+    HOST (host threads): full-resolution rows, summaries, routing keys and key
+    scales bit for bit (same fp64 operation order); factors (Gram-matrix
+    Jacobi against one-sided Jacobi) through their reconstructions, which
+    agree within a storage rounding.  The third case has forced spans longer
+    than the eigenvectors kept in LDS."""
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    w = synth.workload(wid, **over)
+    x = synth.make_inputs(w, n_steps=1)
+    cfg = B.make_config(w)
+    plan = B.plan_spans(cfg, x.surprisal, x.boundary_thr, x.rank_req)
+    et = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    kd = torch.from_numpy(x.k).to(et).cuda()
+    vd = torch.from_numpy(x.v).to(et).cuda()
+    caches = []
+    for mode in (B.SEKV_BUILD_DEVICE, B.SEKV_BUILD_HOST):
+        c = B.SpanCache(cfg, plan)
+        ctx.set_build_mode(mode)
+        B.build_spans(ctx, c, kd, vd, x.surprisal, x.route_proj, x.gate)
+        caches.append(c)
+    ctx.set_build_mode(B.SEKV_BUILD_DEVICE)
+    torch.cuda.synchronize()
+    dev, host = caches
+    for name in ("full_k", "full_v", "sum_k", "sum_v", "rho", "key_scale", "fold"):
+        assert torch.equal(getattr(dev, name), getattr(host, name)), name
+    Lmax = int(max((plan.seg_off[b, 1:plan.n_seg[b] + 1] - plan.seg_off[b, :plan.n_seg[b]] - 1).max()
+                   for b in range(w.batch)))
+    tol = 2.0 ** -7 if w.dtype == "bf16" else 1e-5
+    worst = 0.0
+    for b in range(w.batch):
+        n = int(plan.n_seg[b])
+        for kv in range(w.n_kv_heads):
+            for i in range(0, n, max(1, n // 60)):
+                U1, s1, g1, V1 = B.read_factors(dev, b, kv, i)
+                U2, s2, g2, V2 = B.read_factors(host, b, kv, i)
+                assert np.array_equal(g1, g2)
+                R1, R2 = (U1 * s1) @ V1, (U2 * s2) @ V2
+                worst = max(worst, float(np.abs(R1 - R2).max() / max(np.abs(R2).max(), 1e-30)))
+    log(f"device vs host build ({w.name}, L up to {Lmax}): factors' reconstructions differ by {worst:.2e} relative")
+    assert worst <= tol
+
+
 def test_abi_errors_need_context(ctx):
     """Argument checks of the GPU entry points: documented status, nothing written."""
     import torch
