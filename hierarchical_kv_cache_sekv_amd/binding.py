@@ -27,8 +27,13 @@ EXPORTS = [
     "sekv_profile_enable", "sekv_profile_read", "sekv_ctx_set_split", "sekv_ctx_set_fetch_mode",
     "sekv_ctx_inject_fault", "sekv_profile_read_host", "sekv_route_noalloc", "sekv_dense_workspace_bytes",
     "sekv_dense_attention_decode", "sekv_decode_step", "sekv_profile_read_overlap", "sekv_append_workspace_bytes",
-    "sekv_append_token", "sekv_ctx_set_build_mode",
+    "sekv_append_token", "sekv_ctx_set_build_mode", "sekv_factor_cache_create", "sekv_factor_cache_destroy",
+    "sekv_factor_cache_invalidate", "sekv_factor_cache_stats", "sekv_factor_cache_lookup",
+    "sekv_cached_decode_workspace_bytes", "sekv_cached_decode_host_workspace_bytes", "sekv_cached_attention_decode",
+    "sekv_profile_read_fill",
 ]
+CACHE_HIT, CACHE_FILL, CACHE_BYPASS = 0, 1, 2
+CACHE_PAGE_BYTES = 2 << 20
 SEKV_FETCH_STAGED, SEKV_FETCH_DIRECT = 0, 1
 SEKV_FAULT_NONE, SEKV_FAULT_GATHER = 0, 1
 SEKV_BUILD_DEVICE, SEKV_BUILD_HOST = 0, 1
@@ -47,6 +52,15 @@ class Config(ctypes.Structure):
 
 
 _p = ctypes.c_void_p
+
+
+class CacheStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "lookups", "hits", "fills", "bypasses", "evictions", "bytes_hit", "bytes_filled", "bytes_bypassed",
+        "resident_blocks", "resident_bytes", "pages_used", "pages_total")]
+
+    def as_dict(self) -> dict:
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
 
 
 class Spans(ctypes.Structure):
@@ -95,6 +109,15 @@ def _load():
         "sekv_profile_enable": (i32, [_p, i32]),
         "sekv_profile_read": (i32, [_p] + [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)] * 3),
         "sekv_profile_read_overlap": (i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+        "sekv_profile_read_fill": (i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+        "sekv_factor_cache_create": (i32, [_p, sz, ctypes.POINTER(_p)]),
+        "sekv_factor_cache_destroy": (None, [_p]),
+        "sekv_factor_cache_invalidate": (i32, [_p, i32]),
+        "sekv_factor_cache_stats": (i32, [_p, ctypes.POINTER(CacheStats), i32]),
+        "sekv_factor_cache_lookup": (i32, [_p, i32, C, S, _p, _p, _p, _p]),
+        "sekv_cached_decode_workspace_bytes": (sz, [_p, C, S]),
+        "sekv_cached_decode_host_workspace_bytes": (sz, [_p, C, S]),
+        "sekv_cached_attention_decode": (i32, [_p, _p, i32, C, S, _p, _p, _p, _p, _p, _p, sz, _p, sz, _p, _p]),
         "sekv_decode_step": (i32, [_p, C, S, _p, _p, _p, _p, _p, _p, _p, sz, _p, sz, _p]),
         "sekv_append_workspace_bytes": (sz, [C, S]),
         "sekv_append_token": (i32, [_p, C, S, _p, _p, _p, i32, _p, _p, _p, i32, _p, ctypes.POINTER(i64),
@@ -202,6 +225,8 @@ class Context:
         m1, n1 = ctypes.c_double(), ctypes.c_int64()
         _check(LIB.sekv_profile_read_overlap(self.handle, ctypes.byref(m1), ctypes.byref(n1)))
         res["overlap"] = (m1.value, n1.value)
+        _check(LIB.sekv_profile_read_fill(self.handle, ctypes.byref(m1), ctypes.byref(n1)))
+        res["fill"] = (m1.value, n1.value)
         return res
 
     def set_split(self, entries: int):
@@ -457,6 +482,71 @@ def decode_step(ctx: Context, cache: SpanCache, q, theta, route_out: RouteOut, o
                                 _ptr(route_out.exp_list), _ptr(route_out.exp_mask), _ptr(route_out.exp_count),
                                 _ptr(out), _ptr(route_ws), route_ws.numel(), _ptr(ws.dev), ws.dev.numel(),
                                 _stream_handle(stream)))
+
+
+class FactorCache:
+    """sekv_factor_cache: an HBM arena of ``nbytes`` (whole 2 MiB pages) for
+    host-resident factor blocks, shared by the layers of a model.  ctx None:
+    bookkeeping only (``lookup`` works, the cached decode does not)."""
+
+    def __init__(self, ctx: Optional[Context], nbytes: int):
+        h = _p()
+        _check(LIB.sekv_factor_cache_create(ctx.handle if ctx is not None else None, int(nbytes), ctypes.byref(h)))
+        self.handle = h
+
+    def stats(self, reset: bool = False) -> dict:
+        st = CacheStats()
+        _check(LIB.sekv_factor_cache_stats(self.handle, ctypes.byref(st), int(reset)))
+        return st.as_dict()
+
+    def invalidate(self, layer: int = -1):
+        _check(LIB.sekv_factor_cache_invalidate(self.handle, int(layer)))
+
+    def lookup(self, layer: int, cfg: Config, spans: Spans, exp_list: np.ndarray, exp_count: np.ndarray):
+        """Host bookkeeping of one call: (status, offset), shaped like exp_list."""
+        exp_list = np.ascontiguousarray(exp_list, dtype=np.int32)
+        exp_count = np.ascontiguousarray(exp_count, dtype=np.int32)
+        status = np.full(exp_list.shape, -1, np.int32)
+        offset = np.full(exp_list.shape, -1, np.int64)
+        _check(LIB.sekv_factor_cache_lookup(self.handle, int(layer), ctypes.byref(cfg), ctypes.byref(spans),
+                                            _ptr(exp_list), _ptr(exp_count), _ptr(status), _ptr(offset)))
+        return status, offset
+
+    def close(self):
+        if self.handle:
+            LIB.sekv_factor_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class CachedDecodeWorkspace:
+    """Device and pinned host workspaces of sekv_cached_attention_decode."""
+
+    def __init__(self, cache: SpanCache, device="cuda", ctx: Optional[Context] = None):
+        torch = _torch()
+        st = cache.struct()
+        h = ctx.handle if ctx is not None else None
+        nd = LIB.sekv_cached_decode_workspace_bytes(h, ctypes.byref(cache.cfg), ctypes.byref(st))
+        nh = LIB.sekv_cached_decode_host_workspace_bytes(h, ctypes.byref(cache.cfg), ctypes.byref(st))
+        self.dev = torch.empty(max(nd, 256), dtype=torch.uint8, device=device)
+        self.host = torch.empty(max(nh, 256), dtype=torch.uint8, pin_memory=True)
+
+
+def cached_decode(ctx: Context, fcache: FactorCache, layer: int, cache: SpanCache, q, route_out: RouteOut, out,
+                  ws: CachedDecodeWorkspace, stream=None, copy_stream=None, spans: Optional[Spans] = None):
+    """sekv_cached_attention_decode: one layer's decode through the factor cache."""
+    st = spans if spans is not None else cache.struct()
+    cs = copy_stream.cuda_stream if copy_stream is not None else None
+    _check(LIB.sekv_cached_attention_decode(ctx.handle, fcache.handle, int(layer), ctypes.byref(cache.cfg),
+                                            ctypes.byref(st), _ptr(q), _ptr(route_out.exp_list),
+                                            _ptr(route_out.exp_mask), _ptr(route_out.exp_count), _ptr(out),
+                                            _ptr(ws.dev), ws.dev.numel(), _ptr(ws.host), ws.host.numel(),
+                                            _stream_handle(stream), cs))
 
 
 def tile_values_device(v):

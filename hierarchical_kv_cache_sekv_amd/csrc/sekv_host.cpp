@@ -24,6 +24,7 @@
 #include <vector>
 
 #include "../../include/sekv.h"
+#include "sekv_factor_cache.h"
 #include "sekv_internal.h"
 
 using namespace sekv;
@@ -141,7 +142,7 @@ struct sekv_ctx {
   hipEvent_t ev_ring[kRing] = {};
   ThreadPool* pool = nullptr;
   bool profile = false;
-  EventPairs prof_route, prof_attend, prof_expand, prof_overlap;
+  EventPairs prof_route, prof_attend, prof_expand, prof_overlap, prof_fill;
   hipStream_t aux = nullptr;                          // second stream of sekv_decode_step (default priority)
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;    // its fork / join points
   int32_t split_entries = 0;      // full-resolution entries per split-K chunk (0: automatic)
@@ -476,6 +477,7 @@ void sekv_ctx_destroy(sekv_ctx* c) {
   for (hipEvent_t e : c->prof_attend.ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof_expand.ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prof_overlap.ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->prof_fill.ev) (void)hipEventDestroy(e);
   if (c->aux) (void)hipStreamDestroy(c->aux);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
@@ -1010,11 +1012,16 @@ namespace {
 
 struct DecodePlan {
   AttendArgs a{};
-  size_t off_ml = 0, off_o = 0, off_stage_off = 0, off_stage_fac = 0, off_stage_sg = 0, dev_bytes = 0;
-  size_t h_list = 0, h_count = 0, h_stage_off = 0, h_sg = 0, h_ring = 0, host_bytes = 0;
+  size_t off_ml = 0, off_o = 0, off_stage_off = 0, off_stage_fac = 0, off_stage_sg = 0, off_fill = 0, dev_bytes = 0;
+  size_t h_list = 0, h_count = 0, h_stage_off = 0, h_sg = 0, h_ring = 0, h_fill = 0, host_bytes = 0;
 };
 
-void make_plan(const sekv_config* c, const sekv_spans* s, int32_t split_entries, bool staged, DecodePlan& p) {
+// How the expanded-span pass reaches the factors: device pools or the direct
+// host fetch (no staging), the staged host fetch, or the device factor cache.
+enum PlanFetch { kPlanDirect = 0, kPlanStaged = 1, kPlanCached = 2 };
+
+void make_plan(const sekv_config* c, const sekv_spans* s, int32_t split_entries, int fetch, DecodePlan& p) {
+  const bool staged = fetch == kPlanStaged, cached = fetch == kPlanCached;
   const int B = c->batch, Hkv = c->n_kv_heads, D = c->head_dim, G = c->n_q_heads / Hkv;
   const int BG = B * Hkv;
   AttendArgs& a = p.a;
@@ -1060,6 +1067,10 @@ void make_plan(const sekv_config* c, const sekv_spans* s, int32_t split_entries,
     p.off_stage_fac = off; off = align_up(off + (size_t)s->fac_elems * elem_size(c->dtype));
     p.off_stage_sg = off; off = align_up(off + (size_t)s->sg_elems * sizeof(float));
   }
+  if (cached) {
+    p.off_stage_off = off; off = align_up(off + (size_t)BG * (2 * (size_t)s->seg_cap + 1) * sizeof(int64_t));
+    p.off_fill = off; off = align_up(off + (size_t)BG * s->seg_cap * sizeof(FillItem));
+  }
   p.dev_bytes = off;
   size_t h = 0;
   if (staged) {
@@ -1068,6 +1079,12 @@ void make_plan(const sekv_config* c, const sekv_spans* s, int32_t split_entries,
     p.h_stage_off = h; h = align_up(h + (size_t)BG * (2 * (size_t)s->seg_cap + 1) * sizeof(int64_t));
     p.h_sg = h; h = align_up(h + (size_t)s->sg_elems * sizeof(float));
     p.h_ring = h; h = align_up(h + (size_t)kRing * kRingBytes);
+  }
+  if (cached) {
+    p.h_count = h; h = align_up(h + (size_t)BG * sizeof(int32_t));
+    p.h_list = h; h = align_up(h + (size_t)BG * s->seg_cap * sizeof(int32_t));
+    p.h_stage_off = h; h = align_up(h + (size_t)BG * (2 * (size_t)s->seg_cap + 1) * sizeof(int64_t));
+    p.h_fill = h; h = align_up(h + (size_t)BG * s->seg_cap * sizeof(FillItem));
   }
   p.host_bytes = h;
 }
@@ -1081,14 +1098,14 @@ bool staged_fetch(const sekv_ctx* ctx, const sekv_config* c) {
 size_t sekv_decode_workspace_bytes(const sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s) {
   if (check_config(c) != SEKV_OK || !s) return 0;
   DecodePlan p;
-  make_plan(c, s, ctx ? ctx->split_entries : 0, staged_fetch(ctx, c), p);
+  make_plan(c, s, ctx ? ctx->split_entries : 0, staged_fetch(ctx, c) ? kPlanStaged : kPlanDirect, p);
   return p.dev_bytes;
 }
 
 size_t sekv_decode_host_workspace_bytes(const sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s) {
   if (check_config(c) != SEKV_OK || !s) return 0;
   DecodePlan p;
-  make_plan(c, s, ctx ? ctx->split_entries : 0, staged_fetch(ctx, c), p);
+  make_plan(c, s, ctx ? ctx->split_entries : 0, staged_fetch(ctx, c) ? kPlanStaged : kPlanDirect, p);
   return p.host_bytes;
 }
 
@@ -1097,7 +1114,7 @@ namespace {
 // one call (all chunks of the full-resolution + summary pass).
 sekv_status decode_setup(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s, const void* q,
                          const int32_t* exp_list, const uint8_t* exp_mask, const int32_t* exp_count, float* out,
-                         void* dev_ws, size_t dev_ws_bytes, bool staged, const char* who, DecodePlan& p,
+                         void* dev_ws, size_t dev_ws_bytes, int fetch, const char* who, DecodePlan& p,
                          AttendArgs& a) {
   if (!ctx) return fail(SEKV_EINVAL, "ctx is NULL");
   sekv_status st = check_config(c);
@@ -1106,7 +1123,7 @@ sekv_status decode_setup(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* 
   if (st != SEKV_OK) return st;
   if (!q || !exp_list || !exp_mask || !exp_count || !out || !dev_ws)
     return fail(SEKV_EINVAL, "%s: a pointer argument is NULL", who);
-  make_plan(c, s, ctx->split_entries, staged, p);
+  make_plan(c, s, ctx->split_entries, fetch, p);
   if (dev_ws_bytes < p.dev_bytes) return fail(SEKV_ECAPACITY, "device workspace %zu bytes < %zu needed", dev_ws_bytes, p.dev_bytes);
   if (p.a.tiles_a4 * 32 > 2048) return fail(SEKV_ESHAPE, "internal chunk size too large");
   a = p.a;
@@ -1118,7 +1135,7 @@ sekv_status decode_setup(sekv_ctx* ctx, const sekv_config* c, const sekv_spans* 
   a.part_o = reinterpret_cast<float*>(dws + p.off_o);
   a.out = out;
   a.stage_off = nullptr;
-  if (c->factors_on_host && !staged) {
+  if (c->factors_on_host && fetch == kPlanDirect) {
     // direct fetch: the kernels read the listed spans' factor blocks from the
     // pinned host pools over the bus, through the pools' device addresses
     a.fac = device_address(s->fac);
@@ -1157,7 +1174,8 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   const bool staged = ctx && c && staged_fetch(ctx, c);
   DecodePlan p;
   AttendArgs a;
-  sekv_status st = decode_setup(ctx, c, s, q, exp_list, exp_mask, exp_count, out, dev_ws, dev_ws_bytes, staged,
+  sekv_status st = decode_setup(ctx, c, s, q, exp_list, exp_mask, exp_count, out, dev_ws, dev_ws_bytes,
+                                staged ? kPlanStaged : kPlanDirect,
                                 "sekv_mixed_attention_decode", p, a);
   if (st != SEKV_OK) return st;
   if (staged) {
@@ -1271,6 +1289,281 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
   const auto t_end = std::chrono::steady_clock::now();
   ctx->host_wait_ms += std::chrono::duration<double, std::milli>(t_listed - t_wait).count();
   ctx->host_gather_ms += gather_ms;
+  ctx->host_call_ms += std::chrono::duration<double, std::milli>(t_end - t_call).count();
+  ctx->host_calls += 1;
+  return SEKV_OK;
+}
+
+// ---------------------------------------------------------------- device factor cache
+struct sekv_factor_cache {
+  explicit sekv_factor_cache(int64_t bytes) : book(bytes) {}
+  FactorCacheBook book;
+  int device = -1;
+  char* arena = nullptr;          // device memory of book.arena_bytes() (null: bookkeeping only)
+  hipEvent_t ev_read = nullptr;   // end of the last expanded-span pass that read the arena
+  bool read_recorded = false;
+};
+
+extern "C++" {
+namespace {
+// Host arrays a cache lookup reads, checked.
+sekv_status check_cache_spans(const sekv_config* c, const sekv_spans* s) {
+  sekv_status st = check_config(c);
+  if (st != SEKV_OK) return st;
+  if (!s) return fail(SEKV_EINVAL, "spans is NULL");
+  if (s->seg_cap != seg_cap_of(c)) return fail(SEKV_ESHAPE, "spans seg_cap %d differs from the configuration's %d", s->seg_cap, seg_cap_of(c));
+  if (!s->n_seg_host || !s->seg_off_host || !s->rank_host || !s->fac_off_host || !s->sg_off_host)
+    return fail(SEKV_EINVAL, "the factor cache needs n_seg_host, seg_off_host, rank_host, fac_off_host and sg_off_host");
+  for (int b = 0; b < c->batch; ++b)
+    if (s->n_seg_host[b] < 0 || s->n_seg_host[b] > s->seg_cap)
+      return fail(SEKV_ESHAPE, "n_seg[%d] = %d outside [0, seg_cap=%d]", b, s->n_seg_host[b], s->seg_cap);
+  return SEKV_OK;
+}
+
+// One cache batch over a route list (host copies h_count [B*Hkv], h_list
+// [B*Hkv][seg_cap]): every listed entry is checked first (range, pool bounds),
+// so a bad list leaves the cache untouched; then each entry is looked up in
+// list order and handed to on_entry(g, j, pool index o, factor bytes, sigma|gate
+// bytes, status, arena offset).
+template <class F>
+sekv_status cache_batch(sekv_factor_cache* fc, int32_t layer, const sekv_config* c, const sekv_spans* s,
+                        const int32_t* h_count, const int32_t* h_list, F&& on_entry) {
+  const int Hkv = c->n_kv_heads, D = c->head_dim, BG = c->batch * Hkv;
+  const int es = elem_size(c->dtype);
+  const bool sep = c->basis != 0;
+  const int32_t cap = s->seg_cap;
+  for (int g = 0; g < BG; ++g) {
+    const int b = g / Hkv, cnt = h_count[g];
+    if (cnt < 0 || cnt > s->n_seg_host[b])
+      return fail(SEKV_EHIP, "route count %d for group %d is out of range; out was not written", cnt, g);
+    const int32_t* so = s->seg_off_host + (size_t)b * (cap + 1);
+    for (int j = 0; j < cnt; ++j) {
+      const int S = h_list[(size_t)g * cap + j];
+      if (S < 0 || S >= s->n_seg_host[b])
+        return fail(SEKV_EHIP, "route list entry %d out of range; out was not written", S);
+      const int L = so[S + 1] - so[S] - 1, r = s->rank_host[(size_t)b * cap + S];
+      if (L < 1 || L > kMaxSpan || r < 1 || r > L) return fail(SEKV_ESHAPE, "span %d of sequence %d has L = %d, r = %d", S, b, L, r);
+      const size_t o = (size_t)g * cap + S;
+      const int64_t fe = fac_block_elems(L, r, (r + 7) & ~7, D, sep), ge = sg_entry_elems(r, sep);
+      if (s->fac_off_host[o] < 0 || s->fac_off_host[o] + fe > s->fac_elems || s->sg_off_host[o] < 0 ||
+          s->sg_off_host[o] + ge > s->sg_elems)
+        return fail(SEKV_ESHAPE, "factor block of span %d (group %d) lies outside the pools", S, g);
+    }
+  }
+  fc->book.begin();
+  for (int g = 0; g < BG; ++g) {
+    const int b = g / Hkv, cnt = h_count[g];
+    const int32_t* so = s->seg_off_host + (size_t)b * (cap + 1);
+    for (int j = 0; j < cnt; ++j) {
+      const int S = h_list[(size_t)g * cap + j];
+      const int L = so[S + 1] - so[S] - 1, r = s->rank_host[(size_t)b * cap + S];
+      const size_t o = (size_t)g * cap + S;
+      const int64_t fb = fac_block_elems(L, r, (r + 7) & ~7, D, sep) * es, gb = sg_entry_elems(r, sep) * 4;
+      // tag: the block's host address, so a different pool under the same key refills
+      const int64_t tag = (int64_t)((uintptr_t)s->fac + (uintptr_t)(s->fac_off_host[o] * es));
+      int64_t off = -1;
+      const int32_t st = fc->book.lookup(FactorCacheBook::key(layer, g, S), fb + gb, tag, &off);
+      on_entry(g, j, o, fb, gb, st, off);
+    }
+  }
+  return SEKV_OK;
+}
+}  // namespace
+}  // extern "C++"
+
+sekv_status sekv_factor_cache_create(sekv_ctx* ctx, size_t bytes, sekv_factor_cache** out) {
+  if (!out) return fail(SEKV_EINVAL, "out is NULL");
+  *out = nullptr;
+  if ((int64_t)bytes < FactorCacheBook::kPageBytes)
+    return fail(SEKV_ESHAPE, "a factor cache of %zu bytes is smaller than one %lld-byte page", bytes,
+                (long long)FactorCacheBook::kPageBytes);
+  sekv_factor_cache* fc = new (std::nothrow) sekv_factor_cache((int64_t)bytes);
+  if (!fc) return fail(SEKV_ENOMEM, "cannot allocate the factor cache");
+  if (ctx) {
+    fc->device = ctx->device;
+    hipError_t e = hipSetDevice(ctx->device);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&fc->arena), (size_t)fc->book.arena_bytes());
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&fc->ev_read, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      sekv_factor_cache_destroy(fc);
+      return fail(SEKV_EHIP, "factor cache arena of %lld bytes: %s", (long long)fc->book.arena_bytes(), hipGetErrorString(e));
+    }
+  }
+  *out = fc;
+  return SEKV_OK;
+}
+
+void sekv_factor_cache_destroy(sekv_factor_cache* fc) {
+  if (!fc) return;
+  if (fc->ev_read) {
+    (void)hipEventSynchronize(fc->ev_read);
+    (void)hipEventDestroy(fc->ev_read);
+  }
+  if (fc->arena) (void)hipFree(fc->arena);
+  delete fc;
+}
+
+sekv_status sekv_factor_cache_invalidate(sekv_factor_cache* fc, int32_t layer) {
+  if (!fc) return fail(SEKV_EINVAL, "cache is NULL");
+  if (layer < -1 || layer > 65535) return fail(SEKV_EINVAL, "layer %d outside [-1, 65535]", layer);
+  if (layer < 0) fc->book.clear();
+  else fc->book.invalidate(layer);
+  return SEKV_OK;
+}
+
+sekv_status sekv_factor_cache_stats(sekv_factor_cache* fc, sekv_cache_stats* out, int32_t reset) {
+  if (!fc || !out) return fail(SEKV_EINVAL, "cache or out is NULL");
+  const FactorCacheBook::Stats& st = fc->book.stats();
+  out->lookups = st.lookups;
+  out->hits = st.hits;
+  out->fills = st.fills;
+  out->bypasses = st.bypasses;
+  out->evictions = st.evictions;
+  out->bytes_hit = st.bytes_hit;
+  out->bytes_filled = st.bytes_filled;
+  out->bytes_bypassed = st.bytes_bypassed;
+  out->resident_blocks = fc->book.resident_blocks();
+  out->resident_bytes = fc->book.resident_bytes();
+  out->pages_used = fc->book.pages_used();
+  out->pages_total = fc->book.pages();
+  if (reset) fc->book.reset_stats();
+  return SEKV_OK;
+}
+
+sekv_status sekv_factor_cache_lookup(sekv_factor_cache* fc, int32_t layer, const sekv_config* c, const sekv_spans* s,
+                                     const int32_t* exp_list, const int32_t* exp_count, int32_t* status,
+                                     int64_t* offset) {
+  if (!fc) return fail(SEKV_EINVAL, "cache is NULL");
+  if (layer < 0 || layer > 65535) return fail(SEKV_EINVAL, "layer %d outside [0, 65535]", layer);
+  sekv_status st = check_cache_spans(c, s);
+  if (st != SEKV_OK) return st;
+  if (!exp_list || !exp_count || !status || !offset) return fail(SEKV_EINVAL, "a pointer argument is NULL");
+  const int32_t cap = s->seg_cap;
+  return cache_batch(fc, layer, c, s, exp_count, exp_list,
+                     [&](int g, int j, size_t, int64_t, int64_t, int32_t stt, int64_t off) {
+                       status[(size_t)g * cap + j] = stt;
+                       offset[(size_t)g * cap + j] = off;
+                     });
+}
+
+size_t sekv_cached_decode_workspace_bytes(const sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s) {
+  if (check_config(c) != SEKV_OK || !s) return 0;
+  DecodePlan p;
+  make_plan(c, s, ctx ? ctx->split_entries : 0, kPlanCached, p);
+  return p.dev_bytes;
+}
+
+size_t sekv_cached_decode_host_workspace_bytes(const sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s) {
+  if (check_config(c) != SEKV_OK || !s) return 0;
+  DecodePlan p;
+  make_plan(c, s, ctx ? ctx->split_entries : 0, kPlanCached, p);
+  return p.host_bytes;
+}
+
+sekv_status sekv_cached_attention_decode(sekv_ctx* ctx, sekv_factor_cache* fc, int32_t layer, const sekv_config* c,
+                                         const sekv_spans* s, const void* q, const int32_t* exp_list,
+                                         const uint8_t* exp_mask, const int32_t* exp_count, float* out,
+                                         void* dev_ws, size_t dev_ws_bytes, void* host_ws, size_t host_ws_bytes,
+                                         hipStream_t stream, hipStream_t copy_stream) {
+  if (!fc) return fail(SEKV_EINVAL, "cache is NULL");
+  if (!fc->arena) return fail(SEKV_EINVAL, "the cache has no device arena (it was created without a context)");
+  if (ctx && fc->device != ctx->device) return fail(SEKV_EINVAL, "the cache lives on device %d, the context on %d", fc->device, ctx->device);
+  if (layer < 0 || layer > 65535) return fail(SEKV_EINVAL, "layer %d outside [0, 65535]", layer);
+  if (c && c->factors_on_host != 1) return fail(SEKV_EINVAL, "the factor cache serves host-resident factors (factors_on_host = 1)");
+  DecodePlan p;
+  AttendArgs a;
+  sekv_status st = decode_setup(ctx, c, s, q, exp_list, exp_mask, exp_count, out, dev_ws, dev_ws_bytes, kPlanCached,
+                                "sekv_cached_attention_decode", p, a);
+  if (st != SEKV_OK) return st;
+  if (!host_ws) return fail(SEKV_EINVAL, "the cached decode needs a pinned host workspace");
+  if (host_ws_bytes < p.host_bytes) return fail(SEKV_ECAPACITY, "host workspace %zu bytes < %zu needed", host_ws_bytes, p.host_bytes);
+  if (!is_pinned_host(host_ws)) return fail(SEKV_EINVAL, "host workspace must be pinned (hipHostMalloc)");
+  const char* fac_dev = static_cast<const char*>(device_address(s->fac));
+  const char* sg_dev = static_cast<const char*>(device_address(s->sg));
+  if (!fac_dev || !sg_dev) return fail(SEKV_EHIP, "pinned factor pools have no device address");
+  if (!copy_stream) copy_stream = stream;
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+
+  const int BG = c->batch * c->n_kv_heads;
+  const int es = elem_size(c->dtype);
+  const int32_t cap = s->seg_cap;
+  char* dws = static_cast<char*>(dev_ws);
+  char* hws = static_cast<char*>(host_ws);
+  int32_t* h_count = reinterpret_cast<int32_t*>(hws + p.h_count);
+  int32_t* h_list = reinterpret_cast<int32_t*>(hws + p.h_list);
+  int64_t* h_soff = reinterpret_cast<int64_t*>(hws + p.h_stage_off);
+  FillItem* h_fill = reinterpret_cast<FillItem*>(hws + p.h_fill);
+  const auto t_call = std::chrono::steady_clock::now();
+  // the previous host-resident call's uploads from pinned staging must be done
+  HIP_OR_FAIL(hipEventSynchronize(ctx->ev_copy));
+  HIP_OR_FAIL(hipMemcpyAsync(h_count, exp_count, BG * sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  HIP_OR_FAIL(hipMemcpyAsync(h_list, exp_list, (size_t)BG * cap * sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  HIP_OR_FAIL(hipEventRecord(ctx->ev_list, stream));
+  // the full-resolution + summary pass runs while the host does the bookkeeping and the fills run
+  hipEvent_t t0, t1;
+  HIP_OR_FAIL(prof_pair(ctx, ctx->prof_attend, &t0, &t1));
+  HIP_OR_FAIL(launch_attend_full(a, stream, t0, t1));
+  const auto t_wait = std::chrono::steady_clock::now();
+  HIP_OR_FAIL(hipEventSynchronize(ctx->ev_list));
+  const auto t_listed = std::chrono::steady_clock::now();
+
+  // stage table: per group the first list entry, then (factor, sigma|gate)
+  // offsets per entry, in elements from the arena base (also for bypassed
+  // blocks, which are read from the pinned pools through their device address)
+  int64_t ne = 0;
+  for (int g = 0; g < BG; ++g) {
+    h_soff[g] = ne;
+    ne += std::max(0, h_count[g]);
+  }
+  int n_fill = 0;
+  bool bad_slot = false;
+  const intptr_t arena = (intptr_t)fc->arena;
+  st = cache_batch(fc, layer, c, s, h_count, h_list,
+                   [&](int g, int j, size_t o, int64_t fb, int64_t gb, int32_t stt, int64_t off) {
+                     int64_t* e = h_soff + BG + 2 * (h_soff[g] + j);
+                     const intptr_t fsrc = (intptr_t)(fac_dev + s->fac_off_host[o] * es);
+                     const intptr_t gsrc = (intptr_t)(sg_dev + s->sg_off_host[o] * 4);
+                     if (stt == FactorCacheBook::kBypass) {
+                       e[0] = (int64_t)(fsrc - arena) / es;
+                       e[1] = (int64_t)(gsrc - arena) / 4;
+                       return;
+                     }
+                     if (off < 0 || off + fb + gb > fc->book.arena_bytes()) {
+                       bad_slot = true;
+                       return;
+                     }
+                     e[0] = off / es;
+                     e[1] = (off + fb) / 4;
+                     if (stt == FactorCacheBook::kFill)
+                       h_fill[n_fill++] = FillItem{(uint64_t)fsrc, (uint64_t)gsrc, (uint64_t)off, (uint32_t)fb, (uint32_t)gb};
+                   });
+  if (st != SEKV_OK) return st;
+  if (bad_slot) return fail(SEKV_EHIP, "factor cache slot outside the arena (internal error); out was not written");
+  const auto t_booked = std::chrono::steady_clock::now();
+  FillItem* d_fill = reinterpret_cast<FillItem*>(dws + p.off_fill);
+  int64_t* d_soff = reinterpret_cast<int64_t*>(dws + p.off_stage_off);
+  // slots being refilled may still be read by the previous cached call's expanded pass
+  if (fc->read_recorded) HIP_OR_FAIL(hipStreamWaitEvent(copy_stream, fc->ev_read, 0));
+  HIP_OR_FAIL(hipMemcpyAsync(d_soff, h_soff, (size_t)(BG + 2 * ne) * sizeof(int64_t), hipMemcpyHostToDevice, copy_stream));
+  if (n_fill > 0) {
+    HIP_OR_FAIL(hipMemcpyAsync(d_fill, h_fill, (size_t)n_fill * sizeof(FillItem), hipMemcpyHostToDevice, copy_stream));
+    HIP_OR_FAIL(prof_pair(ctx, ctx->prof_fill, &t0, &t1));
+    HIP_OR_FAIL(launch_cache_fill(d_fill, n_fill, fc->arena, copy_stream, t0, t1));
+  }
+  HIP_OR_FAIL(hipEventRecord(ctx->ev_copy, copy_stream));
+  if (copy_stream != stream) HIP_OR_FAIL(hipStreamWaitEvent(stream, ctx->ev_copy, 0));
+  AttendArgs a5 = a;
+  a5.stage_off = d_soff;
+  a5.stage_fac = fc->arena;
+  a5.stage_sg = reinterpret_cast<const float*>(fc->arena);
+  HIP_OR_FAIL(prof_pair(ctx, ctx->prof_expand, &t0, &t1));
+  HIP_OR_FAIL(launch_attend_expanded(a5, stream, t0, t1));
+  HIP_OR_FAIL(hipEventRecord(fc->ev_read, stream));
+  fc->read_recorded = true;
+  HIP_OR_FAIL(launch_combine(a, stream));
+  const auto t_end = std::chrono::steady_clock::now();
+  ctx->host_wait_ms += std::chrono::duration<double, std::milli>(t_listed - t_wait).count();
+  ctx->host_gather_ms += std::chrono::duration<double, std::milli>(t_booked - t_listed).count();
   ctx->host_call_ms += std::chrono::duration<double, std::milli>(t_end - t_call).count();
   ctx->host_calls += 1;
   return SEKV_OK;
@@ -1457,7 +1750,7 @@ sekv_status sekv_decode_step(sekv_ctx* ctx, const sekv_config* c, const sekv_spa
                              "sekv_mixed_attention_decode");
   DecodePlan p;
   AttendArgs a;
-  st = decode_setup(ctx, c, s, q, exp_list, exp_mask, exp_count, out, dev_ws, dev_ws_bytes, false,
+  st = decode_setup(ctx, c, s, q, exp_list, exp_mask, exp_count, out, dev_ws, dev_ws_bytes, kPlanDirect,
                     "sekv_decode_step", p, a);
   if (st != SEKV_OK) return st;
   HIP_OR_FAIL(hipSetDevice(ctx->device));
@@ -1610,6 +1903,13 @@ sekv_status sekv_profile_read_overlap(sekv_ctx* ctx, double* ms, int64_t* launch
   if (!ctx || !ms || !launches) return fail(SEKV_EINVAL, "sekv_profile_read_overlap: NULL argument");
   HIP_OR_FAIL(hipSetDevice(ctx->device));
   HIP_OR_FAIL(prof_sum(ctx->prof_overlap, ms, launches));
+  return SEKV_OK;
+}
+
+sekv_status sekv_profile_read_fill(sekv_ctx* ctx, double* ms, int64_t* launches) {
+  if (!ctx || !ms || !launches) return fail(SEKV_EINVAL, "sekv_profile_read_fill: NULL argument");
+  HIP_OR_FAIL(hipSetDevice(ctx->device));
+  HIP_OR_FAIL(prof_sum(ctx->prof_fill, ms, launches));
   return SEKV_OK;
 }
 

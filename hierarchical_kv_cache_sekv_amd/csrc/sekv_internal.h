@@ -128,6 +128,17 @@ struct BuildArgs {
   double* vscratch;            // [grid][kMaxSpan][kMaxSpan]
 };
 
+// One factor block copied into the device factor cache: the span's factor
+// block (fac_bytes) and its sigma|gate entry (sg_bytes) go to the cache slot
+// at arena byte offset dst, the entry right after the block.  Sources are
+// device-visible addresses (pinned host pools); every size and address is a
+// multiple of 16 bytes.
+struct FillItem {
+  uint64_t src_fac, src_sg;
+  uint64_t dst;
+  uint32_t fac_bytes, sg_bytes;
+};
+
 // ev0/ev1: optional start/stop events of the kernel itself (both or neither)
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 // Route workgroups the device holds at once (occupancy x compute units).
@@ -149,5 +160,9 @@ hipError_t launch_seal(const SealArgs& a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_build(const BuildArgs& a, int grid, size_t lds_bytes, hipStream_t s);
 // Workgroups of the span build kernel resident at once with lds_bytes of dynamic LDS.
 hipError_t build_resident_blocks(const BuildArgs& a, size_t lds_bytes, int device, int* blocks);
+// Copy n cache fills (items in device memory) into the arena; the arena must
+// hold every dst + fac_bytes + sg_bytes (checked by the caller).
+hipError_t launch_cache_fill(const FillItem* items, int n, char* arena, hipStream_t s, hipEvent_t ev0 = nullptr,
+                             hipEvent_t ev1 = nullptr);
 
 }  // namespace sekv

@@ -2079,6 +2079,45 @@ hipError_t build_resident_blocks(const BuildArgs& a, size_t lds_bytes, int devic
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------- device factor cache fill
+// Each workgroup copies whole items (grid-strided over the list): 16 bytes per
+// lane, four loads in flight per lane before their stores, so that many reads
+// of the pinned host pools are outstanding on the bus at once.
+constexpr int kFillThreads = 256;
+constexpr int kFillGrid = 2048;
+__global__ __launch_bounds__(kFillThreads) void cache_fill_kernel(const FillItem* items, int n, char* arena) {
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const FillItem it = items[i];
+    const int nf = (int)(it.fac_bytes >> 4), tot = nf + (int)(it.sg_bytes >> 4);
+    const uint4* sf = reinterpret_cast<const uint4*>(it.src_fac);
+    const uint4* sg = reinterpret_cast<const uint4*>(it.src_sg);
+    uint4* dst = reinterpret_cast<uint4*>(arena + it.dst);
+    for (int k0 = 0; k0 < tot; k0 += 4 * kFillThreads) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + u * kFillThreads + (int)threadIdx.x;
+        if (k < tot) v[u] = k < nf ? sf[k] : sg[k - nf];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + u * kFillThreads + (int)threadIdx.x;
+        if (k < tot) dst[k] = v[u];
+      }
+    }
+  }
+}
+
+hipError_t launch_cache_fill(const FillItem* items, int n, char* arena, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  if (n <= 0) return hipSuccess;
+  const int grid = std::min(n, kFillGrid);
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(cache_fill_kernel, dim3(grid), dim3(kFillThreads), 0, s, ev0, ev1, 0, items, n, arena);
+  else
+    cache_fill_kernel<<<grid, kFillThreads, 0, s>>>(items, n, arena);
+  return hipGetLastError();
+}
+
 hipError_t launch_reconstruct(const ReconArgs& a, hipStream_t s) {
   recon_scan_kernel<<<a.B * a.Hkv, 64, 0, s>>>(a);
   hipError_t e = hipGetLastError();

@@ -442,6 +442,105 @@ sekv_status sekv_append_token(sekv_ctx* ctx, const sekv_config* cfg, const sekv_
                               int32_t* sealed_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Device factor cache for host-resident factors.  [de-2], [abstract]: the
+ * factor tier lives in CPU memory and a span's factors are loaded when it is
+ * expanded; the pages name the CPU-GPU bandwidth this costs as the method's
+ * limitation ("Bedeutung und Ansprüche").  The cache keeps the factor blocks
+ * (factor block + sigma|gate entry) of recently expanded spans in an HBM arena
+ * across decode steps and layers, so a span expanded again is read from HBM.
+ *
+ * Policy: the arena is cut into 2 MiB pages; a block takes a slot of the
+ * smallest size class that holds it (classes grow by about 1.25x from 1 KiB in
+ * 256-byte steps); a class takes a free page when it has no free slot, and
+ * once every page is assigned it evicts its least recently used block.  Blocks
+ * used by the current call are never evicted by that call: a block that finds
+ * every slot of its class in use by the call is read over the bus directly
+ * (a bypass).  Blocks are keyed by (layer, b * Hkv + kv, span index); a key
+ * whose host address or size changed is refilled.  After rebuilding a layer's
+ * spans in place, invalidate that layer.
+ *
+ * sekv_factor_cache_create: an arena of floor(bytes / 2 MiB) pages on ctx's
+ *   device (hipMalloc), owned by the cache.  ctx may be NULL: then the cache
+ *   has no arena and serves only sekv_factor_cache_lookup (the bookkeeping, on
+ *   the host).  Errors: SEKV_EINVAL, SEKV_ESHAPE (bytes < 2 MiB), SEKV_EHIP,
+ *   SEKV_ENOMEM.
+ * sekv_factor_cache_destroy: waits for the last cached decode that read the
+ *   arena, then frees it.
+ * sekv_factor_cache_invalidate: drops every block of `layer` (0..65535);
+ *   layer = -1 drops everything and returns every page to the free pool.
+ * sekv_factor_cache_stats: counters since the last reset (lookups = hits +
+ *   fills + bypasses; bytes are block bytes) and the current residency;
+ *   reset != 0 zeroes the counters afterwards.
+ */
+typedef struct sekv_factor_cache sekv_factor_cache;
+typedef struct sekv_cache_stats {
+  int64_t lookups, hits, fills, bypasses, evictions;
+  int64_t bytes_hit, bytes_filled, bytes_bypassed;
+  int64_t resident_blocks, resident_bytes;
+  int64_t pages_used, pages_total;
+} sekv_cache_stats;
+
+sekv_status sekv_factor_cache_create(sekv_ctx* ctx, size_t bytes, sekv_factor_cache** out);
+void sekv_factor_cache_destroy(sekv_factor_cache* cache);
+sekv_status sekv_factor_cache_invalidate(sekv_factor_cache* cache, int32_t layer);
+sekv_status sekv_factor_cache_stats(sekv_factor_cache* cache, sekv_cache_stats* out, int32_t reset);
+
+/*
+ * sekv_factor_cache_lookup - the cache bookkeeping of one decode call, on the
+ * host only (no GPU work; what sekv_cached_attention_decode does after its
+ * host wait).  Every listed entry is checked first (counts, span indices,
+ * pool bounds); a bad list changes nothing.  Then the entries are looked up
+ * in list order (group-major).
+ *   exp_list [B][Hkv][seg_cap], exp_count [B][Hkv]: host, read.
+ *   spans: only seg_cap, n_seg_host, seg_off_host, rank_host, fac_off_host,
+ *     sg_off_host, fac (the tag address), fac_elems and sg_elems are read.
+ *   status [B][Hkv][seg_cap] int32: host, written for entries j < count:
+ *     0 hit, 1 fill (a slot was assigned; the cached decode copies the block
+ *     there), 2 bypass.
+ *   offset [B][Hkv][seg_cap] int64: host, written: the slot's byte offset in
+ *     the arena (the sigma|gate entry follows the factor block), -1 for a
+ *     bypass.
+ * Errors: SEKV_EINVAL / SEKV_ESHAPE / SEKV_EHIP (list out of range).
+ */
+sekv_status sekv_factor_cache_lookup(sekv_factor_cache* cache, int32_t layer, const sekv_config* cfg,
+                                     const sekv_spans* spans, const int32_t* exp_list, const int32_t* exp_count,
+                                     int32_t* status, int64_t* offset);
+
+/* Workspaces of sekv_cached_attention_decode: device bytes and pinned host
+ * bytes (0 for an invalid configuration); ctx may be NULL (automatic split). */
+size_t sekv_cached_decode_workspace_bytes(const sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans);
+size_t sekv_cached_decode_host_workspace_bytes(const sekv_ctx* ctx, const sekv_config* cfg, const sekv_spans* spans);
+
+/*
+ * sekv_cached_attention_decode - sekv_mixed_attention_decode for host-resident
+ * factors (cfg->factors_on_host = 1) through a device factor cache; the
+ * result is bit-identical to the direct and staged fetches.  One call serves
+ * one layer; layers of a model share one cache, each under its own `layer`
+ * index (0..65535).
+ *   Sequence: the list is copied to the host and the full-resolution +
+ *   summary pass starts on `stream`; after the one host wait the cache
+ *   bookkeeping assigns slots; the stage table and the fill list are copied
+ *   and the fill kernel pulls the missing blocks from the pinned pools into
+ *   their slots on copy_stream, while the full-resolution pass runs; the
+ *   expanded-span pass then reads hits and fills from HBM (bypassed blocks
+ *   from the pinned pools), followed by the merge on `stream`.
+ *   A layer's route needs that layer's query, which in a model comes from the
+ *   layer below: the fill of a layer overlaps that layer's own
+ *   full-resolution pass, not a later layer's.
+ *   Arguments as sekv_mixed_attention_decode; dev_ws and host_ws (pinned,
+ *   required) sized by the two functions above; copy_stream may be NULL.
+ *   The cache must live on ctx's device.  Calls that share a context or a
+ *   cache must be ordered on one stream.
+ * Errors: as sekv_mixed_attention_decode; a bad route list found after the
+ * host wait returns SEKV_EHIP (out not written, the cache unchanged).
+ */
+sekv_status sekv_cached_attention_decode(sekv_ctx* ctx, sekv_factor_cache* cache, int32_t layer,
+                                         const sekv_config* cfg, const sekv_spans* spans, const void* q,
+                                         const int32_t* exp_list, const uint8_t* exp_mask, const int32_t* exp_count,
+                                         float* out, void* dev_ws, size_t dev_ws_bytes, void* host_ws,
+                                         size_t host_ws_bytes, hipStream_t stream, hipStream_t copy_stream);
+
+/*
  * sekv_dense_attention_decode - the dense baseline: plain softmax attention of
  * each query head over all T cached tokens (logit q.k/sqrt(d)), with the same
  * split-K matrix-core pass and log-sum-exp merge as the full-resolution part
@@ -481,10 +580,14 @@ sekv_status sekv_profile_read(sekv_ctx* ctx, double* route_ms, int64_t* route_la
  * the summary + expanded-span launch). */
 sekv_status sekv_profile_read_overlap(sekv_ctx* ctx, double* ms, int64_t* launches);
 
-/* Host-side phases of staged host-resident decode calls since the last read
- * (always recorded): the host wait for the route list, the threaded gather of
- * factor blocks into pinned staging, and the whole call, in milliseconds
- * summed over `calls` calls; then reset.  Errors: SEKV_EINVAL. */
+/* The same for the cache fill kernels of sekv_cached_attention_decode ("fill"). */
+sekv_status sekv_profile_read_fill(sekv_ctx* ctx, double* ms, int64_t* launches);
+
+/* Host-side phases of staged and cached host-resident decode calls since the
+ * last read (always recorded): the host wait for the route list, the threaded
+ * gather of factor blocks into pinned staging (staged) or the cache
+ * bookkeeping (cached), and the whole call, in milliseconds summed over
+ * `calls` calls; then reset.  Errors: SEKV_EINVAL. */
 sekv_status sekv_profile_read_host(sekv_ctx* ctx, double* wait_ms, double* gather_ms, double* call_ms,
                                    int64_t* calls);
 

@@ -1,6 +1,8 @@
 // Host-only exercise of libsekv's runtime for the address and undefined-behaviour
 // sanitizers: capacities, span planning over random configurations (all
-// reading variants), argument errors, workspace sizing.  No GPU call is made.
+// reading variants), argument errors, workspace sizing, and the device factor
+// cache's bookkeeping (a cache without a device arena) over random route
+// lists.  No GPU call is made.
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -77,6 +79,42 @@ int main() {
     EXPECT(sekv_route_workspace_bytes(&c, &sp) > 0);
     EXPECT(sekv_decode_workspace_bytes(nullptr, &c, &sp) > 0);
     EXPECT(sekv_dense_workspace_bytes(nullptr, &c) > 0);
+    EXPECT(sekv_cached_decode_workspace_bytes(nullptr, &c, &sp) > 0);
+    // factor cache bookkeeping over random lists (a tiny cache: evictions and bypasses)
+    sp.seg_off_host = seg_off.data();
+    sp.fac_off_host = fac_off.data();
+    sp.sg_off_host = sg_off.data();
+    sp.fac = reinterpret_cast<const void*>(uintptr_t(1) << 40);
+    sp.fac_elems = fe;
+    sp.sg_elems = ge;
+    sekv_factor_cache* fc = nullptr;
+    EXPECT(sekv_factor_cache_create(nullptr, (size_t(2) << 20) * (1 + rng() % 2), &fc) == SEKV_OK);
+    std::vector<int32_t> lst((size_t)B * Hkv * seg_cap), cnt((size_t)B * Hkv), stt(lst.size());
+    std::vector<int64_t> off(lst.size());
+    for (int call = 0; call < 6 && fc; ++call) {
+      for (int g = 0; g < B * Hkv; ++g) {
+        const int ns = n_seg[g / Hkv];
+        int n = 0;
+        for (int i = 0; i < ns; ++i)
+          if (rng() % 3 == 0) lst[(size_t)g * seg_cap + n++] = i;
+        cnt[g] = n;
+      }
+      EXPECT(sekv_factor_cache_lookup(fc, call % 3, &c, &sp, lst.data(), cnt.data(), stt.data(), off.data()) ==
+             SEKV_OK);
+      for (int g = 0; g < B * Hkv; ++g)
+        for (int j = 0; j < cnt[g]; ++j) {
+          const size_t k = (size_t)g * seg_cap + j;
+          EXPECT(stt[k] >= 0 && stt[k] <= 2 && (stt[k] == 2) == (off[k] < 0));
+        }
+    }
+    sekv_cache_stats cs{};
+    if (fc) {
+      EXPECT(sekv_factor_cache_stats(fc, &cs, 1) == SEKV_OK);
+      EXPECT(cs.lookups == cs.hits + cs.fills + cs.bypasses);
+      EXPECT(sekv_factor_cache_invalidate(fc, 1) == SEKV_OK);
+      EXPECT(sekv_factor_cache_invalidate(fc, -1) == SEKV_OK);
+      sekv_factor_cache_destroy(fc);
+    }
     ++planned;
   }
   // argument errors
