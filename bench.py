@@ -694,6 +694,137 @@ def measure_host_resident(args):
     return rec
 
 
+# ------------------------------------------------------------------ multi-layer host-resident decode
+def measure_layers(args):
+    """Multi-layer decode with host-resident factors: --layers layers of the
+    128K batch-1 host-factor workload, each with its own seeded K/V, spans,
+    pinned host factor pools and queries (step-to-step correlation
+    --query-corr), decoded layer after layer every step (route, then
+    attention).  The listed spans' factor blocks reach the GPU through one
+    device factor cache of --cache-mb shared by all layers; the same steps are
+    also timed with the direct fetch (every listed block over the bus).  Eager
+    steps (one host wait per layer in the cached mode).  The step's first layer
+    output is compared bit for bit between the two fetches."""
+    import numpy as np
+    import torch
+    from hierarchical_kv_cache_sekv_amd import binding as B
+    from hierarchical_kv_cache_sekv_amd import synth
+
+    N, W, K = args.layers, args.warmup, args.steps
+    Q = max(args.queries, W + K)
+    e = 2
+    ctx = B.Context(0)
+    layers = []
+    t0 = time.time()
+    for li in range(N):
+        w = synth.workload(3, factors_on_host=True, layer=li, query_corr=args.query_corr)
+        x = synth.make_inputs(w, n_steps=Q)
+        cfg = B.make_config(w)
+        plan = B.plan_spans(cfg, x.surprisal, x.boundary_thr, x.rank_req)
+        cache = B.SpanCache(cfg, plan)
+        kd = torch.from_numpy(x.k).to(cache.elem).cuda()
+        vd = torch.from_numpy(x.v).to(cache.elem).cuda()
+        B.build_spans(ctx, cache, kd, vd, x.surprisal, x.route_proj, x.gate)
+        del kd, vd
+        torch.cuda.synchronize()
+        theta = torch.from_numpy(calibrate(B, w, plan, cache, x, [w.expand_frac] * w.batch, Q)).cuda()
+        qd = torch.from_numpy(x.q[:Q]).to(cache.elem).cuda().contiguous()
+        layers.append(dict(w=w, plan=plan, cache=cache, theta=theta, qd=qd, ro=B.RouteOut(cfg, cache.seg_cap),
+                           rws=B.route_workspace(cache), dws=B.DecodeWorkspace(cache, ctx=ctx),
+                           cws=B.CachedDecodeWorkspace(cache, ctx=ctx),
+                           out=torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")))
+        del x
+        log(f"layer {li}: {w.name} built ({time.time() - t0:.1f}s so far)")
+    w0 = layers[0]["w"]
+    fc = B.FactorCache(ctx, args.cache_mb << 20)
+    cs = torch.cuda.Stream()
+
+    def step(i, cached):
+        for li, L in enumerate(layers):
+            qs = L["qd"][i]
+            B.route(ctx, L["cache"], qs, L["theta"], L["ro"], L["rws"])
+            if cached:
+                B.cached_decode(ctx, fc, li, L["cache"], qs, L["ro"], L["out"], L["cws"], copy_stream=cs)
+            else:
+                B.decode(ctx, L["cache"], qs, L["ro"], L["out"], L["dws"])
+
+    # bitwise check of one step, then warm the cache
+    step(0, False)
+    torch.cuda.synchronize()
+    ref = layers[0]["out"].clone()
+    step(0, True)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ref, layers[0]["out"]))
+    fc.invalidate(-1)
+    res = {}
+    for mode in ("direct", "cached"):
+        cached = mode == "cached"
+        # pass 1 timed (no timing events); pass 2 the same steps from the same
+        # (empty) cache with per-kernel events
+        for timed in (True, False):
+            fc.invalidate(-1)
+            for i in range(W):
+                step(i, cached)
+            torch.cuda.synchronize()
+            fc.stats(reset=True)
+            ctx.host_timing()
+            ctx.profile(not timed)
+            t1 = time.perf_counter()
+            for i in range(W, W + K):
+                step(i, cached)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t1) * 1e3 / K
+            if timed:
+                res[mode] = dict(ms=ms, stats=fc.stats(), host=ctx.host_timing())
+                log(f"{mode}: {ms:.3f} ms per step ({N} layers)")
+            else:
+                prof = ctx.profile_read()
+                ctx.profile(False)
+                res[mode].update(kern={k: v[0] * 1e3 / max(v[1], 1) for k, v in prof.items()},
+                                 launches={k: v[1] for k, v in prof.items()})
+    # listed factor bytes per step (what the direct fetch moves over the bus)
+    listed = 0.0
+    for L in layers:
+        for i in range(W, W + K):
+            B.route(ctx, L["cache"], L["qd"][i], L["theta"], L["ro"], L["rws"])
+            torch.cuda.synchronize()
+            cnt = L["ro"].exp_count.cpu().numpy()
+            listed += algorithmic_bytes(L["w"], L["plan"], cnt, L["ro"].exp_list.cpu().numpy(), e)["factors"]
+    listed /= K
+    st = res["cached"]["stats"]
+    bus = (st["bytes_filled"] + st["bytes_bypassed"]) / K
+    kc = res["cached"]["kern"]
+    rec = {
+        "metric": "multi-layer host-resident decode steps/s (all layers, PCIe included)",
+        "value": 1e3 / res["cached"]["ms"], "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": res["cached"]["ms"], "higher_is_better": True, "launch": "eager",
+        "fetch": "device factor cache (HBM, LRU across steps and layers; misses pulled by a fill kernel beside "
+                 "the full-resolution pass)",
+        "dtype": w0.dtype, "data": "synthetic (seeded per layer; Llama-3-8B layer shape)",
+        "config": {"workload": f"{N} x {w0.name}", "layers": N, "batch": w0.batch, "n_ctx": w0.n_ctx,
+                   "rank_range": [w0.rank_lo, w0.rank_hi], "expand_frac_target": w0.expand_frac,
+                   "query_corr": args.query_corr, "cache_bytes": st["pages_total"] * B.CACHE_PAGE_BYTES},
+        "bitwise_equal_to_direct_fetch": same,
+        "direct_fetch": {"ms_per_step": res["direct"]["ms"], "steps_per_s": 1e3 / res["direct"]["ms"],
+                         "bus_bytes_per_step": int(listed),
+                         "bus_gbs_over_step": listed / (res["direct"]["ms"] * 1e-3) / 1e9},
+        "speedup_vs_direct": res["direct"]["ms"] / res["cached"]["ms"],
+        "cache": {"lookups_per_step": st["lookups"] / K, "hit_rate": st["hits"] / max(1, st["lookups"]),
+                  "byte_hit_rate": st["bytes_hit"] / max(1, st["bytes_hit"] + st["bytes_filled"] + st["bytes_bypassed"]),
+                  "bus_bytes_per_step": int(bus), "evictions_per_step": st["evictions"] / K,
+                  "bypasses_per_step": st["bypasses"] / K, "resident_bytes": st["resident_bytes"],
+                  "pages_used": st["pages_used"], "pages_total": st["pages_total"]},
+        "kernels_us_per_launch": {k: round(v, 2) for k, v in kc.items() if res["cached"]["launches"][k]},
+        "launches_per_layer": {k: v / (K * N) for k, v in res["cached"]["launches"].items() if v},
+        "host_us_per_layer": res["cached"]["host"],
+        "fill_kernel_gbs": (st["bytes_filled"] / res["cached"]["launches"]["fill"]) / (kc["fill"] * 1e-6) / 1e9
+        if res["cached"]["launches"]["fill"] else None,
+    }
+    fc.close()
+    ctx.close()
+    return rec
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -716,6 +847,11 @@ def main():
                          "headline workload, the 32K batch-1 and batch-8 workloads, and the host-resident workload")
     ap.add_argument("--append", type=int, default=0, metavar="N",
                     help="only measure online span sealing: N sekv_append_token calls on the workload's caches")
+    ap.add_argument("--layers", type=int, default=0, metavar="N",
+                    help="multi-layer host-resident decode of N layers through the device factor cache")
+    ap.add_argument("--cache-mb", type=int, default=1024, help="device factor cache size (MiB) for --layers")
+    ap.add_argument("--query-corr", type=float, default=0.9,
+                    help="step-to-step query correlation of the --layers workload")
     ap.add_argument("--host-resident", action="store_true",
                     help="only measure the host-resident workload (pinned host factors fetched per step)")
     ap.add_argument("--fetch", choices=("staged", "direct"), default="direct",
@@ -753,6 +889,9 @@ def main():
         sys.exit(2)
     if args.host_resident:
         print(json.dumps(measure_host_resident(args)), flush=True)
+        return
+    if args.layers:
+        print(json.dumps(measure_layers(args)), flush=True)
         return
     if args.append:
         print(json.dumps(measure_append(args)), flush=True)
@@ -811,6 +950,8 @@ def main():
             print(json.dumps(measure_host_resident(args)), flush=True)
             args.append = args.append or 512
             print(json.dumps(measure_append(args)), flush=True)
+            args.layers = args.layers or 4
+            print(json.dumps(measure_layers(args)), flush=True)
     finally:
         if pool is not None:
             pool.close()

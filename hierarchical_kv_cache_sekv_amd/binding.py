@@ -110,7 +110,7 @@ def _load():
         "sekv_profile_read": (i32, [_p] + [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)] * 3),
         "sekv_profile_read_overlap": (i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
         "sekv_profile_read_fill": (i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
-        "sekv_factor_cache_create": (i32, [_p, sz, ctypes.POINTER(_p)]),
+        "sekv_factor_cache_create": (i32, [_p, sz, i32, ctypes.POINTER(_p)]),
         "sekv_factor_cache_destroy": (None, [_p]),
         "sekv_factor_cache_invalidate": (i32, [_p, i32]),
         "sekv_factor_cache_stats": (i32, [_p, ctypes.POINTER(CacheStats), i32]),
@@ -485,13 +485,15 @@ def decode_step(ctx: Context, cache: SpanCache, q, theta, route_out: RouteOut, o
 
 
 class FactorCache:
-    """sekv_factor_cache: an HBM arena of ``nbytes`` (whole 2 MiB pages) for
-    host-resident factor blocks, shared by the layers of a model.  ctx None:
-    bookkeeping only (``lookup`` works, the cached decode does not)."""
+    """sekv_factor_cache: an HBM arena of ``nbytes`` (whole 2 MiB pages, split
+    evenly among ``partitions``; 0: the library's default) for host-resident
+    factor blocks, shared by the layers of a model.  ctx None: bookkeeping
+    only (``lookup`` works, the cached decode does not)."""
 
-    def __init__(self, ctx: Optional[Context], nbytes: int):
+    def __init__(self, ctx: Optional[Context], nbytes: int, partitions: int = 0):
         h = _p()
-        _check(LIB.sekv_factor_cache_create(ctx.handle if ctx is not None else None, int(nbytes), ctypes.byref(h)))
+        _check(LIB.sekv_factor_cache_create(ctx.handle if ctx is not None else None, int(nbytes), int(partitions),
+                                            ctypes.byref(h)))
         self.handle = h
 
     def stats(self, reset: bool = False) -> dict:

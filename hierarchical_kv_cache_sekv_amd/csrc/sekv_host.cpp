@@ -129,6 +129,8 @@ int default_threads() {
 }  // namespace
 
 constexpr int kRing = 3;
+constexpr int kCacheParts = 8;    // default partitions of a device factor cache
+constexpr int kCacheChunks = 4;   // fill launches (chunks of partitions) of one cached decode
 constexpr size_t kRingBytes = 8u << 20;
 
 struct EventPairs {
@@ -1012,7 +1014,7 @@ namespace {
 
 struct DecodePlan {
   AttendArgs a{};
-  size_t off_ml = 0, off_o = 0, off_stage_off = 0, off_stage_fac = 0, off_stage_sg = 0, off_fill = 0, dev_bytes = 0;
+  size_t off_ml = 0, off_o = 0, off_stage_off = 0, off_stage_fac = 0, off_stage_sg = 0, dev_bytes = 0;
   size_t h_list = 0, h_count = 0, h_stage_off = 0, h_sg = 0, h_ring = 0, h_fill = 0, host_bytes = 0;
 };
 
@@ -1069,7 +1071,6 @@ void make_plan(const sekv_config* c, const sekv_spans* s, int32_t split_entries,
   }
   if (cached) {
     p.off_stage_off = off; off = align_up(off + (size_t)BG * (2 * (size_t)s->seg_cap + 1) * sizeof(int64_t));
-    p.off_fill = off; off = align_up(off + (size_t)BG * s->seg_cap * sizeof(FillItem));
   }
   p.dev_bytes = off;
   size_t h = 0;
@@ -1295,13 +1296,26 @@ sekv_status sekv_mixed_attention_decode(sekv_ctx* ctx, const sekv_config* c, con
 }
 
 // ---------------------------------------------------------------- device factor cache
+extern "C++" {
+namespace {
+// One listed entry of a cache batch, prepared by cache_prepare.
+struct CacheItem {
+  uint64_t key;
+  int64_t bytes, tag;    // block bytes (factor block + sigma|gate entry), host address of the block
+  int64_t fac, sg;       // pool element offsets of the factor block and the sigma|gate entry
+  int32_t fb, g;         // factor block bytes, group
+};
+}  // namespace
+}  // extern "C++"
+
 struct sekv_factor_cache {
-  explicit sekv_factor_cache(int64_t bytes) : book(bytes) {}
+  sekv_factor_cache(int64_t bytes, int parts) : book(bytes, parts) {}
   FactorCacheBook book;
   int device = -1;
   char* arena = nullptr;          // device memory of book.arena_bytes() (null: bookkeeping only)
   hipEvent_t ev_read = nullptr;   // end of the last expanded-span pass that read the arena
   bool read_recorded = false;
+  std::vector<CacheItem> items;   // the current call's listed entries
 };
 
 extern "C++" {
@@ -1320,64 +1334,56 @@ sekv_status check_cache_spans(const sekv_config* c, const sekv_spans* s) {
   return SEKV_OK;
 }
 
-// One cache batch over a route list (host copies h_count [B*Hkv], h_list
-// [B*Hkv][seg_cap]): every listed entry is checked first (range, pool bounds),
-// so a bad list leaves the cache untouched; then each entry is looked up in
-// list order and handed to on_entry(g, j, pool index o, factor bytes, sigma|gate
-// bytes, status, arena offset).
-template <class F>
-sekv_status cache_batch(sekv_factor_cache* fc, int32_t layer, const sekv_config* c, const sekv_spans* s,
-                        const int32_t* h_count, const int32_t* h_list, F&& on_entry) {
+// Checks a route list (host copies h_count [B*Hkv], h_list [B*Hkv][seg_cap]):
+// counts, span indices, span shapes and pool bounds of every listed entry,
+// so that a bad list leaves the cache untouched; and prepares the entries in
+// list order (group-major) for cache_lookup_items.
+sekv_status cache_prepare(int32_t layer, const sekv_config* c, const sekv_spans* s, const int32_t* h_count,
+                          const int32_t* h_list, std::vector<CacheItem>& items) {
   const int Hkv = c->n_kv_heads, D = c->head_dim, BG = c->batch * Hkv;
   const int es = elem_size(c->dtype);
   const bool sep = c->basis != 0;
   const int32_t cap = s->seg_cap;
+  items.clear();
   for (int g = 0; g < BG; ++g) {
     const int b = g / Hkv, cnt = h_count[g];
     if (cnt < 0 || cnt > s->n_seg_host[b])
       return fail(SEKV_EHIP, "route count %d for group %d is out of range; out was not written", cnt, g);
     const int32_t* so = s->seg_off_host + (size_t)b * (cap + 1);
+    const int32_t* rk = s->rank_host + (size_t)b * cap;
+    const int64_t* fo = s->fac_off_host + (size_t)g * cap;
+    const int64_t* go = s->sg_off_host + (size_t)g * cap;
+    const int32_t* lst = h_list + (size_t)g * cap;
     for (int j = 0; j < cnt; ++j) {
-      const int S = h_list[(size_t)g * cap + j];
+      const int S = lst[j];
       if (S < 0 || S >= s->n_seg_host[b])
         return fail(SEKV_EHIP, "route list entry %d out of range; out was not written", S);
-      const int L = so[S + 1] - so[S] - 1, r = s->rank_host[(size_t)b * cap + S];
+      const int L = so[S + 1] - so[S] - 1, r = rk[S];
       if (L < 1 || L > kMaxSpan || r < 1 || r > L) return fail(SEKV_ESHAPE, "span %d of sequence %d has L = %d, r = %d", S, b, L, r);
-      const size_t o = (size_t)g * cap + S;
       const int64_t fe = fac_block_elems(L, r, (r + 7) & ~7, D, sep), ge = sg_entry_elems(r, sep);
-      if (s->fac_off_host[o] < 0 || s->fac_off_host[o] + fe > s->fac_elems || s->sg_off_host[o] < 0 ||
-          s->sg_off_host[o] + ge > s->sg_elems)
+      if (fo[S] < 0 || fo[S] + fe > s->fac_elems || go[S] < 0 || go[S] + ge > s->sg_elems)
         return fail(SEKV_ESHAPE, "factor block of span %d (group %d) lies outside the pools", S, g);
-    }
-  }
-  fc->book.begin();
-  for (int g = 0; g < BG; ++g) {
-    const int b = g / Hkv, cnt = h_count[g];
-    const int32_t* so = s->seg_off_host + (size_t)b * (cap + 1);
-    for (int j = 0; j < cnt; ++j) {
-      const int S = h_list[(size_t)g * cap + j];
-      const int L = so[S + 1] - so[S] - 1, r = s->rank_host[(size_t)b * cap + S];
-      const size_t o = (size_t)g * cap + S;
-      const int64_t fb = fac_block_elems(L, r, (r + 7) & ~7, D, sep) * es, gb = sg_entry_elems(r, sep) * 4;
       // tag: the block's host address, so a different pool under the same key refills
-      const int64_t tag = (int64_t)((uintptr_t)s->fac + (uintptr_t)(s->fac_off_host[o] * es));
-      int64_t off = -1;
-      const int32_t st = fc->book.lookup(FactorCacheBook::key(layer, g, S), fb + gb, tag, &off);
-      on_entry(g, j, o, fb, gb, st, off);
+      items.push_back(CacheItem{FactorCacheBook::key(layer, g, S), fe * es + ge * 4,
+                                (int64_t)((uintptr_t)s->fac + (uintptr_t)(fo[S] * es)), fo[S], go[S],
+                                (int32_t)(fe * es), g});
     }
   }
   return SEKV_OK;
 }
+
 }  // namespace
 }  // extern "C++"
 
-sekv_status sekv_factor_cache_create(sekv_ctx* ctx, size_t bytes, sekv_factor_cache** out) {
+sekv_status sekv_factor_cache_create(sekv_ctx* ctx, size_t bytes, int32_t partitions, sekv_factor_cache** out) {
   if (!out) return fail(SEKV_EINVAL, "out is NULL");
   *out = nullptr;
-  if ((int64_t)bytes < FactorCacheBook::kPageBytes)
-    return fail(SEKV_ESHAPE, "a factor cache of %zu bytes is smaller than one %lld-byte page", bytes,
-                (long long)FactorCacheBook::kPageBytes);
-  sekv_factor_cache* fc = new (std::nothrow) sekv_factor_cache((int64_t)bytes);
+  if (partitions == 0) partitions = kCacheParts;
+  if (partitions < 1 || partitions > 256) return fail(SEKV_EINVAL, "partitions %d outside [1, 256]", partitions);
+  if ((int64_t)bytes < FactorCacheBook::kPageBytes * partitions)
+    return fail(SEKV_ESHAPE, "a factor cache of %zu bytes has less than one %lld-byte page per partition (%d)",
+                bytes, (long long)FactorCacheBook::kPageBytes, partitions);
+  sekv_factor_cache* fc = new (std::nothrow) sekv_factor_cache((int64_t)bytes, partitions);
   if (!fc) return fail(SEKV_ENOMEM, "cannot allocate the factor cache");
   if (ctx) {
     fc->device = ctx->device;
@@ -1439,11 +1445,21 @@ sekv_status sekv_factor_cache_lookup(sekv_factor_cache* fc, int32_t layer, const
   if (st != SEKV_OK) return st;
   if (!exp_list || !exp_count || !status || !offset) return fail(SEKV_EINVAL, "a pointer argument is NULL");
   const int32_t cap = s->seg_cap;
-  return cache_batch(fc, layer, c, s, exp_count, exp_list,
-                     [&](int g, int j, size_t, int64_t, int64_t, int32_t stt, int64_t off) {
-                       status[(size_t)g * cap + j] = stt;
-                       offset[(size_t)g * cap + j] = off;
-                     });
+  st = cache_prepare(layer, c, s, exp_count, exp_list, fc->items);
+  if (st != SEKV_OK) return st;
+  fc->book.begin();
+  int g = 0, j = 0;
+  for (const CacheItem& it : fc->items) {
+    if (it.g != g) {
+      g = it.g;
+      j = 0;
+    }
+    int64_t off = -1;
+    status[(size_t)g * cap + j] = fc->book.part(fc->book.part_of_group(g)).lookup(it.key, it.bytes, it.tag, &off);
+    offset[(size_t)g * cap + j] = off;
+    ++j;
+  }
+  return SEKV_OK;
 }
 
 size_t sekv_cached_decode_workspace_bytes(const sekv_ctx* ctx, const sekv_config* c, const sekv_spans* s) {
@@ -1510,48 +1526,76 @@ sekv_status sekv_cached_attention_decode(sekv_ctx* ctx, sekv_factor_cache* fc, i
   // stage table: per group the first list entry, then (factor, sigma|gate)
   // offsets per entry, in elements from the arena base (also for bypassed
   // blocks, which are read from the pinned pools through their device address)
-  int64_t ne = 0;
-  for (int g = 0; g < BG; ++g) {
-    h_soff[g] = ne;
-    ne += std::max(0, h_count[g]);
-  }
-  int n_fill = 0;
-  bool bad_slot = false;
-  const intptr_t arena = (intptr_t)fc->arena;
-  st = cache_batch(fc, layer, c, s, h_count, h_list,
-                   [&](int g, int j, size_t o, int64_t fb, int64_t gb, int32_t stt, int64_t off) {
-                     int64_t* e = h_soff + BG + 2 * (h_soff[g] + j);
-                     const intptr_t fsrc = (intptr_t)(fac_dev + s->fac_off_host[o] * es);
-                     const intptr_t gsrc = (intptr_t)(sg_dev + s->sg_off_host[o] * 4);
-                     if (stt == FactorCacheBook::kBypass) {
-                       e[0] = (int64_t)(fsrc - arena) / es;
-                       e[1] = (int64_t)(gsrc - arena) / 4;
-                       return;
-                     }
-                     if (off < 0 || off + fb + gb > fc->book.arena_bytes()) {
-                       bad_slot = true;
-                       return;
-                     }
-                     e[0] = off / es;
-                     e[1] = (off + fb) / 4;
-                     if (stt == FactorCacheBook::kFill)
-                       h_fill[n_fill++] = FillItem{(uint64_t)fsrc, (uint64_t)gsrc, (uint64_t)off, (uint32_t)fb, (uint32_t)gb};
-                   });
+  st = cache_prepare(layer, c, s, h_count, h_list, fc->items);
   if (st != SEKV_OK) return st;
-  if (bad_slot) return fail(SEKV_EHIP, "factor cache slot outside the arena (internal error); out was not written");
-  const auto t_booked = std::chrono::steady_clock::now();
-  FillItem* d_fill = reinterpret_cast<FillItem*>(dws + p.off_fill);
+  const std::vector<CacheItem>& items = fc->items;
+  const size_t ne = items.size();
+  {
+    int64_t base = 0;
+    for (int g = 0; g < BG; ++g) {
+      h_soff[g] = base;
+      base += h_count[g];
+    }
+  }
+  const FillItem* d_fill = static_cast<const FillItem*>(device_address(h_fill));
+  if (!d_fill) return fail(SEKV_EHIP, "the pinned host workspace has no device address");
   int64_t* d_soff = reinterpret_cast<int64_t*>(dws + p.off_stage_off);
   // slots being refilled may still be read by the previous cached call's expanded pass
   if (fc->read_recorded) HIP_OR_FAIL(hipStreamWaitEvent(copy_stream, fc->ev_read, 0));
-  HIP_OR_FAIL(hipMemcpyAsync(d_soff, h_soff, (size_t)(BG + 2 * ne) * sizeof(int64_t), hipMemcpyHostToDevice, copy_stream));
-  if (n_fill > 0) {
-    HIP_OR_FAIL(hipMemcpyAsync(d_fill, h_fill, (size_t)n_fill * sizeof(FillItem), hipMemcpyHostToDevice, copy_stream));
-    HIP_OR_FAIL(prof_pair(ctx, ctx->prof_fill, &t0, &t1));
-    HIP_OR_FAIL(launch_cache_fill(d_fill, n_fill, fc->arena, copy_stream, t0, t1));
+  // bookkeeping partition by partition (each over its groups' entries in list
+  // order); after every chunk of partitions its fills start on the copy
+  // stream while the host works on the next chunk
+  fc->book.begin();
+  const int P = std::min(fc->book.parts(), BG);
+  const int per = (P + kCacheChunks - 1) / kCacheChunks;
+  const intptr_t arena = (intptr_t)fc->arena;
+  const int64_t arena_bytes = fc->book.arena_bytes();
+  int64_t* ent = h_soff + BG;   // (factor, sigma|gate) offsets per entry, list order
+  bool bad_slot = false;
+  int n_fill = 0;
+  for (int p0 = 0; p0 < P && !bad_slot; p0 += per) {
+    const int f0 = n_fill;
+    for (int pi = p0; pi < std::min(P, p0 + per) && !bad_slot; ++pi) {
+      CachePart& part = fc->book.part(pi);
+      for (int g = pi; g < BG && !bad_slot; g += fc->book.parts()) {
+        for (int64_t i = h_soff[g], i1 = h_soff[g] + h_count[g]; i < i1; ++i) {
+          const CacheItem& it = items[i];
+          int64_t off = -1;
+          const int32_t stt = part.lookup(it.key, it.bytes, it.tag, &off);
+          int64_t* e = ent + 2 * i;
+          const intptr_t fsrc = (intptr_t)(fac_dev + it.fac * es);
+          const intptr_t gsrc = (intptr_t)(sg_dev + it.sg * 4);
+          if (stt == CachePart::kBypass) {
+            e[0] = (int64_t)(fsrc - arena) / es;
+            e[1] = (int64_t)(gsrc - arena) / 4;
+            continue;
+          }
+          if (off < 0 || off + it.bytes > arena_bytes) {
+            bad_slot = true;
+            break;
+          }
+          e[0] = off / es;
+          e[1] = (off + it.fb) / 4;
+          if (stt == CachePart::kFill)
+            h_fill[n_fill++] = FillItem{(uint64_t)fsrc, (uint64_t)gsrc, (uint64_t)off, (uint32_t)it.fb,
+                                        (uint32_t)(it.bytes - it.fb)};
+        }
+      }
+    }
+    if (n_fill > f0 && !bad_slot) {
+      // the kernel reads its items from the pinned workspace (written above)
+      HIP_OR_FAIL(prof_pair(ctx, ctx->prof_fill, &t0, &t1));
+      HIP_OR_FAIL(launch_cache_fill(d_fill + f0, n_fill - f0, fc->arena, copy_stream, t0, t1));
+    }
   }
+  const auto t_booked = std::chrono::steady_clock::now();
+  HIP_OR_FAIL(hipMemcpyAsync(d_soff, h_soff, (size_t)(BG + 2 * ne) * sizeof(int64_t), hipMemcpyHostToDevice, copy_stream));
   HIP_OR_FAIL(hipEventRecord(ctx->ev_copy, copy_stream));
   if (copy_stream != stream) HIP_OR_FAIL(hipStreamWaitEvent(stream, ctx->ev_copy, 0));
+  if (bad_slot) {
+    // nothing reads the arena: the expanded pass and the merge are not launched
+    return fail(SEKV_EHIP, "factor cache slot outside the arena (internal error); out was not written");
+  }
   AttendArgs a5 = a;
   a5.stage_off = d_soff;
   a5.stage_fac = fc->arena;

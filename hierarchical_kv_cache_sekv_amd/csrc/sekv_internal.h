@@ -160,8 +160,9 @@ hipError_t launch_seal(const SealArgs& a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_build(const BuildArgs& a, int grid, size_t lds_bytes, hipStream_t s);
 // Workgroups of the span build kernel resident at once with lds_bytes of dynamic LDS.
 hipError_t build_resident_blocks(const BuildArgs& a, size_t lds_bytes, int device, int* blocks);
-// Copy n cache fills (items in device memory) into the arena; the arena must
-// hold every dst + fac_bytes + sg_bytes (checked by the caller).
+// Copy n cache fills into the arena; `items` is a device-visible address (the
+// pinned host workspace); the arena must hold every dst + fac_bytes +
+// sg_bytes (checked by the caller).
 hipError_t launch_cache_fill(const FillItem* items, int n, char* arena, hipStream_t s, hipEvent_t ev0 = nullptr,
                              hipEvent_t ev1 = nullptr);
 

@@ -14,7 +14,13 @@ five workloads below are synthetic stand-ins with the Llama-3-8B layer shape
 Random streams: ``numpy.random.default_rng([workload_id, stream, b])`` with
 stream ids 0 surprisal, 1 K/V noise, 2 per-block low-rank component, 3 ranks,
 4 rank gates, 5 routing projections, 6 queries, 7 per-sequence expansion
-fractions.
+fractions; layer l > 0 of a multi-layer workload appends l to every seed.
+
+Queries are independent across decode steps unless ``query_corr`` = c > 0:
+then the query of step t is c q_{t-1} + sqrt(1 - c^2) e_t (e the same normal
+draws), a stand-in for the step-to-step similarity of a decoding model's
+queries, which the pages do not quantify; it matters only where results carry
+over between steps (the device factor cache).
 """
 from __future__ import annotations
 
@@ -54,6 +60,9 @@ class Workload:
     rank_cap: str = "full"      # "full": r <= L; "half": r <= ceil(L / 2)
     basis: str = "joint"        # "joint": one basis of [K | V]; "separate": K and V bases
     route_keys: str = "rho"     # "rho": route on rho; "folded": (P^T P q) . kbar / |P kbar|
+    # multi-layer workloads: seed namespace of the layer, and step-to-step query correlation
+    layer: int = 0
+    query_corr: float = 0.0
 
     @property
     def group(self) -> int:
@@ -107,7 +116,7 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def _rng(w: Workload, stream: int, b: int) -> np.random.Generator:
-    return np.random.default_rng([w.wid, stream, b])
+    return np.random.default_rng([w.wid, stream, b] + ([w.layer] if w.layer else []))
 
 
 @dataclasses.dataclass
@@ -195,6 +204,10 @@ def make_inputs(w: Workload, *, n_steps: int | None = None, rank_cap: int | None
             rank_req[b] = _rng(w, 3, b).integers(w.rank_lo, w.rank_hi + 1, cap, dtype=np.int32)
             gate[b] = _rng(w, 4, b).uniform(0.0, 1.0, (Hkv, cap, r_cap)).astype(np.float32)
         q[:, b] = _rng(w, 6, b).standard_normal((steps, Hq, d), dtype=np.float32)
+        if w.query_corr > 0.0:
+            c, s2 = np.float32(w.query_corr), np.float32(math.sqrt(1.0 - w.query_corr ** 2))
+            for t in range(1, steps):
+                q[t, b] = c * q[t - 1, b] + s2 * q[t, b]
     proj = _rng(w, 5, 0).normal(0.0, 1.0 / math.sqrt(d), (Hkv, d, d)).astype(np.float32)
     if w.expand_frac < 0:
         ef = _rng(w, 7, 0).uniform(0.0, -w.expand_frac, B)

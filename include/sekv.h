@@ -449,20 +449,23 @@ sekv_status sekv_append_token(sekv_ctx* ctx, const sekv_config* cfg, const sekv_
  * (factor block + sigma|gate entry) of recently expanded spans in an HBM arena
  * across decode steps and layers, so a span expanded again is read from HBM.
  *
- * Policy: the arena is cut into 2 MiB pages; a block takes a slot of the
+ * Policy: the arena is cut into 2 MiB pages, split evenly among `partitions`
+ * partitions; the blocks of KV group g = b * Hkv + kv belong to partition
+ * g mod partitions, which manages its own pages: a block takes a slot of the
  * smallest size class that holds it (classes grow by about 1.25x from 1 KiB in
- * 256-byte steps); a class takes a free page when it has no free slot, and
- * once every page is assigned it evicts its least recently used block.  Blocks
- * used by the current call are never evicted by that call: a block that finds
- * every slot of its class in use by the call is read over the bus directly
- * (a bypass).  Blocks are keyed by (layer, b * Hkv + kv, span index); a key
+ * 256-byte steps); a class takes a free page of its partition when it has no
+ * free slot, and once every page is assigned it evicts its least recently used
+ * block.  Blocks used by the current call are never evicted by that call: a
+ * block that finds every slot of its class in use by the call is read over the
+ * bus directly (a bypass).  Blocks are keyed by (layer, g, span index); a key
  * whose host address or size changed is refilled.  After rebuilding a layer's
  * spans in place, invalidate that layer.
  *
  * sekv_factor_cache_create: an arena of floor(bytes / 2 MiB) pages on ctx's
- *   device (hipMalloc), owned by the cache.  ctx may be NULL: then the cache
- *   has no arena and serves only sekv_factor_cache_lookup (the bookkeeping, on
- *   the host).  Errors: SEKV_EINVAL, SEKV_ESHAPE (bytes < 2 MiB), SEKV_EHIP,
+ *   device (hipMalloc), owned by the cache; partitions 1..256, 0 for the
+ *   default 8.  ctx may be NULL: then the cache has no arena and serves only
+ *   sekv_factor_cache_lookup (the bookkeeping, on the host).  Errors:
+ *   SEKV_EINVAL, SEKV_ESHAPE (less than one page per partition), SEKV_EHIP,
  *   SEKV_ENOMEM.
  * sekv_factor_cache_destroy: waits for the last cached decode that read the
  *   arena, then frees it.
@@ -480,7 +483,7 @@ typedef struct sekv_cache_stats {
   int64_t pages_used, pages_total;
 } sekv_cache_stats;
 
-sekv_status sekv_factor_cache_create(sekv_ctx* ctx, size_t bytes, sekv_factor_cache** out);
+sekv_status sekv_factor_cache_create(sekv_ctx* ctx, size_t bytes, int32_t partitions, sekv_factor_cache** out);
 void sekv_factor_cache_destroy(sekv_factor_cache* cache);
 sekv_status sekv_factor_cache_invalidate(sekv_factor_cache* cache, int32_t layer);
 sekv_status sekv_factor_cache_stats(sekv_factor_cache* cache, sekv_cache_stats* out, int32_t reset);
@@ -519,9 +522,11 @@ size_t sekv_cached_decode_host_workspace_bytes(const sekv_ctx* ctx, const sekv_c
  * index (0..65535).
  *   Sequence: the list is copied to the host and the full-resolution +
  *   summary pass starts on `stream`; after the one host wait the cache
- *   bookkeeping assigns slots; the stage table and the fill list are copied
- *   and the fill kernel pulls the missing blocks from the pinned pools into
- *   their slots on copy_stream, while the full-resolution pass runs; the
+ *   bookkeeping assigns slots partition by partition, and after every
+ *   quarter of the partitions a fill kernel pulls that part's missing blocks
+ *   from the pinned pools into their slots on copy_stream (reading its item
+ *   list from host_ws) while the host goes on; the stage table is copied;
+ *   all of this runs beside the full-resolution pass; the
  *   expanded-span pass then reads hits and fills from HBM (bypassed blocks
  *   from the pinned pools), followed by the merge on `stream`.
  *   A layer's route needs that layer's query, which in a model comes from the

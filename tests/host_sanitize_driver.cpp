@@ -88,7 +88,8 @@ int main() {
     sp.fac_elems = fe;
     sp.sg_elems = ge;
     sekv_factor_cache* fc = nullptr;
-    EXPECT(sekv_factor_cache_create(nullptr, (size_t(2) << 20) * (1 + rng() % 2), &fc) == SEKV_OK);
+    const int parts = 1 + (int)(rng() % 3);
+    EXPECT(sekv_factor_cache_create(nullptr, (size_t(2) << 20) * parts * (1 + rng() % 2), parts, &fc) == SEKV_OK);
     std::vector<int32_t> lst((size_t)B * Hkv * seg_cap), cnt((size_t)B * Hkv), stt(lst.size());
     std::vector<int64_t> off(lst.size());
     for (int call = 0; call < 6 && fc; ++call) {

@@ -2,14 +2,16 @@
 on a cache created without a context.
 
 The policy under test is the one include/sekv.h documents for
-sekv_factor_cache_create: 2 MiB pages, slot classes growing by about 1.25x
-from 1 KiB in 256-byte steps, a page per class on demand, per-class LRU
-eviction once every page is assigned, blocks of the current call pinned
-(bypass when a class has nothing else to evict), and a refill when a key's
-host address or size changes.  `PolicyModel` restates that policy in plain
-Python; the library must agree with it on every status and slot offset, and
-the results must also satisfy properties that hold under any correct policy
-(disjoint slots, consistent counters, hits at the slot of the fill).
+sekv_factor_cache_create: 2 MiB pages split evenly among partitions (KV group
+g in partition g mod partitions), and per partition slot classes growing by
+about 1.25x from 1 KiB in 256-byte steps, a page per class on demand,
+per-class LRU eviction once the partition's pages are assigned, blocks of the
+current call pinned (bypass when a class has nothing else to evict), and a
+refill when a key's host address or size changes.  `PolicyModel` restates
+that policy in plain Python; the library must agree with it on every status
+and slot offset, and the results must also satisfy properties that hold under
+any correct policy (disjoint slots, consistent counters, hits at the slot of
+the fill).
 """
 import ctypes
 from collections import OrderedDict
@@ -34,10 +36,12 @@ def slot_classes():
         s = (nx + 255) // 256 * 256
 
 
-class PolicyModel:
-    def __init__(self, nbytes):
+class PartModel:
+    """One partition: pages [page0, page0 + pages)."""
+
+    def __init__(self, page0, pages):
         self.cls = slot_classes()
-        self.pages, self.next_page, self.epoch = nbytes // PAGE, 0, 0
+        self.page0, self.pages, self.next_page, self.epoch = page0, pages, 0, 0
         self.free = [[] for _ in self.cls]
         self.lru = [OrderedDict() for _ in self.cls]   # least recent first
         self.ent = {}                                  # key -> [tag, bytes, off, epoch, cls]
@@ -54,7 +58,7 @@ class PolicyModel:
     def take(self, c):
         fr = self.free[c]
         if not fr and self.next_page < self.pages:
-            base = self.next_page * PAGE
+            base = (self.page0 + self.next_page) * PAGE
             self.next_page += 1
             fr.extend(base + i * self.cls[c] for i in reversed(range(PAGE // self.cls[c])))
         if fr:
@@ -85,6 +89,20 @@ class PolicyModel:
         self.ent[key] = [tag, nb, slot, self.epoch, c]
         self.lru[c][key] = None
         return FILL, slot
+
+
+class PolicyModel:
+    def __init__(self, nbytes, parts):
+        n = nbytes // PAGE
+        self.parts = [PartModel(n * p // parts, n * (p + 1) // parts - n * p // parts) for p in range(parts)]
+
+    def begin(self):
+        for p in self.parts:
+            p.begin()
+
+    def lookup(self, key, nb, tag):
+        g = (key >> 32) & 0xFFFF
+        return self.parts[g % len(self.parts)].lookup(key, nb, tag)
 
 
 def make_layout(seed, B_=2, Hkv=2, D=128, n_spans=60, Lmin=1, Lmax=40, rmin=1, rmax=32, uniform=None,
@@ -173,8 +191,8 @@ def test_cache_follows_the_policy_over_random_calls():
     spans = spans_of(cfg, plan)
     BG = cfg.batch * cfg.n_kv_heads
     nbytes = 2 * PAGE + 12345
-    fc = B.FactorCache(None, nbytes)
-    model = PolicyModel(nbytes)
+    fc = B.FactorCache(None, nbytes, partitions=1)
+    model = PolicyModel(nbytes, 1)
     rng = np.random.default_rng(11)
     prev = {}
     totals = {"lookups": 0, "hits": 0, "fills": 0, "bypasses": 0}
@@ -204,8 +222,36 @@ def test_cache_follows_the_policy_over_random_calls():
         assert stats[k] == v
     assert stats["pages_used"] == stats["pages_total"] == 2
     assert stats["evictions"] > 0 and stats["hits"] > 0 and seen_bypass
-    assert stats["resident_blocks"] == len(model.ent)
-    assert stats["resident_bytes"] == sum(e[1] for e in model.ent.values())
+    ents = [e for part in model.parts for e in part.ent.values()]
+    assert stats["resident_blocks"] == len(ents)
+    assert stats["resident_bytes"] == sum(e[1] for e in ents)
+    fc.close()
+
+
+def test_partitions_follow_the_policy_over_random_calls():
+    """Four KV groups over three partitions (groups 0 and 3 share one), seven
+    pages (2 + 2 + 3): each partition runs the policy on its own pages."""
+    cfg, plan = make_layout(8, Lmin=24, rmin=24, tiny_every=5)
+    spans = spans_of(cfg, plan)
+    BG = cfg.batch * cfg.n_kv_heads
+    nbytes = 7 * PAGE
+    fc = B.FactorCache(None, nbytes, partitions=3)
+    model = PolicyModel(nbytes, 3)
+    rng = np.random.default_rng(12)
+    prev = {}
+    for step in range(30):
+        for layer in (0, 2):
+            lists = []
+            for g in range(BG):
+                n = int(plan.n_seg[g // cfg.n_kv_heads])
+                old = prev.get((layer, g), np.zeros(0, np.int64))
+                keep = old[rng.random(old.size) < 0.6]
+                new = rng.choice(n, size=int(rng.integers(0, 24)), replace=False)
+                lists.append(np.unique(np.concatenate([keep, new])).astype(np.int32))
+                prev[(layer, g)] = lists[-1]
+            assert lib_batch(fc, layer, cfg, plan, spans, lists) == model_batch(model, layer, cfg, plan, spans, lists)
+    st = fc.stats()
+    assert st["evictions"] > 0 and st["hits"] > 0 and st["pages_total"] == 7
     fc.close()
 
 
@@ -216,7 +262,7 @@ def test_least_recently_used_block_leaves_first_and_the_call_pins_its_blocks():
     slot = next(s for s in slot_classes() if s >= nb)
     N = PAGE // slot
     assert N + 3 <= 400
-    fc = B.FactorCache(None, PAGE)
+    fc = B.FactorCache(None, PAGE, partitions=1)
     run = lambda lst: lib_batch(fc, 0, cfg, plan, spans, [np.asarray(lst, np.int32)])
     # one call larger than the cache: N fills, then bypasses (nothing of the call is evicted)
     res = run(range(N + 2))
@@ -258,7 +304,7 @@ def test_bad_list_is_rejected_and_changes_nothing():
     cfg, plan = make_layout(9)
     spans = spans_of(cfg, plan)
     BG, cap = cfg.batch * cfg.n_kv_heads, plan.rank.shape[1]
-    fc = B.FactorCache(None, 4 * PAGE)
+    fc = B.FactorCache(None, 4 * PAGE, partitions=2)
     exp_list = np.zeros((BG, cap), np.int32)
     exp_count = np.full(BG, 3, np.int32)
     exp_list[:, :3] = [1, 2, 3]
@@ -274,7 +320,11 @@ def test_bad_list_is_rejected_and_changes_nothing():
         fc.lookup(0, cfg, spans, exp_list, exp_count)
     assert fc.stats() == before
     with pytest.raises(B.SekvError):
-        B.FactorCache(None, PAGE - 1)
+        B.FactorCache(None, PAGE - 1, partitions=1)
+    with pytest.raises(B.SekvError):
+        B.FactorCache(None, 3 * PAGE, partitions=4)
+    with pytest.raises(B.SekvError):
+        B.FactorCache(None, 4 * PAGE, partitions=300)
     with pytest.raises(B.SekvError):
         fc.lookup(70000, cfg, spans, exp_list, np.zeros(BG, np.int32))
     fc.close()

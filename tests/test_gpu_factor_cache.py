@@ -53,7 +53,7 @@ def test_cached_decode_matches_direct_fetch_bitwise_across_layers_and_steps(ctx)
     layers = [Layer(ctx, prepare(synth.workload(3, n_ctx=8192), steps)),
               Layer(ctx, prepare(synth.workload(3, n_ctx=6000, rank_lo=4, rank_hi=24), steps))]
     side = torch.cuda.Stream()
-    fc = B.FactorCache(ctx, 2 * B.CACHE_PAGE_BYTES)    # small: evictions and bypasses
+    fc = B.FactorCache(ctx, 3 * B.CACHE_PAGE_BYTES, partitions=2)    # small: evictions and bypasses
     listed = 0
     for si in steps:
         for li, L in enumerate(layers):
@@ -103,11 +103,11 @@ def test_cached_decode_argument_errors(ctx):
     d = L.dev
     d.route(ctx, 0)
     torch.cuda.synchronize()
-    no_arena = B.FactorCache(None, B.CACHE_PAGE_BYTES)
+    no_arena = B.FactorCache(None, B.CACHE_PAGE_BYTES, partitions=1)
     with pytest.raises(B.SekvError) as e:
         B.cached_decode(ctx, no_arena, 0, d.cache, d.q(0), d.route_out, L.out_c, L.ws)
     assert e.value.status == B.SEKV_EINVAL
-    fc = B.FactorCache(ctx, B.CACHE_PAGE_BYTES)
+    fc = B.FactorCache(ctx, B.CACHE_PAGE_BYTES, partitions=1)
     with pytest.raises(B.SekvError):
         B.cached_decode(ctx, fc, 70000, d.cache, d.q(0), d.route_out, L.out_c, L.ws)
     dev_d = Device(d.p, factors_on_host=False)
