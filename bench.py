@@ -41,7 +41,7 @@ COUNTER_SOURCES = ["hierarchical_kv_cache_sekv_amd/csrc/sekv_kernels.hip",
 # library kernels named in rocprofv3 output -> short names
 KERNELS = ("attend_fused_kernel", "attend_full_kernel", "attend_expanded_kernel", "attend_expanded_wide_kernel",
            "route_kernel", "fold_query_kernel", "combine_kernel", "seal_build_kernel", "seal_compact_kernel",
-           "build_spans_kernel", "build_full_kernel")
+           "build_spans_kernel", "build_full_kernel", "cache_fill_kernel")
 
 
 def log(msg):
