@@ -682,35 +682,36 @@ __device__ __forceinline__ void role_full_summary(const AttendArgs& a, int idx, 
 }
 
 // Role E (expanded spans): one wave per workgroup.  A work item is up to
-// kExpChunk consecutive entries of one (b, kv) expanded list, processed in
-// chunks of consecutive spans whose token groups fit the wave's score
-// buffer.  Per chunk, two passes:
-//   pass 1, per span: y[k][h] = sigma_k gate_k (Vh_K[k] . q_h) log2(e)/sqrt(d)
+// kExpChunk consecutive entries of one (b, kv) expanded list, processed one
+// span at a time in two passes:
+//   pass 1: y[k][h] = sigma_k gate_k (Vh_K[k] . q_h) log2(e)/sqrt(d)
 //           (A = Vh_K rows, B = q) and the token scores s[t][h] = U[t] . y[:, h]
-//           (A = U rows, B = y), kept in LDS; the chunk's maximum per head.
-//   pass 2, per span: p = exp2(s - m), a[k][h] = sum_t U[t][k] p[t][h]
+//           (A = U rows, B = y), kept in LDS; the span's maximum per head.
+//   pass 2: p = exp2(s - m), a[k][h] = sum_t U[t][k] p[t][h]
 //           (A = U^T rows, B = p) and o[j][h] += sum_k W_V[j][k] sigma_k gate_k a[k][h]
 //           (A = W_V rows, B = b).
-// With the chunk maximum known before pass 2, the output accumulators are
-// rescaled once per chunk, not per span, and the two passes keep different
-// registers live.  Head h = lane % 16 (columns >= G unused); ranks and tokens
-// in groups of 16.  The products of scores, U^T p and W_V b are 16x16x16: the
-// result of each (lane 16c + h holds rows 4c..4c+3 of column h) is exactly
-// the B operand the next one takes, so nothing moves between lanes.  bf16: y
-// enters the score product as a two-term bf16 split (hi + lo, about 16
-// significant bits), p and b are rounded to bf16; float: every product in
-// float32.
+// Between the passes the output accumulators are rescaled once to the new
+// maximum; the two passes keep different registers live.  Head h = lane % 16
+// (columns >= G unused); ranks and tokens in groups of 16.  The products of
+// scores, U^T p and W_V b are 16x16x16: the result of each (lane 16c + h
+// holds rows 4c..4c+3 of column h) is exactly the B operand the next one
+// takes, so nothing moves between lanes.  bf16: y enters the score product as
+// a two-term bf16 split (hi + lo, about 16 significant bits), p and b are
+// rounded to bf16; float: every product in float32.
 //
 // Factor data streams through a per-wave LDS ring in 1 KB chunks (16 bytes
 // per lane), loaded into registers one granule (ExpCfg::K chunks) ahead of
 // the consumer and written to the ring a granule at a time.  The stream is a
-// sequence of regions, each starting on a chunk boundary; per chunk of spans:
-//   pass 1: for each span  sigma|gate entry, then Vh_K | U (contiguous),
-//   pass 2: for each span  sigma|gate entry, then U | W_V (contiguous).
+// sequence of regions, each starting on a chunk boundary; per span:
+//   read once (one basis, U at most RING - 1024 K bytes): the sigma|gate
+//     entry, then the whole block Vh_K | U | W_V; pass 2 reads U where pass 1
+//     left it in the ring and sigma * gate from LDS;
+//   one basis, larger U: the entry, Vh_K | U, then U | W_V;
+//   separate bases: the entry's key half, Vh_K | U_K, its value half,
+//     U_V | W_V.
 // Factor block of a span: Vh_K [r][d] (8-element groups rotated by the row) |
 // U [L][rp] | W_V in 16-rank column blocks [d][min(16, rp - 16 g)].  Lanes
 // past the end of a region re-read its last 16 bytes (no extra memory lines).
-// U is read twice (about 6% of a span's factor bytes).
 template <typename T, int RGM> struct ExpCfg;
 // K: 1 KB chunks per granule in flight.  The ring holds a granule in flight
 // plus the largest piece read at once (16 rows of Vh_K or U, or one 16-rank
@@ -719,7 +720,7 @@ template <typename T, int RGM> struct ExpCfg;
 // unit holds.
 template <int RGM> struct ExpCfg<bf16raw, RGM> { static constexpr int K = 4; static constexpr int kRing = 8192; };
 template <int RGM> struct ExpCfg<float, RGM> { static constexpr int K = 8; static constexpr int kRing = 16384; };
-constexpr int kExpTok = 192;   // tokens of one chunk of spans (score buffer)
+constexpr int kExpTok = kMaxSpan;   // tokens of one span (score buffer)
 
 // Byte positions in a per-wave ring of RING bytes (a multiple of 1 KB, not
 // necessarily a power of two).
@@ -823,11 +824,22 @@ struct ItemMeta {
   int L, r, bits;
   uint64_t sga, fa;   // global addresses of the sg entry and the factor block
 };
-// Region `kind` of span i: 0 / 2 sigma|gate, 1 Vh_K | U, 3 U | W_V.  With
-// separate key and value bases (sep) the block is Vh_K | U_K | U_V | W_V and
-// the sigma|gate entry sigma_K | gate | sigma_V | gate: region 2 is the second
-// half of the entry and region 3 is U_V | W_V.
-template <typename T, int D>
+// A span is read once (sigma|gate, then its whole factor block) when its U
+// stays in the ring from the score pass to the weight pass: nothing is
+// written to the ring between the two, and after the score pass the ring
+// holds at least RING - 1024 K bytes before the end of U.  Otherwise (and
+// with separate bases) the weight pass streams U | W_V again.
+template <typename T, int K, uint32_t RING>
+__device__ __forceinline__ bool read_once(int L, int r, bool sep) {
+  return !sep && (uint32_t)(L * ((r + 7) & ~7)) * (uint32_t)sizeof(T) <= RING - 1024u * K;
+}
+
+// Region `kind` of span i: 0 / 2 sigma|gate, 1 Vh_K | U (the whole block
+// Vh_K | U | W_V for a span read once), 3 U | W_V.  With separate key and
+// value bases (sep) the block is Vh_K | U_K | U_V | W_V and the sigma|gate
+// entry sigma_K | gate | sigma_V | gate: region 2 is the second half of the
+// entry and region 3 is U_V | W_V.
+template <typename T, int D, int K, uint32_t RING>
 __device__ __forceinline__ void region_of(const ItemMeta& m, int i, int kind, bool sep, uint64_t& base, uint32_t& size) {
   constexpr uint32_t ES = sizeof(T);
   const int L = __builtin_amdgcn_readlane(m.L, i), r = __builtin_amdgcn_readlane(m.r, i);
@@ -837,48 +849,43 @@ __device__ __forceinline__ void region_of(const ItemMeta& m, int i, int kind, bo
     size = 8u * rq;
   } else if (kind == 1) {
     base = readlane64(m.fa, i);
-    size = ES * ((uint32_t)r * D + (uint32_t)L * rp);
+    size = ES * ((uint32_t)r * D + (uint32_t)L * rp + (read_once<T, K, RING>(L, r, sep) ? D * rp : 0u));
   } else {
     base = readlane64(m.fa, i) + ES * (uint64_t)((uint32_t)r * D + (sep ? (uint32_t)L * rp : 0u));
     size = ES * ((uint32_t)L * rp + D * rp);
   }
 }
 
-// Wave-uniform walk over the regions of an item: chunk [ca, cb) of spans,
-// span i, region kind, byte `off` of a region of `size` bytes at `base`.
-// Chunk starts are the set bits of `cmask` (bit n set as an end marker).
-// Past the last region the final chunk is repeated (never read from the ring).
+// Wave-uniform walk over the regions of an item, span by span: span i,
+// region kind, byte `off` of a region of `size` bytes at `base`.  Per span the
+// regions are 0, 1 (read once); 0, 1, 3 (one basis); 0, 1, 2, 3 (separate
+// bases).  Past the last region the last 1 KB is repeated (never read from
+// the ring).
 struct RegionCursor {
-  int i, kind, ca, cb, n;
+  int i, kind, n;
   bool sep;
-  uint32_t cmask;
   uint32_t off, size;
   uint64_t base;
 };
-__device__ __forceinline__ int chunk_end(uint32_t cmask, int a) { return a + 1 + __builtin_ctz(cmask >> (a + 1)); }
 
-template <typename T, int D>
+template <typename T, int D, int K, uint32_t RING>
 __device__ __forceinline__ void cursor_next(RegionCursor& c, const ItemMeta& m) {
   c.off += 1024u;
   if (c.off < c.size) return;
+  const bool once = c.kind == 1 && read_once<T, K, RING>(__builtin_amdgcn_readlane(m.L, c.i),
+                                                          __builtin_amdgcn_readlane(m.r, c.i), c.sep);
   if (c.kind == 0 || c.kind == 2) {
     c.kind += 1;
-  } else if (c.i + 1 < c.cb) {
+  } else if (c.kind == 1 && !once) {
+    c.kind = c.sep ? 2 : 3;
+  } else if (c.i + 1 < c.n) {
     c.i += 1;
-    c.kind -= 1;
-  } else if (c.kind == 1) {
-    c.i = c.ca;
-    c.kind = 2;
-  } else if (c.cb < c.n) {
-    c.ca = c.cb;
-    c.cb = chunk_end(c.cmask, c.ca);
-    c.i = c.ca;
     c.kind = 0;
   } else {
     c.off -= 1024u;
     return;
   }
-  region_of<T, D>(m, c.i, c.kind, c.sep, c.base, c.size);
+  region_of<T, D, K, RING>(m, c.i, c.kind, c.sep, c.base, c.size);
   c.off = 0;
 }
 __device__ __forceinline__ uint64_t cursor_addr(const RegionCursor& c, int lane) {
@@ -907,7 +914,7 @@ __device__ __forceinline__ void advance(uint4 (&stg)[K * kExpStages], uint32_t& 
 #pragma unroll
     for (int jj = 0; jj < K; ++jj) {
       stg[K * (kExpStages - 1) + jj] = gload16(cursor_addr(c, lane));
-      cursor_next<T, D>(c, m);
+      cursor_next<T, D, K, RING>(c, m);
     }
     written += 1024u * K;
   }
@@ -991,34 +998,18 @@ __device__ __forceinline__ void role_expanded(const AttendArgs& a, int wid, int 
       im.sga = reinterpret_cast<uint64_t>(gb + mgo * 4);
       im.fa = reinterpret_cast<uint64_t>(fb + mfo * ES);
     }
-    // chunks of spans: consecutive spans while their token groups fit kExpTok
-    uint32_t cmask = 1u | (1u << n);
-    {
-      int tg = 0;
-      for (int i = 0; i < n; ++i) {
-        const int t = (__builtin_amdgcn_readlane(im.L, i) + 15) >> 4;
-        if (tg + t > kExpTok / 16) {
-          cmask |= 1u << i;
-          tg = 0;
-        }
-        tg += t;
-      }
-    }
     RegionCursor cur;
     cur.n = n;
     cur.sep = a.sep != 0;
-    cur.cmask = cmask;
-    cur.ca = 0;
-    cur.cb = chunk_end(cmask, 0);
     cur.i = 0;
     cur.kind = 0;
     cur.off = 0;
-    region_of<T, D>(im, 0, 0, cur.sep, cur.base, cur.size);
+    region_of<T, D, K, RING>(im, 0, 0, cur.sep, cur.base, cur.size);
     uint4 stg[K * kExpStages];
 #pragma unroll
     for (int jj = 0; jj < K * kExpStages; ++jj) {
       stg[jj] = gload16(cursor_addr(cur, lane));
-      cursor_next<T, D>(cur, im);
+      cursor_next<T, D, K, RING>(cur, im);
     }
     uint32_t written = 0, spos = 0;
 
@@ -1033,20 +1024,24 @@ __device__ __forceinline__ void role_expanded(const AttendArgs& a, int wid, int 
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) acc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int ca = 0; ca < n; ca = chunk_end(cmask, ca)) {
-      const int cb = chunk_end(cmask, ca);
-      // ---------------- pass 1: scores of the chunk's tokens
+    // one span at a time: its score pass, one rescale, its weight pass
+    for (int ca = 0; ca < n; ++ca) {
+      const int cb = ca + 1;
+      // ---------------- pass 1: scores of the span's tokens
       float cmax = kNegInf;
       int tgb = 0;
+      uint32_t s_u1 = 0;   // U of the span read once: the weight pass reads it where this pass left it
       for (int i = ca; i < cb; ++i) {
         const int L = __builtin_amdgcn_readlane(im.L, i), r = __builtin_amdgcn_readlane(im.r, i);
         const int rp = (r + 7) & ~7, rq = (r + 3) & ~3;
         const bool head_on = ((uint32_t)__builtin_amdgcn_readlane(im.bits, i) >> col) & 1u;
         const int RG = (r + 15) >> 4, TG = (L + 15) >> 4;
+        const bool once = read_once<T, K, RING>(L, r, cur.sep);
         const uint32_t s_sg = spos;
         const uint32_t s_vk = s_sg + kb_round(8u * (uint32_t)rq);
         const uint32_t s_u = s_vk + (uint32_t)(r * D * ES);
-        spos = s_vk + kb_round((uint32_t)((r * D + L * rp) * ES));
+        s_u1 = s_u;
+        spos = s_vk + kb_round((uint32_t)((r * D + L * rp + (once ? D * rp : 0)) * ES));
         advance<T, D, K, RING>(stg, written, s_sg + 8u * (uint32_t)rq, cur, im, lane, ring);
         // sigma * gate (zero past r), staged in LDS: the ring holds the entry
         // only until the next advance
@@ -1131,20 +1126,28 @@ __device__ __forceinline__ void role_expanded(const AttendArgs& a, int wid, int 
         const int L = __builtin_amdgcn_readlane(im.L, i), r = __builtin_amdgcn_readlane(im.r, i);
         const int rp = (r + 7) & ~7, rq = (r + 3) & ~3;
         const int RG = (r + 15) >> 4, TG = (L + 15) >> 4;
-        const uint32_t s_sg = spos;
-        const uint32_t s_u = s_sg + kb_round(8u * (uint32_t)rq);
-        const uint32_t s_w = s_u + (uint32_t)(L * rp * ES);
-        spos = s_u + kb_round((uint32_t)((L * rp + D * rp) * ES));
-        advance<T, D, K, RING>(stg, written, s_sg + 8u * (uint32_t)rq, cur, im, lane, ring);
-        // sigma * gate (zero past r) for step 5, staged in LDS
+        uint32_t s_u;
+        if (read_once<T, K, RING>(L, r, cur.sep)) {
+          s_u = s_u1;                       // still in the ring; sigma * gate still in LDS
+        } else if (!cur.sep) {
+          s_u = spos;                       // U | W_V again; sigma * gate still in LDS
+          spos = s_u + kb_round((uint32_t)((L * rp + D * rp) * ES));
+        } else {
+          // separate bases: sigma_V * gate of the value basis, then U_V | W_V
+          const uint32_t s_sg = spos;
+          s_u = s_sg + kb_round(8u * (uint32_t)rq);
+          spos = s_u + kb_round((uint32_t)((L * rp + D * rp) * ES));
+          advance<T, D, K, RING>(stg, written, s_sg + 8u * (uint32_t)rq, cur, im, lane, ring);
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          const int k = lane + 64 * q2;
-          const int kc = min(k, r - 1);
-          const float sv = *reinterpret_cast<const float*>(ring + RP::add(RP::of(s_sg), 4u * kc));
-          const float gv = *reinterpret_cast<const float*>(ring + RP::add(RP::of(s_sg), 4u * (rq + kc)));
-          stl[k] = k < r ? sv * gv : 0.0f;
+          for (int q2 = 0; q2 < 2; ++q2) {
+            const int k = lane + 64 * q2;
+            const int kc = min(k, r - 1);
+            const float sv = *reinterpret_cast<const float*>(ring + RP::add(RP::of(s_sg), 4u * kc));
+            const float gv = *reinterpret_cast<const float*>(ring + RP::add(RP::of(s_sg), 4u * (rq + kc)));
+            stl[k] = k < r ? sv * gv : 0.0f;
+          }
         }
+        const uint32_t s_w = s_u + (uint32_t)(L * rp * ES);
         f32x4_t am[RGM];
 #pragma unroll
         for (int rg = 0; rg < RGM; ++rg) am[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
