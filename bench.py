@@ -322,6 +322,7 @@ def measure_device(w, x, fracs, args, label, full_rank=False):
     e = 2 if w.dtype == "bf16" else 4
     Q = min(args.queries, x.q.shape[0])
     ctx = B.Context(0)
+    ctx.set_split(args.split)
     cfg = B.make_config(w, False)
     plan = B.plan_spans(cfg, x.surprisal, x.boundary_thr, x.rank_req)
     cache = B.SpanCache(cfg, plan)
@@ -341,7 +342,7 @@ def measure_device(w, x, fracs, args, label, full_rank=False):
     structs = [c.struct() for c in caches]
     outs = [B.RouteOut(cfg, cache.seg_cap) for _ in range(ncopy)]
     rws = B.route_workspace(cache)
-    dws = B.DecodeWorkspace(cache)
+    dws = B.DecodeWorkspace(cache, ctx=ctx)
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     log(f"{label}: {ncopy} cache copies of {resident / 2**20:.0f} MiB each resident in HBM")
     stream = torch.cuda.Stream()
@@ -839,6 +840,8 @@ def main():
     ap.add_argument("--cpu-workers", type=int, default=0, help="oracle worker processes (0: host cores, at most 16)")
     ap.add_argument("--queries", type=int, default=64)
     ap.add_argument("--graph-steps", type=int, default=8, help="decode steps captured per HIP graph")
+    ap.add_argument("--split", type=int, default=0,
+                    help="full-resolution entries per split-K chunk of the mixed decode (0: the library chooses)")
     ap.add_argument("--overlap", action="store_true",
                     help="one sekv_decode_step call per step (full-resolution pass on a second stream beside the "
                          "route) instead of sekv_route + sekv_mixed_attention_decode")

@@ -540,7 +540,11 @@ __device__ __forceinline__ void role_full_summary(const AttendArgs& a, int idx, 
   constexpr int NC = D / 32, NJ = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, cls = lane >> 4;
-  const int g = idx / a.a4_n, chunk = a.a4_lo + idx % a.a4_n;
+  // chunk-major order over the launch: chunk k of every (b, kv) before chunk
+  // k + 1 of any, so the ragged last chunks are dispatched last (a shorter
+  // tail than group-major order: 79.3 against 81.0 us at 128K batch 4)
+  const int BGn = a.B * a.Hkv;
+  const int g = idx % BGn, chunk = a.a4_lo + idx / BGn;
   const int b = g / a.Hkv, kv = g % a.Hkv;
   const int nf = a.n_full[b], ns = a.n_seg[b];
   const int nft = (nf + 31) / 32, nst = (ns + 31) / 32;
