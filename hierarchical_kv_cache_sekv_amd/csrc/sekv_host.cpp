@@ -1049,6 +1049,7 @@ void make_plan(const sekv_config* c, const sekv_spans* s, int32_t split_entries,
   a.nch_a4 = a.nch_full + (int)((nst + tc - 1) / tc);
   a.a4_lo = 0;
   a.a4_n = a.nch_a4;
+  a.chunk_major = 1;
   a.P_max = a.nch_a4 + (s->seg_cap + kExpChunk - 1) / kExpChunk;
   const int64_t max_items = (int64_t)BG * ((s->seg_cap + kExpChunk - 1) / kExpChunk);
   a.n_a5_wg = (int)std::max<int64_t>(1, std::min<int64_t>(kExpWaves, max_items));

@@ -47,6 +47,7 @@ struct AttendArgs {
   int nch_a4;                // chunks (workgroups) per (b, kv) for that pass: nch_full full-res, then summary
   int nch_full;              // chunks of full-resolution tiles per (b, kv)
   int a4_lo, a4_n;           // this launch's chunks of each (b, kv): [a4_lo, a4_lo + a4_n); n_a4_wg = B*Hkv*a4_n
+  int chunk_major;           // 1: workgroups in chunk-major order over the groups, 0: group-major
   int P_max;                 // partial slots per (b, kv)
   int n_a5_wg;               // workgroups (one wave each) of the expanded-span kernel
   int n_fx_wg;               // workgroups (four expanded-span waves each) of the fused launch

@@ -540,11 +540,13 @@ __device__ __forceinline__ void role_full_summary(const AttendArgs& a, int idx, 
   constexpr int NC = D / 32, NJ = D / 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, cls = lane >> 4;
-  // chunk-major order over the launch: chunk k of every (b, kv) before chunk
-  // k + 1 of any, so the ragged last chunks are dispatched last (a shorter
-  // tail than group-major order: 79.3 against 81.0 us at 128K batch 4)
+  // Chunk-major order (mixed decode): chunk k of every (b, kv) before chunk
+  // k + 1 of any, so the ragged last chunks are dispatched last, a shorter
+  // tail (79.3 against 81.0 us at 128K batch 4).  Group-major (dense decode,
+  // 64 chunks per group): 353-355 against 359-361 us.
   const int BGn = a.B * a.Hkv;
-  const int g = idx % BGn, chunk = a.a4_lo + idx / BGn;
+  const int g = a.chunk_major ? idx % BGn : idx / a.a4_n;
+  const int chunk = a.a4_lo + (a.chunk_major ? idx / BGn : idx % a.a4_n);
   const int b = g / a.Hkv, kv = g % a.Hkv;
   const int nf = a.n_full[b], ns = a.n_seg[b];
   const int nft = (nf + 31) / 32, nst = (ns + 31) / 32;
