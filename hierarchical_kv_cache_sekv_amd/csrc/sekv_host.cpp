@@ -1050,9 +1050,15 @@ void make_plan(const sekv_config* c, const sekv_spans* s, int32_t split_entries,
   a.a4_lo = 0;
   a.a4_n = a.nch_a4;
   a.chunk_major = 1;
-  a.P_max = a.nch_a4 + (s->seg_cap + kExpChunk - 1) / kExpChunk;
-  const int64_t max_items = (int64_t)BG * ((s->seg_cap + kExpChunk - 1) / kExpChunk);
+  const int64_t max_items = (int64_t)BG * ((s->seg_cap + kExpChunkMin - 1) / kExpChunkMin);
   a.n_a5_wg = (int)std::max<int64_t>(1, std::min<int64_t>(kExpWaves, max_items));
+  // Items of one group: ceil(count / c), where the expanded-span pass takes
+  // c = kExpChunk, or max(kExpChunkMin, ceil(listed / waves)).  With
+  // c = kExpChunk that is at most ceil(seg_cap / kExpChunk); otherwise either
+  // c >= listed / waves >= count / waves, so at most `waves`, or
+  // c = kExpChunkMin, so at most ceil(seg_cap / kExpChunkMin).
+  a.P_max = a.nch_a4 + (int)std::min<int64_t>((s->seg_cap + kExpChunkMin - 1) / kExpChunkMin,
+                                              std::max<int64_t>(a.n_a5_wg, (s->seg_cap + kExpChunk - 1) / kExpChunk));
   a.n_fx_wg = (a.n_a5_wg + 3) / 4;
   a.n_a4_wg = BG * a.nch_a4;
   int mr = 0;

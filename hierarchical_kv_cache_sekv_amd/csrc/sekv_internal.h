@@ -12,7 +12,8 @@ constexpr int kMaxGroups = 256;      // batch * kv heads handled by one decode l
 constexpr int kMaxSpan = 128;        // longest span body / highest rank the kernels hold
 constexpr int kRouteThreads = 256;   // spans per route workgroup (one lane per span)
 constexpr int kAttnThreads = 256;    // four waves per attention workgroup
-constexpr int kExpChunk = 8;         // expanded spans per work item of the expanded-span kernel
+constexpr int kExpChunk = 8;         // most expanded spans per work item of the expanded-span kernel
+constexpr int kExpChunkMin = 2;      // fewest (the item size adapts to the listed count, see item_spans)
 constexpr int kExpThreads = 64;      // one wave per expanded-span workgroup
 constexpr int kExpWaves = 2048;      // most waves (workgroups) of one expanded-span launch
 constexpr int kMaxDevices = 64;      // devices with a route scratch address
