@@ -449,27 +449,37 @@ struct TileSrc {
 };
 
 template <typename T, int D>
-__device__ __forceinline__ void tile_load(TileOps<T, D>& o, const TileSrc<T>& s, int t, int col, int cls) {
-  constexpr int NC = D / 32, NJ = D / 16;
+__device__ __forceinline__ void tile_load_k(TileOps<T, D>& o, const TileSrc<T>& s, int t, int col, int cls) {
+  constexpr int NC = D / 32;
   const bool summ = t >= s.nft;
-  const int tt = summ ? t - s.nft : t;
-  const int base = tt * 32;
+  const int base = (summ ? t - s.nft : t) * 32;
   const int npart = summ ? s.ns : s.nf;
   const T* krows = summ ? s.sk : s.fk;
-  const T* vt = (summ ? s.svt : s.fvt) + (size_t)tt * 32 * D;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int e = min(base + 8 * (col >> 2) + 4 * h + (col & 3), npart - 1);
 #pragma unroll
     for (int c = 0; c < NC; ++c) o.k[h][c] = ld8(krows + (size_t)e * D + 32 * c + 8 * cls);
   }
+}
+template <typename T, int D>
+__device__ __forceinline__ void tile_load_v(TileOps<T, D>& o, const TileSrc<T>& s, int t, int col, int cls) {
+  constexpr int NJ = D / 16;
+  const bool summ = t >= s.nft;
+  const int tt = summ ? t - s.nft : t;
+  const T* vt = (summ ? s.svt : s.fvt) + (size_t)tt * 32 * D;
 #pragma unroll
   for (int jt = 0; jt < NJ; ++jt) o.v[jt] = ld8(vt + (16 * jt + col) * 32 + 8 * cls);
+}
+template <typename T, int D>
+__device__ __forceinline__ void tile_load(TileOps<T, D>& o, const TileSrc<T>& s, int t, int col, int cls) {
+  tile_load_k<T, D>(o, s, t, col, cls);
+  tile_load_v<T, D>(o, s, t, col, cls);
 }
 
 // Scores, online softmax and P.V of one tile for head `col` of this lane.
 template <typename T, int D, int G>
-__device__ __forceinline__ void tile_step(const TileOps<T, D>& o, const TileSrc<T>& s, int t, int S0,
+__device__ __forceinline__ void tile_step(TileOps<T, D>& o, const TileSrc<T>& s, int t, int tn, int S0,
                                           const uint8_t* smask, const float* slog, const Vec8<T> (&qB)[D / 32],
                                           float qscale, int col, int cls, float& m, float& lsum,
                                           f32x4_t (&acc)[D / 16]) {
@@ -484,6 +494,10 @@ __device__ __forceinline__ void tile_step(const TileOps<T, D>& o, const TileSrc<
 #pragma unroll
     for (int c = 0; c < NC; ++c) sc[h] = mma8(o.k[h][c], qB[c], sc[h]);
   }
+  // the next tile's keys go in flight as soon as the scores have used these
+  // registers, its values after P.V (fused attention at 128K batch 4: 78.0
+  // against 79.2 us; with no expansion 48.9 against 50.3 us)
+  if (tn >= 0) tile_load_k<T, D>(o, s, tn, col, cls);
   // this lane: head col, tile entries 8*cls + 4h + v
   float sv[8];
 #pragma unroll
@@ -523,6 +537,7 @@ __device__ __forceinline__ void tile_step(const TileOps<T, D>& o, const TileSrc<
   pack8(p, pB);
 #pragma unroll
   for (int jt = 0; jt < NJ; ++jt) acc[jt] = mma8(o.v[jt], pB, acc[jt]);
+  if (tn >= 0) tile_load_v<T, D>(o, s, tn, col, cls);
 }
 
 // Role A: one workgroup = a chunk of tiles_a4 32-entry tiles of the (b, kv)
@@ -631,13 +646,13 @@ __device__ __forceinline__ void role_full_summary(const AttendArgs& a, int idx, 
 #pragma unroll
   for (int jt = 0; jt < NJ; ++jt) acc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // This wave's tiles t, t + 4, ...: one operand set, loaded as soon as the
-  // previous tile is scored.  A single set keeps the fused launch at three
-  // waves per SIMD; the other waves of the SIMD cover the load latency.
+  // This wave's tiles t, t + 4, ...: one operand set, refilled with the next
+  // tile inside tile_step as soon as each half has been used.  A single set
+  // keeps the fused launch at three waves per SIMD; the other waves of the
+  // SIMD cover the load latency.
   while (t < t1) {
-    tile_step<T, D, G>(opA, src, t, S0, smask, slog, qB, qscale, col, cls, m, lsum, acc);
+    tile_step<T, D, G>(opA, src, t, t + 4 < t1 ? t + 4 : -1, S0, smask, slog, qB, qscale, col, cls, m, lsum, acc);
     t += 4;
-    if (t < t1) tile_load<T, D>(opA, src, t, col, cls);
   }
 
   // this wave's state of head col: lsum summed over the four lane classes
