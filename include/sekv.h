@@ -177,6 +177,9 @@ typedef struct sekv_spans {
 typedef struct sekv_ctx sekv_ctx;
 
 /* Context for one GPU: events, timing hooks and the copy-side thread pool.
+ * The pool (host gathers of the staged fetch, host-side span builds) has
+ * min(hardware threads, 16) threads, or SEKV_THREADS threads when that
+ * environment variable holds a positive integer; it changes no result.
  * Errors: SEKV_EINVAL (out == NULL), SEKV_EHIP (bad device), SEKV_ENOMEM. */
 sekv_status sekv_ctx_create(int device, sekv_ctx** out);
 void sekv_ctx_destroy(sekv_ctx* ctx);
