@@ -218,6 +218,13 @@ constexpr float kNegInf = -__builtin_inff();
 // is bound by its memory phase: without the chain it still takes 18 us, and
 // streaming the keys alone 12 us.
 //
+// 16 bytes from global memory as a vector value (keeps the staging array in
+// registers; an aggregate copy into it leaves the array in scratch memory).
+typedef unsigned int route_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 route_ld16(const char* p) {
+  const route_u32x4 x = *reinterpret_cast<const route_u32x4*>(p);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
 constexpr int kRouteRowBytes = 128;
 constexpr int kRouteRowStride = 144;
 constexpr int kRouteSpinLimit = 1 << 20;
@@ -279,12 +286,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a)
   }
   if ((int)blockIdx.x >= nb) return;
   if (tid == 0) s_ticket = a.use_ticket ? (int)atomic_add_dev(a.ticket + g, 1u) : (int)blockIdx.x;
+  // Every load before the row stream is unconditional, with its index clamped
+  // into range: a load under a condition becomes a branch, and the compiler
+  // then waits for it inside the branch before the next load is issued.  The
+  // query rows are requested first and stored to LDS after the key rows are
+  // requested, so the row stream does not wait for them.
+  constexpr int QPT = (G * D + kRouteThreads - 1) / kRouteThreads;
+  float qv[QPT];
   if constexpr (FOLD) {
     const float* qf = a.qfold + ((size_t)b * a.Hq + (size_t)kv * G) * D;
-    for (int i = tid; i < G * D; i += kRouteThreads) qs[i] = qf[i];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) qv[k] = qf[min(tid + kRouteThreads * k, G * D - 1)];
   } else {
     const T* q = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)kv * G) * D;
-    for (int i = tid; i < G * D; i += kRouteThreads) qs[i] = load1(q + i);
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) qv[k] = load1(q + min(tid + kRouteThreads * k, G * D - 1));
   }
   float th[G];
 #pragma unroll
@@ -299,19 +315,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteArgs a)
   float z[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) z[gi] = 0.0f;
-  const float ksc = FOLD && tid < nrow ? a.key_scale[(size_t)g * a.seg_cap + S0 + tid] : 0.0f;
+  const float ksc = FOLD ? a.key_scale[(size_t)g * a.seg_cap + S0 + min(tid, nrow - 1)] : 0.0f;
   uint4 v[NP][8];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int piece = tid + kRouteThreads * j, row = piece >> 3, c = piece & 7;
-      v[p][j] = row < nrow ? *reinterpret_cast<const uint4*>(rbase + (size_t)row * D * sizeof(T) + p * kRouteRowBytes + c * 16)
-                           : make_uint4(0, 0, 0, 0);
+      // rows past the tile's last span repeat that span's row; no lane reads them
+      const int piece = tid + kRouteThreads * j, row = min(piece >> 3, nrow - 1), c = piece & 7;
+      v[p][j] = route_ld16(rbase + (size_t)row * D * sizeof(T) + p * kRouteRowBytes + c * 16);
+      // keep the passes' loads in pass order: the first pass's data then lands
+      // first, and its chain runs while the later passes' rows are in flight
+      if (j == 7) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
+  for (int k = 0; k < QPT; ++k)
+    if (tid + kRouteThreads * k < G * D) qs[tid + kRouteThreads * k] = qv[k];
+#pragma unroll
   for (int p = 0; p < NP; ++p) {
-    __syncthreads();  // the previous pass's row reads (and the q staging) are done
+    __syncthreads();  // the previous pass's row reads are done (first pass: the query rows are staged)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int piece = tid + kRouteThreads * j, row = piece >> 3, c = piece & 7;
