@@ -246,20 +246,42 @@ __device__ __forceinline__ uint32_t atomic_load_dev(const uint32_t* p) {
 // Folded routing (route_keys = 1): the query is folded once per call,
 // q'[b][h][j] = fl32(sum over m of fold[kv][j][m] * q[b][h][m]), a sequential
 // fp64 chain in m with every product and sum rounded separately (one thread
-// per output element).
-template <typename T>
+// per output element).  The operands of 16 products are requested at a time
+// (the head dimension is a template parameter, so the loop unrolls); a loop
+// over a run-time length waited for each product's two loads in turn.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void fold_query_kernel(const RouteArgs a) {
 #pragma clang fp contract(off)
   const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int D = a.D, G = a.Hq / a.Hkv;
+  const int G = a.Hq / a.Hkv;
   if (idx >= a.B * a.Hq * D) return;
   const int j = idx % D, bh = idx / D, h = bh % a.Hq;
   const double* M = a.foldm + ((size_t)(h / G) * D + j) * D;
   const T* q = static_cast<const T*>(a.q) + (size_t)bh * D;
   double acc = 0.0;
-  for (int m = 0; m < D; ++m) {
-    const double prod = M[m] * (double)load1(q + m);
-    acc = acc + prod;
+#pragma unroll
+  for (int m0 = 0; m0 < D; m0 += 16) {
+    double mv[16];
+    float qv[16];
+#pragma unroll
+    for (int u = 0; u < 16; u += 2) {
+      const double2 x = *reinterpret_cast<const double2*>(M + m0 + u);
+      mv[u] = x.x;
+      mv[u + 1] = x.y;
+    }
+    float f0[8], f1[8];
+    load8(q + m0, f0);
+    load8(q + m0 + 8, f1);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      qv[u] = f0[u];
+      qv[u + 8] = f1[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const double prod = mv[u] * (double)qv[u];
+      acc = acc + prod;
+    }
   }
   a.qfold[idx] = (float)acc;
 }
@@ -1508,6 +1530,16 @@ __global__ __launch_bounds__(64) void recon_kernel(const ReconArgs a) {
 }
 
 // ---------------------------------------------------------------- dispatch
+#define SEKV_DISPATCH_T(DT, BODY) \
+  do {                              \
+    if ((DT) == 0) {                \
+      using TT = float;             \
+      BODY;                         \
+    } else {                        \
+      using TT = bf16raw;           \
+      BODY;                         \
+    }                               \
+  } while (0)
 #define SEKV_DISPATCH(DT, DIM, GRP, BODY)                                   \
   do {                                                                      \
     if ((DT) == 0) {                                                        \
@@ -2013,8 +2045,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t ev0, hipEv
   if (a.fold) {
     const int n = a.B * a.Hq * a.D;
     hipEvent_t none = nullptr;
-    if (a.dtype == 0) SEKV_LAUNCH(fold_query_kernel<float>, (n + 255) / 256, 256, 0, s, ev0, none, a);
-    else SEKV_LAUNCH(fold_query_kernel<bf16raw>, (n + 255) / 256, 256, 0, s, ev0, none, a);
+    SEKV_DISPATCH_T(a.dtype, ({
+      if (a.D == 64) SEKV_LAUNCH((fold_query_kernel<TT, 64>), (n + 255) / 256, 256, 0, s, ev0, none, a);
+      else SEKV_LAUNCH((fold_query_kernel<TT, 128>), (n + 255) / 256, 256, 0, s, ev0, none, a);
+    }));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SEKV_DISPATCH(a.dtype, a.D, G,
